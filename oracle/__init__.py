@@ -1,0 +1,124 @@
+"""fp64 CPU oracle for the PRISM memory-writing operator (forward pass).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The GPU library
+never loads it, and it shares no code with the GPU library.
+
+The arithmetic lives in ``prism_oracle.c`` (plain C, double precision,
+token-by-token recurrence; the definition and the readings it follows are in
+that file's header).  This module only compiles it with gcc, marshals numpy
+arrays through ctypes and returns double-precision numpy results.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "prism_oracle.c")
+_LIB = os.path.join(_HERE, "libprism_oracle.so")
+_lib = None
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in
+                ("n_seqs", "total_tokens", "heads", "dk", "dv", "L", "dtype")]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc into ``oracle/libprism_oracle.so``."""
+    global _lib
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared",
+                        "-Wall", "-Wextra", "-o", tmp, _SRC], check=True)
+        os.replace(tmp, _LIB)
+        _lib = None
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        lib.prism_oracle_prologue.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P,
+                                              ctypes.c_int]
+        lib.prism_oracle_prologue.restype = ctypes.c_int
+        lib.prism_oracle_fwd.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P, P, P, P,
+                                         ctypes.c_int64, P, P, ctypes.c_int]
+        lib.prism_oracle_fwd.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:      # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _ptr(x: Optional[np.ndarray]):
+    if x is None:
+        return None
+    assert x.flags["C_CONTIGUOUS"]
+    return x.ctypes.data
+
+
+def _dims(inp, dtype_code: int) -> _Dims:
+    return _Dims(inp.n_seqs, inp.total_tokens, inp.heads, inp.dk, inp.dv, inp.L, dtype_code)
+
+
+def _check(inp):
+    code = {"f32": 0, "bf16": 1}[inp.dtype]
+    want = np.float32 if code == 0 else np.uint16
+    for name, arr in inp.arrays().items():
+        if arr is None:
+            continue
+        if arr.dtype != want or not arr.flags["C_CONTIGUOUS"]:
+            raise TypeError(f"oracle input {name}: expected contiguous {want.__name__}")
+    cu = np.ascontiguousarray(inp.cu_seqlens, dtype=np.int32)
+    return code, cu
+
+
+def prologue(inp, threads: Optional[int] = None) -> np.ndarray:
+    """Write keys kw [T, H, dk] in float64."""
+    code, cu = _check(inp)
+    out = np.zeros((inp.total_tokens, inp.heads, inp.dk), dtype=np.float64)
+    d = _dims(inp, code)
+    rc = _load().prism_oracle_prologue(ctypes.byref(d), _ptr(cu), _ptr(inp.k), _ptr(inp.u),
+                                       _ptr(inp.a), _ptr(inp.h), _ptr(inp.b), _ptr(inp.conv_w),
+                                       _ptr(out), threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"prism_oracle_prologue failed ({rc})")
+    return out
+
+
+def fwd(inp, chains: Optional[Sequence[int]] = None, threads: Optional[int] = None):
+    """Forward pass.  Returns (o [T, H, dv], S_final [n_seqs, H, dk, dv]) in float64.
+
+    ``chains`` restricts the evaluation to the listed (sequence * H + head)
+    chains; rows of other chains are left at zero.
+    """
+    code, cu = _check(inp)
+    o = np.zeros((inp.total_tokens, inp.heads, inp.dv), dtype=np.float64)
+    s = np.zeros((inp.n_seqs, inp.heads, inp.dk, inp.dv), dtype=np.float64)
+    ch = None if chains is None else np.ascontiguousarray(np.asarray(chains, dtype=np.int64))
+    if ch is not None and ch.size and (ch.min() < 0 or ch.max() >= inp.n_seqs * inp.heads):
+        raise ValueError("chain index out of range")
+    d = _dims(inp, code)
+    rc = _load().prism_oracle_fwd(ctypes.byref(d), _ptr(cu), _ptr(inp.q), _ptr(inp.k),
+                                  _ptr(inp.v), _ptr(inp.u), _ptr(inp.g), _ptr(inp.b),
+                                  _ptr(inp.a), _ptr(inp.h), _ptr(inp.conv_w),
+                                  _ptr(ch), 0 if ch is None else int(ch.size),
+                                  _ptr(o), _ptr(s), threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"prism_oracle_fwd failed ({rc})")
+    return o, s
