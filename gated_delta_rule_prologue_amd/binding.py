@@ -1,0 +1,215 @@
+"""ctypes binding of libprism (C ABI in ``include/prism.h``).
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every step of the operator runs in the library's HIP kernels.  The
+functions raise if the library is not built -- there is no fallback path.
+
+Names follow the C ABI: ``fwd`` -> prism_fwd, ``prologue`` -> prism_prologue,
+``scan`` -> prism_scan, ``workspace_bytes`` -> prism_workspace_bytes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libprism.so")
+_lib = None
+
+PRISM_OK, PRISM_EINVAL, PRISM_EUNSUPPORTED, PRISM_EHIP = 0, 1, 2, 3
+PRISM_F32, PRISM_BF16 = 0, 1
+MAX_LEVELS = 16
+
+
+class PrismError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status_str(status)} ({status})")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("n_seqs", ctypes.c_int32), ("total_tokens", ctypes.c_int32),
+                ("heads", ctypes.c_int32), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded libprism.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is not built: run __graft_entry__.build() "
+                               "(or python -m gated_delta_rule_prologue_amd.build)")
+        L = ctypes.CDLL(_LIB_PATH)
+        P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        D = ctypes.POINTER(Dims)
+        L.prism_workspace_bytes.argtypes = [D, I]
+        L.prism_workspace_bytes.restype = S
+        L.prism_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, I, P, P, P, S, P]
+        L.prism_fwd.restype = I
+        L.prism_prologue.argtypes = [D, P, P, P, P, P, P, P, I, P, P]
+        L.prism_prologue.restype = I
+        L.prism_scan.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
+        L.prism_scan.restype = I
+        L.prism_status_str.argtypes = [I]
+        L.prism_status_str.restype = ctypes.c_char_p
+        L.prism_abi_version.argtypes = []
+        L.prism_abi_version.restype = I
+        _lib = L
+    return _lib
+
+
+def status_str(s: int) -> str:
+    return lib().prism_status_str(int(s)).decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return PRISM_BF16
+    if t.dtype == torch.float32:
+        return PRISM_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libprism takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("libprism takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def make_dims(n_seqs: int, total_tokens: int, heads: int, dk: int, dv: int, dtype: int) -> Dims:
+    return Dims(n_seqs, total_tokens, heads, dk, dv, dtype)
+
+
+def _dims_of(q_or_k: torch.Tensor, v: Optional[torch.Tensor], cu_seqlens: torch.Tensor) -> Dims:
+    if q_or_k.dim() != 3:
+        raise ValueError("q / k must be [T, H, dk]")
+    T, H, dk = q_or_k.shape
+    dv = v.shape[2] if v is not None else dk
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be int32 [n_seqs + 1] with n_seqs >= 1")
+    return Dims(cu_seqlens.numel() - 1, T, H, dk, dv, _dtype_code(q_or_k))
+
+
+def _expect(name: str, t: Optional[torch.Tensor], shape, dtype):
+    """Shape / dtype check so that the kernels never index past a caller's buffer."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+
+
+def _check_write_branch(d: Dims, dt, k, u, a, h, b, conv_w, L: int):
+    T, H, dk = d.total_tokens, d.heads, d.dk
+    _expect("k", k, (T, H, dk), dt)
+    _expect("b", b, (T, H), dt)
+    _expect("conv_w", conv_w, (H, dk, 4), dt)
+    if not 1 <= int(L) <= MAX_LEVELS:
+        raise ValueError(f"L must be in 1..{MAX_LEVELS}")
+    if L > 1:
+        for name, x in (("u", u), ("a", a), ("h", h)):
+            _expect(name, x, (T, H, L - 1, dk), dt)
+
+
+def _check_scan(d: Dims, dt, q, k, kw, v, g, b):
+    T, H = d.total_tokens, d.heads
+    for name, x in (("q", q), ("k", k), ("kw", kw)):
+        _expect(name, x, (T, H, d.dk), dt)
+    _expect("v", v, (T, H, d.dv), dt)
+    _expect("g", g, (T, H), dt)
+    _expect("b", b, (T, H), dt)
+
+
+def workspace_bytes(dims: Dims, L: int) -> int:
+    return int(lib().prism_workspace_bytes(ctypes.byref(dims), int(L)))
+
+
+def _check(fn: str, status: int):
+    if status != PRISM_OK:
+        raise PrismError(fn, status)
+
+
+def prologue(k, u, a, h, b, conv_w, cu_seqlens, L: int, kw=None, stream=None) -> torch.Tensor:
+    """Write keys kw [T, H, dk] (prism_prologue)."""
+    d = _dims_of(k, None, cu_seqlens)
+    _check_write_branch(d, k.dtype, k, u, a, h, b, conv_w, L)
+    if kw is None:
+        kw = torch.empty_like(k)
+    _expect("kw", kw, k.shape, k.dtype)
+    _check("prism_prologue", lib().prism_prologue(
+        ctypes.byref(d), _ptr(k), _ptr(u), _ptr(a), _ptr(h), _ptr(b), _ptr(conv_w),
+        _ptr(cu_seqlens), int(L), _ptr(kw), _stream(stream)))
+    return kw
+
+
+def scan(q, k, kw, v, g, b, cu_seqlens, o=None, S_final=None, stream=None):
+    """Chunkwise scan from precomputed write keys (prism_scan).  Returns (o, S_final)."""
+    d = _dims_of(q, v, cu_seqlens)
+    _check_scan(d, q.dtype, q, k, kw, v, g, b)
+    if o is None:
+        o = torch.empty_like(v)
+    if S_final is None:
+        S_final = torch.empty((d.n_seqs, d.heads, d.dk, d.dv), dtype=torch.float32, device=q.device)
+    _expect("o", o, v.shape, v.dtype)
+    _expect("S_final", S_final, (d.n_seqs, d.heads, d.dk, d.dv), torch.float32)
+    _check("prism_scan", lib().prism_scan(
+        ctypes.byref(d), _ptr(q), _ptr(k), _ptr(kw), _ptr(v), _ptr(g), _ptr(b), _ptr(cu_seqlens),
+        _ptr(o), _ptr(S_final), _stream(stream)))
+    return o, S_final
+
+
+def fwd(q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L: int, o=None, S_final=None,
+        workspace=None, stream=None):
+    """Full forward pass (prism_fwd).  Returns (o, S_final)."""
+    d = _dims_of(q, v, cu_seqlens)
+    _check_write_branch(d, q.dtype, k, u, a, h, b, conv_w, L)
+    _check_scan(d, q.dtype, q, k, k, v, g, b)
+    need = workspace_bytes(d, L)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if o is None:
+        o = torch.empty_like(v)
+    if S_final is None:
+        S_final = torch.empty((d.n_seqs, d.heads, d.dk, d.dv), dtype=torch.float32, device=q.device)
+    _expect("o", o, v.shape, v.dtype)
+    _expect("S_final", S_final, (d.n_seqs, d.heads, d.dk, d.dv), torch.float32)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    _check("prism_fwd", lib().prism_fwd(
+        ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(g), _ptr(b), _ptr(a), _ptr(h),
+        _ptr(conv_w), _ptr(cu_seqlens), int(L), _ptr(o), _ptr(S_final), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o, S_final
+
+
+def to_device(inp, device="cuda") -> dict:
+    """Upload an ``inputs.Inputs`` to device tensors (bf16 bits reinterpreted, no rounding)."""
+    out = {}
+    for name, arr in inp.arrays().items():
+        if arr is None:
+            out[name] = None
+            continue
+        t = torch.from_numpy(arr)
+        if arr.dtype.name == "uint16":
+            t = t.view(torch.bfloat16)
+        out[name] = t.to(device).contiguous()
+    out["cu_seqlens"] = torch.from_numpy(inp.cu_seqlens).to(device)
+    return out

@@ -1,0 +1,34 @@
+// kernels.h -- internal launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace prism {
+
+struct PrologueArgs {
+    bool bf16;
+    int n_seqs, total_tokens, heads, dk, L;
+    int strip;                      // tokens walked by one thread
+    const void *k, *u, *a, *h, *b, *conv_w;
+    const int32_t* cu_seqlens;
+    void* kw;
+};
+
+struct ScanArgs {
+    bool bf16;
+    int n_seqs, total_tokens, heads, dk, dv;
+    int dv_slice;                   // value columns owned by one workgroup
+    const void *q, *k, *kw, *v, *g, *b;
+    const int32_t* cu_seqlens;
+    void* o;
+    float* s_final;
+};
+
+hipError_t launch_prologue(const PrologueArgs& p, hipStream_t stream);
+
+// Returns hipErrorInvalidValue when (dtype, dk, dv_slice) has no kernel.
+hipError_t launch_scan(const ScanArgs& p, hipStream_t stream);
+bool scan_supported(bool bf16, int dk, int dv, int dv_slice);
+
+}  // namespace prism

@@ -1,0 +1,178 @@
+// prism_api.hip -- C ABI of libprism (declared in include/prism.h): argument
+// validation, kernel selection and launches on the caller's stream.
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "prism.h"
+#include "kernels.h"
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool dims_ok(const prism_dims* d)
+{
+    return d && d->n_seqs >= 1 && d->total_tokens >= 0 && d->heads >= 1 && d->dk >= 1 &&
+           d->dv >= 1 && (d->dtype == PRISM_F32 || d->dtype == PRISM_BF16);
+}
+
+size_t elem_bytes(const prism_dims* d) { return d->dtype == PRISM_BF16 ? 2 : 4; }
+
+// Pointer must be non-null and 16-byte aligned.
+bool ptr_ok(const void* p) { return p && aligned16(p); }
+
+// Per-token arrays may be NULL when there are no tokens at all.
+bool tok_ok(const prism_dims* d, const void* p)
+{
+    return d->total_tokens == 0 ? aligned16(p) : ptr_ok(p);
+}
+
+int env_int(const char* name, int fallback)
+{
+    const char* s = getenv(name);
+    if (!s || !*s)
+        return fallback;
+    char* end = nullptr;
+    long v = strtol(s, &end, 10);
+    return (end && *end == 0 && v > 0 && v < (1 << 20)) ? (int)v : fallback;
+}
+
+// Value columns per scan workgroup: split the dv columns of each chain until
+// there are enough workgroups for the 256 CUs (columns of S are independent).
+int pick_dv_slice(const prism_dims* d)
+{
+    const bool bf16 = d->dtype == PRISM_BF16;
+    const int forced = env_int("PRISM_DV_SLICE", 0);
+    if (forced && prism::scan_supported(bf16, d->dk, d->dv, forced))
+        return forced;
+    const long chains = (long)d->n_seqs * d->heads;
+    const int cands[3] = {64, 32, 16};
+    int best = 0;
+    for (int c : cands) {
+        if (!prism::scan_supported(bf16, d->dk, d->dv, c))
+            continue;
+        best = c;                                   // smallest supported so far
+        if (chains * (d->dv / c) >= 192)
+            return c;                               // largest slice that fills the chip
+    }
+    return best;
+}
+
+prism_status check_scan_shape(const prism_dims* d)
+{
+    const bool bf16 = d->dtype == PRISM_BF16;
+    for (int c : {64, 32, 16})
+        if (prism::scan_supported(bf16, d->dk, d->dv, c))
+            return PRISM_OK;
+    return PRISM_EUNSUPPORTED;
+}
+
+prism_status from_hip(hipError_t e) { return e == hipSuccess ? PRISM_OK : PRISM_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int prism_abi_version(void) { return PRISM_ABI_VERSION; }
+
+const char* prism_status_str(prism_status s)
+{
+    switch (s) {
+    case PRISM_OK: return "ok";
+    case PRISM_EINVAL: return "invalid argument";
+    case PRISM_EUNSUPPORTED: return "unsupported shape or dtype";
+    case PRISM_EHIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+size_t prism_workspace_bytes(const prism_dims* d, int L)
+{
+    if (!dims_ok(d) || L < 1 || L > PRISM_MAX_LEVELS)
+        return 0;
+    size_t n = (size_t)d->total_tokens * (size_t)d->heads * (size_t)d->dk * elem_bytes(d);
+    n = (n + 255) / 256 * 256;
+    return n < 256 ? 256 : n;
+}
+
+prism_status prism_prologue(const prism_dims* d, const void* k, const void* u, const void* a,
+                            const void* h, const void* b, const void* conv_w,
+                            const int32_t* cu_seqlens, int L, void* kw, void* stream)
+{
+    if (!dims_ok(d) || L < 1 || L > PRISM_MAX_LEVELS)
+        return PRISM_EINVAL;
+    if (!tok_ok(d, k) || !tok_ok(d, b) || !ptr_ok(conv_w) || !ptr_ok(cu_seqlens) ||
+        !tok_ok(d, kw))
+        return PRISM_EINVAL;
+    if (L > 1 && (!tok_ok(d, u) || !tok_ok(d, a) || !tok_ok(d, h)))
+        return PRISM_EINVAL;
+    const int vec = d->dtype == PRISM_BF16 ? 8 : 4;
+    if (d->dk % vec != 0)
+        return PRISM_EUNSUPPORTED;
+    prism::PrologueArgs p;
+    p.bf16 = d->dtype == PRISM_BF16;
+    p.n_seqs = d->n_seqs;
+    p.total_tokens = d->total_tokens;
+    p.heads = d->heads;
+    p.dk = d->dk;
+    p.L = L;
+    p.strip = env_int("PRISM_PROLOGUE_STRIP", 16);
+    p.k = k; p.u = u; p.a = a; p.h = h; p.b = b; p.conv_w = conv_w;
+    p.cu_seqlens = cu_seqlens;
+    p.kw = kw;
+    return from_hip(prism::launch_prologue(p, (hipStream_t)stream));
+}
+
+prism_status prism_scan(const prism_dims* d, const void* q, const void* k, const void* kw,
+                        const void* v, const void* g, const void* b, const int32_t* cu_seqlens,
+                        void* o, float* S_final, void* stream)
+{
+    if (!dims_ok(d))
+        return PRISM_EINVAL;
+    if (!tok_ok(d, q) || !tok_ok(d, k) || !tok_ok(d, kw) || !tok_ok(d, v) || !tok_ok(d, g) ||
+        !tok_ok(d, b) || !ptr_ok(cu_seqlens) || !tok_ok(d, o) || !ptr_ok(S_final))
+        return PRISM_EINVAL;
+    prism_status st = check_scan_shape(d);
+    if (st != PRISM_OK)
+        return st;
+    prism::ScanArgs p;
+    p.bf16 = d->dtype == PRISM_BF16;
+    p.n_seqs = d->n_seqs;
+    p.total_tokens = d->total_tokens;
+    p.heads = d->heads;
+    p.dk = d->dk;
+    p.dv = d->dv;
+    p.dv_slice = pick_dv_slice(d);
+    p.q = q; p.k = k; p.kw = kw; p.v = v; p.g = g; p.b = b;
+    p.cu_seqlens = cu_seqlens;
+    p.o = o;
+    p.s_final = S_final;
+    return from_hip(prism::launch_scan(p, (hipStream_t)stream));
+}
+
+prism_status prism_fwd(const prism_dims* d, const void* q, const void* k, const void* v,
+                       const void* u, const void* g, const void* b, const void* a,
+                       const void* h, const void* conv_w, const int32_t* cu_seqlens, int L,
+                       void* o, float* S_final, void* workspace, size_t workspace_bytes,
+                       void* stream)
+{
+    if (!dims_ok(d) || L < 1 || L > PRISM_MAX_LEVELS)
+        return PRISM_EINVAL;
+    if (!tok_ok(d, q) || !tok_ok(d, k) || !tok_ok(d, v) || !tok_ok(d, g) || !tok_ok(d, b) ||
+        !ptr_ok(conv_w) || !ptr_ok(cu_seqlens) || !tok_ok(d, o) || !ptr_ok(S_final) ||
+        !ptr_ok(workspace))
+        return PRISM_EINVAL;
+    if (L > 1 && (!tok_ok(d, u) || !tok_ok(d, a) || !tok_ok(d, h)))
+        return PRISM_EINVAL;
+    if (workspace_bytes < prism_workspace_bytes(d, L))
+        return PRISM_EINVAL;
+    prism_status st = check_scan_shape(d);
+    if (st != PRISM_OK)
+        return st;
+    st = prism_prologue(d, k, u, a, h, b, conv_w, cu_seqlens, L, workspace, stream);
+    if (st != PRISM_OK)
+        return st;
+    return prism_scan(d, q, k, workspace, v, g, b, cu_seqlens, o, S_final, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,168 @@
+// prologue.hip -- fused write-key prologue of PRISM's memory-writing operator.
+//
+// For every token t and head e (all channels i independent):
+//   r_0  = sum_{m=0..3} w[e,i,m] * k[t-3+m]     causal depthwise ShortConv, width 4,
+//                                               taps before the sequence start read 0
+//   r_1  = r_0,  r_{l+1} = r_l * (1 - a_l h_l)  closed-form residual chain
+//   kw   = b_t k_t + sum_{l=1..L-1} a_l r_l u_l
+// PRISM pages: WeChat ICML 2026 summary, sections 消除 Token 间串行 (ShortConv
+// anchor) and 消除 Step 间串行 (residual chain linearised to an element-wise
+// recurrence with a closed form); gist.science summary of arXiv 2602.10796,
+// section 2.2 (anchor, then refinement levels l = 1..L, r^(1) = anchor).
+//
+// Design (HBM-bound streaming, ~0.5 flop/byte):
+//   * one thread owns 16 bytes of channels (8 bf16 / 4 fp32) of one head and
+//     walks a strip of consecutive tokens, so the 3-token conv halo lives in
+//     registers and every k element is read from HBM once (plus a 3-token
+//     halo per strip);
+//   * consecutive threads own consecutive 16-byte channel groups, so every
+//     wavefront load instruction covers whole 256-byte rows of k, u, a, h;
+//   * L is a template parameter: the level loop unrolls completely and h's
+//     last slot (never read by the closed form) is never loaded;
+//   * sequence boundaries come from cu_seqlens on the device (binary search
+//     once per strip, then a forward walk), so no host synchronisation.
+#include "common.h"
+#include "kernels.h"
+
+namespace prism {
+
+template <typename T, int L>
+__global__ __launch_bounds__(256) void prologue_kernel(
+    const T* __restrict__ k, const T* __restrict__ u, const T* __restrict__ a,
+    const T* __restrict__ h, const T* __restrict__ b, const T* __restrict__ conv_w,
+    const int32_t* __restrict__ cu, int n_seqs, int T_total, int H, int dk,
+    int strip, T* __restrict__ kw)
+{
+    constexpr int V = Vec16<T>::N;
+    const int groups = H * dk / V;                       // 16-byte groups per token row
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int cg = (int)(gid % groups);
+    const int64_t t0_64 = (gid / groups) * strip;
+    if (t0_64 >= T_total)
+        return;
+    const int t0 = (int)t0_64;
+    const int t1 = min(T_total, t0 + strip);
+    const int e = (cg * V) / dk;
+    const int i0 = (cg * V) % dk;
+
+    // conv taps for this thread's channels: w[e][i0 + c][m]
+    float w[V][4];
+#pragma unroll
+    for (int c = 0; c < V; ++c) {
+        const T* wp = conv_w + ((int64_t)e * dk + i0 + c) * 4;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            w[c][m] = to_f32(wp[m]);
+    }
+
+    // sequence containing t0: the largest n with cu[n] <= t0 (then t0 < cu[n+1])
+    int lo = 0, hi = n_seqs;
+    while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (cu[mid] <= t0) lo = mid; else hi = mid;
+    }
+    int n = lo;
+    int seq_start = cu[n];
+    int next_start = cu[n + 1];
+
+    const int64_t row = (int64_t)H * dk;                 // elements per token of k / kw
+    const int64_t lrow = (int64_t)H * (L - 1) * dk;      // elements per token of u / a / h
+    const int64_t koff = (int64_t)e * dk + i0;
+    const int64_t loff = (int64_t)e * (L - 1) * dk + i0;
+
+    // conv history: x1 = k[t-1], x2 = k[t-2], x3 = k[t-3] (zero before the sequence start)
+    float x1[V], x2[V], x3[V];
+#pragma unroll
+    for (int c = 0; c < V; ++c) { x1[c] = 0.f; x2[c] = 0.f; x3[c] = 0.f; }
+    if (t0 - 1 >= seq_start) Vec16<T>::load(k + (int64_t)(t0 - 1) * row + koff, x1);
+    if (t0 - 2 >= seq_start) Vec16<T>::load(k + (int64_t)(t0 - 2) * row + koff, x2);
+    if (t0 - 3 >= seq_start) Vec16<T>::load(k + (int64_t)(t0 - 3) * row + koff, x3);
+
+    for (int t = t0; t < t1; ++t) {
+        if (t == next_start) {                           // a new sequence starts at t
+            while (cu[n + 1] <= t) ++n;                  // skips empty sequences; n+1 <= n_seqs
+            next_start = cu[n + 1];
+#pragma unroll
+            for (int c = 0; c < V; ++c) { x1[c] = 0.f; x2[c] = 0.f; x3[c] = 0.f; }
+        }
+        float kt[V];
+        Vec16<T>::load(k + (int64_t)t * row + koff, kt);
+        const float bt = to_f32(b[(int64_t)t * H + e]);
+        float acc[V], r[V];
+#pragma unroll
+        for (int c = 0; c < V; ++c) {
+            r[c] = w[c][3] * kt[c] + w[c][2] * x1[c] + w[c][1] * x2[c] + w[c][0] * x3[c];
+            acc[c] = bt * kt[c];
+        }
+        const T* ub = u + (int64_t)t * lrow + loff;
+        const T* ab = a + (int64_t)t * lrow + loff;
+        const T* hb = h + (int64_t)t * lrow + loff;
+#pragma unroll
+        for (int s = 0; s < L - 1; ++s) {                // level l = s + 1
+            float av[V], uv[V];
+            Vec16<T>::load(ab + s * dk, av);
+            Vec16<T>::load(ub + s * dk, uv);
+#pragma unroll
+            for (int c = 0; c < V; ++c)
+                acc[c] += av[c] * r[c] * uv[c];
+            if (s < L - 2) {                             // residual for the next level
+                float hv[V];
+                Vec16<T>::load(hb + s * dk, hv);
+#pragma unroll
+                for (int c = 0; c < V; ++c)
+                    r[c] *= 1.f - av[c] * hv[c];
+            }
+        }
+        Vec16<T>::store(kw + (int64_t)t * row + koff, acc);
+#pragma unroll
+        for (int c = 0; c < V; ++c) { x3[c] = x2[c]; x2[c] = x1[c]; x1[c] = kt[c]; }
+    }
+}
+
+template <typename T, int L>
+static hipError_t launch_L(const PrologueArgs& p, hipStream_t stream)
+{
+    constexpr int V = Vec16<T>::N;
+    const int64_t groups = (int64_t)p.heads * p.dk / V;
+    const int64_t strips = (p.total_tokens + p.strip - 1) / p.strip;
+    const int64_t threads = groups * strips;
+    if (threads == 0)
+        return hipSuccess;
+    const int64_t blocks = (threads + 255) / 256;
+    hipLaunchKernelGGL((prologue_kernel<T, L>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const T*)p.k, (const T*)p.u, (const T*)p.a, (const T*)p.h, (const T*)p.b,
+                       (const T*)p.conv_w, p.cu_seqlens, p.n_seqs, p.total_tokens, p.heads, p.dk,
+                       p.strip, (T*)p.kw);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_T(const PrologueArgs& p, hipStream_t s)
+{
+    switch (p.L) {
+    case 1: return launch_L<T, 1>(p, s);
+    case 2: return launch_L<T, 2>(p, s);
+    case 3: return launch_L<T, 3>(p, s);
+    case 4: return launch_L<T, 4>(p, s);
+    case 5: return launch_L<T, 5>(p, s);
+    case 6: return launch_L<T, 6>(p, s);
+    case 7: return launch_L<T, 7>(p, s);
+    case 8: return launch_L<T, 8>(p, s);
+    case 9: return launch_L<T, 9>(p, s);
+    case 10: return launch_L<T, 10>(p, s);
+    case 11: return launch_L<T, 11>(p, s);
+    case 12: return launch_L<T, 12>(p, s);
+    case 13: return launch_L<T, 13>(p, s);
+    case 14: return launch_L<T, 14>(p, s);
+    case 15: return launch_L<T, 15>(p, s);
+    case 16: return launch_L<T, 16>(p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_prologue(const PrologueArgs& p, hipStream_t stream)
+{
+    return p.bf16 ? launch_T<uint16_t>(p, stream) : launch_T<float>(p, stream);
+}
+
+}  // namespace prism

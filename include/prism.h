@@ -1,0 +1,144 @@
+/*
+ * prism.h -- C ABI of libprism: the forward pass of PRISM's memory-writing
+ * operator on AMD Instinct MI355X (gfx950).
+ *
+ * The operator (PRISM: Parallel Residual Iterative Sequence Model) keeps, per
+ * (sequence, head), a state S in R^{dk x dv} that starts at zero and, for each
+ * token t of the sequence,
+ *
+ *   r_0   = causal depthwise ShortConv(width 4) of k at t       (local anchor)
+ *   r_1   = r_0,  r_l = r_0 * prod_{j=1..l-1} (1 - a_j * h_j)   (residual chain, closed form)
+ *   kw_t  = b_t k_t + sum_{l=1..L-1} a_l * r_l * u_l             (write key)
+ *   S_t   = g_t (I - b_t k_t k_t^T) S_{t-1} + kw_t v_t^T         (GDN forget/erase + write)
+ *   o_t   = S_t^T q_t
+ *
+ * ("*" is element-wise over the dk channel.)  Sources, all on the PRISM
+ * pages: ICML 2026 PRISM summary (WeChat article), sections 核心迭代形式
+ * (multi-step write), 消除 Token 间串行 (GDN forget, ShortConv anchor),
+ * 消除 Step 间串行 (closed-form residual chain) and 架构形式 (L = 1 is GDN);
+ * gist.science technical summary of arXiv 2602.10796, sections 2.1-2.2;
+ * ICML 2026 poster abstract (the short convolution anchors the initial
+ * residual).  Readings where the pages are silent: the residual product runs
+ * over j = 1..l-1 (so h's last slot is never read); conv tap 3 multiplies the
+ * current token, taps before a sequence start read zero, no bias, no
+ * activation; g and b are per (token, head) scalars, g in linear space; no
+ * query scaling; zero initial state.
+ *
+ * Conventions for every entry point
+ *   - Tensors are dense, row-major, DEVICE pointers owned by the caller; the
+ *     library never allocates, frees or retains them.  They must stay valid
+ *     until the work queued on `stream` has finished.
+ *   - Float inputs share one dtype (prism_dims.dtype): IEEE fp32, or bf16 as
+ *     raw 16-bit patterns.  Outputs o and kw use that dtype; S_final is fp32.
+ *   - Every pointer must be non-null and 16-byte aligned, except that the per-token
+ *     arrays (q, k, v, u, a, h, g, b, o, kw) may be NULL when total_tokens == 0.
+ *     cu_seqlens is int32.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *     asynchronous: they enqueue kernels and return; no host synchronisation
+ *     and no device-to-host copy happens inside.
+ *   - Errors are return codes; nothing is thrown across the boundary.  All
+ *     argument checks happen before any launch, so an error return means that
+ *     nothing was enqueued.  A failed launch returns PRISM_EHIP.
+ *   - Preconditions not checked (they live in device memory): cu_seqlens is
+ *     non-decreasing, cu_seqlens[0] = 0 and cu_seqlens[n_seqs] = total_tokens.
+ *   - The library keeps no state between calls and is re-entrant; calls on
+ *     different streams may overlap if their output buffers do not.
+ */
+#ifndef PRISM_H
+#define PRISM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Other shapes return PRISM_EUNSUPPORTED.  Gates: 0 <= g <= 1 (values below
+ * 1e-30 act as 1e-30: the scan works with log2 g). */
+typedef enum {
+    PRISM_OK = 0,
+    PRISM_EINVAL = 1,          /* null/misaligned pointer, bad size, L out of range */
+    PRISM_EUNSUPPORTED = 2,    /* valid but not implemented here (e.g. dk not in {64, 128}) */
+    PRISM_EHIP = 3             /* a HIP launch failed */
+} prism_status;
+
+typedef enum { PRISM_F32 = 0, PRISM_BF16 = 1 } prism_dtype;
+
+typedef struct {
+    int32_t n_seqs;        /* number of packed sequences, >= 1 */
+    int32_t total_tokens;  /* T = cu_seqlens[n_seqs], >= 0 */
+    int32_t heads;         /* H >= 1 */
+    int32_t dk;            /* key width   (prism_fwd / prism_scan: bf16 64 or 128, fp32 64) */
+    int32_t dv;            /* value width (prism_fwd / prism_scan: 64 or 128) */
+    int32_t dtype;         /* prism_dtype of every float input */
+} prism_dims;
+
+#define PRISM_MAX_LEVELS 16
+
+/* Bytes of device workspace prism_fwd needs: the write keys kw [T, H, dk] in
+ * the input dtype, rounded up to 256 bytes.  Returns 0 for invalid dims or L. */
+size_t prism_workspace_bytes(const prism_dims* d, int L);
+
+/*
+ * Full forward pass: prologue then chunkwise scan, both on `stream`.
+ *
+ *   q, k         [T, H, dk]
+ *   v            [T, H, dv]
+ *   u, a, h      [T, H, L-1, dk]  slot s holds level l = s + 1; NULL allowed iff L == 1
+ *   g, b         [T, H]           forget gate (linear space) and erase/write strength
+ *   conv_w       [H, dk, 4]       ShortConv taps; tap 3 multiplies token t, tap m token t-3+m
+ *   cu_seqlens   [n_seqs + 1]     int32 device array of sequence offsets
+ *   L            levels, 1..PRISM_MAX_LEVELS; L == 1 is exactly Gated DeltaNet
+ *   o            out [T, H, dv], input dtype
+ *   S_final      out fp32 [n_seqs, H, dk, dv], the state after each sequence's last token
+ *                (zero for an empty sequence)
+ *   workspace    device buffer of at least prism_workspace_bytes(d, L) bytes
+ *
+ * Sources: see the header comment above.
+ */
+prism_status prism_fwd(const prism_dims* d,
+                       const void* q, const void* k, const void* v,
+                       const void* u, const void* g, const void* b,
+                       const void* a, const void* h, const void* conv_w,
+                       const int32_t* cu_seqlens, int L,
+                       void* o, float* S_final,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Prologue only: the write keys kw [T, H, dk] (input dtype, rounded to
+ * nearest-even for bf16), i.e. the ShortConv anchor, the closed-form
+ * residual chain and the write-key sum (WeChat page sections 消除 Token 间串行
+ * and 消除 Step 间串行; gist.science section 2.2).  Arguments as in prism_fwd.
+ * dk may be any multiple of 8 (bf16) or 4 (fp32) here.
+ */
+prism_status prism_prologue(const prism_dims* d,
+                            const void* k, const void* u, const void* a,
+                            const void* h, const void* b, const void* conv_w,
+                            const int32_t* cu_seqlens, int L,
+                            void* kw, void* stream);
+
+/*
+ * Scan only, from precomputed write keys kw [T, H, dk] (input dtype): the
+ * gated delta-rule state recurrence S_t = g_t (I - b_t k_t k_t^T) S_{t-1} +
+ * kw_t v_t^T, o_t = S_t^T q_t (WeChat page section 消除 Token 间串行: forget
+ * identical to GDN; gist.science section 2.1: S_t = S_{t-1} A_t + B_t with an
+ * input-only write), evaluated in chunks of 64 tokens.  Other arguments as in
+ * prism_fwd.
+ */
+prism_status prism_scan(const prism_dims* d,
+                        const void* q, const void* k, const void* kw, const void* v,
+                        const void* g, const void* b, const int32_t* cu_seqlens,
+                        void* o, float* S_final, void* stream);
+
+/* Static description of a status code. */
+const char* prism_status_str(prism_status s);
+
+/* ABI version of this header (bumped on any signature change). */
+int prism_abi_version(void);
+#define PRISM_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PRISM_H */

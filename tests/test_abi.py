@@ -1,0 +1,123 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every
+declared symbol, and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "prism.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(prism_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from gated_delta_rule_prologue_amd import binding
+    if not os.path.exists(binding.lib_path()):
+        pytest.fail("libprism.so is not built (run __graft_entry__.build())")
+    return binding.lib()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("prism_fwd", "prism_prologue", "prism_scan", "prism_workspace_bytes",
+              "prism_status_str", "prism_abi_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_abi_version(lib):
+    assert lib.prism_abi_version() == 1
+
+
+def test_status_strings(lib):
+    from gated_delta_rule_prologue_amd import binding
+    assert binding.status_str(0) == "ok"
+    assert "invalid" in binding.status_str(1)
+    assert "unsupported" in binding.status_str(2)
+    assert "HIP" in binding.status_str(3)
+
+
+def test_workspace_bytes(lib):
+    from gated_delta_rule_prologue_amd import binding as B
+    d = B.make_dims(8, 16384, 6, 128, 128, B.PRISM_BF16)
+    assert B.workspace_bytes(d, 4) == 16384 * 6 * 128 * 2
+    d32 = B.make_dims(1, 3, 1, 64, 64, B.PRISM_F32)
+    assert B.workspace_bytes(d32, 2) == 768
+    assert B.workspace_bytes(B.make_dims(1, 0, 1, 64, 64, B.PRISM_BF16), 1) == 256
+    assert B.workspace_bytes(d, 0) == 0 and B.workspace_bytes(d, 17) == 0
+    assert B.workspace_bytes(B.make_dims(0, 0, 1, 64, 64, B.PRISM_BF16), 1) == 0
+
+
+FAKE = 0x10000          # aligned, never dereferenced: every call below fails validation first
+
+
+def _fwd(lib, d, L=2, ws=1 << 30, **over):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, u=FAKE, g=FAKE, b=FAKE, a=FAKE, h=FAKE, conv_w=FAKE,
+                cu=FAKE, o=FAKE, s=FAKE, w=FAKE)
+    args.update(over)
+    return lib.prism_fwd(ctypes.byref(d), args["q"], args["k"], args["v"], args["u"], args["g"],
+                         args["b"], args["a"], args["h"], args["conv_w"], args["cu"], L, args["o"],
+                         args["s"], args["w"], ws, None)
+
+
+def test_fwd_rejects_bad_arguments(lib):
+    from gated_delta_rule_prologue_amd import binding as B
+    # unsupported widths are reported as such (before any launch)
+    assert _fwd(lib, B.make_dims(1, 10, 1, 96, 64, B.PRISM_BF16)) == B.PRISM_EUNSUPPORTED
+    assert _fwd(lib, B.make_dims(1, 10, 1, 128, 128, B.PRISM_F32)) == B.PRISM_EUNSUPPORTED
+    ok = B.make_dims(1, 10, 1, 64, 64, B.PRISM_BF16)
+    # null / misaligned pointers, bad L, small workspace, bad dims
+    assert _fwd(lib, ok, q=None) == B.PRISM_EINVAL
+    assert _fwd(lib, ok, k=FAKE + 2) == B.PRISM_EINVAL
+    assert _fwd(lib, ok, u=None) == B.PRISM_EINVAL
+    assert _fwd(lib, ok, L=0) == B.PRISM_EINVAL
+    assert _fwd(lib, ok, L=17) == B.PRISM_EINVAL
+    assert _fwd(lib, ok, ws=16) == B.PRISM_EINVAL
+    assert _fwd(lib, ok, cu=None) == B.PRISM_EINVAL
+    assert _fwd(lib, ok, s=None) == B.PRISM_EINVAL
+    assert _fwd(lib, B.make_dims(0, 10, 1, 64, 64, B.PRISM_BF16)) == B.PRISM_EINVAL
+    assert _fwd(lib, B.make_dims(1, -1, 1, 64, 64, B.PRISM_BF16)) == B.PRISM_EINVAL
+    assert _fwd(lib, B.make_dims(1, 10, 0, 64, 64, B.PRISM_BF16)) == B.PRISM_EINVAL
+    assert _fwd(lib, B.make_dims(1, 10, 1, 64, 64, 7)) == B.PRISM_EINVAL
+    assert lib.prism_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2,
+                         FAKE, FAKE, FAKE, 1 << 30, None) == B.PRISM_EINVAL
+
+
+def test_prologue_and_scan_reject_bad_arguments(lib):
+    from gated_delta_rule_prologue_amd import binding as B
+    d = B.make_dims(1, 10, 1, 64, 64, B.PRISM_BF16)
+    assert lib.prism_prologue(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 3, FAKE,
+                              None) == B.PRISM_EINVAL
+    assert lib.prism_prologue(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE,
+                              None) == B.PRISM_EINVAL
+    d12 = B.make_dims(1, 10, 1, 12, 64, B.PRISM_BF16)
+    assert lib.prism_prologue(ctypes.byref(d12), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, FAKE,
+                              None) == B.PRISM_EUNSUPPORTED
+    assert lib.prism_scan(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                          None) == B.PRISM_EINVAL
+    d96 = B.make_dims(1, 10, 1, 64, 96, B.PRISM_BF16)
+    assert lib.prism_scan(ctypes.byref(d96), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                          None) == B.PRISM_EUNSUPPORTED
+
+
+def test_binding_checks_shapes_before_calling():
+    torch = pytest.importorskip("torch")
+    from gated_delta_rule_prologue_amd import binding as B
+    q = torch.zeros(4, 2, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 4], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        B.scan(q, q, q, q, torch.zeros(4, 3, dtype=torch.bfloat16), torch.zeros(4, 2), cu)
+    with pytest.raises(ValueError):
+        B.prologue(q, None, None, None, torch.zeros(4, 2, dtype=torch.bfloat16),
+                   torch.zeros(2, 64, 4, dtype=torch.bfloat16), cu.to(torch.int64), 1)

@@ -1,0 +1,191 @@
+"""GPU parity: libprism (HIP, gfx950) against the fp64 oracle, through the C ABI.
+
+Small shapes compare every element; the full-size workloads compare every
+element of a sample of (sequence, head) chains that the oracle evaluates
+exactly, with the same launch configuration the benchmark times.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from gated_delta_rule_prologue_amd.configs import WORKLOADS, Workload
+from gated_delta_rule_prologue_amd.inputs import make_inputs, to_float, f32_to_bf16_bits
+from tests.gpu_common import (TOL, TOL_KW, chain_row_mask, gpu_fwd, gpu_prologue, max_rel, say,
+                              to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gated_delta_rule_prologue_amd import binding
+    binding.lib()          # fails loudly if libprism.so is missing
+
+
+def W(name="t", H=2, dk=64, dv=64, L=4, dtype="bf16", lengths=(100,), seed=5, g_mu=3.0):
+    return Workload(name, heads=H, dk=dk, dv=dv, L=L, dtype=dtype, seed=seed,
+                    lengths=list(lengths), g_mu=g_mu)
+
+
+# ----------------------------------------------------------------------------- prologue
+PROLOGUE_CASES = [
+    W(dtype="f32", dk=64, L=2, lengths=(256,)),
+    W(dtype="f32", dk=64, L=5, lengths=(3, 0, 70, 1, 2, 129)),
+    W(dtype="bf16", dk=64, L=4, lengths=(17, 0, 64, 5)),
+    W(dtype="bf16", dk=128, L=4, lengths=(300, 33)),
+    W(dtype="bf16", dk=128, L=1, lengths=(40,)),
+    W(dtype="bf16", dk=64, L=16, lengths=(20, 9)),
+    W(dtype="bf16", dk=16, L=3, H=3, lengths=(31, 0, 2)),
+]
+
+
+@pytest.mark.parametrize("w", PROLOGUE_CASES, ids=lambda w: f"{w.dtype}-dk{w.dk}-L{w.L}-{len(w.lengths)}seq")
+def test_prologue_matches_oracle(w):
+    inp = make_inputs(w)
+    say(f"prologue {w}")
+    kw = gpu_prologue(inp)
+    ref = oracle.prologue(inp)
+    err = max_rel(kw, ref)
+    say(f"  kw max-rel err {err:.3e}")
+    assert err <= TOL_KW[w.dtype]
+
+
+def test_prologue_residual_amplified():
+    """u unnormalised x10 and a ~ U(0,1): the residual levels dominate kw."""
+    inp = make_inputs(W(dtype="bf16", dk=128, L=4, lengths=(90, 7)))
+    rng = np.random.default_rng(9)
+    inp.u[:] = f32_to_bf16_bits(10.0 * to_float(inp.u) * np.sqrt(inp.dk))
+    inp.a[:] = f32_to_bf16_bits(rng.uniform(0, 1, inp.a.shape).astype(np.float32))
+    kw = gpu_prologue(inp)
+    ref = oracle.prologue(inp)
+    bk = to_float(inp.b)[:, :, None].astype(np.float64) * to_float(inp.k)
+    assert np.max(np.abs(ref - bk)) > 5 * np.max(np.abs(bk))      # residual part dominates
+    assert max_rel(kw, ref) <= TOL_KW["bf16"]
+
+
+# ----------------------------------------------------------------------------- forward
+FWD_CASES = [
+    W(dtype="f32", dk=64, dv=64, L=2, lengths=(256,)),
+    W(dtype="f32", dk=64, dv=64, L=4, lengths=(256,)),              # strict-tolerance run of h
+    W(dtype="f32", dk=64, dv=64, L=3, lengths=(1, 64, 65, 0, 130)),
+    W(dtype="bf16", dk=64, dv=64, L=4, lengths=(200, 64, 1, 0, 77)),
+    W(dtype="bf16", dk=128, dv=128, L=4, lengths=(300, 63)),
+    W(dtype="bf16", dk=128, dv=128, L=1, lengths=(257,)),           # exact GDN
+    W(dtype="bf16", dk=128, dv=64, L=2, lengths=(150,)),
+    W(dtype="bf16", dk=64, dv=128, L=2, lengths=(150,)),
+    W(dtype="bf16", dk=64, dv=64, L=3, lengths=(190,), g_mu=-2.0),  # strong decay
+    W(dtype="bf16", dk=128, dv=128, L=8, lengths=(129,), H=1),
+]
+
+
+@pytest.mark.parametrize("w", FWD_CASES,
+                         ids=lambda w: f"{w.dtype}-dk{w.dk}-dv{w.dv}-L{w.L}-g{w.g_mu}-{len(w.lengths)}seq")
+def test_fwd_matches_oracle(w):
+    inp = make_inputs(w)
+    say(f"fwd {w}")
+    o, s = gpu_fwd(inp)
+    o_ref, s_ref = oracle.fwd(inp)
+    eo, es = max_rel(o, o_ref), max_rel(s, s_ref)
+    say(f"  o err {eo:.3e}  S err {es:.3e}")
+    assert np.isfinite(o).all() and np.isfinite(s).all()
+    assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("dvs", [16, 32, 64])
+@pytest.mark.parametrize("dk", [64, 128])
+def test_every_value_slice_width(dk, dvs, monkeypatch):
+    if dk == 128 and dvs == 64:
+        pytest.skip("no dk=128 kernel with 64 value columns per workgroup")
+    monkeypatch.setenv("PRISM_DV_SLICE", str(dvs))
+    inp = make_inputs(W(dtype="bf16", dk=dk, dv=64, L=3, lengths=(140, 3)))
+    o, s = gpu_fwd(inp)
+    o_ref, s_ref = oracle.fwd(inp)
+    say(f"dk {dk} dvs {dvs}: o {max_rel(o, o_ref):.3e} S {max_rel(s, s_ref):.3e}")
+    assert max_rel(o, o_ref) <= TOL["bf16"] and max_rel(s, s_ref) <= TOL["bf16"]
+
+
+def test_fp32_slice_32(monkeypatch):
+    monkeypatch.setenv("PRISM_DV_SLICE", "32")
+    inp = make_inputs(W(dtype="f32", dk=64, dv=64, L=4, lengths=(200,)))
+    o, s = gpu_fwd(inp)
+    o_ref, s_ref = oracle.fwd(inp)
+    assert max_rel(o, o_ref) <= TOL["f32"] and max_rel(s, s_ref) <= TOL["f32"]
+
+
+def test_scan_alone_from_oracle_write_keys():
+    """prism_scan fed with the oracle's write keys (rounded to the input dtype)."""
+    import torch
+    from gated_delta_rule_prologue_amd import binding
+    inp = make_inputs(W(dtype="bf16", dk=128, dv=128, L=4, lengths=(192, 50)))
+    kw_ref = oracle.prologue(inp)
+    dev = binding.to_device(inp)
+    kw = torch.from_numpy(f32_to_bf16_bits(kw_ref.astype(np.float32))).view(torch.bfloat16).cuda()
+    o, s = binding.scan(dev["q"], dev["k"], kw, dev["v"], dev["g"], dev["b"], dev["cu_seqlens"])
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.fwd(inp)
+    assert max_rel(to_host(o), o_ref) <= TOL["bf16"]
+    assert max_rel(to_host(s), s_ref) <= TOL["bf16"]
+
+
+def test_all_sequences_empty():
+    import torch
+    from gated_delta_rule_prologue_amd import binding
+    inp = make_inputs(W(dtype="bf16", dk=64, dv=64, L=2, lengths=(0, 0, 0)))
+    dev = binding.to_device(inp)
+    s = torch.full((3, 2, 64, 64), 7.0, device="cuda")
+    o, s = binding.fwd(dev["q"], dev["k"], dev["v"], dev["u"], dev["g"], dev["b"], dev["a"],
+                       dev["h"], dev["conv_w"], dev["cu_seqlens"], inp.L, S_final=s)
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and not s.any()
+
+
+def test_deterministic():
+    inp = make_inputs(W(dtype="bf16", dk=128, dv=128, L=4, lengths=(333, 21)))
+    o1, s1 = gpu_fwd(inp)
+    o2, s2 = gpu_fwd(inp)
+    assert np.array_equal(o1, o2) and np.array_equal(s1, s2)
+
+
+# ----------------------------------------------------------------------------- full-size workloads
+def _sample_chains(inp, k, seed):
+    """k chains: the longest sequence's chains first, then a seeded spread."""
+    H = inp.heads
+    lens = np.diff(inp.cu_seqlens)
+    longest = int(np.argmax(lens))
+    rng = np.random.default_rng(seed)
+    pool = [c for c in range(inp.n_seqs * H) if c // H != longest]
+    pick = [longest * H + (k % H)]
+    pick += [int(c) for c in rng.choice(pool, size=min(k - 1, len(pool)), replace=False)] if pool else []
+    return sorted(set(pick))
+
+
+@pytest.mark.parametrize("idx", range(len(WORKLOADS)), ids=[w.name for w in WORKLOADS])
+def test_workload_parity(idx):
+    w = WORKLOADS[idx]
+    say(f"workload {w.name}: generating")
+    inp = make_inputs(w)
+    if idx == 0:
+        chains = None
+    else:
+        chains = _sample_chains(inp, {1: 8, 2: 6, 3: 2, 4: 12}[idx], seed=idx)
+    say(f"workload {w.name}: T={inp.total_tokens} chains={chains}")
+    o, s = gpu_fwd(inp)
+    say(f"workload {w.name}: oracle")
+    o_ref, s_ref = oracle.fwd(inp, chains=chains)
+    if chains is None:
+        eo, es = max_rel(o, o_ref), max_rel(s, s_ref)
+    else:
+        rows = chain_row_mask(inp, chains)
+        smask = np.zeros((inp.n_seqs, inp.heads), dtype=bool)
+        for c in chains:
+            smask[divmod(c, inp.heads)] = True
+        eo = max_rel(o, o_ref, rows)
+        es = max_rel(s, s_ref, smask)
+    say(f"workload {w.name}: o err {eo:.3e} S err {es:.3e}")
+    assert np.isfinite(o).all() and np.isfinite(s).all()
+    assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]
