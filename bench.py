@@ -1,0 +1,226 @@
+"""Benchmark of the PRISM memory-writing forward pass (libprism, one MI355X).
+
+One step = the whole hot path over one batch of the 130M-LM-shaped layer
+(B=8 sequences x T=2048 tokens, H=6 heads, dk=dv=128, L=4, bf16 inputs,
+fp32 state): the prologue kernel (ShortConv anchor, closed-form residual
+chain, write keys) followed by the chunkwise WY/UT scan kernel, i.e. the two
+launches prism_fwd makes, issued through the C ABI as prism_prologue then
+prism_scan on the current stream.  Inputs are synthetic, seeded and already
+resident in HBM; several input copies are rotated so that the 256 MB Infinity
+Cache cannot hold a step's working set from the previous step.
+
+Prints ONE JSON line.  Per-kernel durations come from HIP events recorded on
+the launch stream inside the timed region.  The CPU baseline is the fp64
+oracle (plain C, OpenMP over chains) on the same workload, timed on the host
+cores; its outputs double as a parity check of the last timed step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "PRISM fwd tokens/sec at 1 GPU (L=4) + % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+FP32_MFMA_PEAK_TFLOPS = 157.3
+KERNEL_SOURCES = {
+    "prologue": "gated_delta_rule_prologue_amd/csrc/prologue.hip",
+    "scan": "gated_delta_rule_prologue_amd/csrc/chunk_scan.hip",
+}
+
+
+def algorithmic_work(w, n_seqs, T, esize):
+    """Algorithmic HBM bytes and MFMA flops of one step (see the design doc for the counts).
+
+    Per head-token (ht):
+      prologue bytes = e [dk (k) + 2 (L-1) dk (u, a) + max(L-2, 0) dk (h slots read) + 1 (b) + dk (kw)]
+      scan bytes     = e [3 dk (q, k, kw) + dv (v) + 2 (g, b) + dv (o)]  + S_final (fp32) per chain
+      scan flops     = chunk products of the WY/UT form with C = 64 and dense 64x64 tiles:
+                       4 Gram tiles 8 C dk, K S0 and Q S0 4 dk dv, three 64x64-by-V/X
+                       products 6 C dv, Tm R 2 C dv, state update 4 dk dv, UT inverse ~2C^2/3
+    """
+    H, dk, dv, L = w.heads, w.dk, w.dv, w.L
+    ht = T * H
+    pro = esize * (dk + 2 * (L - 1) * dk + max(L - 2, 0) * dk + 1 + dk) * ht
+    scan = esize * (3 * dk + dv + 2 + dv) * ht + 4 * n_seqs * H * dk * dv
+    C = 64
+    flops_ht = 8 * C * dk + 4 * dk * dv + 6 * C * dv + 2 * C * dv + 4 * dk * dv + (2 * C * C) // 3
+    return {"prologue_bytes": pro, "scan_bytes": scan, "scan_flops": flops_ht * ht,
+            "head_tokens": ht}
+
+
+def source_sha(path):
+    with open(os.path.join(ROOT, path), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    s = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    if not m or not s or s.group(1) != source_sha(KERNEL_SOURCES[kernel]):
+        return None
+    return float(m.group(1))
+
+
+def cpu_baseline(inp, o_gpu, s_gpu):
+    """fp64 oracle on the host cores over the whole workload; also a parity check."""
+    import numpy as np
+    import oracle
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    o_ref, s_ref = oracle.fwd(inp, threads=threads)
+    dt = time.perf_counter() - t0
+    o = o_gpu.float().cpu().numpy().astype(np.float64)
+    s = s_gpu.cpu().numpy().astype(np.float64)
+    eo = float(np.max(np.abs(o - o_ref)) / np.max(np.abs(o_ref)))
+    es = float(np.max(np.abs(s - s_ref)) / np.max(np.abs(s_ref)))
+    try:
+        cpu = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")
+                   if l.startswith("model name"))
+    except (OSError, StopIteration):
+        cpu = "unknown"
+    return ({"value": inp.total_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+             "sample": f"whole workload: all {inp.n_seqs * inp.heads} (sequence, head) chains, "
+                       f"{inp.total_tokens} tokens, fp64, OpenMP over chains",
+             "seconds": dt, "cpu_model": cpu},
+            {"o_max_rel_err": eo, "S_max_rel_err": es, "tolerance": 1e-2,
+             "checked": "last timed step, every element"})
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None, help="workload name (default: lm-130m-layer)")
+    ap.add_argument("--copies", type=int, default=3, help="input copies rotated across steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="after the timed region, run torch copies of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+              "the operator's (sequence, head) chains shard across GPUs without communication, "
+              "so the per-GPU figure is the one reported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_delta_rule_prologue_amd import binding
+    from gated_delta_rule_prologue_amd.configs import BENCH_WORKLOAD, BY_NAME
+    from gated_delta_rule_prologue_amd.inputs import make_inputs
+
+    torch.cuda.set_device(0)
+    binding.lib()
+    w = BY_NAME[args.workload or BENCH_WORKLOAD]
+    inp = make_inputs(w)
+    esize = 2 if w.dtype == "bf16" else 4
+    n_seqs, T = inp.n_seqs, inp.total_tokens
+
+    base = binding.to_device(inp)
+    copies = [base] + [{k: (v.clone() if v is not None else None) for k, v in base.items()}
+                       for _ in range(max(1, args.copies) - 1)]
+    for c in copies:
+        c["kw"] = torch.empty_like(c["k"])
+        c["o"] = torch.empty_like(c["v"])
+        c["S"] = torch.empty((n_seqs, w.heads, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def launch(c):
+        binding.prologue(c["k"], c["u"], c["a"], c["h"], c["b"], c["conv_w"], c["cu_seqlens"],
+                         w.L, kw=c["kw"], stream=stream)
+        binding.scan(c["q"], c["k"], c["kw"], c["v"], c["g"], c["b"], c["cu_seqlens"],
+                     o=c["o"], S_final=c["S"], stream=stream)
+
+    for i in range(args.warmup):
+        launch(copies[i % len(copies)])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        c = copies[i % len(copies)]
+        ev[i][0].record(stream)
+        binding.prologue(c["k"], c["u"], c["a"], c["h"], c["b"], c["conv_w"], c["cu_seqlens"],
+                         w.L, kw=c["kw"], stream=stream)
+        ev[i][1].record(stream)
+        binding.scan(c["q"], c["k"], c["kw"], c["v"], c["g"], c["b"], c["cu_seqlens"],
+                     o=c["o"], S_final=c["S"], stream=stream)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    last = copies[(K - 1) % len(copies)]
+
+    pro_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    scan_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    work = algorithmic_work(w, n_seqs, T, esize)
+
+    def hbm(kernel, nbytes, ms):
+        a = nbytes / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": a / HBM_PEAK_GBS, "traffic": measured_traffic(kernel, w.name),
+                "kernel": kernel, "avg_launch_us": ms * 1e3, "algorithmic_bytes": nbytes}
+
+    pro = hbm("prologue", work["prologue_bytes"], pro_ms)
+    scn = hbm("scan", work["scan_bytes"], scan_ms)
+    scn["mfma_tflops"] = work["scan_flops"] / (scan_ms * 1e-3) / 1e12
+    scn["mfma_frac"] = scn["mfma_tflops"] / (BF16_PEAK_TFLOPS if esize == 2 else FP32_MFMA_PEAK_TFLOPS)
+    scn["algorithmic_flops"] = work["scan_flops"]
+    dominant = scn if scan_ms >= pro_ms else pro
+
+    if args.calibrate_copy_mib:
+        nb = args.calibrate_copy_mib << 20
+        src = torch.empty(nb // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    out = {
+        "metric": METRIC,
+        "value": K * T / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / K * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded; shapes and distributions of the workload, inputs resident in HBM)",
+        "config": {"workload": w.name, "n_seqs": n_seqs, "seq_len": T // n_seqs, "heads": w.heads,
+                   "dk": w.dk, "dv": w.dv, "L": w.L, "tokens_per_step": T,
+                   "head_tokens_per_step": work["head_tokens"], "input_copies": len(copies)},
+        "head_tokens_per_s": K * work["head_tokens"] / elapsed,
+        "roofline": {k: dominant[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
+        "kernels": {"prologue": pro, "scan": scn,
+                    "pipeline_frac_hbm": (work["prologue_bytes"] + work["scan_bytes"]) / HBM_PEAK_GBS
+                    / 1e9 / ((pro_ms + scan_ms) * 1e-3)},
+    }
+    out["roofline"]["kernel"] = dominant["kernel"]
+    if not args.no_cpu_baseline:
+        cb, parity = cpu_baseline(inp, last["o"], last["S"])
+        out["cpu_baseline"] = cb
+        out["parity"] = parity
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

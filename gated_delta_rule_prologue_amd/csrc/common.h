@@ -15,14 +15,21 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t x)
     return __uint_as_float(((uint32_t)x) << 16);
 }
 
-// fp32 -> bf16, round to nearest, ties to even; NaN stays NaN.
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// fp32 -> bf16, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Two fp32 -> packed bf16 pair (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    bf16x2_t h;
+    h[0] = (__bf16)lo;
+    h[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, h);
 }
 
 // Element conversions for the two input storage types.
@@ -49,11 +56,8 @@ template <> struct Vec16<uint16_t> {
     }
     __device__ static void store(uint16_t* p, const float* in)
     {
-        uint32_t w[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            w[i] = (uint32_t)f32_to_bf16(in[2 * i]) | ((uint32_t)f32_to_bf16(in[2 * i + 1]) << 16);
-        *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+        *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(in[0], in[1]), pack_bf16x2(in[2], in[3]),
+                                                  pack_bf16x2(in[4], in[5]), pack_bf16x2(in[6], in[7]));
     }
 };
 template <> struct Vec16<float> {
