@@ -11,12 +11,14 @@
 // section 2.2 (anchor, then refinement levels l = 1..L, r^(1) = anchor).
 //
 // Design (HBM-bound streaming, ~0.5 flop/byte):
-//   * one thread owns 16 bytes of channels (8 bf16 / 4 fp32) of one head and
-//     walks a strip of consecutive tokens, so the 3-token conv halo lives in
-//     registers and every k element is read from HBM once (plus a 3-token
-//     halo per strip);
-//   * consecutive threads own consecutive 16-byte channel groups, so every
-//     wavefront load instruction covers whole 256-byte rows of k, u, a, h;
+//   * one thread owns 16 (or 8) bytes of channels of one head and walks a
+//     strip of consecutive tokens, so the 3-token conv halo lives in registers
+//     and every k element is read from HBM once (plus a 3-token halo per
+//     strip);
+//   * consecutive threads own consecutive channel groups, so every wavefront
+//     load instruction covers whole 256-byte rows of k, u, a, h;
+//   * k, u, a, h are streamed with nontemporal loads (read exactly once);
+//     the write keys are stored normally because the scan reads them next;
 //   * L is a template parameter: the level loop unrolls completely and h's
 //     last slot (never read by the closed form) is never loaded;
 //   * sequence boundaries come from cu_seqlens on the device (binary search
@@ -26,15 +28,75 @@
 
 namespace prism {
 
-template <typename T, int L>
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
+// Raw 8- or 16-byte loads; the streaming form carries the nontemporal hint
+// (inputs read exactly once should not displace cached lines).
+template <int B, bool NT> struct Raw;
+template <bool NT> struct Raw<16, NT> {
+    using V = u32x4_t;
+    __device__ static V ld(const void* p)
+    {
+        const V* q = reinterpret_cast<const V*>(p);
+        if constexpr (NT) return __builtin_nontemporal_load(q);
+        else return *q;
+    }
+};
+template <bool NT> struct Raw<8, NT> {
+    using V = u32x2_t;
+    __device__ static V ld(const void* p)
+    {
+        const V* q = reinterpret_cast<const V*>(p);
+        if constexpr (NT) return __builtin_nontemporal_load(q);
+        else return *q;
+    }
+};
+
+// N elements of T (8 or 16 bytes) <-> fp32.
+template <typename T, int N> struct Lane {
+    static constexpr int B = N * (int)sizeof(T);
+    template <bool NT = false>
+    __device__ static void load(const T* p, float* out)
+    {
+        auto v = Raw<B, NT>::ld(p);
+        constexpr int W = B / 4;
+#pragma unroll
+        for (int i = 0; i < W; ++i) {
+            if constexpr (sizeof(T) == 2) {
+                out[2 * i] = __uint_as_float(v[i] << 16);
+                out[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+            } else {
+                out[i] = __uint_as_float(v[i]);
+            }
+        }
+    }
+    __device__ static void store(T* p, const float* in)
+    {
+        if constexpr (sizeof(T) == 2) {
+            if constexpr (N == 8)
+                *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(in[0], in[1]), pack_bf16x2(in[2], in[3]),
+                                                          pack_bf16x2(in[4], in[5]), pack_bf16x2(in[6], in[7]));
+            else
+                *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(in[0], in[1]), pack_bf16x2(in[2], in[3]));
+        } else {
+            if constexpr (N == 4)
+                *reinterpret_cast<float4*>(p) = make_float4(in[0], in[1], in[2], in[3]);
+            else
+                *reinterpret_cast<float2*>(p) = make_float2(in[0], in[1]);
+        }
+    }
+};
+
+template <typename T, int L, int V>
 __global__ __launch_bounds__(256) void prologue_kernel(
     const T* __restrict__ k, const T* __restrict__ u, const T* __restrict__ a,
     const T* __restrict__ h, const T* __restrict__ b, const T* __restrict__ conv_w,
     const int32_t* __restrict__ cu, int n_seqs, int T_total, int H, int dk,
     int strip, T* __restrict__ kw)
 {
-    constexpr int V = Vec16<T>::N;
-    const int groups = H * dk / V;                       // 16-byte groups per token row
+    using LV = Lane<T, V>;
+    const int groups = H * dk / V;                       // channel groups per token row
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int cg = (int)(gid % groups);
     const int64_t t0_64 = (gid / groups) * strip;
@@ -74,9 +136,9 @@ __global__ __launch_bounds__(256) void prologue_kernel(
     float x1[V], x2[V], x3[V];
 #pragma unroll
     for (int c = 0; c < V; ++c) { x1[c] = 0.f; x2[c] = 0.f; x3[c] = 0.f; }
-    if (t0 - 1 >= seq_start) Vec16<T>::load(k + (int64_t)(t0 - 1) * row + koff, x1);
-    if (t0 - 2 >= seq_start) Vec16<T>::load(k + (int64_t)(t0 - 2) * row + koff, x2);
-    if (t0 - 3 >= seq_start) Vec16<T>::load(k + (int64_t)(t0 - 3) * row + koff, x3);
+    if (t0 - 1 >= seq_start) LV::load(k + (int64_t)(t0 - 1) * row + koff, x1);
+    if (t0 - 2 >= seq_start) LV::load(k + (int64_t)(t0 - 2) * row + koff, x2);
+    if (t0 - 3 >= seq_start) LV::load(k + (int64_t)(t0 - 3) * row + koff, x3);
 
     for (int t = t0; t < t1; ++t) {
         if (t == next_start) {                           // a new sequence starts at t
@@ -86,7 +148,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(
             for (int c = 0; c < V; ++c) { x1[c] = 0.f; x2[c] = 0.f; x3[c] = 0.f; }
         }
         float kt[V];
-        Vec16<T>::load(k + (int64_t)t * row + koff, kt);
+        LV::template load<true>(k + (int64_t)t * row + koff, kt);
         const float bt = to_f32(b[(int64_t)t * H + e]);
         float acc[V], r[V];
 #pragma unroll
@@ -100,40 +162,50 @@ __global__ __launch_bounds__(256) void prologue_kernel(
 #pragma unroll
         for (int s = 0; s < L - 1; ++s) {                // level l = s + 1
             float av[V], uv[V];
-            Vec16<T>::load(ab + s * dk, av);
-            Vec16<T>::load(ub + s * dk, uv);
+            LV::template load<true>(ab + s * dk, av);
+            LV::template load<true>(ub + s * dk, uv);
 #pragma unroll
             for (int c = 0; c < V; ++c)
                 acc[c] += av[c] * r[c] * uv[c];
             if (s < L - 2) {                             // residual for the next level
                 float hv[V];
-                Vec16<T>::load(hb + s * dk, hv);
+                LV::template load<true>(hb + s * dk, hv);
 #pragma unroll
                 for (int c = 0; c < V; ++c)
                     r[c] *= 1.f - av[c] * hv[c];
             }
         }
-        Vec16<T>::store(kw + (int64_t)t * row + koff, acc);
+        LV::store(kw + (int64_t)t * row + koff, acc);
 #pragma unroll
         for (int c = 0; c < V; ++c) { x3[c] = x2[c]; x2[c] = x1[c]; x1[c] = kt[c]; }
     }
 }
 
-template <typename T, int L>
-static hipError_t launch_L(const PrologueArgs& p, hipStream_t stream)
+template <typename T, int L, int V>
+static hipError_t launch_LV(const PrologueArgs& p, hipStream_t stream)
 {
-    constexpr int V = Vec16<T>::N;
     const int64_t groups = (int64_t)p.heads * p.dk / V;
     const int64_t strips = (p.total_tokens + p.strip - 1) / p.strip;
     const int64_t threads = groups * strips;
     if (threads == 0)
         return hipSuccess;
     const int64_t blocks = (threads + 255) / 256;
-    hipLaunchKernelGGL((prologue_kernel<T, L>), dim3((unsigned)blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((prologue_kernel<T, L, V>), dim3((unsigned)blocks), dim3(256), 0, stream,
                        (const T*)p.k, (const T*)p.u, (const T*)p.a, (const T*)p.h, (const T*)p.b,
                        (const T*)p.conv_w, p.cu_seqlens, p.n_seqs, p.total_tokens, p.heads, p.dk,
                        p.strip, (T*)p.kw);
     return hipGetLastError();
+}
+
+// Channels per thread: 16-byte or 8-byte accesses (the narrow form halves the
+// registers a thread holds, which doubles the wavefronts in flight).
+template <typename T, int L>
+static hipError_t launch_L(const PrologueArgs& p, hipStream_t stream)
+{
+    constexpr int wide = 16 / (int)sizeof(T), narrow = 8 / (int)sizeof(T);
+    if (p.narrow)
+        return launch_LV<T, L, narrow>(p, stream);
+    return launch_LV<T, L, wide>(p, stream);
 }
 
 template <typename T>
