@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libprism.so")
-SOURCES = ["prism_api.hip", "prologue.hip", "chunk_scan.hip"]
+SOURCES = ["prism_api.hip", "prologue.hip", "chunk_scan.hip", "chunk_scan_bf16.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

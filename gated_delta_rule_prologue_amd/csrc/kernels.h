@@ -28,8 +28,13 @@ struct ScanArgs {
 
 hipError_t launch_prologue(const PrologueArgs& p, hipStream_t stream);
 
+// Generic chunk scan (fp32 and bf16 operands), LDS-staged intermediates.
 // Returns hipErrorInvalidValue when (dtype, dk, dv_slice) has no kernel.
 hipError_t launch_scan(const ScanArgs& p, hipStream_t stream);
 bool scan_supported(bool bf16, int dk, int dv, int dv_slice);
+
+// bf16 chunk scan with the register-resident state path.
+hipError_t launch_scan_bf16(const ScanArgs& p, hipStream_t stream);
+bool scan_bf16_supported(int dk, int dv, int dv_slice);
 
 }  // namespace prism

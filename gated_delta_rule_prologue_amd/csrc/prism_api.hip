@@ -37,19 +37,34 @@ int env_int(const char* name, int fallback)
     return (end && *end == 0 && v > 0 && v < (1 << 20)) ? (int)v : fallback;
 }
 
+// Which scan kernel runs: the register-resident bf16 kernel unless the
+// generic one is requested (PRISM_SCAN_GENERIC=1) or the shape needs it.
+bool use_bf16_kernel(const prism_dims* d, int dvs)
+{
+    return d->dtype == PRISM_BF16 && env_int("PRISM_SCAN_GENERIC", 0) == 0 &&
+           prism::scan_bf16_supported(d->dk, d->dv, dvs);
+}
+
+bool slice_supported(const prism_dims* d, int dvs)
+{
+    const bool bf16 = d->dtype == PRISM_BF16;
+    if (bf16 && env_int("PRISM_SCAN_GENERIC", 0) == 0)
+        return prism::scan_bf16_supported(d->dk, d->dv, dvs);
+    return prism::scan_supported(bf16, d->dk, d->dv, dvs);
+}
+
 // Value columns per scan workgroup: split the dv columns of each chain until
 // there are enough workgroups for the 256 CUs (columns of S are independent).
 int pick_dv_slice(const prism_dims* d)
 {
-    const bool bf16 = d->dtype == PRISM_BF16;
     const int forced = env_int("PRISM_DV_SLICE", 0);
-    if (forced && prism::scan_supported(bf16, d->dk, d->dv, forced))
+    if (forced && slice_supported(d, forced))
         return forced;
     const long chains = (long)d->n_seqs * d->heads;
     const int cands[3] = {64, 32, 16};
     int best = 0;
     for (int c : cands) {
-        if (!prism::scan_supported(bf16, d->dk, d->dv, c))
+        if (!slice_supported(d, c))
             continue;
         best = c;                                   // smallest supported so far
         if (chains * (d->dv / c) >= 192)
@@ -60,9 +75,8 @@ int pick_dv_slice(const prism_dims* d)
 
 prism_status check_scan_shape(const prism_dims* d)
 {
-    const bool bf16 = d->dtype == PRISM_BF16;
     for (int c : {64, 32, 16})
-        if (prism::scan_supported(bf16, d->dk, d->dv, c))
+        if (slice_supported(d, c))
             return PRISM_OK;
     return PRISM_EUNSUPPORTED;
 }
@@ -148,6 +162,8 @@ prism_status prism_scan(const prism_dims* d, const void* q, const void* k, const
     p.cu_seqlens = cu_seqlens;
     p.o = o;
     p.s_final = S_final;
+    if (use_bf16_kernel(d, p.dv_slice))
+        return from_hip(prism::launch_scan_bf16(p, (hipStream_t)stream));
     return from_hip(prism::launch_scan(p, (hipStream_t)stream));
 }
 

@@ -96,10 +96,15 @@ def test_fwd_matches_oracle(w):
     assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]
 
 
+@pytest.mark.parametrize("generic", [0, 1], ids=["bf16-kernel", "generic-kernel"])
 @pytest.mark.parametrize("dvs", [16, 32, 64])
 @pytest.mark.parametrize("dk", [64, 128])
-def test_every_value_slice_width(dk, dvs, monkeypatch):
+def test_every_value_slice_width(dk, dvs, generic, monkeypatch):
+    """Both bf16 scan kernels (register-resident and generic), every slice width."""
+    if generic and dk == 128 and dvs == 64:
+        pytest.skip("the generic kernel has no dk=128 variant with 64 value columns")
     monkeypatch.setenv("PRISM_DV_SLICE", str(dvs))
+    monkeypatch.setenv("PRISM_SCAN_GENERIC", str(generic))
     inp = make_inputs(W(dtype="bf16", dk=dk, dv=64, L=3, lengths=(140, 3)))
     o, s = gpu_fwd(inp)
     o_ref, s_ref = oracle.fwd(inp)
@@ -141,6 +146,16 @@ def test_all_sequences_empty():
                        dev["h"], dev["conv_w"], dev["cu_seqlens"], inp.L, S_final=s)
     torch.cuda.synchronize()
     assert o.numel() == 0 and not s.any()
+
+
+@pytest.mark.parametrize("w", [FWD_CASES[3], FWD_CASES[4], FWD_CASES[8]],
+                         ids=["dk64-varlen", "dk128", "strong-decay"])
+def test_generic_bf16_kernel(w, monkeypatch):
+    monkeypatch.setenv("PRISM_SCAN_GENERIC", "1")
+    inp = make_inputs(w)
+    o, s = gpu_fwd(inp)
+    o_ref, s_ref = oracle.fwd(inp)
+    assert max_rel(o, o_ref) <= TOL["bf16"] and max_rel(s, s_ref) <= TOL["bf16"]
 
 
 def test_deterministic():
