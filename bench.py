@@ -31,9 +31,13 @@ METRIC = "PRISM fwd tokens/sec at 1 GPU (L=4) + % of HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
 FP32_MFMA_PEAK_TFLOPS = 157.3
+_CSRC = "gated_delta_rule_prologue_amd/csrc/"
+# Sources that determine each kernel as launched (kernel body, shared helpers,
+# dispatch): a committed counter figure is only reported while they are unchanged.
 KERNEL_SOURCES = {
-    "prologue": "gated_delta_rule_prologue_amd/csrc/prologue.hip",
-    "scan": "gated_delta_rule_prologue_amd/csrc/chunk_scan.hip",
+    "prologue": [_CSRC + f for f in ("prologue.hip", "common.h", "kernels.h", "prism_api.hip")],
+    "scan": [_CSRC + f for f in ("chunk_scan_bf16.hip", "chunk_scan.hip", "common.h", "kernels.h",
+                                  "prism_api.hip")],
 }
 
 
@@ -57,9 +61,12 @@ def algorithmic_work(w, n_seqs, T, esize):
             "head_tokens": ht}
 
 
-def source_sha(path):
-    with open(os.path.join(ROOT, path), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(kernel, workload):
