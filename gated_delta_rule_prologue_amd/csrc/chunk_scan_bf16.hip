@@ -1,35 +1,35 @@
-// chunk_scan_bf16.hip -- bf16 chunkwise scan with a register-resident state path
+// chunk_scan_bf16.hip -- bf16 chunkwise scans with a register-resident state path
 //
 // Same recurrence and chunk algebra as chunk_scan.hip (gated delta rule,
 // chunks of 64 tokens, WY/UT form; PRISM pages: WeChat ICML 2026 summary,
 // section 消除 Token 间串行; gist.science summary of arXiv 2602.10796,
-// section 2.1).  This variant evaluates the UT system blockwise:
+// section 2.1).  The UT system is evaluated blockwise:
 //
 //   (I + A_kk) X = R,  A_kk strictly lower, split into 16x16 blocks A_ij:
 //   X_i = T_ii (R_i - sum_{j<i} A_ij X_j),   T_ii = (I + A_ii)^-1,
 //
-// so only the four 16x16 diagonal inverses are formed (one per wavefront,
-// by substitution in fp32) and the off-diagonal coupling is applied on the
-// state path itself.
+// so only the four 16x16 diagonal inverses are formed (by substitution in
+// fp32) and the off-diagonal coupling is applied on the state path itself.
 //
-// Per chunk there are three barriers:
-//   1. stage q, k, kw, v (prefetched into registers during the previous
-//      chunk) and the gates into LDS;
-//   2. Gram blocks with masks and decays (every wavefront takes its diagonal
-//      (t, s) block pair and one or two off-diagonal pairs), then each
-//      wavefront inverts the diagonal block it built;
-//   3. the state path.  Wavefront jb owns 16 value columns of S (fp32, in
-//      MFMA accumulators) and carries them through
-//        S <- gamma_C S + KW^T diag(gamma_C/gamma) V
-//        R  = diag(b gamma) K S0 + A_kkw V
-//        X  = blockwise UT solve (above)
-//        O  = diag(gamma) Q S0 + A_qkw V - A_qk X
-//        S <- S - K^T diag(gamma_C/gamma) X
-//      entirely in registers: products whose right operand is an
-//      intermediate (X, R - A X) use v_mfma_f32_16x16x16_bf16, whose B
-//      operand layout is exactly the accumulator layout of a 16x16 tile, so
-//      no intermediate is written to LDS.  S0^T for the next chunk's K S0 and
-//      Q S0 products goes to LDS rows private to the wavefront.
+// The state path: wavefront jb owns 16 value columns of S (fp32, in MFMA
+// accumulators) and carries them through
+//   S <- gamma_C S + KW^T diag(gamma_C/gamma) V
+//   R  = diag(b gamma) K S0 + A_kkw V
+//   X  = blockwise UT solve (above)
+//   O  = diag(gamma) Q S0 + A_qkw V - A_qk X
+//   S <- S - K^T diag(gamma_C/gamma) X
+// entirely in registers: products with an intermediate operand (S0, X,
+// R - A X) use v_mfma_f32_16x16x16_bf16, whose B operand layout (and, read
+// transposed, whose A operand layout) is exactly the accumulator layout of a
+// 16x16 tile, so no intermediate goes through LDS.
+//
+// Two kernels:
+//   scan_kernel     every wavefront stages rows, builds Gram blocks and
+//                   inverses, then the state wavefronts run the state path
+//                   (three barriers per chunk); any value slice up to 64.
+//   scan_ws_kernel  wavefront-specialised (slices of 16 or 32 columns):
+//                   helper wavefronts prepare chunk c + 1 while the state
+//                   wavefronts run chunk c (two barriers per chunk).
 #include "common.h"
 #include "kernels.h"
 
@@ -88,21 +88,14 @@ __device__ __forceinline__ float wave_inclusive_sum(float v)
     return v;
 }
 
-// Scale the eight k-entries of a 16x16x32 fragment (k = 8 (lane / 16) + e)
-// by f[k]: used to fold diag(gamma_C / gamma) into the V operand.
-__device__ __forceinline__ bf16x8_t scale_k(bf16x8_t x, const float* f, int lane)
+// Two 16x16x16 operand fragments side by side as one 16x16x32 fragment: the
+// contraction index of the wider product runs over both halves (k slots
+// 8 g + 0..3 from lo, 8 g + 4..7 from hi).  Pairing A and B fragments the
+// same way makes a 16x16x32 product equal to the sum of the two 16x16x16
+// products, at the 16x16x32 rate.
+__device__ __forceinline__ bf16x8_t cat8(v4s_t lo, v4s_t hi)
 {
-    const float4 f0 = *reinterpret_cast<const float4*>(f + (lane >> 4) * 8);
-    const float4 f1 = *reinterpret_cast<const float4*>(f + (lane >> 4) * 8 + 4);
-    const uint4 w = __builtin_bit_cast(uint4, x);
-    const float fv[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-    const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
-    uint32_t r[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        r[i] = pack_bf16x2(__uint_as_float(wv[i] << 16) * fv[2 * i],
-                           __uint_as_float(wv[i] & 0xffff0000u) * fv[2 * i + 1]);
-    return __builtin_bit_cast(bf16x8_t, make_uint4(r[0], r[1], r[2], r[3]));
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 __device__ __forceinline__ f32x4_t mma32(bf16x8_t a, bf16x8_t b, f32x4_t c)
@@ -128,7 +121,7 @@ __device__ __forceinline__ void st4(uint16_t* p, f32x4_t x)
 
 template <int D, int DVS>
 struct Layout {
-    static constexpr int LDD = D + 8;            // [64][D] tiles and S0^T [DVS][D]
+    static constexpr int LDD = D + 8;            // [64][D] tiles
     static constexpr int LDC = kC + 8;           // [64][64] matrices
     static constexpr int LDV = DVS + 8;          // [64][DVS] value tiles
     static constexpr int LDT = 16 + 8;           // diagonal inverse blocks [4][16][16]
@@ -136,21 +129,248 @@ struct Layout {
     static constexpr int szV = kC * LDV * 2;
     static constexpr int szM = kC * LDC * 2;
     static constexpr int szTd = kC * LDT * 2;
-    static constexpr int szS0t = DVS * LDD * 2;
     static constexpr int oQ = 0;
     static constexpr int oK = oQ + szRowD;
     static constexpr int oKW = oK + szRowD;
     static constexpr int oV = oKW + szRowD;
-    static constexpr int oAkk = oV + szV;        // four matrices, then S0^T: zeroed once
+    static constexpr int oAkk = oV + szV;        // four matrices: zeroed once
     static constexpr int oAkkw = oAkk + szM;
     static constexpr int oAqkw = oAkkw + szM;
     static constexpr int oAqk = oAqkw + szM;
-    static constexpr int oS0t = oAqk + szM;
-    static constexpr int oTd = oS0t + szS0t;
+    static constexpr int oTd = oAqk + szM;
     static constexpr int oG = oTd + szTd;
     static constexpr int total = oG + 4 * kC * 4;
-    static_assert(oAkk % 16 == 0 && oS0t % 16 == 0 && oTd % 16 == 0 && oG % 16 == 0, "alignment");
+    static_assert(oAkk % 16 == 0 && oTd % 16 == 0 && oG % 16 == 0, "alignment");
 };
+
+// Scale the eight k-entries of a 16x16x32 fragment by f0 (k = 8 (lane / 16) + 0..3)
+// and f1 (+ 4..7): folds diag(gamma_C / gamma) into a V operand.
+__device__ __forceinline__ bf16x8_t scale8(bf16x8_t x, float4 f0, float4 f1)
+{
+    const uint4 w = __builtin_bit_cast(uint4, x);
+    const float fv[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+    const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+    uint32_t r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        r[i] = pack_bf16x2(__uint_as_float(wv[i] << 16) * fv[2 * i],
+                           __uint_as_float(wv[i] & 0xffff0000u) * fv[2 * i + 1]);
+    return __builtin_bit_cast(bf16x8_t, make_uint4(r[0], r[1], r[2], r[3]));
+}
+
+// Keeps the compiler from moving instructions across this point: the state
+// path issues each batch of LDS reads one computation ahead of its use, and
+// the scheduler would otherwise sink every read next to its MFMA (one
+// wavefront per SIMD leaves nothing else to hide the LDS latency).
+#define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// The per-chunk state path of one wavefront (value columns 16 jb .. 16 jb + 15):
+//   a. S <- gamma_C S + KW^T diag(fac) V
+//   b. R = diag(b gamma) K S0 + A_kkw V;   O^T = (diag(gamma) Q S0 + A_qkw V)^T
+//   c. X_i = T_ii (R_i - sum_{j<i} A_kk{ij} X_j)
+//   d. O^T += -(A_qk X)^T (the tile holds -A_qk), stored as bf16
+//   e. S <- S - K^T diag(fac) X
+// S0, the state at the chunk start, enters b straight from the accumulators: a
+// 16x16 fp32 accumulator tile converted to bf16 is both the B operand and the
+// transposed A operand of a 16x16x16 product.  O is produced transposed, so a
+// lane holds four consecutive value columns of one token (8-byte stores).
+// All tiles are bf16 in LDS with the strides of Layout; S is fp32 in accumulators.
+// T_ii is read from sTd, or with TD_IN_AKK from the diagonal blocks of A_kk
+// (which the state path never needs otherwise).
+template <int D, int DVS, bool TD_IN_AKK = false>
+__device__ __forceinline__ void state_path(
+    f32x4_t (&S)[D / 16], const uint16_t* sQ, const uint16_t* sK, const uint16_t* sKW,
+    const uint16_t* sV, const uint16_t* sAkk, const uint16_t* sAkkw, const uint16_t* sAqkw,
+    const uint16_t* sAqk, const uint16_t* sTd, const float* sBv, const float* sGam,
+    const float* sFac, float gC, uint16_t* o, int c0, int nt, int64_t rowV, int e, int DV,
+    int j0, int jb, int lane)
+{
+    using Ly = Layout<D, DVS>;
+    constexpr int LDD = Ly::LDD, LDC = Ly::LDC, LDV = Ly::LDV, LDT = Ly::LDT;
+    constexpr int NI = D / 16;
+    const int li = lane & 15, lg = lane >> 4;
+
+    // S0 as bf16 16x16x16 operands
+    v4s_t s0b[NI];
+#pragma unroll
+    for (int ib = 0; ib < NI; ++ib)
+        s0b[ib] = as_b16(S[ib], 1.f, 1.f, 1.f, 1.f);
+
+    // ---- reads for a
+    bf16x8_t vf[2], kwf[2][NI];
+    float4 fc[4];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+        vf[h2] = frag_col(sV + h2 * 32 * LDV + jb * 16, LDV, lane);
+        fc[2 * h2] = *reinterpret_cast<const float4*>(sFac + h2 * 32 + lg * 8);
+        fc[2 * h2 + 1] = *reinterpret_cast<const float4*>(sFac + h2 * 32 + lg * 8 + 4);
+    }
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int ib = 0; ib < NI; ++ib)
+            kwf[h2][ib] = frag_col(sKW + h2 * 32 * LDD + ib * 16, LDD, lane);
+
+    // reads for b, one 16-token block tb per batch, double-buffered
+    v4s_t kf[2][NI], qf[2][NI];
+    bf16x8_t akw[2][2], aqw[2][2];
+    float4 gm[2], bb[2];
+    float go[2];
+    auto load_b = [&](int tb, int sl) {
+#pragma unroll
+        for (int kb = 0; kb < NI; ++kb) {
+            kf[sl][kb] = frag4_row(sK + tb * 16 * LDD + kb * 16, LDD, lane);
+            qf[sl][kb] = frag4_row(sQ + tb * 16 * LDD + kb * 16, LDD, lane);
+        }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            if (h2 < (tb + 2) / 2) {
+                akw[sl][h2] = frag_row(sAkkw + tb * 16 * LDC + h2 * 32, LDC, lane);
+                aqw[sl][h2] = frag_row(sAqkw + tb * 16 * LDC + h2 * 32, LDC, lane);
+            }
+        }
+        gm[sl] = *reinterpret_cast<const float4*>(sGam + tb * 16 + lg * 4);
+        bb[sl] = *reinterpret_cast<const float4*>(sBv + tb * 16 + lg * 4);
+        go[sl] = sGam[tb * 16 + li];
+    };
+    load_b(0, 0);
+    SCHED_FENCE();
+
+    // ---- a. S <- gamma_C S + KW^T diag(fac) V   (NI independent accumulators)
+    bf16x8_t vs[2];
+    vs[0] = scale8(vf[0], fc[0], fc[1]);
+    vs[1] = scale8(vf[1], fc[2], fc[3]);
+#pragma unroll
+    for (int ib = 0; ib < NI; ++ib)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            S[ib][r] *= gC;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int ib = 0; ib < NI; ++ib)
+            S[ib] = mma32(kwf[h2][ib], vs[h2], S[ib]);
+    SCHED_FENCE();
+
+    // ---- b, with the reads of c, d issued beside the third block
+    f32x4_t R[4], OT[4];
+    v4s_t akk[6], td[4], aqk[10];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+        const int sl = tb & 1;
+        if (tb + 1 < 4)
+            load_b(tb + 1, sl ^ 1);
+        if (tb == 2) {
+#pragma unroll
+            for (int i = 1, n = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < i; ++j, ++n)
+                    akk[n] = frag4_row(sAkk + i * 16 * LDC + j * 16, LDC, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                td[i] = TD_IN_AKK ? frag4_row(sAkk + i * 16 * LDC + i * 16, LDC, lane)
+                                  : frag4_row(sTd + i * 16 * LDT, LDT, lane);
+#pragma unroll
+            for (int i = 0, n = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j <= i; ++j, ++n)
+                    aqk[n] = frag4_row(sAqk + i * 16 * LDC + j * 16, LDC, lane);
+        }
+        SCHED_FENCE();
+        f32x4_t ra = {0.f, 0.f, 0.f, 0.f}, oa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kp = 0; kp < NI / 2; ++kp) {
+            const bf16x8_t s0p = cat8(s0b[2 * kp], s0b[2 * kp + 1]);
+            ra = mma32(cat8(kf[sl][2 * kp], kf[sl][2 * kp + 1]), s0p, ra);   // (K S0)[t][j]
+            oa = mma32(s0p, cat8(qf[sl][2 * kp], qf[sl][2 * kp + 1]), oa);   // (Q S0)^T[j][t]
+        }
+        const float gmv[4] = {gm[sl].x, gm[sl].y, gm[sl].z, gm[sl].w};
+        const float bbv[4] = {bb[sl].x, bb[sl].y, bb[sl].z, bb[sl].w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            ra[r] *= bbv[r] * gmv[r];
+            oa[r] *= go[sl];
+        }
+#pragma unroll
+        for (int h2 = 0; h2 < (tb + 2) / 2; ++h2) {
+            ra = mma32(akw[sl][h2], vf[h2], ra);
+            oa = mma32(vf[h2], aqw[sl][h2], oa);          // (A_qkw V)^T
+        }
+        R[tb] = ra;
+        OT[tb] = oa;
+        SCHED_FENCE();
+    }
+
+    // reads for e (first two blocks) and its scales
+    v4s_t ke[4][NI];
+    float4 fe[4];
+    auto load_e = [&](int tb) {
+#pragma unroll
+        for (int ib = 0; ib < NI; ++ib)
+            ke[tb][ib] = frag4_col(sK + tb * 16 * LDD + ib * 16, LDD, lane);
+        fe[tb] = *reinterpret_cast<const float4*>(sFac + tb * 16 + lg * 4);
+    };
+    load_e(0);
+    load_e(1);
+    SCHED_FENCE();
+
+    // ---- c. X_i = T_ii (R_i - sum_{j<i} A_ij X_j)   (16x16x16, B operands from registers)
+    f32x4_t X[4];
+    v4s_t nX[4];                         // -X_j as bf16 B operands
+#pragma unroll
+    for (int i = 0, n = 0; i < 4; ++i) {
+        f32x4_t y = R[i];
+#pragma unroll
+        for (int j = 0; j < i; ++j, ++n)
+            y = mma16(akk[n], nX[j], y);
+        f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+        x = mma16(td[i], as_b16(y, 1.f, 1.f, 1.f, 1.f), x);
+        X[i] = x;
+        nX[i] = as_b16(x, -1.f, -1.f, -1.f, -1.f);
+    }
+    SCHED_FENCE();
+    load_e(2);
+    load_e(3);
+    SCHED_FENCE();
+
+    // ---- d. O^T += X^T (-A_qk)^T; token rows past the chunk's last token fall
+    //      outside the buffer range and are dropped by the hardware
+    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+        o + (int64_t)c0 * rowV, 0, nt * (int)rowV * 2, 0x00020000);
+    v4s_t xb[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb)
+        xb[sb] = as_b16(X[sb], 1.f, 1.f, 1.f, 1.f);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+        const int n = tb * (tb + 1) / 2;             // aqk[n + sb] is block (tb, sb)
+        f32x4_t oa = OT[tb];
+#pragma unroll
+        for (int sb = 0; sb <= tb; sb += 2) {
+            if (sb + 1 <= tb)
+                oa = mma32(cat8(xb[sb], xb[sb + 1]), cat8(aqk[n + sb], aqk[n + sb + 1]), oa);
+            else
+                oa = mma16(xb[sb], aqk[n + sb], oa);
+        }
+        // lane (li, lg): token tb * 16 + li, value columns 4 lg .. 4 lg + 3 of block jb
+        const int t = tb * 16 + li;
+        typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+        const u32x2_t w = {pack_bf16x2(oa[0], oa[1]), pack_bf16x2(oa[2], oa[3])};
+        __builtin_amdgcn_raw_buffer_store_b64(w, orsrc, (t * (int)rowV + e * DV + j0 + jb * 16 + lg * 4) * 2,
+                                              0, 0);
+    }
+
+    // ---- e. S <- S - K^T diag(fac) X   (NI independent accumulators per block)
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp) {
+        const bf16x8_t bx = cat8(as_b16(X[2 * tp], -fe[2 * tp].x, -fe[2 * tp].y, -fe[2 * tp].z, -fe[2 * tp].w),
+                                 as_b16(X[2 * tp + 1], -fe[2 * tp + 1].x, -fe[2 * tp + 1].y,
+                                        -fe[2 * tp + 1].z, -fe[2 * tp + 1].w));
+#pragma unroll
+        for (int ib = 0; ib < NI; ++ib)
+            S[ib] = mma32(cat8(ke[2 * tp][ib], ke[2 * tp + 1][ib]), bx, S[ib]);
+    }
+}
 
 // Off-diagonal (t-block, s-block) pairs; wavefront w takes kOff[w] and kOff[w + 4].
 __constant__ const int kOffT[6] = {1, 2, 2, 3, 3, 3};
@@ -183,7 +403,6 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(
     uint16_t* sAkkw = reinterpret_cast<uint16_t*>(smem + Ly::oAkkw);
     uint16_t* sAqkw = reinterpret_cast<uint16_t*>(smem + Ly::oAqkw);
     uint16_t* sAqk = reinterpret_cast<uint16_t*>(smem + Ly::oAqk);   // holds -A_qk
-    uint16_t* sS0t = reinterpret_cast<uint16_t*>(smem + Ly::oS0t);
     uint16_t* sTd = reinterpret_cast<uint16_t*>(smem + Ly::oTd);
     float* sLam = reinterpret_cast<float*>(smem + Ly::oG);
     float* sBv = sLam + kC;
@@ -203,7 +422,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(
     const int64_t rowQK = (int64_t)H * D, rowV = (int64_t)H * DV;
 
     {
-        constexpr int nz = (4 * Ly::szM + Ly::szS0t) / 16;
+        constexpr int nz = 4 * Ly::szM / 16;
         uint4* z = reinterpret_cast<uint4*>(smem + Ly::oAkk);
         for (int i = tid; i < nz; i += kThreads)
             z[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -261,7 +480,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(
     };
     if (nchunks > 0)
         prefetch(0);
-    __syncthreads();
+    lds_barrier();
 
     for (int ch = 0; ch < nchunks; ++ch) {
         const int c0 = seq0 + ch * kC;
@@ -293,7 +512,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(
         }
         if (ch + 1 < nchunks)
             prefetch(ch + 1);
-        __syncthreads();
+        lds_barrier();
 
         // ================= 2. Gram blocks, masks; diagonal inverse of block `wave` =================
 #pragma unroll
@@ -370,112 +589,14 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(
                 if ((r >> 2) == lg)
                     Td[r * LDT] = f32_to_bf16(x[r]);
         }
-        __syncthreads();
+        lds_barrier();
 
         // ================= 3. state path: wavefront jb, value columns 16 jb .. 16 jb + 15 =================
-        if (wave < NJ) {
-            const int jb = wave;
-            const float gC = __builtin_amdgcn_exp2f(lamC);
-            const uint16_t* s0t = sS0t + jb * 16 * LDD;
-
-            // a. S <- gamma_C S + KW^T diag(fac) V
-            bf16x8_t vf[2], vs[2];
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                vf[h2] = frag_col(sV + h2 * 32 * LDV + jb * 16, LDV, lane);
-                vs[h2] = scale_k(vf[h2], sFac + h2 * 32, lane);
-            }
-#pragma unroll
-            for (int ib = 0; ib < NI; ++ib) {
-                f32x4_t acc = S[ib];
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[r] *= gC;
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2)
-                    acc = mma32(frag_col(sKW + h2 * 32 * LDD + ib * 16, LDD, lane), vs[h2], acc);
-                S[ib] = acc;
-            }
-
-            // b. R_tb = diag(b gamma) (K S0)_tb + A_kkw V ;  O partial = diag(gamma) (Q S0)_tb + A_qkw V
-            bf16x8_t sf[D / 32];
-#pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk)
-                sf[kk] = frag_row(s0t + kk * 32, LDD, lane);
-            f32x4_t R[4], O[4];
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                f32x4_t ra = {0.f, 0.f, 0.f, 0.f}, oa = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < D / 32; ++kk) {
-                    ra = mma32(frag_row(sK + tb * 16 * LDD + kk * 32, LDD, lane), sf[kk], ra);
-                    oa = mma32(frag_row(sQ + tb * 16 * LDD + kk * 32, LDD, lane), sf[kk], oa);
-                }
-                const float4 gm = *reinterpret_cast<const float4*>(sGam + tb * 16 + lg * 4);
-                const float4 bb = *reinterpret_cast<const float4*>(sBv + tb * 16 + lg * 4);
-                const float gmv[4] = {gm.x, gm.y, gm.z, gm.w}, bbv[4] = {bb.x, bb.y, bb.z, bb.w};
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    ra[r] *= bbv[r] * gmv[r];
-                    oa[r] *= gmv[r];
-                }
-#pragma unroll
-                for (int h2 = 0; h2 < (tb + 2) / 2; ++h2) {
-                    ra = mma32(frag_row(sAkkw + tb * 16 * LDC + h2 * 32, LDC, lane), vf[h2], ra);
-                    oa = mma32(frag_row(sAqkw + tb * 16 * LDC + h2 * 32, LDC, lane), vf[h2], oa);
-                }
-                R[tb] = ra;
-                O[tb] = oa;
-            }
-
-            // c. X_i = T_ii (R_i - sum_{j<i} A_ij X_j)   (16x16x16, B operands from registers)
-            f32x4_t X[4];
-            v4s_t nX[4];                         // -X_j as bf16 B operands
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                f32x4_t y = R[i];
-#pragma unroll
-                for (int j = 0; j < i; ++j)
-                    y = mma16(frag4_row(sAkk + i * 16 * LDC + j * 16, LDC, lane), nX[j], y);
-                f32x4_t x = {0.f, 0.f, 0.f, 0.f};
-                x = mma16(frag4_row(sTd + i * 16 * LDT, LDT, lane), as_b16(y, 1.f, 1.f, 1.f, 1.f), x);
-                X[i] = x;
-                nX[i] = as_b16(x, -1.f, -1.f, -1.f, -1.f);
-            }
-
-            // d. O_tb += -A_qk X  (sAqk holds -A_qk); rows past the chunk's last
-            //    token fall outside the buffer range and are dropped by the hardware
-            const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-                o + (int64_t)c0 * rowV, 0, nt * (int)rowV * 2, 0x00020000);
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                f32x4_t oa = O[tb];
-#pragma unroll
-                for (int sb = 0; sb <= tb; ++sb)
-                    oa = mma16(frag4_row(sAqk + tb * 16 * LDC + sb * 16, LDC, lane),
-                               as_b16(X[sb], 1.f, 1.f, 1.f, 1.f), oa);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = tb * 16 + lg * 4 + r;
-                    __builtin_amdgcn_raw_buffer_store_b16(
-                        f32_to_bf16(oa[r]), orsrc, (t * (int)rowV + e * DV + j0 + jb * 16 + li) * 2, 0, 0);
-                }
-            }
-
-            // e. S <- S - K^T diag(fac) X ;  f. S0^T for the next chunk (rows private to jb)
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                const float4 fv = *reinterpret_cast<const float4*>(sFac + tb * 16 + lg * 4);
-                const v4s_t bx = as_b16(X[tb], -fv.x, -fv.y, -fv.z, -fv.w);
-#pragma unroll
-                for (int ib = 0; ib < NI; ++ib)
-                    S[ib] = mma16(frag4_col(sK + tb * 16 * LDD + ib * 16, LDD, lane), bx, S[ib]);
-            }
-#pragma unroll
-            for (int ib = 0; ib < NI; ++ib)
-                st4(sS0t + (jb * 16 + li) * LDD + ib * 16 + lg * 4, S[ib]);
-        }
-        __syncthreads();
+        if (wave < NJ)
+            state_path<D, DVS>(S, sQ, sK, sKW, sV, sAkk, sAkkw, sAqkw, sAqk, sTd, sBv, sGam,
+                               sFac, __builtin_amdgcn_exp2f(lamC), o, c0, nt, rowV, e, DV, j0, wave,
+                               lane);
+        lds_barrier();
     }
 
     if (wave < NJ) {
@@ -489,6 +610,497 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(
             }
         }
     }
+}
+
+
+// ---------------------------------------------------------------------------
+// Wavefront-specialised variant (value slices of 16 or 32 columns).
+//
+// NJ = DVS / 16 state wavefronts run the state path of chunk c while the
+// other NH = 4 - NJ helper wavefronts prepare chunk c + 1.  The q, k, kw, v
+// rows are double-buffered in LDS; the chunk matrices are single-buffered and
+// carried in helper registers until the state path has finished with them.
+// Per chunk:
+//   phase A: state path of chunk c (rows buffer c % 2, matrices of c)
+//            helpers: start loading the rows of chunk c + 2 (registers);
+//            Gram blocks, masks and diagonal inverses of chunk c + 1 from the
+//            rows buffer (c + 1) % 2, into registers
+//   barrier
+//   phase B: helpers write the matrices and gates of chunk c + 1, and store
+//            the rows of chunk c + 2 into buffer c % 2
+//   barrier
+// so each load has a whole state path to arrive.
+// ---------------------------------------------------------------------------
+// Workgroups are dispatched to the eight XCDs round-robin (workgroup w runs
+// on XCD w % 8), and each XCD has its own L2.  When the chains split evenly
+// over the XCDs, all value slices of a chain go to one XCD, so its q, k, kw
+// rows come from HBM once and from that L2 for the other slices.
+constexpr int kXcds = 8;
+#ifndef HWS_DIAG_BLOCKS
+#define HWS_DIAG_BLOCKS 2                        // row blocks loaded by the diagonal helper (of 4)
+#endif
+__device__ __forceinline__ void xcd_map(int n_slices, int& slice, int& chain)
+{
+    const unsigned w = blockIdx.x;
+    const unsigned n_chains = gridDim.x / (unsigned)n_slices;
+    if (n_chains % kXcds == 0) {
+        const unsigned x = w % kXcds, j = w / kXcds;
+        chain = (int)((j / (unsigned)n_slices) * kXcds + x);
+        slice = (int)(j % (unsigned)n_slices);
+    } else {
+        slice = (int)(w % (unsigned)n_slices);
+        chain = (int)(w / (unsigned)n_slices);
+    }
+}
+
+template <int D, int DVS>
+struct LayoutWS {
+    using L = Layout<D, DVS>;
+    static constexpr int szRows = 3 * L::szRowD + L::szV;   // q, k, kw, v of one chunk
+    static constexpr int oRows = 0;                          // two row buffers
+    static constexpr int oAkk = oRows + 2 * szRows;          // diagonal blocks hold T_ii
+    static constexpr int oAkkw = oAkk + L::szM;
+    static constexpr int oAqkw = oAkkw + L::szM;
+    static constexpr int oAqk = oAqkw + L::szM;              // holds -A_qk
+    static constexpr int oG = oAqk + L::szM;                 // b, gamma, gamma_C / gamma
+    static constexpr int oScr = oG + 3 * kC * 4;             // A_ii rows for the inverses
+    static constexpr int oLam = oScr + 4 * 16 * 16 * 2;      // log2 decay sums, one slot per helper
+    static constexpr int total = oLam + 3 * kC * 4;
+    static_assert(szRows % 16 == 0 && oAkk % 16 == 0 && oG % 16 == 0 && oScr % 16 == 0 &&
+                  oLam % 16 == 0, "alignment");
+};
+
+// Per-workgroup context shared by the two wavefront roles.
+struct WsCtx {
+    unsigned char* smem;
+    const uint16_t *q, *k, *kw, *v, *g, *b;
+    uint16_t* o;
+    float* s_final;
+    int n, e, H, DV, j0, seq0, seq1, nchunks, lane;
+    int64_t rowQK, rowV;
+};
+
+template <int D, int DVS>
+struct WsBuf {
+    using L = Layout<D, DVS>;
+    using Ly = LayoutWS<D, DVS>;
+    unsigned char* base;
+    __device__ unsigned char* rows(int c) const { return base + Ly::oRows + (c & 1) * Ly::szRows; }
+    __device__ uint16_t* Q(int c) const { return reinterpret_cast<uint16_t*>(rows(c)); }
+    __device__ uint16_t* K(int c) const { return reinterpret_cast<uint16_t*>(rows(c) + L::szRowD); }
+    __device__ uint16_t* KW(int c) const { return reinterpret_cast<uint16_t*>(rows(c) + 2 * L::szRowD); }
+    __device__ uint16_t* V(int c) const { return reinterpret_cast<uint16_t*>(rows(c) + 3 * L::szRowD); }
+    __device__ uint16_t* Akk() const { return reinterpret_cast<uint16_t*>(base + Ly::oAkk); }
+    __device__ uint16_t* Akkw() const { return reinterpret_cast<uint16_t*>(base + Ly::oAkkw); }
+    __device__ uint16_t* Aqkw() const { return reinterpret_cast<uint16_t*>(base + Ly::oAqkw); }
+    __device__ uint16_t* Aqk() const { return reinterpret_cast<uint16_t*>(base + Ly::oAqk); }
+    __device__ float* G() const { return reinterpret_cast<float*>(base + Ly::oG); }
+    __device__ uint16_t* Scr() const { return reinterpret_cast<uint16_t*>(base + Ly::oScr); }
+    __device__ float* Lam(int slot) const { return reinterpret_cast<float*>(base + Ly::oLam) + slot * kC; }
+};
+
+// Gram pairs (t-block, s-block) of each helper role: role 0 takes the four
+// diagonal pairs (and with them the diagonal inverses and the gates); the
+// off-diagonal pairs go to one helper (roles 1) or are split over two (2, 3).
+template <int ROLE> struct Pairs;
+template <> struct Pairs<0> {
+    static constexpr int n = 4;
+    static constexpr int t[4] = {0, 1, 2, 3}, s[4] = {0, 1, 2, 3};
+};
+template <> struct Pairs<1> {
+    static constexpr int n = 6;
+    static constexpr int t[6] = {1, 2, 2, 3, 3, 3}, s[6] = {0, 0, 1, 0, 1, 2};
+};
+template <> struct Pairs<2> {
+    static constexpr int n = 3;
+    static constexpr int t[3] = {1, 2, 2}, s[3] = {0, 0, 1};
+};
+template <> struct Pairs<3> {
+    static constexpr int n = 3;
+    static constexpr int t[3] = {3, 3, 3}, s[3] = {0, 1, 2};
+};
+
+// Unit lower-triangular 16x16 inverse, four blocks per wavefront: lane
+// (16 g + i) holds row i of the strictly lower block A_g in a[] and returns
+// column i of (I + A_g)^-1 in x[] (right-looking substitution in fp32; the
+// entry A_g[r][c] is broadcast from lane 16 g + r with a DPP row broadcast).
+template <int R>
+__device__ __forceinline__ float row_bcast(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + R, 0xF, 0xF, false));
+}
+template <int C, int R>
+__device__ __forceinline__ void subst_col(float (&x)[16], const float (&a)[16], float nxc)
+{
+    if constexpr (R < 16) {
+        x[R] = fmaf(row_bcast<R>(a[C]), nxc, x[R]);
+        subst_col<C, R + 1>(x, a, nxc);
+    }
+}
+template <int C>
+__device__ __forceinline__ void subst(float (&x)[16], const float (&a)[16])
+{
+    if constexpr (C < 15) {
+        subst_col<C, C + 1>(x, a, -x[C]);
+        subst<C + 1>(x, a);
+    }
+}
+
+// Helper wavefront: loads and stores the 16-token row blocks LB0 .. LB0 + NLB - 1
+// of q, k, kw, v, and builds the Gram pairs of its role from the rows in LDS.
+// Role 0 also inverts the diagonal blocks and publishes the gate vectors.
+template <int D, int DVS, int ROLE, int LB0, int NLB>
+__device__ __forceinline__ void helper_loop(const WsCtx& c)
+{
+    using L = Layout<D, DVS>;
+    using P = Pairs<ROLE>;
+    constexpr int LDD = L::LDD, LDC = L::LDC, LDV = L::LDV;
+    constexpr int KS = D / 32;
+    constexpr int NP = P::n;
+    constexpr bool DIAG = ROLE == 0;
+    constexpr int VL = DVS / 8;                  // 16-byte v vectors per token row
+    const WsBuf<D, DVS> m{c.smem};
+    const int lane = c.lane, li = lane & 15, lg = lane >> 4;
+
+    // ---- rows of one chunk in flight (this wavefront's blocks), 16-byte pieces.
+    // Each load instruction covers whole token rows (RPI rows of D channels), so
+    // every cache line it touches is used in full; buffer loads bounded at the
+    // chunk's last token return zeros past it.
+    constexpr int PPR = D / 8;                   // 16-byte pieces per row
+    constexpr int RPI = 64 / PPR;                // rows per instruction
+    constexpr uint32_t kRsrcFlags = 0x00020000;
+    const int pr = lane / PPR, pc = (lane % PPR) * 8;
+    uint4 rq[NLB][KS], rk[NLB][KS], rw[NLB][KS], rv[NLB];
+    uint16_t ng = 0x3f80u, nb = 0u;              // bf16 1.0 and 0.0 past the chunk end
+    auto load = [&](int ch) {
+        const int c0 = c.seq0 + ch * kC;
+        const int nt = min(kC, c.seq1 - c0);
+        const int rowQK = (int)c.rowQK, rowV = (int)c.rowV;
+        const int64_t base = (int64_t)c0 * c.rowQK + (int64_t)c.e * D;
+        const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(c.k + base), 0, nt * rowQK * 2, kRsrcFlags);
+        const __amdgpu_buffer_rsrc_t rKW = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(c.kw + base), 0, nt * rowQK * 2, kRsrcFlags);
+        const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(c.q + base), 0, nt * rowQK * 2, kRsrcFlags);
+        const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(c.v + (int64_t)c0 * c.rowV + (int64_t)c.e * c.DV + c.j0), 0,
+            nt * rowV * 2, kRsrcFlags);
+#pragma unroll
+        for (int u = 0; u < NLB; ++u) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int off = (((LB0 + u) * 16 + ks * RPI + pr) * rowQK + pc) * 2;
+                rk[u][ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rK, off, 0, 0));
+                rw[u][ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rKW, off, 0, 0));
+                rq[u][ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rQ, off, 0, 0));
+            }
+            const int offv = (((LB0 + u) * 16 + lane / VL) * rowV + (lane % VL) * 8) * 2;
+            rv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rV, offv, 0, 0));
+        }
+        // gates: every helper needs them for its masks
+        const __amdgpu_buffer_rsrc_t rG = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(c.g + (int64_t)c0 * c.H + c.e), 0, nt * c.H * 2, kRsrcFlags);
+        const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(c.b + (int64_t)c0 * c.H + c.e), 0, nt * c.H * 2, kRsrcFlags);
+        ng = __builtin_amdgcn_raw_buffer_load_b16(rG, lane * c.H * 2, 0, 0);
+        nb = __builtin_amdgcn_raw_buffer_load_b16(rB, lane * c.H * 2, 0, 0);
+        if (lane >= nt)
+            ng = 0x3f80u;                        // decay 1 past the chunk end (b reads 0)
+    };
+    uint16_t cg = 0x3f80u, cb = 0u;              // gates of the chunk being prepared
+    auto store_rows = [&](int ch) {
+        uint16_t *sQ = m.Q(ch), *sK = m.K(ch), *sKW = m.KW(ch), *sV = m.V(ch);
+#pragma unroll
+        for (int u = 0; u < NLB; ++u) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int off = ((LB0 + u) * 16 + ks * RPI + pr) * LDD + pc;
+                *reinterpret_cast<uint4*>(sK + off) = rk[u][ks];
+                *reinterpret_cast<uint4*>(sKW + off) = rw[u][ks];
+                *reinterpret_cast<uint4*>(sQ + off) = rq[u][ks];
+            }
+            if (lane < 16 * VL)
+                *reinterpret_cast<uint4*>(sV + ((LB0 + u) * 16 + lane / VL) * LDV + (lane % VL) * 8) = rv[u];
+        }
+        cg = ng;
+        cb = nb;
+    };
+
+    // ---- one chunk's matrices in registers (bf16 pairs, accumulator layout)
+    uint2 mkk[NP], mkw[NP], mqk[NP], mqw[NP];
+    uint32_t tcol[8];                            // role 0: column li of T_lg, bf16 pairs
+    float gb = 0.f, gg = 0.f, gf = 0.f;          // b, gamma, gamma_C / gamma of token `lane`
+    auto prep = [&](int ch) {
+        const float lam = wave_inclusive_sum(__log2f(fmaxf(bf16_to_f32(cg), 1e-30f)));
+        const float bv = bf16_to_f32(cb);
+        if constexpr (DIAG) {
+            const float lamC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam), 63));
+            gb = bv;
+            gg = __builtin_amdgcn_exp2f(lam);
+            gf = __builtin_amdgcn_exp2f(lamC - lam);
+        }
+        const uint16_t *sQ = m.Q(ch), *sK = m.K(ch), *sKW = m.KW(ch);
+        float* sLam = m.Lam(ROLE < 2 ? ROLE : ROLE - 1);
+        sLam[lane] = lam;
+        bf16x8_t bk[KS], bq[KS];
+        float lt = 0.f, bt = 0.f;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int tb = P::t[p], sb = P::s[p];
+            const int t = tb * 16 + li;
+            if (p == 0 || P::t[p] != P::t[p > 0 ? p - 1 : 0]) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    bk[ks] = frag_row(sK + tb * 16 * LDD + ks * 32, LDD, lane);
+                    bq[ks] = frag_row(sQ + tb * 16 * LDD + ks * 32, LDD, lane);
+                }
+                lt = sLam[t];
+                bt = __shfl(bv, t, 64);
+            }
+            bf16x8_t ak[KS], aw[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                ak[ks] = sb == tb ? bk[ks] : frag_row(sK + sb * 16 * LDD + ks * 32, LDD, lane);
+                aw[ks] = frag_row(sKW + sb * 16 * LDD + ks * 32, LDD, lane);
+            }
+            f32x4_t gkk = {0.f, 0.f, 0.f, 0.f}, gkw = gkk, gqk = gkk, gqw = gkk;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                gkk = mma32(ak[ks], bk[ks], gkk);         // transposed blocks: element (s, t)
+                gkw = mma32(aw[ks], bk[ks], gkw);
+                gqk = mma32(ak[ks], bq[ks], gqk);
+                gqw = mma32(aw[ks], bq[ks], gqw);
+            }
+            const int s0 = sb * 16 + lg * 4;
+            const float4 ls4 = *reinterpret_cast<const float4*>(sLam + s0);
+            const float lsv[4] = {ls4.x, ls4.y, ls4.z, ls4.w};
+            f32x4_t vkk, vkw, vqk, vqw;
+            if (sb == tb) {
+                // diagonal block: causal masks, decay 2^(lam_t - lam_s) per element
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int s = s0 + r;
+                    const float dec = __builtin_amdgcn_exp2f(fminf(lt - lsv[r], 0.f));
+                    const float mi = s <= t ? dec : 0.f;
+                    const float ms = s < t ? dec * bt : 0.f;
+                    vkk[r] = ms * gkk[r];
+                    vkw[r] = ms * gkw[r];
+                    vqk[r] = -mi * gqk[r];
+                    vqw[r] = mi * gqw[r];
+                }
+            } else {
+                // s-block entirely before t: 2^(lam_t - lam_s) = 2^(lam_t - lam_e) 2^(lam_e - lam_s)
+                // with lam_e the last token of the s-block; both factors are <= 1
+                // because lam never increases along the chunk
+                const float le = sLam[sb * 16 + 15];
+                const float et = __builtin_amdgcn_exp2f(lt - le), bet = bt * et;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float fs = __builtin_amdgcn_exp2f(le - lsv[r]);
+                    const float mi = et * fs, ms = bet * fs;
+                    vkk[r] = ms * gkk[r];
+                    vkw[r] = ms * gkw[r];
+                    vqk[r] = -mi * gqk[r];
+                    vqw[r] = mi * gqw[r];
+                }
+            }
+            mkk[p] = make_uint2(pack_bf16x2(vkk[0], vkk[1]), pack_bf16x2(vkk[2], vkk[3]));
+            mkw[p] = make_uint2(pack_bf16x2(vkw[0], vkw[1]), pack_bf16x2(vkw[2], vkw[3]));
+            mqk[p] = make_uint2(pack_bf16x2(vqk[0], vqk[1]), pack_bf16x2(vqk[2], vqk[3]));
+            mqw[p] = make_uint2(pack_bf16x2(vqw[0], vqw[1]), pack_bf16x2(vqw[2], vqw[3]));
+            if constexpr (DIAG)                          // A_tt row li, columns 4 lg .. 4 lg + 3
+                *reinterpret_cast<uint2*>(m.Scr() + (tb * 16 + li) * 16 + lg * 4) = mkk[p];
+        }
+        if constexpr (DIAG) {
+            // lane (16 g + i): row i of A_g, then column i of T_g = (I + A_g)^-1
+            const uint16_t* row = m.Scr() + lane * 16;
+            const uint4 w0 = *reinterpret_cast<const uint4*>(row);
+            const uint4 w1 = *reinterpret_cast<const uint4*>(row + 8);
+            const uint32_t wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+            float a[16], x[16];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                a[2 * j] = __uint_as_float(wv[j] << 16);
+                a[2 * j + 1] = __uint_as_float(wv[j] & 0xffff0000u);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                x[r] = (r == li) ? 1.f : 0.f;
+            subst<0>(x, a);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                tcol[j] = pack_bf16x2(x[2 * j], x[2 * j + 1]);
+        }
+    };
+    auto write_mats = [&]() {
+        uint16_t *Akk = m.Akk(), *Akkw = m.Akkw(), *Aqkw = m.Aqkw(), *Aqk = m.Aqk();
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int off = (P::t[p] * 16 + li) * LDC + P::s[p] * 16 + lg * 4;
+            if constexpr (!DIAG)                 // the diagonal blocks of A_kk hold T_tt
+                *reinterpret_cast<uint2*>(Akk + off) = mkk[p];
+            *reinterpret_cast<uint2*>(Akkw + off) = mkw[p];
+            *reinterpret_cast<uint2*>(Aqk + off) = mqk[p];
+            *reinterpret_cast<uint2*>(Aqkw + off) = mqw[p];
+        }
+        if constexpr (DIAG) {
+            // column li of T_lg into the diagonal block lg of A_kk
+            uint16_t* Tc = Akk + (lg * 16) * LDC + lg * 16 + li;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                Tc[(2 * j) * LDC] = (uint16_t)(tcol[j] & 0xffffu);
+                Tc[(2 * j + 1) * LDC] = (uint16_t)(tcol[j] >> 16);
+            }
+            float* G = m.G();
+            G[lane] = gb;
+            G[kC + lane] = gg;
+            G[2 * kC + lane] = gf;
+        }
+    };
+
+    const int nch = c.nchunks;
+    if (nch > 0)
+        load(0);
+    lds_barrier();                               // LDS cleared
+    if (nch > 0) {
+        store_rows(0);
+        if (nch > 1)
+            load(1);
+    }
+    lds_barrier();                               // rows of chunk 0 visible
+    if (nch > 0) {
+        prep(0);
+        write_mats();
+        if (nch > 1)
+            store_rows(1);
+    }
+    lds_barrier();
+    for (int ch = 0; ch < nch; ++ch) {
+        // phase A (beside the state path of chunk ch)
+        if (ch + 2 < nch)
+            load(ch + 2);
+        if (ch + 1 < nch)
+            prep(ch + 1);
+        lds_barrier();
+        // phase B
+        if (ch + 1 < nch)
+            write_mats();
+        if (ch + 2 < nch)
+            store_rows(ch + 2);
+        lds_barrier();
+    }
+}
+
+// State wavefront jb: value columns 16 jb .. 16 jb + 15 of the slice.
+template <int D, int DVS>
+__device__ __forceinline__ void state_loop(const WsCtx& c, int jb)
+{
+    constexpr int NI = D / 16;
+    const WsBuf<D, DVS> m{c.smem};
+    const int lane = c.lane, li = lane & 15, lg = lane >> 4;
+    f32x4_t S[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+        S[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    lds_barrier();
+    lds_barrier();
+    lds_barrier();
+    const float* G = m.G();
+    for (int ch = 0; ch < c.nchunks; ++ch) {
+        const int c0 = c.seq0 + ch * kC;
+        const int nt = min(kC, c.seq1 - c0);
+        // gamma_C = gamma of the last token (gates past the chunk end are 1)
+        state_path<D, DVS, true>(S, m.Q(ch), m.K(ch), m.KW(ch), m.V(ch), m.Akk(), m.Akkw(), m.Aqkw(),
+                                 m.Aqk(), nullptr, G, G + kC, G + 2 * kC, G[2 * kC - 1], c.o,
+                                 c0, nt, c.rowV, c.e, c.DV, c.j0, jb, lane);
+        lds_barrier();
+        lds_barrier();
+    }
+#pragma unroll
+    for (int ib = 0; ib < NI; ++ib) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = ib * 16 + lg * 4 + r;
+            c.s_final[(((int64_t)c.n * c.H + c.e) * D + i) * c.DV + c.j0 + jb * 16 + li] = S[ib][r];
+        }
+    }
+}
+
+template <int D, int DVS>
+__global__ __launch_bounds__(kThreads) void scan_ws_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ kw, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ g, const uint16_t* __restrict__ b,
+    const int32_t* __restrict__ cu, int H, int DV, int n_slices, uint16_t* __restrict__ o,
+    float* __restrict__ s_final)
+{
+    using Ly = LayoutWS<D, DVS>;
+    constexpr int NJ = DVS / 16;
+    static_assert(NJ == 1 || NJ == 2, "one or two state wavefronts");
+    static_assert(Ly::total <= 160 * 1024, "LDS budget");
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Ly::total];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int slice, chain;
+    xcd_map(n_slices, slice, chain);
+
+    WsCtx c;
+    c.smem = smem;
+    c.q = q; c.k = k; c.kw = kw; c.v = v; c.g = g; c.b = b;
+    c.o = o;
+    c.s_final = s_final;
+    c.n = chain / H;
+    c.e = chain % H;
+    c.H = H;
+    c.DV = DV;
+    c.j0 = slice * DVS;
+    c.seq0 = cu[c.n];
+    c.seq1 = cu[c.n + 1];
+    c.nchunks = (c.seq1 - c.seq0 + kC - 1) / kC;
+    c.lane = tid & 63;
+    c.rowQK = (int64_t)H * D;
+    c.rowV = (int64_t)H * DV;
+
+    {
+        // matrices (their upper blocks are never written), gates, scratch
+        constexpr int nz = (Ly::total - Ly::oAkk) / 16;
+        uint4* z = reinterpret_cast<uint4*>(smem + Ly::oAkk);
+        for (int i = tid; i < nz; i += kThreads)
+            z[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+
+    // Every role passes the same number of barriers: 3 + 2 per chunk.
+    if (wave < NJ) {
+        state_loop<D, DVS>(c, wave);
+    } else if constexpr (NJ == 2) {              // diagonal pairs | six off-diagonal pairs
+        if (wave == 2)
+            helper_loop<D, DVS, 0, 0, HWS_DIAG_BLOCKS>(c);
+        else
+            helper_loop<D, DVS, 1, HWS_DIAG_BLOCKS, 4 - HWS_DIAG_BLOCKS>(c);
+    } else {                                     // diagonal | three | three
+        if (wave == 1)
+            helper_loop<D, DVS, 0, 0, 1>(c);
+        else if (wave == 2)
+            helper_loop<D, DVS, 2, 1, 1>(c);
+        else
+            helper_loop<D, DVS, 3, 2, 2>(c);
+    }
+}
+
+template <int D, int DVS>
+static hipError_t launch_ws(const ScanArgs& p, hipStream_t stream)
+{
+    const int n_slices = p.dv / DVS;
+    const int64_t blocks = (int64_t)p.n_seqs * p.heads * n_slices;
+    if (blocks == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL((scan_ws_kernel<D, DVS>), dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                       (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.kw,
+                       (const uint16_t*)p.v, (const uint16_t*)p.g, (const uint16_t*)p.b,
+                       p.cu_seqlens, p.heads, p.dv, n_slices, (uint16_t*)p.o, p.s_final);
+    return hipGetLastError();
 }
 
 template <int D, int DVS>
@@ -518,6 +1130,11 @@ hipError_t launch_scan_bf16(const ScanArgs& p, hipStream_t s)
 {
     if (!scan_bf16_supported(p.dk, p.dv, p.dv_slice))
         return hipErrorInvalidValue;
+    if (p.specialised) {
+        if (p.dk == 64)
+            return p.dv_slice == 16 ? bf16scan::launch_ws<64, 16>(p, s) : bf16scan::launch_ws<64, 32>(p, s);
+        return p.dv_slice == 16 ? bf16scan::launch_ws<128, 16>(p, s) : bf16scan::launch_ws<128, 32>(p, s);
+    }
     if (p.dk == 64) {
         if (p.dv_slice == 16) return bf16scan::launch<64, 16>(p, s);
         if (p.dv_slice == 32) return bf16scan::launch<64, 32>(p, s);

@@ -32,6 +32,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, h);
 }
 
+// Workgroup barrier that orders LDS accesses only.  Every exchange between the
+// wavefronts of one workgroup in these kernels goes through LDS, so global
+// loads (prefetches) and stores stay in flight across it; a full
+// __syncthreads() would wait for all of them first.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Element conversions for the two input storage types.
 __device__ __forceinline__ float to_f32(uint16_t x) { return bf16_to_f32(x); }
 __device__ __forceinline__ float to_f32(float x) { return x; }

@@ -20,6 +20,7 @@ struct ScanArgs {
     bool bf16;
     int n_seqs, total_tokens, heads, dk, dv;
     int dv_slice;                   // value columns owned by one workgroup
+    bool specialised;               // bf16: helper wavefronts prepare the next chunk (dv_slice <= 32)
     const void *q, *k, *kw, *v, *g, *b;
     const int32_t* cu_seqlens;
     void* o;

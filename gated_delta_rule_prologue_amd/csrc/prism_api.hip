@@ -34,7 +34,7 @@ int env_int(const char* name, int fallback)
         return fallback;
     char* end = nullptr;
     long v = strtol(s, &end, 10);
-    return (end && *end == 0 && v > 0 && v < (1 << 20)) ? (int)v : fallback;
+    return (end && *end == 0 && v >= 0 && v < (1 << 20)) ? (int)v : fallback;
 }
 
 // Which scan kernel runs: the register-resident bf16 kernel unless the
@@ -131,6 +131,8 @@ prism_status prism_prologue(const prism_dims* d, const void* k, const void* u, c
     p.dk = d->dk;
     p.L = L;
     p.strip = env_int("PRISM_PROLOGUE_STRIP", 8);
+    if (p.strip < 1)
+        p.strip = 8;
     p.narrow = env_int("PRISM_PROLOGUE_NARROW", 0) != 0;
     p.k = k; p.u = u; p.a = a; p.h = h; p.b = b; p.conv_w = conv_w;
     p.cu_seqlens = cu_seqlens;
@@ -158,6 +160,7 @@ prism_status prism_scan(const prism_dims* d, const void* q, const void* k, const
     p.dk = d->dk;
     p.dv = d->dv;
     p.dv_slice = pick_dv_slice(d);
+    p.specialised = p.bf16 && p.dv_slice <= 32 && env_int("PRISM_SCAN_SPECIALISED", 1) != 0;
     p.q = q; p.k = k; p.kw = kw; p.v = v; p.g = g; p.b = b;
     p.cu_seqlens = cu_seqlens;
     p.o = o;

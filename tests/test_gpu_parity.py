@@ -96,19 +96,57 @@ def test_fwd_matches_oracle(w):
     assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]
 
 
-@pytest.mark.parametrize("generic", [0, 1], ids=["bf16-kernel", "generic-kernel"])
+SCAN_KERNELS = {                 # environment selecting each bf16 scan kernel
+    "specialised": {"PRISM_SCAN_GENERIC": "0", "PRISM_SCAN_SPECIALISED": "1"},
+    "register": {"PRISM_SCAN_GENERIC": "0", "PRISM_SCAN_SPECIALISED": "0"},
+    "generic": {"PRISM_SCAN_GENERIC": "1"},
+}
+
+
+@pytest.mark.parametrize("kernel", list(SCAN_KERNELS))
 @pytest.mark.parametrize("dvs", [16, 32, 64])
 @pytest.mark.parametrize("dk", [64, 128])
-def test_every_value_slice_width(dk, dvs, generic, monkeypatch):
-    """Both bf16 scan kernels (register-resident and generic), every slice width."""
-    if generic and dk == 128 and dvs == 64:
+def test_every_value_slice_width(dk, dvs, kernel, monkeypatch):
+    """Every bf16 scan kernel at every value-slice width it has; sequences of
+    0, 1, 2 and 3 chunks with full and ragged last chunks."""
+    if kernel == "generic" and dk == 128 and dvs == 64:
         pytest.skip("the generic kernel has no dk=128 variant with 64 value columns")
+    if kernel == "specialised" and dvs == 64:
+        pytest.skip("the specialised kernel serves slices of 16 and 32 value columns")
     monkeypatch.setenv("PRISM_DV_SLICE", str(dvs))
-    monkeypatch.setenv("PRISM_SCAN_GENERIC", str(generic))
-    inp = make_inputs(W(dtype="bf16", dk=dk, dv=64, L=3, lengths=(140, 3)))
+    for key, val in SCAN_KERNELS[kernel].items():
+        monkeypatch.setenv(key, val)
+    inp = make_inputs(W(dtype="bf16", dk=dk, dv=64, L=3, lengths=(140, 3, 0, 64, 128, 65)))
     o, s = gpu_fwd(inp)
     o_ref, s_ref = oracle.fwd(inp)
-    say(f"dk {dk} dvs {dvs}: o {max_rel(o, o_ref):.3e} S {max_rel(s, s_ref):.3e}")
+    say(f"{kernel} dk {dk} dvs {dvs}: o {max_rel(o, o_ref):.3e} S {max_rel(s, s_ref):.3e}")
+    assert max_rel(o, o_ref) <= TOL["bf16"] and max_rel(s, s_ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("kernel", ["specialised", "register"])
+def test_bf16_kernels_long_sequence(kernel, monkeypatch):
+    """Dozens of chunks through one chain: the double-buffered matrices and the
+    staged rows alternate many times."""
+    monkeypatch.setenv("PRISM_DV_SLICE", "32")
+    for key, val in SCAN_KERNELS[kernel].items():
+        monkeypatch.setenv(key, val)
+    inp = make_inputs(W(dtype="bf16", dk=128, dv=128, L=4, H=1, lengths=(2000, 37)))
+    o, s = gpu_fwd(inp)
+    o_ref, s_ref = oracle.fwd(inp)
+    say(f"{kernel} long: o {max_rel(o, o_ref):.3e} S {max_rel(s, s_ref):.3e}")
+    assert max_rel(o, o_ref) <= TOL["bf16"] and max_rel(s, s_ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dvs", [16, 32])
+@pytest.mark.parametrize("lengths", [(130, 0, 64, 300), (65, 1, 128, 7, 200, 0, 90, 33)],
+                         ids=["8-chains", "16-chains"])
+def test_slices_grouped_per_xcd(dvs, lengths, monkeypatch):
+    """Chain counts divisible by eight take the XCD-grouped workgroup order."""
+    monkeypatch.setenv("PRISM_DV_SLICE", str(dvs))
+    inp = make_inputs(W(dtype="bf16", dk=128, dv=128, L=4, H=2, lengths=lengths))
+    o, s = gpu_fwd(inp)
+    o_ref, s_ref = oracle.fwd(inp)
+    say(f"xcd-grouped dvs {dvs} {lengths}: o {max_rel(o, o_ref):.3e} S {max_rel(s, s_ref):.3e}")
     assert max_rel(o, o_ref) <= TOL["bf16"] and max_rel(s, s_ref) <= TOL["bf16"]
 
 
