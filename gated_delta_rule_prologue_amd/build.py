@@ -11,6 +11,11 @@ import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
 
+try:
+    from . import check_isa
+except ImportError:                      # run as a script
+    import check_isa
+
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
@@ -18,6 +23,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libprism.so")
 SOURCES = ["prism_api.hip", "prologue.hip", "chunk_scan.hip", "chunk_scan_bf16.hip"]
+CHECKED = ["chunk_scan_bf16.hip", "chunk_scan.hip"]      # sources with mixed-size MFMA chains
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -59,8 +65,19 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         cmds.append([hipcc, *HIPCC_FLAGS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj])
+    # device assembly of the MFMA kernels, for the machine-code check below
+    asm = {src: os.path.join(BUILD, os.path.splitext(src)[0] + ".s") for src in CHECKED}
+    for src, out in asm.items():
+        cmds.append([hipcc, *HIPCC_FLAGS, *extra_flags, "-S", "--cuda-device-only",
+                     os.path.join(CSRC, src), "-o", out])
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
+    for src, out in asm.items():
+        bad = check_isa.scan(open(out).read())
+        if bad:
+            lines = "\n".join(f"  {f[:70]}: {i}" for f, i in bad[:10])
+            raise RuntimeError(f"{src}: a 16x16x16 MFMA overlaps the result of an in-flight "
+                               f"16x16x32 MFMA (see check_isa.py):\n{lines}")
     tmp = LIB + ".tmp%d" % os.getpid()
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)

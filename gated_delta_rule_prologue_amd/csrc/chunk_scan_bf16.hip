@@ -341,16 +341,20 @@ __device__ __forceinline__ void state_path(
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb)
         xb[sb] = as_b16(X[sb], 1.f, 1.f, 1.f, 1.f);
+    const v4s_t zero4 = {0, 0, 0, 0};
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
         const int n = tb * (tb + 1) / 2;             // aqk[n + sb] is block (tb, sb)
         f32x4_t oa = OT[tb];
+        // every product of the chain is 16x16x32 (an odd block is paired with a
+        // zero block): a dependent 16x16x16 and 16x16x32 pair whose results the
+        // compiler places two registers apart corrupts the accumulator
 #pragma unroll
         for (int sb = 0; sb <= tb; sb += 2) {
             if (sb + 1 <= tb)
                 oa = mma32(cat8(xb[sb], xb[sb + 1]), cat8(aqk[n + sb], aqk[n + sb + 1]), oa);
             else
-                oa = mma16(xb[sb], aqk[n + sb], oa);
+                oa = mma32(cat8(xb[sb], zero4), cat8(aqk[n + sb], zero4), oa);
         }
         // lane (li, lg): token tb * 16 + li, value columns 4 lg .. 4 lg + 3 of block jb
         const int t = tb * 16 + li;
@@ -699,21 +703,22 @@ struct WsBuf {
     __device__ float* Lam(int slot) const { return reinterpret_cast<float*>(base + Ly::oLam) + slot * kC; }
 };
 
-// Gram pairs (t-block, s-block) of each helper role: role 0 takes the four
-// diagonal pairs (and with them the diagonal inverses and the gates); the
-// off-diagonal pairs go to one helper (roles 1) or are split over two (2, 3).
+// Gram pairs (t-block, s-block) of each helper role, ordered by t-block: role 0
+// takes the four diagonal pairs (their A_kk blocks go to the inverse scratch)
+// and (1, 0), and publishes the gates; the other off-diagonal pairs go to one
+// helper (role 1) or are split over two (roles 2, 3).
 template <int ROLE> struct Pairs;
 template <> struct Pairs<0> {
-    static constexpr int n = 4;
-    static constexpr int t[4] = {0, 1, 2, 3}, s[4] = {0, 1, 2, 3};
+    static constexpr int n = 5;
+    static constexpr int t[5] = {0, 1, 1, 2, 3}, s[5] = {0, 0, 1, 2, 3};
 };
 template <> struct Pairs<1> {
-    static constexpr int n = 6;
-    static constexpr int t[6] = {1, 2, 2, 3, 3, 3}, s[6] = {0, 0, 1, 0, 1, 2};
+    static constexpr int n = 5;
+    static constexpr int t[5] = {2, 2, 3, 3, 3}, s[5] = {0, 1, 0, 1, 2};
 };
 template <> struct Pairs<2> {
-    static constexpr int n = 3;
-    static constexpr int t[3] = {1, 2, 2}, s[3] = {0, 0, 1};
+    static constexpr int n = 2;
+    static constexpr int t[2] = {2, 2}, s[2] = {0, 1};
 };
 template <> struct Pairs<3> {
     static constexpr int n = 3;
@@ -722,28 +727,57 @@ template <> struct Pairs<3> {
 
 // Unit lower-triangular 16x16 inverse, four blocks per wavefront: lane
 // (16 g + i) holds row i of the strictly lower block A_g in a[] and returns
-// column i of (I + A_g)^-1 in x[] (right-looking substitution in fp32; the
-// entry A_g[r][c] is broadcast from lane 16 g + r with a DPP row broadcast).
-template <int R>
-__device__ __forceinline__ float row_bcast(float v)
-{
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + R, 0xF, 0xF, false));
-}
+// column i of (I + A_g)^-1 in x[] (right-looking substitution in fp32).  Step c
+// updates x[r] -= A_g[r][c] x[c] for r > c with one v_fmac_f32 each, the entry
+// A_g[r][c] coming from lane 16 g + r through a DPP row broadcast of a[c]
+// (`row_newbcast`, which the compiler does not fuse into the FMA by itself).
+// a[] is complete before the first step; the s_nop covers the two wait states a
+// DPP read needs after a VALU write of its source.
 template <int C, int R>
-__device__ __forceinline__ void subst_col(float (&x)[16], const float (&a)[16], float nxc)
+__device__ __forceinline__ void subst_col(float (&x)[16], float ac, float xc)
 {
     if constexpr (R < 16) {
-        x[R] = fmaf(row_bcast<R>(a[C]), nxc, x[R]);
-        subst_col<C, R + 1>(x, a, nxc);
+        asm volatile("v_fmac_f32_dpp %0, %1, -%2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                     : "+v"(x[R])
+                     : "v"(ac), "v"(xc), "i"(R));
+        subst_col<C, R + 1>(x, ac, xc);
     }
 }
 template <int C>
 __device__ __forceinline__ void subst(float (&x)[16], const float (&a)[16])
 {
     if constexpr (C < 15) {
-        subst_col<C, C + 1>(x, a, -x[C]);
+        asm volatile("s_nop 1");
+        subst_col<C, C + 1>(x, a[C], x[C]);
         subst<C + 1>(x, a);
     }
+}
+
+// T_g = (I + A_g)^-1 for the four diagonal blocks of A_kk: scr holds the strictly
+// lower blocks A_g row-major (rows of 16 bf16, block g at row 16 g); column i of
+// T_g goes to the diagonal block g of Akk (row stride LDC).  One wavefront.
+template <int LDC>
+__device__ __forceinline__ void invert_diag(const uint16_t* scr, uint16_t* Akk, int lane)
+{
+    const int li = lane & 15, lg = lane >> 4;
+    const uint16_t* row = scr + lane * 16;
+    const uint4 w0 = *reinterpret_cast<const uint4*>(row);
+    const uint4 w1 = *reinterpret_cast<const uint4*>(row + 8);
+    const uint32_t wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    float a[16], x[16];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        a[2 * j] = __uint_as_float(wv[j] << 16);
+        a[2 * j + 1] = __uint_as_float(wv[j] & 0xffff0000u);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        x[r] = (r == li) ? 1.f : 0.f;
+    subst<0>(x, a);
+    uint16_t* Tc = Akk + (lg * 16) * LDC + lg * 16 + li;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        Tc[r * LDC] = f32_to_bf16(x[r]);
 }
 
 // Helper wavefront: loads and stores the 16-token row blocks LB0 .. LB0 + NLB - 1
@@ -772,41 +806,55 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
     const int pr = lane / PPR, pc = (lane % PPR) * 8;
     uint4 rq[NLB][KS], rk[NLB][KS], rw[NLB][KS], rv[NLB];
     uint16_t ng = 0x3f80u, nb = 0u;              // bf16 1.0 and 0.0 past the chunk end
-    auto load = [&](int ch) {
+    // Loads of one chunk, issued in NLB + 1 groups (the gates, then one row
+    // block each) so that they can be spread over the Gram computation.
+    struct Src {
+        __amdgpu_buffer_rsrc_t k, kw, q, v, g, b;
+        int nt;
+    };
+    auto src = [&](int ch) {
         const int c0 = c.seq0 + ch * kC;
         const int nt = min(kC, c.seq1 - c0);
-        const int rowQK = (int)c.rowQK, rowV = (int)c.rowV;
         const int64_t base = (int64_t)c0 * c.rowQK + (int64_t)c.e * D;
-        const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(c.k + base), 0, nt * rowQK * 2, kRsrcFlags);
-        const __amdgpu_buffer_rsrc_t rKW = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(c.kw + base), 0, nt * rowQK * 2, kRsrcFlags);
-        const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(c.q + base), 0, nt * rowQK * 2, kRsrcFlags);
-        const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc(
+        const int nqk = nt * (int)c.rowQK * 2;   // rows past the chunk end read as zero
+        Src r;
+        r.k = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(c.k + base), 0, nqk, kRsrcFlags);
+        r.kw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(c.kw + base), 0, nqk, kRsrcFlags);
+        r.q = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(c.q + base), 0, nqk, kRsrcFlags);
+        r.v = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t*>(c.v + (int64_t)c0 * c.rowV + (int64_t)c.e * c.DV + c.j0), 0,
-            nt * rowV * 2, kRsrcFlags);
-#pragma unroll
-        for (int u = 0; u < NLB; ++u) {
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int off = (((LB0 + u) * 16 + ks * RPI + pr) * rowQK + pc) * 2;
-                rk[u][ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rK, off, 0, 0));
-                rw[u][ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rKW, off, 0, 0));
-                rq[u][ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rQ, off, 0, 0));
-            }
-            const int offv = (((LB0 + u) * 16 + lane / VL) * rowV + (lane % VL) * 8) * 2;
-            rv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rV, offv, 0, 0));
-        }
-        // gates: every helper needs them for its masks
-        const __amdgpu_buffer_rsrc_t rG = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(c.g + (int64_t)c0 * c.H + c.e), 0, nt * c.H * 2, kRsrcFlags);
-        const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(c.b + (int64_t)c0 * c.H + c.e), 0, nt * c.H * 2, kRsrcFlags);
-        ng = __builtin_amdgcn_raw_buffer_load_b16(rG, lane * c.H * 2, 0, 0);
-        nb = __builtin_amdgcn_raw_buffer_load_b16(rB, lane * c.H * 2, 0, 0);
-        if (lane >= nt)
+            nt * (int)c.rowV * 2, kRsrcFlags);
+        r.g = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(c.g + (int64_t)c0 * c.H + c.e), 0,
+                                                nt * c.H * 2, kRsrcFlags);
+        r.b = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(c.b + (int64_t)c0 * c.H + c.e), 0,
+                                                nt * c.H * 2, kRsrcFlags);
+        r.nt = nt;
+        return r;
+    };
+    auto load_gates = [&](const Src& r) {
+        ng = __builtin_amdgcn_raw_buffer_load_b16(r.g, lane * c.H * 2, 0, 0);
+        nb = __builtin_amdgcn_raw_buffer_load_b16(r.b, lane * c.H * 2, 0, 0);
+        if (lane >= r.nt)
             ng = 0x3f80u;                        // decay 1 past the chunk end (b reads 0)
+    };
+    auto load_block = [&](const Src& r, int u) {
+        const int rowQK = (int)c.rowQK, rowV = (int)c.rowV;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int off = (((LB0 + u) * 16 + ks * RPI + pr) * rowQK + pc) * 2;
+            rk[u][ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r.k, off, 0, 0));
+            rw[u][ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r.kw, off, 0, 0));
+            rq[u][ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r.q, off, 0, 0));
+        }
+        const int offv = (((LB0 + u) * 16 + lane / VL) * rowV + (lane % VL) * 8) * 2;
+        rv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r.v, offv, 0, 0));
+    };
+    auto load = [&](int ch) {
+        const Src r = src(ch);
+        load_gates(r);
+#pragma unroll
+        for (int u = 0; u < NLB; ++u)
+            load_block(r, u);
     };
     uint16_t cg = 0x3f80u, cb = 0u;              // gates of the chunk being prepared
     auto store_rows = [&](int ch) {
@@ -829,9 +877,15 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
 
     // ---- one chunk's matrices in registers (bf16 pairs, accumulator layout)
     uint2 mkk[NP], mkw[NP], mqk[NP], mqw[NP];
-    uint32_t tcol[8];                            // role 0: column li of T_lg, bf16 pairs
     float gb = 0.f, gg = 0.f, gf = 0.f;          // b, gamma, gamma_C / gamma of token `lane`
-    auto prep = [&](int ch) {
+    // prep(ch, lch): matrices of chunk ch; the loads of chunk lch (if >= 0) are
+    // issued between its Gram pairs
+    auto prep = [&](int ch, int lch) {
+        Src lsrc;
+        if (lch >= 0) {
+            lsrc = src(lch);
+            load_gates(lsrc);
+        }
         const float lam = wave_inclusive_sum(__log2f(fmaxf(bf16_to_f32(cg), 1e-30f)));
         const float bv = bf16_to_f32(cb);
         if constexpr (DIAG) {
@@ -849,6 +903,14 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
         for (int p = 0; p < NP; ++p) {
             const int tb = P::t[p], sb = P::s[p];
             const int t = tb * 16 + li;
+#pragma unroll
+            for (int u = 0; u < NLB; ++u) {
+                if (p == u * NP / NLB && lch >= 0) {
+                    SCHED_FENCE();
+                    load_block(lsrc, u);
+                    SCHED_FENCE();
+                }
+            }
             if (p == 0 || P::t[p] != P::t[p > 0 ? p - 1 : 0]) {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
@@ -909,28 +971,8 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
             mkw[p] = make_uint2(pack_bf16x2(vkw[0], vkw[1]), pack_bf16x2(vkw[2], vkw[3]));
             mqk[p] = make_uint2(pack_bf16x2(vqk[0], vqk[1]), pack_bf16x2(vqk[2], vqk[3]));
             mqw[p] = make_uint2(pack_bf16x2(vqw[0], vqw[1]), pack_bf16x2(vqw[2], vqw[3]));
-            if constexpr (DIAG)                          // A_tt row li, columns 4 lg .. 4 lg + 3
+            if (tb == sb)                                // A_tt row li, columns 4 lg .. 4 lg + 3
                 *reinterpret_cast<uint2*>(m.Scr() + (tb * 16 + li) * 16 + lg * 4) = mkk[p];
-        }
-        if constexpr (DIAG) {
-            // lane (16 g + i): row i of A_g, then column i of T_g = (I + A_g)^-1
-            const uint16_t* row = m.Scr() + lane * 16;
-            const uint4 w0 = *reinterpret_cast<const uint4*>(row);
-            const uint4 w1 = *reinterpret_cast<const uint4*>(row + 8);
-            const uint32_t wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-            float a[16], x[16];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                a[2 * j] = __uint_as_float(wv[j] << 16);
-                a[2 * j + 1] = __uint_as_float(wv[j] & 0xffff0000u);
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                x[r] = (r == li) ? 1.f : 0.f;
-            subst<0>(x, a);
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                tcol[j] = pack_bf16x2(x[2 * j], x[2 * j + 1]);
         }
     };
     auto write_mats = [&]() {
@@ -938,20 +980,13 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             const int off = (P::t[p] * 16 + li) * LDC + P::s[p] * 16 + lg * 4;
-            if constexpr (!DIAG)                 // the diagonal blocks of A_kk hold T_tt
+            if (P::t[p] != P::s[p])              // the diagonal blocks of A_kk hold T_tt
                 *reinterpret_cast<uint2*>(Akk + off) = mkk[p];
             *reinterpret_cast<uint2*>(Akkw + off) = mkw[p];
             *reinterpret_cast<uint2*>(Aqk + off) = mqk[p];
             *reinterpret_cast<uint2*>(Aqkw + off) = mqw[p];
         }
         if constexpr (DIAG) {
-            // column li of T_lg into the diagonal block lg of A_kk
-            uint16_t* Tc = Akk + (lg * 16) * LDC + lg * 16 + li;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                Tc[(2 * j) * LDC] = (uint16_t)(tcol[j] & 0xffffu);
-                Tc[(2 * j + 1) * LDC] = (uint16_t)(tcol[j] >> 16);
-            }
             float* G = m.G();
             G[lane] = gb;
             G[kC + lane] = gg;
@@ -970,18 +1005,21 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
     }
     lds_barrier();                               // rows of chunk 0 visible
     if (nch > 0) {
-        prep(0);
+        prep(0, -1);
         write_mats();
+        if constexpr (DIAG)                      // chunk 0; later chunks: a state wavefront
+            invert_diag<LDC>(m.Scr(), m.Akk(), lane);
         if (nch > 1)
             store_rows(1);
     }
     lds_barrier();
     for (int ch = 0; ch < nch; ++ch) {
-        // phase A (beside the state path of chunk ch)
-        if (ch + 2 < nch)
-            load(ch + 2);
+        // phase A (beside the state path of chunk ch): matrices of chunk ch + 1,
+        // with the loads of chunk ch + 2 spread between its Gram pairs
         if (ch + 1 < nch)
-            prep(ch + 1);
+            prep(ch + 1, ch + 2 < nch ? ch + 2 : -1);
+        else if (ch + 2 < nch)
+            load(ch + 2);
         lds_barrier();
         // phase B
         if (ch + 1 < nch)
@@ -1015,6 +1053,10 @@ __device__ __forceinline__ void state_loop(const WsCtx& c, int jb)
                                  m.Aqk(), nullptr, G, G + kC, G + 2 * kC, G[2 * kC - 1], c.o,
                                  c0, nt, c.rowV, c.e, c.DV, c.j0, jb, lane);
         lds_barrier();
+        // phase B: the diagonal inverses of chunk ch + 1 (their A_ii were built in
+        // phase A), beside the helpers' matrix and row stores
+        if (jb == 0 && ch + 1 < c.nchunks)
+            invert_diag<Layout<D, DVS>::LDC>(m.Scr(), m.Akk(), lane);
         lds_barrier();
     }
 #pragma unroll
