@@ -196,7 +196,11 @@ __device__ __forceinline__ void state_path(
     for (int ib = 0; ib < NI; ++ib)
         s0b[ib] = as_b16(S[ib], 1.f, 1.f, 1.f, 1.f);
 
-    // ---- reads for a
+    // LDS reads run a short, fixed distance ahead of their MFMAs: a wavefront
+    // can wait precisely only for the oldest of at most 15 outstanding reads,
+    // so each batch is kept small and issued a few steps before its use.
+
+    // ---- a. S <- gamma_C S + KW^T diag(fac) V   (NI independent accumulators)
     bf16x8_t vf[2], kwf[2][NI];
     float4 fc[4];
 #pragma unroll
@@ -205,99 +209,118 @@ __device__ __forceinline__ void state_path(
         fc[2 * h2] = *reinterpret_cast<const float4*>(sFac + h2 * 32 + lg * 8);
         fc[2 * h2 + 1] = *reinterpret_cast<const float4*>(sFac + h2 * 32 + lg * 8 + 4);
     }
+    auto load_kw = [&](int ib) {
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int ib = 0; ib < NI; ++ib)
+        for (int h2 = 0; h2 < 2; ++h2)
             kwf[h2][ib] = frag_col(sKW + h2 * 32 * LDD + ib * 16, LDD, lane);
-
-    // reads for b, one 16-token block tb per batch, double-buffered
-    v4s_t kf[2][NI], qf[2][NI];
-    bf16x8_t akw[2][2], aqw[2][2];
-    float4 gm[2], bb[2];
-    float go[2];
-    auto load_b = [&](int tb, int sl) {
-#pragma unroll
-        for (int kb = 0; kb < NI; ++kb) {
-            kf[sl][kb] = frag4_row(sK + tb * 16 * LDD + kb * 16, LDD, lane);
-            qf[sl][kb] = frag4_row(sQ + tb * 16 * LDD + kb * 16, LDD, lane);
-        }
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-            if (h2 < (tb + 2) / 2) {
-                akw[sl][h2] = frag_row(sAkkw + tb * 16 * LDC + h2 * 32, LDC, lane);
-                aqw[sl][h2] = frag_row(sAqkw + tb * 16 * LDC + h2 * 32, LDC, lane);
-            }
-        }
-        gm[sl] = *reinterpret_cast<const float4*>(sGam + tb * 16 + lg * 4);
-        bb[sl] = *reinterpret_cast<const float4*>(sBv + tb * 16 + lg * 4);
-        go[sl] = sGam[tb * 16 + li];
     };
-    load_b(0, 0);
+    constexpr int AHEAD_A = 3;                      // 4 transpose reads per step
+#pragma unroll
+    for (int ib = 0; ib < AHEAD_A; ++ib)
+        load_kw(ib);
     SCHED_FENCE();
-
-    // ---- a. S <- gamma_C S + KW^T diag(fac) V   (NI independent accumulators)
     bf16x8_t vs[2];
     vs[0] = scale8(vf[0], fc[0], fc[1]);
     vs[1] = scale8(vf[1], fc[2], fc[3]);
 #pragma unroll
-    for (int ib = 0; ib < NI; ++ib)
+    for (int ib = 0; ib < NI; ++ib) {
+        if (ib + AHEAD_A < NI)
+            load_kw(ib + AHEAD_A);
+        SCHED_FENCE();
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             S[ib][r] *= gC;
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int ib = 0; ib < NI; ++ib)
-            S[ib] = mma32(kwf[h2][ib], vs[h2], S[ib]);
-    SCHED_FENCE();
-
-    // ---- b, with the reads of c, d issued beside the third block
-    f32x4_t R[4], OT[4];
-    v4s_t akk[6], td[4], aqk[10];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-        const int sl = tb & 1;
-        if (tb + 1 < 4)
-            load_b(tb + 1, sl ^ 1);
-        if (tb == 2) {
-#pragma unroll
-            for (int i = 1, n = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < i; ++j, ++n)
-                    akk[n] = frag4_row(sAkk + i * 16 * LDC + j * 16, LDC, lane);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                td[i] = TD_IN_AKK ? frag4_row(sAkk + i * 16 * LDC + i * 16, LDC, lane)
-                                  : frag4_row(sTd + i * 16 * LDT, LDT, lane);
-#pragma unroll
-            for (int i = 0, n = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j <= i; ++j, ++n)
-                    aqk[n] = frag4_row(sAqk + i * 16 * LDC + j * 16, LDC, lane);
-        }
+        S[ib] = mma32(kwf[0][ib], vs[0], S[ib]);
+        S[ib] = mma32(kwf[1][ib], vs[1], S[ib]);
         SCHED_FENCE();
-        f32x4_t ra = {0.f, 0.f, 0.f, 0.f}, oa = {0.f, 0.f, 0.f, 0.f};
+    }
+
+    // ---- b, one (16-token block tb, 32-channel pair kp) unit at a time
+    constexpr int NKP = NI / 2;
+    constexpr int NU = 4 * NKP;                     // units
+    v4s_t kf[NU][2], qf[NU][2];
+    bf16x8_t akw[4][2], aqw[4][2];
+    float4 gm[4], bb[4];
+    float go[4];
+    v4s_t akk[6], td[4], aqk[10];
+    auto load_unit = [&](int u) {
+        const int tb = u / NKP, kp = u % NKP;
 #pragma unroll
-        for (int kp = 0; kp < NI / 2; ++kp) {
-            const bf16x8_t s0p = cat8(s0b[2 * kp], s0b[2 * kp + 1]);
-            ra = mma32(cat8(kf[sl][2 * kp], kf[sl][2 * kp + 1]), s0p, ra);   // (K S0)[t][j]
-            oa = mma32(s0p, cat8(qf[sl][2 * kp], qf[sl][2 * kp + 1]), oa);   // (Q S0)^T[j][t]
+        for (int h = 0; h < 2; ++h) {
+            kf[u][h] = frag4_row(sK + tb * 16 * LDD + (2 * kp + h) * 16, LDD, lane);
+            qf[u][h] = frag4_row(sQ + tb * 16 * LDD + (2 * kp + h) * 16, LDD, lane);
         }
-        const float gmv[4] = {gm[sl].x, gm[sl].y, gm[sl].z, gm[sl].w};
-        const float bbv[4] = {bb[sl].x, bb[sl].y, bb[sl].z, bb[sl].w};
+        if (kp == 0) {                              // per-block operands and gates
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            ra[r] *= bbv[r] * gmv[r];
-            oa[r] *= go[sl];
+            for (int h2 = 0; h2 < 2; ++h2) {
+                if (h2 < (tb + 2) / 2) {
+                    akw[tb][h2] = frag_row(sAkkw + tb * 16 * LDC + h2 * 32, LDC, lane);
+                    aqw[tb][h2] = frag_row(sAqkw + tb * 16 * LDC + h2 * 32, LDC, lane);
+                }
+            }
+            gm[tb] = *reinterpret_cast<const float4*>(sGam + tb * 16 + lg * 4);
+            bb[tb] = *reinterpret_cast<const float4*>(sBv + tb * 16 + lg * 4);
+            go[tb] = sGam[tb * 16 + li];
         }
+        // the operands of c and d, spread over the last eight units
+        const int w = u - (NU - 8);
+        if (w >= 0) {
 #pragma unroll
-        for (int h2 = 0; h2 < (tb + 2) / 2; ++h2) {
-            ra = mma32(akw[sl][h2], vf[h2], ra);
-            oa = mma32(vf[h2], aqw[sl][h2], oa);          // (A_qkw V)^T
+            for (int q = 0; q < 3; ++q) {
+                const int idx = w * 3 + q;          // 0 .. 23: akk 0..5, td 6..9, aqk 10..19
+                if (idx < 6) {
+                    const int i2 = idx < 1 ? 1 : idx < 3 ? 2 : 3;
+                    const int j2 = idx - (i2 * (i2 - 1)) / 2;
+                    akk[idx] = frag4_row(sAkk + i2 * 16 * LDC + j2 * 16, LDC, lane);
+                } else if (idx < 10) {
+                    const int i2 = idx - 6;
+                    td[i2] = TD_IN_AKK ? frag4_row(sAkk + i2 * 16 * LDC + i2 * 16, LDC, lane)
+                                       : frag4_row(sTd + i2 * 16 * LDT, LDT, lane);
+                } else if (idx < 20) {
+                    const int n2 = idx - 10;
+                    const int i2 = n2 < 1 ? 0 : n2 < 3 ? 1 : n2 < 6 ? 2 : 3;
+                    const int j2 = n2 - (i2 * (i2 + 1)) / 2;
+                    aqk[n2] = frag4_row(sAqk + i2 * 16 * LDC + j2 * 16, LDC, lane);
+                }
+            }
         }
-        R[tb] = ra;
-        OT[tb] = oa;
+    };
+    f32x4_t R[4], OT[4];
+    constexpr int AHEAD_B = 4;                      // 2 paired reads per unit (+ per-block extras)
+#pragma unroll
+    for (int u = 0; u < AHEAD_B; ++u)
+        load_unit(u);
+    SCHED_FENCE();
+    f32x4_t ra = {0.f, 0.f, 0.f, 0.f}, oa = ra;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int tb = u / NKP, kp = u % NKP;
+        if (u + AHEAD_B < NU)
+            load_unit(u + AHEAD_B);
+        SCHED_FENCE();
+        if (kp == 0) {
+            ra = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            oa = ra;
+        }
+        const bf16x8_t s0p = cat8(s0b[2 * kp], s0b[2 * kp + 1]);
+        ra = mma32(cat8(kf[u][0], kf[u][1]), s0p, ra);        // (K S0)[t][j]
+        oa = mma32(s0p, cat8(qf[u][0], qf[u][1]), oa);        // (Q S0)^T[j][t]
+        if (kp == NKP - 1) {
+            const float gmv[4] = {gm[tb].x, gm[tb].y, gm[tb].z, gm[tb].w};
+            const float bbv[4] = {bb[tb].x, bb[tb].y, bb[tb].z, bb[tb].w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                ra[r] *= bbv[r] * gmv[r];
+                oa[r] *= go[tb];
+            }
+#pragma unroll
+            for (int h2 = 0; h2 < (tb + 2) / 2; ++h2) {
+                ra = mma32(akw[tb][h2], vf[h2], ra);
+                oa = mma32(vf[h2], aqw[tb][h2], oa);          // (A_qkw V)^T
+            }
+            R[tb] = ra;
+            OT[tb] = oa;
+        }
         SCHED_FENCE();
     }
 
