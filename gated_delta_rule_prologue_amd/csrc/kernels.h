@@ -9,7 +9,7 @@ namespace prism {
 struct PrologueArgs {
     bool bf16;
     int n_seqs, total_tokens, heads, dk, L;
-    int strip;                      // tokens walked by one thread
+    int strip;                      // tokens walked by one thread: 4, 8 or 16
     bool narrow;                    // 8-byte instead of 16-byte channel groups
     const void *k, *u, *a, *h, *b, *conv_w;
     const int32_t* cu_seqlens;

@@ -130,8 +130,8 @@ prism_status prism_prologue(const prism_dims* d, const void* k, const void* u, c
     p.heads = d->heads;
     p.dk = d->dk;
     p.L = L;
-    p.strip = env_int("PRISM_PROLOGUE_STRIP", 8);
-    if (p.strip < 1)
+    p.strip = env_int("PRISM_PROLOGUE_STRIP", 8);      // 4, 8 or 16 tokens per thread
+    if (p.strip != 4 && p.strip != 16)
         p.strip = 8;
     p.narrow = env_int("PRISM_PROLOGUE_NARROW", 0) != 0;
     p.k = k; p.u = u; p.a = a; p.h = h; p.b = b; p.conv_w = conv_w;

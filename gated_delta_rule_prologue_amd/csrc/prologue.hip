@@ -19,10 +19,13 @@
 //     load instruction covers whole 256-byte rows of k, u, a, h;
 //   * k, u, a, h are streamed with nontemporal loads (read exactly once);
 //     the write keys are stored normally because the scan reads them next;
-//   * L is a template parameter: the level loop unrolls completely and h's
-//     last slot (never read by the closed form) is never loaded;
+//   * L and the strip length are template parameters: the level loop and the
+//     token loop unroll completely, h's last slot (never read by the closed
+//     form) is never loaded, and the inputs of token t + 1 are loaded while
+//     token t is computed (two register sets, alternating);
 //   * sequence boundaries come from cu_seqlens on the device (binary search
-//     once per strip, then a forward walk), so no host synchronisation.
+//     once per strip, then a forward walk that marks the sequence starts in
+//     the strip), so no host synchronisation and no reads inside the loop.
 #include "common.h"
 #include "kernels.h"
 
@@ -88,13 +91,14 @@ template <typename T, int N> struct Lane {
     }
 };
 
-template <typename T, int L, int V>
+template <typename T, int L, int V, int STRIP>
 __global__ __launch_bounds__(256) void prologue_kernel(
     const T* __restrict__ k, const T* __restrict__ u, const T* __restrict__ a,
     const T* __restrict__ h, const T* __restrict__ b, const T* __restrict__ conv_w,
     const int32_t* __restrict__ cu, int n_seqs, int T_total, int H, int dk,
-    int strip, T* __restrict__ kw)
+    T* __restrict__ kw)
 {
+    constexpr int strip = STRIP;
     using LV = Lane<T, V>;
     const int groups = H * dk / V;                       // channel groups per token row
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -140,36 +144,77 @@ __global__ __launch_bounds__(256) void prologue_kernel(
     if (t0 - 2 >= seq_start) LV::load(k + (int64_t)(t0 - 2) * row + koff, x2);
     if (t0 - 3 >= seq_start) LV::load(k + (int64_t)(t0 - 3) * row + koff, x3);
 
-    for (int t = t0; t < t1; ++t) {
-        if (t == next_start) {                           // a new sequence starts at t
-            while (cu[n + 1] <= t) ++n;                  // skips empty sequences; n+1 <= n_seqs
-            next_start = cu[n + 1];
+    // Software pipeline over the strip: the raw inputs of token t + 1 are in
+    // flight while token t is computed, so a thread always has two tokens of
+    // loads outstanding.
+    using R = Raw<LV::B, true>;
+    using RV = typename R::V;
+    struct In {
+        RV k, a[L > 1 ? L - 1 : 1], u[L > 1 ? L - 1 : 1], h[L > 2 ? L - 2 : 1];
+        T b;
+    };
+    auto fetch = [&](int t, In& x) {
+        x.k = R::ld(k + (int64_t)t * row + koff);
+        x.b = b[(int64_t)t * H + e];
+        const T* ub = u + (int64_t)t * lrow + loff;
+        const T* ab = a + (int64_t)t * lrow + loff;
+        const T* hb = h + (int64_t)t * lrow + loff;
+#pragma unroll
+        for (int s = 0; s < L - 1; ++s) {
+            x.a[s] = R::ld(ab + s * dk);
+            x.u[s] = R::ld(ub + s * dk);
+            if (s < L - 2)
+                x.h[s] = R::ld(hb + s * dk);
+        }
+    };
+    auto unpack = [&](const RV& v, float* out) {
+        constexpr int W = LV::B / 4;
+#pragma unroll
+        for (int i = 0; i < W; ++i) {
+            if constexpr (sizeof(T) == 2) {
+                out[2 * i] = __uint_as_float(v[i] << 16);
+                out[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+            } else {
+                out[i] = __uint_as_float(v[i]);
+            }
+        }
+    };
+
+    // tokens of the strip where a new sequence starts (bit t - t0), found before
+    // the token loop so that the loop itself reads nothing but the inputs
+    uint32_t resets = 0;
+    for (int ns = next_start; ns < t1;) {               // ns > t0: t0 < cu[n + 1]
+        resets |= 1u << (ns - t0);
+        ++n;
+        while (cu[n + 1] <= ns) ++n;                     // skips empty sequences; n+1 <= n_seqs
+        ns = cu[n + 1];
+    }
+
+    auto step = [&](int t, const In& x) {
+        if ((resets >> (t - t0)) & 1u) {                 // a new sequence starts at t
 #pragma unroll
             for (int c = 0; c < V; ++c) { x1[c] = 0.f; x2[c] = 0.f; x3[c] = 0.f; }
         }
         float kt[V];
-        LV::template load<true>(k + (int64_t)t * row + koff, kt);
-        const float bt = to_f32(b[(int64_t)t * H + e]);
+        unpack(x.k, kt);
+        const float bt = to_f32(x.b);
         float acc[V], r[V];
 #pragma unroll
         for (int c = 0; c < V; ++c) {
             r[c] = w[c][3] * kt[c] + w[c][2] * x1[c] + w[c][1] * x2[c] + w[c][0] * x3[c];
             acc[c] = bt * kt[c];
         }
-        const T* ub = u + (int64_t)t * lrow + loff;
-        const T* ab = a + (int64_t)t * lrow + loff;
-        const T* hb = h + (int64_t)t * lrow + loff;
 #pragma unroll
         for (int s = 0; s < L - 1; ++s) {                // level l = s + 1
             float av[V], uv[V];
-            LV::template load<true>(ab + s * dk, av);
-            LV::template load<true>(ub + s * dk, uv);
+            unpack(x.a[s], av);
+            unpack(x.u[s], uv);
 #pragma unroll
             for (int c = 0; c < V; ++c)
                 acc[c] += av[c] * r[c] * uv[c];
             if (s < L - 2) {                             // residual for the next level
                 float hv[V];
-                LV::template load<true>(hb + s * dk, hv);
+                unpack(x.h[s], hv);
 #pragma unroll
                 for (int c = 0; c < V; ++c)
                     r[c] *= 1.f - av[c] * hv[c];
@@ -178,23 +223,48 @@ __global__ __launch_bounds__(256) void prologue_kernel(
         LV::store(kw + (int64_t)t * row + koff, acc);
 #pragma unroll
         for (int c = 0; c < V; ++c) { x3[c] = x2[c]; x2[c] = x1[c]; x1[c] = kt[c]; }
+    };
+
+    // Two register sets used alternately over the fully unrolled strip: no
+    // loop-carried copies (which would wait for the loads just issued), and the
+    // prefetches are unconditional (past a short strip's end they re-read its
+    // last token), so every wait is for the older set only.
+    In X[2];
+    fetch(t0, X[0]);
+#pragma unroll
+    for (int i = 0; i < STRIP; ++i) {
+        if (i + 1 < STRIP)
+            fetch(min(t0 + i + 1, t1 - 1), X[(i + 1) & 1]);
+        if (t0 + i < t1)
+            step(t0 + i, X[i & 1]);
     }
 }
 
-template <typename T, int L, int V>
-static hipError_t launch_LV(const PrologueArgs& p, hipStream_t stream)
+template <typename T, int L, int V, int S>
+static hipError_t launch_LVS(const PrologueArgs& p, hipStream_t stream)
 {
     const int64_t groups = (int64_t)p.heads * p.dk / V;
-    const int64_t strips = (p.total_tokens + p.strip - 1) / p.strip;
+    const int64_t strips = (p.total_tokens + S - 1) / S;
     const int64_t threads = groups * strips;
     if (threads == 0)
         return hipSuccess;
     const int64_t blocks = (threads + 255) / 256;
-    hipLaunchKernelGGL((prologue_kernel<T, L, V>), dim3((unsigned)blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((prologue_kernel<T, L, V, S>), dim3((unsigned)blocks), dim3(256), 0, stream,
                        (const T*)p.k, (const T*)p.u, (const T*)p.a, (const T*)p.h, (const T*)p.b,
                        (const T*)p.conv_w, p.cu_seqlens, p.n_seqs, p.total_tokens, p.heads, p.dk,
-                       p.strip, (T*)p.kw);
+                       (T*)p.kw);
     return hipGetLastError();
+}
+
+// Tokens per thread: 4, 8 (default) or 16.
+template <typename T, int L, int V>
+static hipError_t launch_LV(const PrologueArgs& p, hipStream_t stream)
+{
+    if (p.strip == 4)
+        return launch_LVS<T, L, V, 4>(p, stream);
+    if (p.strip == 16)
+        return launch_LVS<T, L, V, 16>(p, stream);
+    return launch_LVS<T, L, V, 8>(p, stream);
 }
 
 // Channels per thread: 16-byte or 8-byte accesses (the narrow form halves the
