@@ -214,24 +214,33 @@ __device__ __forceinline__ void state_path(
         for (int h2 = 0; h2 < 2; ++h2)
             kwf[h2][ib] = frag_col(sKW + h2 * 32 * LDD + ib * 16, LDD, lane);
     };
-    constexpr int AHEAD_A = 3;                      // 4 transpose reads per step
-#pragma unroll
-    for (int ib = 0; ib < AHEAD_A; ++ib)
-        load_kw(ib);
+    // two 16-row blocks per step, so that each accumulator's second product is
+    // not issued right behind its first (a dependent 16x16x32 product waits for
+    // its predecessor's result)
+    load_kw(0);
+    load_kw(1);
+    load_kw(2);
+    load_kw(3);
     SCHED_FENCE();
     bf16x8_t vs[2];
     vs[0] = scale8(vf[0], fc[0], fc[1]);
     vs[1] = scale8(vf[1], fc[2], fc[3]);
 #pragma unroll
-    for (int ib = 0; ib < NI; ++ib) {
-        if (ib + AHEAD_A < NI)
-            load_kw(ib + AHEAD_A);
+    for (int ib = 0; ib < NI; ib += 2) {
+        if (ib + 4 < NI) {
+            load_kw(ib + 4);
+            load_kw(ib + 5);
+        }
         SCHED_FENCE();
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+        for (int r = 0; r < 4; ++r) {
             S[ib][r] *= gC;
+            S[ib + 1][r] *= gC;
+        }
         S[ib] = mma32(kwf[0][ib], vs[0], S[ib]);
+        S[ib + 1] = mma32(kwf[0][ib + 1], vs[0], S[ib + 1]);
         S[ib] = mma32(kwf[1][ib], vs[1], S[ib]);
+        S[ib + 1] = mma32(kwf[1][ib + 1], vs[1], S[ib + 1]);
         SCHED_FENCE();
     }
 
