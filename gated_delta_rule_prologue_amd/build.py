@@ -73,11 +73,17 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     for src, out in asm.items():
-        bad = check_isa.scan(open(out).read())
+        text = open(out).read()
+        bad = check_isa.scan(text)
         if bad:
             lines = "\n".join(f"  {f[:70]}: {i}" for f, i in bad[:10])
             raise RuntimeError(f"{src}: a 16x16x16 MFMA overlaps the result of an in-flight "
                                f"16x16x32 MFMA (see check_isa.py):\n{lines}")
+        bad = check_isa.scan_dpp(text)
+        if bad:
+            lines = "\n".join(f"  {f[:70]}: {i}" for f, i in bad[:10])
+            raise RuntimeError(f"{src}: a DPP source is read fewer than two wait states after "
+                               f"its VALU write (see check_isa.py):\n{lines}")
     tmp = LIB + ".tmp%d" % os.getpid()
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)

@@ -7,6 +7,12 @@ two products had different shapes (16x16x16 after 16x16x32 or the reverse):
 their write-backs to the shared registers race.  Same-shape pairs laid out
 this way are frequent in correct builds and are left alone.  Every kernel is
 scanned for a mixed-shape pair; the build fails if one is found.
+
+A DPP instruction reads its first source through the cross-lane network, which
+needs two wait states after a VALU write of that register; the hardware does
+not insert them.  The compiler does for its own DPP instructions, but not for
+hand-written ones inside inline asm (the block inverse of the scan), so every
+DPP instruction is checked against the two instructions before it.
 """
 import re
 import sys
@@ -45,8 +51,60 @@ def scan(asm_text: str):
     return bad
 
 
+_VR = re.compile(r"v\[(\d+):(\d+)\]")
+_V1 = re.compile(r"v(\d+)$")
+
+
+def _vgprs(op: str):
+    op = op.strip().lstrip("-|")
+    m = _VR.match(op)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = _V1.match(op)
+    return {int(m.group(1))} if m else set()
+
+
+def scan_dpp(asm_text: str):
+    """DPP instructions whose first source was written by a VALU instruction
+    fewer than two wait states before (s_nop N counts N + 1)."""
+    bad = []
+    hist = []        # (mnemonic, VGPRs written or s_nop count) of the last instructions
+    func = "?"
+    for line in asm_text.splitlines():
+        m = re.match(r"^(_Z\S+):", line)
+        if m:
+            func, hist = m.group(1), []
+            continue
+        s = line.split(";")[0].strip()
+        if not s or s.startswith(".") or s.endswith(":"):
+            continue
+        for ins in s.split("\n"):
+            mnem, _, rest = ins.strip().partition(" ")
+            ops = [o for o in rest.split(",")] if rest else []
+            if "_dpp" in mnem and len(ops) >= 2:
+                src = _vgprs(ops[1])
+                ws = 0
+                for pm, pw in reversed(hist):
+                    if ws >= 2:
+                        break
+                    if pm == "s_nop":
+                        ws += pw + 1
+                        continue
+                    if pm.startswith("v_") and pw & src:
+                        bad.append((func, ins.strip()))
+                        break
+                    ws += 1
+            if mnem == "s_nop":
+                hist.append(("s_nop", int(ops[0], 0) if ops else 0))
+            else:
+                hist.append((mnem, _vgprs(ops[0]) if mnem.startswith("v_") and ops else set()))
+            hist = hist[-8:]
+    return bad
+
+
 if __name__ == "__main__":
-    found = scan(open(sys.argv[1]).read())
+    text = open(sys.argv[1]).read()
+    found = scan(text) + scan_dpp(text)
     for f, i in found:
         print(f[:80], i)
     print(len(found), "suspect instructions")

@@ -42,6 +42,7 @@ constexpr int kThreads = 256;
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 typedef short v8s_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
+typedef __attribute__((address_space(3))) int lds_int_t;
 
 __device__ __forceinline__ v4s_t lds_read_tr(const uint16_t* p)
 {
@@ -96,6 +97,24 @@ __device__ __forceinline__ float wave_inclusive_sum(float v)
 __device__ __forceinline__ bf16x8_t cat8(v4s_t lo, v4s_t hi)
 {
     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Two 16x16x16 operand fragments of consecutive 16-row blocks (rows 4g .. 4g+3
+// of `lo` and of `hi` in lane group g = lane / 16) as one 16x16x32 fragment
+// holding rows 8g .. 8g+7 of the 32-row pair in lane group g, so that it pairs
+// with a plain 16-byte row read of the other operand.  Per dword:
+// v_permlane32_swap exchanges lane groups 2, 3 of lo with groups 0, 1 of hi,
+// giving (lo0 lo1 hi0 hi1 | lo2 lo3 hi2 hi3); v_permlane16_swap then exchanges
+// the odd groups of the first with the even groups of the second, giving
+// (lo0 lo2 hi0 hi2 | lo1 lo3 hi1 hi3): rows 8g .. 8g+3 and 8g+4 .. 8g+7.
+__device__ __forceinline__ bf16x8_t pair_rows(v4s_t lo, v4s_t hi)
+{
+    const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+    const auto x0 = __builtin_amdgcn_permlane32_swap(a.x, b.x, false, false);
+    const auto y0 = __builtin_amdgcn_permlane16_swap(x0[0], x0[1], false, false);
+    const auto x1 = __builtin_amdgcn_permlane32_swap(a.y, b.y, false, false);
+    const auto y1 = __builtin_amdgcn_permlane16_swap(x1[0], x1[1], false, false);
+    return __builtin_bit_cast(bf16x8_t, make_uint4(y0[0], y1[0], y0[1], y1[1]));
 }
 
 __device__ __forceinline__ f32x4_t mma32(bf16x8_t a, bf16x8_t b, f32x4_t c)
@@ -176,22 +195,19 @@ __device__ __forceinline__ bf16x8_t scale8(bf16x8_t x, float4 f0, float4 f1)
 // lane holds four consecutive value columns of one token (8-byte stores).
 // All tiles are bf16 in LDS with the strides of Layout; S is fp32 in accumulators.
 // T_ii is read from sTd, or with TD_IN_AKK from the diagonal blocks of A_kk
-// (which the state path never needs otherwise).
-template <int D, int DVS, bool TD_IN_AKK = false>
-__device__ __forceinline__ void state_path(
-    f32x4_t (&S)[D / 16], const uint16_t* sQ, const uint16_t* sK, const uint16_t* sKW,
-    const uint16_t* sV, const uint16_t* sAkk, const uint16_t* sAkkw, const uint16_t* sAqkw,
-    const uint16_t* sAqk, const uint16_t* sTd, const float* sBv, const float* sGam,
-    const float* sFac, float gC, uint16_t* o, int c0, int nt, int64_t rowV, int e, int DV,
-    int j0, int jb, int lane)
+// (which the state path never needs otherwise), which then hold T_ii transposed.
+// a. S <- gamma_C S + KW^T diag(fac) V for value columns 16 jb .. 16 jb + 15;
+// first captures S0 (the state before the update) as bf16 16x16x16 operands in
+// s0b and leaves the V fragments in vf for b.
+template <int D, int DVS>
+__device__ __forceinline__ void a_step(f32x4_t (&S)[D / 16], v4s_t (&s0b)[D / 16], bf16x8_t (&vf)[2],
+                                       const uint16_t* sKW, const uint16_t* sV, const float* sFac,
+                                       float gC, int jb, int lane)
 {
     using Ly = Layout<D, DVS>;
-    constexpr int LDD = Ly::LDD, LDC = Ly::LDC, LDV = Ly::LDV, LDT = Ly::LDT;
+    constexpr int LDD = Ly::LDD, LDV = Ly::LDV;
     constexpr int NI = D / 16;
-    const int li = lane & 15, lg = lane >> 4;
-
-    // S0 as bf16 16x16x16 operands
-    v4s_t s0b[NI];
+    const int lg = lane >> 4;
 #pragma unroll
     for (int ib = 0; ib < NI; ++ib)
         s0b[ib] = as_b16(S[ib], 1.f, 1.f, 1.f, 1.f);
@@ -199,9 +215,7 @@ __device__ __forceinline__ void state_path(
     // LDS reads run a short, fixed distance ahead of their MFMAs: a wavefront
     // can wait precisely only for the oldest of at most 15 outstanding reads,
     // so each batch is kept small and issued a few steps before its use.
-
-    // ---- a. S <- gamma_C S + KW^T diag(fac) V   (NI independent accumulators)
-    bf16x8_t vf[2], kwf[2][NI];
+    bf16x8_t kwf[2][NI];
     float4 fc[4];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
@@ -243,22 +257,43 @@ __device__ __forceinline__ void state_path(
         S[ib + 1] = mma32(kwf[1][ib + 1], vs[1], S[ib + 1]);
         SCHED_FENCE();
     }
+}
+
+// With SPLIT the a-step has already run (a_step, which filled s0b and vf);
+// otherwise state_path runs it first.
+template <int D, int DVS, bool TD_IN_AKK = false, bool SPLIT = false>
+__device__ __forceinline__ void state_path(
+    f32x4_t (&S)[D / 16], v4s_t (&s0b)[D / 16], bf16x8_t (&vf)[2], const uint16_t* sQ,
+    const uint16_t* sK, const uint16_t* sKW,
+    const uint16_t* sV, const uint16_t* sAkk, const uint16_t* sAkkw, const uint16_t* sAqkw,
+    const uint16_t* sAqk, const uint16_t* sTd, const float* sBv, const float* sGam,
+    const float* sFac, float gC, uint16_t* o, int c0, int nt, int64_t rowV, int e, int DV,
+    int j0, int jb, int lane)
+{
+    using Ly = Layout<D, DVS>;
+    constexpr int LDD = Ly::LDD, LDC = Ly::LDC, LDT = Ly::LDT;
+    constexpr int NI = D / 16;
+    const int li = lane & 15, lg = lane >> 4;
+    if constexpr (!SPLIT)
+        a_step<D, DVS>(S, s0b, vf, sKW, sV, sFac, gC, jb, lane);
 
     // ---- b, one (16-token block tb, 32-channel pair kp) unit at a time
     constexpr int NKP = NI / 2;
     constexpr int NU = 4 * NKP;                     // units
-    v4s_t kf[NU][2], qf[NU][2];
+    // S0 as 16x16x32 operands pairing with 16-byte row reads of K and Q
+    bf16x8_t s0q[NKP];
+#pragma unroll
+    for (int kp = 0; kp < NKP; ++kp)
+        s0q[kp] = pair_rows(s0b[2 * kp], s0b[2 * kp + 1]);
+    bf16x8_t kf[NU], qf[NU];
     bf16x8_t akw[4][2], aqw[4][2];
     float4 gm[4], bb[4];
     float go[4];
     v4s_t akk[6], td[4], aqk[10];
     auto load_unit = [&](int u) {
         const int tb = u / NKP, kp = u % NKP;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            kf[u][h] = frag4_row(sK + tb * 16 * LDD + (2 * kp + h) * 16, LDD, lane);
-            qf[u][h] = frag4_row(sQ + tb * 16 * LDD + (2 * kp + h) * 16, LDD, lane);
-        }
+        kf[u] = frag_row(sK + tb * 16 * LDD + kp * 32, LDD, lane);
+        qf[u] = frag_row(sQ + tb * 16 * LDD + kp * 32, LDD, lane);
         if (kp == 0) {                              // per-block operands and gates
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
@@ -271,27 +306,31 @@ __device__ __forceinline__ void state_path(
             bb[tb] = *reinterpret_cast<const float4*>(sBv + tb * 16 + lg * 4);
             go[tb] = sGam[tb * 16 + li];
         }
-        // the operands of c and d, spread over the last eight units
-        const int w = u - (NU - 8);
+        // the operands of c, spread over the last five units
+        const int w = u - (NU - 5);
         if (w >= 0) {
 #pragma unroll
-            for (int q = 0; q < 3; ++q) {
-                const int idx = w * 3 + q;          // 0 .. 23: akk 0..5, td 6..9, aqk 10..19
+            for (int q = 0; q < 2; ++q) {
+                const int idx = w * 2 + q;          // 0 .. 9: akk 0..5, td 6..9
                 if (idx < 6) {
                     const int i2 = idx < 1 ? 1 : idx < 3 ? 2 : 3;
                     const int j2 = idx - (i2 * (i2 - 1)) / 2;
                     akk[idx] = frag4_row(sAkk + i2 * 16 * LDC + j2 * 16, LDC, lane);
                 } else if (idx < 10) {
                     const int i2 = idx - 6;
-                    td[i2] = TD_IN_AKK ? frag4_row(sAkk + i2 * 16 * LDC + i2 * 16, LDC, lane)
+                    td[i2] = TD_IN_AKK ? frag4_col(sAkk + i2 * 16 * LDC + i2 * 16, LDC, lane)
                                        : frag4_row(sTd + i2 * 16 * LDT, LDT, lane);
-                } else if (idx < 20) {
-                    const int n2 = idx - 10;
-                    const int i2 = n2 < 1 ? 0 : n2 < 3 ? 1 : n2 < 6 ? 2 : 3;
-                    const int j2 = n2 - (i2 * (i2 + 1)) / 2;
-                    aqk[n2] = frag4_row(sAqk + i2 * 16 * LDC + j2 * 16, LDC, lane);
                 }
             }
+        }
+    };
+    // the operands of d, read while c runs
+    auto load_aqk = [&]() {
+#pragma unroll
+        for (int n2 = 0; n2 < 10; ++n2) {
+            const int i2 = n2 < 1 ? 0 : n2 < 3 ? 1 : n2 < 6 ? 2 : 3;
+            const int j2 = n2 - (i2 * (i2 + 1)) / 2;
+            aqk[n2] = frag4_row(sAqk + i2 * 16 * LDC + j2 * 16, LDC, lane);
         }
     };
     f32x4_t R[4], OT[4];
@@ -311,9 +350,8 @@ __device__ __forceinline__ void state_path(
             ra = f32x4_t{0.f, 0.f, 0.f, 0.f};
             oa = ra;
         }
-        const bf16x8_t s0p = cat8(s0b[2 * kp], s0b[2 * kp + 1]);
-        ra = mma32(cat8(kf[u][0], kf[u][1]), s0p, ra);        // (K S0)[t][j]
-        oa = mma32(s0p, cat8(qf[u][0], qf[u][1]), oa);        // (Q S0)^T[j][t]
+        ra = mma32(kf[u], s0q[kp], ra);                       // (K S0)[t][j]
+        oa = mma32(s0q[kp], qf[u], oa);                       // (Q S0)^T[j][t]
         if (kp == NKP - 1) {
             const float gmv[4] = {gm[tb].x, gm[tb].y, gm[tb].z, gm[tb].w};
             const float bbv[4] = {bb[tb].x, bb[tb].y, bb[tb].z, bb[tb].w};
@@ -333,17 +371,19 @@ __device__ __forceinline__ void state_path(
         SCHED_FENCE();
     }
 
-    // reads for e (first two blocks) and its scales
-    v4s_t ke[4][NI];
+    // reads for e (first 32 tokens) and its scales: K^T fragments with tokens
+    // 8g .. 8g+7 of each 32-token pair in lane group g
+    bf16x8_t ke[2][NI];
     float4 fe[4];
-    auto load_e = [&](int tb) {
+    auto load_e = [&](int tp) {
 #pragma unroll
         for (int ib = 0; ib < NI; ++ib)
-            ke[tb][ib] = frag4_col(sK + tb * 16 * LDD + ib * 16, LDD, lane);
-        fe[tb] = *reinterpret_cast<const float4*>(sFac + tb * 16 + lg * 4);
+            ke[tp][ib] = frag_col(sK + tp * 32 * LDD + ib * 16, LDD, lane);
+        fe[2 * tp] = *reinterpret_cast<const float4*>(sFac + tp * 32 + lg * 4);
+        fe[2 * tp + 1] = *reinterpret_cast<const float4*>(sFac + tp * 32 + 16 + lg * 4);
     };
     load_e(0);
-    load_e(1);
+    load_aqk();
     SCHED_FENCE();
 
     // ---- c. X_i = T_ii (R_i - sum_{j<i} A_ij X_j)   (16x16x16, B operands from registers)
@@ -361,8 +401,7 @@ __device__ __forceinline__ void state_path(
         nX[i] = as_b16(x, -1.f, -1.f, -1.f, -1.f);
     }
     SCHED_FENCE();
-    load_e(2);
-    load_e(3);
+    load_e(1);
     SCHED_FENCE();
 
     // ---- d. O^T += X^T (-A_qk)^T; token rows past the chunk's last token fall
@@ -399,12 +438,13 @@ __device__ __forceinline__ void state_path(
     // ---- e. S <- S - K^T diag(fac) X   (NI independent accumulators per block)
 #pragma unroll
     for (int tp = 0; tp < 2; ++tp) {
-        const bf16x8_t bx = cat8(as_b16(X[2 * tp], -fe[2 * tp].x, -fe[2 * tp].y, -fe[2 * tp].z, -fe[2 * tp].w),
-                                 as_b16(X[2 * tp + 1], -fe[2 * tp + 1].x, -fe[2 * tp + 1].y,
-                                        -fe[2 * tp + 1].z, -fe[2 * tp + 1].w));
+        const bf16x8_t bx = pair_rows(
+            as_b16(X[2 * tp], -fe[2 * tp].x, -fe[2 * tp].y, -fe[2 * tp].z, -fe[2 * tp].w),
+            as_b16(X[2 * tp + 1], -fe[2 * tp + 1].x, -fe[2 * tp + 1].y, -fe[2 * tp + 1].z,
+                   -fe[2 * tp + 1].w));
 #pragma unroll
         for (int ib = 0; ib < NI; ++ib)
-            S[ib] = mma32(cat8(ke[2 * tp][ib], ke[2 * tp + 1][ib]), bx, S[ib]);
+            S[ib] = mma32(ke[tp][ib], bx, S[ib]);
     }
 }
 
@@ -628,10 +668,13 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(
         lds_barrier();
 
         // ================= 3. state path: wavefront jb, value columns 16 jb .. 16 jb + 15 =================
-        if (wave < NJ)
-            state_path<D, DVS>(S, sQ, sK, sKW, sV, sAkk, sAkkw, sAqkw, sAqk, sTd, sBv, sGam,
+        if (wave < NJ) {
+            v4s_t s0b[D / 16];
+            bf16x8_t vf[2];
+            state_path<D, DVS>(S, s0b, vf, sQ, sK, sKW, sV, sAkk, sAkkw, sAqkw, sAqk, sTd, sBv, sGam,
                                sFac, __builtin_amdgcn_exp2f(lamC), o, c0, nt, rowV, e, DV, j0, wave,
                                lane);
+        }
         lds_barrier();
     }
 
@@ -698,10 +741,11 @@ struct LayoutWS {
     static constexpr int oAkkw = oAkk + L::szM;
     static constexpr int oAqkw = oAkkw + L::szM;
     static constexpr int oAqk = oAqkw + L::szM;              // holds -A_qk
-    static constexpr int oG = oAqk + L::szM;                 // b, gamma, gamma_C / gamma
-    static constexpr int oScr = oG + 3 * kC * 4;             // A_ii rows for the inverses
+    static constexpr int oG = oAqk + L::szM;                 // b, gamma, gamma_C / gamma; two chunks
+    static constexpr int oScr = oG + 2 * 3 * kC * 4;         // A_ii rows for the inverses
     static constexpr int oLam = oScr + 4 * 16 * 16 * 2;      // log2 decay sums, one slot per helper
-    static constexpr int total = oLam + 3 * kC * 4;
+    static constexpr int oFlag = oLam + 4 * kC * 4;          // scratch-ready flags (eight waves)
+    static constexpr int total = oFlag + 16;
     static_assert(szRows % 16 == 0 && oAkk % 16 == 0 && oG % 16 == 0 && oScr % 16 == 0 &&
                   oLam % 16 == 0, "alignment");
 };
@@ -730,15 +774,23 @@ struct WsBuf {
     __device__ uint16_t* Akkw() const { return reinterpret_cast<uint16_t*>(base + Ly::oAkkw); }
     __device__ uint16_t* Aqkw() const { return reinterpret_cast<uint16_t*>(base + Ly::oAqkw); }
     __device__ uint16_t* Aqk() const { return reinterpret_cast<uint16_t*>(base + Ly::oAqk); }
-    __device__ float* G() const { return reinterpret_cast<float*>(base + Ly::oG); }
+    __device__ float* G(int c) const { return reinterpret_cast<float*>(base + Ly::oG) + (c & 1) * 3 * kC; }
     __device__ uint16_t* Scr() const { return reinterpret_cast<uint16_t*>(base + Ly::oScr); }
     __device__ float* Lam(int slot) const { return reinterpret_cast<float*>(base + Ly::oLam) + slot * kC; }
+    // volatile LDS words (explicitly in the LDS address space: volatile accesses
+    // through a generic pointer would become flat accesses)
+    __device__ volatile lds_int_t* Flag(int i) const
+    {
+        return (volatile lds_int_t*)(reinterpret_cast<int*>(base + Ly::oFlag) + i);
+    }
 };
 
-// Gram pairs (t-block, s-block) of each helper role, ordered by t-block: role 0
-// takes the four diagonal pairs (their A_kk blocks go to the inverse scratch)
-// and (1, 0), and publishes the gates; the other off-diagonal pairs go to one
-// helper (role 1) or are split over two (roles 2, 3).
+// Gram pairs (t-block, s-block) of each helper role, ordered by t-block.  With
+// four wavefronts, role 0 takes the four diagonal pairs (their A_kk blocks go
+// to the inverse scratch) and (1, 0); the other off-diagonal pairs go to one
+// helper (role 1) or are split over two (roles 2, 3).  With eight wavefronts
+// the ten pairs are split over roles 4, 6, 5 and 3, and role 7 (no pairs) only
+// moves rows.
 template <int ROLE> struct Pairs;
 template <> struct Pairs<0> {
     static constexpr int n = 5;
@@ -756,6 +808,22 @@ template <> struct Pairs<3> {
     static constexpr int n = 3;
     static constexpr int t[3] = {3, 3, 3}, s[3] = {0, 1, 2};
 };
+template <> struct Pairs<4> {
+    static constexpr int n = 2;
+    static constexpr int t[2] = {0, 1}, s[2] = {0, 1};
+};
+template <> struct Pairs<5> {
+    static constexpr int n = 2;
+    static constexpr int t[2] = {2, 3}, s[2] = {2, 3};
+};
+template <> struct Pairs<6> {
+    static constexpr int n = 3;
+    static constexpr int t[3] = {1, 2, 2}, s[3] = {0, 0, 1};
+};
+template <> struct Pairs<7> {
+    static constexpr int n = 0;
+    static constexpr int t[1] = {0}, s[1] = {0};
+};
 
 // Unit lower-triangular 16x16 inverse, four blocks per wavefront: lane
 // (16 g + i) holds row i of the strictly lower block A_g in a[] and returns
@@ -763,15 +831,23 @@ template <> struct Pairs<3> {
 // updates x[r] -= A_g[r][c] x[c] for r > c with one v_fmac_f32 each, the entry
 // A_g[r][c] coming from lane 16 g + r through a DPP row broadcast of a[c]
 // (`row_newbcast`, which the compiler does not fuse into the FMA by itself).
-// a[] is complete before the first step; the s_nop covers the two wait states a
-// DPP read needs after a VALU write of its source.
+// A DPP read needs two wait states after a VALU write of its source, and the
+// hardware does not enforce them; the compiler does not see into the asm, so
+// the first FMA of each step carries its own s_nop in the same statement (the
+// compiler may place the write of a[c] right before it).  The later FMAs of the
+// step read the same register.
 template <int C, int R>
 __device__ __forceinline__ void subst_col(float (&x)[16], float ac, float xc)
 {
     if constexpr (R < 16) {
-        asm volatile("v_fmac_f32_dpp %0, %1, -%2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
-                     : "+v"(x[R])
-                     : "v"(ac), "v"(xc), "i"(R));
+        if constexpr (R == C + 1)
+            asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %1, -%2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                         : "+v"(x[R])
+                         : "v"(ac), "v"(xc), "i"(R));
+        else
+            asm volatile("v_fmac_f32_dpp %0, %1, -%2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                         : "+v"(x[R])
+                         : "v"(ac), "v"(xc), "i"(R));
         subst_col<C, R + 1>(x, ac, xc);
     }
 }
@@ -779,24 +855,19 @@ template <int C>
 __device__ __forceinline__ void subst(float (&x)[16], const float (&a)[16])
 {
     if constexpr (C < 15) {
-        asm volatile("s_nop 1");
         subst_col<C, C + 1>(x, a[C], x[C]);
         subst<C + 1>(x, a);
     }
 }
 
-// T_g = (I + A_g)^-1 for the four diagonal blocks of A_kk: scr holds the strictly
-// lower blocks A_g row-major (rows of 16 bf16, block g at row 16 g); column i of
-// T_g goes to the diagonal block g of Akk (row stride LDC).  One wavefront.
-template <int LDC>
-__device__ __forceinline__ void invert_diag(const uint16_t* scr, uint16_t* Akk, int lane)
+// Column li of (I + A)^-1 for a strictly lower 16x16 block A whose row li (16
+// bf16) is at `row`; lanes 16 g .. 16 g + 15 must hold the rows of one block.
+__device__ __forceinline__ void invert_cols(const uint16_t* row, float (&x)[16], int li)
 {
-    const int li = lane & 15, lg = lane >> 4;
-    const uint16_t* row = scr + lane * 16;
     const uint4 w0 = *reinterpret_cast<const uint4*>(row);
     const uint4 w1 = *reinterpret_cast<const uint4*>(row + 8);
     const uint32_t wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-    float a[16], x[16];
+    float a[16];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         a[2 * j] = __uint_as_float(wv[j] << 16);
@@ -806,16 +877,42 @@ __device__ __forceinline__ void invert_diag(const uint16_t* scr, uint16_t* Akk, 
     for (int r = 0; r < 16; ++r)
         x[r] = (r == li) ? 1.f : 0.f;
     subst<0>(x, a);
-    uint16_t* Tc = Akk + (lg * 16) * LDC + lg * 16 + li;
+}
+
+// Column i of a block inverse as row i of the transposed block (two 16-byte stores).
+__device__ __forceinline__ void store_trow(uint16_t* p, const float (&x)[16])
+{
+    uint32_t w[8];
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-        Tc[r * LDC] = f32_to_bf16(x[r]);
+    for (int r = 0; r < 8; ++r)
+        w[r] = pack_bf16x2(x[2 * r], x[2 * r + 1]);
+    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(p + 8) = make_uint4(w[4], w[5], w[6], w[7]);
+}
+
+// T_g = (I + A_g)^-1 for the four diagonal blocks of A_kk: scr holds the strictly
+// lower blocks A_g row-major (rows of 16 bf16, block g at row 16 g); T_g goes
+// transposed into the diagonal block g of Akk (row stride LDC).  One wavefront.
+template <int LDC>
+__device__ __forceinline__ void invert_diag(const uint16_t* scr, uint16_t* Akk, int lane)
+{
+    const int li = lane & 15, lg = lane >> 4;
+    float x[16];
+    invert_cols(scr + lane * 16, x, li);
+    store_trow(Akk + (lg * 16 + li) * LDC + lg * 16, x);
 }
 
 // Helper wavefront: loads and stores the 16-token row blocks LB0 .. LB0 + NLB - 1
-// of q, k, kw, v, and builds the Gram pairs of its role from the rows in LDS.
-// Role 0 also inverts the diagonal blocks and publishes the gate vectors.
-template <int D, int DVS, int ROLE, int LB0, int NLB>
+// of q, k, kw, v (NLB may be 0), and builds the Gram pairs of its role from the
+// rows in LDS (role 7 has none).  With GATES it also publishes the gate vectors.
+// Eight wavefronts: the two helpers with the diagonal pairs build the A_kk part
+// of those pairs first and raise flag SIG once their A_tt rows are in the
+// scratch; the INV wavefront (a row mover) waits for both flags (a bounded
+// wait: both writers reach them before the phase barrier), inverts the four
+// diagonal blocks in one pass and stores T_tt with the phase-B stores.
+// SLOT: this wavefront's row of decay sums in LDS.
+template <int D, int DVS, int ROLE, int LB0, int NLB, bool GATES, int SLOT, bool INV = false,
+          int SIG = -1>
 __device__ __forceinline__ void helper_loop(const WsCtx& c)
 {
     using L = Layout<D, DVS>;
@@ -823,7 +920,10 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
     constexpr int LDD = L::LDD, LDC = L::LDC, LDV = L::LDV;
     constexpr int KS = D / 32;
     constexpr int NP = P::n;
-    constexpr bool DIAG = ROLE == 0;
+    constexpr int NPA = NP > 0 ? NP : 1;         // array extents
+    constexpr int NLBA = NLB > 0 ? NLB : 1;
+    constexpr bool DIAG = GATES;
+    float tinv[16];                              // column li of T_(lane / 16)
     constexpr int VL = DVS / 8;                  // 16-byte v vectors per token row
     const WsBuf<D, DVS> m{c.smem};
     const int lane = c.lane, li = lane & 15, lg = lane >> 4;
@@ -836,8 +936,9 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
     constexpr int RPI = 64 / PPR;                // rows per instruction
     constexpr uint32_t kRsrcFlags = 0x00020000;
     const int pr = lane / PPR, pc = (lane % PPR) * 8;
-    uint4 rq[NLB][KS], rk[NLB][KS], rw[NLB][KS], rv[NLB];
-    uint16_t ng = 0x3f80u, nb = 0u;              // bf16 1.0 and 0.0 past the chunk end
+    uint4 rq[NLBA][KS], rk[NLBA][KS], rw[NLBA][KS], rv[NLBA];
+    uint16_t ng = 0x3f80u, nb = 0u;              // gates in flight (b reads 0 past the chunk end)
+    bool nin = false;                            // token `lane` inside the chunk in flight
     // Loads of one chunk, issued in NLB + 1 groups (the gates, then one row
     // block each) so that they can be spread over the Gram computation.
     struct Src {
@@ -866,9 +967,8 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
     auto load_gates = [&](const Src& r) {
         ng = __builtin_amdgcn_raw_buffer_load_b16(r.g, lane * c.H * 2, 0, 0);
         nb = __builtin_amdgcn_raw_buffer_load_b16(r.b, lane * c.H * 2, 0, 0);
-        if (lane >= r.nt)
-            ng = 0x3f80u;                        // decay 1 past the chunk end (b reads 0)
-    };
+        nin = lane < r.nt;                       // decay 1 past the chunk end, applied once the
+    };                                           // gates are taken over (no wait here)
     auto load_block = [&](const Src& r, int u) {
         const int rowQK = (int)c.rowQK, rowV = (int)c.rowV;
 #pragma unroll
@@ -903,16 +1003,31 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
             if (lane < 16 * VL)
                 *reinterpret_cast<uint4*>(sV + ((LB0 + u) * 16 + lane / VL) * LDV + (lane % VL) * 8) = rv[u];
         }
-        cg = ng;
+        cg = nin ? ng : (uint16_t)0x3f80u;
         cb = nb;
     };
 
     // ---- one chunk's matrices in registers (bf16 pairs, accumulator layout)
-    uint2 mkk[NP], mkw[NP], mqk[NP], mqw[NP];
-    float gb = 0.f, gg = 0.f, gf = 0.f;          // b, gamma, gamma_C / gamma of token `lane`
+    uint2 mkk[NPA], mkw[NPA], mqk[NPA], mqw[NPA];
     // prep(ch, lch): matrices of chunk ch; the loads of chunk lch (if >= 0) are
     // issued between its Gram pairs
     auto prep = [&](int ch, int lch) {
+        if constexpr (NP == 0) {                 // rows (and the inverses)
+            if (lch >= 0)
+                load(lch);
+            if constexpr (INV) {
+                volatile lds_int_t* f0 = m.Flag(0);
+                volatile lds_int_t* f1 = m.Flag(1);
+                for (int spin = 0; spin < (1 << 20); ++spin) {
+                    if (*f0 == ch + 1 && *f1 == ch + 1)
+                        break;
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                asm volatile("" ::: "memory");   // the scratch reads stay below the wait
+                invert_cols(m.Scr() + lane * 16, tinv, li);
+            }
+            return;
+        }
         Src lsrc;
         if (lch >= 0) {
             lsrc = src(lch);
@@ -921,54 +1036,69 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
         const float lam = wave_inclusive_sum(__log2f(fmaxf(bf16_to_f32(cg), 1e-30f)));
         const float bv = bf16_to_f32(cb);
         if constexpr (DIAG) {
+            // gates of chunk ch, in the buffer the state path of chunk ch - 1 does not read
             const float lamC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam), 63));
-            gb = bv;
-            gg = __builtin_amdgcn_exp2f(lam);
-            gf = __builtin_amdgcn_exp2f(lamC - lam);
+            float* G = m.G(ch);
+            G[lane] = bv;
+            G[kC + lane] = __builtin_amdgcn_exp2f(lam);
+            G[2 * kC + lane] = __builtin_amdgcn_exp2f(lamC - lam);
         }
         const uint16_t *sQ = m.Q(ch), *sK = m.K(ch), *sKW = m.KW(ch);
-        float* sLam = m.Lam(ROLE < 2 ? ROLE : ROLE - 1);
+        float* sLam = m.Lam(SLOT);
         sLam[lane] = lam;
-        bf16x8_t bk[KS], bq[KS];
-        float lt = 0.f, bt = 0.f;
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
+        // operands of pair p (t-block rows taken over from `prev` when pair p - 1
+        // has the same t-block) and its decay sums
+        struct Ops {
+            bf16x8_t bk[KS], bq[KS], ak[KS], aw[KS];
+            float lt, bt, le;
+            float4 ls4;
+        };
+        auto read_ops = [&](int p, Ops& o, const Ops& prev) {
             const int tb = P::t[p], sb = P::s[p];
             const int t = tb * 16 + li;
-#pragma unroll
-            for (int u = 0; u < NLB; ++u) {
-                if (p == u * NP / NLB && lch >= 0) {
-                    SCHED_FENCE();
-                    load_block(lsrc, u);
-                    SCHED_FENCE();
-                }
-            }
-            if (p == 0 || P::t[p] != P::t[p > 0 ? p - 1 : 0]) {
+            if (p > 0 && P::t[p > 0 ? p - 1 : 0] == tb) {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    bk[ks] = frag_row(sK + tb * 16 * LDD + ks * 32, LDD, lane);
-                    bq[ks] = frag_row(sQ + tb * 16 * LDD + ks * 32, LDD, lane);
+                    o.bk[ks] = prev.bk[ks];
+                    o.bq[ks] = prev.bq[ks];
                 }
-                lt = sLam[t];
-                bt = __shfl(bv, t, 64);
+                o.lt = prev.lt;
+                o.bt = prev.bt;
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    o.bk[ks] = frag_row(sK + tb * 16 * LDD + ks * 32, LDD, lane);
+                    o.bq[ks] = frag_row(sQ + tb * 16 * LDD + ks * 32, LDD, lane);
+                }
+                o.lt = sLam[t];
+                o.bt = __shfl(bv, t, 64);
             }
-            bf16x8_t ak[KS], aw[KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                ak[ks] = sb == tb ? bk[ks] : frag_row(sK + sb * 16 * LDD + ks * 32, LDD, lane);
-                aw[ks] = frag_row(sKW + sb * 16 * LDD + ks * 32, LDD, lane);
+                o.ak[ks] = sb == tb ? o.bk[ks] : frag_row(sK + sb * 16 * LDD + ks * 32, LDD, lane);
+                o.aw[ks] = frag_row(sKW + sb * 16 * LDD + ks * 32, LDD, lane);
             }
+            o.ls4 = *reinterpret_cast<const float4*>(sLam + sb * 16 + lg * 4);
+            o.le = sb == tb ? 0.f : sLam[sb * 16 + 15];
+        };
+        // part 0: the four matrices of pair p; 1: its A_kk block only; 2: the other three
+        auto compute = [&](int p, const Ops& o, int part) {
+            const int tb = P::t[p], sb = P::s[p];
+            const int t = tb * 16 + li;
             f32x4_t gkk = {0.f, 0.f, 0.f, 0.f}, gkw = gkk, gqk = gkk, gqw = gkk;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                gkk = mma32(ak[ks], bk[ks], gkk);         // transposed blocks: element (s, t)
-                gkw = mma32(aw[ks], bk[ks], gkw);
-                gqk = mma32(ak[ks], bq[ks], gqk);
-                gqw = mma32(aw[ks], bq[ks], gqw);
+                if (part != 2)
+                    gkk = mma32(o.ak[ks], o.bk[ks], gkk); // transposed blocks: element (s, t)
+                if (part != 1) {
+                    gkw = mma32(o.aw[ks], o.bk[ks], gkw);
+                    gqk = mma32(o.ak[ks], o.bq[ks], gqk);
+                    gqw = mma32(o.aw[ks], o.bq[ks], gqw);
+                }
             }
             const int s0 = sb * 16 + lg * 4;
-            const float4 ls4 = *reinterpret_cast<const float4*>(sLam + s0);
-            const float lsv[4] = {ls4.x, ls4.y, ls4.z, ls4.w};
+            const float lsv[4] = {o.ls4.x, o.ls4.y, o.ls4.z, o.ls4.w};
+            const float lt = o.lt, bt = o.bt;
             f32x4_t vkk, vkw, vqk, vqw;
             if (sb == tb) {
                 // diagonal block: causal masks, decay 2^(lam_t - lam_s) per element
@@ -987,7 +1117,7 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
                 // s-block entirely before t: 2^(lam_t - lam_s) = 2^(lam_t - lam_e) 2^(lam_e - lam_s)
                 // with lam_e the last token of the s-block; both factors are <= 1
                 // because lam never increases along the chunk
-                const float le = sLam[sb * 16 + 15];
+                const float le = o.le;
                 const float et = __builtin_amdgcn_exp2f(lt - le), bet = bt * et;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -999,12 +1129,59 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
                     vqw[r] = mi * gqw[r];
                 }
             }
-            mkk[p] = make_uint2(pack_bf16x2(vkk[0], vkk[1]), pack_bf16x2(vkk[2], vkk[3]));
-            mkw[p] = make_uint2(pack_bf16x2(vkw[0], vkw[1]), pack_bf16x2(vkw[2], vkw[3]));
-            mqk[p] = make_uint2(pack_bf16x2(vqk[0], vqk[1]), pack_bf16x2(vqk[2], vqk[3]));
-            mqw[p] = make_uint2(pack_bf16x2(vqw[0], vqw[1]), pack_bf16x2(vqw[2], vqw[3]));
-            if (tb == sb)                                // A_tt row li, columns 4 lg .. 4 lg + 3
-                *reinterpret_cast<uint2*>(m.Scr() + (tb * 16 + li) * 16 + lg * 4) = mkk[p];
+            if (part != 2) {
+                mkk[p] = make_uint2(pack_bf16x2(vkk[0], vkk[1]), pack_bf16x2(vkk[2], vkk[3]));
+                if (tb == sb)                            // A_tt row li, columns 4 lg .. 4 lg + 3
+                    *reinterpret_cast<uint2*>(m.Scr() + (tb * 16 + li) * 16 + lg * 4) = mkk[p];
+            }
+            if (part != 1) {
+                mkw[p] = make_uint2(pack_bf16x2(vkw[0], vkw[1]), pack_bf16x2(vkw[2], vkw[3]));
+                mqk[p] = make_uint2(pack_bf16x2(vqk[0], vqk[1]), pack_bf16x2(vqk[2], vqk[3]));
+                mqw[p] = make_uint2(pack_bf16x2(vqw[0], vqw[1]), pack_bf16x2(vqw[2], vqw[3]));
+            }
+        };
+        if constexpr (SIG >= 0) {
+            // two diagonal pairs: both A_tt blocks first, then the flag, then the rest
+            static_assert(NP == 2 && NLB == 0 && P::t[0] == P::s[0] && P::t[1] == P::s[1],
+                          "SIG: two diagonal pairs, no rows");
+            Ops ops[2];
+            read_ops(0, ops[0], ops[0]);
+            read_ops(1, ops[1], ops[0]);
+            SCHED_FENCE();
+            compute(0, ops[0], 1);
+            compute(1, ops[1], 1);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            *m.Flag(SIG) = ch + 1;
+            compute(0, ops[0], 2);
+            compute(1, ops[1], 2);
+        } else if constexpr (NLB == 0) {
+            // no rows to move: the operands of pair p + 1 are read while pair p computes
+            Ops ops[2];
+            read_ops(0, ops[0], ops[0]);
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                if (p + 1 < NP)
+                    read_ops(p + 1, ops[(p + 1) & 1], ops[p & 1]);
+                SCHED_FENCE();
+                compute(p, ops[p & 1], 0);
+                SCHED_FENCE();
+            }
+        } else {
+            // the row loads of chunk lch are spread between the pairs
+            Ops o;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+#pragma unroll
+                for (int u = 0; u < NLB; ++u) {
+                    if (p == u * NP / NLB && lch >= 0) {
+                        SCHED_FENCE();
+                        load_block(lsrc, u);
+                        SCHED_FENCE();
+                    }
+                }
+                read_ops(p, o, o);
+                compute(p, o, 0);
+            }
         }
     };
     auto write_mats = [&]() {
@@ -1018,12 +1195,8 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
             *reinterpret_cast<uint2*>(Aqk + off) = mqk[p];
             *reinterpret_cast<uint2*>(Aqkw + off) = mqw[p];
         }
-        if constexpr (DIAG) {
-            float* G = m.G();
-            G[lane] = gb;
-            G[kC + lane] = gg;
-            G[2 * kC + lane] = gf;
-        }
+        if constexpr (INV)                       // T_tt transposed
+            store_trow(Akk + (lg * 16 + li) * LDC + lg * 16, tinv);
     };
 
     const int nch = c.nchunks;
@@ -1039,12 +1212,11 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
     if (nch > 0) {
         prep(0, -1);
         write_mats();
-        if constexpr (DIAG)                      // chunk 0; later chunks: a state wavefront
-            invert_diag<LDC>(m.Scr(), m.Akk(), lane);
         if (nch > 1)
             store_rows(1);
     }
-    lds_barrier();
+    lds_barrier();                               // A_ii of chunk 0 in the scratch
+    lds_barrier();                               // T_ii of chunk 0 (a state wavefront)
     for (int ch = 0; ch < nch; ++ch) {
         // phase A (beside the state path of chunk ch): matrices of chunk ch + 1,
         // with the loads of chunk ch + 2 spread between its Gram pairs
@@ -1063,7 +1235,9 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
 }
 
 // State wavefront jb: value columns 16 jb .. 16 jb + 15 of the slice.
-template <int D, int DVS>
+// INV: wavefront 0 inverts the diagonal blocks (in phase B).  SPLIT: the a-step
+// of chunk ch + 1 runs in phase B of chunk ch, beside the helpers' stores.
+template <int D, int DVS, bool INV, bool SPLIT>
 __device__ __forceinline__ void state_loop(const WsCtx& c, int jb)
 {
     constexpr int NI = D / 16;
@@ -1076,19 +1250,35 @@ __device__ __forceinline__ void state_loop(const WsCtx& c, int jb)
     lds_barrier();
     lds_barrier();
     lds_barrier();
-    const float* G = m.G();
+    // the helpers have built the matrices of chunk 0; invert its diagonal blocks
+    if (INV && jb == 0 && c.nchunks > 0)
+        invert_diag<Layout<D, DVS>::LDC>(m.Scr(), m.Akk(), lane);
+    v4s_t s0b[NI];
+    bf16x8_t vf[2];
+    // a-step of chunk ch from the gates G(ch): gamma_C = gamma of the last token
+    // (gates past the chunk end are 1)
+    auto a_of = [&](int ch) {
+        const float* G = m.G(ch);
+        a_step<D, DVS>(S, s0b, vf, m.KW(ch), m.V(ch), G + 2 * kC, G[2 * kC - 1], jb, lane);
+    };
+    if (SPLIT && c.nchunks > 0)
+        a_of(0);
+    lds_barrier();
     for (int ch = 0; ch < c.nchunks; ++ch) {
         const int c0 = c.seq0 + ch * kC;
         const int nt = min(kC, c.seq1 - c0);
-        // gamma_C = gamma of the last token (gates past the chunk end are 1)
-        state_path<D, DVS, true>(S, m.Q(ch), m.K(ch), m.KW(ch), m.V(ch), m.Akk(), m.Akkw(), m.Aqkw(),
-                                 m.Aqk(), nullptr, G, G + kC, G + 2 * kC, G[2 * kC - 1], c.o,
-                                 c0, nt, c.rowV, c.e, c.DV, c.j0, jb, lane);
+        const float* G = m.G(ch);
+        state_path<D, DVS, true, SPLIT>(S, s0b, vf, m.Q(ch), m.K(ch), m.KW(ch), m.V(ch), m.Akk(),
+                                        m.Akkw(), m.Aqkw(), m.Aqk(), nullptr, G, G + kC, G + 2 * kC,
+                                        G[2 * kC - 1], c.o, c0, nt, c.rowV, c.e, c.DV, c.j0, jb,
+                                        lane);
         lds_barrier();
         // phase B: the diagonal inverses of chunk ch + 1 (their A_ii were built in
-        // phase A), beside the helpers' matrix and row stores
-        if (jb == 0 && ch + 1 < c.nchunks)
+        // phase A) or the a-step of chunk ch + 1, beside the helpers' stores
+        if (INV && jb == 0 && ch + 1 < c.nchunks)
             invert_diag<Layout<D, DVS>::LDC>(m.Scr(), m.Akk(), lane);
+        if (SPLIT && ch + 1 < c.nchunks)
+            a_of(ch + 1);
         lds_barrier();
     }
 #pragma unroll
@@ -1101,8 +1291,12 @@ __device__ __forceinline__ void state_loop(const WsCtx& c, int jb)
     }
 }
 
-template <int D, int DVS>
-__global__ __launch_bounds__(kThreads) void scan_ws_kernel(
+// NW wavefronts: 4 (one per SIMD) or 8 (two per SIMD; slices of 32 columns).
+// Wavefront w runs on SIMD w % 4: with eight, the two state wavefronts share
+// their SIMDs with the two row movers, and each remaining SIMD runs two Gram
+// helpers (five pairs per SIMD).
+template <int D, int DVS, int NW>
+__global__ __launch_bounds__(NW * 64) void scan_ws_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ kw, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ g, const uint16_t* __restrict__ b,
@@ -1112,6 +1306,7 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(
     using Ly = LayoutWS<D, DVS>;
     constexpr int NJ = DVS / 16;
     static_assert(NJ == 1 || NJ == 2, "one or two state wavefronts");
+    static_assert(NW == 4 || (NW == 8 && NJ == 2), "four, or eight with two state wavefronts");
     static_assert(Ly::total <= 160 * 1024, "LDS budget");
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[Ly::total];
@@ -1141,36 +1336,45 @@ __global__ __launch_bounds__(kThreads) void scan_ws_kernel(
         // matrices (their upper blocks are never written), gates, scratch
         constexpr int nz = (Ly::total - Ly::oAkk) / 16;
         uint4* z = reinterpret_cast<uint4*>(smem + Ly::oAkk);
-        for (int i = tid; i < nz; i += kThreads)
+        for (int i = tid; i < nz; i += NW * 64)
             z[i] = make_uint4(0u, 0u, 0u, 0u);
     }
 
-    // Every role passes the same number of barriers: 3 + 2 per chunk.
+    // Every role passes the same number of barriers: 4 + 2 per chunk.
     if (wave < NJ) {
-        state_loop<D, DVS>(c, wave);
+        state_loop<D, DVS, NW == 4, NW == 8>(c, wave);
+    } else if constexpr (NW == 8) {
+        switch (wave) {
+        case 2: helper_loop<D, DVS, 4, 0, 0, true, 0, false, 0>(c); break;   // (0,0) (1,1), gates
+        case 3: helper_loop<D, DVS, 6, 0, 0, false, 1>(c); break;             // (1,0) (2,0) (2,1)
+        case 4: helper_loop<D, DVS, 7, 0, 2, false, 0, true>(c); break;       // rows 0, 1; T_tt
+        case 5: helper_loop<D, DVS, 7, 2, 2, false, 0>(c); break;             // rows of blocks 2, 3
+        case 6: helper_loop<D, DVS, 5, 0, 0, false, 2, false, 1>(c); break;  // (2,2) (3,3)
+        default: helper_loop<D, DVS, 3, 0, 0, false, 3>(c); break;            // (3,0) (3,1) (3,2)
+        }
     } else if constexpr (NJ == 2) {              // diagonal pairs | six off-diagonal pairs
         if (wave == 2)
-            helper_loop<D, DVS, 0, 0, HWS_DIAG_BLOCKS>(c);
+            helper_loop<D, DVS, 0, 0, HWS_DIAG_BLOCKS, true, 0>(c);
         else
-            helper_loop<D, DVS, 1, HWS_DIAG_BLOCKS, 4 - HWS_DIAG_BLOCKS>(c);
+            helper_loop<D, DVS, 1, HWS_DIAG_BLOCKS, 4 - HWS_DIAG_BLOCKS, false, 1>(c);
     } else {                                     // diagonal | three | three
         if (wave == 1)
-            helper_loop<D, DVS, 0, 0, 1>(c);
+            helper_loop<D, DVS, 0, 0, 1, true, 0>(c);
         else if (wave == 2)
-            helper_loop<D, DVS, 2, 1, 1>(c);
+            helper_loop<D, DVS, 2, 1, 1, false, 1>(c);
         else
-            helper_loop<D, DVS, 3, 2, 2>(c);
+            helper_loop<D, DVS, 3, 2, 2, false, 2>(c);
     }
 }
 
-template <int D, int DVS>
+template <int D, int DVS, int NW>
 static hipError_t launch_ws(const ScanArgs& p, hipStream_t stream)
 {
     const int n_slices = p.dv / DVS;
     const int64_t blocks = (int64_t)p.n_seqs * p.heads * n_slices;
     if (blocks == 0)
         return hipSuccess;
-    hipLaunchKernelGGL((scan_ws_kernel<D, DVS>), dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((scan_ws_kernel<D, DVS, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
                        (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.kw,
                        (const uint16_t*)p.v, (const uint16_t*)p.g, (const uint16_t*)p.b,
                        p.cu_seqlens, p.heads, p.dv, n_slices, (uint16_t*)p.o, p.s_final);
@@ -1205,9 +1409,13 @@ hipError_t launch_scan_bf16(const ScanArgs& p, hipStream_t s)
     if (!scan_bf16_supported(p.dk, p.dv, p.dv_slice))
         return hipErrorInvalidValue;
     if (p.specialised) {
-        if (p.dk == 64)
-            return p.dv_slice == 16 ? bf16scan::launch_ws<64, 16>(p, s) : bf16scan::launch_ws<64, 32>(p, s);
-        return p.dv_slice == 16 ? bf16scan::launch_ws<128, 16>(p, s) : bf16scan::launch_ws<128, 32>(p, s);
+        const bool w8 = p.ws_waves == 8;
+        if (p.dk == 64) {
+            if (p.dv_slice == 16) return bf16scan::launch_ws<64, 16, 4>(p, s);
+            return w8 ? bf16scan::launch_ws<64, 32, 8>(p, s) : bf16scan::launch_ws<64, 32, 4>(p, s);
+        }
+        if (p.dv_slice == 16) return bf16scan::launch_ws<128, 16, 4>(p, s);
+        return w8 ? bf16scan::launch_ws<128, 32, 8>(p, s) : bf16scan::launch_ws<128, 32, 4>(p, s);
     }
     if (p.dk == 64) {
         if (p.dv_slice == 16) return bf16scan::launch<64, 16>(p, s);

@@ -21,6 +21,7 @@ struct ScanArgs {
     int n_seqs, total_tokens, heads, dk, dv;
     int dv_slice;                   // value columns owned by one workgroup
     bool specialised;               // bf16: helper wavefronts prepare the next chunk (dv_slice <= 32)
+    int ws_waves;                   // wavefronts of the specialised kernel: 4, or 8 (dv_slice 32)
     const void *q, *k, *kw, *v, *g, *b;
     const int32_t* cu_seqlens;
     void* o;

@@ -161,6 +161,7 @@ prism_status prism_scan(const prism_dims* d, const void* q, const void* k, const
     p.dv = d->dv;
     p.dv_slice = pick_dv_slice(d);
     p.specialised = p.bf16 && p.dv_slice <= 32 && env_int("PRISM_SCAN_SPECIALISED", 1) != 0;
+    p.ws_waves = env_int("PRISM_SCAN_WAVES", 8) == 4 ? 4 : 8;
     p.q = q; p.k = k; p.kw = kw; p.v = v; p.g = g; p.b = b;
     p.cu_seqlens = cu_seqlens;
     p.o = o;

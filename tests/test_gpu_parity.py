@@ -97,7 +97,8 @@ def test_fwd_matches_oracle(w):
 
 
 SCAN_KERNELS = {                 # environment selecting each bf16 scan kernel
-    "specialised": {"PRISM_SCAN_GENERIC": "0", "PRISM_SCAN_SPECIALISED": "1"},
+    "specialised": {"PRISM_SCAN_GENERIC": "0", "PRISM_SCAN_SPECIALISED": "1", "PRISM_SCAN_WAVES": "8"},
+    "specialised4": {"PRISM_SCAN_GENERIC": "0", "PRISM_SCAN_SPECIALISED": "1", "PRISM_SCAN_WAVES": "4"},
     "register": {"PRISM_SCAN_GENERIC": "0", "PRISM_SCAN_SPECIALISED": "0"},
     "generic": {"PRISM_SCAN_GENERIC": "1"},
 }
@@ -111,7 +112,7 @@ def test_every_value_slice_width(dk, dvs, kernel, monkeypatch):
     0, 1, 2 and 3 chunks with full and ragged last chunks."""
     if kernel == "generic" and dk == 128 and dvs == 64:
         pytest.skip("the generic kernel has no dk=128 variant with 64 value columns")
-    if kernel == "specialised" and dvs == 64:
+    if kernel.startswith("specialised") and dvs == 64:
         pytest.skip("the specialised kernel serves slices of 16 and 32 value columns")
     monkeypatch.setenv("PRISM_DV_SLICE", str(dvs))
     for key, val in SCAN_KERNELS[kernel].items():
@@ -123,7 +124,7 @@ def test_every_value_slice_width(dk, dvs, kernel, monkeypatch):
     assert max_rel(o, o_ref) <= TOL["bf16"] and max_rel(s, s_ref) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("kernel", ["specialised", "register"])
+@pytest.mark.parametrize("kernel", ["specialised", "specialised4", "register"])
 def test_bf16_kernels_long_sequence(kernel, monkeypatch):
     """Dozens of chunks through one chain: the double-buffered matrices and the
     staged rows alternate many times."""
