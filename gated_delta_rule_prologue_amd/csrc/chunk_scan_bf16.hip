@@ -1024,7 +1024,9 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
                     __builtin_amdgcn_s_sleep(1);
                 }
                 asm volatile("" ::: "memory");   // the scratch reads stay below the wait
+                __builtin_amdgcn_s_setprio(2);
                 invert_cols(m.Scr() + lane * 16, tinv, li);
+                __builtin_amdgcn_s_setprio(0);
             }
             return;
         }
@@ -1052,6 +1054,28 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
             bf16x8_t bk[KS], bq[KS], ak[KS], aw[KS];
             float lt, bt, le;
             float4 ls4;
+        };
+        // what the A_kk block of a diagonal pair needs (K rows, decay sums), and the rest
+        auto read_kk = [&](int p, Ops& o) {
+            const int tb = P::t[p];
+            const int t = tb * 16 + li;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                o.bk[ks] = frag_row(sK + tb * 16 * LDD + ks * 32, LDD, lane);
+                o.ak[ks] = o.bk[ks];
+            }
+            o.lt = sLam[t];
+            o.bt = __shfl(bv, t, 64);
+            o.ls4 = *reinterpret_cast<const float4*>(sLam + tb * 16 + lg * 4);
+            o.le = 0.f;
+        };
+        auto read_rest = [&](int p, Ops& o) {
+            const int tb = P::t[p];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                o.bq[ks] = frag_row(sQ + tb * 16 * LDD + ks * 32, LDD, lane);
+                o.aw[ks] = frag_row(sKW + tb * 16 * LDD + ks * 32, LDD, lane);
+            }
         };
         auto read_ops = [&](int p, Ops& o, const Ops& prev) {
             const int tb = P::t[p], sb = P::s[p];
@@ -1144,14 +1168,19 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
             // two diagonal pairs: both A_tt blocks first, then the flag, then the rest
             static_assert(NP == 2 && NLB == 0 && P::t[0] == P::s[0] && P::t[1] == P::s[1],
                           "SIG: two diagonal pairs, no rows");
+            // (raised issue priority until the flag: the inverse waits on it)
+            __builtin_amdgcn_s_setprio(2);
             Ops ops[2];
-            read_ops(0, ops[0], ops[0]);
-            read_ops(1, ops[1], ops[0]);
+            read_kk(0, ops[0]);
+            read_kk(1, ops[1]);
             SCHED_FENCE();
+            read_rest(0, ops[0]);
             compute(0, ops[0], 1);
             compute(1, ops[1], 1);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             *m.Flag(SIG) = ch + 1;
+            __builtin_amdgcn_s_setprio(0);
+            read_rest(1, ops[1]);
             compute(0, ops[0], 2);
             compute(1, ops[1], 2);
         } else if constexpr (NLB == 0) {
