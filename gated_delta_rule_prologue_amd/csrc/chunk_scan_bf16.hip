@@ -158,7 +158,7 @@ struct Layout {
     static constexpr int oAqk = oAqkw + szM;
     static constexpr int oTd = oAqk + szM;
     static constexpr int oG = oTd + szTd;
-    static constexpr int total = oG + 4 * kC * 4;
+    static constexpr int total = oG + 5 * kC * 4;
     static_assert(oAkk % 16 == 0 && oTd % 16 == 0 && oG % 16 == 0, "alignment");
 };
 
@@ -266,7 +266,7 @@ __device__ __forceinline__ void state_path(
     f32x4_t (&S)[D / 16], v4s_t (&s0b)[D / 16], bf16x8_t (&vf)[2], const uint16_t* sQ,
     const uint16_t* sK, const uint16_t* sKW,
     const uint16_t* sV, const uint16_t* sAkk, const uint16_t* sAkkw, const uint16_t* sAqkw,
-    const uint16_t* sAqk, const uint16_t* sTd, const float* sBv, const float* sGam,
+    const uint16_t* sAqk, const uint16_t* sTd, const float* sBG, const float* sGam,
     const float* sFac, float gC, uint16_t* o, int c0, int nt, int64_t rowV, int e, int DV,
     int j0, int jb, int lane)
 {
@@ -277,41 +277,49 @@ __device__ __forceinline__ void state_path(
     if constexpr (!SPLIT)
         a_step<D, DVS>(S, s0b, vf, sKW, sV, sFac, gC, jb, lane);
 
-    // ---- b, one (16-token block tb, 32-channel pair kp) unit at a time
+    // ---- b, one unit (two 16-token blocks 2 tp, 2 tp + 1; 32-channel step kp) at a
+    //      time: four independent accumulator chains (R and O^T of both blocks)
     constexpr int NKP = NI / 2;
-    constexpr int NU = 4 * NKP;                     // units
+    constexpr int NU = 2 * NKP;                     // units
     // S0 as 16x16x32 operands pairing with 16-byte row reads of K and Q
     bf16x8_t s0q[NKP];
 #pragma unroll
     for (int kp = 0; kp < NKP; ++kp)
         s0q[kp] = pair_rows(s0b[2 * kp], s0b[2 * kp + 1]);
-    bf16x8_t kf[NU], qf[NU];
+    bf16x8_t kf[NU][2], qf[NU][2];
     bf16x8_t akw[4][2], aqw[4][2];
-    float4 gm[4], bb[4];
+    float4 bg[4];
     float go[4];
     v4s_t akk[6], td[4], aqk[10];
     auto load_unit = [&](int u) {
-        const int tb = u / NKP, kp = u % NKP;
-        kf[u] = frag_row(sK + tb * 16 * LDD + kp * 32, LDD, lane);
-        qf[u] = frag_row(sQ + tb * 16 * LDD + kp * 32, LDD, lane);
+        const int tp = u / NKP, kp = u % NKP;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int tb = 2 * tp + h;
+            kf[u][h] = frag_row(sK + tb * 16 * LDD + kp * 32, LDD, lane);
+            qf[u][h] = frag_row(sQ + tb * 16 * LDD + kp * 32, LDD, lane);
+        }
         if (kp == 0) {                              // per-block operands and gates
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                if (h2 < (tb + 2) / 2) {
-                    akw[tb][h2] = frag_row(sAkkw + tb * 16 * LDC + h2 * 32, LDC, lane);
-                    aqw[tb][h2] = frag_row(sAqkw + tb * 16 * LDC + h2 * 32, LDC, lane);
+            for (int h = 0; h < 2; ++h) {
+                const int tb = 2 * tp + h;
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    if (h2 < (tb + 2) / 2) {
+                        akw[tb][h2] = frag_row(sAkkw + tb * 16 * LDC + h2 * 32, LDC, lane);
+                        aqw[tb][h2] = frag_row(sAqkw + tb * 16 * LDC + h2 * 32, LDC, lane);
+                    }
                 }
+                bg[tb] = *reinterpret_cast<const float4*>(sBG + tb * 16 + lg * 4);
+                go[tb] = sGam[tb * 16 + li];
             }
-            gm[tb] = *reinterpret_cast<const float4*>(sGam + tb * 16 + lg * 4);
-            bb[tb] = *reinterpret_cast<const float4*>(sBv + tb * 16 + lg * 4);
-            go[tb] = sGam[tb * 16 + li];
         }
-        // the operands of c, spread over the last five units
-        const int w = u - (NU - 5);
+        // the operands of c, spread over the last three units
+        const int w = u - (NU - 3);
         if (w >= 0) {
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int idx = w * 2 + q;          // 0 .. 9: akk 0..5, td 6..9
+            for (int q = 0; q < 4; ++q) {
+                const int idx = w * 4 + q;          // 0 .. 9: akk 0..5, td 6..9
                 if (idx < 6) {
                     const int i2 = idx < 1 ? 1 : idx < 3 ? 2 : 3;
                     const int j2 = idx - (i2 * (i2 - 1)) / 2;
@@ -334,39 +342,62 @@ __device__ __forceinline__ void state_path(
         }
     };
     f32x4_t R[4], OT[4];
-    constexpr int AHEAD_B = 4;                      // 2 paired reads per unit (+ per-block extras)
+    constexpr int AHEAD_B = 1;                      // 4 reads per unit (+ per-block extras)
 #pragma unroll
     for (int u = 0; u < AHEAD_B; ++u)
         load_unit(u);
     SCHED_FENCE();
-    f32x4_t ra = {0.f, 0.f, 0.f, 0.f}, oa = ra;
+    f32x4_t ra[2], oa[2];
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-        const int tb = u / NKP, kp = u % NKP;
+        const int tp = u / NKP, kp = u % NKP;
         if (u + AHEAD_B < NU)
             load_unit(u + AHEAD_B);
         SCHED_FENCE();
         if (kp == 0) {
-            ra = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            oa = ra;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                ra[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                oa[h] = ra[h];
+            }
         }
-        ra = mma32(kf[u], s0q[kp], ra);                       // (K S0)[t][j]
-        oa = mma32(s0q[kp], qf[u], oa);                       // (Q S0)^T[j][t]
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            ra[h] = mma32(kf[u][h], s0q[kp], ra[h]);          // (K S0)[t][j]
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            oa[h] = mma32(s0q[kp], qf[u][h], oa[h]);          // (Q S0)^T[j][t]
         if (kp == NKP - 1) {
-            const float gmv[4] = {gm[tb].x, gm[tb].y, gm[tb].z, gm[tb].w};
-            const float bbv[4] = {bb[tb].x, bb[tb].y, bb[tb].z, bb[tb].w};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                ra[r] *= bbv[r] * gmv[r];
-                oa[r] *= go[tb];
+            for (int h = 0; h < 2; ++h) {
+                const int tb = 2 * tp + h;
+                const float bgv[4] = {bg[tb].x, bg[tb].y, bg[tb].z, bg[tb].w};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    ra[h][r] *= bgv[r];
+                    oa[h][r] *= go[tb];
+                }
             }
 #pragma unroll
-            for (int h2 = 0; h2 < (tb + 2) / 2; ++h2) {
-                ra = mma32(akw[tb][h2], vf[h2], ra);
-                oa = mma32(vf[h2], aqw[tb][h2], oa);          // (A_qkw V)^T
+            for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int tb = 2 * tp + h;
+                    if (h2 < (tb + 2) / 2)
+                        ra[h] = mma32(akw[tb][h2], vf[h2], ra[h]);
+                }
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int tb = 2 * tp + h;
+                    if (h2 < (tb + 2) / 2)
+                        oa[h] = mma32(vf[h2], aqw[tb][h2], oa[h]);   // (A_qkw V)^T
+                }
             }
-            R[tb] = ra;
-            OT[tb] = oa;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                R[2 * tp + h] = ra[h];
+                OT[2 * tp + h] = oa[h];
+            }
         }
         SCHED_FENCE();
     }
@@ -484,6 +515,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(
     float* sBv = sLam + kC;
     float* sGam = sBv + kC;
     float* sFac = sGam + kC;
+    float* sBG = sFac + kC;                      // b gamma
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -570,6 +602,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(
             sBv[lane] = bf16_to_f32(pb);
             sGam[lane] = __builtin_amdgcn_exp2f(lam);
             sFac[lane] = __builtin_amdgcn_exp2f(lamC - lam);      // gamma_C / gamma_t <= 1
+            sBG[lane] = bf16_to_f32(pb) * __builtin_amdgcn_exp2f(lam);
         }
 #pragma unroll
         for (int j = 0; j < NQ; ++j) {
@@ -671,7 +704,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(
         if (wave < NJ) {
             v4s_t s0b[D / 16];
             bf16x8_t vf[2];
-            state_path<D, DVS>(S, s0b, vf, sQ, sK, sKW, sV, sAkk, sAkkw, sAqkw, sAqk, sTd, sBv, sGam,
+            state_path<D, DVS>(S, s0b, vf, sQ, sK, sKW, sV, sAkk, sAkkw, sAqkw, sAqk, sTd, sBG, sGam,
                                sFac, __builtin_amdgcn_exp2f(lamC), o, c0, nt, rowV, e, DV, j0, wave,
                                lane);
         }
@@ -741,7 +774,7 @@ struct LayoutWS {
     static constexpr int oAkkw = oAkk + L::szM;
     static constexpr int oAqkw = oAkkw + L::szM;
     static constexpr int oAqk = oAqkw + L::szM;              // holds -A_qk
-    static constexpr int oG = oAqk + L::szM;                 // b, gamma, gamma_C / gamma; two chunks
+    static constexpr int oG = oAqk + L::szM;                 // b gamma, gamma, gamma_C / gamma; two chunks
     static constexpr int oScr = oG + 2 * 3 * kC * 4;         // A_ii rows for the inverses
     static constexpr int oLam = oScr + 4 * 16 * 16 * 2;      // log2 decay sums, one slot per helper
     static constexpr int oFlag = oLam + 4 * kC * 4;          // scratch-ready flags (eight waves)
@@ -1041,7 +1074,7 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
             // gates of chunk ch, in the buffer the state path of chunk ch - 1 does not read
             const float lamC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam), 63));
             float* G = m.G(ch);
-            G[lane] = bv;
+            G[lane] = bv * __builtin_amdgcn_exp2f(lam);
             G[kC + lane] = __builtin_amdgcn_exp2f(lam);
             G[2 * kC + lane] = __builtin_amdgcn_exp2f(lamC - lam);
         }
