@@ -945,7 +945,7 @@ __device__ __forceinline__ void invert_diag(const uint16_t* scr, uint16_t* Akk, 
 // diagonal blocks in one pass and stores T_tt with the phase-B stores.
 // SLOT: this wavefront's row of decay sums in LDS.
 template <int D, int DVS, int ROLE, int LB0, int NLB, bool GATES, int SLOT, bool INV = false,
-          int SIG = -1>
+          int SIG = -1, bool EARLY = false>
 __device__ __forceinline__ void helper_loop(const WsCtx& c)
 {
     using L = Layout<D, DVS>;
@@ -1022,22 +1022,28 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
             load_block(r, u);
     };
     uint16_t cg = 0x3f80u, cb = 0u;              // gates of the chunk being prepared
-    auto store_rows = [&](int ch) {
+    // parts: 0 all rows, 1 q and k only (and the gates), 2 kw and v only
+    auto store_rows = [&](int ch, int parts) {
         uint16_t *sQ = m.Q(ch), *sK = m.K(ch), *sKW = m.KW(ch), *sV = m.V(ch);
 #pragma unroll
         for (int u = 0; u < NLB; ++u) {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int off = ((LB0 + u) * 16 + ks * RPI + pr) * LDD + pc;
-                *reinterpret_cast<uint4*>(sK + off) = rk[u][ks];
-                *reinterpret_cast<uint4*>(sKW + off) = rw[u][ks];
-                *reinterpret_cast<uint4*>(sQ + off) = rq[u][ks];
+                if (parts != 2) {
+                    *reinterpret_cast<uint4*>(sK + off) = rk[u][ks];
+                    *reinterpret_cast<uint4*>(sQ + off) = rq[u][ks];
+                }
+                if (parts != 1)
+                    *reinterpret_cast<uint4*>(sKW + off) = rw[u][ks];
             }
-            if (lane < 16 * VL)
+            if (parts != 1 && lane < 16 * VL)
                 *reinterpret_cast<uint4*>(sV + ((LB0 + u) * 16 + lane / VL) * LDV + (lane % VL) * 8) = rv[u];
         }
-        cg = nin ? ng : (uint16_t)0x3f80u;
-        cb = nb;
+        if (parts != 2) {
+            cg = nin ? ng : (uint16_t)0x3f80u;
+            cb = nb;
+        }
     };
 
     // ---- one chunk's matrices in registers (bf16 pairs, accumulator layout)
@@ -1061,6 +1067,11 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
                 invert_cols(m.Scr() + lane * 16, tinv, li);
                 __builtin_amdgcn_s_setprio(0);
             }
+            // kw and v rows of chunk lch go to the buffer chunk lch - 2 uses: the
+            // state path has read that chunk's kw and v in its a-step (phase B of
+            // the previous chunk), so only q and k wait for phase B
+            if (EARLY && lch >= 0)
+                store_rows(lch, 2);
             return;
         }
         Src lsrc;
@@ -1266,7 +1277,7 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
         load(0);
     lds_barrier();                               // LDS cleared
     if (nch > 0) {
-        store_rows(0);
+        store_rows(0, 0);
         if (nch > 1)
             load(1);
     }
@@ -1275,7 +1286,7 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
         prep(0, -1);
         write_mats();
         if (nch > 1)
-            store_rows(1);
+            store_rows(1, 0);
     }
     lds_barrier();                               // A_ii of chunk 0 in the scratch
     lds_barrier();                               // T_ii of chunk 0 (a state wavefront)
@@ -1291,7 +1302,7 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
         if (ch + 1 < nch)
             write_mats();
         if (ch + 2 < nch)
-            store_rows(ch + 2);
+            store_rows(ch + 2, EARLY ? 1 : 0);
         lds_barrier();
     }
 }
@@ -1409,8 +1420,8 @@ __global__ __launch_bounds__(NW * 64) void scan_ws_kernel(
         switch (wave) {
         case 2: helper_loop<D, DVS, 4, 0, 0, true, 0, false, 0>(c); break;   // (0,0) (1,1), gates
         case 3: helper_loop<D, DVS, 6, 0, 0, false, 1>(c); break;             // (1,0) (2,0) (2,1)
-        case 4: helper_loop<D, DVS, 7, 0, 2, false, 0, true>(c); break;       // rows 0, 1; T_tt
-        case 5: helper_loop<D, DVS, 7, 2, 2, false, 0>(c); break;             // rows of blocks 2, 3
+        case 4: helper_loop<D, DVS, 7, 0, 2, false, 0, true, -1, true>(c); break;   // rows 0, 1; T_tt
+        case 5: helper_loop<D, DVS, 7, 2, 2, false, 0, false, -1, true>(c); break;  // rows of blocks 2, 3
         case 6: helper_loop<D, DVS, 5, 0, 0, false, 2, false, 1>(c); break;  // (2,2) (3,3)
         default: helper_loop<D, DVS, 3, 0, 0, false, 3>(c); break;            // (3,0) (3,1) (3,2)
         }
