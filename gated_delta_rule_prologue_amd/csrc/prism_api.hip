@@ -53,13 +53,24 @@ bool slice_supported(const prism_dims* d, int dvs)
     return prism::scan_supported(bf16, d->dk, d->dv, dvs);
 }
 
+bool ws8_enabled()
+{
+    return env_int("PRISM_SCAN_SPECIALISED", 1) != 0 && env_int("PRISM_SCAN_WAVES", 8) != 4;
+}
+
 // Value columns per scan workgroup: split the dv columns of each chain until
 // there are enough workgroups for the 256 CUs (columns of S are independent).
+// bf16 takes 32-column slices whenever the eight-wavefront kernel serves them:
+// its per-chunk latency is the lowest, so it wins even where 64-column slices
+// would fill the chip (measured on the recsys, varlen and 64k workloads).
 int pick_dv_slice(const prism_dims* d)
 {
     const int forced = env_int("PRISM_DV_SLICE", 0);
     if (forced && slice_supported(d, forced))
         return forced;
+    if (d->dtype == PRISM_BF16 && env_int("PRISM_SCAN_GENERIC", 0) == 0 && ws8_enabled() &&
+        slice_supported(d, 32))
+        return 32;
     const long chains = (long)d->n_seqs * d->heads;
     const int cands[3] = {64, 32, 16};
     int best = 0;
