@@ -29,7 +29,8 @@
 //                   (three barriers per chunk); any value slice up to 64.
 //   scan_ws_kernel  wavefront-specialised (slices of 16 or 32 columns):
 //                   helper wavefronts prepare chunk c + 1 while the state
-//                   wavefronts run chunk c (two barriers per chunk).
+//                   wavefronts run chunk c (two barriers per chunk); four
+//                   wavefronts, or eight (two per SIMD) for 32 columns.
 #include "common.h"
 #include "kernels.h"
 
@@ -748,9 +749,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(
 // over the XCDs, all value slices of a chain go to one XCD, so its q, k, kw
 // rows come from HBM once and from that L2 for the other slices.
 constexpr int kXcds = 8;
-#ifndef HWS_DIAG_BLOCKS
-#define HWS_DIAG_BLOCKS 2                        // row blocks loaded by the diagonal helper (of 4)
-#endif
+constexpr int kDiagRowBlocks = 2;               // four wavefronts: row blocks moved by the diagonal helper
 __device__ __forceinline__ void xcd_map(int n_slices, int& slice, int& chain)
 {
     const unsigned w = blockIdx.x;
@@ -1288,15 +1287,13 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
         if (nch > 1)
             store_rows(1, 0);
     }
-    lds_barrier();                               // A_ii of chunk 0 in the scratch
-    lds_barrier();                               // T_ii of chunk 0 (a state wavefront)
+    lds_barrier();                               // matrices of chunk 0 (A_ii in the scratch)
+    lds_barrier();                               // T_ii of chunk 0 (four wavefronts: a state wavefront)
     for (int ch = 0; ch < nch; ++ch) {
         // phase A (beside the state path of chunk ch): matrices of chunk ch + 1,
         // with the loads of chunk ch + 2 spread between its Gram pairs
         if (ch + 1 < nch)
             prep(ch + 1, ch + 2 < nch ? ch + 2 : -1);
-        else if (ch + 2 < nch)
-            load(ch + 2);
         lds_barrier();
         // phase B
         if (ch + 1 < nch)
@@ -1427,9 +1424,9 @@ __global__ __launch_bounds__(NW * 64) void scan_ws_kernel(
         }
     } else if constexpr (NJ == 2) {              // diagonal pairs | six off-diagonal pairs
         if (wave == 2)
-            helper_loop<D, DVS, 0, 0, HWS_DIAG_BLOCKS, true, 0>(c);
+            helper_loop<D, DVS, 0, 0, kDiagRowBlocks, true, 0>(c);
         else
-            helper_loop<D, DVS, 1, HWS_DIAG_BLOCKS, 4 - HWS_DIAG_BLOCKS, false, 1>(c);
+            helper_loop<D, DVS, 1, kDiagRowBlocks, 4 - kDiagRowBlocks, false, 1>(c);
     } else {                                     // diagonal | three | three
         if (wave == 1)
             helper_loop<D, DVS, 0, 0, 1, true, 0>(c);
