@@ -48,12 +48,14 @@ def _load():
             build()
         lib = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
-        lib.prism_oracle_prologue.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P,
+        lib.prism_oracle_prologue.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P, P,
                                               ctypes.c_int]
         lib.prism_oracle_prologue.restype = ctypes.c_int
-        lib.prism_oracle_fwd.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P, P, P, P,
-                                         ctypes.c_int64, P, P, ctypes.c_int]
+        lib.prism_oracle_fwd.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P, P, P, P, P, P, P,
+                                         P, ctypes.c_int64, P, P, ctypes.c_int]
         lib.prism_oracle_fwd.restype = ctypes.c_int
+        lib.prism_oracle_k_history.argtypes = [ctypes.POINTER(_Dims), P, P, P, P]
+        lib.prism_oracle_k_history.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -88,26 +90,52 @@ def _check(inp):
     return code, cu
 
 
-def prologue(inp, threads: Optional[int] = None) -> np.ndarray:
-    """Write keys kw [T, H, dk] in float64."""
+def _hist(inp, k_hist):
+    """Carried conv history [n_seqs, H, 3, dk] in the inputs' storage type, or None."""
+    if k_hist is None:
+        return None
+    want = np.float32 if inp.dtype == "f32" else np.uint16
+    k_hist = np.ascontiguousarray(k_hist)
+    if k_hist.dtype != want or k_hist.shape != (inp.n_seqs, inp.heads, 3, inp.dk):
+        raise TypeError(f"k_hist: expected {want.__name__} [{inp.n_seqs}, {inp.heads}, 3, {inp.dk}]")
+    return k_hist
+
+
+def _state(inp, S_init):
+    if S_init is None:
+        return None
+    S_init = np.ascontiguousarray(S_init, dtype=np.float64)
+    if S_init.shape != (inp.n_seqs, inp.heads, inp.dk, inp.dv):
+        raise ValueError("S_init: expected [n_seqs, H, dk, dv]")
+    return S_init
+
+
+def prologue(inp, threads: Optional[int] = None, k_hist=None) -> np.ndarray:
+    """Write keys kw [T, H, dk] in float64 (``k_hist``: carried conv history)."""
     code, cu = _check(inp)
+    hist = _hist(inp, k_hist)
     out = np.zeros((inp.total_tokens, inp.heads, inp.dk), dtype=np.float64)
     d = _dims(inp, code)
     rc = _load().prism_oracle_prologue(ctypes.byref(d), _ptr(cu), _ptr(inp.k), _ptr(inp.u),
                                        _ptr(inp.a), _ptr(inp.h), _ptr(inp.b), _ptr(inp.conv_w),
-                                       _ptr(out), threads or default_threads())
+                                       _ptr(hist), _ptr(out), threads or default_threads())
     if rc != 0:
         raise RuntimeError(f"prism_oracle_prologue failed ({rc})")
     return out
 
 
-def fwd(inp, chains: Optional[Sequence[int]] = None, threads: Optional[int] = None):
+def fwd(inp, chains: Optional[Sequence[int]] = None, threads: Optional[int] = None,
+        S_init=None, k_hist=None):
     """Forward pass.  Returns (o [T, H, dv], S_final [n_seqs, H, dk, dv]) in float64.
 
     ``chains`` restricts the evaluation to the listed (sequence * H + head)
-    chains; rows of other chains are left at zero.
+    chains; rows of other chains are left at zero.  ``S_init`` [n_seqs, H, dk,
+    dv] is the state each sequence starts from and ``k_hist`` [n_seqs, H, 3,
+    dk] (input storage type) the three k rows before each sequence's first
+    token; both default to zero.
     """
     code, cu = _check(inp)
+    hist, s0 = _hist(inp, k_hist), _state(inp, S_init)
     o = np.zeros((inp.total_tokens, inp.heads, inp.dv), dtype=np.float64)
     s = np.zeros((inp.n_seqs, inp.heads, inp.dk, inp.dv), dtype=np.float64)
     ch = None if chains is None else np.ascontiguousarray(np.asarray(chains, dtype=np.int64))
@@ -116,9 +144,34 @@ def fwd(inp, chains: Optional[Sequence[int]] = None, threads: Optional[int] = No
     d = _dims(inp, code)
     rc = _load().prism_oracle_fwd(ctypes.byref(d), _ptr(cu), _ptr(inp.q), _ptr(inp.k),
                                   _ptr(inp.v), _ptr(inp.u), _ptr(inp.g), _ptr(inp.b),
-                                  _ptr(inp.a), _ptr(inp.h), _ptr(inp.conv_w),
-                                  _ptr(ch), 0 if ch is None else int(ch.size),
+                                  _ptr(inp.a), _ptr(inp.h), _ptr(inp.conv_w), _ptr(s0),
+                                  _ptr(hist), _ptr(ch), 0 if ch is None else int(ch.size),
                                   _ptr(o), _ptr(s), threads or default_threads())
     if rc != 0:
         raise RuntimeError(f"prism_oracle_fwd failed ({rc})")
     return o, s
+
+
+def k_history(inp, k_hist=None) -> np.ndarray:
+    """The conv history to carry past the end of each sequence: [n_seqs, H, 3,
+    dk] float64, slot m = k at position (sequence end - 3 + m), read from
+    ``k_hist`` (or zero) for positions before the sequence start."""
+    code, cu = _check(inp)
+    hist = _hist(inp, k_hist)
+    out = np.zeros((inp.n_seqs, inp.heads, 3, inp.dk), dtype=np.float64)
+    rc = _load().prism_oracle_k_history(ctypes.byref(_dims(inp, code)), _ptr(cu), _ptr(inp.k),
+                                        _ptr(hist), _ptr(out))
+    if rc != 0:
+        raise RuntimeError(f"prism_oracle_k_history failed ({rc})")
+    return out
+
+
+def decode_step(step, S, k_hist, threads: Optional[int] = None):
+    """One token of every sequence: the recurrence itself with the state and
+    conv history carried in.  ``step`` holds one token per sequence
+    (cu_seqlens = 0, 1, ..., n_seqs).  Returns (o [n_seqs, H, dv], S_new,
+    k_hist_new [n_seqs, H, 3, dk]) in float64."""
+    if not np.array_equal(step.cu_seqlens, np.arange(step.n_seqs + 1)):
+        raise ValueError("a decode step holds exactly one token per sequence")
+    o, s = fwd(step, threads=threads, S_init=S, k_hist=k_hist)
+    return o, s, k_history(step, k_hist)

@@ -9,11 +9,13 @@
  *
  * What it computes (one reading of the pages, fixed once for all code):
  *
- *   Per (sequence n, head e) chain, state S in R^{dk x dv}, S = 0 at the
- *   sequence start.  For every token t of the sequence, in order:
+ *   Per (sequence n, head e) chain, state S in R^{dk x dv}, S = S_init[n, e]
+ *   at the sequence start (zero when no S_init is given).  For every token t
+ *   of the sequence, in order:
  *
  *     r_0[i]  = sum_{m=0..3} w[e,i,m] * k[t-3+m, e, i]        causal depthwise
- *               (taps before the sequence start read zero)      ShortConv, width 4
+ *               (taps before the sequence start read the       ShortConv, width 4
+ *                carried history, zero when none is given)
  *     r_1     = r_0
  *     r_l     = r_0 * prod_{j=1..l-1} (1 - a_j * h_j)          closed-form residual
  *     kw      = b_t k_t + sum_{l=1..L-1} a_l * r_l * u_l        write key
@@ -39,6 +41,11 @@
  *     residual update r^(l+1) = r^(l) - delta^(l)).
  *   - ICML 2026 poster abstract: a short convolution anchors the initial
  *     residual.
+ *   - WeChat page, section 背景：无限背包 vs 有限背包, and the poster page's
+ *     lay summary: the whole history lives in a fixed-size state matrix
+ *     updated one token at a time (an RNN recurrence), so a sequence can be
+ *     processed in pieces by carrying S (and the convolution's last three
+ *     inputs) from one piece to the next.
  *
  * Readings where the pages are silent or garbled (all code follows them):
  *   - the product in the residual closed form runs over j = 1..l-1, so the
@@ -46,7 +53,10 @@
  *   - conv tap 3 multiplies the current token, taps 0..2 the three before it;
  *     no bias and no activation after the convolution;
  *   - g and b are per (token, head) scalars; g is a linear-space gate;
- *   - no query scaling; the initial state is zero.
+ *   - no query scaling; the initial state is zero unless S_init is given;
+ *   - carried conv history k_hist [n_seqs, H, 3, dk]: slot m holds k at
+ *     position (sequence start - 3 + m), i.e. slot 2 is the token just before
+ *     the first one; zero when no history is given.
  *
  * Precision: all arithmetic in double.  Inputs are fp32 or bf16 (raw 16-bit
  * patterns) and are widened exactly.
@@ -79,11 +89,25 @@ static double elem(const void* p, int64_t dtype, int64_t i)
     return (double)f;
 }
 
-/* Write key of token t, head e into kw[0..dk).  seq_start is the first token
- * of t's sequence (conv taps before it read zero). */
+/* k at position tau, channel i, of sequence n (first token seq_start), head e:
+ * the token's own row, or the carried history before the sequence start. */
+static double k_at(const oracle_dims* d, const void* k, const void* k_hist, int64_t n,
+                   int64_t seq_start, int64_t tau, int64_t e, int64_t i)
+{
+    const int64_t H = d->heads, dk = d->dk;
+    if (tau >= seq_start)
+        return elem(k, d->dtype, (tau * H + e) * dk + i);
+    if (!k_hist || tau < seq_start - 3)
+        return 0.0;
+    return elem(k_hist, d->dtype, ((n * H + e) * 3 + (tau - seq_start + 3)) * dk + i);
+}
+
+/* Write key of token t, head e into kw[0..dk).  t belongs to sequence n, whose
+ * first token is seq_start (conv taps before it read the carried history, or
+ * zero without one). */
 static void write_key(const oracle_dims* d, const void* k, const void* u, const void* a,
-                      const void* h, const void* b, const void* conv_w,
-                      int64_t seq_start, int64_t t, int64_t e, double* kw)
+                      const void* h, const void* b, const void* conv_w, const void* k_hist,
+                      int64_t n, int64_t seq_start, int64_t t, int64_t e, double* kw)
 {
     const int64_t H = d->heads, dk = d->dk, L = d->L, dt = d->dtype;
     const double bt = elem(b, dt, t * H + e);
@@ -91,10 +115,8 @@ static void write_key(const oracle_dims* d, const void* k, const void* u, const 
         /* r_0: causal depthwise convolution over k along the token axis. */
         double r0 = 0.0;
         for (int64_t m = 0; m < 4; ++m) {
-            int64_t tau = t - 3 + m;
-            if (tau < seq_start)
-                continue;
-            r0 += elem(conv_w, dt, (e * dk + i) * 4 + m) * elem(k, dt, (tau * H + e) * dk + i);
+            r0 += elem(conv_w, dt, (e * dk + i) * 4 + m) *
+                  k_at(d, k, k_hist, n, seq_start, t - 3 + m, e, i);
         }
         double acc = bt * elem(k, dt, (t * H + e) * dk + i);
         for (int64_t l = 1; l <= L - 1; ++l) {
@@ -111,10 +133,11 @@ static void write_key(const oracle_dims* d, const void* k, const void* u, const 
     }
 }
 
-/* kw for every token and head: out[T, H, dk] (double). */
+/* kw for every token and head: out[T, H, dk] (double).  k_hist may be NULL. */
 int prism_oracle_prologue(const oracle_dims* d, const int32_t* cu_seqlens,
                           const void* k, const void* u, const void* a, const void* h,
-                          const void* b, const void* conv_w, double* kw_out, int nthreads)
+                          const void* b, const void* conv_w, const void* k_hist,
+                          double* kw_out, int nthreads)
 {
     if (!d || !cu_seqlens || !k || !b || !conv_w || !kw_out || d->L < 1)
         return 1;
@@ -127,7 +150,8 @@ int prism_oracle_prologue(const oracle_dims* d, const int32_t* cu_seqlens,
     for (int64_t item = 0; item < n_items; ++item) {
         int64_t n = item / H, e = item % H;
         for (int64_t t = cu_seqlens[n]; t < cu_seqlens[n + 1]; ++t)
-            write_key(d, k, u, a, h, b, conv_w, cu_seqlens[n], t, e, kw_out + (t * H + e) * dk);
+            write_key(d, k, u, a, h, b, conv_w, k_hist, n, cu_seqlens[n], t, e,
+                      kw_out + (t * H + e) * dk);
     }
     return 0;
 }
@@ -135,12 +159,15 @@ int prism_oracle_prologue(const oracle_dims* d, const int32_t* cu_seqlens,
 /*
  * Full forward.  chains: optional list of (sequence * heads + head) indices to
  * evaluate (NULL = all).  Only the selected chains' rows of o_out [T, H, dv]
- * and blocks of s_out [n_seqs, H, dk, dv] are written.
+ * and blocks of s_out [n_seqs, H, dk, dv] are written.  s_init
+ * [n_seqs, H, dk, dv] and k_hist [n_seqs, H, 3, dk] (input dtype) may be NULL
+ * (zero state, zero history).
  */
 int prism_oracle_fwd(const oracle_dims* d, const int32_t* cu_seqlens,
                      const void* q, const void* k, const void* v, const void* u,
                      const void* g, const void* b, const void* a, const void* h,
-                     const void* conv_w, const int64_t* chains, int64_t n_chains,
+                     const void* conv_w, const double* s_init, const void* k_hist,
+                     const int64_t* chains, int64_t n_chains,
                      double* o_out, double* s_out, int nthreads)
 {
     if (!d || !cu_seqlens || !q || !k || !v || !g || !b || !conv_w || !o_out || !s_out || d->L < 1)
@@ -167,8 +194,10 @@ int prism_oracle_fwd(const oracle_dims* d, const int32_t* cu_seqlens,
             free(S); free(kw); free(kt); free(p); free(qt); free(vt);
             continue;
         }
+        if (s_init)
+            memcpy(S, s_init + c * dk * dv, (size_t)(dk * dv) * sizeof(double));
         for (int64_t t = cu_seqlens[n]; t < cu_seqlens[n + 1]; ++t) {
-            write_key(d, k, u, a, h, b, conv_w, cu_seqlens[n], t, e, kw);
+            write_key(d, k, u, a, h, b, conv_w, k_hist, n, cu_seqlens[n], t, e, kw);
             const double gt = elem(g, dt, t * H + e);
             const double bt = elem(b, dt, t * H + e);
             for (int64_t i = 0; i < dk; ++i) {
@@ -200,4 +229,25 @@ int prism_oracle_fwd(const oracle_dims* d, const int32_t* cu_seqlens,
         free(S); free(kw); free(kt); free(p); free(qt); free(vt);
     }
     return status;
+}
+
+/*
+ * The convolution history to carry into the next piece of each sequence:
+ * out[n, e, m, :] = k at position (sequence end - 3 + m), taken from the
+ * carried history k_hist (may be NULL: zero) where that position lies before
+ * the sequence start.  out is [n_seqs, H, 3, dk] (double).
+ */
+int prism_oracle_k_history(const oracle_dims* d, const int32_t* cu_seqlens, const void* k,
+                           const void* k_hist, double* out)
+{
+    if (!d || !cu_seqlens || !out || (d->total_tokens > 0 && !k))
+        return 1;
+    const int64_t H = d->heads, dk = d->dk;
+    for (int64_t n = 0; n < d->n_seqs; ++n)
+        for (int64_t e = 0; e < H; ++e)
+            for (int64_t m = 0; m < 3; ++m)
+                for (int64_t i = 0; i < dk; ++i)
+                    out[((n * H + e) * 3 + m) * dk + i] =
+                        k_at(d, k, k_hist, n, cu_seqlens[n], cu_seqlens[n + 1] - 3 + m, e, i);
+    return 0;
 }

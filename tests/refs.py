@@ -27,14 +27,17 @@ def f64(x):
 # ---------------------------------------------------------------------------
 # write branch
 # ---------------------------------------------------------------------------
-def anchor_convolve(k, conv_w, cu):
+def anchor_convolve(k, conv_w, cu, hist=None):
     """ShortConv anchor r_0 by numpy.convolve, one channel and sequence at a time.
 
     ``np.convolve(x, w[::-1])[n] = sum_m w[m] x[n - 3 + m]`` with x read as
     zero before the sequence start: the causal width-4 depthwise convolution.
+    With ``hist`` [n_seqs, H, 3, dk], the three rows before each sequence are
+    prepended to it (oldest first) and the first three outputs dropped.
     """
     k = f64(k)
     w = f64(conv_w)
+    hist = f64(hist)
     T, H, dk = k.shape
     r0 = np.zeros_like(k)
     for n in range(len(cu) - 1):
@@ -43,11 +46,15 @@ def anchor_convolve(k, conv_w, cu):
             continue
         for e in range(H):
             for i in range(dk):
-                r0[lo:hi, e, i] = np.convolve(k[lo:hi, e, i], w[e, i, ::-1])[: hi - lo]
+                x = k[lo:hi, e, i]
+                if hist is not None:
+                    x = np.concatenate([hist[n, e, :, i], x])
+                full = np.convolve(x, w[e, i, ::-1])[: len(x)]
+                r0[lo:hi, e, i] = full[len(x) - (hi - lo):]
     return r0
 
 
-def write_key_iterative(inp):
+def write_key_iterative(inp, hist=None):
     """kw by running the residual chain as repeated subtraction.
 
     Linearised refinement step of the gist.science summary, section 2.2:
@@ -60,7 +67,7 @@ def write_key_iterative(inp):
     kw = b[:, :, None] * k
     if inp.L == 1:
         return kw
-    r = anchor_convolve(inp.k, inp.conv_w, inp.cu_seqlens)
+    r = anchor_convolve(inp.k, inp.conv_w, inp.cu_seqlens, hist)
     a, h, u = f64(inp.a), f64(inp.h), f64(inp.u)
     for s in range(inp.L - 1):
         kw = kw + a[:, :, s] * r * u[:, :, s]
@@ -71,11 +78,12 @@ def write_key_iterative(inp):
 # ---------------------------------------------------------------------------
 # state recurrence
 # ---------------------------------------------------------------------------
-def gdn_delta_form(inp):
+def gdn_delta_form(inp, S0=None):
     """L = 1 reference: Gated DeltaNet in prediction-error form.
 
     S <- g S + b k (v - g S^T k)^T, o = S^T q.  Algebraically equal to
-    g (I - b k k^T) S + b k v^T but evaluated differently.
+    g (I - b k k^T) S + b k v^T but evaluated differently.  ``S0``
+    [n_seqs, H, dk, dv]: start states (zero by default).
     """
     q, k, v, g, b = (f64(x) for x in (inp.q, inp.k, inp.v, inp.g, inp.b))
     T, H, dk = k.shape
@@ -85,7 +93,7 @@ def gdn_delta_form(inp):
     S_fin = np.zeros((len(cu) - 1, H, dk, dv))
     for n in range(len(cu) - 1):
         for e in range(H):
-            S = np.zeros((dk, dv))
+            S = np.zeros((dk, dv)) if S0 is None else np.array(S0[n, e], dtype=np.float64)
             for t in range(int(cu[n]), int(cu[n + 1])):
                 pred = g[t, e] * (S.T @ k[t, e])
                 S = g[t, e] * S + b[t, e] * np.outer(k[t, e], v[t, e] - pred)
@@ -110,7 +118,7 @@ def linear_attention_bruteforce(q, kw, v, cu):
     return o
 
 
-def chunkwise_ut(inp, kw, C):
+def chunkwise_ut(inp, kw, C, S0=None):
     """Dense chunkwise (WY/UT) evaluation of the recurrence, chunk size C.
 
     Inside a chunk with incoming state S0, cumulative log-gates lam and
@@ -128,7 +136,7 @@ def chunkwise_ut(inp, kw, C):
     S_fin = np.zeros((len(cu) - 1, H, dk, dv))
     for n in range(len(cu) - 1):
         for e in range(H):
-            S = np.zeros((dk, dv))
+            S = np.zeros((dk, dv)) if S0 is None else np.array(S0[n, e], dtype=np.float64)
             for c0 in range(int(cu[n]), int(cu[n + 1]), C):
                 c1 = min(c0 + C, int(cu[n + 1]))
                 m = c1 - c0
