@@ -4,8 +4,10 @@ Argument marshalling only: torch tensors supply device memory and the current
 HIP stream; every step of the operator runs in the library's HIP kernels.  The
 functions raise if the library is not built -- there is no fallback path.
 
-Names follow the C ABI: ``fwd`` -> prism_fwd, ``prologue`` -> prism_prologue,
-``scan`` -> prism_scan, ``workspace_bytes`` -> prism_workspace_bytes.
+Names follow the C ABI: ``fwd`` -> prism_fwd, ``fwd_resume`` ->
+prism_fwd_resume, ``decode_step`` -> prism_decode_step, ``prologue`` ->
+prism_prologue, ``scan`` -> prism_scan, ``workspace_bytes`` ->
+prism_workspace_bytes.
 """
 from __future__ import annotations
 
@@ -57,6 +59,10 @@ def lib():
         L.prism_prologue.restype = I
         L.prism_scan.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
         L.prism_scan.restype = I
+        L.prism_fwd_resume.argtypes = [D, P, P, P, P, P, P, P, P, P, P, I, P, P, P, P, P, P, S, P]
+        L.prism_fwd_resume.restype = I
+        L.prism_decode_step.argtypes = [D, P, P, P, P, P, P, P, P, P, I, P, P, P, P]
+        L.prism_decode_step.restype = I
         L.prism_status_str.argtypes = [I]
         L.prism_status_str.restype = ctypes.c_char_p
         L.prism_abi_version.argtypes = []
@@ -198,6 +204,64 @@ def fwd(q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L: int, o=None, S_final=None
         _ptr(conv_w), _ptr(cu_seqlens), int(L), _ptr(o), _ptr(S_final), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return o, S_final
+
+
+def fwd_resume(q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L: int, S_init=None, k_hist=None,
+               o=None, S_final=None, k_hist_out=None, workspace=None, stream=None):
+    """Forward pass continuing from a carried state and conv history
+    (prism_fwd_resume).  ``S_init`` fp32 [n_seqs, H, dk, dv] and ``k_hist``
+    [n_seqs, H, 3, dk] default to zero; ``k_hist_out`` (optional, may be
+    ``k_hist``) receives the history to carry on.  Returns (o, S_final,
+    k_hist_out)."""
+    d = _dims_of(q, v, cu_seqlens)
+    _check_write_branch(d, q.dtype, k, u, a, h, b, conv_w, L)
+    _check_scan(d, q.dtype, q, k, k, v, g, b)
+    n, H = d.n_seqs, d.heads
+    if S_init is not None:
+        _expect("S_init", S_init, (n, H, d.dk, d.dv), torch.float32)
+    for name, x in (("k_hist", k_hist), ("k_hist_out", k_hist_out)):
+        if x is not None:
+            _expect(name, x, (n, H, 3, d.dk), q.dtype)
+    need = workspace_bytes(d, L)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if o is None:
+        o = torch.empty_like(v)
+    if S_final is None:
+        S_final = torch.empty((n, H, d.dk, d.dv), dtype=torch.float32, device=q.device)
+    _expect("o", o, v.shape, v.dtype)
+    _expect("S_final", S_final, (n, H, d.dk, d.dv), torch.float32)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    _check("prism_fwd_resume", lib().prism_fwd_resume(
+        ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(g), _ptr(b), _ptr(a), _ptr(h),
+        _ptr(conv_w), _ptr(cu_seqlens), int(L), _ptr(S_init), _ptr(k_hist), _ptr(o),
+        _ptr(S_final), _ptr(k_hist_out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o, S_final, k_hist_out
+
+
+def decode_step(q, k, v, u, g, b, a, h, conv_w, L: int, S, k_hist, o=None, stream=None):
+    """One new token per sequence (prism_decode_step): q, k [N, H, dk], v [N, H,
+    dv], u/a/h [N, H, L-1, dk], g/b [N, H].  ``S`` fp32 [N, H, dk, dv] and
+    ``k_hist`` [N, H, 3, dk] are updated in place.  Returns o [N, H, dv]."""
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q / v must be [N, H, d]")
+    N, H, dk = q.shape
+    d = Dims(N, N, H, dk, v.shape[2], _dtype_code(q))
+    _check_write_branch(d, q.dtype, k, u, a, h, b, conv_w, L)
+    _expect("q", q, (N, H, dk), q.dtype)
+    _expect("v", v, (N, H, d.dv), q.dtype)
+    _expect("g", g, (N, H), q.dtype)
+    _expect("S", S, (N, H, dk, d.dv), torch.float32)
+    _expect("k_hist", k_hist, (N, H, 3, dk), q.dtype)
+    if o is None:
+        o = torch.empty_like(v)
+    _expect("o", o, v.shape, v.dtype)
+    _check("prism_decode_step", lib().prism_decode_step(
+        ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(g), _ptr(b), _ptr(a), _ptr(h),
+        _ptr(conv_w), int(L), _ptr(S), _ptr(k_hist), _ptr(o), _stream(stream)))
+    return o
 
 
 def to_device(inp, device="cuda") -> dict:

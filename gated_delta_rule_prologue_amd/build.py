@@ -22,7 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libprism.so")
-SOURCES = ["prism_api.hip", "prologue.hip", "chunk_scan.hip", "chunk_scan_bf16.hip"]
+SOURCES = ["prism_api.hip", "prologue.hip", "chunk_scan.hip", "chunk_scan_bf16.hip", "decode.hip"]
 CHECKED = ["chunk_scan_bf16.hip", "chunk_scan.hip"]      # sources with mixed-size MFMA chains
 ARCH = "gfx950"
 

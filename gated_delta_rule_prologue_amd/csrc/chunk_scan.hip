@@ -240,8 +240,8 @@ template <typename T, int D, int DVS>
 __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ kw,
     const T* __restrict__ v, const T* __restrict__ g, const T* __restrict__ b,
-    const int32_t* __restrict__ cu, int H, int DV, int n_slices, T* __restrict__ o,
-    float* __restrict__ s_final)
+    const int32_t* __restrict__ cu, int H, int DV, int n_slices,
+    const float* __restrict__ s_init, T* __restrict__ o, float* __restrict__ s_final)
 {
     using Ly = Layout<T, D, DVS>;
     using M = Mfma<T>;
@@ -301,10 +301,30 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
             z[i] = make_uint4(0u, 0u, 0u, 0u);
     }
 
+    // state tile qd of this wavefront: rows ib * 16 + (lane >> 4) * 4 + r, column
+    // jb * 16 + (lane & 15) of the slice; start state from s_init (or zero), also
+    // kept transposed in LDS as the b-step operand S0^T
     f32x4_t S[NSW];
 #pragma unroll
-    for (int i = 0; i < NSW; ++i)
-        S[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int qd = 0; qd < NSW; ++qd) {
+        S[qd] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (s_init) {
+            const int sidx = wave * NSW + qd, ib = sidx / NJ, jb = sidx % NJ;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = ib * 16 + (lane >> 4) * 4 + r;
+                S[qd][r] = s_init[(((int64_t)n * H + e) * D + i) * DV + j0 + jb * 16 + (lane & 15)];
+            }
+        }
+    }
+    if (s_init) {
+        __syncthreads();                         // after the zeroing of S0^T above
+#pragma unroll
+        for (int qd = 0; qd < NSW; ++qd) {
+            const int sidx = wave * NSW + qd, ib = sidx / NJ, jb = sidx % NJ;
+            st4(sS0t + (jb * 16 + (lane & 15)) * LDD + ib * 16 + (lane >> 4) * 4, S[qd]);
+        }
+    }
 
     // ---- register prefetch of one chunk ----
     // Per-thread element offsets inside a chunk do not change from chunk to
@@ -634,7 +654,7 @@ static hipError_t launch(const ScanArgs& p, hipStream_t stream)
     hipLaunchKernelGGL((chunk_scan_kernel<T, D, DVS>), dim3((unsigned)blocks), dim3(kThreads), 0,
                        stream, (const T*)p.q, (const T*)p.k, (const T*)p.kw, (const T*)p.v,
                        (const T*)p.g, (const T*)p.b, p.cu_seqlens, p.heads, p.dv, n_slices,
-                       (T*)p.o, p.s_final);
+                       p.s_init, (T*)p.o, p.s_final);
     return hipGetLastError();
 }
 

@@ -482,6 +482,25 @@ __device__ __forceinline__ void state_path(
 
 // Off-diagonal (t-block, s-block) pairs; wavefront w takes kOff[w] and kOff[w + 4].
 __constant__ const int kOffT[6] = {1, 2, 2, 3, 3, 3};
+// Start state of one state wavefront: S[ib][r] = S_init[ib * 16 + lg * 4 + r][li]
+// relative to base (the wavefront's first column of the chain's fp32 state,
+// row pitch DV), or zero without a start state.
+template <int D>
+__device__ __forceinline__ void load_state(f32x4_t (&S)[D / 16], const float* s_init, int64_t base,
+                                           int DV, int lane, bool active)
+{
+    const int li = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int ib = 0; ib < D / 16; ++ib) {
+        S[ib] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (s_init && active) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                S[ib][r] = s_init[base + (int64_t)(ib * 16 + lg * 4 + r) * DV + li];
+        }
+    }
+}
+
 __constant__ const int kOffS[6] = {0, 0, 1, 0, 1, 2};
 
 template <int D, int DVS>
@@ -489,8 +508,8 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ kw, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ g, const uint16_t* __restrict__ b,
-    const int32_t* __restrict__ cu, int H, int DV, int n_slices, uint16_t* __restrict__ o,
-    float* __restrict__ s_final)
+    const int32_t* __restrict__ cu, int H, int DV, int n_slices,
+    const float* __restrict__ s_init, uint16_t* __restrict__ o, float* __restrict__ s_final)
 {
     using Ly = Layout<D, DVS>;
     constexpr int LDD = Ly::LDD, LDC = Ly::LDC, LDV = Ly::LDV, LDT = Ly::LDT;
@@ -538,9 +557,8 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(
     }
 
     f32x4_t S[NI];                               // S[:, 16 jb : 16 jb + 16] of wavefront jb
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-        S[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    load_state<D>(S, s_init, (((int64_t)n * H + e) * D) * DV + j0 + wave * 16, DV, lane,
+                  wave < NJ);
 
     // ---- register prefetch (per-thread offsets fixed across chunks) ----
     int offq[NQ], tq[NQ], offv[NVT], tv[NVT];
@@ -787,6 +805,7 @@ struct WsCtx {
     unsigned char* smem;
     const uint16_t *q, *k, *kw, *v, *g, *b;
     uint16_t* o;
+    const float* s_init;
     float* s_final;
     int n, e, H, DV, j0, seq0, seq1, nchunks, lane;
     int64_t rowQK, rowV;
@@ -1314,9 +1333,8 @@ __device__ __forceinline__ void state_loop(const WsCtx& c, int jb)
     const WsBuf<D, DVS> m{c.smem};
     const int lane = c.lane, li = lane & 15, lg = lane >> 4;
     f32x4_t S[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-        S[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    load_state<D>(S, c.s_init, (((int64_t)c.n * c.H + c.e) * D) * c.DV + c.j0 + jb * 16, c.DV,
+                  lane, true);
     lds_barrier();
     lds_barrier();
     lds_barrier();
@@ -1370,8 +1388,8 @@ __global__ __launch_bounds__(NW * 64) void scan_ws_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ kw, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ g, const uint16_t* __restrict__ b,
-    const int32_t* __restrict__ cu, int H, int DV, int n_slices, uint16_t* __restrict__ o,
-    float* __restrict__ s_final)
+    const int32_t* __restrict__ cu, int H, int DV, int n_slices,
+    const float* __restrict__ s_init, uint16_t* __restrict__ o, float* __restrict__ s_final)
 {
     using Ly = LayoutWS<D, DVS>;
     constexpr int NJ = DVS / 16;
@@ -1389,6 +1407,7 @@ __global__ __launch_bounds__(NW * 64) void scan_ws_kernel(
     c.smem = smem;
     c.q = q; c.k = k; c.kw = kw; c.v = v; c.g = g; c.b = b;
     c.o = o;
+    c.s_init = s_init;
     c.s_final = s_final;
     c.n = chain / H;
     c.e = chain % H;
@@ -1447,7 +1466,8 @@ static hipError_t launch_ws(const ScanArgs& p, hipStream_t stream)
     hipLaunchKernelGGL((scan_ws_kernel<D, DVS, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
                        (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.kw,
                        (const uint16_t*)p.v, (const uint16_t*)p.g, (const uint16_t*)p.b,
-                       p.cu_seqlens, p.heads, p.dv, n_slices, (uint16_t*)p.o, p.s_final);
+                       p.cu_seqlens, p.heads, p.dv, n_slices, p.s_init, (uint16_t*)p.o,
+                       p.s_final);
     return hipGetLastError();
 }
 
@@ -1461,7 +1481,8 @@ static hipError_t launch(const ScanArgs& p, hipStream_t stream)
     hipLaunchKernelGGL((scan_kernel<D, DVS>), dim3((unsigned)blocks), dim3(kThreads), 0, stream,
                        (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.kw,
                        (const uint16_t*)p.v, (const uint16_t*)p.g, (const uint16_t*)p.b,
-                       p.cu_seqlens, p.heads, p.dv, n_slices, (uint16_t*)p.o, p.s_final);
+                       p.cu_seqlens, p.heads, p.dv, n_slices, p.s_init, (uint16_t*)p.o,
+                       p.s_final);
     return hipGetLastError();
 }
 

@@ -12,6 +12,7 @@ struct PrologueArgs {
     int strip;                      // tokens walked by one thread: 4, 8 or 16
     bool narrow;                    // 8-byte instead of 16-byte channel groups
     const void *k, *u, *a, *h, *b, *conv_w;
+    const void* k_hist;             // [n_seqs, H, 3, dk] carried conv history, or null (zero)
     const int32_t* cu_seqlens;
     void* kw;
 };
@@ -24,11 +25,31 @@ struct ScanArgs {
     int ws_waves;                   // wavefronts of the specialised kernel: 4, or 8 (dv_slice 32)
     const void *q, *k, *kw, *v, *g, *b;
     const int32_t* cu_seqlens;
+    const float* s_init;            // [n_seqs, H, dk, dv] start states, or null (zero)
     void* o;
     float* s_final;
 };
 
 hipError_t launch_prologue(const PrologueArgs& p, hipStream_t stream);
+
+// k_hist_out[n, e, m, :] = k at position (end of sequence n) - 3 + m, read from
+// k_hist (or zero) before the sequence start.  k_hist_out may equal k_hist.
+hipError_t launch_k_history(bool bf16, int n_seqs, int heads, int dk, const void* k,
+                            const void* k_hist, const int32_t* cu_seqlens, void* k_hist_out,
+                            hipStream_t stream);
+
+struct DecodeArgs {
+    bool bf16;
+    int n_seqs, heads, dk, dv, L;
+    const void *q, *k, *v, *u, *a, *h, *g, *b, *conv_w;
+    float* S;                       // [n_seqs, H, dk, dv], updated in place
+    void* k_hist;                   // [n_seqs, H, 3, dk], updated in place
+    void* o;
+};
+
+// One token per sequence through the recurrence (state and history in place).
+hipError_t launch_decode(const DecodeArgs& p, hipStream_t stream);
+bool decode_supported(int dk, int dv);
 
 // Generic chunk scan (fp32 and bf16 operands), LDS-staged intermediates.
 // Returns hipErrorInvalidValue when (dtype, dk, dv_slice) has no kernel.

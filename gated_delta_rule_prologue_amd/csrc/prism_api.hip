@@ -94,6 +94,105 @@ prism_status check_scan_shape(const prism_dims* d)
 
 prism_status from_hip(hipError_t e) { return e == hipSuccess ? PRISM_OK : PRISM_EHIP; }
 
+// Optional pointer: null, or 16-byte aligned.
+bool opt_ok(const void* p) { return aligned16(p); }
+
+prism_status prologue_impl(const prism_dims* d, const void* k, const void* u, const void* a,
+                           const void* h, const void* b, const void* conv_w, const void* k_hist,
+                           const int32_t* cu_seqlens, int L, void* kw, void* stream)
+{
+    if (!dims_ok(d) || L < 1 || L > PRISM_MAX_LEVELS)
+        return PRISM_EINVAL;
+    if (!tok_ok(d, k) || !tok_ok(d, b) || !ptr_ok(conv_w) || !ptr_ok(cu_seqlens) ||
+        !tok_ok(d, kw) || !opt_ok(k_hist))
+        return PRISM_EINVAL;
+    if (L > 1 && (!tok_ok(d, u) || !tok_ok(d, a) || !tok_ok(d, h)))
+        return PRISM_EINVAL;
+    const int vec = d->dtype == PRISM_BF16 ? 8 : 4;
+    if (d->dk % vec != 0)
+        return PRISM_EUNSUPPORTED;
+    prism::PrologueArgs p;
+    p.bf16 = d->dtype == PRISM_BF16;
+    p.n_seqs = d->n_seqs;
+    p.total_tokens = d->total_tokens;
+    p.heads = d->heads;
+    p.dk = d->dk;
+    p.L = L;
+    p.strip = env_int("PRISM_PROLOGUE_STRIP", 8);      // 4, 8 or 16 tokens per thread
+    if (p.strip != 4 && p.strip != 16)
+        p.strip = 8;
+    p.narrow = env_int("PRISM_PROLOGUE_NARROW", 0) != 0;
+    p.k = k; p.u = u; p.a = a; p.h = h; p.b = b; p.conv_w = conv_w;
+    p.k_hist = k_hist;
+    p.cu_seqlens = cu_seqlens;
+    p.kw = kw;
+    return from_hip(prism::launch_prologue(p, (hipStream_t)stream));
+}
+
+prism_status scan_impl(const prism_dims* d, const void* q, const void* k, const void* kw,
+                       const void* v, const void* g, const void* b, const int32_t* cu_seqlens,
+                       const float* S_init, void* o, float* S_final, void* stream)
+{
+    if (!dims_ok(d))
+        return PRISM_EINVAL;
+    if (!tok_ok(d, q) || !tok_ok(d, k) || !tok_ok(d, kw) || !tok_ok(d, v) || !tok_ok(d, g) ||
+        !tok_ok(d, b) || !ptr_ok(cu_seqlens) || !tok_ok(d, o) || !ptr_ok(S_final) ||
+        !opt_ok(S_init))
+        return PRISM_EINVAL;
+    prism_status st = check_scan_shape(d);
+    if (st != PRISM_OK)
+        return st;
+    prism::ScanArgs p;
+    p.bf16 = d->dtype == PRISM_BF16;
+    p.n_seqs = d->n_seqs;
+    p.total_tokens = d->total_tokens;
+    p.heads = d->heads;
+    p.dk = d->dk;
+    p.dv = d->dv;
+    p.dv_slice = pick_dv_slice(d);
+    p.specialised = p.bf16 && p.dv_slice <= 32 && env_int("PRISM_SCAN_SPECIALISED", 1) != 0;
+    p.ws_waves = env_int("PRISM_SCAN_WAVES", 8) == 4 ? 4 : 8;
+    p.q = q; p.k = k; p.kw = kw; p.v = v; p.g = g; p.b = b;
+    p.cu_seqlens = cu_seqlens;
+    p.s_init = S_init;
+    p.o = o;
+    p.s_final = S_final;
+    if (use_bf16_kernel(d, p.dv_slice))
+        return from_hip(prism::launch_scan_bf16(p, (hipStream_t)stream));
+    return from_hip(prism::launch_scan(p, (hipStream_t)stream));
+}
+
+prism_status fwd_impl(const prism_dims* d, const void* q, const void* k, const void* v,
+                      const void* u, const void* g, const void* b, const void* a, const void* h,
+                      const void* conv_w, const int32_t* cu_seqlens, int L, const float* S_init,
+                      const void* k_hist, void* o, float* S_final, void* k_hist_out,
+                      void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!dims_ok(d) || L < 1 || L > PRISM_MAX_LEVELS)
+        return PRISM_EINVAL;
+    if (!tok_ok(d, q) || !tok_ok(d, k) || !tok_ok(d, v) || !tok_ok(d, g) || !tok_ok(d, b) ||
+        !ptr_ok(conv_w) || !ptr_ok(cu_seqlens) || !tok_ok(d, o) || !ptr_ok(S_final) ||
+        !ptr_ok(workspace) || !opt_ok(S_init) || !opt_ok(k_hist) || !opt_ok(k_hist_out))
+        return PRISM_EINVAL;
+    if (L > 1 && (!tok_ok(d, u) || !tok_ok(d, a) || !tok_ok(d, h)))
+        return PRISM_EINVAL;
+    if (workspace_bytes < prism_workspace_bytes(d, L))
+        return PRISM_EINVAL;
+    prism_status st = check_scan_shape(d);
+    if (st != PRISM_OK)
+        return st;
+    st = prologue_impl(d, k, u, a, h, b, conv_w, k_hist, cu_seqlens, L, workspace, stream);
+    if (st != PRISM_OK)
+        return st;
+    st = scan_impl(d, q, k, workspace, v, g, b, cu_seqlens, S_init, o, S_final, stream);
+    if (st != PRISM_OK || !k_hist_out)
+        return st;
+    // after the prologue on the same stream: k_hist_out may be k_hist itself
+    return from_hip(prism::launch_k_history(d->dtype == PRISM_BF16, d->n_seqs, d->heads, d->dk,
+                                            k, k_hist, cu_seqlens, k_hist_out,
+                                            (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -124,62 +223,14 @@ prism_status prism_prologue(const prism_dims* d, const void* k, const void* u, c
                             const void* h, const void* b, const void* conv_w,
                             const int32_t* cu_seqlens, int L, void* kw, void* stream)
 {
-    if (!dims_ok(d) || L < 1 || L > PRISM_MAX_LEVELS)
-        return PRISM_EINVAL;
-    if (!tok_ok(d, k) || !tok_ok(d, b) || !ptr_ok(conv_w) || !ptr_ok(cu_seqlens) ||
-        !tok_ok(d, kw))
-        return PRISM_EINVAL;
-    if (L > 1 && (!tok_ok(d, u) || !tok_ok(d, a) || !tok_ok(d, h)))
-        return PRISM_EINVAL;
-    const int vec = d->dtype == PRISM_BF16 ? 8 : 4;
-    if (d->dk % vec != 0)
-        return PRISM_EUNSUPPORTED;
-    prism::PrologueArgs p;
-    p.bf16 = d->dtype == PRISM_BF16;
-    p.n_seqs = d->n_seqs;
-    p.total_tokens = d->total_tokens;
-    p.heads = d->heads;
-    p.dk = d->dk;
-    p.L = L;
-    p.strip = env_int("PRISM_PROLOGUE_STRIP", 8);      // 4, 8 or 16 tokens per thread
-    if (p.strip != 4 && p.strip != 16)
-        p.strip = 8;
-    p.narrow = env_int("PRISM_PROLOGUE_NARROW", 0) != 0;
-    p.k = k; p.u = u; p.a = a; p.h = h; p.b = b; p.conv_w = conv_w;
-    p.cu_seqlens = cu_seqlens;
-    p.kw = kw;
-    return from_hip(prism::launch_prologue(p, (hipStream_t)stream));
+    return prologue_impl(d, k, u, a, h, b, conv_w, nullptr, cu_seqlens, L, kw, stream);
 }
 
 prism_status prism_scan(const prism_dims* d, const void* q, const void* k, const void* kw,
                         const void* v, const void* g, const void* b, const int32_t* cu_seqlens,
                         void* o, float* S_final, void* stream)
 {
-    if (!dims_ok(d))
-        return PRISM_EINVAL;
-    if (!tok_ok(d, q) || !tok_ok(d, k) || !tok_ok(d, kw) || !tok_ok(d, v) || !tok_ok(d, g) ||
-        !tok_ok(d, b) || !ptr_ok(cu_seqlens) || !tok_ok(d, o) || !ptr_ok(S_final))
-        return PRISM_EINVAL;
-    prism_status st = check_scan_shape(d);
-    if (st != PRISM_OK)
-        return st;
-    prism::ScanArgs p;
-    p.bf16 = d->dtype == PRISM_BF16;
-    p.n_seqs = d->n_seqs;
-    p.total_tokens = d->total_tokens;
-    p.heads = d->heads;
-    p.dk = d->dk;
-    p.dv = d->dv;
-    p.dv_slice = pick_dv_slice(d);
-    p.specialised = p.bf16 && p.dv_slice <= 32 && env_int("PRISM_SCAN_SPECIALISED", 1) != 0;
-    p.ws_waves = env_int("PRISM_SCAN_WAVES", 8) == 4 ? 4 : 8;
-    p.q = q; p.k = k; p.kw = kw; p.v = v; p.g = g; p.b = b;
-    p.cu_seqlens = cu_seqlens;
-    p.o = o;
-    p.s_final = S_final;
-    if (use_bf16_kernel(d, p.dv_slice))
-        return from_hip(prism::launch_scan_bf16(p, (hipStream_t)stream));
-    return from_hip(prism::launch_scan(p, (hipStream_t)stream));
+    return scan_impl(d, q, k, kw, v, g, b, cu_seqlens, nullptr, o, S_final, stream);
 }
 
 prism_status prism_fwd(const prism_dims* d, const void* q, const void* k, const void* v,
@@ -188,23 +239,48 @@ prism_status prism_fwd(const prism_dims* d, const void* q, const void* k, const 
                        void* o, float* S_final, void* workspace, size_t workspace_bytes,
                        void* stream)
 {
-    if (!dims_ok(d) || L < 1 || L > PRISM_MAX_LEVELS)
+    return fwd_impl(d, q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L, nullptr, nullptr, o,
+                    S_final, nullptr, workspace, workspace_bytes, stream);
+}
+
+prism_status prism_fwd_resume(const prism_dims* d, const void* q, const void* k, const void* v,
+                              const void* u, const void* g, const void* b, const void* a,
+                              const void* h, const void* conv_w, const int32_t* cu_seqlens,
+                              int L, const float* S_init, const void* k_hist, void* o,
+                              float* S_final, void* k_hist_out, void* workspace,
+                              size_t workspace_bytes, void* stream)
+{
+    return fwd_impl(d, q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L, S_init, k_hist, o, S_final,
+                    k_hist_out, workspace, workspace_bytes, stream);
+}
+
+prism_status prism_decode_step(const prism_dims* d, const void* q, const void* k, const void* v,
+                               const void* u, const void* g, const void* b, const void* a,
+                               const void* h, const void* conv_w, int L, float* S, void* k_hist,
+                               void* o, void* stream)
+{
+    if (!dims_ok(d) || L < 1 || L > PRISM_MAX_LEVELS || d->total_tokens != d->n_seqs)
         return PRISM_EINVAL;
-    if (!tok_ok(d, q) || !tok_ok(d, k) || !tok_ok(d, v) || !tok_ok(d, g) || !tok_ok(d, b) ||
-        !ptr_ok(conv_w) || !ptr_ok(cu_seqlens) || !tok_ok(d, o) || !ptr_ok(S_final) ||
-        !ptr_ok(workspace))
+    if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(g) || !ptr_ok(b) || !ptr_ok(conv_w) ||
+        !ptr_ok(S) || !ptr_ok(k_hist) || !ptr_ok(o))
         return PRISM_EINVAL;
-    if (L > 1 && (!tok_ok(d, u) || !tok_ok(d, a) || !tok_ok(d, h)))
+    if (L > 1 && (!ptr_ok(u) || !ptr_ok(a) || !ptr_ok(h)))
         return PRISM_EINVAL;
-    if (workspace_bytes < prism_workspace_bytes(d, L))
-        return PRISM_EINVAL;
-    prism_status st = check_scan_shape(d);
-    if (st != PRISM_OK)
-        return st;
-    st = prism_prologue(d, k, u, a, h, b, conv_w, cu_seqlens, L, workspace, stream);
-    if (st != PRISM_OK)
-        return st;
-    return prism_scan(d, q, k, workspace, v, g, b, cu_seqlens, o, S_final, stream);
+    if (!prism::decode_supported(d->dk, d->dv))
+        return PRISM_EUNSUPPORTED;
+    prism::DecodeArgs p;
+    p.bf16 = d->dtype == PRISM_BF16;
+    p.n_seqs = d->n_seqs;
+    p.heads = d->heads;
+    p.dk = d->dk;
+    p.dv = d->dv;
+    p.L = L;
+    p.q = q; p.k = k; p.v = v; p.u = u; p.a = a; p.h = h; p.g = g; p.b = b;
+    p.conv_w = conv_w;
+    p.S = S;
+    p.k_hist = k_hist;
+    p.o = o;
+    return from_hip(prism::launch_decode(p, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -25,7 +25,10 @@
 //     token t is computed (two register sets, alternating);
 //   * sequence boundaries come from cu_seqlens on the device (binary search
 //     once per strip, then a forward walk that marks the sequence starts in
-//     the strip), so no host synchronisation and no reads inside the loop.
+//     the strip), so no host synchronisation and no reads inside the loop;
+//   * a carried history (HIST: the three k rows before each sequence's first
+//     token, from an earlier piece of the same sequences) replaces the zero
+//     taps before a sequence start; it is read only where a sequence starts.
 #include "common.h"
 #include "kernels.h"
 
@@ -91,12 +94,12 @@ template <typename T, int N> struct Lane {
     }
 };
 
-template <typename T, int L, int V, int STRIP>
+template <typename T, int L, int V, int STRIP, bool HIST>
 __global__ __launch_bounds__(256) void prologue_kernel(
     const T* __restrict__ k, const T* __restrict__ u, const T* __restrict__ a,
     const T* __restrict__ h, const T* __restrict__ b, const T* __restrict__ conv_w,
-    const int32_t* __restrict__ cu, int n_seqs, int T_total, int H, int dk,
-    T* __restrict__ kw)
+    const T* __restrict__ k_hist, const int32_t* __restrict__ cu, int n_seqs, int T_total,
+    int H, int dk, T* __restrict__ kw)
 {
     constexpr int strip = STRIP;
     using LV = Lane<T, V>;
@@ -136,13 +139,22 @@ __global__ __launch_bounds__(256) void prologue_kernel(
     const int64_t koff = (int64_t)e * dk + i0;
     const int64_t loff = (int64_t)e * (L - 1) * dk + i0;
 
-    // conv history: x1 = k[t-1], x2 = k[t-2], x3 = k[t-3] (zero before the sequence start)
+    // conv history: x1 = k[t-1], x2 = k[t-2], x3 = k[t-3]; before the sequence
+    // start the carried history of sequence n (slot 2 = the token just before
+    // it) or zero
     float x1[V], x2[V], x3[V];
 #pragma unroll
     for (int c = 0; c < V; ++c) { x1[c] = 0.f; x2[c] = 0.f; x3[c] = 0.f; }
-    if (t0 - 1 >= seq_start) LV::load(k + (int64_t)(t0 - 1) * row + koff, x1);
-    if (t0 - 2 >= seq_start) LV::load(k + (int64_t)(t0 - 2) * row + koff, x2);
-    if (t0 - 3 >= seq_start) LV::load(k + (int64_t)(t0 - 3) * row + koff, x3);
+    auto tap = [&](int tau, int start, int seq, float* x) {
+        if (tau >= start)
+            LV::load(k + (int64_t)tau * row + koff, x);
+        else if (HIST)
+            LV::load(k_hist + ((int64_t)seq * H * 3 + (int64_t)e * 3 + (tau - start + 3)) * dk + i0, x);
+    };
+    tap(t0 - 1, seq_start, n, x1);
+    tap(t0 - 2, seq_start, n, x2);
+    tap(t0 - 3, seq_start, n, x3);
+    int hseq = n;                                        // sequence of the latest reset (HIST)
 
     // Software pipeline over the strip: the raw inputs of token t + 1 are in
     // flight while token t is computed, so a thread always has two tokens of
@@ -194,6 +206,12 @@ __global__ __launch_bounds__(256) void prologue_kernel(
         if ((resets >> (t - t0)) & 1u) {                 // a new sequence starts at t
 #pragma unroll
             for (int c = 0; c < V; ++c) { x1[c] = 0.f; x2[c] = 0.f; x3[c] = 0.f; }
+            if constexpr (HIST) {
+                while (cu[hseq + 1] <= t) ++hseq;        // the non-empty sequence starting at t
+                tap(t - 1, t, hseq, x1);
+                tap(t - 2, t, hseq, x2);
+                tap(t - 3, t, hseq, x3);
+            }
         }
         float kt[V];
         unpack(x.k, kt);
@@ -240,7 +258,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(
     }
 }
 
-template <typename T, int L, int V, int S>
+template <typename T, int L, int V, int S, bool HIST = false>
 static hipError_t launch_LVS(const PrologueArgs& p, hipStream_t stream)
 {
     const int64_t groups = (int64_t)p.heads * p.dk / V;
@@ -249,10 +267,10 @@ static hipError_t launch_LVS(const PrologueArgs& p, hipStream_t stream)
     if (threads == 0)
         return hipSuccess;
     const int64_t blocks = (threads + 255) / 256;
-    hipLaunchKernelGGL((prologue_kernel<T, L, V, S>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const T*)p.k, (const T*)p.u, (const T*)p.a, (const T*)p.h, (const T*)p.b,
-                       (const T*)p.conv_w, p.cu_seqlens, p.n_seqs, p.total_tokens, p.heads, p.dk,
-                       (T*)p.kw);
+    hipLaunchKernelGGL((prologue_kernel<T, L, V, S, HIST>), dim3((unsigned)blocks), dim3(256), 0,
+                       stream, (const T*)p.k, (const T*)p.u, (const T*)p.a, (const T*)p.h,
+                       (const T*)p.b, (const T*)p.conv_w, (const T*)p.k_hist, p.cu_seqlens,
+                       p.n_seqs, p.total_tokens, p.heads, p.dk, (T*)p.kw);
     return hipGetLastError();
 }
 
@@ -268,11 +286,14 @@ static hipError_t launch_LV(const PrologueArgs& p, hipStream_t stream)
 }
 
 // Channels per thread: 16-byte or 8-byte accesses (the narrow form halves the
-// registers a thread holds, which doubles the wavefronts in flight).
+// registers a thread holds, which doubles the wavefronts in flight).  With a
+// carried history: 16-byte groups and strips of 8 tokens only.
 template <typename T, int L>
 static hipError_t launch_L(const PrologueArgs& p, hipStream_t stream)
 {
     constexpr int wide = 16 / (int)sizeof(T), narrow = 8 / (int)sizeof(T);
+    if (p.k_hist)
+        return launch_LVS<T, L, wide, 8, true>(p, stream);
     if (p.narrow)
         return launch_LV<T, L, narrow>(p, stream);
     return launch_LV<T, L, wide>(p, stream);
@@ -305,6 +326,67 @@ static hipError_t launch_T(const PrologueArgs& p, hipStream_t s)
 hipError_t launch_prologue(const PrologueArgs& p, hipStream_t stream)
 {
     return p.bf16 ? launch_T<uint16_t>(p, stream) : launch_T<float>(p, stream);
+}
+
+}  // namespace prism
+
+namespace prism {
+
+// One thread per (sequence, head, 4 channels): reads its old history and k
+// rows first, then writes, so k_hist_out may be k_hist itself.
+template <typename T>
+__global__ __launch_bounds__(256) void k_history_kernel(
+    const T* __restrict__ k, const T* k_hist, const int32_t* __restrict__ cu, int n_seqs,
+    int H, int dk, T* k_hist_out)
+{
+    const int groups = dk / 4;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= (int64_t)n_seqs * H * groups)
+        return;
+    const int i0 = (int)(gid % groups) * 4;
+    const int e = (int)((gid / groups) % H);
+    const int n = (int)(gid / groups / H);
+    const int start = cu[n], end = cu[n + 1];
+    T rows[3][4];
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+        const int tau = end - 3 + m;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            T x = from_f32<T>(0.f);
+            if (tau >= start)
+                x = k[((int64_t)tau * H + e) * dk + i0 + c];
+            else if (k_hist)
+                x = k_hist[(((int64_t)n * H + e) * 3 + (tau - start + 3)) * dk + i0 + c];
+            rows[m][c] = x;
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < 3; ++m)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            k_hist_out[(((int64_t)n * H + e) * 3 + m) * dk + i0 + c] = rows[m][c];
+}
+
+hipError_t launch_k_history(bool bf16, int n_seqs, int heads, int dk, const void* k,
+                            const void* k_hist, const int32_t* cu_seqlens, void* k_hist_out,
+                            hipStream_t stream)
+{
+    if (dk % 4 != 0)
+        return hipErrorInvalidValue;
+    const int64_t threads = (int64_t)n_seqs * heads * (dk / 4);
+    if (threads == 0)
+        return hipSuccess;
+    const unsigned blocks = (unsigned)((threads + 255) / 256);
+    if (bf16)
+        hipLaunchKernelGGL((k_history_kernel<uint16_t>), dim3(blocks), dim3(256), 0, stream,
+                           (const uint16_t*)k, (const uint16_t*)k_hist, cu_seqlens, n_seqs, heads,
+                           dk, (uint16_t*)k_hist_out);
+    else
+        hipLaunchKernelGGL((k_history_kernel<float>), dim3(blocks), dim3(256), 0, stream,
+                           (const float*)k, (const float*)k_hist, cu_seqlens, n_seqs, heads, dk,
+                           (float*)k_hist_out);
+    return hipGetLastError();
 }
 
 }  // namespace prism

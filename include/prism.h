@@ -3,8 +3,9 @@
  * operator on AMD Instinct MI355X (gfx950).
  *
  * The operator (PRISM: Parallel Residual Iterative Sequence Model) keeps, per
- * (sequence, head), a state S in R^{dk x dv} that starts at zero and, for each
- * token t of the sequence,
+ * (sequence, head), a state S in R^{dk x dv} that starts at zero (or at a
+ * carried state, prism_fwd_resume and prism_decode_step) and, for each token t
+ * of the sequence,
  *
  *   r_0   = causal depthwise ShortConv(width 4) of k at t       (local anchor)
  *   r_1   = r_0,  r_l = r_0 * prod_{j=1..l-1} (1 - a_j * h_j)   (residual chain, closed form)
@@ -131,12 +132,72 @@ prism_status prism_scan(const prism_dims* d,
                         const void* g, const void* b, const int32_t* cu_seqlens,
                         void* o, float* S_final, void* stream);
 
+/*
+ * Forward pass that continues sequences from an earlier call: the same
+ * operator as prism_fwd, started from a carried state and convolution history
+ * instead of zeros.  The state matrix holds a sequence's whole history in a
+ * fixed size and is updated one token at a time (WeChat page section
+ * 背景：无限背包 vs 有限背包; poster page, lay summary), so a sequence split into
+ * pieces and run piece by piece, carrying S_final and k_hist_out of one call
+ * into S_init and k_hist of the next, gives the outputs of one call over the
+ * whole sequence (up to rounding).
+ *
+ *   S_init      fp32 [n_seqs, H, dk, dv] state before each sequence's first token,
+ *               or NULL (zero).  May be the same buffer as S_final (in-place update).
+ *   k_hist      [n_seqs, H, 3, dk] input dtype: the three k rows before each
+ *               sequence's first token, oldest first (slot 2 is the token just
+ *               before it); the ShortConv taps before the sequence start read
+ *               them instead of zero.  NULL = zero.
+ *   k_hist_out  [n_seqs, H, 3, dk] or NULL (not written): the history to carry
+ *               on, i.e. the last three k rows of each sequence, with k_hist
+ *               (or zero) filling in for sequences shorter than three tokens.
+ *               May be the same buffer as k_hist.
+ * Other arguments, shapes and errors as in prism_fwd; the optional pointers
+ * must be 16-byte aligned when given.
+ */
+prism_status prism_fwd_resume(const prism_dims* d,
+                              const void* q, const void* k, const void* v,
+                              const void* u, const void* g, const void* b,
+                              const void* a, const void* h, const void* conv_w,
+                              const int32_t* cu_seqlens, int L,
+                              const float* S_init, const void* k_hist,
+                              void* o, float* S_final, void* k_hist_out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One decode step: exactly one new token for each of the n_seqs sequences
+ * (d->total_tokens must equal d->n_seqs; no cu_seqlens), run through the
+ * recurrence in its token-by-token form with the state and the convolution
+ * history updated in place (WeChat page sections 背景：无限背包 vs 有限背包 and
+ * 消除 Token 间串行; gist.science section 2.1, S_t = S_{t-1} A_t + B_t).
+ *
+ *   q, k        [n_seqs, H, dk]       the new token of each sequence
+ *   v           [n_seqs, H, dv]
+ *   u, a, h     [n_seqs, H, L-1, dk]  NULL allowed iff L == 1
+ *   g, b        [n_seqs, H]
+ *   conv_w      [H, dk, 4]
+ *   S           fp32 [n_seqs, H, dk, dv], in/out: the state before the token,
+ *               replaced by the state after it
+ *   k_hist      [n_seqs, H, 3, dk] input dtype, in/out: the three k rows before
+ *               the token (oldest first), replaced by the three ending with it
+ *   o           out [n_seqs, H, dv], input dtype
+ * All pointers non-null and 16-byte aligned (u, a, h may be NULL when L == 1).
+ * dk and dv in {64, 128}, else PRISM_EUNSUPPORTED.  The write key is kept in
+ * fp32 here (prism_fwd rounds it to the input dtype between its two kernels).
+ * A sequence of decode steps equals prism_fwd_resume over the same tokens.
+ */
+prism_status prism_decode_step(const prism_dims* d,
+                               const void* q, const void* k, const void* v,
+                               const void* u, const void* g, const void* b,
+                               const void* a, const void* h, const void* conv_w, int L,
+                               float* S, void* k_hist, void* o, void* stream);
+
 /* Static description of a status code. */
 const char* prism_status_str(prism_status s);
 
 /* ABI version of this header (bumped on any signature change). */
 int prism_abi_version(void);
-#define PRISM_ABI_VERSION 1
+#define PRISM_ABI_VERSION 2
 
 #ifdef __cplusplus
 }

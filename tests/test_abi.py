@@ -27,7 +27,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("prism_fwd", "prism_prologue", "prism_scan", "prism_workspace_bytes",
-              "prism_status_str", "prism_abi_version"):
+              "prism_status_str", "prism_abi_version", "prism_fwd_resume", "prism_decode_step"):
         assert n in names
 
 
@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib.prism_abi_version() == 1
+    assert lib.prism_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -109,6 +109,51 @@ def test_prologue_and_scan_reject_bad_arguments(lib):
     d96 = B.make_dims(1, 10, 1, 64, 96, B.PRISM_BF16)
     assert lib.prism_scan(ctypes.byref(d96), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                           None) == B.PRISM_EUNSUPPORTED
+
+
+def _resume(lib, d, L=2, ws=1 << 30, **over):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, u=FAKE, g=FAKE, b=FAKE, a=FAKE, h=FAKE, conv_w=FAKE,
+                cu=FAKE, s0=None, hist=None, o=FAKE, s=FAKE, hout=None, w=FAKE)
+    args.update(over)
+    A = args
+    return lib.prism_fwd_resume(ctypes.byref(d), A["q"], A["k"], A["v"], A["u"], A["g"], A["b"],
+                                A["a"], A["h"], A["conv_w"], A["cu"], L, A["s0"], A["hist"],
+                                A["o"], A["s"], A["hout"], A["w"], ws, None)
+
+
+def test_fwd_resume_rejects_bad_arguments(lib):
+    from gated_delta_rule_prologue_amd import binding as B
+    ok = B.make_dims(1, 10, 1, 64, 64, B.PRISM_BF16)
+    # the optional pointers must be aligned when given
+    assert _resume(lib, ok, s0=FAKE + 4) == B.PRISM_EINVAL
+    assert _resume(lib, ok, hist=FAKE + 2) == B.PRISM_EINVAL
+    assert _resume(lib, ok, hout=FAKE + 8) == B.PRISM_EINVAL
+    assert _resume(lib, ok, s=None) == B.PRISM_EINVAL
+    assert _resume(lib, ok, L=0) == B.PRISM_EINVAL
+    assert _resume(lib, ok, ws=16) == B.PRISM_EINVAL
+    assert _resume(lib, B.make_dims(1, 10, 1, 96, 64, B.PRISM_BF16)) == B.PRISM_EUNSUPPORTED
+
+
+def _decode(lib, d, L=2, **over):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, u=FAKE, g=FAKE, b=FAKE, a=FAKE, h=FAKE, conv_w=FAKE,
+                S=FAKE, hist=FAKE, o=FAKE)
+    args.update(over)
+    A = args
+    return lib.prism_decode_step(ctypes.byref(d), A["q"], A["k"], A["v"], A["u"], A["g"], A["b"],
+                                 A["a"], A["h"], A["conv_w"], L, A["S"], A["hist"], A["o"], None)
+
+
+def test_decode_step_rejects_bad_arguments(lib):
+    from gated_delta_rule_prologue_amd import binding as B
+    ok = B.make_dims(4, 4, 2, 64, 64, B.PRISM_BF16)
+    assert _decode(lib, B.make_dims(4, 5, 2, 64, 64, B.PRISM_BF16)) == B.PRISM_EINVAL  # one token each
+    assert _decode(lib, ok, S=None) == B.PRISM_EINVAL
+    assert _decode(lib, ok, hist=None) == B.PRISM_EINVAL
+    assert _decode(lib, ok, hist=FAKE + 2) == B.PRISM_EINVAL
+    assert _decode(lib, ok, u=None) == B.PRISM_EINVAL
+    assert _decode(lib, ok, L=17) == B.PRISM_EINVAL
+    assert _decode(lib, B.make_dims(4, 4, 2, 96, 64, B.PRISM_BF16)) == B.PRISM_EUNSUPPORTED
+    assert _decode(lib, B.make_dims(4, 4, 2, 64, 32, B.PRISM_F32)) == B.PRISM_EUNSUPPORTED
 
 
 def test_binding_checks_shapes_before_calling():
