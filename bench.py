@@ -13,6 +13,12 @@ Prints ONE JSON line.  Per-kernel durations come from HIP events recorded on
 the launch stream inside the timed region.  The CPU baseline is the fp64
 oracle (plain C, OpenMP over chains) on the same workload, timed on the host
 cores; its outputs double as a parity check of the last timed step.
+
+The line also carries a "decode" object: the single-token decode step
+(prism_decode_step, state and convolution history carried in place) timed
+on serving batches shaped like the recommendation and language-model layers,
+each against its HBM roofline.  It is measured after the forward pass and is
+not part of "value".
 """
 from __future__ import annotations
 
@@ -38,7 +44,13 @@ KERNEL_SOURCES = {
     "prologue": [_CSRC + f for f in ("prologue.hip", "common.h", "kernels.h", "prism_api.hip")],
     "scan": [_CSRC + f for f in ("chunk_scan_bf16.hip", "chunk_scan.hip", "common.h", "kernels.h",
                                   "prism_api.hip")],
+    "decode": [_CSRC + f for f in ("decode.hip", "common.h", "kernels.h", "prism_api.hip")],
 }
+# Decode batches: (name, sequences, heads, dk, dv, L), one new token per sequence.
+DECODE_BATCHES = [
+    ("recsys-serving-512x8", 512, 8, 64, 64, 8),
+    ("lm-130m-serving-256x6", 256, 6, 128, 128, 4),
+]
 
 
 def algorithmic_work(w, n_seqs, T, esize):
@@ -114,6 +126,71 @@ def cpu_baseline(inp, o_gpu, s_gpu):
              "checked": "last timed step, every element"})
 
 
+def decode_bytes(n, H, dk, dv, L, esize):
+    """Algorithmic HBM bytes of one decode step over n sequences: the fp32 state
+    read and written (8 dk dv per chain) plus, per chain, e [q, k (2 dk), v (dv),
+    u, a (2 (L-1) dk), h slots read (max(L-2, 0) dk), g, b (2), history read and
+    written (6 dk), o (dv)], plus the conv taps once per head (4 dk e)."""
+    chains = n * H
+    per = 8 * dk * dv + esize * (2 * dk + dv + 2 * (L - 1) * dk + max(L - 2, 0) * dk + 2 + 6 * dk + dv)
+    return chains * per + H * 4 * dk * esize
+
+
+def decode_bench(steps, warmup):
+    """Time prism_decode_step on each serving batch.  Inputs, states and
+    histories are rotated over enough copies that a step's working set is not
+    left in the 256 MB Infinity Cache by the step before."""
+    import torch
+    from gated_delta_rule_prologue_amd import binding
+    from gated_delta_rule_prologue_amd.configs import Workload
+    from gated_delta_rule_prologue_amd.inputs import make_inputs
+
+    out = {}
+    stream = torch.cuda.current_stream()
+    for name, n, H, dk, dv, L in DECODE_BATCHES:
+        w = Workload(name, heads=H, dk=dk, dv=dv, L=L, dtype="bf16", seed=2000,
+                     lengths=[1] * n)
+        step = make_inputs(w)
+        nbytes = decode_bytes(n, H, dk, dv, L, 2)
+        ncopy = max(2, min(16, -(-(640 << 20) // nbytes)))
+        base = binding.to_device(step)
+        copies = []
+        for i in range(ncopy):
+            c = {k: (v.clone() if v is not None else None) for k, v in base.items()}
+            c["S"] = torch.zeros((n, H, dk, dv), dtype=torch.float32, device="cuda")
+            c["hist"] = torch.zeros((n, H, 3, dk), dtype=torch.bfloat16, device="cuda")
+            c["o"] = torch.empty_like(c["v"])
+            copies.append(c)
+
+        def run(c):
+            binding.decode_step(c["q"], c["k"], c["v"], c["u"], c["g"], c["b"], c["a"], c["h"],
+                                c["conv_w"], L, c["S"], c["hist"], o=c["o"], stream=stream)
+
+        for i in range(warmup):
+            run(copies[i % ncopy])
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            ev[i][0].record(stream)
+            run(copies[i % ncopy])
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+        ach = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {
+            "sequences": n, "heads": H, "dk": dk, "dv": dv, "L": L, "dtype": "bf16",
+            "tokens_per_s": steps * n / elapsed, "us_per_step": elapsed / steps * 1e6,
+            "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic("decode", name),
+                         "kernel": "decode", "avg_launch_us": ms * 1e3,
+                         "algorithmic_bytes": nbytes},
+            "state_copies": ncopy,
+        }
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +199,9 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name (default: lm-130m-layer)")
     ap.add_argument("--copies", type=int, default=3, help="input copies rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only the decode steps (profiling runs); prints their JSON object")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after the timed region, run torch copies of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -139,6 +219,9 @@ def main():
 
     torch.cuda.set_device(0)
     binding.lib()
+    if args.decode_only:
+        print(json.dumps({"decode": decode_bench(args.steps, args.warmup)}), flush=True)
+        return
     w = BY_NAME[args.workload or BENCH_WORKLOAD]
     inp = make_inputs(w)
     esize = 2 if w.dtype == "bf16" else 4
@@ -197,14 +280,6 @@ def main():
     scn["algorithmic_flops"] = work["scan_flops"]
     dominant = scn if scan_ms >= pro_ms else pro
 
-    if args.calibrate_copy_mib:
-        nb = args.calibrate_copy_mib << 20
-        src = torch.empty(nb // 4, dtype=torch.float32, device="cuda").fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-
     out = {
         "metric": METRIC,
         "value": K * T / elapsed,
@@ -228,6 +303,16 @@ def main():
                     / 1e9 / ((pro_ms + scan_ms) * 1e-3)},
     }
     out["roofline"]["kernel"] = dominant["kernel"]
+    if not args.no_decode:
+        out["decode"] = decode_bench(max(20, K), max(5, args.warmup))
+    # last copy kernels of the run: the reference for the counter calibration
+    if args.calibrate_copy_mib:
+        nb = args.calibrate_copy_mib << 20
+        src = torch.empty(nb // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         cb, parity = cpu_baseline(inp, last["o"], last["S"])
         out["cpu_baseline"] = cb
