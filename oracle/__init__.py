@@ -26,7 +26,7 @@ _lib = None
 
 class _Dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in
-                ("n_seqs", "total_tokens", "heads", "dk", "dv", "L", "dtype")]
+                ("n_seqs", "total_tokens", "heads", "dk", "dv", "L", "dtype", "residual")]
 
 
 def build(force: bool = True) -> str:
@@ -35,7 +35,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.run(["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared",
-                        "-Wall", "-Wextra", "-o", tmp, _SRC], check=True)
+                        "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"], check=True)
         os.replace(tmp, _LIB)
         _lib = None
     return _LIB
@@ -74,8 +74,12 @@ def _ptr(x: Optional[np.ndarray]):
     return x.ctypes.data
 
 
-def _dims(inp, dtype_code: int) -> _Dims:
-    return _Dims(inp.n_seqs, inp.total_tokens, inp.heads, inp.dk, inp.dv, inp.L, dtype_code)
+RESIDUAL = {"linear": 0, "gelu": 1}
+
+
+def _dims(inp, dtype_code: int, residual: str = "linear") -> _Dims:
+    return _Dims(inp.n_seqs, inp.total_tokens, inp.heads, inp.dk, inp.dv, inp.L, dtype_code,
+                 RESIDUAL[residual])
 
 
 def _check(inp):
@@ -110,12 +114,13 @@ def _state(inp, S_init):
     return S_init
 
 
-def prologue(inp, threads: Optional[int] = None, k_hist=None) -> np.ndarray:
-    """Write keys kw [T, H, dk] in float64 (``k_hist``: carried conv history)."""
+def prologue(inp, threads: Optional[int] = None, k_hist=None, residual: str = "linear") -> np.ndarray:
+    """Write keys kw [T, H, dk] in float64 (``k_hist``: carried conv history;
+    ``residual``: "linear" closed form or "gelu" refinement chain)."""
     code, cu = _check(inp)
     hist = _hist(inp, k_hist)
     out = np.zeros((inp.total_tokens, inp.heads, inp.dk), dtype=np.float64)
-    d = _dims(inp, code)
+    d = _dims(inp, code, residual)
     rc = _load().prism_oracle_prologue(ctypes.byref(d), _ptr(cu), _ptr(inp.k), _ptr(inp.u),
                                        _ptr(inp.a), _ptr(inp.h), _ptr(inp.b), _ptr(inp.conv_w),
                                        _ptr(hist), _ptr(out), threads or default_threads())
@@ -125,14 +130,15 @@ def prologue(inp, threads: Optional[int] = None, k_hist=None) -> np.ndarray:
 
 
 def fwd(inp, chains: Optional[Sequence[int]] = None, threads: Optional[int] = None,
-        S_init=None, k_hist=None):
+        S_init=None, k_hist=None, residual: str = "linear"):
     """Forward pass.  Returns (o [T, H, dv], S_final [n_seqs, H, dk, dv]) in float64.
 
     ``chains`` restricts the evaluation to the listed (sequence * H + head)
     chains; rows of other chains are left at zero.  ``S_init`` [n_seqs, H, dk,
     dv] is the state each sequence starts from and ``k_hist`` [n_seqs, H, 3,
     dk] (input storage type) the three k rows before each sequence's first
-    token; both default to zero.
+    token; both default to zero.  ``residual``: "linear" (closed-form chain) or
+    "gelu" (non-linear refinement chain).
     """
     code, cu = _check(inp)
     hist, s0 = _hist(inp, k_hist), _state(inp, S_init)
@@ -141,7 +147,7 @@ def fwd(inp, chains: Optional[Sequence[int]] = None, threads: Optional[int] = No
     ch = None if chains is None else np.ascontiguousarray(np.asarray(chains, dtype=np.int64))
     if ch is not None and ch.size and (ch.min() < 0 or ch.max() >= inp.n_seqs * inp.heads):
         raise ValueError("chain index out of range")
-    d = _dims(inp, code)
+    d = _dims(inp, code, residual)
     rc = _load().prism_oracle_fwd(ctypes.byref(d), _ptr(cu), _ptr(inp.q), _ptr(inp.k),
                                   _ptr(inp.v), _ptr(inp.u), _ptr(inp.g), _ptr(inp.b),
                                   _ptr(inp.a), _ptr(inp.h), _ptr(inp.conv_w), _ptr(s0),
@@ -166,12 +172,12 @@ def k_history(inp, k_hist=None) -> np.ndarray:
     return out
 
 
-def decode_step(step, S, k_hist, threads: Optional[int] = None):
+def decode_step(step, S, k_hist, threads: Optional[int] = None, residual: str = "linear"):
     """One token of every sequence: the recurrence itself with the state and
     conv history carried in.  ``step`` holds one token per sequence
     (cu_seqlens = 0, 1, ..., n_seqs).  Returns (o [n_seqs, H, dv], S_new,
     k_hist_new [n_seqs, H, 3, dk]) in float64."""
     if not np.array_equal(step.cu_seqlens, np.arange(step.n_seqs + 1)):
         raise ValueError("a decode step holds exactly one token per sequence")
-    o, s = fwd(step, threads=threads, S_init=S, k_hist=k_hist)
+    o, s = fwd(step, threads=threads, S_init=S, k_hist=k_hist, residual=residual)
     return o, s, k_history(step, k_hist)

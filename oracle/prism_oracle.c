@@ -26,6 +26,15 @@
  *   "*" is element-wise over the dk channel.  At L = 1 this is exactly the
  *   Gated DeltaNet recurrence.
  *
+ *   Non-linear refinement variant (residual = ORACLE_RESIDUAL_GELU): the
+ *   residual chain keeps its GELU instead of the closed form,
+ *
+ *     r_1 = r_0,   r_{l+1} = r_l - a_l * GELU(h_l * r_l),   GELU(x) = x Phi(x),
+ *
+ *   with the same write key sum.  It reduces to the closed form when GELU is
+ *   replaced by the identity, and equals it for L <= 2 (no residual update is
+ *   used before the last level).
+ *
  * Sources (PRISM pages):
  *   - ICML 2026 PRISM summary (WeChat article), section 核心迭代形式: the
  *     step-size x residual x direction write, sum over L levels.
@@ -38,7 +47,8 @@
  *   - gist.science technical summary of arXiv 2602.10796, section 2.1
  *     (S_t = S_{t-1} A_t + B_t with an input-only write) and section 2.2
  *     (ShortConv anchor, refinement steps l = 1..L with r^(1) the anchor,
- *     residual update r^(l+1) = r^(l) - delta^(l)).
+ *     residual update r^(l+1) = r^(l) - delta^(l), delta^(l) the GELU of the
+ *     predicted gain times the residual, a step-size gate per level).
  *   - ICML 2026 poster abstract: a short convolution anchors the initial
  *     residual.
  *   - WeChat page, section 背景：无限背包 vs 有限背包, and the poster page's
@@ -54,6 +64,9 @@
  *     no bias and no activation after the convolution;
  *   - g and b are per (token, head) scalars; g is a linear-space gate;
  *   - no query scaling; the initial state is zero unless S_init is given;
+ *   - GELU variant: the gain of the gist page's delta is h_l and the step-size
+ *     gate a_l scales the subtracted GELU, so that the linearised chain
+ *     (GELU -> identity) is the closed form above; GELU is the exact erf form;
  *   - carried conv history k_hist [n_seqs, H, 3, dk]: slot m holds k at
  *     position (sequence start - 3 + m), i.e. slot 2 is the token just before
  *     the first one; zero when no history is given.
@@ -65,8 +78,12 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <math.h>
+
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
+#define ORACLE_RESIDUAL_LINEAR 0
+#define ORACLE_RESIDUAL_GELU 1
 
 typedef struct {
     int64_t n_seqs;
@@ -76,7 +93,14 @@ typedef struct {
     int64_t dv;
     int64_t L;
     int64_t dtype;      /* ORACLE_F32 or ORACLE_BF16 */
+    int64_t residual;   /* ORACLE_RESIDUAL_LINEAR or ORACLE_RESIDUAL_GELU */
 } oracle_dims;
+
+/* GELU(x) = x * Phi(x), Phi the standard normal CDF, in its erf form. */
+static double gelu(double x)
+{
+    return 0.5 * x * (1.0 + erf(x / sqrt(2.0)));
+}
 
 /* Exact widening of element i of an fp32 or bf16 array. */
 static double elem(const void* p, int64_t dtype, int64_t i)
@@ -119,6 +143,18 @@ static void write_key(const oracle_dims* d, const void* k, const void* u, const 
                   k_at(d, k, k_hist, n, seq_start, t - 3 + m, e, i);
         }
         double acc = bt * elem(k, dt, (t * H + e) * dk + i);
+        if (d->residual == ORACLE_RESIDUAL_GELU) {
+            /* r_{l+1} = r_l - a_l GELU(h_l r_l), level by level */
+            double r = r0;
+            for (int64_t l = 1; l <= L - 1; ++l) {
+                int64_t sl = ((t * H + e) * (L - 1) + (l - 1)) * dk + i;
+                acc += elem(a, dt, sl) * r * elem(u, dt, sl);
+                if (l <= L - 2)
+                    r -= elem(a, dt, sl) * gelu(elem(h, dt, sl) * r);
+            }
+            kw[i] = acc;
+            continue;
+        }
         for (int64_t l = 1; l <= L - 1; ++l) {
             /* closed form r_l = r_0 * prod_{j=1..l-1} (1 - a_j h_j) */
             double prod = 1.0;

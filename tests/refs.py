@@ -75,6 +75,29 @@ def write_key_iterative(inp, hist=None):
     return kw
 
 
+def gelu_cdf(x):
+    """GELU(x) = x Phi(x) with Phi from scipy's normal distribution."""
+    from scipy.stats import norm
+    return x * norm.cdf(x)
+
+
+def write_key_gelu(inp, hist=None):
+    """kw with the non-linear refinement chain of the gist.science summary,
+    section 2.2: r^(1) = anchor, r^(l+1) = r^(l) - a_l * GELU(h_l * r^(l)); level
+    l contributes a_l * r^(l) * u_l to the key."""
+    k = f64(inp.k)
+    b = f64(inp.b)
+    kw = b[:, :, None] * k
+    if inp.L == 1:
+        return kw
+    r = anchor_convolve(inp.k, inp.conv_w, inp.cu_seqlens, hist)
+    a, h, u = f64(inp.a), f64(inp.h), f64(inp.u)
+    for s in range(inp.L - 1):
+        kw = kw + a[:, :, s] * r * u[:, :, s]
+        r = r - a[:, :, s] * gelu_cdf(h[:, :, s] * r)
+    return kw
+
+
 # ---------------------------------------------------------------------------
 # state recurrence
 # ---------------------------------------------------------------------------
