@@ -41,7 +41,10 @@ _CSRC = "gated_delta_rule_prologue_amd/csrc/"
 # Sources that determine each kernel as launched (kernel body, shared helpers,
 # dispatch): a committed counter figure is only reported while they are unchanged.
 KERNEL_SOURCES = {
-    "prologue": [_CSRC + f for f in ("prologue.hip", "common.h", "kernels.h", "prism_api.hip")],
+    "prologue": [_CSRC + f for f in ("prologue.hip", "prologue_kernel.h", "prologue_bf16.hip",
+                                      "prologue_f32.hip", "prologue_bf16_ext.hip",
+                                      "prologue_f32_ext.hip", "common.h", "kernels.h",
+                                      "prism_api.hip")],
     "scan": [_CSRC + f for f in ("chunk_scan_bf16.hip", "chunk_scan.hip", "common.h", "kernels.h",
                                   "prism_api.hip")],
     "decode": [_CSRC + f for f in ("decode.hip", "common.h", "kernels.h", "prism_api.hip")],
@@ -136,10 +139,21 @@ def decode_bytes(n, H, dk, dv, L, esize):
     return chains * per + H * 4 * dk * esize
 
 
+def raw_args(*xs):
+    """Arguments of one C-ABI call, marshalled once: tensors as device pointers.
+    A timed loop of short kernels calls the library with these directly, so
+    that the binding's per-call shape checks (tens of microseconds of Python)
+    do not leave the GPU idle between the events around each launch; every
+    loop is preceded by a checked call through the binding with the same
+    tensors."""
+    return [None if x is None else (x.data_ptr() if hasattr(x, "data_ptr") else x) for x in xs]
+
+
 def decode_bench(steps, warmup):
     """Time prism_decode_step on each serving batch.  Inputs, states and
     histories are rotated over enough copies that a step's working set is not
     left in the 256 MB Infinity Cache by the step before."""
+    import ctypes
     import torch
     from gated_delta_rule_prologue_amd import binding
     from gated_delta_rule_prologue_amd.configs import Workload
@@ -162,26 +176,34 @@ def decode_bench(steps, warmup):
             c["o"] = torch.empty_like(c["v"])
             copies.append(c)
 
-        def run(c):
+        for c in copies:                   # checked calls through the binding
             binding.decode_step(c["q"], c["k"], c["v"], c["u"], c["g"], c["b"], c["a"], c["h"],
                                 c["conv_w"], L, c["S"], c["hist"], o=c["o"], stream=stream)
-
+        lib = binding.lib()
+        dims = binding.Dims(n, n, H, dk, dv, binding.PRISM_BF16)
+        args = [[ctypes.byref(dims)] + raw_args(c["q"], c["k"], c["v"], c["u"], c["g"], c["b"],
+                                                 c["a"], c["h"], c["conv_w"], L, 0, c["S"],
+                                                 c["hist"], c["o"], stream.cuda_stream)
+                for c in copies]
         for i in range(warmup):
-            run(copies[i % ncopy])
+            lib.prism_decode_step(*args[i % ncopy])
         torch.cuda.synchronize()
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        status = 0
         t0 = time.perf_counter()
         for i in range(steps):
             ev[i][0].record(stream)
-            run(copies[i % ncopy])
+            status |= lib.prism_decode_step(*args[i % ncopy])
             ev[i][1].record(stream)
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
+        assert status == 0, binding.status_str(status)
         ms = sum(a.elapsed_time(b) for a, b in ev) / steps
         ach = nbytes / (ms * 1e-3) / 1e9
         out[name] = {
             "sequences": n, "heads": H, "dk": dk, "dv": dv, "L": L, "dtype": "bf16",
             "tokens_per_s": steps * n / elapsed, "us_per_step": elapsed / steps * 1e6,
+            "tokens_per_s_kernel": n / (ms * 1e-3),
             "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic("decode", name),
                          "kernel": "decode", "avg_launch_us": ms * 1e3,
@@ -273,6 +295,28 @@ def main():
                 "frac": a / HBM_PEAK_GBS, "traffic": measured_traffic(kernel, w.name),
                 "kernel": kernel, "avg_launch_us": ms * 1e3, "algorithmic_bytes": nbytes}
 
+    # the non-linear refinement variant of the prologue (GELU residual chain), same
+    # inputs and bytes, timed on its own after the forward steps
+    import ctypes
+    lib = binding.lib()
+    dims = binding.Dims(n_seqs, T, w.heads, w.dk, w.dv, binding.PRISM_BF16 if esize == 2 else 0)
+    gargs = []
+    for c in copies:                       # checked calls through the binding
+        binding.prologue_ex(c["k"], c["u"], c["a"], c["h"], c["b"], c["conv_w"], c["cu_seqlens"],
+                            w.L, residual="gelu", kw=c["kw"], stream=stream)
+        gargs.append([ctypes.byref(dims)] + raw_args(c["k"], c["u"], c["a"], c["h"], c["b"],
+                                                      c["conv_w"], None, c["cu_seqlens"], w.L, 1,
+                                                      c["kw"], stream.cuda_stream))
+    gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    status = 0
+    for i in range(K):
+        gev[i][0].record(stream)
+        status |= lib.prism_prologue_ex(*gargs[i % len(copies)])
+        gev[i][1].record(stream)
+    torch.cuda.synchronize()
+    assert status == 0, binding.status_str(status)
+    gelu_ms = sum(a.elapsed_time(b) for a, b in gev) / K
+
     pro = hbm("prologue", work["prologue_bytes"], pro_ms)
     scn = hbm("scan", work["scan_bytes"], scan_ms)
     scn["mfma_tflops"] = work["scan_flops"] / (scan_ms * 1e-3) / 1e12
@@ -299,6 +343,8 @@ def main():
         "head_tokens_per_s": K * work["head_tokens"] / elapsed,
         "roofline": {k: dominant[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
         "kernels": {"prologue": pro, "scan": scn,
+                    "prologue_gelu": dict(hbm("prologue", work["prologue_bytes"], gelu_ms),
+                                          kernel="prologue (GELU residual chain)", traffic=None),
                     "pipeline_frac_hbm": (work["prologue_bytes"] + work["scan_bytes"]) / HBM_PEAK_GBS
                     / 1e9 / ((pro_ms + scan_ms) * 1e-3)},
     }

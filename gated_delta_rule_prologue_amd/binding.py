@@ -6,8 +6,8 @@ functions raise if the library is not built -- there is no fallback path.
 
 Names follow the C ABI: ``fwd`` -> prism_fwd, ``fwd_resume`` ->
 prism_fwd_resume, ``decode_step`` -> prism_decode_step, ``prologue`` ->
-prism_prologue, ``scan`` -> prism_scan, ``workspace_bytes`` ->
-prism_workspace_bytes.
+prism_prologue, ``prologue_ex`` -> prism_prologue_ex, ``scan`` -> prism_scan,
+``workspace_bytes`` -> prism_workspace_bytes.
 """
 from __future__ import annotations
 
@@ -22,6 +22,7 @@ _lib = None
 
 PRISM_OK, PRISM_EINVAL, PRISM_EUNSUPPORTED, PRISM_EHIP = 0, 1, 2, 3
 PRISM_F32, PRISM_BF16 = 0, 1
+RESIDUAL = {"linear": 0, "gelu": 1}          # prism_residual
 MAX_LEVELS = 16
 
 
@@ -59,9 +60,11 @@ def lib():
         L.prism_prologue.restype = I
         L.prism_scan.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
         L.prism_scan.restype = I
-        L.prism_fwd_resume.argtypes = [D, P, P, P, P, P, P, P, P, P, P, I, P, P, P, P, P, P, S, P]
+        L.prism_prologue_ex.argtypes = [D, P, P, P, P, P, P, P, P, I, I, P, P]
+        L.prism_prologue_ex.restype = I
+        L.prism_fwd_resume.argtypes = [D, P, P, P, P, P, P, P, P, P, P, I, I, P, P, P, P, P, P, S, P]
         L.prism_fwd_resume.restype = I
-        L.prism_decode_step.argtypes = [D, P, P, P, P, P, P, P, P, P, I, P, P, P, P]
+        L.prism_decode_step.argtypes = [D, P, P, P, P, P, P, P, P, P, I, I, P, P, P, P]
         L.prism_decode_step.restype = I
         L.prism_status_str.argtypes = [I]
         L.prism_status_str.restype = ctypes.c_char_p
@@ -166,6 +169,23 @@ def prologue(k, u, a, h, b, conv_w, cu_seqlens, L: int, kw=None, stream=None) ->
     return kw
 
 
+def prologue_ex(k, u, a, h, b, conv_w, cu_seqlens, L: int, k_hist=None, residual="linear",
+                kw=None, stream=None) -> torch.Tensor:
+    """Write keys with a carried history and a choice of residual chain
+    (prism_prologue_ex; ``residual`` is "linear" or "gelu")."""
+    d = _dims_of(k, None, cu_seqlens)
+    _check_write_branch(d, k.dtype, k, u, a, h, b, conv_w, L)
+    if k_hist is not None:
+        _expect("k_hist", k_hist, (d.n_seqs, d.heads, 3, d.dk), k.dtype)
+    if kw is None:
+        kw = torch.empty_like(k)
+    _expect("kw", kw, k.shape, k.dtype)
+    _check("prism_prologue_ex", lib().prism_prologue_ex(
+        ctypes.byref(d), _ptr(k), _ptr(u), _ptr(a), _ptr(h), _ptr(b), _ptr(conv_w), _ptr(k_hist),
+        _ptr(cu_seqlens), int(L), RESIDUAL[residual], _ptr(kw), _stream(stream)))
+    return kw
+
+
 def scan(q, k, kw, v, g, b, cu_seqlens, o=None, S_final=None, stream=None):
     """Chunkwise scan from precomputed write keys (prism_scan).  Returns (o, S_final)."""
     d = _dims_of(q, v, cu_seqlens)
@@ -207,12 +227,13 @@ def fwd(q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L: int, o=None, S_final=None
 
 
 def fwd_resume(q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L: int, S_init=None, k_hist=None,
-               o=None, S_final=None, k_hist_out=None, workspace=None, stream=None):
+               o=None, S_final=None, k_hist_out=None, workspace=None, stream=None,
+               residual="linear"):
     """Forward pass continuing from a carried state and conv history
     (prism_fwd_resume).  ``S_init`` fp32 [n_seqs, H, dk, dv] and ``k_hist``
     [n_seqs, H, 3, dk] default to zero; ``k_hist_out`` (optional, may be
-    ``k_hist``) receives the history to carry on.  Returns (o, S_final,
-    k_hist_out)."""
+    ``k_hist``) receives the history to carry on; ``residual`` is "linear"
+    or "gelu".  Returns (o, S_final, k_hist_out)."""
     d = _dims_of(q, v, cu_seqlens)
     _check_write_branch(d, q.dtype, k, u, a, h, b, conv_w, L)
     _check_scan(d, q.dtype, q, k, k, v, g, b)
@@ -235,13 +256,14 @@ def fwd_resume(q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L: int, S_init=None, 
         raise ValueError(f"workspace needs {need} bytes")
     _check("prism_fwd_resume", lib().prism_fwd_resume(
         ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(g), _ptr(b), _ptr(a), _ptr(h),
-        _ptr(conv_w), _ptr(cu_seqlens), int(L), _ptr(S_init), _ptr(k_hist), _ptr(o),
+        _ptr(conv_w), _ptr(cu_seqlens), int(L), RESIDUAL[residual], _ptr(S_init), _ptr(k_hist), _ptr(o),
         _ptr(S_final), _ptr(k_hist_out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return o, S_final, k_hist_out
 
 
-def decode_step(q, k, v, u, g, b, a, h, conv_w, L: int, S, k_hist, o=None, stream=None):
+def decode_step(q, k, v, u, g, b, a, h, conv_w, L: int, S, k_hist, o=None, stream=None,
+                residual="linear"):
     """One new token per sequence (prism_decode_step): q, k [N, H, dk], v [N, H,
     dv], u/a/h [N, H, L-1, dk], g/b [N, H].  ``S`` fp32 [N, H, dk, dv] and
     ``k_hist`` [N, H, 3, dk] are updated in place.  Returns o [N, H, dv]."""
@@ -260,7 +282,7 @@ def decode_step(q, k, v, u, g, b, a, h, conv_w, L: int, S, k_hist, o=None, strea
     _expect("o", o, v.shape, v.dtype)
     _check("prism_decode_step", lib().prism_decode_step(
         ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(g), _ptr(b), _ptr(a), _ptr(h),
-        _ptr(conv_w), int(L), _ptr(S), _ptr(k_hist), _ptr(o), _stream(stream)))
+        _ptr(conv_w), int(L), RESIDUAL[residual], _ptr(S), _ptr(k_hist), _ptr(o), _stream(stream)))
     return o
 
 

@@ -22,7 +22,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libprism.so")
-SOURCES = ["prism_api.hip", "prologue.hip", "chunk_scan.hip", "chunk_scan_bf16.hip", "decode.hip"]
+SOURCES = ["prism_api.hip", "prologue.hip", "prologue_bf16.hip", "prologue_f32.hip",
+           "prologue_bf16_ext.hip", "prologue_f32_ext.hip", "chunk_scan.hip",
+           "chunk_scan_bf16.hip", "decode.hip"]
 CHECKED = ["chunk_scan_bf16.hip", "chunk_scan.hip"]      # sources with mixed-size MFMA chains
 ARCH = "gfx950"
 

@@ -43,6 +43,23 @@ __device__ __forceinline__ void lds_barrier()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// GELU(x) = x Phi(x) = x (1 + erf(x / sqrt 2)) / 2, with erf from the rational
+// approximation of Abramowitz & Stegun, Handbook of Mathematical Functions,
+// formula 7.1.26 (after Hastings): for z >= 0,
+//   erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2),  t = 1 / (1 + p z),
+// absolute error <= 1.5e-7, and erf is odd.  Branch-free: one reciprocal, one
+// exp2, a degree-5 polynomial (the library erff costs several times as much and
+// branches on |x|).  Relative error of the result about 2e-7.
+__device__ __forceinline__ float gelu_as(float x)
+{
+    const float z = fabsf(x) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(1.f + 0.3275911f * z);
+    const float poly =
+        t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+    const float e = 1.f - poly * __builtin_amdgcn_exp2f(-z * z * 1.44269504088896341f);
+    return 0.5f * x * (1.f + __builtin_copysignf(e, x));
+}
+
 // Element conversions for the two input storage types.
 __device__ __forceinline__ float to_f32(uint16_t x) { return bf16_to_f32(x); }
 __device__ __forceinline__ float to_f32(float x) { return x; }

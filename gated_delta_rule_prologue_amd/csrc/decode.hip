@@ -6,6 +6,7 @@
 // Per (sequence n, head e), for the sequence's one new token:
 //   r_0  = w3 k + w2 hist[2] + w1 hist[1] + w0 hist[0]     ShortConv anchor
 //   kw   = b k + sum_{l=1..L-1} a_l r_l u_l,  r_{l+1} = r_l (1 - a_l h_l)
+//          (or r_{l+1} = r_l - a_l GELU(h_l r_l), the non-linear refinement chain)
 //   p    = S^T k
 //   S   <- g (S - b k p^T) + kw v^T                         = g (I - b k k^T) S + kw v^T
 //   o    = S^T q
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(NTH) void decode_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ u, const T* __restrict__ a, const T* __restrict__ h,
     const T* __restrict__ g, const T* __restrict__ b, const T* __restrict__ conv_w, int H, int L,
-    float* __restrict__ S, T* __restrict__ k_hist, T* __restrict__ o)
+    bool gelu, float* __restrict__ S, T* __restrict__ k_hist, T* __restrict__ o)
 {
     constexpr int CG = DV / 4;                   // 4-column groups
     constexpr int RG = NTH / CG;                 // row groups
@@ -110,8 +111,13 @@ __global__ __launch_bounds__(NTH) void decode_kernel(
         for (int s = 0; s < L - 1; ++s) {        // level l = s + 1
             const float av = to_f32(la[s * DK + i]);
             acc += av * r * to_f32(lu[s * DK + i]);
-            if (s < L - 2)
-                r *= 1.f - av * to_f32(lh[s * DK + i]);
+            if (s < L - 2) {
+                const float hv = to_f32(lh[s * DK + i]);
+                if (gelu)                        // r - a GELU(h r)
+                    r -= av * gelu_as(hv * r);
+                else
+                    r *= 1.f - av * hv;
+            }
         }
         sKW[i] = acc;
         sK[i] = kt;
@@ -174,7 +180,7 @@ static hipError_t launch_dec(const DecodeArgs& p, hipStream_t stream)
     hipLaunchKernelGGL((decode_kernel<T, DK, DV, NTH>), dim3((unsigned)blocks), dim3(NTH), lev, stream,
                        (const T*)p.q, (const T*)p.k, (const T*)p.v, (const T*)p.u, (const T*)p.a,
                        (const T*)p.h, (const T*)p.g, (const T*)p.b, (const T*)p.conv_w, p.heads,
-                       p.L, p.S, (T*)p.k_hist, (T*)p.o);
+                       p.L, p.gelu, p.S, (T*)p.k_hist, (T*)p.o);
     return hipGetLastError();
 }
 

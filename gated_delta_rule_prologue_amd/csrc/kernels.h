@@ -11,6 +11,7 @@ struct PrologueArgs {
     int n_seqs, total_tokens, heads, dk, L;
     int strip;                      // tokens walked by one thread: 4, 8 or 16
     bool narrow;                    // 8-byte instead of 16-byte channel groups
+    bool gelu;                      // residual chain r - a GELU(h r) instead of the closed form
     const void *k, *u, *a, *h, *b, *conv_w;
     const void* k_hist;             // [n_seqs, H, 3, dk] carried conv history, or null (zero)
     const int32_t* cu_seqlens;
@@ -41,6 +42,7 @@ hipError_t launch_k_history(bool bf16, int n_seqs, int heads, int dk, const void
 struct DecodeArgs {
     bool bf16;
     int n_seqs, heads, dk, dv, L;
+    bool gelu;                      // residual chain r - a GELU(h r) instead of the closed form
     const void *q, *k, *v, *u, *a, *h, *g, *b, *conv_w;
     float* S;                       // [n_seqs, H, dk, dv], updated in place
     void* k_hist;                   // [n_seqs, H, 3, dk], updated in place

@@ -97,11 +97,13 @@ prism_status from_hip(hipError_t e) { return e == hipSuccess ? PRISM_OK : PRISM_
 // Optional pointer: null, or 16-byte aligned.
 bool opt_ok(const void* p) { return aligned16(p); }
 
+bool residual_ok(int r) { return r == PRISM_RESIDUAL_LINEAR || r == PRISM_RESIDUAL_GELU; }
+
 prism_status prologue_impl(const prism_dims* d, const void* k, const void* u, const void* a,
                            const void* h, const void* b, const void* conv_w, const void* k_hist,
-                           const int32_t* cu_seqlens, int L, void* kw, void* stream)
+                           const int32_t* cu_seqlens, int L, int residual, void* kw, void* stream)
 {
-    if (!dims_ok(d) || L < 1 || L > PRISM_MAX_LEVELS)
+    if (!dims_ok(d) || L < 1 || L > PRISM_MAX_LEVELS || !residual_ok(residual))
         return PRISM_EINVAL;
     if (!tok_ok(d, k) || !tok_ok(d, b) || !ptr_ok(conv_w) || !ptr_ok(cu_seqlens) ||
         !tok_ok(d, kw) || !opt_ok(k_hist))
@@ -122,6 +124,7 @@ prism_status prologue_impl(const prism_dims* d, const void* k, const void* u, co
     if (p.strip != 4 && p.strip != 16)
         p.strip = 8;
     p.narrow = env_int("PRISM_PROLOGUE_NARROW", 0) != 0;
+    p.gelu = residual == PRISM_RESIDUAL_GELU;
     p.k = k; p.u = u; p.a = a; p.h = h; p.b = b; p.conv_w = conv_w;
     p.k_hist = k_hist;
     p.cu_seqlens = cu_seqlens;
@@ -164,11 +167,11 @@ prism_status scan_impl(const prism_dims* d, const void* q, const void* k, const 
 
 prism_status fwd_impl(const prism_dims* d, const void* q, const void* k, const void* v,
                       const void* u, const void* g, const void* b, const void* a, const void* h,
-                      const void* conv_w, const int32_t* cu_seqlens, int L, const float* S_init,
-                      const void* k_hist, void* o, float* S_final, void* k_hist_out,
-                      void* workspace, size_t workspace_bytes, void* stream)
+                      const void* conv_w, const int32_t* cu_seqlens, int L, int residual,
+                      const float* S_init, const void* k_hist, void* o, float* S_final,
+                      void* k_hist_out, void* workspace, size_t workspace_bytes, void* stream)
 {
-    if (!dims_ok(d) || L < 1 || L > PRISM_MAX_LEVELS)
+    if (!dims_ok(d) || L < 1 || L > PRISM_MAX_LEVELS || !residual_ok(residual))
         return PRISM_EINVAL;
     if (!tok_ok(d, q) || !tok_ok(d, k) || !tok_ok(d, v) || !tok_ok(d, g) || !tok_ok(d, b) ||
         !ptr_ok(conv_w) || !ptr_ok(cu_seqlens) || !tok_ok(d, o) || !ptr_ok(S_final) ||
@@ -181,7 +184,8 @@ prism_status fwd_impl(const prism_dims* d, const void* q, const void* k, const v
     prism_status st = check_scan_shape(d);
     if (st != PRISM_OK)
         return st;
-    st = prologue_impl(d, k, u, a, h, b, conv_w, k_hist, cu_seqlens, L, workspace, stream);
+    st = prologue_impl(d, k, u, a, h, b, conv_w, k_hist, cu_seqlens, L, residual, workspace,
+                       stream);
     if (st != PRISM_OK)
         return st;
     st = scan_impl(d, q, k, workspace, v, g, b, cu_seqlens, S_init, o, S_final, stream);
@@ -223,7 +227,16 @@ prism_status prism_prologue(const prism_dims* d, const void* k, const void* u, c
                             const void* h, const void* b, const void* conv_w,
                             const int32_t* cu_seqlens, int L, void* kw, void* stream)
 {
-    return prologue_impl(d, k, u, a, h, b, conv_w, nullptr, cu_seqlens, L, kw, stream);
+    return prologue_impl(d, k, u, a, h, b, conv_w, nullptr, cu_seqlens, L, PRISM_RESIDUAL_LINEAR,
+                         kw, stream);
+}
+
+prism_status prism_prologue_ex(const prism_dims* d, const void* k, const void* u, const void* a,
+                               const void* h, const void* b, const void* conv_w,
+                               const void* k_hist, const int32_t* cu_seqlens, int L, int residual,
+                               void* kw, void* stream)
+{
+    return prologue_impl(d, k, u, a, h, b, conv_w, k_hist, cu_seqlens, L, residual, kw, stream);
 }
 
 prism_status prism_scan(const prism_dims* d, const void* q, const void* k, const void* kw,
@@ -239,27 +252,28 @@ prism_status prism_fwd(const prism_dims* d, const void* q, const void* k, const 
                        void* o, float* S_final, void* workspace, size_t workspace_bytes,
                        void* stream)
 {
-    return fwd_impl(d, q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L, nullptr, nullptr, o,
-                    S_final, nullptr, workspace, workspace_bytes, stream);
+    return fwd_impl(d, q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L, PRISM_RESIDUAL_LINEAR,
+                    nullptr, nullptr, o, S_final, nullptr, workspace, workspace_bytes, stream);
 }
 
 prism_status prism_fwd_resume(const prism_dims* d, const void* q, const void* k, const void* v,
                               const void* u, const void* g, const void* b, const void* a,
                               const void* h, const void* conv_w, const int32_t* cu_seqlens,
-                              int L, const float* S_init, const void* k_hist, void* o,
-                              float* S_final, void* k_hist_out, void* workspace,
+                              int L, int residual, const float* S_init, const void* k_hist,
+                              void* o, float* S_final, void* k_hist_out, void* workspace,
                               size_t workspace_bytes, void* stream)
 {
-    return fwd_impl(d, q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L, S_init, k_hist, o, S_final,
-                    k_hist_out, workspace, workspace_bytes, stream);
+    return fwd_impl(d, q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L, residual, S_init, k_hist, o,
+                    S_final, k_hist_out, workspace, workspace_bytes, stream);
 }
 
 prism_status prism_decode_step(const prism_dims* d, const void* q, const void* k, const void* v,
                                const void* u, const void* g, const void* b, const void* a,
-                               const void* h, const void* conv_w, int L, float* S, void* k_hist,
-                               void* o, void* stream)
+                               const void* h, const void* conv_w, int L, int residual, float* S,
+                               void* k_hist, void* o, void* stream)
 {
-    if (!dims_ok(d) || L < 1 || L > PRISM_MAX_LEVELS || d->total_tokens != d->n_seqs)
+    if (!dims_ok(d) || L < 1 || L > PRISM_MAX_LEVELS || d->total_tokens != d->n_seqs ||
+        !residual_ok(residual))
         return PRISM_EINVAL;
     if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(g) || !ptr_ok(b) || !ptr_ok(conv_w) ||
         !ptr_ok(S) || !ptr_ok(k_hist) || !ptr_ok(o))
@@ -275,6 +289,7 @@ prism_status prism_decode_step(const prism_dims* d, const void* q, const void* k
     p.dk = d->dk;
     p.dv = d->dv;
     p.L = L;
+    p.gelu = residual == PRISM_RESIDUAL_GELU;
     p.q = q; p.k = k; p.v = v; p.u = u; p.a = a; p.h = h; p.g = g; p.b = b;
     p.conv_w = conv_w;
     p.S = S;

@@ -66,6 +66,17 @@ typedef enum {
 
 typedef enum { PRISM_F32 = 0, PRISM_BF16 = 1 } prism_dtype;
 
+/* Form of the residual chain of the write key (the `residual` argument).
+ *   PRISM_RESIDUAL_LINEAR  r_l = r_0 * prod_{j=1..l-1} (1 - a_j * h_j): the GELU of the
+ *                          refinement step absorbed into the gain, giving an element-wise
+ *                          linear recurrence with a closed form (WeChat page section
+ *                          消除 Step 间串行).  This is what prism_fwd computes.
+ *   PRISM_RESIDUAL_GELU    r_1 = r_0, r_{l+1} = r_l - a_l * GELU(h_l * r_l), GELU(x) = x Phi(x):
+ *                          the refinement step with its non-linearity kept (gist.science
+ *                          summary, section 2.2: delta = GELU(gain * residual), one step-size
+ *                          gate per level).  Identical to the linear form for L <= 2. */
+typedef enum { PRISM_RESIDUAL_LINEAR = 0, PRISM_RESIDUAL_GELU = 1 } prism_residual;
+
 typedef struct {
     int32_t n_seqs;        /* number of packed sequences, >= 1 */
     int32_t total_tokens;  /* T = cu_seqlens[n_seqs], >= 0 */
@@ -120,6 +131,19 @@ prism_status prism_prologue(const prism_dims* d,
                             void* kw, void* stream);
 
 /*
+ * Prologue with the options of the carried-state path: k_hist [n_seqs, H, 3, dk]
+ * (or NULL = zero) supplies the three k rows before each sequence's first token
+ * (see prism_fwd_resume), and `residual` (prism_residual) selects the form of
+ * the residual chain.  Other arguments as in prism_prologue; a residual value
+ * outside prism_residual returns PRISM_EINVAL.
+ */
+prism_status prism_prologue_ex(const prism_dims* d,
+                               const void* k, const void* u, const void* a,
+                               const void* h, const void* b, const void* conv_w,
+                               const void* k_hist, const int32_t* cu_seqlens, int L,
+                               int residual, void* kw, void* stream);
+
+/*
  * Scan only, from precomputed write keys kw [T, H, dk] (input dtype): the
  * gated delta-rule state recurrence S_t = g_t (I - b_t k_t k_t^T) S_{t-1} +
  * kw_t v_t^T, o_t = S_t^T q_t (WeChat page section 消除 Token 间串行: forget
@@ -152,6 +176,7 @@ prism_status prism_scan(const prism_dims* d,
  *               on, i.e. the last three k rows of each sequence, with k_hist
  *               (or zero) filling in for sequences shorter than three tokens.
  *               May be the same buffer as k_hist.
+ *   residual    prism_residual: the closed-form chain of prism_fwd or the GELU chain.
  * Other arguments, shapes and errors as in prism_fwd; the optional pointers
  * must be 16-byte aligned when given.
  */
@@ -159,7 +184,7 @@ prism_status prism_fwd_resume(const prism_dims* d,
                               const void* q, const void* k, const void* v,
                               const void* u, const void* g, const void* b,
                               const void* a, const void* h, const void* conv_w,
-                              const int32_t* cu_seqlens, int L,
+                              const int32_t* cu_seqlens, int L, int residual,
                               const float* S_init, const void* k_hist,
                               void* o, float* S_final, void* k_hist_out,
                               void* workspace, size_t workspace_bytes, void* stream);
@@ -181,6 +206,7 @@ prism_status prism_fwd_resume(const prism_dims* d,
  *   k_hist      [n_seqs, H, 3, dk] input dtype, in/out: the three k rows before
  *               the token (oldest first), replaced by the three ending with it
  *   o           out [n_seqs, H, dv], input dtype
+ *   residual    prism_residual (form of the residual chain)
  * All pointers non-null and 16-byte aligned (u, a, h may be NULL when L == 1).
  * dk and dv in {64, 128}, else PRISM_EUNSUPPORTED.  The write key is kept in
  * fp32 here (prism_fwd rounds it to the input dtype between its two kernels).
@@ -190,7 +216,7 @@ prism_status prism_decode_step(const prism_dims* d,
                                const void* q, const void* k, const void* v,
                                const void* u, const void* g, const void* b,
                                const void* a, const void* h, const void* conv_w, int L,
-                               float* S, void* k_hist, void* o, void* stream);
+                               int residual, float* S, void* k_hist, void* o, void* stream);
 
 /* Static description of a status code. */
 const char* prism_status_str(prism_status s);

@@ -27,7 +27,8 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("prism_fwd", "prism_prologue", "prism_scan", "prism_workspace_bytes",
-              "prism_status_str", "prism_abi_version", "prism_fwd_resume", "prism_decode_step"):
+              "prism_status_str", "prism_abi_version", "prism_fwd_resume", "prism_decode_step",
+              "prism_prologue_ex"):
         assert n in names
 
 
@@ -111,13 +112,13 @@ def test_prologue_and_scan_reject_bad_arguments(lib):
                           None) == B.PRISM_EUNSUPPORTED
 
 
-def _resume(lib, d, L=2, ws=1 << 30, **over):
+def _resume(lib, d, L=2, ws=1 << 30, residual=0, **over):
     args = dict(q=FAKE, k=FAKE, v=FAKE, u=FAKE, g=FAKE, b=FAKE, a=FAKE, h=FAKE, conv_w=FAKE,
                 cu=FAKE, s0=None, hist=None, o=FAKE, s=FAKE, hout=None, w=FAKE)
     args.update(over)
     A = args
     return lib.prism_fwd_resume(ctypes.byref(d), A["q"], A["k"], A["v"], A["u"], A["g"], A["b"],
-                                A["a"], A["h"], A["conv_w"], A["cu"], L, A["s0"], A["hist"],
+                                A["a"], A["h"], A["conv_w"], A["cu"], L, residual, A["s0"], A["hist"],
                                 A["o"], A["s"], A["hout"], A["w"], ws, None)
 
 
@@ -132,15 +133,18 @@ def test_fwd_resume_rejects_bad_arguments(lib):
     assert _resume(lib, ok, L=0) == B.PRISM_EINVAL
     assert _resume(lib, ok, ws=16) == B.PRISM_EINVAL
     assert _resume(lib, B.make_dims(1, 10, 1, 96, 64, B.PRISM_BF16)) == B.PRISM_EUNSUPPORTED
+    assert _resume(lib, ok, residual=2) == B.PRISM_EINVAL
+    assert _resume(lib, ok, residual=-1) == B.PRISM_EINVAL
 
 
-def _decode(lib, d, L=2, **over):
+def _decode(lib, d, L=2, residual=0, **over):
     args = dict(q=FAKE, k=FAKE, v=FAKE, u=FAKE, g=FAKE, b=FAKE, a=FAKE, h=FAKE, conv_w=FAKE,
                 S=FAKE, hist=FAKE, o=FAKE)
     args.update(over)
     A = args
     return lib.prism_decode_step(ctypes.byref(d), A["q"], A["k"], A["v"], A["u"], A["g"], A["b"],
-                                 A["a"], A["h"], A["conv_w"], L, A["S"], A["hist"], A["o"], None)
+                                 A["a"], A["h"], A["conv_w"], L, residual, A["S"], A["hist"],
+                                 A["o"], None)
 
 
 def test_decode_step_rejects_bad_arguments(lib):
@@ -154,6 +158,18 @@ def test_decode_step_rejects_bad_arguments(lib):
     assert _decode(lib, ok, L=17) == B.PRISM_EINVAL
     assert _decode(lib, B.make_dims(4, 4, 2, 96, 64, B.PRISM_BF16)) == B.PRISM_EUNSUPPORTED
     assert _decode(lib, B.make_dims(4, 4, 2, 64, 32, B.PRISM_F32)) == B.PRISM_EUNSUPPORTED
+    assert _decode(lib, ok, residual=5) == B.PRISM_EINVAL
+
+
+def test_prologue_ex_rejects_bad_arguments(lib):
+    from gated_delta_rule_prologue_amd import binding as B
+    d = B.make_dims(1, 10, 1, 64, 64, B.PRISM_BF16)
+    call = lambda L=3, residual=1, hist=None, kw=FAKE: lib.prism_prologue_ex(
+        ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, hist, FAKE, L, residual, kw, None)
+    assert call(residual=2) == B.PRISM_EINVAL
+    assert call(hist=FAKE + 2) == B.PRISM_EINVAL
+    assert call(kw=None) == B.PRISM_EINVAL
+    assert call(L=17) == B.PRISM_EINVAL
 
 
 def test_binding_checks_shapes_before_calling():
