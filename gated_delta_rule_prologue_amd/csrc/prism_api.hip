@@ -120,9 +120,9 @@ prism_status prologue_impl(const prism_dims* d, const void* k, const void* u, co
     p.heads = d->heads;
     p.dk = d->dk;
     p.L = L;
-    p.strip = env_int("PRISM_PROLOGUE_STRIP", 8);      // 4, 8 or 16 tokens per thread
-    if (p.strip != 4 && p.strip != 16)
-        p.strip = 8;
+    p.strip = env_int("PRISM_PROLOGUE_STRIP", 4);      // 4, 8 or 16 tokens per thread
+    if (p.strip != 8 && p.strip != 16)
+        p.strip = 4;
     p.narrow = env_int("PRISM_PROLOGUE_NARROW", 0) != 0;
     p.gelu = residual == PRISM_RESIDUAL_GELU;
     p.k = k; p.u = u; p.a = a; p.h = h; p.b = b; p.conv_w = conv_w;
