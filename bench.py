@@ -45,8 +45,8 @@ KERNEL_SOURCES = {
                                       "prologue_f32.hip", "prologue_bf16_ext.hip",
                                       "prologue_f32_ext.hip", "common.h", "kernels.h",
                                       "prism_api.hip")],
-    "scan": [_CSRC + f for f in ("chunk_scan_bf16.hip", "chunk_scan.hip", "common.h", "kernels.h",
-                                  "prism_api.hip")],
+    "scan": [_CSRC + f for f in ("chunk_scan_bf16.hip", "chunk_scan.hip", "long_seq.hip", "common.h",
+                                  "kernels.h", "prism_api.hip")],
     "decode": [_CSRC + f for f in ("decode.hip", "common.h", "kernels.h", "prism_api.hip")],
 }
 # Decode batches: (name, sequences, heads, dk, dv, L), one new token per sequence.
@@ -252,17 +252,25 @@ def main():
     base = binding.to_device(inp)
     copies = [base] + [{k: (v.clone() if v is not None else None) for k, v in base.items()}
                        for _ in range(max(1, args.copies) - 1)]
+    # the scan's segment buffers (few long sequences only; see prism_scan_ex)
+    dims = binding.Dims(n_seqs, T, w.heads, w.dk, w.dv, binding.PRISM_BF16 if esize == 2 else 0)
+    split_bytes = binding.scan_workspace_bytes(dims)
     for c in copies:
         c["kw"] = torch.empty_like(c["k"])
         c["o"] = torch.empty_like(c["v"])
         c["S"] = torch.empty((n_seqs, w.heads, w.dk, w.dv), dtype=torch.float32, device="cuda")
+        c["ws"] = torch.empty(split_bytes, dtype=torch.uint8, device="cuda") if split_bytes else None
     stream = torch.cuda.current_stream()
+
+    # one step = the launches prism_fwd makes: the prologue, then the scan
+    def scan(c):
+        binding.scan_ex(c["q"], c["k"], c["kw"], c["v"], c["g"], c["b"], c["cu_seqlens"],
+                        o=c["o"], S_final=c["S"], workspace=c["ws"], stream=stream)
 
     def launch(c):
         binding.prologue(c["k"], c["u"], c["a"], c["h"], c["b"], c["conv_w"], c["cu_seqlens"],
                          w.L, kw=c["kw"], stream=stream)
-        binding.scan(c["q"], c["k"], c["kw"], c["v"], c["g"], c["b"], c["cu_seqlens"],
-                     o=c["o"], S_final=c["S"], stream=stream)
+        scan(c)
 
     for i in range(args.warmup):
         launch(copies[i % len(copies)])
@@ -278,8 +286,7 @@ def main():
         binding.prologue(c["k"], c["u"], c["a"], c["h"], c["b"], c["conv_w"], c["cu_seqlens"],
                          w.L, kw=c["kw"], stream=stream)
         ev[i][1].record(stream)
-        binding.scan(c["q"], c["k"], c["kw"], c["v"], c["g"], c["b"], c["cu_seqlens"],
-                     o=c["o"], S_final=c["S"], stream=stream)
+        scan(c)
         ev[i][2].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -339,7 +346,8 @@ def main():
         "data": "synthetic (seeded; shapes and distributions of the workload, inputs resident in HBM)",
         "config": {"workload": w.name, "n_seqs": n_seqs, "seq_len": T // n_seqs, "heads": w.heads,
                    "dk": w.dk, "dv": w.dv, "L": w.L, "tokens_per_step": T,
-                   "head_tokens_per_step": work["head_tokens"], "input_copies": len(copies)},
+                   "head_tokens_per_step": work["head_tokens"], "input_copies": len(copies),
+                   "scan_segments_workspace_bytes": split_bytes},
         "head_tokens_per_s": K * work["head_tokens"] / elapsed,
         "roofline": {k: dominant[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
         "kernels": {"prologue": pro, "scan": scn,

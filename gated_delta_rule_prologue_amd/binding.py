@@ -7,7 +7,8 @@ functions raise if the library is not built -- there is no fallback path.
 Names follow the C ABI: ``fwd`` -> prism_fwd, ``fwd_resume`` ->
 prism_fwd_resume, ``decode_step`` -> prism_decode_step, ``prologue`` ->
 prism_prologue, ``prologue_ex`` -> prism_prologue_ex, ``scan`` -> prism_scan,
-``workspace_bytes`` -> prism_workspace_bytes.
+``scan_ex`` -> prism_scan_ex, ``workspace_bytes`` -> prism_workspace_bytes,
+``scan_workspace_bytes`` -> prism_scan_workspace_bytes.
 """
 from __future__ import annotations
 
@@ -60,6 +61,10 @@ def lib():
         L.prism_prologue.restype = I
         L.prism_scan.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
         L.prism_scan.restype = I
+        L.prism_scan_ex.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, S, P]
+        L.prism_scan_ex.restype = I
+        L.prism_scan_workspace_bytes.argtypes = [D]
+        L.prism_scan_workspace_bytes.restype = S
         L.prism_prologue_ex.argtypes = [D, P, P, P, P, P, P, P, P, I, I, P, P]
         L.prism_prologue_ex.restype = I
         L.prism_fwd_resume.argtypes = [D, P, P, P, P, P, P, P, P, P, P, I, I, P, P, P, P, P, P, S, P]
@@ -199,6 +204,36 @@ def scan(q, k, kw, v, g, b, cu_seqlens, o=None, S_final=None, stream=None):
     _check("prism_scan", lib().prism_scan(
         ctypes.byref(d), _ptr(q), _ptr(k), _ptr(kw), _ptr(v), _ptr(g), _ptr(b), _ptr(cu_seqlens),
         _ptr(o), _ptr(S_final), _stream(stream)))
+    return o, S_final
+
+
+def scan_workspace_bytes(dims: Dims) -> int:
+    return int(lib().prism_scan_workspace_bytes(ctypes.byref(dims)))
+
+
+def scan_ex(q, k, kw, v, g, b, cu_seqlens, S_init=None, o=None, S_final=None, workspace=None,
+            stream=None):
+    """Scan with a start state and the segment split for few long sequences
+    (prism_scan_ex).  Returns (o, S_final)."""
+    d = _dims_of(q, v, cu_seqlens)
+    _check_scan(d, q.dtype, q, k, kw, v, g, b)
+    if S_init is not None:
+        _expect("S_init", S_init, (d.n_seqs, d.heads, d.dk, d.dv), torch.float32)
+    need = scan_workspace_bytes(d)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if o is None:
+        o = torch.empty_like(v)
+    if S_final is None:
+        S_final = torch.empty((d.n_seqs, d.heads, d.dk, d.dv), dtype=torch.float32, device=q.device)
+    _expect("o", o, v.shape, v.dtype)
+    _expect("S_final", S_final, (d.n_seqs, d.heads, d.dk, d.dv), torch.float32)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    _check("prism_scan_ex", lib().prism_scan_ex(
+        ctypes.byref(d), _ptr(q), _ptr(k), _ptr(kw), _ptr(v), _ptr(g), _ptr(b), _ptr(cu_seqlens),
+        _ptr(S_init), _ptr(o), _ptr(S_final), _ptr(workspace), nbytes, _stream(stream)))
     return o, S_final
 
 

@@ -768,10 +768,10 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(
 // rows come from HBM once and from that L2 for the other slices.
 constexpr int kXcds = 8;
 constexpr int kDiagRowBlocks = 2;               // four wavefronts: row blocks moved by the diagonal helper
-__device__ __forceinline__ void xcd_map(int n_slices, int& slice, int& chain)
+__device__ __forceinline__ void xcd_map(unsigned w, unsigned n_blocks, int n_slices, int& slice,
+                                        int& chain)
 {
-    const unsigned w = blockIdx.x;
-    const unsigned n_chains = gridDim.x / (unsigned)n_slices;
+    const unsigned n_chains = n_blocks / (unsigned)n_slices;
     if (n_chains % kXcds == 0) {
         const unsigned x = w % kXcds, j = w / kXcds;
         chain = (int)((j / (unsigned)n_slices) * kXcds + x);
@@ -808,6 +808,7 @@ struct WsCtx {
     const float* s_init;
     float* s_final;
     int n, e, H, DV, j0, seq0, seq1, nchunks, lane;
+    bool s_identity;                             // start from S = I (dv = dk) instead of s_init
     int64_t rowQK, rowV;
 };
 
@@ -1003,11 +1004,14 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
         const int nqk = nt * (int)c.rowQK * 2;   // rows past the chunk end read as zero
         Src r;
         r.k = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(c.k + base), 0, nqk, kRsrcFlags);
-        r.kw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(c.kw + base), 0, nqk, kRsrcFlags);
+        // a null kw or v reads as zero (an empty buffer range): the transition-only
+        // scan, whose write term kw v^T vanishes
+        r.kw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(c.kw ? c.kw + base : c.k), 0,
+                                                 c.kw ? nqk : 0, kRsrcFlags);
         r.q = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(c.q + base), 0, nqk, kRsrcFlags);
         r.v = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(c.v + (int64_t)c0 * c.rowV + (int64_t)c.e * c.DV + c.j0), 0,
-            nt * (int)c.rowV * 2, kRsrcFlags);
+            const_cast<uint16_t*>(c.v ? c.v + (int64_t)c0 * c.rowV + (int64_t)c.e * c.DV + c.j0 : c.k),
+            0, c.v ? nt * (int)c.rowV * 2 : 0, kRsrcFlags);
         r.g = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(c.g + (int64_t)c0 * c.H + c.e), 0,
                                                 nt * c.H * 2, kRsrcFlags);
         r.b = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(c.b + (int64_t)c0 * c.H + c.e), 0,
@@ -1335,6 +1339,13 @@ __device__ __forceinline__ void state_loop(const WsCtx& c, int jb)
     f32x4_t S[NI];
     load_state<D>(S, c.s_init, (((int64_t)c.n * c.H + c.e) * D) * c.DV + c.j0 + jb * 16, c.DV,
                   lane, true);
+    if (c.s_identity) {
+#pragma unroll
+        for (int ib = 0; ib < NI; ++ib)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                S[ib][r] = (ib * 16 + lg * 4 + r == c.j0 + jb * 16 + li) ? 1.f : 0.f;
+    }
     lds_barrier();
     lds_barrier();
     lds_barrier();
@@ -1389,7 +1400,9 @@ __global__ __launch_bounds__(NW * 64) void scan_ws_kernel(
     const uint16_t* __restrict__ kw, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ g, const uint16_t* __restrict__ b,
     const int32_t* __restrict__ cu, int H, int DV, int n_slices,
-    const float* __restrict__ s_init, uint16_t* __restrict__ o, float* __restrict__ s_final)
+    const float* __restrict__ s_init, int s_identity, uint16_t* __restrict__ o,
+    float* __restrict__ s_final, int split_block, int DV1, int n_slices1, uint16_t* __restrict__ o1,
+    float* __restrict__ s_final1)
 {
     using Ly = LayoutWS<D, DVS>;
     constexpr int NJ = DVS / 16;
@@ -1400,26 +1413,37 @@ __global__ __launch_bounds__(NW * 64) void scan_ws_kernel(
     __shared__ __attribute__((aligned(16))) unsigned char smem[Ly::total];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // Blocks from split_block on run a second scan over the same sequences: the
+    // transitions alone (start S = I with DV1 = D columns, no write term),
+    // writing o1 and s_final1.  One launch keeps both on the chip at once.
+    const bool job1 = (int)blockIdx.x >= split_block;
     int slice, chain;
-    xcd_map(n_slices, slice, chain);
+    if (job1)
+        xcd_map(blockIdx.x - (unsigned)split_block, gridDim.x - (unsigned)split_block, n_slices1,
+                slice, chain);
+    else
+        xcd_map(blockIdx.x, min(gridDim.x, (unsigned)split_block), n_slices, slice, chain);
 
     WsCtx c;
     c.smem = smem;
-    c.q = q; c.k = k; c.kw = kw; c.v = v; c.g = g; c.b = b;
-    c.o = o;
-    c.s_init = s_init;
-    c.s_final = s_final;
+    c.q = q; c.k = k; c.g = g; c.b = b;
+    c.kw = job1 ? nullptr : kw;
+    c.v = job1 ? nullptr : v;
+    c.o = job1 ? o1 : o;
+    c.s_init = job1 ? nullptr : s_init;
+    c.s_identity = job1 || s_identity != 0;
+    c.s_final = job1 ? s_final1 : s_final;
     c.n = chain / H;
     c.e = chain % H;
     c.H = H;
-    c.DV = DV;
+    c.DV = job1 ? DV1 : DV;
     c.j0 = slice * DVS;
     c.seq0 = cu[c.n];
     c.seq1 = cu[c.n + 1];
     c.nchunks = (c.seq1 - c.seq0 + kC - 1) / kC;
     c.lane = tid & 63;
     c.rowQK = (int64_t)H * D;
-    c.rowV = (int64_t)H * DV;
+    c.rowV = (int64_t)H * c.DV;              // the second job's rows are DV1 wide
 
     {
         // matrices (their upper blocks are never written), gates, scratch
@@ -1466,8 +1490,26 @@ static hipError_t launch_ws(const ScanArgs& p, hipStream_t stream)
     hipLaunchKernelGGL((scan_ws_kernel<D, DVS, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
                        (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.kw,
                        (const uint16_t*)p.v, (const uint16_t*)p.g, (const uint16_t*)p.b,
-                       p.cu_seqlens, p.heads, p.dv, n_slices, p.s_init, (uint16_t*)p.o,
-                       p.s_final);
+                       p.cu_seqlens, p.heads, p.dv, n_slices, p.s_init, p.identity_init ? 1 : 0, (uint16_t*)p.o,
+                       p.s_final, 0x7fffffff, 0, 1, nullptr, nullptr);
+    return hipGetLastError();
+}
+
+// Two scans in one launch of the eight-wavefront kernel: `a` as given, and
+// `m`, the transitions alone over the same sequences (kw = v = null, start
+// S = I, m.dv = D columns), in the blocks after a's.
+template <int D>
+static hipError_t launch_pair(const ScanArgs& a, const ScanArgs& m, hipStream_t stream)
+{
+    const int na = a.dv / 32, nm = m.dv / 32;
+    const int64_t ba = (int64_t)a.n_seqs * a.heads * na, bm = (int64_t)m.n_seqs * m.heads * nm;
+    if (ba + bm == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL((scan_ws_kernel<D, 32, 8>), dim3((unsigned)(ba + bm)), dim3(512), 0, stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.kw,
+                       (const uint16_t*)a.v, (const uint16_t*)a.g, (const uint16_t*)a.b,
+                       a.cu_seqlens, a.heads, a.dv, na, a.s_init, 0, (uint16_t*)a.o, a.s_final,
+                       (int)ba, m.dv, nm, (uint16_t*)m.o, m.s_final);
     return hipGetLastError();
 }
 
@@ -1495,9 +1537,21 @@ bool scan_bf16_supported(int dk, int dv, int dvs)
     return (dk == 64 || dk == 128) && (dvs == 16 || dvs == 32 || dvs == 64);
 }
 
+hipError_t launch_scan_bf16_pair(const ScanArgs& a, const ScanArgs& m, hipStream_t s)
+{
+    if (!scan_bf16_supported(a.dk, a.dv, 32) || m.dv != a.dk || !a.specialised || a.ws_waves != 8 ||
+        m.n_seqs != a.n_seqs || m.cu_seqlens != a.cu_seqlens)
+        return hipErrorInvalidValue;
+    return a.dk == 64 ? bf16scan::launch_pair<64>(a, m, s) : bf16scan::launch_pair<128>(a, m, s);
+}
+
 hipError_t launch_scan_bf16(const ScanArgs& p, hipStream_t s)
 {
     if (!scan_bf16_supported(p.dk, p.dv, p.dv_slice))
+        return hipErrorInvalidValue;
+    // the transition-only form (identity start, no write term) exists in the
+    // wavefront-specialised kernels only
+    if ((p.identity_init || !p.kw || !p.v) && !p.specialised)
         return hipErrorInvalidValue;
     if (p.specialised) {
         const bool w8 = p.ws_waves == 8;

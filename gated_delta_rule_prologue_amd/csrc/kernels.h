@@ -27,6 +27,8 @@ struct ScanArgs {
     const void *q, *k, *kw, *v, *g, *b;
     const int32_t* cu_seqlens;
     const float* s_init;            // [n_seqs, H, dk, dv] start states, or null (zero)
+    bool identity_init;             // start from S = I (needs dv == dk); with kw = v = null this
+                                    // scans the transition alone (specialised bf16 kernels only)
     void* o;
     float* s_final;
 };
@@ -49,6 +51,14 @@ struct DecodeArgs {
     void* o;
 };
 
+// Few long sequences: the scan split into P segments per sequence, scanned
+// side by side and chained (long_seq.hip).  split_segments gives P (1 = no
+// split) for the shape and the number of compute units; the launch needs
+// split_workspace_bytes of device scratch.  Specialised bf16 kernels only.
+int split_segments(int n_seqs, int heads, int dk, int dv, int total_tokens, int cus);
+size_t split_workspace_bytes(int n_seqs, int heads, int dk, int dv, int total_tokens, int P);
+hipError_t launch_split_scan(const ScanArgs& p, int P, void* ws, hipStream_t stream);
+
 // One token per sequence through the recurrence (state and history in place).
 hipError_t launch_decode(const DecodeArgs& p, hipStream_t stream);
 bool decode_supported(int dk, int dv);
@@ -60,6 +70,10 @@ bool scan_supported(bool bf16, int dk, int dv, int dv_slice);
 
 // bf16 chunk scan with the register-resident state path.
 hipError_t launch_scan_bf16(const ScanArgs& p, hipStream_t stream);
+// `a` on the eight-wavefront kernel (32-column slices) and, in the same launch,
+// `m`: the transitions alone over the same sequences (m.dv = dk, start S = I,
+// no write term), writing m.o and m.s_final.
+hipError_t launch_scan_bf16_pair(const ScanArgs& a, const ScanArgs& m, hipStream_t stream);
 bool scan_bf16_supported(int dk, int dv, int dv_slice);
 
 }  // namespace prism

@@ -94,6 +94,39 @@ prism_status check_scan_shape(const prism_dims* d)
 
 prism_status from_hip(hipError_t e) { return e == hipSuccess ? PRISM_OK : PRISM_EHIP; }
 
+int device_cus()
+{
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    return n;
+}
+
+// Segments per sequence of the split scan for a forward pass (1 = one scan
+// launch over whole sequences).  The split serves few, long sequences on the
+// eight-wavefront bf16 kernel; PRISM_SPLIT=0 turns it off, PRISM_SPLIT=P >= 2
+// forces P segments.
+int split_for(const prism_dims* d)
+{
+    if (d->dtype != PRISM_BF16 || env_int("PRISM_SCAN_GENERIC", 0) != 0 || !ws8_enabled() ||
+        pick_dv_slice(d) != 32 || d->total_tokens == 0)
+        return 1;
+    const int forced = env_int("PRISM_SPLIT", -1);
+    if (forced == 0)
+        return 1;
+    if (forced >= 2 && forced <= 64)
+        return (d->dk == 64 || d->dk == 128) && (d->dv == 64 || d->dv == 128) ? forced : 1;
+    return prism::split_segments(d->n_seqs, d->heads, d->dk, d->dv, d->total_tokens, device_cus());
+}
+
+size_t kw_bytes(const prism_dims* d)
+{
+    size_t n = (size_t)d->total_tokens * (size_t)d->heads * (size_t)d->dk * elem_bytes(d);
+    n = (n + 255) / 256 * 256;
+    return n < 256 ? 256 : n;
+}
+
 // Optional pointer: null, or 16-byte aligned.
 bool opt_ok(const void* p) { return aligned16(p); }
 
@@ -134,7 +167,7 @@ prism_status prologue_impl(const prism_dims* d, const void* k, const void* u, co
 
 prism_status scan_impl(const prism_dims* d, const void* q, const void* k, const void* kw,
                        const void* v, const void* g, const void* b, const int32_t* cu_seqlens,
-                       const float* S_init, void* o, float* S_final, void* stream)
+                       const float* S_init, void* o, float* S_final, void* split_ws, void* stream)
 {
     if (!dims_ok(d))
         return PRISM_EINVAL;
@@ -158,8 +191,12 @@ prism_status scan_impl(const prism_dims* d, const void* q, const void* k, const 
     p.q = q; p.k = k; p.kw = kw; p.v = v; p.g = g; p.b = b;
     p.cu_seqlens = cu_seqlens;
     p.s_init = S_init;
+    p.identity_init = false;
     p.o = o;
     p.s_final = S_final;
+    const int P = split_ws ? split_for(d) : 1;
+    if (P >= 2)
+        return from_hip(prism::launch_split_scan(p, P, split_ws, (hipStream_t)stream));
     if (use_bf16_kernel(d, p.dv_slice))
         return from_hip(prism::launch_scan_bf16(p, (hipStream_t)stream));
     return from_hip(prism::launch_scan(p, (hipStream_t)stream));
@@ -188,7 +225,8 @@ prism_status fwd_impl(const prism_dims* d, const void* q, const void* k, const v
                        stream);
     if (st != PRISM_OK)
         return st;
-    st = scan_impl(d, q, k, workspace, v, g, b, cu_seqlens, S_init, o, S_final, stream);
+    st = scan_impl(d, q, k, workspace, v, g, b, cu_seqlens, S_init, o, S_final,
+                   static_cast<unsigned char*>(workspace) + kw_bytes(d), stream);
     if (st != PRISM_OK || !k_hist_out)
         return st;
     // after the prologue on the same stream: k_hist_out may be k_hist itself
@@ -214,13 +252,19 @@ const char* prism_status_str(prism_status s)
     return "unknown status";
 }
 
+size_t prism_scan_workspace_bytes(const prism_dims* d)
+{
+    if (!dims_ok(d))
+        return 0;
+    return prism::split_workspace_bytes(d->n_seqs, d->heads, d->dk, d->dv, d->total_tokens,
+                                        split_for(d));
+}
+
 size_t prism_workspace_bytes(const prism_dims* d, int L)
 {
     if (!dims_ok(d) || L < 1 || L > PRISM_MAX_LEVELS)
         return 0;
-    size_t n = (size_t)d->total_tokens * (size_t)d->heads * (size_t)d->dk * elem_bytes(d);
-    n = (n + 255) / 256 * 256;
-    return n < 256 ? 256 : n;
+    return kw_bytes(d) + prism_scan_workspace_bytes(d);
 }
 
 prism_status prism_prologue(const prism_dims* d, const void* k, const void* u, const void* a,
@@ -243,7 +287,21 @@ prism_status prism_scan(const prism_dims* d, const void* q, const void* k, const
                         const void* v, const void* g, const void* b, const int32_t* cu_seqlens,
                         void* o, float* S_final, void* stream)
 {
-    return scan_impl(d, q, k, kw, v, g, b, cu_seqlens, nullptr, o, S_final, stream);
+    return scan_impl(d, q, k, kw, v, g, b, cu_seqlens, nullptr, o, S_final, nullptr, stream);
+}
+
+prism_status prism_scan_ex(const prism_dims* d, const void* q, const void* k, const void* kw,
+                           const void* v, const void* g, const void* b, const int32_t* cu_seqlens,
+                           const float* S_init, void* o, float* S_final, void* workspace,
+                           size_t workspace_bytes, void* stream)
+{
+    if (!dims_ok(d))
+        return PRISM_EINVAL;
+    const size_t need = prism_scan_workspace_bytes(d);
+    if (need > 0 && (!ptr_ok(workspace) || workspace_bytes < need))
+        return PRISM_EINVAL;
+    return scan_impl(d, q, k, kw, v, g, b, cu_seqlens, S_init, o, S_final,
+                     need > 0 ? workspace : nullptr, stream);
 }
 
 prism_status prism_fwd(const prism_dims* d, const void* q, const void* k, const void* v,

@@ -88,8 +88,9 @@ typedef struct {
 
 #define PRISM_MAX_LEVELS 16
 
-/* Bytes of device workspace prism_fwd needs: the write keys kw [T, H, dk] in
- * the input dtype, rounded up to 256 bytes.  Returns 0 for invalid dims or L. */
+/* Bytes of device workspace prism_fwd (and prism_fwd_resume) needs: the write
+ * keys kw [T, H, dk] in the input dtype, rounded up to 256 bytes, plus
+ * prism_scan_workspace_bytes(d).  Returns 0 for invalid dims or L. */
 size_t prism_workspace_bytes(const prism_dims* d, int L);
 
 /*
@@ -217,6 +218,32 @@ prism_status prism_decode_step(const prism_dims* d,
                                const void* u, const void* g, const void* b,
                                const void* a, const void* h, const void* conv_w, int L,
                                int residual, float* S, void* k_hist, void* o, void* stream);
+
+/*
+ * Scan only, with the options of the full forward pass: a start state S_init
+ * (fp32 [n_seqs, H, dk, dv], NULL = zero; may be S_final) and a device
+ * workspace of prism_scan_workspace_bytes(d) bytes (NULL allowed when that is
+ * 0).  With few, long sequences (too few (sequence, head) chains to occupy
+ * the GPU) each sequence is cut into segments that are scanned side by side
+ * from zero, together with scans of their transitions alone; the segments are
+ * then chained through the transitions and the carried state is added to
+ * the outputs.  The recurrence is affine in the state (gist.science section
+ * 2.1: S_t = S_{t-1} A_t + B_t with input-only A_t, B_t), so this changes the
+ * result only by rounding.  The workspace holds those segment buffers.
+ * prism_fwd and prism_fwd_resume run this scan.  Other arguments as in
+ * prism_scan.
+ */
+prism_status prism_scan_ex(const prism_dims* d,
+                           const void* q, const void* k, const void* kw, const void* v,
+                           const void* g, const void* b, const int32_t* cu_seqlens,
+                           const float* S_init, void* o, float* S_final,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace prism_scan_ex needs for the shape (0: no segment
+ * split for it).  Depends on the current device's compute-unit count and on
+ * PRISM_SPLIT (0 = never split, P >= 2 = always P segments).  Returns 0 for
+ * invalid dims. */
+size_t prism_scan_workspace_bytes(const prism_dims* d);
 
 /* Static description of a status code. */
 const char* prism_status_str(prism_status s);
