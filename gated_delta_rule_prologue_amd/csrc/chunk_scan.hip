@@ -647,8 +647,6 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(
 template <typename T, int D, int DVS>
 static hipError_t launch(const ScanArgs& p, hipStream_t stream)
 {
-    if (p.identity_init || !p.kw || !p.v)       // transition-only scans: specialised kernels
-        return hipErrorInvalidValue;
     const int n_slices = p.dv / DVS;
     const int64_t blocks = (int64_t)p.n_seqs * p.heads * n_slices;
     if (blocks == 0)

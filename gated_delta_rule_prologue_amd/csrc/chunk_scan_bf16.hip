@@ -808,7 +808,7 @@ struct WsCtx {
     const float* s_init;
     float* s_final;
     int n, e, H, DV, j0, seq0, seq1, nchunks, lane;
-    bool s_identity;                             // start from S = I (dv = dk) instead of s_init
+    bool s_identity;                             // start from S = I (the transition-only job)
     int64_t rowQK, rowV;
 };
 
@@ -1400,7 +1400,7 @@ __global__ __launch_bounds__(NW * 64) void scan_ws_kernel(
     const uint16_t* __restrict__ kw, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ g, const uint16_t* __restrict__ b,
     const int32_t* __restrict__ cu, int H, int DV, int n_slices,
-    const float* __restrict__ s_init, int s_identity, uint16_t* __restrict__ o,
+    const float* __restrict__ s_init, uint16_t* __restrict__ o,
     float* __restrict__ s_final, int split_block, int DV1, int n_slices1, uint16_t* __restrict__ o1,
     float* __restrict__ s_final1)
 {
@@ -1431,7 +1431,7 @@ __global__ __launch_bounds__(NW * 64) void scan_ws_kernel(
     c.v = job1 ? nullptr : v;
     c.o = job1 ? o1 : o;
     c.s_init = job1 ? nullptr : s_init;
-    c.s_identity = job1 || s_identity != 0;
+    c.s_identity = job1;
     c.s_final = job1 ? s_final1 : s_final;
     c.n = chain / H;
     c.e = chain % H;
@@ -1490,7 +1490,7 @@ static hipError_t launch_ws(const ScanArgs& p, hipStream_t stream)
     hipLaunchKernelGGL((scan_ws_kernel<D, DVS, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
                        (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.kw,
                        (const uint16_t*)p.v, (const uint16_t*)p.g, (const uint16_t*)p.b,
-                       p.cu_seqlens, p.heads, p.dv, n_slices, p.s_init, p.identity_init ? 1 : 0, (uint16_t*)p.o,
+                       p.cu_seqlens, p.heads, p.dv, n_slices, p.s_init, (uint16_t*)p.o,
                        p.s_final, 0x7fffffff, 0, 1, nullptr, nullptr);
     return hipGetLastError();
 }
@@ -1508,7 +1508,7 @@ static hipError_t launch_pair(const ScanArgs& a, const ScanArgs& m, hipStream_t 
     hipLaunchKernelGGL((scan_ws_kernel<D, 32, 8>), dim3((unsigned)(ba + bm)), dim3(512), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.kw,
                        (const uint16_t*)a.v, (const uint16_t*)a.g, (const uint16_t*)a.b,
-                       a.cu_seqlens, a.heads, a.dv, na, a.s_init, 0, (uint16_t*)a.o, a.s_final,
+                       a.cu_seqlens, a.heads, a.dv, na, a.s_init, (uint16_t*)a.o, a.s_final,
                        (int)ba, m.dv, nm, (uint16_t*)m.o, m.s_final);
     return hipGetLastError();
 }
@@ -1548,10 +1548,6 @@ hipError_t launch_scan_bf16_pair(const ScanArgs& a, const ScanArgs& m, hipStream
 hipError_t launch_scan_bf16(const ScanArgs& p, hipStream_t s)
 {
     if (!scan_bf16_supported(p.dk, p.dv, p.dv_slice))
-        return hipErrorInvalidValue;
-    // the transition-only form (identity start, no write term) exists in the
-    // wavefront-specialised kernels only
-    if ((p.identity_init || !p.kw || !p.v) && !p.specialised)
         return hipErrorInvalidValue;
     if (p.specialised) {
         const bool w8 = p.ws_waves == 8;

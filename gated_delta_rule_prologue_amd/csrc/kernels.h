@@ -27,8 +27,6 @@ struct ScanArgs {
     const void *q, *k, *kw, *v, *g, *b;
     const int32_t* cu_seqlens;
     const float* s_init;            // [n_seqs, H, dk, dv] start states, or null (zero)
-    bool identity_init;             // start from S = I (needs dv == dk); with kw = v = null this
-                                    // scans the transition alone (specialised bf16 kernels only)
     void* o;
     float* s_final;
 };

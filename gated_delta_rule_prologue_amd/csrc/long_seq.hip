@@ -256,13 +256,11 @@ hipError_t launch_split_scan(const ScanArgs& p, int P, void* ws, hipStream_t s)
     a.n_seqs = segs;
     a.cu_seqlens = seg_cu;
     a.s_init = nullptr;
-    a.identity_init = false;
     a.s_final = S_loc;
     ScanArgs m = a;
     m.dv = dk;
     m.kw = nullptr;
     m.v = nullptr;
-    m.identity_init = true;
     m.o = op;
     m.s_final = M;
     if ((err = launch_scan_bf16_pair(a, m, s)) != hipSuccess)

@@ -191,7 +191,6 @@ prism_status scan_impl(const prism_dims* d, const void* q, const void* k, const 
     p.q = q; p.k = k; p.kw = kw; p.v = v; p.g = g; p.b = b;
     p.cu_seqlens = cu_seqlens;
     p.s_init = S_init;
-    p.identity_init = false;
     p.o = o;
     p.s_final = S_final;
     const int P = split_ws ? split_for(d) : 1;
