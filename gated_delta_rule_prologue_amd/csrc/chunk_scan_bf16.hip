@@ -1402,7 +1402,7 @@ __global__ __launch_bounds__(NW * 64) void scan_ws_kernel(
     const int32_t* __restrict__ cu, int H, int DV, int n_slices,
     const float* __restrict__ s_init, uint16_t* __restrict__ o,
     float* __restrict__ s_final, int split_block, int DV1, int n_slices1, uint16_t* __restrict__ o1,
-    float* __restrict__ s_final1)
+    float* __restrict__ s_final1, int skip1)
 {
     using Ly = LayoutWS<D, DVS>;
     constexpr int NJ = DVS / 16;
@@ -1416,13 +1416,20 @@ __global__ __launch_bounds__(NW * 64) void scan_ws_kernel(
     // Blocks from split_block on run a second scan over the same sequences: the
     // transitions alone (start S = I with DV1 = D columns, no write term),
     // writing o1 and s_final1.  One launch keeps both on the chip at once.
+    // With skip1 = P > 1 the second scan leaves out sequences 0, P, 2P, ...
+    // (first segments started from zero need no transition).
     const bool job1 = (int)blockIdx.x >= split_block;
     int slice, chain;
-    if (job1)
+    if (job1) {
         xcd_map(blockIdx.x - (unsigned)split_block, gridDim.x - (unsigned)split_block, n_slices1,
                 slice, chain);
-    else
+        if (skip1 > 1) {
+            const int s1 = chain / H;
+            chain = ((s1 / (skip1 - 1)) * skip1 + 1 + s1 % (skip1 - 1)) * H + chain % H;
+        }
+    } else {
         xcd_map(blockIdx.x, min(gridDim.x, (unsigned)split_block), n_slices, slice, chain);
+    }
 
     WsCtx c;
     c.smem = smem;
@@ -1491,25 +1498,27 @@ static hipError_t launch_ws(const ScanArgs& p, hipStream_t stream)
                        (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.kw,
                        (const uint16_t*)p.v, (const uint16_t*)p.g, (const uint16_t*)p.b,
                        p.cu_seqlens, p.heads, p.dv, n_slices, p.s_init, (uint16_t*)p.o,
-                       p.s_final, 0x7fffffff, 0, 1, nullptr, nullptr);
+                       p.s_final, 0x7fffffff, 0, 1, nullptr, nullptr, 0);
     return hipGetLastError();
 }
 
 // Two scans in one launch of the eight-wavefront kernel: `a` as given, and
 // `m`, the transitions alone over the same sequences (kw = v = null, start
-// S = I, m.dv = D columns), in the blocks after a's.
+// S = I, m.dv = D columns) except every skip-th one from the first (skip > 1),
+// in the blocks after a's.
 template <int D>
-static hipError_t launch_pair(const ScanArgs& a, const ScanArgs& m, hipStream_t stream)
+static hipError_t launch_pair(const ScanArgs& a, const ScanArgs& m, int skip, hipStream_t stream)
 {
     const int na = a.dv / 32, nm = m.dv / 32;
-    const int64_t ba = (int64_t)a.n_seqs * a.heads * na, bm = (int64_t)m.n_seqs * m.heads * nm;
+    const int m_seqs = skip > 1 ? m.n_seqs / skip * (skip - 1) : m.n_seqs;
+    const int64_t ba = (int64_t)a.n_seqs * a.heads * na, bm = (int64_t)m_seqs * m.heads * nm;
     if (ba + bm == 0)
         return hipSuccess;
     hipLaunchKernelGGL((scan_ws_kernel<D, 32, 8>), dim3((unsigned)(ba + bm)), dim3(512), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.kw,
                        (const uint16_t*)a.v, (const uint16_t*)a.g, (const uint16_t*)a.b,
                        a.cu_seqlens, a.heads, a.dv, na, a.s_init, (uint16_t*)a.o, a.s_final,
-                       (int)ba, m.dv, nm, (uint16_t*)m.o, m.s_final);
+                       (int)ba, m.dv, nm, (uint16_t*)m.o, m.s_final, skip);
     return hipGetLastError();
 }
 
@@ -1537,12 +1546,13 @@ bool scan_bf16_supported(int dk, int dv, int dvs)
     return (dk == 64 || dk == 128) && (dvs == 16 || dvs == 32 || dvs == 64);
 }
 
-hipError_t launch_scan_bf16_pair(const ScanArgs& a, const ScanArgs& m, hipStream_t s)
+hipError_t launch_scan_bf16_pair(const ScanArgs& a, const ScanArgs& m, int skip, hipStream_t s)
 {
     if (!scan_bf16_supported(a.dk, a.dv, 32) || m.dv != a.dk || !a.specialised || a.ws_waves != 8 ||
-        m.n_seqs != a.n_seqs || m.cu_seqlens != a.cu_seqlens)
+        m.n_seqs != a.n_seqs || m.cu_seqlens != a.cu_seqlens || (skip > 1 && a.n_seqs % skip != 0))
         return hipErrorInvalidValue;
-    return a.dk == 64 ? bf16scan::launch_pair<64>(a, m, s) : bf16scan::launch_pair<128>(a, m, s);
+    return a.dk == 64 ? bf16scan::launch_pair<64>(a, m, skip, s)
+                      : bf16scan::launch_pair<128>(a, m, skip, s);
 }
 
 hipError_t launch_scan_bf16(const ScanArgs& p, hipStream_t s)

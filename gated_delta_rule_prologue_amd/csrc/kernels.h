@@ -70,8 +70,9 @@ bool scan_supported(bool bf16, int dk, int dv, int dv_slice);
 hipError_t launch_scan_bf16(const ScanArgs& p, hipStream_t stream);
 // `a` on the eight-wavefront kernel (32-column slices) and, in the same launch,
 // `m`: the transitions alone over the same sequences (m.dv = dk, start S = I,
-// no write term), writing m.o and m.s_final.
-hipError_t launch_scan_bf16_pair(const ScanArgs& a, const ScanArgs& m, hipStream_t stream);
+// no write term), writing m.o and m.s_final; with skip > 1 the sequences
+// 0, skip, 2 skip, ... are left out of `m`.
+hipError_t launch_scan_bf16_pair(const ScanArgs& a, const ScanArgs& m, int skip, hipStream_t stream);
 bool scan_bf16_supported(int dk, int dv, int dv_slice);
 
 }  // namespace prism

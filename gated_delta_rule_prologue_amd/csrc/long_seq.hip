@@ -67,8 +67,9 @@ __global__ __launch_bounds__(256) void combine_kernel(
     const int n = chain / H, e = chain % H;
     const int64_t seg = ((int64_t)n * P + p) * H + e;
     const float* Mp = M + seg * D * D + (int64_t)rb * B * D;
-    for (int x = tid; x < B * D; x += 256)
-        sM[x / D][x % D] = Mp[x];
+    if (S_prev)                                  // (no M_p for a first segment from zero)
+        for (int x = tid; x < B * D; x += 256)
+            sM[x / D][x % D] = Mp[x];
     const float* prev = S_prev ? S_prev + n * prev_nstride + (int64_t)e * D * DV : nullptr;
     for (int x = tid; x < D * B; x += 256)
         sP[x / B][x % B] = prev ? prev[(int64_t)(x / B) * DV + cb * B + x % B] : 0.f;
@@ -79,7 +80,8 @@ __global__ __launch_bounds__(256) void combine_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r)
         acc[r] = loc[(int64_t)(rb * B + rr * 4 + r) * DV + j];
-    for (int k = 0; k < D; ++k) {
+    // a zero start state skips the product (M_p of such a first segment is never computed)
+    for (int k = 0; prev && k < D; ++k) {
         const float pk = sP[k][jj];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -263,7 +265,8 @@ hipError_t launch_split_scan(const ScanArgs& p, int P, void* ws, hipStream_t s)
     m.v = nullptr;
     m.o = op;
     m.s_final = M;
-    if ((err = launch_scan_bf16_pair(a, m, s)) != hipSuccess)
+    // a first segment started from zero needs neither its transition nor o'
+    if ((err = launch_scan_bf16_pair(a, m, p.s_init ? 0 : P, s)) != hipSuccess)
         return err;
     // 2. chain the segments (all but the last step), 3. add the carried states
     // to the outputs, 4. the last step, which writes S_final: the correction
