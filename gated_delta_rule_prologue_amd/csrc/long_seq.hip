@@ -93,8 +93,8 @@ __global__ __launch_bounds__(256) void combine_kernel(
         out[(int64_t)(rb * B + rr * 4 + r) * DV + j] = acc[r];
 }
 
-// o[t] += S_in(p)^T o'[t].  Grid: (segment x group of kTPW tiles of 64 tokens
-// counted from the segment start, heads).  The segment's start state is
+// o[t] += S_in(p)^T o'[t].  Grid: (heads, segment x group of kTPW tiles of 64
+// tokens counted from the segment start).  The segment's start state is
 // staged once as S_in^T in bf16 (LDS); wave w computes rows 16 w .. 16 w + 15
 // of a tile on 16x16x32 bf16 MFMA (A = o' rows straight from HBM, B = S_in^T
 // from LDS) and the fp32 tile goes through LDS for a 16-byte read-modify-write
@@ -113,8 +113,9 @@ __global__ __launch_bounds__(256) void correct_kernel(
     __shared__ __attribute__((aligned(16))) float sC[64 * LDC];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m = lane & 15, g = lane >> 4;
-    const int sg = blockIdx.x / groups, grp = blockIdx.x % groups;
-    const int e = blockIdx.y;
+    const int sg = blockIdx.y / groups, grp = blockIdx.y % groups;
+    const int e = blockIdx.x;                    // heads fastest: the rows of one token are
+                                                 // read by workgroups dispatched together
     if (sg % P == 0 && !S_init)
         return;                                  // a first segment started from zero
     const int start = seg_cu[sg], end = seg_cu[sg + 1];
@@ -124,9 +125,11 @@ __global__ __launch_bounds__(256) void correct_kernel(
     const int ntiles = min(kTPW, (end - t_first + 63) / 64);
     const float* Sp = sg % P == 0 ? S_init + ((int64_t)(sg / P) * H + e) * D * DV
                                   : S_in + ((int64_t)sg * H + e) * D * DV;
+    // consecutive lanes take consecutive rows k, so the transposed 2-byte LDS
+    // writes of a wavefront fall in consecutive banks
     for (int x = tid; x < D * DV / 4; x += 256) {
-        const int k = (x * 4) / DV, j = (x * 4) % DV;
-        const float4 v4 = reinterpret_cast<const float4*>(Sp)[x];
+        const int k = x % D, j = (x / D) * 4;
+        const float4 v4 = *reinterpret_cast<const float4*>(Sp + (int64_t)k * DV + j);
         sB[(j + 0) * LDB + k] = f32_to_bf16(v4.x);
         sB[(j + 1) * LDB + k] = f32_to_bf16(v4.y);
         sB[(j + 2) * LDB + k] = f32_to_bf16(v4.z);
@@ -300,7 +303,7 @@ hipError_t launch_split_scan(const ScanArgs& p, int P, void* ws, hipStream_t s)
         // no segment is longer than ceil(T / P / 64) chunks of 64 tokens
         const int tiles = (T + P * 64 - 1) / (P * 64);
         const int groups = (tiles + longseq::kTPW - 1) / longseq::kTPW;
-        const dim3 grid((unsigned)(segs * groups), (unsigned)H);
+        const dim3 grid((unsigned)H, (unsigned)(segs * groups));
 #define PRISM_CORRECT(DK_, DV_)                                                                   \
         hipLaunchKernelGGL((longseq::correct_kernel<DK_, DV_>), grid, dim3(256), 0, s, op, S_in,   \
                            p.s_init, seg_cu, P, groups, H, (uint16_t*)p.o)
