@@ -53,6 +53,7 @@ KERNEL_SOURCES = {
 DECODE_BATCHES = [
     ("recsys-serving-512x8", 512, 8, 64, 64, 8),
     ("lm-130m-serving-256x6", 256, 6, 128, 128, 4),
+    ("lm-130m-serving-8x6", 8, 6, 128, 128, 4),        # small batch: launch-latency bound
 ]
 
 
@@ -200,10 +201,35 @@ def decode_bench(steps, warmup):
         assert status == 0, binding.status_str(status)
         ms = sum(a.elapsed_time(b) for a, b in ev) / steps
         ach = nbytes / (ms * 1e-3) / 1e9
+        # the same steps replayed from a HIP graph (captured once; no launch
+        # overhead between steps): the per-step time a serving loop would see
+        G, R = 16, 4
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for i in range(G):
+                lib.prism_decode_step(*(args[i % ncopy][:-1] + [side.cuda_stream]))
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream().cuda_stream
+            for i in range(G):
+                lib.prism_decode_step(*(args[i % ncopy][:-1] + [cap]))
+        graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(R):
+            graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_us = g0.elapsed_time(g1) * 1e3 / (R * G)
         out[name] = {
             "sequences": n, "heads": H, "dk": dk, "dv": dv, "L": L, "dtype": "bf16",
             "tokens_per_s": steps * n / elapsed, "us_per_step": elapsed / steps * 1e6,
             "tokens_per_s_kernel": n / (ms * 1e-3),
+            "graph_us_per_step": graph_us, "tokens_per_s_graph": n / (graph_us * 1e-6),
             "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic("decode", name),
                          "kernel": "decode", "avg_launch_us": ms * 1e3,
