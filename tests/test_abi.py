@@ -182,3 +182,24 @@ def test_binding_checks_shapes_before_calling():
     with pytest.raises(ValueError):
         B.prologue(q, None, None, None, torch.zeros(4, 2, dtype=torch.bfloat16),
                    torch.zeros(2, 64, 4, dtype=torch.bfloat16), cu.to(torch.int64), 1)
+
+
+def test_scan_workspace_bytes_for_forced_split(lib, monkeypatch):
+    """With PRISM_SPLIT=P the scan workspace holds o' (bf16 [T, H, dk]), S_loc and
+    S_in (fp32 [n P, H, dk, dv]), M (fp32 [n P, H, dk, dk]) and the segment
+    offsets, each rounded up to 256 bytes; prism_workspace_bytes adds the write
+    keys.  Off (PRISM_SPLIT=0), and for fp32 inputs, it is zero."""
+    from gated_delta_rule_prologue_amd import binding as B
+    up = lambda x: (x + 255) // 256 * 256
+    n, T, H, dk, dv, P = 2, 1000, 3, 128, 64, 3
+    d = B.make_dims(n, T, H, dk, dv, B.PRISM_BF16)
+    monkeypatch.setenv("PRISM_SPLIT", str(P))
+    segs = n * P
+    want = (up(T * H * dk * 2) + 2 * up(segs * H * dk * dv * 4) + up(segs * H * dk * dk * 4)
+            + up((segs + 1) * 4))
+    assert B.scan_workspace_bytes(d) == want
+    assert B.workspace_bytes(d, 4) == up(T * H * dk * 2) + want
+    monkeypatch.setenv("PRISM_SPLIT", "0")
+    assert B.scan_workspace_bytes(d) == 0
+    monkeypatch.setenv("PRISM_SPLIT", str(P))
+    assert B.scan_workspace_bytes(B.make_dims(n, T, H, 64, 64, B.PRISM_F32)) == 0
