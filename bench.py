@@ -58,7 +58,7 @@ DECODE_BATCHES = [
 
 
 def algorithmic_work(w, n_seqs, T, esize):
-    """Algorithmic HBM bytes and MFMA flops of one step (see the design doc for the counts).
+    """Algorithmic HBM bytes and MFMA flops of one step.
 
     Per head-token (ht):
       prologue bytes = e [dk (k) + 2 (L-1) dk (u, a) + max(L-2, 0) dk (h slots read) + 1 (b) + dk (kw)]
@@ -255,7 +255,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+        print(f"bench.py: measures one GPU only (--gpus {args.gpus} requested); "
               "the operator's (sequence, head) chains shard across GPUs without communication, "
               "so the per-GPU figure is the one reported", file=sys.stderr)
         sys.exit(2)
