@@ -56,6 +56,9 @@ def _load():
         lib.prism_oracle_fwd.restype = ctypes.c_int
         lib.prism_oracle_k_history.argtypes = [ctypes.POINTER(_Dims), P, P, P, P]
         lib.prism_oracle_k_history.restype = ctypes.c_int
+        lib.prism_oracle_bwd.argtypes = [ctypes.POINTER(_Dims)] + [P] * 14 + [ctypes.c_int64] + \
+            [P] * 10 + [ctypes.c_int]
+        lib.prism_oracle_bwd.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -181,3 +184,36 @@ def decode_step(step, S, k_hist, threads: Optional[int] = None, residual: str = 
         raise ValueError("a decode step holds exactly one token per sequence")
     o, s = fwd(step, threads=threads, S_init=S, k_hist=k_hist, residual=residual)
     return o, s, k_history(step, k_hist)
+
+
+def bwd(inp, d_o, dS_final=None, S_init=None, chains: Optional[Sequence[int]] = None,
+        threads: Optional[int] = None):
+    """Backward pass (closed-form residual chain) for the loss
+    sum <d_o, o> + <dS_final, S_final>: a dict of float64 gradients for q, k,
+    v [T, H, d], u, a, h [T, H, L-1, dk] (L > 1), g, b [T, H], conv_w [H, dk, 4]
+    and S_init [n_seqs, H, dk, dv].  ``chains`` restricts the evaluation (rows of
+    other chains stay zero; conv_w sums over the listed chains only)."""
+    code, cu = _check(inp)
+    T, H, dk, dv, L = inp.total_tokens, inp.heads, inp.dk, inp.dv, inp.L
+    d_o = np.ascontiguousarray(d_o, dtype=np.float64)
+    if d_o.shape != (T, H, dv):
+        raise ValueError("d_o: expected [T, H, dv]")
+    dsf = None if dS_final is None else np.ascontiguousarray(dS_final, dtype=np.float64)
+    s0 = _state(inp, S_init)
+    out = {"q": np.zeros((T, H, dk)), "k": np.zeros((T, H, dk)), "v": np.zeros((T, H, dv)),
+           "g": np.zeros((T, H)), "b": np.zeros((T, H)), "conv_w": np.zeros((H, dk, 4)),
+           "S_init": np.zeros((inp.n_seqs, H, dk, dv))}
+    lv = (T, H, max(L - 1, 0), dk)
+    for n in ("u", "a", "h"):
+        out[n] = np.zeros(lv) if L > 1 else None
+    ch = None if chains is None else np.ascontiguousarray(np.asarray(chains, dtype=np.int64))
+    rc = _load().prism_oracle_bwd(
+        ctypes.byref(_dims(inp, code)), _ptr(cu), _ptr(inp.q), _ptr(inp.k), _ptr(inp.v),
+        _ptr(inp.u), _ptr(inp.g), _ptr(inp.b), _ptr(inp.a), _ptr(inp.h), _ptr(inp.conv_w),
+        _ptr(s0), _ptr(d_o), _ptr(dsf), _ptr(ch), 0 if ch is None else int(ch.size),
+        _ptr(out["q"]), _ptr(out["k"]), _ptr(out["v"]), _ptr(out["u"]), _ptr(out["g"]),
+        _ptr(out["b"]), _ptr(out["a"]), _ptr(out["h"]), _ptr(out["conv_w"]), _ptr(out["S_init"]),
+        threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"prism_oracle_bwd failed ({rc})")
+    return out

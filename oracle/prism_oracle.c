@@ -287,3 +287,214 @@ int prism_oracle_k_history(const oracle_dims* d, const int32_t* cu_seqlens, cons
                         k_at(d, k, k_hist, n, cu_seqlens[n], cu_seqlens[n + 1] - 3 + m, e, i);
     return 0;
 }
+
+/*
+ * Backward pass of the forward above (closed-form residual chain, L >= 1), for
+ * the loss  sum_t <do_t, o_t> + <dS_final, S_final>  of given upstream
+ * gradients.  Reverse-mode differentiation of the token recurrence, written
+ * out step by step:
+ *
+ *   G <- dS_final (or 0);  for t = last .. first of the sequence:
+ *     G     += q_t do_t^T                       (o_t = S_t^T q_t)
+ *     dq_t   = S_t do_t,  dv_t = G^T kw_t,  dkw_t = G v_t
+ *     P      = S_{t-1} - b_t k_t p^T,  p = S_{t-1}^T k_t
+ *     dg_t   = <G, P>,  dP = g_t G,  y = dP^T k_t
+ *     db_t  += -(y . p),  dk_t += -b_t (dP p + S_{t-1} y)
+ *     G      = dP - b_t k_t y^T                 (S_t = g_t P + kw_t v_t^T)
+ *   dS_init = G
+ *
+ * then through the write key kw_t = b_t k_t + sum_l a_l r_l u_l with
+ * r_{l+1} = r_l (1 - a_l h_l), r_1 = r_0 = sum_m w_m k_{t-3+m}: the residual
+ * chain in reverse (dr_l = dkw a_l u_l + dr_{l+1} (1 - a_l h_l)), then the
+ * convolution (dw_m += dr_0 k_{t-3+m}, dk_{t-3+m} += w_m dr_0 inside the
+ * sequence).  Taps that read a carried history contribute to no input
+ * gradient here.  All outputs are double; chains, when given, restrict the
+ * evaluation like prism_oracle_fwd (dconv_w then sums over those chains only).
+ * The per-chain states are kept in full, so this is for small inputs or a few
+ * chains.
+ */
+int prism_oracle_bwd(const oracle_dims* d, const int32_t* cu_seqlens,
+                     const void* q, const void* k, const void* v, const void* u,
+                     const void* g, const void* b, const void* a, const void* h,
+                     const void* conv_w, const double* s_init, const double* d_o,
+                     const double* d_sfinal, const int64_t* chains, int64_t n_chains,
+                     double* dq, double* dk, double* dv, double* du, double* dg, double* db,
+                     double* da, double* dh, double* dconv_w, double* ds_init, int nthreads)
+{
+    if (!d || !cu_seqlens || !q || !k || !v || !g || !b || !conv_w || !d_o || !dq || !dk ||
+        !dv || !dg || !db || !dconv_w || d->L < 1 || d->residual != ORACLE_RESIDUAL_LINEAR)
+        return 1;
+    if (d->L > 1 && (!u || !a || !h || !du || !da || !dh))
+        return 1;
+    const int64_t H = d->heads, dk_ = d->dk, dv_ = d->dv, dt = d->dtype, L = d->L;
+    const int64_t n_items = chains ? n_chains : d->n_seqs * H;
+    int status = 0;
+    (void)nthreads;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int64_t item = 0; item < n_items; ++item) {
+        const int64_t c = chains ? chains[item] : item;
+        const int64_t n = c / H, e = c % H;
+        const int64_t t0 = cu_seqlens[n], len = cu_seqlens[n + 1] - cu_seqlens[n];
+        const int64_t SZ = dk_ * dv_;
+        double* Ss = (double*)calloc((size_t)((len + 1) * SZ), sizeof(double));
+        double* kw = (double*)malloc((size_t)((len > 0 ? len : 1) * dk_) * sizeof(double));
+        double* dkw = (double*)calloc((size_t)((len > 0 ? len : 1) * dk_), sizeof(double));
+        double* G = (double*)calloc((size_t)SZ, sizeof(double));
+        double* P = (double*)malloc((size_t)SZ * sizeof(double));
+        double* p = (double*)malloc((size_t)dv_ * sizeof(double));
+        double* y = (double*)malloc((size_t)dv_ * sizeof(double));
+        double* r = (double*)malloc((size_t)(L > 1 ? L : 2) * sizeof(double));
+        double* dwc = (double*)calloc((size_t)(dk_ * 4), sizeof(double));
+        if (!Ss || !kw || !dkw || !G || !P || !p || !y || !r || !dwc) {
+#pragma omp atomic write
+            status = 2;
+            free(Ss); free(kw); free(dkw); free(G); free(P); free(p); free(y); free(r); free(dwc);
+            continue;
+        }
+        if (s_init)
+            memcpy(Ss, s_init + c * SZ, (size_t)SZ * sizeof(double));
+        /* forward: S_{t} at Ss[(t - t0 + 1) SZ] */
+        for (int64_t j = 0; j < len; ++j) {
+            const int64_t t = t0 + j;
+            write_key(d, k, u, a, h, b, conv_w, NULL, n, t0, t, e, kw + j * dk_);
+            const double gt = elem(g, dt, t * H + e), bt = elem(b, dt, t * H + e);
+            const double* S0 = Ss + j * SZ;
+            double* S1 = Ss + (j + 1) * SZ;
+            for (int64_t jj = 0; jj < dv_; ++jj) {
+                double acc = 0.0;
+                for (int64_t i = 0; i < dk_; ++i)
+                    acc += S0[i * dv_ + jj] * elem(k, dt, (t * H + e) * dk_ + i);
+                p[jj] = acc;
+            }
+            for (int64_t i = 0; i < dk_; ++i) {
+                const double ki = elem(k, dt, (t * H + e) * dk_ + i);
+                for (int64_t jj = 0; jj < dv_; ++jj)
+                    S1[i * dv_ + jj] = gt * (S0[i * dv_ + jj] - bt * ki * p[jj]) +
+                                       kw[j * dk_ + i] * elem(v, dt, (t * H + e) * dv_ + jj);
+            }
+        }
+        /* reverse through the state recurrence */
+        if (d_sfinal)
+            memcpy(G, d_sfinal + c * SZ, (size_t)SZ * sizeof(double));
+        for (int64_t j = len - 1; j >= 0; --j) {
+            const int64_t t = t0 + j;
+            const double gt = elem(g, dt, t * H + e), bt = elem(b, dt, t * H + e);
+            const double* Sm = Ss + j * SZ;           /* S_{t-1} */
+            const double* St = Ss + (j + 1) * SZ;     /* S_t */
+            const double* dot = d_o + (t * H + e) * dv_;
+            for (int64_t i = 0; i < dk_; ++i) {
+                const double qi = elem(q, dt, (t * H + e) * dk_ + i);
+                for (int64_t jj = 0; jj < dv_; ++jj)
+                    G[i * dv_ + jj] += qi * dot[jj];
+            }
+            for (int64_t i = 0; i < dk_; ++i) {
+                double aq = 0.0, aw = 0.0;
+                for (int64_t jj = 0; jj < dv_; ++jj) {
+                    aq += St[i * dv_ + jj] * dot[jj];
+                    aw += G[i * dv_ + jj] * elem(v, dt, (t * H + e) * dv_ + jj);
+                }
+                dq[(t * H + e) * dk_ + i] = aq;
+                dkw[j * dk_ + i] = aw;
+            }
+            for (int64_t jj = 0; jj < dv_; ++jj) {
+                double acc = 0.0, pk = 0.0;
+                for (int64_t i = 0; i < dk_; ++i) {
+                    acc += G[i * dv_ + jj] * kw[j * dk_ + i];
+                    pk += Sm[i * dv_ + jj] * elem(k, dt, (t * H + e) * dk_ + i);
+                }
+                dv[(t * H + e) * dv_ + jj] = acc;
+                p[jj] = pk;
+            }
+            double dgt = 0.0;
+            for (int64_t i = 0; i < dk_; ++i) {
+                const double ki = elem(k, dt, (t * H + e) * dk_ + i);
+                for (int64_t jj = 0; jj < dv_; ++jj) {
+                    P[i * dv_ + jj] = Sm[i * dv_ + jj] - bt * ki * p[jj];
+                    dgt += G[i * dv_ + jj] * P[i * dv_ + jj];
+                }
+            }
+            dg[t * H + e] = dgt;
+            /* dP = g G (in place), y = dP^T k */
+            for (int64_t x = 0; x < SZ; ++x)
+                G[x] *= gt;
+            for (int64_t jj = 0; jj < dv_; ++jj) {
+                double acc = 0.0;
+                for (int64_t i = 0; i < dk_; ++i)
+                    acc += G[i * dv_ + jj] * elem(k, dt, (t * H + e) * dk_ + i);
+                y[jj] = acc;
+            }
+            double yp = 0.0;
+            for (int64_t jj = 0; jj < dv_; ++jj)
+                yp += y[jj] * p[jj];
+            db[t * H + e] = -yp;
+            for (int64_t i = 0; i < dk_; ++i) {
+                double a1 = 0.0, a2 = 0.0;
+                for (int64_t jj = 0; jj < dv_; ++jj) {
+                    a1 += G[i * dv_ + jj] * p[jj];
+                    a2 += Sm[i * dv_ + jj] * y[jj];
+                }
+                dk[(t * H + e) * dk_ + i] = -bt * (a1 + a2);
+            }
+            for (int64_t i = 0; i < dk_; ++i) {
+                const double ki = elem(k, dt, (t * H + e) * dk_ + i);
+                for (int64_t jj = 0; jj < dv_; ++jj)
+                    G[i * dv_ + jj] -= bt * ki * y[jj];
+            }
+        }
+        if (ds_init)
+            memcpy(ds_init + c * SZ, G, (size_t)SZ * sizeof(double));
+        /* through the write key, token by token (the conv spreads over 4 tokens,
+         * so dk of earlier tokens is accumulated here after their own rows) */
+        for (int64_t j = 0; j < len; ++j) {
+            const int64_t t = t0 + j;
+            const double bt = elem(b, dt, t * H + e);
+            for (int64_t i = 0; i < dk_; ++i) {
+                const double kt = elem(k, dt, (t * H + e) * dk_ + i);
+                const double dkwi = dkw[j * dk_ + i];
+                db[t * H + e] += dkwi * kt;
+                dk[(t * H + e) * dk_ + i] += bt * dkwi;
+                if (L == 1)
+                    continue;
+                double r0 = 0.0;
+                for (int64_t m = 0; m < 4; ++m)
+                    r0 += elem(conv_w, dt, (e * dk_ + i) * 4 + m) *
+                          k_at(d, k, NULL, n, t0, t - 3 + m, e, i);
+                /* r[l] for l = 1 .. L-1 */
+                r[1] = r0;
+                for (int64_t l = 1; l < L - 1; ++l) {
+                    const int64_t sl = ((t * H + e) * (L - 1) + (l - 1)) * dk_ + i;
+                    r[l + 1] = r[l] * (1.0 - elem(a, dt, sl) * elem(h, dt, sl));
+                }
+                double dr_next = 0.0;                  /* dr_{l+1} */
+                for (int64_t l = L - 1; l >= 1; --l) {
+                    const int64_t sl = ((t * H + e) * (L - 1) + (l - 1)) * dk_ + i;
+                    const double al = elem(a, dt, sl), ul = elem(u, dt, sl), hl = elem(h, dt, sl);
+                    du[sl] = dkwi * al * r[l];
+                    double dal = dkwi * ul * r[l];
+                    double dhl = 0.0, drl = dkwi * al * ul;
+                    if (l <= L - 2) {
+                        dal -= dr_next * hl * r[l];
+                        dhl = -dr_next * al * r[l];
+                        drl += dr_next * (1.0 - al * hl);
+                    }
+                    da[sl] = dal;
+                    dh[sl] = dhl;
+                    dr_next = drl;
+                }
+                /* dr_next is now dr_1 = dr_0 */
+                for (int64_t m = 0; m < 4; ++m) {
+                    const int64_t tau = t - 3 + m;
+                    if (tau < t0)
+                        continue;
+                    dwc[i * 4 + m] += dr_next * elem(k, dt, (tau * H + e) * dk_ + i);
+                    dk[(tau * H + e) * dk_ + i] += elem(conv_w, dt, (e * dk_ + i) * 4 + m) * dr_next;
+                }
+            }
+        }
+#pragma omp critical
+        for (int64_t x = 0; x < dk_ * 4; ++x)
+            dconv_w[e * dk_ * 4 + x] += dwc[x];
+        free(Ss); free(kw); free(dkw); free(G); free(P); free(p); free(y); free(r); free(dwc);
+    }
+    return status;
+}
