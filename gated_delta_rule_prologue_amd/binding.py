@@ -8,7 +8,7 @@ Names follow the C ABI: ``fwd`` -> prism_fwd, ``fwd_resume`` ->
 prism_fwd_resume, ``decode_step`` -> prism_decode_step, ``prologue`` ->
 prism_prologue, ``prologue_ex`` -> prism_prologue_ex, ``scan`` -> prism_scan,
 ``scan_ex`` -> prism_scan_ex, ``workspace_bytes`` -> prism_workspace_bytes,
-``scan_workspace_bytes`` -> prism_scan_workspace_bytes.
+``scan_workspace_bytes`` -> prism_scan_workspace_bytes, ``bwd`` -> prism_bwd.
 """
 from __future__ import annotations
 
@@ -70,6 +70,10 @@ def lib():
         L.prism_fwd_resume.argtypes = [D, P, P, P, P, P, P, P, P, P, P, I, I, P, P, P, P, P, P, S, P]
         L.prism_fwd_resume.restype = I
         L.prism_decode_step.argtypes = [D, P, P, P, P, P, P, P, P, P, I, I, P, P, P, P]
+        L.prism_bwd_workspace_bytes.argtypes = [D, I]
+        L.prism_bwd_workspace_bytes.restype = S
+        L.prism_bwd.argtypes = [D] + [P] * 10 + [I] + [P] * 14 + [S, P]
+        L.prism_bwd.restype = I
         L.prism_decode_step.restype = I
         L.prism_status_str.argtypes = [I]
         L.prism_status_str.restype = ctypes.c_char_p
@@ -319,6 +323,40 @@ def decode_step(q, k, v, u, g, b, a, h, conv_w, L: int, S, k_hist, o=None, strea
         ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(g), _ptr(b), _ptr(a), _ptr(h),
         _ptr(conv_w), int(L), RESIDUAL[residual], _ptr(S), _ptr(k_hist), _ptr(o), _stream(stream)))
     return o
+
+
+def bwd(q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L: int, dO, dS_final=None, S_init=None,
+        want_dS_init: bool = True, workspace=None, stream=None) -> dict:
+    """Gradients of sum <dO, o> + <dS_final, S_final> (prism_bwd, closed-form
+    residual chain): a dict of fp32 tensors q, k, v, u, a, h, g, b, conv_w and
+    S_init (the last when ``want_dS_init``)."""
+    d = _dims_of(q, v, cu_seqlens)
+    _check_write_branch(d, q.dtype, k, u, a, h, b, conv_w, L)
+    _check_scan(d, q.dtype, q, k, k, v, g, b)
+    _expect("dO", dO, v.shape, v.dtype)
+    n, T, H, dk, dv = d.n_seqs, d.total_tokens, d.heads, d.dk, d.dv
+    for name, x in (("dS_final", dS_final), ("S_init", S_init)):
+        if x is not None:
+            _expect(name, x, (n, H, dk, dv), torch.float32)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    out = {"q": torch.empty((T, H, dk), **f32), "k": torch.empty((T, H, dk), **f32),
+           "v": torch.empty((T, H, dv), **f32), "g": torch.empty((T, H), **f32),
+           "b": torch.empty((T, H), **f32), "conv_w": torch.empty((H, dk, 4), **f32),
+           "S_init": torch.empty((n, H, dk, dv), **f32) if want_dS_init else None}
+    for name in ("u", "a", "h"):
+        out[name] = torch.empty((T, H, L - 1, dk), **f32) if L > 1 else None
+    need = int(lib().prism_bwd_workspace_bytes(ctypes.byref(d), int(L)))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    _check("prism_bwd", lib().prism_bwd(
+        ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(g), _ptr(b), _ptr(a), _ptr(h),
+        _ptr(conv_w), _ptr(cu_seqlens), int(L), _ptr(S_init), _ptr(dO), _ptr(dS_final),
+        _ptr(out["q"]), _ptr(out["k"]), _ptr(out["v"]), _ptr(out["u"]), _ptr(out["g"]),
+        _ptr(out["b"]), _ptr(out["a"]), _ptr(out["h"]), _ptr(out["conv_w"]), _ptr(out["S_init"]),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
 
 
 def to_device(inp, device="cuda") -> dict:

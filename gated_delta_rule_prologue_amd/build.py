@@ -24,7 +24,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libprism.so")
 SOURCES = ["prism_api.hip", "prologue.hip", "prologue_bf16.hip", "prologue_f32.hip",
            "prologue_bf16_ext.hip", "prologue_f32_ext.hip", "chunk_scan.hip",
-           "chunk_scan_bf16.hip", "decode.hip", "long_seq.hip"]
+           "chunk_scan_bf16.hip", "decode.hip", "long_seq.hip", "backward.hip"]
 CHECKED = ["chunk_scan_bf16.hip", "chunk_scan.hip"]      # sources with mixed-size MFMA chains
 ARCH = "gfx950"
 

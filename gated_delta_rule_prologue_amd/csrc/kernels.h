@@ -57,6 +57,23 @@ int split_segments(int n_seqs, int heads, int dk, int dv, int total_tokens, int 
 size_t split_workspace_bytes(int n_seqs, int heads, int dk, int dv, int total_tokens, int P);
 hipError_t launch_split_scan(const ScanArgs& p, int P, void* ws, hipStream_t stream);
 
+// Backward pass (closed-form residual chain): fp32 gradients of the loss
+// sum <dO, o> + <dS_final, S_final>; kw from the prologue (input dtype).
+struct BwdArgs {
+    bool bf16;
+    int n_seqs, total_tokens, heads, dk, dv, L;
+    const void *q, *k, *v, *kw, *u, *a, *h, *g, *b, *conv_w, *dO;
+    const int32_t* cu_seqlens;
+    const float* s_init;            // or null (zero)
+    const float* ds_final;          // or null (zero)
+    float *gq, *gk, *gv, *gu, *ga, *gh, *gg, *gb, *gconv;
+    float* gs_init;                 // or null (not written)
+    float* ws;                      // bwd_workspace_floats(...) floats
+};
+size_t bwd_workspace_floats(int n_seqs, int total_tokens, int heads, int dk, int dv);
+bool bwd_supported(int dk, int dv);
+hipError_t launch_bwd(const BwdArgs& p, hipStream_t stream);
+
 // One token per sequence through the recurrence (state and history in place).
 hipError_t launch_decode(const DecodeArgs& p, hipStream_t stream);
 bool decode_supported(int dk, int dv);

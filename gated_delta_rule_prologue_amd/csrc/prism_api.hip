@@ -324,6 +324,60 @@ prism_status prism_fwd_resume(const prism_dims* d, const void* q, const void* k,
                     S_final, k_hist_out, workspace, workspace_bytes, stream);
 }
 
+size_t prism_bwd_workspace_bytes(const prism_dims* d, int L)
+{
+    if (!dims_ok(d) || L < 1 || L > PRISM_MAX_LEVELS)
+        return 0;
+    return kw_bytes(d) + prism::bwd_workspace_floats(d->n_seqs, d->total_tokens, d->heads, d->dk,
+                                                     d->dv) * sizeof(float);
+}
+
+prism_status prism_bwd(const prism_dims* d, const void* q, const void* k, const void* v,
+                       const void* u, const void* g, const void* b, const void* a, const void* h,
+                       const void* conv_w, const int32_t* cu_seqlens, int L, const float* S_init,
+                       const void* dO, const float* dS_final, float* dq, float* dk, float* dv,
+                       float* du, float* dg, float* db, float* da, float* dh, float* dconv_w,
+                       float* dS_init, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!dims_ok(d) || L < 1 || L > PRISM_MAX_LEVELS)
+        return PRISM_EINVAL;
+    if (!tok_ok(d, q) || !tok_ok(d, k) || !tok_ok(d, v) || !tok_ok(d, g) || !tok_ok(d, b) ||
+        !tok_ok(d, dO) || !ptr_ok(conv_w) || !ptr_ok(cu_seqlens) || !tok_ok(d, dq) ||
+        !tok_ok(d, dk) || !tok_ok(d, dv) || !tok_ok(d, dg) || !tok_ok(d, db) || !ptr_ok(dconv_w) ||
+        !ptr_ok(workspace) || !opt_ok(S_init) || !opt_ok(dS_final) || !opt_ok(dS_init))
+        return PRISM_EINVAL;
+    if (L > 1 && (!tok_ok(d, u) || !tok_ok(d, a) || !tok_ok(d, h) || !tok_ok(d, du) ||
+                  !tok_ok(d, da) || !tok_ok(d, dh)))
+        return PRISM_EINVAL;
+    if (!prism::bwd_supported(d->dk, d->dv))
+        return PRISM_EUNSUPPORTED;
+    if (workspace_bytes < prism_bwd_workspace_bytes(d, L))
+        return PRISM_EINVAL;
+    prism_status st = prologue_impl(d, k, u, a, h, b, conv_w, nullptr, cu_seqlens, L,
+                                    PRISM_RESIDUAL_LINEAR, workspace, stream);
+    if (st != PRISM_OK)
+        return st;
+    prism::BwdArgs p;
+    p.bf16 = d->dtype == PRISM_BF16;
+    p.n_seqs = d->n_seqs;
+    p.total_tokens = d->total_tokens;
+    p.heads = d->heads;
+    p.dk = d->dk;
+    p.dv = d->dv;
+    p.L = L;
+    p.q = q; p.k = k; p.v = v; p.kw = workspace; p.u = u; p.a = a; p.h = h; p.g = g; p.b = b;
+    p.conv_w = conv_w;
+    p.dO = dO;
+    p.cu_seqlens = cu_seqlens;
+    p.s_init = S_init;
+    p.ds_final = dS_final;
+    p.gq = dq; p.gk = dk; p.gv = dv; p.gu = du; p.ga = da; p.gh = dh; p.gg = dg; p.gb = db;
+    p.gconv = dconv_w;
+    p.gs_init = dS_init;
+    p.ws = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + kw_bytes(d));
+    return from_hip(prism::launch_bwd(p, (hipStream_t)stream));
+}
+
 prism_status prism_decode_step(const prism_dims* d, const void* q, const void* k, const void* v,
                                const void* u, const void* g, const void* b, const void* a,
                                const void* h, const void* conv_w, int L, int residual, float* S,

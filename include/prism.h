@@ -245,6 +245,38 @@ prism_status prism_scan_ex(const prism_dims* d,
  * invalid dims. */
 size_t prism_scan_workspace_bytes(const prism_dims* d);
 
+/*
+ * Backward pass of prism_fwd with the closed-form residual chain: the fp32
+ * gradients of the loss  sum_t <dO_t, o_t> + <dS_final, S_final>  with respect
+ * to every input, by reverse-mode differentiation of the token recurrence
+ * (WeChat page sections 核心迭代形式, 消除 Token 间串行, 消除 Step 间串行;
+ * gist.science section 2.1).  The write keys are recomputed by the prologue;
+ * the scan is walked backwards from chunk-start checkpoints, token by token.
+ *
+ *   inputs as in prism_fwd; S_init as in prism_fwd_resume (NULL = zero)
+ *   dO          [T, H, dv], input dtype
+ *   dS_final    fp32 [n_seqs, H, dk, dv] or NULL (zero)
+ *   dq, dk      out fp32 [T, H, dk]          dv  out fp32 [T, H, dv]
+ *   du, da, dh  out fp32 [T, H, L-1, dk] (NULL allowed iff L == 1; h's last
+ *               slot, which the forward never reads, gets zero)
+ *   dg, db      out fp32 [T, H]              dconv_w  out fp32 [H, dk, 4]
+ *   dS_init     out fp32 [n_seqs, H, dk, dv] or NULL (not written)
+ *   workspace   prism_bwd_workspace_bytes(d, L) bytes
+ * dk, dv in {64, 128}, else PRISM_EUNSUPPORTED.  Gradients accumulated over
+ * value slices and tokens use fp32 atomics, so the last bits may differ from
+ * run to run.
+ */
+size_t prism_bwd_workspace_bytes(const prism_dims* d, int L);
+prism_status prism_bwd(const prism_dims* d,
+                       const void* q, const void* k, const void* v,
+                       const void* u, const void* g, const void* b,
+                       const void* a, const void* h, const void* conv_w,
+                       const int32_t* cu_seqlens, int L, const float* S_init,
+                       const void* dO, const float* dS_final,
+                       float* dq, float* dk, float* dv, float* du, float* dg, float* db,
+                       float* da, float* dh, float* dconv_w, float* dS_init,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* prism_status_str(prism_status s);
 

@@ -28,7 +28,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("prism_fwd", "prism_prologue", "prism_scan", "prism_workspace_bytes",
               "prism_status_str", "prism_abi_version", "prism_fwd_resume", "prism_decode_step",
-              "prism_prologue_ex", "prism_scan_ex", "prism_scan_workspace_bytes"):
+              "prism_prologue_ex", "prism_scan_ex", "prism_scan_workspace_bytes", "prism_bwd",
+              "prism_bwd_workspace_bytes"):
         assert n in names
 
 
