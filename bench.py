@@ -17,8 +17,9 @@ cores; its outputs double as a parity check of the last timed step.
 The line also carries a "decode" object: the single-token decode step
 (prism_decode_step, state and convolution history carried in place) timed
 on serving batches shaped like the recommendation and language-model layers,
-each against its HBM roofline.  It is measured after the forward pass and is
-not part of "value".
+each against its HBM roofline, and a "backward" object: prism_bwd (the
+gradients of every input for an upstream dO) on the same workload.  Both are
+measured after the forward pass and are not part of "value".
 """
 from __future__ import annotations
 
@@ -239,6 +240,64 @@ def decode_bench(steps, warmup):
     return out
 
 
+def bwd_bytes(w, n_seqs, T, esize):
+    """Algorithmic HBM bytes of one backward pass: the inputs read (q, k, v,
+    u, a, h slots read, g, b, conv taps and dO, input dtype) and every gradient
+    written once (fp32), per head-token, plus dS_init (fp32) per chain."""
+    H, dk, dv, L = w.heads, w.dk, w.dv, w.L
+    ht = T * H
+    reads = esize * (2 * dk + dv + 2 * (L - 1) * dk + max(L - 2, 0) * dk + 2 + dv)
+    writes = 4 * (2 * dk + dv + 3 * (L - 1) * dk + 2)
+    return ht * (reads + writes) + 4 * n_seqs * H * dk * dv + H * dk * 4 * (esize + 4)
+
+
+def bwd_bench(w, inp, dev_copies, steps, warmup):
+    """Time prism_bwd (gradients of every input) on the workload, with the
+    upstream gradient dO and no carried state."""
+    import ctypes
+    import torch
+    from gated_delta_rule_prologue_amd import binding
+    stream = torch.cuda.current_stream()
+    esize = 2 if w.dtype == "bf16" else 4
+    T, H = inp.total_tokens, inp.heads
+    dims = binding.Dims(inp.n_seqs, T, H, w.dk, w.dv, binding.PRISM_BF16 if esize == 2 else 0)
+    lib = binding.lib()
+    need = int(lib.prism_bwd_workspace_bytes(ctypes.byref(dims), w.L))
+    args = []
+    for c in dev_copies:
+        g = torch.Generator(device="cuda").manual_seed(7)
+        c["dO"] = torch.randn(c["v"].shape, device="cuda", generator=g).to(c["v"].dtype)
+        out = binding.bwd(c["q"], c["k"], c["v"], c["u"], c["g"], c["b"], c["a"], c["h"],
+                          c["conv_w"], c["cu_seqlens"], w.L, c["dO"], want_dS_init=True)
+        c["grads"] = out
+        c["bws"] = torch.empty(need, dtype=torch.uint8, device="cuda")
+        args.append([ctypes.byref(dims)] + raw_args(
+            c["q"], c["k"], c["v"], c["u"], c["g"], c["b"], c["a"], c["h"], c["conv_w"],
+            c["cu_seqlens"], w.L, None, c["dO"], None, out["q"], out["k"], out["v"], out["u"],
+            out["g"], out["b"], out["a"], out["h"], out["conv_w"], out["S_init"], c["bws"], need,
+            stream.cuda_stream))
+    for i in range(warmup):
+        lib.prism_bwd(*args[i % len(args)])
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    status = 0
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        status |= lib.prism_bwd(*args[i % len(args)])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    assert status == 0, binding.status_str(status)
+    ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    nbytes = bwd_bytes(w, inp.n_seqs, T, esize)
+    ach = nbytes / (ms * 1e-3) / 1e9
+    return {"tokens_per_s": steps * T / elapsed, "us_per_call": ms * 1e3,
+            "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": "backward (all launches)",
+                         "avg_launch_us": ms * 1e3, "algorithmic_bytes": nbytes}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -248,6 +307,7 @@ def main():
     ap.add_argument("--copies", type=int, default=3, help="input copies rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode steps (profiling runs); prints their JSON object")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -383,6 +443,8 @@ def main():
                     / 1e9 / ((pro_ms + scan_ms) * 1e-3)},
     }
     out["roofline"]["kernel"] = dominant["kernel"]
+    if not args.no_backward:
+        out["backward"] = bwd_bench(w, inp, copies[:2], max(5, K // 5), 2)
     if not args.no_decode:
         out["decode"] = decode_bench(max(20, K), max(5, args.warmup))
     # last copy kernels of the run: the reference for the counter calibration

@@ -25,7 +25,7 @@ LIB = os.path.join(PKG, "libprism.so")
 SOURCES = ["prism_api.hip", "prologue.hip", "prologue_bf16.hip", "prologue_f32.hip",
            "prologue_bf16_ext.hip", "prologue_f32_ext.hip", "chunk_scan.hip",
            "chunk_scan_bf16.hip", "decode.hip", "long_seq.hip", "backward.hip"]
-CHECKED = ["chunk_scan_bf16.hip", "chunk_scan.hip"]      # sources with mixed-size MFMA chains
+CHECKED = ["chunk_scan_bf16.hip", "chunk_scan.hip", "backward.hip"]   # MFMA chains, DPP
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -11,15 +11,16 @@
 // and dS_init = G at the sequence start; then the write key backwards through
 // the residual chain and the ShortConv taps.
 //
-// Design: correct first, a plain token-by-token form (the chunkwise form of
-// the forward is the faster route; see the forward scan for its algebra).
-//   * scan_bwd_kernel: one 256-thread workgroup per (sequence, head, 32 value
-//     columns); thread (rg, cg) holds rows rg + 32 r, columns 4 cg .. 4 cg + 3
-//     of S and G in registers.  A first sweep stores S at every chunk start
-//     (64 tokens); then, chunk by chunk from the last, the chunk's states are
-//     recomputed into a per-workgroup scratch and the chunk is walked
-//     backwards.  Column sums (over the dk rows) go through LDS; row sums (over
-//     the 32 columns) through lane shuffles, then fp32 atomics into dq, dk and
+// Design: a token-by-token form (the chunkwise form of the forward is the
+// faster route; see the forward scan for its algebra).
+//   * scan_bwd_kernel: one wavefront per (sequence, head, 8 value columns).
+//     The columns of S and G evolve independently, so all column sums stay
+//     in the wavefront (DPP and row swaps, no LDS barrier on the recurrence).
+//     A first sweep stores S every 8 tokens (16 at dk = 64); then, sub-chunk
+//     by sub-chunk from the last, the sub-chunk's states are recomputed into
+//     registers from its checkpoint and walked backwards.  A sub-chunk's
+//     inputs are fetched one sub-chunk ahead with 16-byte loads and staged in
+//     LDS.  Row sums (over the 8 columns) go to fp32 atomics into dq, dk and
 //     dkw, which the value slices of a chain share.
 //   * write_key_bwd_kernel: one thread per (head, channel, block of 64 tokens):
 //     the residual chain backwards (du, da, dh written, dr_0 formed), b and
@@ -30,288 +31,336 @@
 namespace prism {
 namespace bwd {
 
-constexpr int kC = 64;                           // chunk of the checkpoint sweep
-constexpr int kCols = 32;                        // value columns per workgroup
+constexpr int kC = 64;                           // token block of the write-key backward
+constexpr int kCols = 8;                         // value columns per wavefront of the scan backward
 
-// checkpoint slot of the chunk starting at token s of sequence n (unique, < T/64 + n_seqs + 1)
-__device__ __forceinline__ int64_t ckpt_slot(int s, int n) { return (int64_t)(s / kC) + n; }
+// tokens per checkpoint of the scan backward: one sub-chunk's states stay in
+// registers (8 x 16 per lane at dk = 128, 16 x 8 at dk = 64)
+__host__ __device__ constexpr int sub_len(int dk) { return dk == 128 ? 8 : 16; }
+
+// checkpoint slot of the sub-chunk starting at token s of sequence n (unique, < T/SUB + n_seqs + 1)
+template <int SUB>
+__device__ __forceinline__ int64_t ckpt_slot(int s, int n) { return (int64_t)(s / SUB) + n; }
 
 template <typename T>
 __device__ __forceinline__ float ld(const T* p, int64_t i) { return to_f32(p[i]); }
 
-// Sum over the lanes of a wavefront that share lane % 8 (the eight row groups
-// of one column group in a wavefront).
-__device__ __forceinline__ float sum_rows8(float x)
+// Cross-lane sums without LDS: DPP quad permutations and row rotations within
+// rows of 16 lanes, and the gfx950 row swaps (v_permlane16_swap exchanges the
+// odd rows of one operand with the even rows of the other, v_permlane32_swap
+// the halves) across rows; each step adds a lane's partner to it.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
 {
-    x += __shfl_xor(x, 8);
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
 }
-// Sum over the eight consecutive lanes of one row group (its 8 column groups).
-__device__ __forceinline__ float sum_cols8(float x)
+__device__ __forceinline__ float add_xor16(float x)
 {
-    x += __shfl_xor(x, 1);
-    x += __shfl_xor(x, 2);
-    x += __shfl_xor(x, 4);
-    return x;
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor32(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// sum over the four lanes of a quad (lane bits 0-1: the column pairs)
+__device__ __forceinline__ float sum_quad(float x)
+{
+    x += dpp<0xB1>(x);                           // quad_perm [1,0,3,2]
+    return x + dpp<0x4E>(x);                     // quad_perm [2,3,0,1]
+}
+// sum over the sixteen lanes that share lane % 4 (lane bits 2-5: the row groups)
+__device__ __forceinline__ float sum_rowgroups(float x)
+{
+    x += dpp<0x124>(x);                          // row_ror:4
+    x += dpp<0x128>(x);                          // row_ror:8
+    return add_xor32(add_xor16(x));
 }
 
+// One wavefront per (sequence n, head e, 8 value columns).  The columns of S
+// and of G evolve independently, so every column sum stays inside the
+// wavefront.  Lane (rg, cp) = (lane >> 2, lane & 3) holds rows rg + 16 r and
+// the two columns 2 cp, 2 cp + 1 of the slice.
 template <typename T, int DK>
-__global__ __launch_bounds__(256) void scan_bwd_kernel(
+__global__ __launch_bounds__(64) void scan_bwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ kw,
     const T* __restrict__ v, const T* __restrict__ g, const T* __restrict__ b,
     const T* __restrict__ dO, const int32_t* __restrict__ cu, int H, int DV,
     const float* __restrict__ S_init, const float* __restrict__ dS_final,
-    float* __restrict__ ckpt, float* __restrict__ scr,
+    float* __restrict__ ckpt,
     float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dkw,
     float* __restrict__ dv, float* __restrict__ dg, float* __restrict__ db,
     float* __restrict__ dS_init)
 {
-    constexpr int RPT = DK / 32;                 // rows per thread
-    constexpr int EL = RPT * 4;                  // state elements per thread
-    __shared__ float red[2][4][3][kCols];        // per wavefront column partials, double-buffered
-    __shared__ float redg[2][4];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int cg = tid & 7, rg = tid >> 3;       // column group, row group (0..31)
+    constexpr int RPT = DK / 16;                 // rows per lane
+    constexpr int EL = 2 * RPT;                  // state elements per lane
+    constexpr int SUB = sub_len(DK);
+    constexpr int VE = 16 / (int)sizeof(T);      // elements per 16-byte vector
+    constexpr int KV = SUB * DK / VE;            // 16-byte vectors of one [SUB, DK] tile
+    constexpr int KPL = KV / 64;                 // ... per lane
+    constexpr int VPT = kCols / VE;              // 16-byte vectors of one token's 8 columns
+    constexpr int VV = SUB * VPT;                // ... of a sub-chunk
+    static_assert(KV % 64 == 0 && 2 * VV <= 64, "staging layout");
+    __shared__ uint4 sK[KV], sW[KV], sQ[KV], sV[VV], sD[VV];
+    __shared__ float sG[SUB], sB[SUB];
+
+    const int lane = threadIdx.x;
+    const int cp = lane & 3, rg = lane >> 2;
     const int slices = DV / kCols;
     const int slice = blockIdx.x % slices;
     const int chain = blockIdx.x / slices;
     const int n = chain / H, e = chain % H;
-    const int j0 = slice * kCols + cg * 4;       // first of this thread's 4 columns
+    const int j0 = slice * kCols + cp * 2;       // first of this lane's 2 columns
     const int seq0 = cu[n], seq1 = cu[n + 1];
-    const int64_t wg = blockIdx.x;
-    // this thread's elements of a dk x 32 slice, stored thread-major in scratch
-    const int64_t SL = (int64_t)DK * kCols;
-    auto st_idx = [&](int r, int c) { return (int64_t)(r * 4 + c) * 256 + tid; };
+    const int nsub = (seq1 - seq0 + SUB - 1) / SUB;
 
     float S[EL], G[EL];
     const int64_t sbase = ((int64_t)chain * DK) * DV;    // [n, e] block of S_init / dS_final
 #pragma unroll
     for (int r = 0; r < RPT; ++r)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int64_t x = sbase + (int64_t)(rg + 32 * r) * DV + j0 + c;
-            S[r * 4 + c] = S_init ? S_init[x] : 0.f;
-            G[r * 4 + c] = dS_final ? dS_final[x] : 0.f;
+        for (int c = 0; c < 2; ++c) {
+            const int64_t x = sbase + (int64_t)(rg + 16 * r) * DV + j0 + c;
+            S[r * 2 + c] = S_init ? S_init[x] : 0.f;
+            G[r * 2 + c] = dS_final ? dS_final[x] : 0.f;
         }
-    int buf = 0;
-    // column sums of up to three vectors of this thread's 4 columns over the dk rows
-    auto colsum = [&](float (&x)[3][4], int nv, float gpart, float& gsum) {
-#pragma unroll
-        for (int vv = 0; vv < 3; ++vv)
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-                if (vv < nv)
-                    x[vv][c] = sum_rows8(x[vv][c]);
-        float gw = gpart;
-        for (int o = 32; o > 0; o >>= 1)
-            gw += __shfl_xor(gw, o);
-        if (lane < 8) {
-#pragma unroll
-            for (int vv = 0; vv < 3; ++vv)
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    if (vv < nv)
-                        red[buf][wave][vv][cg * 4 + c] = x[vv][c];
-        }
-        if (lane == 0)
-            redg[buf][wave] = gw;
-        __syncthreads();
-#pragma unroll
-        for (int vv = 0; vv < 3; ++vv)
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-                if (vv < nv)
-                    x[vv][c] = red[buf][0][vv][cg * 4 + c] + red[buf][1][vv][cg * 4 + c] +
-                               red[buf][2][vv][cg * 4 + c] + red[buf][3][vv][cg * 4 + c];
-        gsum = redg[buf][0] + redg[buf][1] + redg[buf][2] + redg[buf][3];
-        buf ^= 1;
+    auto ckpt_at = [&](int s) {
+        return ckpt + ((ckpt_slot<SUB>(s, n) * H + e) * slices + slice) * (int64_t)(EL * 64) + lane;
     };
-    // one forward token: S <- g (S - b k p^T) + kw v^T
-    auto step_fwd = [&](int t) {
-        const int64_t rk = ((int64_t)t * H + e) * DK, rv = ((int64_t)t * H + e) * DV + j0;
-        float kk[RPT], ww[RPT], vv4[4];
+
+    // ---- a sub-chunk's inputs, loaded a sub-chunk ahead into registers, then staged in LDS
+    struct Pre {
+        uint4 k[KPL], w[KPL], q[KPL], vd;
+        float gb;
+    };
+    auto pre_load = [&](int c, bool back, Pre& P) {
+        const int last = seq1 - 1;               // tokens past the sequence end read its last one
+#pragma unroll
+        for (int x = 0; x < KPL; ++x) {
+            const int idx = lane + 64 * x;
+            const int t = min(c + idx / (DK / VE), last);
+            const int64_t o = ((int64_t)t * H + e) * DK / VE + idx % (DK / VE);
+            P.k[x] = reinterpret_cast<const uint4*>(k)[o];
+            P.w[x] = reinterpret_cast<const uint4*>(kw)[o];
+            if (back)
+                P.q[x] = reinterpret_cast<const uint4*>(q)[o];
+        }
+        const int vl = lane < VV ? lane : lane - VV;
+        const int t = min(c + vl / VPT, last);
+        const int64_t ov = (((int64_t)t * H + e) * DV + slice * kCols) / VE + vl % VPT;
+        P.vd = make_uint4(0u, 0u, 0u, 0u);
+        if (lane < VV)
+            P.vd = reinterpret_cast<const uint4*>(v)[ov];
+        else if (back && lane < 2 * VV)
+            P.vd = reinterpret_cast<const uint4*>(dO)[ov];
+        const int tg = min(c + (lane % SUB), last);
+        P.gb = lane < 2 * SUB ? ld(lane < SUB ? g : b, (int64_t)tg * H + e) : 0.f;
+    };
+    auto pre_store = [&](const Pre& P, bool back) {
+#pragma unroll
+        for (int x = 0; x < KPL; ++x) {
+            sK[lane + 64 * x] = P.k[x];
+            sW[lane + 64 * x] = P.w[x];
+            if (back)
+                sQ[lane + 64 * x] = P.q[x];
+        }
+        if (lane < VV)
+            sV[lane] = P.vd;
+        else if (back && lane < 2 * VV)
+            sD[lane - VV] = P.vd;
+        if (lane < SUB)
+            sG[lane] = P.gb;
+        else if (lane < 2 * SUB)
+            sB[lane - SUB] = P.gb;
+    };
+    auto at = [](const uint4* base, int i) { return to_f32(reinterpret_cast<const T*>(base)[i]); };
+
+    // ---- forward token j of the staged sub-chunk: S <- g (S - b k p^T) + kw v^T
+    auto fapply = [&](int j) {
+        float kk[RPT], ww[RPT], vv[2];
 #pragma unroll
         for (int r = 0; r < RPT; ++r) {
-            kk[r] = ld(k, rk + rg + 32 * r);
-            ww[r] = ld(kw, rk + rg + 32 * r);
+            kk[r] = at(sK, j * DK + rg + 16 * r);
+            ww[r] = at(sW, j * DK + rg + 16 * r);
         }
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-            vv4[c] = ld(v, rv + c);
-        const float gt = ld(g, (int64_t)t * H + e), bt = ld(b, (int64_t)t * H + e);
-        float x[3][4];
+        for (int c = 0; c < 2; ++c)
+            vv[c] = at(sV, j * kCols + cp * 2 + c);
+        const float gt = sG[j], bt = sB[j];
+        float p[2];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < 2; ++c) {
             float acc = 0.f;
 #pragma unroll
             for (int r = 0; r < RPT; ++r)
-                acc += S[r * 4 + c] * kk[r];
-            x[0][c] = acc;
+                acc += S[r * 2 + c] * kk[r];
+            p[c] = sum_rowgroups(acc);
         }
-        float gs;
-        colsum(x, 1, 0.f, gs);
 #pragma unroll
         for (int r = 0; r < RPT; ++r)
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                S[r * 4 + c] = gt * (S[r * 4 + c] - bt * kk[r] * x[0][c]) + ww[r] * vv4[c];
+            for (int c = 0; c < 2; ++c)
+                S[r * 2 + c] = gt * (S[r * 2 + c] - bt * kk[r] * p[c]) + ww[r] * vv[c];
     };
 
-    // sweep 1: S at every chunk start
-    for (int t = seq0; t < seq1; ++t) {
-        if ((t - seq0) % kC == 0) {
-            float* cp = ckpt + (ckpt_slot(t, n) * H * (DV / kCols) + (int64_t)e * slices + slice) * SL;
+    // ---- backward token t = c + j of the staged sub-chunk; Sm = S_{t-1}, S = S_t on entry
+    auto bapply = [&](int c0, int j, const float (&Sm)[EL]) {
+        const int t = c0 + j;
+        const int64_t rk = ((int64_t)t * H + e) * DK, rv = ((int64_t)t * H + e) * DV + j0;
+        float kk[RPT], qq[RPT], ww[RPT], vv[2], dd[2];
 #pragma unroll
-            for (int r = 0; r < RPT; ++r)
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    cp[st_idx(r, c)] = S[r * 4 + c];
+        for (int r = 0; r < RPT; ++r) {
+            kk[r] = at(sK, j * DK + rg + 16 * r);
+            qq[r] = at(sQ, j * DK + rg + 16 * r);
+            ww[r] = at(sW, j * DK + rg + 16 * r);
         }
-        step_fwd(t);
-    }
-
-    // sweep 2: chunks from the last, states recomputed into scratch, then walked back
-    float* sc = scr + wg * (int64_t)(kC + 1) * SL;
-    const int nch = (seq1 - seq0 + kC - 1) / kC;
-    for (int ch = nch - 1; ch >= 0; --ch) {
-        const int c0 = seq0 + ch * kC, c1 = min(seq1, c0 + kC);
-        const float* cp = ckpt + (ckpt_slot(c0, n) * H * (DV / kCols) + (int64_t)e * slices + slice) * SL;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            vv[c] = at(sV, j * kCols + cp * 2 + c);
+            dd[c] = at(sD, j * kCols + cp * 2 + c);
+        }
+        const float gt = sG[j], bt = sB[j];
+        // G += q dO^T; dq = S_t dO and dkw = G v over this slice's columns
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            float aq = 0.f, aw = 0.f;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                G[r * 2 + c] += qq[r] * dd[c];
+                aq += S[r * 2 + c] * dd[c];
+                aw += G[r * 2 + c] * vv[c];
+            }
+            aq = sum_quad(aq);
+            aw = sum_quad(aw);
+            if (cp == 0) {
+                atomicAdd(dq + rk + rg + 16 * r, aq);
+                atomicAdd(dkw + rk + rg + 16 * r, aw);
+            }
+        }
+        // dv = G^T kw; p = S_{t-1}^T k (column sums over the dk rows)
+        float p[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            float a1 = 0.f, a2 = 0.f;
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) {
+                a1 += G[r * 2 + c] * ww[r];
+                a2 += Sm[r * 2 + c] * kk[r];
+            }
+            a1 = sum_rowgroups(a1);
+            p[c] = sum_rowgroups(a2);
+            if (rg == 0)
+                dv[rv + c] = a1;
+        }
+        // dg = <G, P>, P = S_{t-1} - b k p^T; dP = g G; y = dP^T k
+        float dgp = 0.f;
 #pragma unroll
         for (int r = 0; r < RPT; ++r)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                S[r * 4 + c] = cp[st_idx(r, c)];
-                sc[st_idx(r, c)] = S[r * 4 + c];
+            for (int c = 0; c < 2; ++c) {
+                dgp += G[r * 2 + c] * (Sm[r * 2 + c] - bt * kk[r] * p[c]);
+                G[r * 2 + c] *= gt;
             }
-        for (int t = c0; t < c1; ++t) {
-            step_fwd(t);
-            float* so = sc + (int64_t)(t - c0 + 1) * SL;
+        dgp = sum_rowgroups(sum_quad(dgp));
+        float y[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            float a1 = 0.f;
 #pragma unroll
             for (int r = 0; r < RPT; ++r)
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    so[st_idx(r, c)] = S[r * 4 + c];
+                a1 += G[r * 2 + c] * kk[r];
+            y[c] = sum_rowgroups(a1);
         }
-        // S holds S_{c1 - 1}
-        for (int t = c1 - 1; t >= c0; --t) {
-            const float* sp = sc + (int64_t)(t - c0) * SL;
-            float Sm[EL];
-#pragma unroll
-            for (int r = 0; r < RPT; ++r)
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    Sm[r * 4 + c] = sp[st_idx(r, c)];
-            const int64_t rk = ((int64_t)t * H + e) * DK, rv = ((int64_t)t * H + e) * DV + j0;
-            float kk[RPT], qq[RPT], ww[RPT], vv4[4], do4[4];
-#pragma unroll
-            for (int r = 0; r < RPT; ++r) {
-                kk[r] = ld(k, rk + rg + 32 * r);
-                qq[r] = ld(q, rk + rg + 32 * r);
-                ww[r] = ld(kw, rk + rg + 32 * r);
-            }
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                vv4[c] = ld(v, rv + c);
-                do4[c] = ld(dO, rv + c);
-            }
-            const float gt = ld(g, (int64_t)t * H + e), bt = ld(b, (int64_t)t * H + e);
-            // G += q dO^T; dq = S_t dO and dkw = G v (row sums: lanes, then atomics)
-#pragma unroll
-            for (int r = 0; r < RPT; ++r) {
-                float aq = 0.f, aw = 0.f;
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    G[r * 4 + c] += qq[r] * do4[c];
-                    aq += S[r * 4 + c] * do4[c];
-                    aw += G[r * 4 + c] * vv4[c];
-                }
-                aq = sum_cols8(aq);
-                aw = sum_cols8(aw);
-                if (cg == 0) {
-                    atomicAdd(dq + rk + rg + 32 * r, aq);
-                    atomicAdd(dkw + rk + rg + 32 * r, aw);
-                }
-            }
-            // column sums: dv = G^T kw and p = S_{t-1}^T k
-            float x[3][4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                float a1 = 0.f, a2 = 0.f;
-#pragma unroll
-                for (int r = 0; r < RPT; ++r) {
-                    a1 += G[r * 4 + c] * ww[r];
-                    a2 += Sm[r * 4 + c] * kk[r];
-                }
-                x[0][c] = a1;
-                x[1][c] = a2;
-            }
-            float gs;
-            colsum(x, 2, 0.f, gs);
-            if (rg == 0)
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    dv[rv + c] = x[0][c];
-            float p4[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-                p4[c] = x[1][c];
-            // dg = <G, P>, P = S_{t-1} - b k p^T; dP = g G; y = dP^T k
-            float dgp = 0.f;
-#pragma unroll
-            for (int r = 0; r < RPT; ++r)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    dgp += G[r * 4 + c] * (Sm[r * 4 + c] - bt * kk[r] * p4[c]);
-                    G[r * 4 + c] *= gt;
-                }
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                float a1 = 0.f;
-#pragma unroll
-                for (int r = 0; r < RPT; ++r)
-                    a1 += G[r * 4 + c] * kk[r];
-                x[0][c] = a1;
-            }
-            float dgs;
-            colsum(x, 1, dgp, dgs);
-            float y4[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-                y4[c] = x[0][c];
-            if (tid == 0)
-                atomicAdd(dg + (int64_t)t * H + e, dgs);
-            if (rg == 0) {                       // db -= y . p over this slice's columns
-                float yp = y4[0] * p4[0] + y4[1] * p4[1] + y4[2] * p4[2] + y4[3] * p4[3];
-                yp = sum_cols8(yp);
-                if (cg == 0)
-                    atomicAdd(db + (int64_t)t * H + e, -yp);
-            }
-            // dk -= b (dP p + S_{t-1} y); G = dP - b k y^T
-#pragma unroll
-            for (int r = 0; r < RPT; ++r) {
-                float a1 = 0.f;
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    a1 += G[r * 4 + c] * p4[c] + Sm[r * 4 + c] * y4[c];
-                    G[r * 4 + c] -= bt * kk[r] * y4[c];
-                }
-                a1 = sum_cols8(a1);
-                if (cg == 0)
-                    atomicAdd(dk + rk + rg + 32 * r, -bt * a1);
-            }
-#pragma unroll
-            for (int x2 = 0; x2 < EL; ++x2)
-                S[x2] = Sm[x2];
+        const float yp = sum_quad(y[0] * p[0] + y[1] * p[1]);
+        if (lane == 0) {
+            atomicAdd(dg + (int64_t)t * H + e, dgp);
+            atomicAdd(db + (int64_t)t * H + e, -yp);   // db -= y . p
         }
+        // dk -= b (dP p + S_{t-1} y); G = dP - b k y^T
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            float a1 = 0.f;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                a1 += G[r * 2 + c] * p[c] + Sm[r * 2 + c] * y[c];
+                G[r * 2 + c] -= bt * kk[r] * y[c];
+            }
+            a1 = sum_quad(a1);
+            if (cp == 0)
+                atomicAdd(dk + rk + rg + 16 * r, -bt * a1);
+        }
+#pragma unroll
+        for (int x = 0; x < EL; ++x)
+            S[x] = Sm[x];
+    };
+
+    // sweep 1: S at every sub-chunk start, into the checkpoints
+    Pre P;
+    if (nsub > 0)
+        pre_load(seq0, false, P);
+    for (int m = 0; m < nsub; ++m) {
+        const int c0 = seq0 + m * SUB, len = min(SUB, seq1 - c0);
+        lds_barrier();                           // the previous sub-chunk's LDS reads are done
+        pre_store(P, false);
+        lds_barrier();
+        if (m + 1 < nsub)
+            pre_load(c0 + SUB, false, P);
+        float* cpt = ckpt_at(c0);
+#pragma unroll
+        for (int x = 0; x < EL; ++x)
+            cpt[x * 64] = S[x];
+#pragma unroll
+        for (int j = 0; j < SUB; ++j)
+            if (j < len)
+                fapply(j);
+    }
+
+    // sweep 2: sub-chunks from the last; each one's states recomputed into
+    // registers from its checkpoint, then walked backwards
+    float Cn[EL];
+    if (nsub > 0) {
+        pre_load(seq0 + (nsub - 1) * SUB, true, P);
+        const float* cpt = ckpt_at(seq0 + (nsub - 1) * SUB);
+#pragma unroll
+        for (int x = 0; x < EL; ++x)
+            Cn[x] = cpt[x * 64];
+    }
+    for (int m = nsub - 1; m >= 0; --m) {
+        const int c0 = seq0 + m * SUB, len = min(SUB, seq1 - c0);
+        lds_barrier();
+        pre_store(P, true);
+        lds_barrier();
+        float Ss[SUB][EL];                       // Ss[j] = S before token c0 + j
+#pragma unroll
+        for (int x = 0; x < EL; ++x)
+            S[x] = Cn[x];
+        if (m > 0) {
+            pre_load(c0 - SUB, true, P);
+            const float* cpt = ckpt_at(c0 - SUB);
+#pragma unroll
+            for (int x = 0; x < EL; ++x)
+                Cn[x] = cpt[x * 64];
+        }
+#pragma unroll
+        for (int j = 0; j < SUB; ++j) {
+#pragma unroll
+            for (int x = 0; x < EL; ++x)
+                Ss[j][x] = S[x];
+            if (j < len)
+                fapply(j);
+        }
+#pragma unroll
+        for (int j = SUB - 1; j >= 0; --j)
+            if (j < len)
+                bapply(c0, j, Ss[j]);
     }
     if (dS_init) {
 #pragma unroll
         for (int r = 0; r < RPT; ++r)
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                dS_init[sbase + (int64_t)(rg + 32 * r) * DV + j0 + c] = G[r * 4 + c];
+            for (int c = 0; c < 2; ++c)
+                dS_init[sbase + (int64_t)(rg + 16 * r) * DV + j0 + c] = G[r * 2 + c];
     }
 }
 
@@ -421,10 +470,8 @@ __global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ p, int64_
 
 size_t bwd_workspace_floats(int n_seqs, int total_tokens, int heads, int dk, int dv)
 {
-    const int64_t slots = total_tokens / bwd::kC + n_seqs + 1;
-    const int64_t wgs = (int64_t)n_seqs * heads * (dv / bwd::kCols);
-    return (size_t)(slots * heads * dk * dv)                      // chunk-start states
-         + (size_t)(wgs * (bwd::kC + 1) * dk * bwd::kCols)       // one chunk of states per workgroup
+    const int64_t slots = total_tokens / bwd::sub_len(dk) + n_seqs + 1;
+    return (size_t)(slots * heads * dk * dv)                      // sub-chunk start states
          + (size_t)total_tokens * heads * dk;                     // dkw
 }
 
@@ -434,11 +481,10 @@ template <typename T, int DK>
 static hipError_t launch_bwd_T(const BwdArgs& p, hipStream_t s)
 {
     const int H = p.heads, T_ = p.total_tokens;
-    const int64_t slots = T_ / bwd::kC + p.n_seqs + 1;
+    const int64_t slots = T_ / bwd::sub_len(DK) + p.n_seqs + 1;
     float* ckpt = p.ws;
-    float* scr = ckpt + slots * H * DK * p.dv;
+    float* dkw = ckpt + slots * H * DK * p.dv;
     const int64_t wgs = (int64_t)p.n_seqs * H * (p.dv / bwd::kCols);
-    float* dkw = scr + wgs * (bwd::kC + 1) * DK * bwd::kCols;
     // accumulators start at zero (a fill kernel: no memset node under graph capture)
     auto zero = [&](float* x, int64_t n) {
         if (n > 0)
@@ -454,10 +500,10 @@ static hipError_t launch_bwd_T(const BwdArgs& p, hipStream_t s)
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || wgs == 0)
         return err;
-    hipLaunchKernelGGL((bwd::scan_bwd_kernel<T, DK>), dim3((unsigned)wgs), dim3(256), 0, s,
+    hipLaunchKernelGGL((bwd::scan_bwd_kernel<T, DK>), dim3((unsigned)wgs), dim3(64), 0, s,
                        (const T*)p.q, (const T*)p.k, (const T*)p.kw, (const T*)p.v, (const T*)p.g,
                        (const T*)p.b, (const T*)p.dO, p.cu_seqlens, H, p.dv, p.s_init, p.ds_final,
-                       ckpt, scr, p.gq, p.gk, dkw, p.gv, p.gg, p.gb, p.gs_init);
+                       ckpt, p.gq, p.gk, dkw, p.gv, p.gg, p.gb, p.gs_init);
     if ((err = hipGetLastError()) != hipSuccess || T_ == 0)
         return err;
     const int64_t threads = ((int64_t)(T_ + bwd::kC - 1) / bwd::kC) * H * DK;
