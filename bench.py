@@ -38,6 +38,7 @@ METRIC = "PRISM fwd tokens/sec at 1 GPU (L=4) + % of HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
 FP32_MFMA_PEAK_TFLOPS = 157.3
+FP32_VALU_PEAK_TFLOPS = 157.3    # MI355X fp32 vector (packed FMA); unpacked: 256 CU x 64 lanes x 2 x 2.4 GHz = 78.6
 _CSRC = "gated_delta_rule_prologue_amd/csrc/"
 # Sources that determine each kernel as launched (kernel body, shared helpers,
 # dispatch): a committed counter figure is only reported while they are unchanged.
@@ -251,6 +252,15 @@ def bwd_bytes(w, n_seqs, T, esize):
     return ht * (reads + writes) + 4 * n_seqs * H * dk * dv + H * dk * 4 * (esize + 4)
 
 
+def bwd_flops(w, T):
+    """fp32 vector flops of one backward pass in its token-recurrent form, per
+    element of the dk x dv state and head-token: the forward token twice (the
+    checkpoint sweep and the recomputation; p = S^T k 2, the update 5) and the
+    reverse token (G += q dO^T 2, dq 2, dkw 2, dv 2, p 2, dg 4, G *= g 1,
+    y 2, dk 4, G -= b k y^T 2): 37 in all."""
+    return 37 * T * w.heads * w.dk * w.dv
+
+
 def bwd_bench(w, inp, dev_copies, steps, warmup):
     """Time prism_bwd (gradients of every input) on the workload, with the
     upstream gradient dO and no carried state."""
@@ -291,11 +301,16 @@ def bwd_bench(w, inp, dev_copies, steps, warmup):
     assert status == 0, binding.status_str(status)
     ms = sum(a.elapsed_time(b) for a, b in ev) / steps
     nbytes = bwd_bytes(w, inp.n_seqs, T, esize)
+    flops = bwd_flops(w, T)
     ach = nbytes / (ms * 1e-3) / 1e9
+    tf = flops / (ms * 1e-3) / 1e12
     return {"tokens_per_s": steps * T / elapsed, "us_per_call": ms * 1e3,
-            "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": "backward (all launches)",
-                         "avg_launch_us": ms * 1e3, "algorithmic_bytes": nbytes}}
+            "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_VALU_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tf / FP32_VALU_PEAK_TFLOPS, "traffic": None,
+                         "kernel": "backward (all launches)", "avg_launch_us": ms * 1e3,
+                         "algorithmic_flops": flops},
+            "hbm": {"achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": ach / HBM_PEAK_GBS, "algorithmic_bytes": nbytes}}
 
 
 def main():
