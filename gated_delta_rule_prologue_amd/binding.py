@@ -8,7 +8,8 @@ Names follow the C ABI: ``fwd`` -> prism_fwd, ``fwd_resume`` ->
 prism_fwd_resume, ``decode_step`` -> prism_decode_step, ``prologue`` ->
 prism_prologue, ``prologue_ex`` -> prism_prologue_ex, ``scan`` -> prism_scan,
 ``scan_ex`` -> prism_scan_ex, ``workspace_bytes`` -> prism_workspace_bytes,
-``scan_workspace_bytes`` -> prism_scan_workspace_bytes, ``bwd`` -> prism_bwd.
+``scan_workspace_bytes`` -> prism_scan_workspace_bytes, ``bwd`` -> prism_bwd_ex (prism_bwd
+with a residual choice).
 """
 from __future__ import annotations
 
@@ -74,6 +75,8 @@ def lib():
         L.prism_bwd_workspace_bytes.restype = S
         L.prism_bwd.argtypes = [D] + [P] * 10 + [I] + [P] * 14 + [S, P]
         L.prism_bwd.restype = I
+        L.prism_bwd_ex.argtypes = [D] + [P] * 10 + [I, I] + [P] * 14 + [S, P]
+        L.prism_bwd_ex.restype = I
         L.prism_decode_step.restype = I
         L.prism_status_str.argtypes = [I]
         L.prism_status_str.restype = ctypes.c_char_p
@@ -326,10 +329,12 @@ def decode_step(q, k, v, u, g, b, a, h, conv_w, L: int, S, k_hist, o=None, strea
 
 
 def bwd(q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L: int, dO, dS_final=None, S_init=None,
-        want_dS_init: bool = True, workspace=None, stream=None) -> dict:
-    """Gradients of sum <dO, o> + <dS_final, S_final> (prism_bwd, closed-form
-    residual chain): a dict of fp32 tensors q, k, v, u, a, h, g, b, conv_w and
-    S_init (the last when ``want_dS_init``)."""
+        want_dS_init: bool = True, workspace=None, stream=None, residual="linear") -> dict:
+    """Gradients of sum <dO, o> + <dS_final, S_final> (prism_bwd_ex;
+    ``residual`` "linear" closed-form chain or "gelu"): a dict of fp32 tensors
+    q, k, v, u, a, h, g, b, conv_w and S_init (the last when ``want_dS_init``)."""
+    if residual not in RESIDUAL:
+        raise ValueError(f"residual must be one of {sorted(RESIDUAL)}")
     d = _dims_of(q, v, cu_seqlens)
     _check_write_branch(d, q.dtype, k, u, a, h, b, conv_w, L)
     _check_scan(d, q.dtype, q, k, k, v, g, b)
@@ -350,9 +355,10 @@ def bwd(q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L: int, dO, dS_final=None, S
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if workspace.numel() * workspace.element_size() < need:
         raise ValueError(f"workspace needs {need} bytes")
-    _check("prism_bwd", lib().prism_bwd(
+    _check("prism_bwd_ex", lib().prism_bwd_ex(
         ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(g), _ptr(b), _ptr(a), _ptr(h),
-        _ptr(conv_w), _ptr(cu_seqlens), int(L), _ptr(S_init), _ptr(dO), _ptr(dS_final),
+        _ptr(conv_w), _ptr(cu_seqlens), int(L), RESIDUAL[residual], _ptr(S_init), _ptr(dO),
+        _ptr(dS_final),
         _ptr(out["q"]), _ptr(out["k"]), _ptr(out["v"]), _ptr(out["u"]), _ptr(out["g"]),
         _ptr(out["b"]), _ptr(out["a"]), _ptr(out["h"]), _ptr(out["conv_w"]), _ptr(out["S_init"]),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))

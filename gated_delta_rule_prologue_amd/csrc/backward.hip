@@ -23,7 +23,7 @@
 //     LDS.  Row sums (over the 8 columns) go to fp32 atomics into dq, dk and
 //     dkw, which the value slices of a chain share.
 //   * write_key_bwd_kernel: one thread per (head, channel, block of 64 tokens):
-//     the residual chain backwards (du, da, dh written, dr_0 formed), b and
+//     the residual chain (closed form or GELU refinement) backwards (du, da, dh written, dr_0 formed), b and
 //     the taps (dk, db through atomics; dconv_w summed over the block first).
 #include "common.h"
 #include "kernels.h"
@@ -370,7 +370,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void write_key_bwd_kernel(
     const T* __restrict__ k, const T* __restrict__ u, const T* __restrict__ a,
     const T* __restrict__ h, const T* __restrict__ b, const T* __restrict__ conv_w,
-    const int32_t* __restrict__ cu, int n_seqs, int T_total, int H, int DK, int L,
+    const int32_t* __restrict__ cu, int n_seqs, int T_total, int H, int DK, int L, bool gelu,
     const float* __restrict__ dkw, float* __restrict__ dk, float* __restrict__ du,
     float* __restrict__ da, float* __restrict__ dh, float* __restrict__ db,
     float* __restrict__ dconv_w)
@@ -423,12 +423,15 @@ __global__ __launch_bounds__(256) void write_key_bwd_kernel(
             kx[m] = tau >= s0 ? ld(k, ((int64_t)tau * H + e) * DK + i) : 0.f;
         }
         const float r0 = w[0] * kx[0] + w[1] * kx[1] + w[2] * kx[2] + w[3] * kx[3];
-        // residuals r_l, l = 1 .. L-1 (closed form as a running product)
+        // residuals r_l, l = 1 .. L-1 (the closed form as a running product, or
+        // the GELU refinement chain)
         float r[16];
         r[1] = r0;
         const int64_t lb = (int64_t)t * lrow + (int64_t)e * (L - 1) * DK + i;
-        for (int l = 1; l < L - 1; ++l)
-            r[l + 1] = r[l] * (1.f - ld(a, lb + (int64_t)(l - 1) * DK) * ld(h, lb + (int64_t)(l - 1) * DK));
+        for (int l = 1; l < L - 1; ++l) {
+            const float al = ld(a, lb + (int64_t)(l - 1) * DK), hl = ld(h, lb + (int64_t)(l - 1) * DK);
+            r[l + 1] = gelu ? r[l] - al * gelu_as(hl * r[l]) : r[l] * (1.f - al * hl);
+        }
         float dr_next = 0.f;
         for (int l = L - 1; l >= 1; --l) {
             const int64_t sl = lb + (int64_t)(l - 1) * DK;
@@ -436,9 +439,17 @@ __global__ __launch_bounds__(256) void write_key_bwd_kernel(
             du[sl] = g_kw * al * r[l];
             float dal = g_kw * ul * r[l], dhl = 0.f, drl = g_kw * al * ul;
             if (l <= L - 2) {
-                dal -= dr_next * hl * r[l];
-                dhl = -dr_next * al * r[l];
-                drl += dr_next * (1.f - al * hl);
+                if (gelu) {                      // r_{l+1} = r_l - a_l GELU(h_l r_l)
+                    float gp;
+                    const float gv = gelu_as_grad(hl * r[l], gp);
+                    dal -= dr_next * gv;
+                    dhl = -dr_next * al * r[l] * gp;
+                    drl += dr_next * (1.f - al * hl * gp);
+                } else {                         // r_{l+1} = r_l (1 - a_l h_l)
+                    dal -= dr_next * hl * r[l];
+                    dhl = -dr_next * al * r[l];
+                    drl += dr_next * (1.f - al * hl);
+                }
             }
             da[sl] = dal;
             dh[sl] = dhl;
@@ -510,7 +521,7 @@ static hipError_t launch_bwd_T(const BwdArgs& p, hipStream_t s)
     hipLaunchKernelGGL((bwd::write_key_bwd_kernel<T>), dim3((unsigned)((threads + 255) / 256)),
                        dim3(256), 0, s, (const T*)p.k, (const T*)p.u, (const T*)p.a,
                        (const T*)p.h, (const T*)p.b, (const T*)p.conv_w, p.cu_seqlens, p.n_seqs,
-                       T_, H, DK, p.L, dkw, p.gk, p.gu, p.ga, p.gh, p.gb, p.gconv);
+                       T_, H, DK, p.L, p.gelu, dkw, p.gk, p.gu, p.ga, p.gh, p.gb, p.gconv);
     return hipGetLastError();
 }
 

@@ -60,6 +60,20 @@ __device__ __forceinline__ float gelu_as(float x)
     return 0.5f * x * (1.f + __builtin_copysignf(e, x));
 }
 
+// GELU(x) and GELU'(x) = Phi(x) + x phi(x), phi(x) = exp(-x^2 / 2) / sqrt(2 pi):
+// Phi from the same erf approximation as gelu_as, phi from one exp2.
+__device__ __forceinline__ float gelu_as_grad(float x, float& dgelu)
+{
+    const float z = fabsf(x) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(1.f + 0.3275911f * z);
+    const float poly =
+        t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+    const float ez = __builtin_amdgcn_exp2f(-z * z * 1.44269504088896341f);   // exp(-x^2 / 2)
+    const float phi_cdf = 0.5f * (1.f + __builtin_copysignf(1.f - poly * ez, x));
+    dgelu = phi_cdf + x * ez * 0.39894228040143268f;
+    return x * phi_cdf;
+}
+
 // Element conversions for the two input storage types.
 __device__ __forceinline__ float to_f32(uint16_t x) { return bf16_to_f32(x); }
 __device__ __forceinline__ float to_f32(float x) { return x; }

@@ -62,6 +62,7 @@ hipError_t launch_split_scan(const ScanArgs& p, int P, void* ws, hipStream_t str
 struct BwdArgs {
     bool bf16;
     int n_seqs, total_tokens, heads, dk, dv, L;
+    bool gelu;                      // residual chain r - a GELU(h r) instead of the closed form
     const void *q, *k, *v, *kw, *u, *a, *h, *g, *b, *conv_w, *dO;
     const int32_t* cu_seqlens;
     const float* s_init;            // or null (zero)

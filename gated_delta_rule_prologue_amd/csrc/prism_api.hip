@@ -332,14 +332,15 @@ size_t prism_bwd_workspace_bytes(const prism_dims* d, int L)
                                                      d->dv) * sizeof(float);
 }
 
-prism_status prism_bwd(const prism_dims* d, const void* q, const void* k, const void* v,
-                       const void* u, const void* g, const void* b, const void* a, const void* h,
-                       const void* conv_w, const int32_t* cu_seqlens, int L, const float* S_init,
-                       const void* dO, const float* dS_final, float* dq, float* dk, float* dv,
-                       float* du, float* dg, float* db, float* da, float* dh, float* dconv_w,
-                       float* dS_init, void* workspace, size_t workspace_bytes, void* stream)
+prism_status prism_bwd_ex(const prism_dims* d, const void* q, const void* k, const void* v,
+                          const void* u, const void* g, const void* b, const void* a, const void* h,
+                          const void* conv_w, const int32_t* cu_seqlens, int L, int residual,
+                          const float* S_init, const void* dO, const float* dS_final, float* dq,
+                          float* dk, float* dv, float* du, float* dg, float* db, float* da,
+                          float* dh, float* dconv_w, float* dS_init, void* workspace,
+                          size_t workspace_bytes, void* stream)
 {
-    if (!dims_ok(d) || L < 1 || L > PRISM_MAX_LEVELS)
+    if (!dims_ok(d) || L < 1 || L > PRISM_MAX_LEVELS || !residual_ok(residual))
         return PRISM_EINVAL;
     if (!tok_ok(d, q) || !tok_ok(d, k) || !tok_ok(d, v) || !tok_ok(d, g) || !tok_ok(d, b) ||
         !tok_ok(d, dO) || !ptr_ok(conv_w) || !ptr_ok(cu_seqlens) || !tok_ok(d, dq) ||
@@ -353,8 +354,8 @@ prism_status prism_bwd(const prism_dims* d, const void* q, const void* k, const 
         return PRISM_EUNSUPPORTED;
     if (workspace_bytes < prism_bwd_workspace_bytes(d, L))
         return PRISM_EINVAL;
-    prism_status st = prologue_impl(d, k, u, a, h, b, conv_w, nullptr, cu_seqlens, L,
-                                    PRISM_RESIDUAL_LINEAR, workspace, stream);
+    prism_status st = prologue_impl(d, k, u, a, h, b, conv_w, nullptr, cu_seqlens, L, residual,
+                                    workspace, stream);
     if (st != PRISM_OK)
         return st;
     prism::BwdArgs p;
@@ -365,6 +366,7 @@ prism_status prism_bwd(const prism_dims* d, const void* q, const void* k, const 
     p.dk = d->dk;
     p.dv = d->dv;
     p.L = L;
+    p.gelu = residual == PRISM_RESIDUAL_GELU;
     p.q = q; p.k = k; p.v = v; p.kw = workspace; p.u = u; p.a = a; p.h = h; p.g = g; p.b = b;
     p.conv_w = conv_w;
     p.dO = dO;
@@ -376,6 +378,18 @@ prism_status prism_bwd(const prism_dims* d, const void* q, const void* k, const 
     p.gs_init = dS_init;
     p.ws = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + kw_bytes(d));
     return from_hip(prism::launch_bwd(p, (hipStream_t)stream));
+}
+
+prism_status prism_bwd(const prism_dims* d, const void* q, const void* k, const void* v,
+                       const void* u, const void* g, const void* b, const void* a, const void* h,
+                       const void* conv_w, const int32_t* cu_seqlens, int L, const float* S_init,
+                       const void* dO, const float* dS_final, float* dq, float* dk, float* dv,
+                       float* du, float* dg, float* db, float* da, float* dh, float* dconv_w,
+                       float* dS_init, void* workspace, size_t workspace_bytes, void* stream)
+{
+    return prism_bwd_ex(d, q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L, PRISM_RESIDUAL_LINEAR,
+                        S_init, dO, dS_final, dq, dk, dv, du, dg, db, da, dh, dconv_w, dS_init,
+                        workspace, workspace_bytes, stream);
 }
 
 prism_status prism_decode_step(const prism_dims* d, const void* q, const void* k, const void* v,

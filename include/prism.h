@@ -279,6 +279,21 @@ prism_status prism_bwd(const prism_dims* d,
                        float* da, float* dh, float* dconv_w, float* dS_init,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* prism_bwd with a choice of residual chain (prism_residual): the closed form
+ * (PRISM_RESIDUAL_LINEAR, as prism_bwd) or the non-linear refinement chain
+ * r_{l+1} = r_l - a_l GELU(h_l r_l) of the WeChat page, section 消除 Step 间串行
+ * (PRISM_RESIDUAL_GELU; forward as in prism_fwd_resume).  Any other value:
+ * PRISM_EINVAL.  Other arguments, layouts and errors as in prism_bwd. */
+prism_status prism_bwd_ex(const prism_dims* d,
+                          const void* q, const void* k, const void* v,
+                          const void* u, const void* g, const void* b,
+                          const void* a, const void* h, const void* conv_w,
+                          const int32_t* cu_seqlens, int L, int residual, const float* S_init,
+                          const void* dO, const float* dS_final,
+                          float* dq, float* dk, float* dv, float* du, float* dg, float* db,
+                          float* da, float* dh, float* dconv_w, float* dS_init,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* prism_status_str(prism_status s);
 

@@ -187,8 +187,8 @@ def decode_step(step, S, k_hist, threads: Optional[int] = None, residual: str = 
 
 
 def bwd(inp, d_o, dS_final=None, S_init=None, chains: Optional[Sequence[int]] = None,
-        threads: Optional[int] = None):
-    """Backward pass (closed-form residual chain) for the loss
+        threads: Optional[int] = None, residual: str = "linear"):
+    """Backward pass (``residual``: "linear" closed-form chain or "gelu") for the loss
     sum <d_o, o> + <dS_final, S_final>: a dict of float64 gradients for q, k,
     v [T, H, d], u, a, h [T, H, L-1, dk] (L > 1), g, b [T, H], conv_w [H, dk, 4]
     and S_init [n_seqs, H, dk, dv].  ``chains`` restricts the evaluation (rows of
@@ -208,7 +208,7 @@ def bwd(inp, d_o, dS_final=None, S_init=None, chains: Optional[Sequence[int]] = 
         out[n] = np.zeros(lv) if L > 1 else None
     ch = None if chains is None else np.ascontiguousarray(np.asarray(chains, dtype=np.int64))
     rc = _load().prism_oracle_bwd(
-        ctypes.byref(_dims(inp, code)), _ptr(cu), _ptr(inp.q), _ptr(inp.k), _ptr(inp.v),
+        ctypes.byref(_dims(inp, code, residual)), _ptr(cu), _ptr(inp.q), _ptr(inp.k), _ptr(inp.v),
         _ptr(inp.u), _ptr(inp.g), _ptr(inp.b), _ptr(inp.a), _ptr(inp.h), _ptr(inp.conv_w),
         _ptr(s0), _ptr(d_o), _ptr(dsf), _ptr(ch), 0 if ch is None else int(ch.size),
         _ptr(out["q"]), _ptr(out["k"]), _ptr(out["v"]), _ptr(out["u"]), _ptr(out["g"]),

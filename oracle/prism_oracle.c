@@ -102,6 +102,12 @@ static double gelu(double x)
     return 0.5 * x * (1.0 + erf(x / sqrt(2.0)));
 }
 
+/* GELU'(x) = Phi(x) + x phi(x), phi the standard normal density. */
+static double gelu_prime(double x)
+{
+    return 0.5 * (1.0 + erf(x / sqrt(2.0))) + x * exp(-0.5 * x * x) / sqrt(2.0 * 3.14159265358979323846);
+}
+
 /* Exact widening of element i of an fp32 or bf16 array. */
 static double elem(const void* p, int64_t dtype, int64_t i)
 {
@@ -289,7 +295,7 @@ int prism_oracle_k_history(const oracle_dims* d, const int32_t* cu_seqlens, cons
 }
 
 /*
- * Backward pass of the forward above (closed-form residual chain, L >= 1), for
+ * Backward pass of the forward above (either residual chain, L >= 1), for
  * the loss  sum_t <do_t, o_t> + <dS_final, S_final>  of given upstream
  * gradients.  Reverse-mode differentiation of the token recurrence, written
  * out step by step:
@@ -305,8 +311,10 @@ int prism_oracle_k_history(const oracle_dims* d, const int32_t* cu_seqlens, cons
  *
  * then through the write key kw_t = b_t k_t + sum_l a_l r_l u_l with
  * r_{l+1} = r_l (1 - a_l h_l), r_1 = r_0 = sum_m w_m k_{t-3+m}: the residual
- * chain in reverse (dr_l = dkw a_l u_l + dr_{l+1} (1 - a_l h_l)), then the
- * convolution (dw_m += dr_0 k_{t-3+m}, dk_{t-3+m} += w_m dr_0 inside the
+ * chain in reverse (dr_l = dkw a_l u_l + dr_{l+1} (1 - a_l h_l)); with the
+ * GELU chain r_{l+1} = r_l - a_l GELU(h_l r_l) the factor (1 - a_l h_l)
+ * becomes 1 - a_l h_l GELU'(h_l r_l), da_l takes -dr_{l+1} GELU(h_l r_l) and
+ * dh_l = -dr_{l+1} a_l r_l GELU'(h_l r_l); then the convolution (dw_m += dr_0 k_{t-3+m}, dk_{t-3+m} += w_m dr_0 inside the
  * sequence).  Taps that read a carried history contribute to no input
  * gradient here.  All outputs are double; chains, when given, restrict the
  * evaluation like prism_oracle_fwd (dconv_w then sums over those chains only).
@@ -322,7 +330,8 @@ int prism_oracle_bwd(const oracle_dims* d, const int32_t* cu_seqlens,
                      double* da, double* dh, double* dconv_w, double* ds_init, int nthreads)
 {
     if (!d || !cu_seqlens || !q || !k || !v || !g || !b || !conv_w || !d_o || !dq || !dk ||
-        !dv || !dg || !db || !dconv_w || d->L < 1 || d->residual != ORACLE_RESIDUAL_LINEAR)
+        !dv || !dg || !db || !dconv_w || d->L < 1 ||
+        (d->residual != ORACLE_RESIDUAL_LINEAR && d->residual != ORACLE_RESIDUAL_GELU))
         return 1;
     if (d->L > 1 && (!u || !a || !h || !du || !da || !dh))
         return 1;
@@ -460,10 +469,12 @@ int prism_oracle_bwd(const oracle_dims* d, const int32_t* cu_seqlens,
                     r0 += elem(conv_w, dt, (e * dk_ + i) * 4 + m) *
                           k_at(d, k, NULL, n, t0, t - 3 + m, e, i);
                 /* r[l] for l = 1 .. L-1 */
+                const int gel = d->residual == ORACLE_RESIDUAL_GELU;
                 r[1] = r0;
                 for (int64_t l = 1; l < L - 1; ++l) {
                     const int64_t sl = ((t * H + e) * (L - 1) + (l - 1)) * dk_ + i;
-                    r[l + 1] = r[l] * (1.0 - elem(a, dt, sl) * elem(h, dt, sl));
+                    const double al = elem(a, dt, sl), hl = elem(h, dt, sl);
+                    r[l + 1] = gel ? r[l] - al * gelu(hl * r[l]) : r[l] * (1.0 - al * hl);
                 }
                 double dr_next = 0.0;                  /* dr_{l+1} */
                 for (int64_t l = L - 1; l >= 1; --l) {
@@ -473,9 +484,16 @@ int prism_oracle_bwd(const oracle_dims* d, const int32_t* cu_seqlens,
                     double dal = dkwi * ul * r[l];
                     double dhl = 0.0, drl = dkwi * al * ul;
                     if (l <= L - 2) {
-                        dal -= dr_next * hl * r[l];
-                        dhl = -dr_next * al * r[l];
-                        drl += dr_next * (1.0 - al * hl);
+                        if (gel) {                     /* r_{l+1} = r_l - a_l GELU(h_l r_l) */
+                            const double x = hl * r[l], gp = gelu_prime(x);
+                            dal -= dr_next * gelu(x);
+                            dhl = -dr_next * al * r[l] * gp;
+                            drl += dr_next * (1.0 - al * hl * gp);
+                        } else {                       /* r_{l+1} = r_l (1 - a_l h_l) */
+                            dal -= dr_next * hl * r[l];
+                            dhl = -dr_next * al * r[l];
+                            drl += dr_next * (1.0 - al * hl);
+                        }
                     }
                     da[sl] = dal;
                     dh[sl] = dhl;

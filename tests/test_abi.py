@@ -29,7 +29,7 @@ def test_header_declares_the_entry_points():
     for n in ("prism_fwd", "prism_prologue", "prism_scan", "prism_workspace_bytes",
               "prism_status_str", "prism_abi_version", "prism_fwd_resume", "prism_decode_step",
               "prism_prologue_ex", "prism_scan_ex", "prism_scan_workspace_bytes", "prism_bwd",
-              "prism_bwd_workspace_bytes"):
+              "prism_bwd_workspace_bytes", "prism_bwd_ex"):
         assert n in names
 
 
@@ -171,6 +171,24 @@ def test_prologue_ex_rejects_bad_arguments(lib):
     assert call(hist=FAKE + 2) == B.PRISM_EINVAL
     assert call(kw=None) == B.PRISM_EINVAL
     assert call(L=17) == B.PRISM_EINVAL
+
+
+def test_bwd_ex_rejects_bad_arguments(lib):
+    from gated_delta_rule_prologue_amd import binding as B
+    d = B.make_dims(1, 10, 1, 64, 64, B.PRISM_BF16)
+    call = lambda L=3, residual=1, dq=FAKE, ws=1 << 30: lib.prism_bwd_ex(
+        ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, L, residual,
+        None, FAKE, None, dq, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws, None)
+    assert call(residual=2) == B.PRISM_EINVAL
+    assert call(residual=-1) == B.PRISM_EINVAL
+    assert call(L=0) == B.PRISM_EINVAL
+    assert call(dq=None) == B.PRISM_EINVAL
+    assert call(ws=16) == B.PRISM_EINVAL
+    d96 = B.make_dims(1, 10, 1, 96, 64, B.PRISM_BF16)
+    assert lib.prism_bwd_ex(
+        ctypes.byref(d96), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 1,
+        None, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+        1 << 30, None) == B.PRISM_EUNSUPPORTED
 
 
 def test_binding_checks_shapes_before_calling():

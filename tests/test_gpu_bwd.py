@@ -1,5 +1,5 @@
-"""GPU parity of the backward pass (prism_bwd, closed-form residual chain)
-against the fp64 oracle's backward (itself pinned against finite differences
+"""GPU parity of the backward pass (prism_bwd_ex with the closed-form residual
+chain, and with the GELU refinement chain) against the fp64 oracle's backward (itself pinned against finite differences
 and torch autograd): every gradient, max-relative error per tensor, at the
 forward's tolerances (1e-4 fp32 inputs, 1e-2 bf16 inputs)."""
 import numpy as np
@@ -28,7 +28,7 @@ def W(dtype="bf16", H=2, dk=64, dv=64, L=4, lengths=(150, 1, 0, 70), seed=71, g_
                     lengths=list(lengths), g_mu=g_mu)
 
 
-def run(inp, with_state=True, seed=4, chains=None):
+def run(inp, with_state=True, seed=4, chains=None, residual="linear"):
     import torch
     from gated_delta_rule_prologue_amd import binding
     from tests.test_gpu_state import dev_tensor
@@ -48,9 +48,10 @@ def run(inp, with_state=True, seed=4, chains=None):
     got = binding.bwd(dev["q"], dev["k"], dev["v"], dev["u"], dev["g"], dev["b"], dev["a"], dev["h"],
                       dev["conv_w"], dev["cu_seqlens"], inp.L, dev_tensor(d_o_store),
                       dS_final=None if dsf is None else dev_tensor(dsf),
-                      S_init=None if S0 is None else dev_tensor(S0))
+                      S_init=None if S0 is None else dev_tensor(S0), residual=residual)
     torch.cuda.synchronize()
-    ref = oracle.bwd(inp, d_o.astype(np.float64), dS_final=dsf, S_init=S0, chains=chains)
+    ref = oracle.bwd(inp, d_o.astype(np.float64), dS_final=dsf, S_init=S0, chains=chains,
+                     residual=residual)
     return {n: (None if got[n] is None else got[n].cpu().numpy().astype(np.float64)) for n in NAMES}, ref
 
 
@@ -117,3 +118,20 @@ def test_bwd_lm_layer_sampled_chains():
     masks["S_init"] = smask
     ref["conv_w"] = None
     check(got, ref, "bf16", masks)
+
+
+GELU_CASES = [
+    W(dtype="f32", dk=64, dv=64, L=4, lengths=(130, 1, 64, 0, 5)),
+    W(dtype="bf16", dk=128, dv=128, L=5, lengths=(200, 65)),
+]
+
+
+@pytest.mark.parametrize("w", GELU_CASES, ids=lambda w: f"{w.dtype}-dk{w.dk}-dv{w.dv}-L{w.L}")
+def test_bwd_gelu_matches_oracle(w):
+    """The GELU refinement chain r_{l+1} = r_l - a_l GELU(h_l r_l), with the
+    residual levels amplified so that they carry the write key."""
+    from tests.test_gpu_gelu import amplify
+    inp = amplify(make_inputs(w))
+    say(f"bwd gelu {w}")
+    got, ref = run(inp, residual="gelu")
+    check(got, ref, w.dtype)

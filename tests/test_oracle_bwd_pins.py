@@ -1,4 +1,5 @@
-"""Pins of the oracle's backward pass (closed-form residual chain).
+"""Pins of the oracle's backward pass (closed-form residual chain, and the
+non-linear refinement chain r_{l+1} = r_l - a_l GELU(h_l r_l)).
 
 The backward is reverse-mode differentiation of the forward recurrence; it is
 checked against (1) central finite differences of the fp64 forward oracle,
@@ -30,20 +31,21 @@ def upstream(inp, seed=3):
     return d_o, dsf
 
 
-def loss(inp, d_o, dsf, S_init=None):
-    o, s = oracle.fwd(inp, S_init=S_init)
+def loss(inp, d_o, dsf, S_init=None, residual="linear"):
+    o, s = oracle.fwd(inp, S_init=S_init, residual=residual)
     return float(np.sum(o * d_o) + np.sum(s * dsf))
 
 
-@pytest.mark.parametrize("L", [1, 2, 4])
-def test_backward_matches_finite_differences(L):
+@pytest.mark.parametrize("L,residual", [(1, "linear"), (2, "linear"), (4, "linear"),
+                                        (3, "gelu"), (4, "gelu")])
+def test_backward_matches_finite_differences(L, residual):
     """Every input element, central differences with steps of 2^-10 (exact in
     fp32 for these magnitudes), against the fp64 forward."""
     inp = small(L=L)
     d_o, dsf = upstream(inp)
     rng = np.random.default_rng(8)
     S0 = 0.3 * rng.standard_normal((inp.n_seqs, inp.heads, inp.dk, inp.dv))
-    grads = oracle.bwd(inp, d_o, dS_final=dsf, S_init=S0)
+    grads = oracle.bwd(inp, d_o, dS_final=dsf, S_init=S0, residual=residual)
     hstep = 2.0 ** -10
     for name in FIELDS:
         x = getattr(inp, name)
@@ -54,8 +56,8 @@ def test_backward_matches_finite_differences(L):
             xp, xm = x.copy(), x.copy()
             xp[idx] += np.float32(hstep)
             xm[idx] -= np.float32(hstep)
-            lp = loss(dataclasses.replace(inp, **{name: xp}), d_o, dsf, S0)
-            lm = loss(dataclasses.replace(inp, **{name: xm}), d_o, dsf, S0)
+            lp = loss(dataclasses.replace(inp, **{name: xp}), d_o, dsf, S0, residual)
+            lm = loss(dataclasses.replace(inp, **{name: xm}), d_o, dsf, S0, residual)
             fd[idx] = (lp - lm) / (2 * hstep)
         err = np.max(np.abs(fd - grads[name])) / max(np.max(np.abs(fd)), 1e-12)
         assert err < 1e-4, (name, err)
@@ -64,12 +66,13 @@ def test_backward_matches_finite_differences(L):
         sp, sm = S0.copy(), S0.copy()
         sp[idx] += 0.5
         sm[idx] -= 0.5
-        fd = loss(inp, d_o, dsf, sp) - loss(inp, d_o, dsf, sm)
+        fd = loss(inp, d_o, dsf, sp, residual) - loss(inp, d_o, dsf, sm, residual)
         assert abs(fd - grads["S_init"][idx]) < 1e-9 * max(1.0, abs(fd))
 
 
-def torch_forward(inp, tensors, S0):
-    """Token-by-token forward in torch fp64 (closed-form chain), independent of the oracle."""
+def torch_forward(inp, tensors, S0, residual="linear"):
+    """Token-by-token forward in torch fp64 (either chain; torch's exact erf
+    GELU), independent of the oracle."""
     import torch
     q, k, v, u, g, b, a, h, w = (tensors[n] for n in FIELDS)
     cu = inp.cu_seqlens
@@ -87,7 +90,10 @@ def torch_forward(inp, tensors, S0):
                 kw = b[t, e] * k[t, e]
                 for s in range(inp.L - 1):
                     kw = kw + a[t, e, s] * r * u[t, e, s]
-                    r = r * (1 - a[t, e, s] * h[t, e, s])
+                    if residual == "gelu":
+                        r = r - a[t, e, s] * torch.nn.functional.gelu(h[t, e, s] * r)
+                    else:
+                        r = r * (1 - a[t, e, s] * h[t, e, s])
                 p = S.T @ k[t, e]
                 S = g[t, e] * (S - b[t, e] * torch.outer(k[t, e], p)) + torch.outer(kw, v[t, e])
                 outs.append(((t, e), S.T @ q[t, e]))
@@ -95,8 +101,9 @@ def torch_forward(inp, tensors, S0):
     return outs, finals
 
 
-@pytest.mark.parametrize("L", [1, 3, 5])
-def test_backward_matches_torch_autograd(L):
+@pytest.mark.parametrize("L,residual", [(1, "linear"), (3, "linear"), (5, "linear"),
+                                        (3, "gelu"), (5, "gelu")])
+def test_backward_matches_torch_autograd(L, residual):
     torch = pytest.importorskip("torch")
     inp = small(L=L, lengths=(9, 2, 5), dk=5, dv=4)
     d_o, dsf = upstream(inp, seed=5)
@@ -110,11 +117,11 @@ def test_backward_matches_torch_autograd(L):
         for n in ("u", "a", "h"):
             tensors[n] = torch.zeros((inp.total_tokens, inp.heads, 0, inp.dk), dtype=torch.float64)
     S0t = torch.tensor(S0, requires_grad=True)
-    outs, finals = torch_forward(inp, tensors, S0t)
+    outs, finals = torch_forward(inp, tensors, S0t, residual)
     total = sum((o * torch.tensor(d_o[te])).sum() for te, o in outs)
     total = total + sum((s * torch.tensor(dsf[ne])).sum() for ne, s in finals)
     total.backward()
-    grads = oracle.bwd(inp, d_o, dS_final=dsf, S_init=S0)
+    grads = oracle.bwd(inp, d_o, dS_final=dsf, S_init=S0, residual=residual)
     for n in FIELDS:
         if getattr(inp, n) is None:
             continue
