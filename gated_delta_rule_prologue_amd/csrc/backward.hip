@@ -102,7 +102,9 @@ __global__ __launch_bounds__(64) void scan_bwd_kernel(
     constexpr int VPT = kCols / VE;              // 16-byte vectors of one token's 8 columns
     constexpr int VV = SUB * VPT;                // ... of a sub-chunk
     static_assert(KV % 64 == 0 && 2 * VV <= 64, "staging layout");
-    __shared__ uint4 sK[KV], sW[KV], sQ[KV], sV[VV], sD[VV];
+    // a sub-chunk's rows, widened to fp32 once when staged
+    __shared__ __attribute__((aligned(16))) float sK[SUB * DK], sW[SUB * DK], sQ[SUB * DK];
+    __shared__ __attribute__((aligned(16))) float sV[SUB * kCols], sD[SUB * kCols];
     __shared__ float sG[SUB], sB[SUB];
 
     const int lane = threadIdx.x;
@@ -157,27 +159,42 @@ __global__ __launch_bounds__(64) void scan_bwd_kernel(
         const int tg = min(c + (lane % SUB), last);
         P.gb = lane < 2 * SUB ? ld(lane < SUB ? g : b, (int64_t)tg * H + e) : 0.f;
     };
+    // 16 bytes of T at element idx * VE of dst, as fp32
+    auto put = [](float* dst, int idx, const uint4& raw) {
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+        float4* d4 = reinterpret_cast<float4*>(dst + idx * VE);
+        if constexpr (sizeof(T) == 2) {
+            d4[0] = make_float4(__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                                __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u));
+            d4[1] = make_float4(__uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xffff0000u),
+                                __uint_as_float(w[3] << 16), __uint_as_float(w[3] & 0xffff0000u));
+        } else {
+            d4[0] = make_float4(__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]),
+                                __uint_as_float(w[3]));
+        }
+    };
     auto pre_store = [&](const Pre& P, bool back) {
 #pragma unroll
         for (int x = 0; x < KPL; ++x) {
-            sK[lane + 64 * x] = P.k[x];
-            sW[lane + 64 * x] = P.w[x];
+            put(sK, lane + 64 * x, P.k[x]);
+            put(sW, lane + 64 * x, P.w[x]);
             if (back)
-                sQ[lane + 64 * x] = P.q[x];
+                put(sQ, lane + 64 * x, P.q[x]);
         }
         if (lane < VV)
-            sV[lane] = P.vd;
+            put(sV, lane, P.vd);
         else if (back && lane < 2 * VV)
-            sD[lane - VV] = P.vd;
+            put(sD, lane - VV, P.vd);
         if (lane < SUB)
             sG[lane] = P.gb;
         else if (lane < 2 * SUB)
             sB[lane - SUB] = P.gb;
     };
-    auto at = [](const uint4* base, int i) { return to_f32(reinterpret_cast<const T*>(base)[i]); };
+    auto at = [](const float* base, int i) { return base[i]; };
 
-    // ---- forward token j of the staged sub-chunk: S <- g (S - b k p^T) + kw v^T
-    auto fapply = [&](int j) {
+    // ---- forward token j of the staged sub-chunk: So <- g (Si - b k p^T) + kw v^T
+    // (So may be Si)
+    auto fapply = [&](int j, const float (&Si)[EL], float (&So)[EL]) {
         float kk[RPT], ww[RPT], vv[2];
 #pragma unroll
         for (int r = 0; r < RPT; ++r) {
@@ -194,20 +211,28 @@ __global__ __launch_bounds__(64) void scan_bwd_kernel(
             float acc = 0.f;
 #pragma unroll
             for (int r = 0; r < RPT; ++r)
-                acc += S[r * 2 + c] * kk[r];
+                acc += Si[r * 2 + c] * kk[r];
             p[c] = sum_rowgroups(acc);
         }
 #pragma unroll
         for (int r = 0; r < RPT; ++r)
 #pragma unroll
             for (int c = 0; c < 2; ++c)
-                S[r * 2 + c] = gt * (S[r * 2 + c] - bt * kk[r] * p[c]) + ww[r] * vv[c];
+                So[r * 2 + c] = gt * (Si[r * 2 + c] - bt * kk[r] * p[c]) + ww[r] * vv[c];
     };
 
-    // ---- backward token t = c + j of the staged sub-chunk; Sm = S_{t-1}, S = S_t on entry
-    auto bapply = [&](int c0, int j, const float (&Sm)[EL]) {
+    // fp32 atomics into one token's row of dk floats: a buffer resource over the
+    // row and a fixed lane offset, so no per-atomic address arithmetic
+    auto row_rsrc = [&](float* base, int64_t rk) {
+        return __builtin_amdgcn_make_buffer_rsrc(base + rk, 0, DK * 4, 0x00020000);
+    };
+    const int aoff = rg * 4;
+
+    // ---- backward token t = c + j of the staged sub-chunk; St = S_t, Sm = S_{t-1}
+    auto bapply = [&](int c0, int j, const float (&St)[EL], const float (&Sm)[EL]) {
         const int t = c0 + j;
         const int64_t rk = ((int64_t)t * H + e) * DK, rv = ((int64_t)t * H + e) * DV + j0;
+        const auto rq = row_rsrc(dq, rk), rw = row_rsrc(dkw, rk), rkk = row_rsrc(dk, rk);
         float kk[RPT], qq[RPT], ww[RPT], vv[2], dd[2];
 #pragma unroll
         for (int r = 0; r < RPT; ++r) {
@@ -228,14 +253,14 @@ __global__ __launch_bounds__(64) void scan_bwd_kernel(
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 G[r * 2 + c] += qq[r] * dd[c];
-                aq += S[r * 2 + c] * dd[c];
+                aq += St[r * 2 + c] * dd[c];
                 aw += G[r * 2 + c] * vv[c];
             }
             aq = sum_quad(aq);
             aw = sum_quad(aw);
             if (cp == 0) {
-                atomicAdd(dq + rk + rg + 16 * r, aq);
-                atomicAdd(dkw + rk + rg + 16 * r, aw);
+                __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(aq, rq, aoff + 64 * r, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(aw, rw, aoff + 64 * r, 0, 0);
             }
         }
         // dv = G^T kw; p = S_{t-1}^T k (column sums over the dk rows)
@@ -288,11 +313,8 @@ __global__ __launch_bounds__(64) void scan_bwd_kernel(
             }
             a1 = sum_quad(a1);
             if (cp == 0)
-                atomicAdd(dk + rk + rg + 16 * r, -bt * a1);
+                __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(-bt * a1, rkk, aoff + 64 * r, 0, 0);
         }
-#pragma unroll
-        for (int x = 0; x < EL; ++x)
-            S[x] = Sm[x];
     };
 
     // sweep 1: S at every sub-chunk start, into the checkpoints
@@ -313,7 +335,7 @@ __global__ __launch_bounds__(64) void scan_bwd_kernel(
 #pragma unroll
         for (int j = 0; j < SUB; ++j)
             if (j < len)
-                fapply(j);
+                fapply(j, S, S);
     }
 
     // sweep 2: sub-chunks from the last; each one's states recomputed into
@@ -331,10 +353,10 @@ __global__ __launch_bounds__(64) void scan_bwd_kernel(
         lds_barrier();
         pre_store(P, true);
         lds_barrier();
-        float Ss[SUB][EL];                       // Ss[j] = S before token c0 + j
+        float Ss[SUB + 1][EL];                   // Ss[j] = S before token c0 + j
 #pragma unroll
         for (int x = 0; x < EL; ++x)
-            S[x] = Cn[x];
+            Ss[0][x] = Cn[x];
         if (m > 0) {
             pre_load(c0 - SUB, true, P);
             const float* cpt = ckpt_at(c0 - SUB);
@@ -343,17 +365,13 @@ __global__ __launch_bounds__(64) void scan_bwd_kernel(
                 Cn[x] = cpt[x * 64];
         }
 #pragma unroll
-        for (int j = 0; j < SUB; ++j) {
-#pragma unroll
-            for (int x = 0; x < EL; ++x)
-                Ss[j][x] = S[x];
+        for (int j = 0; j < SUB; ++j)
             if (j < len)
-                fapply(j);
-        }
+                fapply(j, Ss[j], Ss[j + 1]);
 #pragma unroll
         for (int j = SUB - 1; j >= 0; --j)
             if (j < len)
-                bapply(c0, j, Ss[j]);
+                bapply(c0, j, Ss[j + 1], Ss[j]);
     }
     if (dS_init) {
 #pragma unroll
