@@ -384,6 +384,11 @@ __global__ __launch_bounds__(64) void scan_bwd_kernel(
 
 // One thread per (head e, channel i, block of 64 tokens): for each token of the
 // block, the write key backwards.  dkw (fp32) comes from the scan backward.
+// The thread also runs the chain backward for the three tokens after its block,
+// so every contribution to dk of its block's tokens (b k and the four taps of
+// the tokens that read them) is summed in registers and added to dk, which
+// already holds the scan's part, with one read-modify-write: no other thread
+// of this kernel touches those elements.
 template <typename T>
 __global__ __launch_bounds__(256) void write_key_bwd_kernel(
     const T* __restrict__ k, const T* __restrict__ u, const T* __restrict__ a,
@@ -413,74 +418,98 @@ __global__ __launch_bounds__(256) void write_key_bwd_kernel(
     }
     int sn = lo;
     float dw[4] = {0.f, 0.f, 0.f, 0.f};
+    // dr_0 of tokens t-3 .. t and the end of the sequence each belongs to
+    float dr[4] = {0.f, 0.f, 0.f, 0.f};
+    int se[4] = {-1, -1, -1, -1};
     const int64_t lrow = (int64_t)H * (L - 1) * DK;
-    for (int t = t_lo; t < t_hi; ++t) {
-        while (cu[sn + 1] <= t)
-            ++sn;                                // the sequence holding t (skips empty ones)
-        const int s0 = cu[sn];
-        const int64_t rk = ((int64_t)t * H + e) * DK + i;
-        const float g_kw = dkw[rk];
-        const float kt = ld(k, rk), bt = ld(b, (int64_t)t * H + e);
-        // b k part of the key
-        atomicAdd(dk + rk, bt * g_kw);
-        float dbp = g_kw * kt;
-        for (int o = 32; o > 0; o >>= 1)         // one atomic per wavefront: its lanes are
-            dbp += __shfl_xor(dbp, o);           // 64 channels of one (token, head) when DK >= 64
-        if (DK >= 64) {
-            if ((threadIdx.x & 63) == 0)
-                atomicAdd(db + (int64_t)t * H + e, dbp);
-        } else {
-            atomicAdd(db + (int64_t)t * H + e, g_kw * kt);
-        }
-        if (L == 1)
-            continue;
-        float kx[4];
+    for (int t = t_lo; t < t_hi + 3; ++t) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int tau = t - 3 + m;
-            kx[m] = tau >= s0 ? ld(k, ((int64_t)tau * H + e) * DK + i) : 0.f;
+        for (int x = 0; x < 3; ++x) {
+            dr[x] = dr[x + 1];
+            se[x] = se[x + 1];
         }
-        const float r0 = w[0] * kx[0] + w[1] * kx[1] + w[2] * kx[2] + w[3] * kx[3];
-        // residuals r_l, l = 1 .. L-1 (the closed form as a running product, or
-        // the GELU refinement chain)
-        float r[16];
-        r[1] = r0;
-        const int64_t lb = (int64_t)t * lrow + (int64_t)e * (L - 1) * DK + i;
-        for (int l = 1; l < L - 1; ++l) {
-            const float al = ld(a, lb + (int64_t)(l - 1) * DK), hl = ld(h, lb + (int64_t)(l - 1) * DK);
-            r[l + 1] = gelu ? r[l] - al * gelu_as(hl * r[l]) : r[l] * (1.f - al * hl);
-        }
-        float dr_next = 0.f;
-        for (int l = L - 1; l >= 1; --l) {
-            const int64_t sl = lb + (int64_t)(l - 1) * DK;
-            const float al = ld(a, sl), ul = ld(u, sl), hl = ld(h, sl);
-            du[sl] = g_kw * al * r[l];
-            float dal = g_kw * ul * r[l], dhl = 0.f, drl = g_kw * al * ul;
-            if (l <= L - 2) {
-                if (gelu) {                      // r_{l+1} = r_l - a_l GELU(h_l r_l)
-                    float gp;
-                    const float gv = gelu_as_grad(hl * r[l], gp);
-                    dal -= dr_next * gv;
-                    dhl = -dr_next * al * r[l] * gp;
-                    drl += dr_next * (1.f - al * hl * gp);
-                } else {                         // r_{l+1} = r_l (1 - a_l h_l)
-                    dal -= dr_next * hl * r[l];
-                    dhl = -dr_next * al * r[l];
-                    drl += dr_next * (1.f - al * hl);
+        dr[3] = 0.f;
+        se[3] = -1;
+        if (t < T_total) {
+            while (cu[sn + 1] <= t)
+                ++sn;                            // the sequence holding t (skips empty ones)
+            const int s0 = cu[sn];
+            se[3] = cu[sn + 1];
+            const bool own = t < t_hi;
+            const int64_t rk = ((int64_t)t * H + e) * DK + i;
+            const float g_kw = dkw[rk];
+            if (own) {                           // db from the b k part of the key
+                const float kt = ld(k, rk);
+                float dbp = g_kw * kt;
+                for (int o = 32; o > 0; o >>= 1) // one atomic per wavefront: its lanes are
+                    dbp += __shfl_xor(dbp, o);   // 64 channels of one (token, head) when DK >= 64
+                if (DK >= 64) {
+                    if ((threadIdx.x & 63) == 0)
+                        atomicAdd(db + (int64_t)t * H + e, dbp);
+                } else {
+                    atomicAdd(db + (int64_t)t * H + e, g_kw * kt);
                 }
             }
-            da[sl] = dal;
-            dh[sl] = dhl;
-            dr_next = drl;
-        }
-        // the taps: dw_m += dr_0 k_{t-3+m}, dk_{t-3+m} += w_m dr_0 inside the sequence
+            if (L > 1) {
+                float kx[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int tau = t - 3 + m;
-            if (tau < s0)
-                continue;
-            dw[m] += dr_next * kx[m];
-            atomicAdd(dk + ((int64_t)tau * H + e) * DK + i, w[m] * dr_next);
+                for (int m = 0; m < 4; ++m) {
+                    const int tau = t - 3 + m;
+                    kx[m] = tau >= s0 ? ld(k, ((int64_t)tau * H + e) * DK + i) : 0.f;
+                }
+                const float r0 = w[0] * kx[0] + w[1] * kx[1] + w[2] * kx[2] + w[3] * kx[3];
+                // residuals r_l, l = 1 .. L-1 (the closed form as a running product, or
+                // the GELU refinement chain)
+                float r[16];
+                r[1] = r0;
+                const int64_t lb = (int64_t)t * lrow + (int64_t)e * (L - 1) * DK + i;
+                for (int l = 1; l < L - 1; ++l) {
+                    const float al = ld(a, lb + (int64_t)(l - 1) * DK), hl = ld(h, lb + (int64_t)(l - 1) * DK);
+                    r[l + 1] = gelu ? r[l] - al * gelu_as(hl * r[l]) : r[l] * (1.f - al * hl);
+                }
+                float dr_next = 0.f;
+                for (int l = L - 1; l >= 1; --l) {
+                    const int64_t sl = lb + (int64_t)(l - 1) * DK;
+                    const float al = ld(a, sl), ul = ld(u, sl), hl = ld(h, sl);
+                    float dal = g_kw * ul * r[l], dhl = 0.f, drl = g_kw * al * ul;
+                    if (l <= L - 2) {
+                        if (gelu) {              // r_{l+1} = r_l - a_l GELU(h_l r_l)
+                            float gp;
+                            const float gv = gelu_as_grad(hl * r[l], gp);
+                            dal -= dr_next * gv;
+                            dhl = -dr_next * al * r[l] * gp;
+                            drl += dr_next * (1.f - al * hl * gp);
+                        } else {                 // r_{l+1} = r_l (1 - a_l h_l)
+                            dal -= dr_next * hl * r[l];
+                            dhl = -dr_next * al * r[l];
+                            drl += dr_next * (1.f - al * hl);
+                        }
+                    }
+                    if (own) {
+                        du[sl] = g_kw * al * r[l];
+                        da[sl] = dal;
+                        dh[sl] = dhl;
+                    }
+                    dr_next = drl;
+                }
+                dr[3] = dr_next;                 // dr_0 of token t
+                if (own) {                       // the taps: dw_m += dr_0 k_{t-3+m}
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+                        dw[m] += dr_next * kx[m];
+                }
+            }
+        }
+        // dk of token tau = t - 3: b dkw, and w_{3-d} dr_0 of token tau + d in its sequence
+        const int tau = t - 3;
+        if (tau >= t_lo) {
+            const int64_t rt = ((int64_t)tau * H + e) * DK + i;
+            float acc = ld(b, (int64_t)tau * H + e) * dkw[rt] + w[3] * dr[0];
+#pragma unroll
+            for (int dd = 1; dd < 4; ++dd)
+                if (se[dd] == se[0])
+                    acc += w[3 - dd] * dr[dd];
+            dk[rt] += acc;
         }
     }
     if (L > 1)
