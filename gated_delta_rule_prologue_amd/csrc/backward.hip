@@ -22,7 +22,7 @@
 //     inputs are fetched one sub-chunk ahead with 16-byte loads and staged in
 //     LDS.  Row sums (over the 8 columns) go to fp32 atomics into dq, dk and
 //     dkw, which the value slices of a chain share.
-//   * write_key_bwd_kernel: one thread per (head, channel, block of 64 tokens):
+//   * write_key_bwd_kernel: one thread per (head, channel, block of 16 tokens):
 //     the residual chain (closed form or GELU refinement) backwards (du, da, dh written, dr_0 formed), b and
 //     the taps (dk, db through atomics; dconv_w summed over the block first).
 #include "common.h"
@@ -31,7 +31,7 @@
 namespace prism {
 namespace bwd {
 
-constexpr int kC = 64;                           // token block of the write-key backward
+constexpr int kC = 16;                           // token block of the write-key backward
 constexpr int kCols = 8;                         // value columns per wavefront of the scan backward
 
 // tokens per checkpoint of the scan backward: one sub-chunk's states stay in
@@ -382,18 +382,18 @@ __global__ __launch_bounds__(64) void scan_bwd_kernel(
     }
 }
 
-// One thread per (head e, channel i, block of 64 tokens): for each token of the
+// One thread per (head e, channel i, block of 16 tokens): for each token of the
 // block, the write key backwards.  dkw (fp32) comes from the scan backward.
 // The thread also runs the chain backward for the three tokens after its block,
 // so every contribution to dk of its block's tokens (b k and the four taps of
 // the tokens that read them) is summed in registers and added to dk, which
 // already holds the scan's part, with one read-modify-write: no other thread
 // of this kernel touches those elements.
-template <typename T>
+template <typename T, int L>
 __global__ __launch_bounds__(256) void write_key_bwd_kernel(
     const T* __restrict__ k, const T* __restrict__ u, const T* __restrict__ a,
     const T* __restrict__ h, const T* __restrict__ b, const T* __restrict__ conv_w,
-    const int32_t* __restrict__ cu, int n_seqs, int T_total, int H, int DK, int L, bool gelu,
+    const int32_t* __restrict__ cu, int n_seqs, int T_total, int H, int DK, bool gelu,
     const float* __restrict__ dkw, float* __restrict__ dk, float* __restrict__ du,
     float* __restrict__ da, float* __restrict__ dh, float* __restrict__ db,
     float* __restrict__ dconv_w)
@@ -417,6 +417,7 @@ __global__ __launch_bounds__(256) void write_key_bwd_kernel(
         if (cu[mid] <= t_lo) lo = mid; else hi = mid;
     }
     int sn = lo;
+    int s0 = cu[sn], s1 = cu[sn + 1];            // bounds of the sequence holding t
     float dw[4] = {0.f, 0.f, 0.f, 0.f};
     // dr_0 of tokens t-3 .. t and the end of the sequence each belongs to
     float dr[4] = {0.f, 0.f, 0.f, 0.f};
@@ -431,10 +432,12 @@ __global__ __launch_bounds__(256) void write_key_bwd_kernel(
         dr[3] = 0.f;
         se[3] = -1;
         if (t < T_total) {
-            while (cu[sn + 1] <= t)
-                ++sn;                            // the sequence holding t (skips empty ones)
-            const int s0 = cu[sn];
-            se[3] = cu[sn + 1];
+            while (s1 <= t) {                    // the sequence holding t (skips empty ones)
+                ++sn;
+                s0 = s1;
+                s1 = cu[sn + 1];
+            }
+            se[3] = s1;
             const bool own = t < t_hi;
             const int64_t rk = ((int64_t)t * H + e) * DK + i;
             const float g_kw = dkw[rk];
@@ -450,7 +453,7 @@ __global__ __launch_bounds__(256) void write_key_bwd_kernel(
                     atomicAdd(db + (int64_t)t * H + e, g_kw * kt);
                 }
             }
-            if (L > 1) {
+            if constexpr (L > 1) {
                 float kx[4];
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
@@ -460,14 +463,16 @@ __global__ __launch_bounds__(256) void write_key_bwd_kernel(
                 const float r0 = w[0] * kx[0] + w[1] * kx[1] + w[2] * kx[2] + w[3] * kx[3];
                 // residuals r_l, l = 1 .. L-1 (the closed form as a running product, or
                 // the GELU refinement chain)
-                float r[16];
+                float r[L];
                 r[1] = r0;
                 const int64_t lb = (int64_t)t * lrow + (int64_t)e * (L - 1) * DK + i;
+#pragma unroll
                 for (int l = 1; l < L - 1; ++l) {
                     const float al = ld(a, lb + (int64_t)(l - 1) * DK), hl = ld(h, lb + (int64_t)(l - 1) * DK);
                     r[l + 1] = gelu ? r[l] - al * gelu_as(hl * r[l]) : r[l] * (1.f - al * hl);
                 }
                 float dr_next = 0.f;
+#pragma unroll
                 for (int l = L - 1; l >= 1; --l) {
                     const int64_t sl = lb + (int64_t)(l - 1) * DK;
                     const float al = ld(a, sl), ul = ld(u, sl), hl = ld(h, sl);
@@ -512,7 +517,7 @@ __global__ __launch_bounds__(256) void write_key_bwd_kernel(
             dk[rt] += acc;
         }
     }
-    if (L > 1)
+    if constexpr (L > 1)
 #pragma unroll
         for (int m = 0; m < 4; ++m)
             atomicAdd(dconv_w + ((int64_t)e * DK + i) * 4 + m, dw[m]);
@@ -534,6 +539,42 @@ size_t bwd_workspace_floats(int n_seqs, int total_tokens, int heads, int dk, int
 }
 
 bool bwd_supported(int dk, int dv) { return (dk == 64 || dk == 128) && (dv == 64 || dv == 128); }
+
+template <typename T, int L>
+static hipError_t launch_wk_L(const BwdArgs& p, const float* dkw, dim3 grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((bwd::write_key_bwd_kernel<T, L>), grid, dim3(256), 0, s, (const T*)p.k,
+                       (const T*)p.u, (const T*)p.a, (const T*)p.h, (const T*)p.b,
+                       (const T*)p.conv_w, p.cu_seqlens, p.n_seqs, p.total_tokens, p.heads, p.dk,
+                       p.gelu, dkw, p.gk, p.gu, p.ga, p.gh, p.gb, p.gconv);
+    return hipGetLastError();
+}
+
+// The level count as a template parameter: the chain loops unroll and each
+// token's loads issue together.
+template <typename T>
+static hipError_t launch_wk(const BwdArgs& p, const float* dkw, dim3 grid, hipStream_t s)
+{
+    switch (p.L) {
+    case 1: return launch_wk_L<T, 1>(p, dkw, grid, s);
+    case 2: return launch_wk_L<T, 2>(p, dkw, grid, s);
+    case 3: return launch_wk_L<T, 3>(p, dkw, grid, s);
+    case 4: return launch_wk_L<T, 4>(p, dkw, grid, s);
+    case 5: return launch_wk_L<T, 5>(p, dkw, grid, s);
+    case 6: return launch_wk_L<T, 6>(p, dkw, grid, s);
+    case 7: return launch_wk_L<T, 7>(p, dkw, grid, s);
+    case 8: return launch_wk_L<T, 8>(p, dkw, grid, s);
+    case 9: return launch_wk_L<T, 9>(p, dkw, grid, s);
+    case 10: return launch_wk_L<T, 10>(p, dkw, grid, s);
+    case 11: return launch_wk_L<T, 11>(p, dkw, grid, s);
+    case 12: return launch_wk_L<T, 12>(p, dkw, grid, s);
+    case 13: return launch_wk_L<T, 13>(p, dkw, grid, s);
+    case 14: return launch_wk_L<T, 14>(p, dkw, grid, s);
+    case 15: return launch_wk_L<T, 15>(p, dkw, grid, s);
+    case 16: return launch_wk_L<T, 16>(p, dkw, grid, s);
+    default: return hipErrorInvalidValue;
+    }
+}
 
 template <typename T, int DK>
 static hipError_t launch_bwd_T(const BwdArgs& p, hipStream_t s)
@@ -565,11 +606,7 @@ static hipError_t launch_bwd_T(const BwdArgs& p, hipStream_t s)
     if ((err = hipGetLastError()) != hipSuccess || T_ == 0)
         return err;
     const int64_t threads = ((int64_t)(T_ + bwd::kC - 1) / bwd::kC) * H * DK;
-    hipLaunchKernelGGL((bwd::write_key_bwd_kernel<T>), dim3((unsigned)((threads + 255) / 256)),
-                       dim3(256), 0, s, (const T*)p.k, (const T*)p.u, (const T*)p.a,
-                       (const T*)p.h, (const T*)p.b, (const T*)p.conv_w, p.cu_seqlens, p.n_seqs,
-                       T_, H, DK, p.L, p.gelu, dkw, p.gk, p.gu, p.ga, p.gh, p.gb, p.gconv);
-    return hipGetLastError();
+    return launch_wk<T>(p, dkw, dim3((unsigned)((threads + 255) / 256)), s);
 }
 
 hipError_t launch_bwd(const BwdArgs& p, hipStream_t s)
