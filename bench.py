@@ -132,6 +132,21 @@ def cpu_baseline(inp, o_gpu, s_gpu):
              "checked": "last timed step, every element"})
 
 
+def oracle_timed(fn, units, unit, sample, min_seconds=2.0, max_passes=50):
+    """The fp64 oracle as it is, timed on the host cores beside a GPU row: fn()
+    repeated until about min_seconds have been measured; units of work per call."""
+    import oracle
+    reps, spent = 0, 0.0
+    while reps == 0 or (spent < min_seconds and reps < max_passes):
+        t0 = time.perf_counter()
+        fn()
+        spent += time.perf_counter() - t0
+        reps += 1
+    dt = spent / reps
+    return {"value": units / dt, "unit": unit, "cores": oracle.default_threads(), "kind": "oracle",
+            "sample": f"{sample}; mean of {reps} passes", "seconds": dt, "passes": reps}
+
+
 def decode_bytes(n, H, dk, dv, L, esize):
     """Algorithmic HBM bytes of one decode step over n sequences: the fp32 state
     read and written (8 dk dv per chain) plus, per chain, e [q, k (2 dk), v (dv),
@@ -152,7 +167,7 @@ def raw_args(*xs):
     return [None if x is None else (x.data_ptr() if hasattr(x, "data_ptr") else x) for x in xs]
 
 
-def decode_bench(steps, warmup):
+def decode_bench(steps, warmup, with_oracle=False):
     """Time prism_decode_step on each serving batch.  Inputs, states and
     histories are rotated over enough copies that a step's working set is not
     left in the 256 MB Infinity Cache by the step before."""
@@ -238,6 +253,14 @@ def decode_bench(steps, warmup):
                          "algorithmic_bytes": nbytes},
             "state_copies": ncopy,
         }
+        if with_oracle:
+            import numpy as np
+            import oracle
+            S0 = np.zeros((n, H, dk, dv))
+            h0 = np.zeros((n, H, 3, dk), dtype=np.uint16)
+            out[name]["cpu_baseline"] = oracle_timed(
+                lambda: oracle.decode_step(step, S0, h0), n, "tokens/s",
+                f"the whole batch: one decode step of all {n * H} (sequence, head) chains, fp64")
     return out
 
 
@@ -261,7 +284,7 @@ def bwd_flops(w, T):
     return 37 * T * w.heads * w.dk * w.dv
 
 
-def bwd_bench(w, inp, dev_copies, steps, warmup):
+def bwd_bench(w, inp, dev_copies, steps, warmup, with_oracle=False):
     """Time prism_bwd (gradients of every input) on the workload, with the
     upstream gradient dO and no carried state."""
     import ctypes
@@ -304,13 +327,29 @@ def bwd_bench(w, inp, dev_copies, steps, warmup):
     flops = bwd_flops(w, T)
     ach = nbytes / (ms * 1e-3) / 1e9
     tf = flops / (ms * 1e-3) / 1e12
-    return {"tokens_per_s": steps * T / elapsed, "us_per_call": ms * 1e3,
+    res = {"tokens_per_s": steps * T / elapsed, "us_per_call": ms * 1e3,
             "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_VALU_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": tf / FP32_VALU_PEAK_TFLOPS, "traffic": None,
                          "kernel": "backward (all launches)", "avg_launch_us": ms * 1e3,
                          "algorithmic_flops": flops},
             "hbm": {"achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": ach / HBM_PEAK_GBS, "algorithmic_bytes": nbytes}}
+    if with_oracle:
+        # a bounded sample: as many whole (sequence, head) chains as host threads
+        # (the oracle keeps every state of a chain), scaled to tokens/s of the
+        # workload by the chains' share of its head-tokens
+        import numpy as np
+        import oracle
+        nch = min(inp.n_seqs * H, oracle.default_threads())
+        chains = list(range(nch))
+        lens = np.diff(inp.cu_seqlens)
+        ht = int(sum(lens[c // H] for c in chains))
+        d_o = np.random.default_rng(7).standard_normal((T, H, w.dv))
+        res["cpu_baseline"] = oracle_timed(
+            lambda: oracle.bwd(inp, d_o, chains=chains), ht / H, "tokens/s",
+            f"{nch} whole (sequence, head) chains ({ht} head-tokens) of the workload, fp64, one "
+            f"thread per chain; tokens/s = head-tokens/s / H", min_seconds=1.0, max_passes=5)
+    return res
 
 
 def main():
@@ -459,9 +498,11 @@ def main():
     }
     out["roofline"]["kernel"] = dominant["kernel"]
     if not args.no_backward:
-        out["backward"] = bwd_bench(w, inp, copies[:2], max(5, K // 5), 2)
+        out["backward"] = bwd_bench(w, inp, copies[:2], max(5, K // 5), 2,
+                                    with_oracle=not args.no_cpu_baseline)
     if not args.no_decode:
-        out["decode"] = decode_bench(max(20, K), max(5, args.warmup))
+        out["decode"] = decode_bench(max(20, K), max(5, args.warmup),
+                                     with_oracle=not args.no_cpu_baseline)
     # last copy kernels of the run: the reference for the counter calibration
     if args.calibrate_copy_mib:
         nb = args.calibrate_copy_mib << 20
@@ -473,6 +514,10 @@ def main():
     if not args.no_cpu_baseline:
         cb, parity = cpu_baseline(inp, last["o"], last["S"])
         out["cpu_baseline"] = cb
+        import oracle
+        out["kernels"]["prologue_gelu"]["cpu_baseline"] = oracle_timed(
+            lambda: oracle.prologue(inp, residual="gelu"), T, "tokens/s",
+            f"whole workload: write keys of all {T} tokens x {w.heads} heads, fp64")
         out["parity"] = parity
     print(json.dumps(out), flush=True)
 
