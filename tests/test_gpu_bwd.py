@@ -69,6 +69,7 @@ def check(got, ref, dtype, mask_rows=None):
 
 
 CASES = [
+    W(dtype="bf16", dk=64, dv=64, L=16, lengths=(40, 3)),
     W(dtype="f32", dk=64, dv=64, L=3, lengths=(130, 1, 64, 0, 5)),
     W(dtype="bf16", dk=64, dv=64, L=4),
     W(dtype="bf16", dk=128, dv=128, L=4, lengths=(200, 65)),
@@ -98,13 +99,16 @@ def test_bwd_strong_decay():
     check(got, ref, "f32")
 
 
-def test_bwd_lm_layer_sampled_chains():
-    """The LM layer at full size (B=8, T=2048, H=6, d=128, L=4): every gradient
-    of two sampled (sequence, head) chains; conv_w is summed over all chains
-    on the GPU, so it is checked on a separate reduced run above."""
-    w = BY_NAME["lm-130m-layer"]
+@pytest.mark.parametrize("name,chains", [("lm-130m-layer", [5, 37]),
+                                         ("recsys-history", [0, 77, 130, 255])])
+def test_bwd_full_size_sampled_chains(name, chains):
+    """Full-size workloads: the LM layer (B=8, T=2048, H=6, d=128, L=4) and the
+    recommendation histories (B=64, T=1024, H=4, d=64, L=4): every gradient of
+    sampled (sequence, head) chains; conv_w is summed over all chains on the
+    GPU, so it is checked on the reduced runs above."""
+    w = BY_NAME[name]
     inp = make_inputs(w)
-    chains = [5, 37]
+    say(f"{name}: chains {chains}")
     got, ref = run(inp, with_state=False, chains=chains)
     H = inp.heads
     rows = np.zeros((inp.total_tokens, H), dtype=bool)
