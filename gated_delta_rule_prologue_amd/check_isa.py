@@ -1,4 +1,4 @@
-"""Build-time check of the scan kernels' machine code (gfx950).
+"""Build-time check of the scan and backward kernels' machine code (gfx950).
 
 An MFMA whose accumulator input is the result of a recent MFMA, and whose
 destination only partly overlaps that accumulator (the compiler allows the two
