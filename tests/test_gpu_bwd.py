@@ -139,3 +139,24 @@ def test_bwd_gelu_matches_oracle(w):
     say(f"bwd gelu {w}")
     got, ref = run(inp, residual="gelu")
     check(got, ref, w.dtype)
+
+
+def test_bwd_all_sequences_empty():
+    """No tokens at all: every per-token gradient is empty, dconv_w is zero and
+    dS_init equals dS_final (G never moves)."""
+    import torch
+    from gated_delta_rule_prologue_amd import binding
+    from tests.test_gpu_state import dev_tensor
+    inp = make_inputs(W(dtype="bf16", lengths=(0, 0, 0)))
+    assert inp.total_tokens == 0
+    dev = binding.to_device(inp)
+    rng = np.random.default_rng(2)
+    dsf = rng.standard_normal((inp.n_seqs, inp.heads, inp.dk, inp.dv)).astype(np.float32)
+    dO = torch.empty((0, inp.heads, inp.dv), dtype=torch.bfloat16, device="cuda")
+    got = binding.bwd(dev["q"], dev["k"], dev["v"], dev["u"], dev["g"], dev["b"], dev["a"],
+                      dev["h"], dev["conv_w"], dev["cu_seqlens"], inp.L, dO,
+                      dS_final=dev_tensor(dsf))
+    torch.cuda.synchronize()
+    assert np.array_equal(got["S_init"].cpu().numpy(), dsf)
+    assert not got["conv_w"].cpu().numpy().any()
+    assert got["q"].numel() == 0 and got["v"].numel() == 0

@@ -110,3 +110,68 @@ def test_forward_replays_from_a_graph(split, monkeypatch):
         torch.cuda.synchronize()
         assert np.array_equal(to_host(o), ref_o) and np.array_equal(to_host(S), ref_S), rep
     say(f"split={split}: three replays identical to eager")
+
+
+def test_backward_replays_from_a_graph():
+    """prism_bwd_ex (write-key recomputation, zero fills, scan backward,
+    write-key backward) captured once and replayed three times into outputs
+    poisoned with NaN before each replay.  dv and dS_init are written once per
+    element and must equal the eager call bit for bit; the gradients summed
+    with fp32 atomics over value slices (dq, dk, dg, db, dconv_w, and through
+    dkw du, da, dh) only up to the order of those sums."""
+    import ctypes
+    import torch
+    from gated_delta_rule_prologue_amd import binding
+    inp = make_inputs(W(dk=64, dv=64, L=3, lengths=(150, 1, 0, 70)))
+    dev = binding.to_device(inp)
+    T, H, dk, dv, L, n = inp.total_tokens, inp.heads, inp.dk, inp.dv, inp.L, inp.n_seqs
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    dO = torch.randn(dev["v"].shape, device="cuda", generator=gen).to(torch.bfloat16)
+    dsf = torch.randn((n, H, dk, dv), device="cuda", generator=gen)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    out = {"q": torch.empty((T, H, dk), **f32), "k": torch.empty((T, H, dk), **f32),
+           "v": torch.empty((T, H, dv), **f32), "u": torch.empty((T, H, L - 1, dk), **f32),
+           "g": torch.empty((T, H), **f32), "b": torch.empty((T, H), **f32),
+           "a": torch.empty((T, H, L - 1, dk), **f32), "h": torch.empty((T, H, L - 1, dk), **f32),
+           "conv_w": torch.empty((H, dk, 4), **f32), "S_init": torch.empty((n, H, dk, dv), **f32)}
+    d = binding.Dims(n, T, H, dk, dv, binding.PRISM_BF16)
+    lib = binding.lib()
+    need = int(lib.prism_bwd_workspace_bytes(ctypes.byref(d), L))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def call(stream):
+        return lib.prism_bwd_ex(
+            ctypes.byref(d), P(dev["q"]), P(dev["k"]), P(dev["v"]), P(dev["u"]), P(dev["g"]),
+            P(dev["b"]), P(dev["a"]), P(dev["h"]), P(dev["conv_w"]), P(dev["cu_seqlens"]), L, 0,
+            None, P(dO), P(dsf), P(out["q"]), P(out["k"]), P(out["v"]), P(out["u"]), P(out["g"]),
+            P(out["b"]), P(out["a"]), P(out["h"]), P(out["conv_w"]), P(out["S_init"]), P(ws),
+            need, ctypes.c_void_p(stream))
+
+    assert call(torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    ref = {k: v.cpu().numpy() for k, v in out.items()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        assert call(side.cuda_stream) == 0
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        assert call(torch.cuda.current_stream().cuda_stream) == 0
+    for rep in range(3):
+        for t in out.values():
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, t in out.items():
+            got = t.cpu().numpy()
+            assert np.isfinite(got).all(), (rep, name)
+            if name in ("v", "S_init"):
+                assert np.array_equal(got, ref[name]), (rep, name)
+            else:
+                scale = max(float(np.max(np.abs(ref[name]))), 1e-30)
+                assert float(np.max(np.abs(got - ref[name]))) <= 1e-5 * scale, (rep, name)
+        say(f"backward replay {rep}: dv, dS_init identical to eager, the rest within 1e-5")
