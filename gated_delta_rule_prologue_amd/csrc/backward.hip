@@ -1,5 +1,6 @@
 // backward.hip -- gradients of PRISM's memory-writing operator (closed-form
-// residual chain) for the loss sum <dO, o> + <dS_final, S_final>.
+// residual chain, or the GELU refinement chain) for the loss
+// sum <dO, o> + <dS_final, S_final>.
 //
 // Reverse-mode differentiation of the token recurrence (WeChat ICML 2026
 // PRISM summary, sections 核心迭代形式, 消除 Token 间串行 and 消除 Step 间串行;
@@ -20,11 +21,12 @@
 //     by sub-chunk from the last, the sub-chunk's states are recomputed into
 //     registers from its checkpoint and walked backwards.  A sub-chunk's
 //     inputs are fetched one sub-chunk ahead with 16-byte loads and staged in
-//     LDS.  Row sums (over the 8 columns) go to fp32 atomics into dq, dk and
-//     dkw, which the value slices of a chain share.
-//   * write_key_bwd_kernel: one thread per (head, channel, block of 16 tokens):
-//     the residual chain (closed form or GELU refinement) backwards (du, da, dh written, dr_0 formed), b and
-//     the taps (dk, db through atomics; dconv_w summed over the block first).
+//     LDS as fp32.  Row sums (over the 8 columns) go to fp32 buffer atomics
+//     into dq, dk and dkw, which the value slices of a chain share.
+//   * write_key_bwd_kernel: one thread per (head, channel, block of 16 tokens),
+//     the level count a template parameter: the residual chain backwards (du,
+//     da, dh written, dr_0 formed), then dk's write-key part (b k and the taps)
+//     summed in registers and added once; db and dconv_w through atomics.
 #include "common.h"
 #include "kernels.h"
 
