@@ -17,16 +17,21 @@
 //   * scan_bwd_kernel: one wavefront per (sequence, head, 8 value columns).
 //     The columns of S and G evolve independently, so all column sums stay
 //     in the wavefront (DPP and row swaps, no LDS barrier on the recurrence).
-//     A first sweep stores S every 8 tokens (16 at dk = 64); then, sub-chunk
-//     by sub-chunk from the last, the sub-chunk's states are recomputed into
-//     registers from its checkpoint and walked backwards.  A sub-chunk's
-//     inputs are fetched one sub-chunk ahead with 16-byte loads and staged in
-//     LDS as fp32.  Row sums (over the 8 columns) go to fp32 buffer atomics
-//     into dq, dk and dkw, which the value slices of a chain share.
+//     A first launch stores S every 4 tokens (16 at dk = 64) and, beside it,
+//     runs G alone backwards to store the gradient at the ends of P segments
+//     per sequence; a second walks all segments side by side: sub-chunk by
+//     sub-chunk from a segment's last, the sub-chunk's states are recomputed
+//     into registers from its checkpoint and walked backwards with every
+//     gradient output.  A sub-chunk's inputs are fetched one sub-chunk ahead
+//     with 16-byte loads and staged in LDS as fp32.  Row sums (over the 8
+//     columns) go to fp32 buffer atomics into dq, dk and dkw, which the value
+//     slices of a chain share.
 //   * write_key_bwd_kernel: one thread per (head, channel, block of 16 tokens),
 //     the level count a template parameter: the residual chain backwards (du,
 //     da, dh written, dr_0 formed), then dk's write-key part (b k and the taps)
 //     summed in registers and added once; db and dconv_w through atomics.
+#include <stdlib.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -35,10 +40,12 @@ namespace bwd {
 
 constexpr int kC = 16;                           // token block of the write-key backward
 constexpr int kCols = 8;                         // value columns per wavefront of the scan backward
+constexpr int kMaxSeg = 8;                       // segments per sequence of the scan backward
 
 // tokens per checkpoint of the scan backward: one sub-chunk's states stay in
-// registers (8 x 16 per lane at dk = 128, 16 x 8 at dk = 64)
-__host__ __device__ constexpr int sub_len(int dk) { return dk == 128 ? 8 : 16; }
+// registers (4 x 16 floats per lane at dk = 128, 16 x 8 at dk = 64), few enough
+// for two wavefronts per SIMD in the segment walk
+__host__ __device__ constexpr int sub_len(int dk) { return dk == 128 ? 4 : 16; }
 
 // checkpoint slot of the sub-chunk starting at token s of sequence n (unique, < T/SUB + n_seqs + 1)
 template <int SUB>
@@ -84,13 +91,21 @@ __device__ __forceinline__ float sum_rowgroups(float x)
 // and of G evolve independently, so every column sum stays inside the
 // wavefront.  Lane (rg, cp) = (lane >> 2, lane & 3) holds rows rg + 16 r and
 // the two columns 2 cp, 2 cp + 1 of the slice.
-template <typename T, int DK>
+// Two launches, MODE 0 then MODE 1.  Each sequence is cut into P segments of
+// whole sub-chunks.  MODE 0 runs two roles side by side over whole sequences:
+// the forward sweep that stores S at every sub-chunk start (workgroups
+// [0, nw)), and the reverse sweep of G alone (G += q dO^T, G <- A_t^T G), which
+// stores the gradient flowing into each segment's last state from the tokens
+// after it (workgroups [nw, 2 nw), P > 1 only).  MODE 1 then walks all segments
+// of every chain side by side (workgroup p nw + w: segment p), each from its
+// stored G, with every gradient output.
+template <typename T, int DK, int MODE>
 __global__ __launch_bounds__(64) void scan_bwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ kw,
     const T* __restrict__ v, const T* __restrict__ g, const T* __restrict__ b,
     const T* __restrict__ dO, const int32_t* __restrict__ cu, int H, int DV,
     const float* __restrict__ S_init, const float* __restrict__ dS_final,
-    float* __restrict__ ckpt,
+    float* __restrict__ ckpt, float* __restrict__ gbuf, int P, int nw,
     float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dkw,
     float* __restrict__ dv, float* __restrict__ dg, float* __restrict__ db,
     float* __restrict__ dS_init)
@@ -112,12 +127,24 @@ __global__ __launch_bounds__(64) void scan_bwd_kernel(
     const int lane = threadIdx.x;
     const int cp = lane & 3, rg = lane >> 2;
     const int slices = DV / kCols;
-    const int slice = blockIdx.x % slices;
-    const int chain = blockIdx.x / slices;
+    int wid = blockIdx.x, seg = 0;
+    bool grole = false;                          // MODE 0: the G sweep
+    if constexpr (MODE == 0) {
+        grole = wid >= nw;
+        if (grole)
+            wid -= nw;
+    } else {
+        seg = wid / nw;
+        wid -= seg * nw;
+    }
+    const int slice = wid % slices;
+    const int chain = wid / slices;
     const int n = chain / H, e = chain % H;
     const int j0 = slice * kCols + cp * 2;       // first of this lane's 2 columns
     const int seq0 = cu[n], seq1 = cu[n + 1];
     const int nsub = (seq1 - seq0 + SUB - 1) / SUB;
+    // segment width: whole sub-chunks, at least one
+    const int W = max(SUB, ((seq1 - seq0 + P - 1) / P + SUB - 1) / SUB * SUB);
 
     float S[EL], G[EL];
     const int64_t sbase = ((int64_t)chain * DK) * DV;    // [n, e] block of S_init / dS_final
@@ -131,6 +158,10 @@ __global__ __launch_bounds__(64) void scan_bwd_kernel(
         }
     auto ckpt_at = [&](int s) {
         return ckpt + ((ckpt_slot<SUB>(s, n) * H + e) * slices + slice) * (int64_t)(EL * 64) + lane;
+    };
+    // gradient into the last state of segment p from the tokens after it
+    auto gbuf_at = [&](int p) {
+        return gbuf + ((((int64_t)n * P + p) * H + e) * slices + slice) * (int64_t)(EL * 64) + lane;
     };
 
     // ---- a sub-chunk's inputs, loaded a sub-chunk ahead into registers, then staged in LDS
@@ -319,48 +350,116 @@ __global__ __launch_bounds__(64) void scan_bwd_kernel(
         }
     };
 
-    // sweep 1: S at every sub-chunk start, into the checkpoints
-    Pre P;
-    if (nsub > 0)
-        pre_load(seq0, false, P);
-    for (int m = 0; m < nsub; ++m) {
-        const int c0 = seq0 + m * SUB, len = min(SUB, seq1 - c0);
-        lds_barrier();                           // the previous sub-chunk's LDS reads are done
-        pre_store(P, false);
-        lds_barrier();
-        if (m + 1 < nsub)
-            pre_load(c0 + SUB, false, P);
-        float* cpt = ckpt_at(c0);
+    Pre P_;
+    if constexpr (MODE == 0) {
+        if (!grole) {
+            // S at every sub-chunk start, into the checkpoints
+            if (nsub > 0)
+                pre_load(seq0, false, P_);
+            for (int m = 0; m < nsub; ++m) {
+                const int c0 = seq0 + m * SUB, len = min(SUB, seq1 - c0);
+                lds_barrier();                   // the previous sub-chunk's LDS reads are done
+                pre_store(P_, false);
+                lds_barrier();
+                if (m + 1 < nsub)
+                    pre_load(c0 + SUB, false, P_);
+                float* cpt = ckpt_at(c0);
 #pragma unroll
-        for (int x = 0; x < EL; ++x)
-            cpt[x * 64] = S[x];
+                for (int x = 0; x < EL; ++x)
+                    cpt[x * 64] = S[x];
 #pragma unroll
-        for (int j = 0; j < SUB; ++j)
-            if (j < len)
-                fapply(j, S, S);
+                for (int j = 0; j < SUB; ++j)
+                    if (j < len)
+                        fapply(j, S, S);
+            }
+            return;
+        }
+        // the G sweep: per token from the last, G += q dO^T, then G <- g (G - b k (G^T k)^T);
+        // after a segment's first token t the result is the gradient into S_{t-1}
+        auto gstep = [&](int j) {
+            float kk[RPT], qq[RPT], dd[2];
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) {
+                kk[r] = at(sK, j * DK + rg + 16 * r);
+                qq[r] = at(sQ, j * DK + rg + 16 * r);
+            }
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                dd[c] = at(sD, j * kCols + cp * 2 + c);
+            const float gt = sG[j], bt = sB[j];
+            float y[2];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                float acc = 0.f;
+#pragma unroll
+                for (int r = 0; r < RPT; ++r) {
+                    G[r * 2 + c] += qq[r] * dd[c];
+                    acc += G[r * 2 + c] * kk[r];
+                }
+                y[c] = sum_rowgroups(acc);
+            }
+#pragma unroll
+            for (int r = 0; r < RPT; ++r)
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+                    G[r * 2 + c] = gt * (G[r * 2 + c] - bt * kk[r] * y[c]);
+        };
+        if (nsub > 0)
+            pre_load(seq0 + (nsub - 1) * SUB, true, P_);
+        for (int m = nsub - 1; m >= 0; --m) {
+            const int c0 = seq0 + m * SUB, len = min(SUB, seq1 - c0);
+            lds_barrier();
+            pre_store(P_, true);
+            lds_barrier();
+            if (m > 0)
+                pre_load(c0 - SUB, true, P_);
+#pragma unroll
+            for (int j = SUB - 1; j >= 0; --j) {
+                if (j < len) {
+                    gstep(j);
+                    const int off = c0 + j - seq0;
+                    if (off > 0 && off % W == 0) {
+                        float* gp = gbuf_at(off / W - 1);
+#pragma unroll
+                        for (int x = 0; x < EL; ++x)
+                            gp[x * 64] = G[x];
+                    }
+                }
+            }
+        }
+        return;
     }
 
-    // sweep 2: sub-chunks from the last; each one's states recomputed into
-    // registers from its checkpoint, then walked backwards
+    // MODE 1: segment seg of the sequence, sub-chunk by sub-chunk from its last;
+    // each sub-chunk's states recomputed into registers from its checkpoint,
+    // then walked backwards
+    const int a0 = seq0 + seg * W, a1 = min(seq1, a0 + W);
+    if (a0 < seq1 && a1 < seq1) {                // not the last segment: G from the G sweep
+        const float* gp = gbuf_at(seg);
+#pragma unroll
+        for (int x = 0; x < EL; ++x)
+            G[x] = gp[x * 64];
+    }
+    const int m_lo = (a0 - seq0) / SUB, m_hi = a0 < seq1 ? (a1 - seq0 + SUB - 1) / SUB : m_lo;
     float Cn[EL];
-    if (nsub > 0) {
-        pre_load(seq0 + (nsub - 1) * SUB, true, P);
-        const float* cpt = ckpt_at(seq0 + (nsub - 1) * SUB);
+    if (m_hi > m_lo) {
+        pre_load(seq0 + (m_hi - 1) * SUB, true, P_);
+        const float* cpt = ckpt_at(seq0 + (m_hi - 1) * SUB);
 #pragma unroll
         for (int x = 0; x < EL; ++x)
             Cn[x] = cpt[x * 64];
     }
-    for (int m = nsub - 1; m >= 0; --m) {
+    for (int m = m_hi - 1; m >= m_lo; --m) {
         const int c0 = seq0 + m * SUB, len = min(SUB, seq1 - c0);
         lds_barrier();
-        pre_store(P, true);
+        pre_store(P_, true);
         lds_barrier();
         float Ss[SUB + 1][EL];                   // Ss[j] = S before token c0 + j
 #pragma unroll
         for (int x = 0; x < EL; ++x)
             Ss[0][x] = Cn[x];
-        if (m > 0) {
-            pre_load(c0 - SUB, true, P);
+        if (m > m_lo) {
+            pre_load(c0 - SUB, true, P_);
             const float* cpt = ckpt_at(c0 - SUB);
 #pragma unroll
             for (int x = 0; x < EL; ++x)
@@ -375,7 +474,7 @@ __global__ __launch_bounds__(64) void scan_bwd_kernel(
             if (j < len)
                 bapply(c0, j, Ss[j + 1], Ss[j]);
     }
-    if (dS_init) {
+    if (seg == 0 && dS_init) {                   // G is now the gradient of the start state
 #pragma unroll
         for (int r = 0; r < RPT; ++r)
 #pragma unroll
@@ -537,7 +636,26 @@ size_t bwd_workspace_floats(int n_seqs, int total_tokens, int heads, int dk, int
 {
     const int64_t slots = total_tokens / bwd::sub_len(dk) + n_seqs + 1;
     return (size_t)(slots * heads * dk * dv)                      // sub-chunk start states
+         + (size_t)n_seqs * bwd::kMaxSeg * heads * dk * dv        // segment-boundary gradients
          + (size_t)total_tokens * heads * dk;                     // dkw
+}
+
+// Segments per sequence for the scan backward.  The segment walk holds two
+// wavefronts per SIMD (2048 on the chip): with at least that many (chain,
+// value slice) wavefronts one segment is best; below it, kMaxSeg short
+// segments (measured at the LM layer, 768 wavefronts: 4.0 ms at P = 8, 4.1 at
+// 5, 4.2 at 4, 4.5 at 2, 5.7 at 1; at the recommendation workload, 2048
+// wavefronts: 2.9 ms at P = 1, 3.1 at 2 to 8).  PRISM_BWD_SEGMENTS=P forces P.
+int bwd_segments(int n_seqs, int heads, int dv)
+{
+    const char* env = getenv("PRISM_BWD_SEGMENTS");
+    if (env && *env) {
+        const int f = atoi(env);
+        if (f >= 1 && f <= bwd::kMaxSeg)
+            return f;
+    }
+    const int64_t nw = (int64_t)n_seqs * heads * (dv / bwd::kCols);
+    return nw >= 2048 ? 1 : bwd::kMaxSeg;
 }
 
 bool bwd_supported(int dk, int dv) { return (dk == 64 || dk == 128) && (dv == 64 || dv == 128); }
@@ -584,8 +702,10 @@ static hipError_t launch_bwd_T(const BwdArgs& p, hipStream_t s)
     const int H = p.heads, T_ = p.total_tokens;
     const int64_t slots = T_ / bwd::sub_len(DK) + p.n_seqs + 1;
     float* ckpt = p.ws;
-    float* dkw = ckpt + slots * H * DK * p.dv;
+    float* gbuf = ckpt + slots * H * DK * p.dv;
+    float* dkw = gbuf + (int64_t)p.n_seqs * bwd::kMaxSeg * H * DK * p.dv;
     const int64_t wgs = (int64_t)p.n_seqs * H * (p.dv / bwd::kCols);
+    const int P = bwd_segments(p.n_seqs, H, p.dv);
     // accumulators start at zero (a fill kernel: no memset node under graph capture)
     auto zero = [&](float* x, int64_t n) {
         if (n > 0)
@@ -601,10 +721,19 @@ static hipError_t launch_bwd_T(const BwdArgs& p, hipStream_t s)
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || wgs == 0)
         return err;
-    hipLaunchKernelGGL((bwd::scan_bwd_kernel<T, DK>), dim3((unsigned)wgs), dim3(64), 0, s,
-                       (const T*)p.q, (const T*)p.k, (const T*)p.kw, (const T*)p.v, (const T*)p.g,
-                       (const T*)p.b, (const T*)p.dO, p.cu_seqlens, H, p.dv, p.s_init, p.ds_final,
-                       ckpt, p.gq, p.gk, dkw, p.gv, p.gg, p.gb, p.gs_init);
+    // checkpoints and (P > 1) the segment-boundary gradients, then the segments
+    hipLaunchKernelGGL((bwd::scan_bwd_kernel<T, DK, 0>), dim3((unsigned)(wgs * (P > 1 ? 2 : 1))),
+                       dim3(64), 0, s, (const T*)p.q, (const T*)p.k, (const T*)p.kw,
+                       (const T*)p.v, (const T*)p.g, (const T*)p.b, (const T*)p.dO, p.cu_seqlens,
+                       H, p.dv, p.s_init, p.ds_final, ckpt, gbuf, P, (int)wgs, p.gq, p.gk, dkw,
+                       p.gv, p.gg, p.gb, p.gs_init);
+    if ((err = hipGetLastError()) != hipSuccess)
+        return err;
+    hipLaunchKernelGGL((bwd::scan_bwd_kernel<T, DK, 1>), dim3((unsigned)(wgs * P)), dim3(64), 0, s,
+                       (const T*)p.q, (const T*)p.k, (const T*)p.kw, (const T*)p.v,
+                       (const T*)p.g, (const T*)p.b, (const T*)p.dO, p.cu_seqlens, H, p.dv,
+                       p.s_init, p.ds_final, ckpt, gbuf, P, (int)wgs, p.gq, p.gk, dkw, p.gv,
+                       p.gg, p.gb, p.gs_init);
     if ((err = hipGetLastError()) != hipSuccess || T_ == 0)
         return err;
     const int64_t threads = ((int64_t)(T_ + bwd::kC - 1) / bwd::kC) * H * DK;

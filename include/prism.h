@@ -251,9 +251,10 @@ size_t prism_scan_workspace_bytes(const prism_dims* d);
  * to every input, by reverse-mode differentiation of the token recurrence
  * (WeChat page sections 核心迭代形式, 消除 Token 间串行, 消除 Step 间串行;
  * gist.science section 2.1).  The write keys are recomputed by the prologue;
- * the scan is walked backwards token by token from states checkpointed every
- * 8 tokens (16 at dk = 64), which the workspace holds (dk * dv fp32 per
- * (checkpoint, head): about 4 B * H * dk * dv * (T / 8 + n_seqs)).
+ * the scan is walked backwards token by token, in up to 8 segments per
+ * sequence side by side, from states checkpointed every 4 tokens (16 at
+ * dk = 64) and gradients stored at the segment ends, which the workspace
+ * holds (about 4 B * H * dk * dv * (T / 4 + 9 n_seqs)).
  *
  *   inputs as in prism_fwd; S_init as in prism_fwd_resume (NULL = zero)
  *   dO          [T, H, dv], input dtype

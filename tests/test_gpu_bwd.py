@@ -160,3 +160,16 @@ def test_bwd_all_sequences_empty():
     assert np.array_equal(got["S_init"].cpu().numpy(), dsf)
     assert not got["conv_w"].cpu().numpy().any()
     assert got["q"].numel() == 0 and got["v"].numel() == 0
+
+
+@pytest.mark.parametrize("segs", ["1", "2", "3", "8"])
+def test_bwd_segment_counts(segs, monkeypatch):
+    """The scan backward cuts every sequence into P segments walked side by
+    side from gradients stored at their ends by a reverse sweep of G alone:
+    any P gives the oracle's gradients, on ragged and empty sequences."""
+    monkeypatch.setenv("PRISM_BWD_SEGMENTS", segs)
+    w = W(dtype="bf16", dk=128, dv=128, L=4, lengths=(300, 1, 0, 97, 33))
+    inp = make_inputs(w)
+    say(f"segments {segs}")
+    got, ref = run(inp)
+    check(got, ref, "bf16")
