@@ -113,16 +113,19 @@ __global__ __launch_bounds__(64) void scan_bwd_kernel(
     constexpr int RPT = DK / 16;                 // rows per lane
     constexpr int EL = 2 * RPT;                  // state elements per lane
     constexpr int SUB = sub_len(DK);
+    // tokens staged at once: the sub-chunk in the segment walk; 16 in the two
+    // sweeps of the first launch, which keep no per-token states
+    constexpr int NST = MODE == 0 && SUB < 16 ? 16 : SUB;
     constexpr int VE = 16 / (int)sizeof(T);      // elements per 16-byte vector
-    constexpr int KV = SUB * DK / VE;            // 16-byte vectors of one [SUB, DK] tile
+    constexpr int KV = NST * DK / VE;            // 16-byte vectors of one [NST, DK] tile
     constexpr int KPL = KV / 64;                 // ... per lane
     constexpr int VPT = kCols / VE;              // 16-byte vectors of one token's 8 columns
-    constexpr int VV = SUB * VPT;                // ... of a sub-chunk
-    static_assert(KV % 64 == 0 && 2 * VV <= 64, "staging layout");
-    // a sub-chunk's rows, widened to fp32 once when staged
-    __shared__ __attribute__((aligned(16))) float sK[SUB * DK], sW[SUB * DK], sQ[SUB * DK];
-    __shared__ __attribute__((aligned(16))) float sV[SUB * kCols], sD[SUB * kCols];
-    __shared__ float sG[SUB], sB[SUB];
+    constexpr int VV = NST * VPT;                // ... of the staged tokens
+    static_assert(KV % 64 == 0 && 2 * VV <= 64 && NST % SUB == 0, "staging layout");
+    // the staged rows, widened to fp32 once
+    __shared__ __attribute__((aligned(16))) float sK[NST * DK], sW[NST * DK], sQ[NST * DK];
+    __shared__ __attribute__((aligned(16))) float sV[NST * kCols], sD[NST * kCols];
+    __shared__ float sG[NST], sB[NST];
 
     const int lane = threadIdx.x;
     const int cp = lane & 3, rg = lane >> 2;
@@ -189,8 +192,8 @@ __global__ __launch_bounds__(64) void scan_bwd_kernel(
             P.vd = reinterpret_cast<const uint4*>(v)[ov];
         else if (back && lane < 2 * VV)
             P.vd = reinterpret_cast<const uint4*>(dO)[ov];
-        const int tg = min(c + (lane % SUB), last);
-        P.gb = lane < 2 * SUB ? ld(lane < SUB ? g : b, (int64_t)tg * H + e) : 0.f;
+        const int tg = min(c + (lane % NST), last);
+        P.gb = lane < 2 * NST ? ld(lane < NST ? g : b, (int64_t)tg * H + e) : 0.f;
     };
     // 16 bytes of T at element idx * VE of dst, as fp32
     auto put = [](float* dst, int idx, const uint4& raw) {
@@ -218,10 +221,10 @@ __global__ __launch_bounds__(64) void scan_bwd_kernel(
             put(sV, lane, P.vd);
         else if (back && lane < 2 * VV)
             put(sD, lane - VV, P.vd);
-        if (lane < SUB)
+        if (lane < NST)
             sG[lane] = P.gb;
-        else if (lane < 2 * SUB)
-            sB[lane - SUB] = P.gb;
+        else if (lane < 2 * NST)
+            sB[lane - NST] = P.gb;
     };
     auto at = [](const float* base, int i) { return base[i]; };
 
@@ -354,23 +357,28 @@ __global__ __launch_bounds__(64) void scan_bwd_kernel(
     if constexpr (MODE == 0) {
         if (!grole) {
             // S at every sub-chunk start, into the checkpoints
-            if (nsub > 0)
+            const int nst = (seq1 - seq0 + NST - 1) / NST;
+            if (nst > 0)
                 pre_load(seq0, false, P_);
-            for (int m = 0; m < nsub; ++m) {
-                const int c0 = seq0 + m * SUB, len = min(SUB, seq1 - c0);
-                lds_barrier();                   // the previous sub-chunk's LDS reads are done
+            for (int m = 0; m < nst; ++m) {
+                const int c0 = seq0 + m * NST, len = min(NST, seq1 - c0);
+                lds_barrier();                   // the previous tokens' LDS reads are done
                 pre_store(P_, false);
                 lds_barrier();
-                if (m + 1 < nsub)
-                    pre_load(c0 + SUB, false, P_);
-                float* cpt = ckpt_at(c0);
+                if (m + 1 < nst)
+                    pre_load(c0 + NST, false, P_);
 #pragma unroll
-                for (int x = 0; x < EL; ++x)
-                    cpt[x * 64] = S[x];
+                for (int j = 0; j < NST; ++j) {
+                    if (j < len) {
+                        if (j % SUB == 0) {      // a sub-chunk start: checkpoint
+                            float* cpt = ckpt_at(c0 + j);
 #pragma unroll
-                for (int j = 0; j < SUB; ++j)
-                    if (j < len)
+                            for (int x = 0; x < EL; ++x)
+                                cpt[x * 64] = S[x];
+                        }
                         fapply(j, S, S);
+                    }
+                }
             }
             return;
         }
@@ -404,17 +412,18 @@ __global__ __launch_bounds__(64) void scan_bwd_kernel(
                 for (int c = 0; c < 2; ++c)
                     G[r * 2 + c] = gt * (G[r * 2 + c] - bt * kk[r] * y[c]);
         };
-        if (nsub > 0)
-            pre_load(seq0 + (nsub - 1) * SUB, true, P_);
-        for (int m = nsub - 1; m >= 0; --m) {
-            const int c0 = seq0 + m * SUB, len = min(SUB, seq1 - c0);
+        const int nst = (seq1 - seq0 + NST - 1) / NST;
+        if (nst > 0)
+            pre_load(seq0 + (nst - 1) * NST, true, P_);
+        for (int m = nst - 1; m >= 0; --m) {
+            const int c0 = seq0 + m * NST, len = min(NST, seq1 - c0);
             lds_barrier();
             pre_store(P_, true);
             lds_barrier();
             if (m > 0)
-                pre_load(c0 - SUB, true, P_);
+                pre_load(c0 - NST, true, P_);
 #pragma unroll
-            for (int j = SUB - 1; j >= 0; --j) {
+            for (int j = NST - 1; j >= 0; --j) {
                 if (j < len) {
                     gstep(j);
                     const int off = c0 + j - seq0;
