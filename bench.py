@@ -48,7 +48,7 @@ KERNEL_SOURCES = {
                                       "prologue_f32_ext.hip", "common.h", "kernels.h",
                                       "prism_api.hip")],
     "scan": [_CSRC + f for f in ("chunk_scan_bf16.hip", "chunk_scan.hip", "long_seq.hip", "common.h",
-                                  "kernels.h", "prism_api.hip")],
+                                  "kernels.h", "prism_api.hip", "mfma_bf16.h")],
     "decode": [_CSRC + f for f in ("decode.hip", "common.h", "kernels.h", "prism_api.hip")],
 }
 # Decode batches: (name, sequences, heads, dk, dv, L), one new token per sequence.
@@ -65,16 +65,17 @@ def algorithmic_work(w, n_seqs, T, esize):
     Per head-token (ht):
       prologue bytes = e [dk (k) + 2 (L-1) dk (u, a) + max(L-2, 0) dk (h slots read) + 1 (b) + dk (kw)]
       scan bytes     = e [3 dk (q, k, kw) + dv (v) + 2 (g, b) + dv (o)]  + S_final (fp32) per chain
-      scan flops     = chunk products of the WY/UT form with C = 64 and dense 64x64 tiles:
-                       4 Gram tiles 8 C dk, K S0 and Q S0 4 dk dv, three 64x64-by-V/X
-                       products 6 C dv, Tm R 2 C dv, state update 4 dk dv, UT inverse ~2C^2/3
+      scan flops     = the chunkwise WY/UT form with C = 64 counted with dense C x C tiles:
+                       10 C dk + 8 C dv + 8 dk dv + 2 C^2 / 3 per head-token (four Gram tiles
+                       and the UT-transformed keys T (b gamma K), the three C x C-by-V/X products
+                       and T R, K S0 and Q S0, the state update, the C x C inverse)
     """
     H, dk, dv, L = w.heads, w.dk, w.dv, w.L
     ht = T * H
     pro = esize * (dk + 2 * (L - 1) * dk + max(L - 2, 0) * dk + 1 + dk) * ht
     scan = esize * (3 * dk + dv + 2 + dv) * ht + 4 * n_seqs * H * dk * dv
     C = 64
-    flops_ht = 8 * C * dk + 4 * dk * dv + 6 * C * dv + 2 * C * dv + 4 * dk * dv + (2 * C * C) // 3
+    flops_ht = 10 * C * dk + 8 * C * dv + 8 * dk * dv + round(2 * C * C / 3)
     return {"prologue_bytes": pro, "scan_bytes": scan, "scan_flops": flops_ht * ht,
             "head_tokens": ht}
 
@@ -99,6 +100,23 @@ def measured_traffic(kernel, workload):
     if not m or not s or s.group(1) != source_sha(KERNEL_SOURCES[kernel]):
         return None
     return float(m.group(1))
+
+
+def measured_mfma(kernel, workload):
+    """MFMA utilisation per launch from the committed rocprofv3 counter summary
+    (profiles/<kernel>_<workload>_mfma.md): (busy fraction of all SIMD cycles,
+    MFMA flops executed), or None when there is none or the kernel's sources
+    changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_mfma.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    b = re.search(r"mfma_busy_frac:\s*([0-9.eE+-]+)", text)
+    f = re.search(r"mfma_flops_per_launch:\s*([0-9.eE+-]+)", text)
+    s = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    if not b or not f or not s or s.group(1) != source_sha(KERNEL_SOURCES[kernel]):
+        return None
+    return float(b.group(1)), float(f.group(1))
 
 
 def cpu_baseline(inp, o_gpu, s_gpu):
@@ -469,6 +487,14 @@ def main():
     scn["mfma_tflops"] = work["scan_flops"] / (scan_ms * 1e-3) / 1e12
     scn["mfma_frac"] = scn["mfma_tflops"] / (BF16_PEAK_TFLOPS if esize == 2 else FP32_MFMA_PEAK_TFLOPS)
     scn["algorithmic_flops"] = work["scan_flops"]
+    # the same from rocprofv3 counters (committed summary, same source-hash rule
+    # as traffic): MFMA-busy share of all SIMD cycles, and the flops the MFMA
+    # units executed (redundant work included) over this run's launch time
+    mc = measured_mfma("scan", w.name)
+    scn["mfma_counters"] = None if mc is None else {
+        "busy_frac": mc[0], "flops_per_launch": mc[1],
+        "tflops_executed": mc[1] / (scan_ms * 1e-3) / 1e12,
+        "frac_of_peak": mc[1] / (scan_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
     dominant = scn if scan_ms >= pro_ms else pro
 
     out = {

@@ -9,7 +9,7 @@ prism_fwd_resume, ``decode_step`` -> prism_decode_step, ``prologue`` ->
 prism_prologue, ``prologue_ex`` -> prism_prologue_ex, ``scan`` -> prism_scan,
 ``scan_ex`` -> prism_scan_ex, ``workspace_bytes`` -> prism_workspace_bytes,
 ``scan_workspace_bytes`` -> prism_scan_workspace_bytes, ``bwd`` -> prism_bwd_ex (prism_bwd
-with a residual choice).
+with a residual choice), ``scan_wait_giveups`` -> prism_scan_wait_giveups.
 """
 from __future__ import annotations
 
@@ -80,6 +80,8 @@ def lib():
         L.prism_decode_step.restype = I
         L.prism_status_str.argtypes = [I]
         L.prism_status_str.restype = ctypes.c_char_p
+        L.prism_scan_wait_giveups.argtypes = [ctypes.POINTER(ctypes.c_uint), I]
+        L.prism_scan_wait_giveups.restype = I
         L.prism_abi_version.argtypes = []
         L.prism_abi_version.restype = I
         _lib = L
@@ -363,6 +365,14 @@ def bwd(q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L: int, dO, dS_final=None, S
         _ptr(out["b"]), _ptr(out["a"]), _ptr(out["h"]), _ptr(out["conv_w"]), _ptr(out["S_init"]),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
+
+
+def scan_wait_giveups(reset: bool = True) -> int:
+    """Bounded in-kernel waits that gave up since the last reset
+    (prism_scan_wait_giveups, synchronous); 0 when every scan ran as designed."""
+    n = ctypes.c_uint(0)
+    _check("prism_scan_wait_giveups", lib().prism_scan_wait_giveups(ctypes.byref(n), int(reset)))
+    return int(n.value)
 
 
 def to_device(inp, device="cuda") -> dict:

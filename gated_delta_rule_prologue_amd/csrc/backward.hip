@@ -145,7 +145,6 @@ __global__ __launch_bounds__(64) void scan_bwd_kernel(
     const int n = chain / H, e = chain % H;
     const int j0 = slice * kCols + cp * 2;       // first of this lane's 2 columns
     const int seq0 = cu[n], seq1 = cu[n + 1];
-    const int nsub = (seq1 - seq0 + SUB - 1) / SUB;
     // segment width: whole sub-chunks, at least one
     const int W = max(SUB, ((seq1 - seq0 + P - 1) / P + SUB - 1) / SUB * SUB);
 

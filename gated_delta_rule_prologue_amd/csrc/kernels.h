@@ -84,6 +84,11 @@ bool decode_supported(int dk, int dv);
 hipError_t launch_scan(const ScanArgs& p, hipStream_t stream);
 bool scan_supported(bool bf16, int dk, int dv, int dv_slice);
 
+// fp32 scan token by token (fp32 inputs at dk = 128, whose chunkwise tiles
+// exceed the LDS); any dk in {64, 128}, dv a multiple of 32.
+hipError_t launch_scan_f32_recurrent(const ScanArgs& p, hipStream_t stream);
+bool scan_f32_recurrent_supported(int dk, int dv);
+
 // bf16 chunk scan with the register-resident state path.
 hipError_t launch_scan_bf16(const ScanArgs& p, hipStream_t stream);
 // `a` on the eight-wavefront kernel (32-column slices) and, in the same launch,
@@ -92,5 +97,8 @@ hipError_t launch_scan_bf16(const ScanArgs& p, hipStream_t stream);
 // 0, skip, 2 skip, ... are left out of `m`.
 hipError_t launch_scan_bf16_pair(const ScanArgs& a, const ScanArgs& m, int skip, hipStream_t stream);
 bool scan_bf16_supported(int dk, int dv, int dv_slice);
+// Bounded in-kernel waits of the bf16 scan that gave up (synchronous read of
+// a device counter on the current device; reset sets it back to zero).
+hipError_t read_wait_giveups(unsigned int* count, bool reset);
 
 }  // namespace prism

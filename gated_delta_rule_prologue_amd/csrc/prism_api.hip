@@ -84,8 +84,18 @@ int pick_dv_slice(const prism_dims* d)
     return best;
 }
 
+// fp32 takes the token-recurrent scan at dk = 128 (its chunkwise tiles do not
+// fit the LDS there), and anywhere with PRISM_SCAN_RECURRENT=1.
+bool use_f32_recurrent(const prism_dims* d)
+{
+    return d->dtype == PRISM_F32 && prism::scan_f32_recurrent_supported(d->dk, d->dv) &&
+           (d->dk == 128 || env_int("PRISM_SCAN_RECURRENT", 0) != 0);
+}
+
 prism_status check_scan_shape(const prism_dims* d)
 {
+    if (use_f32_recurrent(d))
+        return PRISM_OK;
     for (int c : {64, 32, 16})
         if (slice_supported(d, c))
             return PRISM_OK;
@@ -193,6 +203,8 @@ prism_status scan_impl(const prism_dims* d, const void* q, const void* k, const 
     p.s_init = S_init;
     p.o = o;
     p.s_final = S_final;
+    if (use_f32_recurrent(d))
+        return from_hip(prism::launch_scan_f32_recurrent(p, (hipStream_t)stream));
     const int P = split_ws ? split_for(d) : 1;
     if (P >= 2)
         return from_hip(prism::launch_split_scan(p, P, split_ws, (hipStream_t)stream));
@@ -390,6 +402,13 @@ prism_status prism_bwd(const prism_dims* d, const void* q, const void* k, const 
     return prism_bwd_ex(d, q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L, PRISM_RESIDUAL_LINEAR,
                         S_init, dO, dS_final, dq, dk, dv, du, dg, db, da, dh, dconv_w, dS_init,
                         workspace, workspace_bytes, stream);
+}
+
+prism_status prism_scan_wait_giveups(unsigned int* count, int reset)
+{
+    if (!count)
+        return PRISM_EINVAL;
+    return from_hip(prism::read_wait_giveups(count, reset != 0));
 }
 
 prism_status prism_decode_step(const prism_dims* d, const void* q, const void* k, const void* v,

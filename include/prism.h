@@ -81,7 +81,7 @@ typedef struct {
     int32_t n_seqs;        /* number of packed sequences, >= 1 */
     int32_t total_tokens;  /* T = cu_seqlens[n_seqs], >= 0 */
     int32_t heads;         /* H >= 1 */
-    int32_t dk;            /* key width   (prism_fwd / prism_scan: bf16 64 or 128, fp32 64) */
+    int32_t dk;            /* key width   (prism_fwd / prism_scan: 64 or 128) */
     int32_t dv;            /* value width (prism_fwd / prism_scan: 64 or 128) */
     int32_t dtype;         /* prism_dtype of every float input */
 } prism_dims;
@@ -149,8 +149,9 @@ prism_status prism_prologue_ex(const prism_dims* d,
  * gated delta-rule state recurrence S_t = g_t (I - b_t k_t k_t^T) S_{t-1} +
  * kw_t v_t^T, o_t = S_t^T q_t (WeChat page section 消除 Token 间串行: forget
  * identical to GDN; gist.science section 2.1: S_t = S_{t-1} A_t + B_t with an
- * input-only write), evaluated in chunks of 64 tokens.  Other arguments as in
- * prism_fwd.
+ * input-only write), evaluated in chunks of 64 tokens (fp32 inputs at
+ * dk = 128: token by token, whose fp32 chunk tiles would not fit the on-chip
+ * memory).  Other arguments as in prism_fwd.
  */
 prism_status prism_scan(const prism_dims* d,
                         const void* q, const void* k, const void* kw, const void* v,
@@ -282,7 +283,7 @@ prism_status prism_bwd(const prism_dims* d,
 
 /* prism_bwd with a choice of residual chain (prism_residual): the closed form
  * (PRISM_RESIDUAL_LINEAR, as prism_bwd) or the non-linear refinement chain
- * r_{l+1} = r_l - a_l GELU(h_l r_l) of the WeChat page, section 消除 Step 间串行
+ * r_{l+1} = r_l - a_l GELU(h_l r_l) of the gist.science summary, section 2.2
  * (PRISM_RESIDUAL_GELU; forward as in prism_fwd_resume).  Any other value:
  * PRISM_EINVAL.  Other arguments, layouts and errors as in prism_bwd. */
 prism_status prism_bwd_ex(const prism_dims* d,
@@ -294,6 +295,20 @@ prism_status prism_bwd_ex(const prism_dims* d,
                           float* dq, float* dk, float* dv, float* du, float* dg, float* db,
                           float* da, float* dh, float* dconv_w, float* dS_init,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Diagnostic: the number of bounded in-kernel waits that gave up since the
+ * last reset, on the current device.  The eight-wavefront bf16 scan has one
+ * bounded LDS-flag wait per chunk (the workgroup's diagonal-inverse handoff);
+ * every writer raises its flag before the next barrier, so the count stays
+ * 0, and a nonzero count means some output of a scan since the reset may be
+ * wrong.  Writes the count to *count (host pointer, non-null); reset != 0
+ * sets it back to zero.  Unlike every other entry point this call is
+ * synchronous: it reads (and with reset writes) a device word with a blocking
+ * copy, so call it outside graph capture.  PRISM_EINVAL for a null pointer,
+ * PRISM_EHIP if the copy fails.
+ */
+prism_status prism_scan_wait_giveups(unsigned int* count, int reset);
 
 /* Static description of a status code. */
 const char* prism_status_str(prism_status s);

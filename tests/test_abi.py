@@ -29,7 +29,7 @@ def test_header_declares_the_entry_points():
     for n in ("prism_fwd", "prism_prologue", "prism_scan", "prism_workspace_bytes",
               "prism_status_str", "prism_abi_version", "prism_fwd_resume", "prism_decode_step",
               "prism_prologue_ex", "prism_scan_ex", "prism_scan_workspace_bytes", "prism_bwd",
-              "prism_bwd_workspace_bytes", "prism_bwd_ex"):
+              "prism_bwd_workspace_bytes", "prism_bwd_ex", "prism_scan_wait_giveups"):
         assert n in names
 
 
@@ -48,6 +48,11 @@ def test_status_strings(lib):
     assert "invalid" in binding.status_str(1)
     assert "unsupported" in binding.status_str(2)
     assert "HIP" in binding.status_str(3)
+
+
+def test_wait_giveups_rejects_null(lib):
+    from gated_delta_rule_prologue_amd import binding as B
+    assert lib.prism_scan_wait_giveups(None, 0) == B.PRISM_EINVAL
 
 
 def test_workspace_bytes(lib):
@@ -77,7 +82,8 @@ def test_fwd_rejects_bad_arguments(lib):
     from gated_delta_rule_prologue_amd import binding as B
     # unsupported widths are reported as such (before any launch)
     assert _fwd(lib, B.make_dims(1, 10, 1, 96, 64, B.PRISM_BF16)) == B.PRISM_EUNSUPPORTED
-    assert _fwd(lib, B.make_dims(1, 10, 1, 128, 128, B.PRISM_F32)) == B.PRISM_EUNSUPPORTED
+    assert _fwd(lib, B.make_dims(1, 10, 1, 96, 128, B.PRISM_F32)) == B.PRISM_EUNSUPPORTED
+    assert _fwd(lib, B.make_dims(1, 10, 1, 128, 48, B.PRISM_F32)) == B.PRISM_EUNSUPPORTED
     ok = B.make_dims(1, 10, 1, 64, 64, B.PRISM_BF16)
     # null / misaligned pointers, bad L, small workspace, bad dims
     assert _fwd(lib, ok, q=None) == B.PRISM_EINVAL

@@ -30,6 +30,24 @@ def test_forward_bytes_match_the_workload_table():
     assert work["prologue_bytes"] == 2562 * 98304
 
 
+def test_scan_flops_dense_count():
+    """Scan flops per head-token with dense 64 x 64 tiles: 10 C dk + 8 C dv +
+    8 dk dv + 2 C^2 / 3 = 281,259 at dk = dv = 128 and 109,227 at 64."""
+    w, n, T = lm()
+    assert bench.algorithmic_work(w, n, T, 2)["scan_flops"] == 281259 * 98304
+    w64 = BY_NAME["recsys-history"]
+    assert bench.algorithmic_work(w64, 64, 64 * 1024, 2)["scan_flops"] == 109227 * 64 * 1024 * 4
+
+
+def test_mfma_counters_only_for_unchanged_sources(monkeypatch):
+    m = bench.measured_mfma("scan", "lm-130m-layer")
+    if m is None:
+        pytest.skip("no MFMA counter summary for the current scan sources")
+    assert 0.0 < m[0] < 1.0 and m[1] > 0
+    monkeypatch.setattr(bench, "source_sha", lambda paths: "0" * 64)
+    assert bench.measured_mfma("scan", "lm-130m-layer") is None
+
+
 def test_backward_work_models():
     w, n, T = lm()
     assert bench.bwd_flops(w, T) == 37 * 16384 * 6 * 128 * 128

@@ -124,6 +124,55 @@ def test_bwd_full_size_sampled_chains(name, chains):
     check(got, ref, "bf16", masks)
 
 
+def _chain_rows(x, inp, chains):
+    """Rows of the given (sequence * H + head) chains of a per-token tensor [T, H, ...],
+    concatenated (torch tensors are sliced on the device before the copy)."""
+    cu, H = inp.cu_seqlens, inp.heads
+    parts = [x[int(cu[c // H]):int(cu[c // H + 1]), c % H] for c in chains]
+    if hasattr(x, "cpu"):
+        import torch
+        return torch.cat(parts).cpu().numpy().astype(np.float64)
+    return np.concatenate(parts).astype(np.float64)
+
+
+@pytest.mark.parametrize("name,chains", [("long-context-64k", [5]),
+                                         ("varlen-histories", [3, 1010, 2047, 2600, 4095])])
+def test_bwd_large_workloads_sampled_chains(name, chains):
+    """The 64k workload (one sequence of 65,536 tokens, H=16, d=128: the backward
+    cuts it into 8 segments and keeps checkpoints of ~18 GB) and the varlen
+    workload (4,096 chains: one segment each): every gradient of the sampled
+    chains, compared row by row (only those rows are copied to the host)."""
+    import torch
+    from gated_delta_rule_prologue_amd import binding
+    from gated_delta_rule_prologue_amd.inputs import f32_to_bf16_bits, to_float
+    from tests.test_gpu_state import dev_tensor
+    w = BY_NAME[name]
+    inp = make_inputs(w)
+    lens = np.diff(inp.cu_seqlens)
+    chains = sorted(set(chains) | {int(np.argmax(lens)) * inp.heads})
+    say(f"{name}: T={inp.total_tokens} chains {chains}")
+    d_o = to_float(f32_to_bf16_bits(np.random.default_rng(4).standard_normal(
+        (inp.total_tokens, inp.heads, inp.dv)).astype(np.float32)))
+    dev = binding.to_device(inp)
+    got = binding.bwd(dev["q"], dev["k"], dev["v"], dev["u"], dev["g"], dev["b"], dev["a"],
+                      dev["h"], dev["conv_w"], dev["cu_seqlens"], inp.L,
+                      dev_tensor(f32_to_bf16_bits(d_o)))
+    torch.cuda.synchronize()
+    got_rows = {n: _chain_rows(got[n], inp, chains) for n in ("q", "k", "v", "u", "a", "h", "g", "b")}
+    got_s = np.stack([got["S_init"][c // inp.heads, c % inp.heads].cpu().numpy() for c in chains])
+    del got, dev
+    say(f"{name}: oracle")
+    ref = oracle.bwd(inp, d_o.astype(np.float64), chains=chains)
+    for n in ("q", "k", "v", "u", "a", "h", "g", "b"):
+        err = max_rel(got_rows[n], _chain_rows(ref[n], inp, chains))
+        say(f"  d{n} err {err:.3e}")
+        assert np.isfinite(got_rows[n]).all() and err <= TOL["bf16"], (n, err)
+    ref_s = np.stack([ref["S_init"][c // inp.heads, c % inp.heads] for c in chains])
+    err = max_rel(got_s, ref_s)
+    say(f"  dS_init err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 GELU_CASES = [
     W(dtype="f32", dk=64, dv=64, L=4, lengths=(130, 1, 64, 0, 5)),
     W(dtype="bf16", dk=128, dv=128, L=5, lengths=(200, 65)),

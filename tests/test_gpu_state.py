@@ -97,6 +97,7 @@ def to_host_bits(bits):
 
 RESUME_CASES = [
     W(dtype="f32", dk=64, dv=64, L=2, lengths=(130, 1, 2, 0, 64)),
+    W(dtype="f32", dk=128, dv=128, L=4, lengths=(90, 1, 0, 65)),       # token-recurrent fp32
     W(dtype="bf16", dk=64, dv=64, L=4, lengths=(200, 1, 2, 3, 0, 65)),
     W(dtype="bf16", dk=128, dv=128, L=4, lengths=(150, 2, 64)),
     W(dtype="bf16", dk=128, dv=64, L=1, lengths=(70, 1)),
@@ -120,8 +121,6 @@ def test_fwd_resume_every_scan_kernel(dk, kernel, monkeypatch):
     for key, val in SCAN_KERNELS[kernel].items():
         monkeypatch.setenv(key, val)
     slices = [16, 32] if kernel.startswith("specialised") else [32, 64]
-    if kernel == "generic" and dk == 128:
-        slices = [32]
     inp = make_inputs(W(dtype="bf16", dk=dk, dv=64, L=3, lengths=(140, 3, 0, 64, 65)))
     for dvs in slices:
         monkeypatch.setenv("PRISM_DV_SLICE", str(dvs))
