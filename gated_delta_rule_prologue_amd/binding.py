@@ -5,7 +5,7 @@ HIP stream; every step of the operator runs in the library's HIP kernels.  The
 functions raise if the library is not built -- there is no fallback path.
 
 Names follow the C ABI: ``fwd`` -> prism_fwd, ``fwd_resume`` ->
-prism_fwd_resume, ``decode_step`` -> prism_decode_step, ``prologue`` ->
+prism_fwd_resume, ``fwd_noalloc`` -> prism_fwd_noalloc, ``decode_step`` -> prism_decode_step, ``prologue`` ->
 prism_prologue, ``prologue_ex`` -> prism_prologue_ex, ``scan`` -> prism_scan,
 ``scan_ex`` -> prism_scan_ex, ``workspace_bytes`` -> prism_workspace_bytes,
 ``scan_workspace_bytes`` -> prism_scan_workspace_bytes, ``bwd`` -> prism_bwd_ex (prism_bwd
@@ -22,7 +22,8 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libprism.so")
 _lib = None
 
-PRISM_OK, PRISM_EINVAL, PRISM_EUNSUPPORTED, PRISM_EHIP = 0, 1, 2, 3
+PRISM_OK, PRISM_EINVAL, PRISM_EUNSUPPORTED, PRISM_EHIP, PRISM_ENOSPACE = 0, 1, 2, 3, 4
+NOALLOC_MAX_BYTES = 64 << 20                 # PRISM_NOALLOC_MAX_BYTES
 PRISM_F32, PRISM_BF16 = 0, 1
 RESIDUAL = {"linear": 0, "gelu": 1}          # prism_residual
 MAX_LEVELS = 16
@@ -58,6 +59,8 @@ def lib():
         L.prism_workspace_bytes.restype = S
         L.prism_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, I, P, P, P, S, P]
         L.prism_fwd.restype = I
+        L.prism_fwd_noalloc.argtypes = [D, P, P, P, P, P, P, P, P, P, P, I, P, P, P]
+        L.prism_fwd_noalloc.restype = I
         L.prism_prologue.argtypes = [D, P, P, P, P, P, P, P, I, P, P]
         L.prism_prologue.restype = I
         L.prism_scan.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
@@ -267,6 +270,21 @@ def fwd(q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L: int, o=None, S_final=None
         ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(g), _ptr(b), _ptr(a), _ptr(h),
         _ptr(conv_w), _ptr(cu_seqlens), int(L), _ptr(o), _ptr(S_final), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o, S_final
+
+
+def fwd_noalloc(q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L: int, o, S_final, stream=None):
+    """Forward pass with the library's static scratch as workspace
+    (prism_fwd_noalloc): the caller passes the outputs o and S_final, and
+    nothing is allocated.  Returns (o, S_final)."""
+    d = _dims_of(q, v, cu_seqlens)
+    _check_write_branch(d, q.dtype, k, u, a, h, b, conv_w, L)
+    _check_scan(d, q.dtype, q, k, k, v, g, b)
+    _expect("o", o, v.shape, v.dtype)
+    _expect("S_final", S_final, (d.n_seqs, d.heads, d.dk, d.dv), torch.float32)
+    _check("prism_fwd_noalloc", lib().prism_fwd_noalloc(
+        ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(g), _ptr(b), _ptr(a), _ptr(h),
+        _ptr(conv_w), _ptr(cu_seqlens), int(L), _ptr(o), _ptr(S_final), _stream(stream)))
     return o, S_final
 
 

@@ -1,12 +1,40 @@
 // prism_api.hip -- C ABI of libprism (declared in include/prism.h): argument
 // validation, kernel selection and launches on the caller's stream.
+#include <mutex>
 #include <stdint.h>
 #include <stdlib.h>
 
 #include "prism.h"
 #include "kernels.h"
 
+// Workspace of prism_fwd_noalloc: a file-scope device array, one copy per GPU
+// for the life of the process.  Host code never passes `scratch` itself (in
+// host code the name is only a stand-in for the device symbol); it passes the
+// device address hipGetSymbolAddress returned on that device.
+static __device__ __align__(256) unsigned char scratch[PRISM_NOALLOC_MAX_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device, looked up once per device
+// (with that device current) and kept; null if the lookup fails.
+void* scratch_ptr()
+{
+    static std::mutex mu;
+    static void* ptr[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess)
+            return nullptr;
+        ptr[dev] = p;
+    }
+    return ptr[dev];
+}
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -259,6 +287,7 @@ const char* prism_status_str(prism_status s)
     case PRISM_EINVAL: return "invalid argument";
     case PRISM_EUNSUPPORTED: return "unsupported shape or dtype";
     case PRISM_EHIP: return "HIP launch failed";
+    case PRISM_ENOSPACE: return "workspace needed exceeds the library's static scratch";
     }
     return "unknown status";
 }
@@ -323,6 +352,24 @@ prism_status prism_fwd(const prism_dims* d, const void* q, const void* k, const 
 {
     return fwd_impl(d, q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L, PRISM_RESIDUAL_LINEAR,
                     nullptr, nullptr, o, S_final, nullptr, workspace, workspace_bytes, stream);
+}
+
+prism_status prism_fwd_noalloc(const prism_dims* d, const void* q, const void* k, const void* v,
+                               const void* u, const void* g, const void* b, const void* a,
+                               const void* h, const void* conv_w, const int32_t* cu_seqlens,
+                               int L, void* o, float* S_final, void* stream)
+{
+    if (!dims_ok(d) || L < 1 || L > PRISM_MAX_LEVELS)
+        return PRISM_EINVAL;
+    const size_t need = prism_workspace_bytes(d, L);
+    if (need > (size_t)PRISM_NOALLOC_MAX_BYTES)
+        return PRISM_ENOSPACE;
+    void* ws = scratch_ptr();
+    if (!ws)
+        return PRISM_EHIP;
+    return fwd_impl(d, q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L, PRISM_RESIDUAL_LINEAR,
+                    nullptr, nullptr, o, S_final, nullptr, ws, (size_t)PRISM_NOALLOC_MAX_BYTES,
+                    stream);
 }
 
 prism_status prism_fwd_resume(const prism_dims* d, const void* q, const void* k, const void* v,

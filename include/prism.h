@@ -61,7 +61,8 @@ typedef enum {
     PRISM_OK = 0,
     PRISM_EINVAL = 1,          /* null/misaligned pointer, bad size, L out of range */
     PRISM_EUNSUPPORTED = 2,    /* valid but not implemented here (e.g. dk not in {64, 128}) */
-    PRISM_EHIP = 3             /* a HIP launch failed */
+    PRISM_EHIP = 3,            /* a HIP launch failed */
+    PRISM_ENOSPACE = 4         /* prism_fwd_noalloc: the shape needs more than the static scratch */
 } prism_status;
 
 typedef enum { PRISM_F32 = 0, PRISM_BF16 = 1 } prism_dtype;
@@ -117,6 +118,35 @@ prism_status prism_fwd(const prism_dims* d,
                        const int32_t* cu_seqlens, int L,
                        void* o, float* S_final,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * prism_fwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The workspace prism_fwd would take lives instead in
+ * a static device array of PRISM_NOALLOC_MAX_BYTES inside the library, one
+ * per GPU, held from the first call on that GPU until the process ends; its
+ * device address is looked up once per GPU on the first call there (that
+ * first call is not capturable; later ones are).  The call itself allocates
+ * nothing.
+ *
+ *   Arguments, layouts and results as in prism_fwd (the caller still provides
+ *   every input and output buffer).
+ *   PRISM_ENOSPACE when prism_workspace_bytes(d, L) exceeds
+ *   PRISM_NOALLOC_MAX_BYTES (e.g. the LM layer B=8, T=2048, H=6, d=128 needs
+ *   about 25 MB and fits; one 65,536-token sequence of 16 heads does not).
+ *   PRISM_EHIP if the scratch address cannot be looked up.
+ * Every call on one GPU uses the same scratch: calls that overlap on one GPU
+ * (different streams, or host threads) race and must be serialised by the
+ * caller.  The scratch keeps the last call's contents; every byte a call reads
+ * from it is written earlier in the same call.
+ */
+#define PRISM_NOALLOC_MAX_BYTES (64u << 20)
+prism_status prism_fwd_noalloc(const prism_dims* d,
+                               const void* q, const void* k, const void* v,
+                               const void* u, const void* g, const void* b,
+                               const void* a, const void* h, const void* conv_w,
+                               const int32_t* cu_seqlens, int L,
+                               void* o, float* S_final, void* stream);
 
 /*
  * Prologue only: the write keys kw [T, H, dk] (input dtype, rounded to

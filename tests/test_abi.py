@@ -29,7 +29,8 @@ def test_header_declares_the_entry_points():
     for n in ("prism_fwd", "prism_prologue", "prism_scan", "prism_workspace_bytes",
               "prism_status_str", "prism_abi_version", "prism_fwd_resume", "prism_decode_step",
               "prism_prologue_ex", "prism_scan_ex", "prism_scan_workspace_bytes", "prism_bwd",
-              "prism_bwd_workspace_bytes", "prism_bwd_ex", "prism_scan_wait_giveups"):
+              "prism_bwd_workspace_bytes", "prism_bwd_ex", "prism_scan_wait_giveups",
+              "prism_fwd_noalloc"):
         assert n in names
 
 
@@ -48,6 +49,20 @@ def test_status_strings(lib):
     assert "invalid" in binding.status_str(1)
     assert "unsupported" in binding.status_str(2)
     assert "HIP" in binding.status_str(3)
+
+
+def test_fwd_noalloc_rejects_bad_arguments(lib):
+    from gated_delta_rule_prologue_amd import binding as B
+    ok = B.make_dims(1, 10, 1, 64, 64, B.PRISM_BF16)
+    call = lambda d, L=2: lib.prism_fwd_noalloc(ctypes.byref(d), *([FAKE] * 10), L, FAKE, FAKE,
+                                                None)
+    assert call(ok, L=0) == B.PRISM_EINVAL
+    assert call(B.make_dims(0, 10, 1, 64, 64, B.PRISM_BF16)) == B.PRISM_EINVAL
+    # the scratch bound is checked before the device is touched
+    big = B.make_dims(1, 65536, 16, 128, 128, B.PRISM_BF16)
+    assert B.workspace_bytes(big, 4) > B.NOALLOC_MAX_BYTES
+    assert call(big, L=4) == B.PRISM_ENOSPACE
+    assert "scratch" in B.status_str(B.PRISM_ENOSPACE)
 
 
 def test_wait_giveups_rejects_null(lib):
