@@ -84,6 +84,14 @@ bool decode_supported(int dk, int dv);
 hipError_t launch_scan(const ScanArgs& p, hipStream_t stream);
 bool scan_supported(bool bf16, int dk, int dv, int dv_slice);
 
+// Two-pass bf16 scan: the per-chunk matrices of every (chunk, head) at once
+// (chunk_gram.hip, into gram_workspace_bytes of device memory), then the
+// sequential state products from them (chunk_scan_state.hip).
+size_t gram_workspace_bytes(int n_seqs, int total_tokens, int heads);
+hipError_t launch_gram(const ScanArgs& p, void* ws, hipStream_t stream);
+hipError_t launch_scan_state(const ScanArgs& p, const void* mats, hipStream_t stream);
+bool scan_state_supported(int dk, int dv);
+
 // fp32 scan token by token (fp32 inputs at dk = 128, whose chunkwise tiles
 // exceed the LDS); any dk in {64, 128}, dv a multiple of 32.
 hipError_t launch_scan_f32_recurrent(const ScanArgs& p, hipStream_t stream);

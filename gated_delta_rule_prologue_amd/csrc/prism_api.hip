@@ -158,6 +158,19 @@ int split_for(const prism_dims* d)
     return prism::split_segments(d->n_seqs, d->heads, d->dk, d->dv, d->total_tokens, device_cus());
 }
 
+// The two-pass bf16 scan (per-chunk matrices of all chunks at once, then the
+// WY state kernel) is opt-in with PRISM_SCAN_TWOPASS=1 (and a workspace): on
+// MI355X it is slower than the single fused kernel (the matrices make a round
+// trip through HBM, and the state kernel's helpers bound its chunk rate).
+bool use_two_pass(const prism_dims* d)
+{
+    return d->dtype == PRISM_BF16 && env_int("PRISM_SCAN_GENERIC", 0) == 0 &&
+           env_int("PRISM_SCAN_TWOPASS", 0) == 1 && prism::scan_state_supported(d->dk, d->dv) &&
+           d->total_tokens > 0;
+}
+
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
 size_t kw_bytes(const prism_dims* d)
 {
     size_t n = (size_t)d->total_tokens * (size_t)d->heads * (size_t)d->dk * elem_bytes(d);
@@ -236,6 +249,12 @@ prism_status scan_impl(const prism_dims* d, const void* q, const void* k, const 
     const int P = split_ws ? split_for(d) : 1;
     if (P >= 2)
         return from_hip(prism::launch_split_scan(p, P, split_ws, (hipStream_t)stream));
+    if (split_ws && use_two_pass(d)) {
+        hipError_t e = prism::launch_gram(p, split_ws, (hipStream_t)stream);
+        if (e == hipSuccess)
+            e = prism::launch_scan_state(p, split_ws, (hipStream_t)stream);
+        return from_hip(e);
+    }
     if (use_bf16_kernel(d, p.dv_slice))
         return from_hip(prism::launch_scan_bf16(p, (hipStream_t)stream));
     return from_hip(prism::launch_scan(p, (hipStream_t)stream));
@@ -296,8 +315,12 @@ size_t prism_scan_workspace_bytes(const prism_dims* d)
 {
     if (!dims_ok(d))
         return 0;
-    return prism::split_workspace_bytes(d->n_seqs, d->heads, d->dk, d->dv, d->total_tokens,
-                                        split_for(d));
+    const int P = split_for(d);
+    if (P >= 2)
+        return prism::split_workspace_bytes(d->n_seqs, d->heads, d->dk, d->dv, d->total_tokens, P);
+    if (use_two_pass(d))
+        return round256(prism::gram_workspace_bytes(d->n_seqs, d->total_tokens, d->heads));
+    return 0;
 }
 
 size_t prism_workspace_bytes(const prism_dims* d, int L)

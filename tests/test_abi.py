@@ -70,10 +70,21 @@ def test_wait_giveups_rejects_null(lib):
     assert lib.prism_scan_wait_giveups(None, 0) == B.PRISM_EINVAL
 
 
-def test_workspace_bytes(lib):
+def test_workspace_bytes(lib, monkeypatch):
+    """prism_workspace_bytes: the write keys (input dtype, 256-byte rounded)
+    plus, for the opt-in two-pass bf16 scan, the per-chunk matrices: 20 KB (T,
+    A_kkw, A_qkw, -A_qk as ten bf16 16x16 blocks each) per head and virtual
+    chunk, floor(T / 64) + n_seqs virtual chunks."""
     from gated_delta_rule_prologue_amd import binding as B
+    up = lambda x: (x + 255) // 256 * 256
     d = B.make_dims(8, 16384, 6, 128, 128, B.PRISM_BF16)
+    monkeypatch.delenv("PRISM_SCAN_TWOPASS", raising=False)
     assert B.workspace_bytes(d, 4) == 16384 * 6 * 128 * 2
+    assert B.scan_workspace_bytes(d) == 0
+    monkeypatch.setenv("PRISM_SCAN_TWOPASS", "1")
+    assert B.workspace_bytes(d, 4) == 16384 * 6 * 128 * 2 + up((16384 // 64 + 8) * 6 * 20480)
+    assert B.scan_workspace_bytes(d) == up((16384 // 64 + 8) * 6 * 20480)
+    monkeypatch.delenv("PRISM_SCAN_TWOPASS")
     d32 = B.make_dims(1, 3, 1, 64, 64, B.PRISM_F32)
     assert B.workspace_bytes(d32, 2) == 768
     assert B.workspace_bytes(B.make_dims(1, 0, 1, 64, 64, B.PRISM_BF16), 1) == 256
@@ -228,7 +239,8 @@ def test_scan_workspace_bytes_for_forced_split(lib, monkeypatch):
     """With PRISM_SPLIT=P the scan workspace holds o' (bf16 [T, H, dk]), S_loc and
     S_in (fp32 [n P, H, dk, dv]), M (fp32 [n P, H, dk, dk]) and the segment
     offsets, each rounded up to 256 bytes; prism_workspace_bytes adds the write
-    keys.  Off (PRISM_SPLIT=0), and for fp32 inputs, it is zero."""
+    keys.  Off (PRISM_SPLIT=0), and for fp32 inputs, it is zero (the
+    opt-in two-pass scan then needs its per-chunk matrices)."""
     from gated_delta_rule_prologue_amd import binding as B
     up = lambda x: (x + 255) // 256 * 256
     n, T, H, dk, dv, P = 2, 1000, 3, 128, 64, 3
@@ -241,5 +253,8 @@ def test_scan_workspace_bytes_for_forced_split(lib, monkeypatch):
     assert B.workspace_bytes(d, 4) == up(T * H * dk * 2) + want
     monkeypatch.setenv("PRISM_SPLIT", "0")
     assert B.scan_workspace_bytes(d) == 0
+    monkeypatch.setenv("PRISM_SCAN_TWOPASS", "1")
+    assert B.scan_workspace_bytes(d) == up((T // 64 + n) * H * 20480)   # two-pass matrices
+    monkeypatch.delenv("PRISM_SCAN_TWOPASS")
     monkeypatch.setenv("PRISM_SPLIT", str(P))
     assert B.scan_workspace_bytes(B.make_dims(n, T, H, 64, 64, B.PRISM_F32)) == 0

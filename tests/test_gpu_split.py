@@ -100,4 +100,6 @@ def test_long_context_takes_the_split():
     assert binding.workspace_bytes(d, w.L) > kw
     lm = BY_NAME["lm-130m-layer"]
     d2 = binding.make_dims(8, 16384, lm.heads, lm.dk, lm.dv, binding.PRISM_BF16)
+    # the LM layer does not split: the write keys only (the fused scan needs no scratch)
+    assert binding.scan_workspace_bytes(d2) == 0
     assert binding.workspace_bytes(d2, lm.L) == 16384 * lm.heads * lm.dk * 2

@@ -117,10 +117,12 @@ def test_fwd_resume_matches_oracle(w):
 @pytest.mark.parametrize("dk", [64, 128])
 def test_fwd_resume_every_scan_kernel(dk, kernel, monkeypatch):
     """The start state enters every bf16 scan kernel (slices of 16 and 32
-    columns for the wavefront-specialised kernels, 64 for the others)."""
+    columns for the wavefront-specialised kernels, 32 for the two-pass scan,
+    32 and 64 for the others)."""
     for key, val in SCAN_KERNELS[kernel].items():
         monkeypatch.setenv(key, val)
-    slices = [16, 32] if kernel.startswith("specialised") else [32, 64]
+    slices = ([16, 32] if kernel.startswith("specialised") else [32] if kernel == "twopass"
+              else [32, 64])
     inp = make_inputs(W(dtype="bf16", dk=dk, dv=64, L=3, lengths=(140, 3, 0, 64, 65)))
     for dvs in slices:
         monkeypatch.setenv("PRISM_DV_SLICE", str(dvs))
