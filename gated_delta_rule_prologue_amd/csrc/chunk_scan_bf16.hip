@@ -688,6 +688,7 @@ struct LayoutWS {
 struct WsCtx {
     unsigned char* smem;
     const uint16_t *q, *k, *kw, *v, *g, *b;
+    const uint16_t *u, *a, *h, *cw;              // prologue inputs (fused write keys only)
     uint16_t* o;
     const float* s_init;
     float* s_final;
@@ -810,6 +811,148 @@ __device__ __forceinline__ void invert_diag(const uint16_t* scr, uint16_t* Akk, 
     store_trow(Akk + (lg * 16 + li) * LDC + lg * 16, x);
 }
 
+// ---- Fused write keys (LF = L levels): a chunk's kw rows computed in place of
+// being read from memory, with the prologue's arithmetic (PRISM pages: WeChat
+// ICML 2026 summary, sections 消除 Token 间串行 and 消除 Step 间串行;
+// gist.science summary of arXiv 2602.10796, section 2.2):
+//   r_1  = sum_m w[e,i,m] k[t-3+m]   (ShortConv, taps before the sequence start read 0)
+//   r_{l+1} = r_l (1 - a_l h_l),  kw = b k + sum_{l=1..L-1} a_l r_l u_l.
+// Four wavefronts (r = 0..3) share a chunk: lane (channel piece p = lane % (D/8),
+// token strip) walks ST consecutive tokens of 8 channels, so the conv taps stay
+// in registers; with L <= 4 the inputs of token j + 1 are loaded while token j
+// is computed.
+// Every load is a bounded buffer load: taps before the sequence start and
+// tokens past the chunk's end read zeros (a zero kw row there).
+template <int D>
+__device__ __forceinline__ void load_taps(const WsCtx& c, float (&w)[8][4])
+{
+    const int pc = (c.lane % (D / 8)) * 8;
+    const uint16_t* p = c.cw + ((int64_t)c.e * D + pc) * 4;    // conv_w [H][D][4]
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        const uint4 v = *reinterpret_cast<const uint4*>(p + 8 * x);
+        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int lo = 8 * x + 2 * i, hi = lo + 1;
+            w[lo / 4][lo % 4] = __uint_as_float(wv[i] << 16);
+            w[hi / 4][hi % 4] = __uint_as_float(wv[i] & 0xffff0000u);
+        }
+    }
+}
+
+template <int D, int LF>
+__device__ __forceinline__ void fused_kw(const WsCtx& c, uint16_t* sKW, int ch, int r, const float (&w)[8][4])
+{
+    constexpr int LDD = D + 8;
+    constexpr int NPC = D / 8;                   // 16-byte channel pieces per row
+    constexpr int SPW = 64 / NPC;                // token strips per wavefront
+    constexpr int ST = kC / (4 * SPW);           // tokens per strip
+    constexpr int NS = LF - 1;                   // u, a slots (levels 1 .. L-1)
+    constexpr int NH = LF > 2 ? LF - 2 : 1;      // h slots read (the last one never is)
+    constexpr uint32_t fl = 0x00020000;
+    const int lane = c.lane;
+    const int pc = (lane % NPC) * 8;
+    const int tl0 = (r * SPW + lane / NPC) * ST; // first token of the strip, chunk-relative
+    const int c0 = c.seq0 + ch * kC;
+    const int nt = __builtin_amdgcn_readfirstlane(max(0, min(kC, c.seq1 - c0)));
+    const int hb = max(c.seq0, c0 - 3);          // first k row a tap may read
+    const int rowQK = (int)c.rowQK, lrow = c.H * NS * D;
+    const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(c.k + (int64_t)hb * rowQK + c.e * D),
+                                                      0, (c0 + nt - hb) * rowQK * 2, fl);
+    const int64_t lbase = (int64_t)c0 * lrow + (int64_t)c.e * NS * D;
+    const auto ru = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(c.u + lbase), 0, nt * lrow * 2, fl);
+    const auto ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(c.a + lbase), 0, nt * lrow * 2, fl);
+    const auto rh = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(c.h + lbase), 0, nt * lrow * 2, fl);
+    const auto rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(c.b + (int64_t)c0 * c.H + c.e), 0,
+                                                      nt * c.H * 2, fl);
+    auto ld = [&](__amdgpu_buffer_rsrc_t rs, int off) {
+        return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+    };
+    auto unpack = [](const uint4& v, float* out) {
+        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[2 * i] = __uint_as_float(wv[i] << 16);
+            out[2 * i + 1] = __uint_as_float(wv[i] & 0xffff0000u);
+        }
+    };
+    // k row of chunk-relative token tl (negative offsets: before the range, zero)
+    auto koff = [&](int tl) { return ((c0 + tl - hb) * rowQK + pc) * 2; };
+    struct In {
+        uint4 k, u[NS], a[NS], h[NH];
+        uint16_t b;
+    };
+    auto fetch = [&](int tl, In& x) {
+        x.k = ld(rk, koff(tl));
+        const int lo = (tl * lrow + pc) * 2;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            x.u[s] = ld(ru, lo + s * D * 2);
+            x.a[s] = ld(ra, lo + s * D * 2);
+            if (s < LF - 2)
+                x.h[s] = ld(rh, lo + s * D * 2);
+        }
+        x.b = __builtin_amdgcn_raw_buffer_load_b16(rb, tl * c.H * 2, 0, 0);
+    };
+    // two input sets (token j + 1 in flight while token j is computed) where
+    // they fit the registers (L <= 4); one otherwise
+    constexpr bool PIPE = LF <= 4;
+    float x1[8], x2[8], x3[8];                   // k at t - 1, t - 2, t - 3
+    {
+        const uint4 h1 = ld(rk, koff(tl0 - 1)), h2 = ld(rk, koff(tl0 - 2)), h3 = ld(rk, koff(tl0 - 3));
+        unpack(h1, x1);
+        unpack(h2, x2);
+        unpack(h3, x3);
+    }
+    In X[PIPE ? 2 : 1];
+    fetch(tl0, X[0]);
+#pragma unroll
+    for (int j = 0; j < ST; ++j) {
+        if constexpr (PIPE) {
+            if (j + 1 < ST)
+                fetch(tl0 + j + 1, X[(j + 1) & 1]);
+        } else if (j > 0) {
+            SCHED_FENCE();
+            fetch(tl0 + j, X[0]);
+        }
+        const In& x = X[PIPE ? (j & 1) : 0];
+        float kt[8], rr[8], acc[8];
+        unpack(x.k, kt);
+        const float bt = bf16_to_f32(x.b);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            rr[i] = w[i][3] * kt[i] + w[i][2] * x1[i] + w[i][1] * x2[i] + w[i][0] * x3[i];
+            acc[i] = bt * kt[i];
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            float av[8], uv[8];
+            unpack(x.a[s], av);
+            unpack(x.u[s], uv);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                acc[i] += av[i] * rr[i] * uv[i];
+            if (s < LF - 2) {
+                float hv[8];
+                unpack(x.h[s], hv);
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    rr[i] *= 1.f - av[i] * hv[i];
+            }
+        }
+        *reinterpret_cast<uint4*>(sKW + (tl0 + j) * LDD + pc) =
+            make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                       pack_bf16x2(acc[6], acc[7]));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            x3[i] = x2[i];
+            x2[i] = x1[i];
+            x1[i] = kt[i];
+        }
+    }
+}
+
 // Helper wavefront: loads and stores the 16-token row blocks LB0 .. LB0 + NLB - 1
 // of q, k, kw, v (NLB may be 0), and builds the Gram pairs of its role from the
 // rows in LDS (role 7 has none).  With GATES it also publishes the gate vectors.
@@ -819,10 +962,15 @@ __device__ __forceinline__ void invert_diag(const uint16_t* scr, uint16_t* Akk, 
 // wait: both writers reach them before the phase barrier), inverts the four
 // diagonal blocks in one pass and stores T_tt with the phase-B stores.
 // SLOT: this wavefront's row of decay sums in LDS.
+// LF > 0: the write keys are fused (computed, not read): the row movers leave
+// kw alone, and the Gram helper with KWR = r >= 0 computes its quarter of every
+// chunk's kw rows (fused_kw) in phase B, two chunks ahead, where the kw rows
+// would otherwise have been stored.
 template <int D, int DVS, int ROLE, int LB0, int NLB, bool GATES, int SLOT, bool INV = false,
-          int SIG = -1, bool EARLY = false>
+          int SIG = -1, bool EARLY = false, int LF = 0, int KWR = -1>
 __device__ __forceinline__ void helper_loop(const WsCtx& c)
 {
+    static_assert(KWR < 0 || (LF > 0 && NLB == 0), "fused write keys: Gram helpers only");
     using L = Layout<D, DVS>;
     using P = Pairs<ROLE>;
     constexpr int LDD = L::LDD, LDC = L::LDC, LDV = L::LDV;
@@ -886,7 +1034,8 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
         for (int ks = 0; ks < KS; ++ks) {
             const int off = (((LB0 + u) * 16 + ks * RPI + pr) * rowQK + pc) * 2;
             rk[u][ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r.k, off, 0, 0));
-            rw[u][ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r.kw, off, 0, 0));
+            if constexpr (LF == 0)
+                rw[u][ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r.kw, off, 0, 0));
             rq[u][ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r.q, off, 0, 0));
         }
         const int offv = (((LB0 + u) * 16 + lane / VL) * rowV + (lane % VL) * 8) * 2;
@@ -912,8 +1061,9 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
                     *reinterpret_cast<uint4*>(sK + off) = rk[u][ks];
                     *reinterpret_cast<uint4*>(sQ + off) = rq[u][ks];
                 }
-                if (parts != 1)
-                    *reinterpret_cast<uint4*>(sKW + off) = rw[u][ks];
+                if constexpr (LF == 0)
+                    if (parts != 1)
+                        *reinterpret_cast<uint4*>(sKW + off) = rw[u][ks];
             }
             if (parts != 1 && lane < 16 * VL)
                 *reinterpret_cast<uint4*>(sV + ((LB0 + u) * 16 + lane / VL) * LDV + (lane % VL) * 8) = rv[u];
@@ -1155,6 +1305,9 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
             store_trow(Akk + (lg * 16 + li) * LDC + lg * 16, tinv);
     };
 
+    float taps[8][4];
+    if constexpr (KWR >= 0)
+        load_taps<D>(c, taps);
     const int nch = c.nchunks;
     if (nch > 0)
         load(0);
@@ -1163,13 +1316,18 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
         store_rows(0, 0);
         if (nch > 1)
             load(1);
+        if constexpr (KWR >= 0)
+            fused_kw<D, LF>(c, m.KW(0), 0, KWR, taps);
     }
     lds_barrier();                               // rows of chunk 0 visible
     if (nch > 0) {
         prep(0, -1);
         write_mats();
-        if (nch > 1)
+        if (nch > 1) {
             store_rows(1, 0);
+            if constexpr (KWR >= 0)
+                fused_kw<D, LF>(c, m.KW(1), 1, KWR, taps);
+        }
     }
     lds_barrier();                               // matrices of chunk 0 (A_ii in the scratch)
     lds_barrier();                               // T_ii of chunk 0 (four wavefronts: a state wavefront)
@@ -1182,8 +1340,12 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
         // phase B
         if (ch + 1 < nch)
             write_mats();
-        if (ch + 2 < nch)
+        if (ch + 2 < nch) {
             store_rows(ch + 2, EARLY ? 1 : 0);
+            // kw rows of chunk ch + 2 into the buffer whose kw chunk ch no longer needs
+            if constexpr (KWR >= 0)
+                fused_kw<D, LF>(c, m.KW(ch + 2), ch + 2, KWR, taps);
+        }
         lds_barrier();
     }
 }
@@ -1255,7 +1417,9 @@ __device__ __forceinline__ void state_loop(const WsCtx& c, int jb)
 // Wavefront w runs on SIMD w % 4: with eight, the two state wavefronts share
 // their SIMDs with the two row movers, and each remaining SIMD runs two Gram
 // helpers (five pairs per SIMD).
-template <int D, int DVS, int NW>
+// LF > 0: the write keys are computed in the kernel from u, a, h and the conv
+// taps cw (L = LF levels, closed form, no carried history) instead of read from kw.
+template <int D, int DVS, int NW, int LF = 0>
 __global__ __launch_bounds__(NW * 64) void scan_ws_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ kw, const uint16_t* __restrict__ v,
@@ -1263,8 +1427,11 @@ __global__ __launch_bounds__(NW * 64) void scan_ws_kernel(
     const int32_t* __restrict__ cu, int H, int DV, int n_slices,
     const float* __restrict__ s_init, uint16_t* __restrict__ o,
     float* __restrict__ s_final, int split_block, int DV1, int n_slices1, uint16_t* __restrict__ o1,
-    float* __restrict__ s_final1, int skip1)
+    float* __restrict__ s_final1, int skip1, const uint16_t* __restrict__ u = nullptr,
+    const uint16_t* __restrict__ a = nullptr, const uint16_t* __restrict__ h = nullptr,
+    const uint16_t* __restrict__ cw = nullptr)
 {
+    static_assert(LF == 0 || NW == 8, "fused write keys: the eight-wavefront kernel");
     using Ly = LayoutWS<D, DVS>;
     constexpr int NJ = DVS / 16;
     static_assert(NJ == 1 || NJ == 2, "one or two state wavefronts");
@@ -1295,6 +1462,7 @@ __global__ __launch_bounds__(NW * 64) void scan_ws_kernel(
     WsCtx c;
     c.smem = smem;
     c.q = q; c.k = k; c.g = g; c.b = b;
+    c.u = u; c.a = a; c.h = h; c.cw = cw;
     c.kw = job1 ? nullptr : kw;
     c.v = job1 ? nullptr : v;
     c.o = job1 ? o1 : o;
@@ -1325,13 +1493,14 @@ __global__ __launch_bounds__(NW * 64) void scan_ws_kernel(
     if (wave < NJ) {
         state_loop<D, DVS, NW == 4, NW == 8>(c, wave);
     } else if constexpr (NW == 8) {
+        constexpr int K0 = LF ? 0 : -1, K1 = LF ? 1 : -1, K2 = LF ? 2 : -1, K3 = LF ? 3 : -1;
         switch (wave) {
-        case 2: helper_loop<D, DVS, 4, 0, 0, true, 0, false, 0>(c); break;   // (0,0) (1,1), gates
-        case 3: helper_loop<D, DVS, 6, 0, 0, false, 1>(c); break;             // (1,0) (2,0) (2,1)
-        case 4: helper_loop<D, DVS, 7, 0, 2, false, 0, true, -1, true>(c); break;   // rows 0, 1; T_tt
-        case 5: helper_loop<D, DVS, 7, 2, 2, false, 0, false, -1, true>(c); break;  // rows of blocks 2, 3
-        case 6: helper_loop<D, DVS, 5, 0, 0, false, 2, false, 1>(c); break;  // (2,2) (3,3)
-        default: helper_loop<D, DVS, 3, 0, 0, false, 3>(c); break;            // (3,0) (3,1) (3,2)
+        case 2: helper_loop<D, DVS, 4, 0, 0, true, 0, false, 0, false, LF, K0>(c); break;   // (0,0) (1,1), gates
+        case 3: helper_loop<D, DVS, 6, 0, 0, false, 1, false, -1, false, LF, K1>(c); break; // (1,0) (2,0) (2,1)
+        case 4: helper_loop<D, DVS, 7, 0, 2, false, 0, true, -1, true, LF>(c); break;       // rows 0, 1; T_tt
+        case 5: helper_loop<D, DVS, 7, 2, 2, false, 0, false, -1, true, LF>(c); break;      // rows of blocks 2, 3
+        case 6: helper_loop<D, DVS, 5, 0, 0, false, 2, false, 1, false, LF, K2>(c); break;  // (2,2) (3,3)
+        default: helper_loop<D, DVS, 3, 0, 0, false, 3, false, -1, false, LF, K3>(c); break; // (3,0) (3,1) (3,2)
         }
     } else if constexpr (NJ == 2) {              // diagonal pairs | six off-diagonal pairs
         if (wave == 2)
@@ -1360,6 +1529,22 @@ static hipError_t launch_ws(const ScanArgs& p, hipStream_t stream)
                        (const uint16_t*)p.v, (const uint16_t*)p.g, (const uint16_t*)p.b,
                        p.cu_seqlens, p.heads, p.dv, n_slices, p.s_init, (uint16_t*)p.o,
                        p.s_final, 0x7fffffff, 0, 1, nullptr, nullptr, 0);
+    return hipGetLastError();
+}
+
+template <int D, int LF>
+static hipError_t launch_fused(const ScanArgs& p, hipStream_t stream)
+{
+    const int n_slices = p.dv / 32;
+    const int64_t blocks = (int64_t)p.n_seqs * p.heads * n_slices;
+    if (blocks == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL((scan_ws_kernel<D, 32, 8, LF>), dim3((unsigned)blocks), dim3(512), 0, stream,
+                       (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.kw,
+                       (const uint16_t*)p.v, (const uint16_t*)p.g, (const uint16_t*)p.b,
+                       p.cu_seqlens, p.heads, p.dv, n_slices, p.s_init, (uint16_t*)p.o,
+                       p.s_final, 0x7fffffff, 0, 1, nullptr, nullptr, 0, (const uint16_t*)p.u,
+                       (const uint16_t*)p.a, (const uint16_t*)p.h, (const uint16_t*)p.conv_w);
     return hipGetLastError();
 }
 
@@ -1428,10 +1613,24 @@ hipError_t read_wait_giveups(unsigned int* count, bool reset)
     return e;
 }
 
+// dk = 128 with L = 8 does not fit the Gram helpers' registers (it would spill)
+bool scan_fused_kw_supported(int dk, int dv, int L)
+{
+    return scan_bf16_supported(dk, dv, 32) && (L == 4 || (L == 8 && dk == 64));
+}
+
 hipError_t launch_scan_bf16(const ScanArgs& p, hipStream_t s)
 {
     if (!scan_bf16_supported(p.dk, p.dv, p.dv_slice))
         return hipErrorInvalidValue;
+    if (p.fused_L > 0) {
+        if (!scan_fused_kw_supported(p.dk, p.dv, p.fused_L) || !p.specialised || p.ws_waves != 8 ||
+            p.dv_slice != 32 || !p.u || !p.a || !p.h || !p.conv_w)
+            return hipErrorInvalidValue;
+        if (p.dk == 64)
+            return p.fused_L == 4 ? bf16scan::launch_fused<64, 4>(p, s) : bf16scan::launch_fused<64, 8>(p, s);
+        return bf16scan::launch_fused<128, 4>(p, s);
+    }
     if (p.specialised) {
         const bool w8 = p.ws_waves == 8;
         if (p.dk == 64) {

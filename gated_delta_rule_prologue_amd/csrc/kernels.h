@@ -29,6 +29,11 @@ struct ScanArgs {
     const float* s_init;            // [n_seqs, H, dk, dv] start states, or null (zero)
     void* o;
     float* s_final;
+    // fused write keys (bf16, eight-wavefront kernel): fused_L = L > 0 computes kw
+    // from k, u, a, h, b and conv_w inside the scan (closed form, no carried
+    // history) instead of reading kw; 0 reads kw
+    int fused_L = 0;
+    const void *u = nullptr, *a = nullptr, *h = nullptr, *conv_w = nullptr;
 };
 
 hipError_t launch_prologue(const PrologueArgs& p, hipStream_t stream);
@@ -99,6 +104,7 @@ bool scan_f32_recurrent_supported(int dk, int dv);
 
 // bf16 chunk scan with the register-resident state path.
 hipError_t launch_scan_bf16(const ScanArgs& p, hipStream_t stream);
+bool scan_fused_kw_supported(int dk, int dv, int L);
 // `a` on the eight-wavefront kernel (32-column slices) and, in the same launch,
 // `m`: the transitions alone over the same sequences (m.dv = dk, start S = I,
 // no write term), writing m.o and m.s_final; with skip > 1 the sequences

@@ -216,9 +216,28 @@ prism_status prologue_impl(const prism_dims* d, const void* k, const void* u, co
     return from_hip(prism::launch_prologue(p, (hipStream_t)stream));
 }
 
+// Fused write keys (PRISM_FUSED_KW=1): prism_fwd computes kw inside the scan
+// (the eight-wavefront kernel's Gram helpers) instead of launching the prologue,
+// where that kernel serves the shape: bf16, L = 4 or 8, the closed-form chain,
+// no carried history, 32-column slices, no segment split or two-pass scan.
+bool use_fused_kw(const prism_dims* d, int L, int residual, const void* k_hist)
+{
+    return env_int("PRISM_FUSED_KW", 0) == 1 && d->dtype == PRISM_BF16 &&
+           residual == PRISM_RESIDUAL_LINEAR && !k_hist &&
+           prism::scan_fused_kw_supported(d->dk, d->dv, L) && use_bf16_kernel(d, 32) &&
+           pick_dv_slice(d) == 32 && ws8_enabled() && split_for(d) < 2 && !use_two_pass(d) &&
+           d->total_tokens > 0;
+}
+
+struct FusedKw {
+    int L = 0;
+    const void *u = nullptr, *a = nullptr, *h = nullptr, *conv_w = nullptr;
+};
+
 prism_status scan_impl(const prism_dims* d, const void* q, const void* k, const void* kw,
                        const void* v, const void* g, const void* b, const int32_t* cu_seqlens,
-                       const float* S_init, void* o, float* S_final, void* split_ws, void* stream)
+                       const float* S_init, void* o, float* S_final, void* split_ws, void* stream,
+                       const FusedKw& fk = FusedKw())
 {
     if (!dims_ok(d))
         return PRISM_EINVAL;
@@ -244,6 +263,11 @@ prism_status scan_impl(const prism_dims* d, const void* q, const void* k, const 
     p.s_init = S_init;
     p.o = o;
     p.s_final = S_final;
+    if (fk.L > 0) {
+        p.fused_L = fk.L;
+        p.u = fk.u; p.a = fk.a; p.h = fk.h; p.conv_w = fk.conv_w;
+        return from_hip(prism::launch_scan_bf16(p, (hipStream_t)stream));
+    }
     if (use_f32_recurrent(d))
         return from_hip(prism::launch_scan_f32_recurrent(p, (hipStream_t)stream));
     const int P = split_ws ? split_for(d) : 1;
@@ -279,12 +303,20 @@ prism_status fwd_impl(const prism_dims* d, const void* q, const void* k, const v
     prism_status st = check_scan_shape(d);
     if (st != PRISM_OK)
         return st;
-    st = prologue_impl(d, k, u, a, h, b, conv_w, k_hist, cu_seqlens, L, residual, workspace,
-                       stream);
-    if (st != PRISM_OK)
-        return st;
-    st = scan_impl(d, q, k, workspace, v, g, b, cu_seqlens, S_init, o, S_final,
-                   static_cast<unsigned char*>(workspace) + kw_bytes(d), stream);
+    if (use_fused_kw(d, L, residual, k_hist)) {
+        FusedKw fk;
+        fk.L = L;
+        fk.u = u; fk.a = a; fk.h = h; fk.conv_w = conv_w;
+        st = scan_impl(d, q, k, workspace, v, g, b, cu_seqlens, S_init, o, S_final,
+                       static_cast<unsigned char*>(workspace) + kw_bytes(d), stream, fk);
+    } else {
+        st = prologue_impl(d, k, u, a, h, b, conv_w, k_hist, cu_seqlens, L, residual, workspace,
+                           stream);
+        if (st != PRISM_OK)
+            return st;
+        st = scan_impl(d, q, k, workspace, v, g, b, cu_seqlens, S_init, o, S_final,
+                       static_cast<unsigned char*>(workspace) + kw_bytes(d), stream);
+    }
     if (st != PRISM_OK || !k_hist_out)
         return st;
     // after the prologue on the same stream: k_hist_out may be k_hist itself
