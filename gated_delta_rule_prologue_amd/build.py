@@ -25,9 +25,10 @@ LIB = os.path.join(PKG, "libprism.so")
 SOURCES = ["prism_api.hip", "prologue.hip", "prologue_bf16.hip", "prologue_f32.hip",
            "prologue_bf16_ext.hip", "prologue_f32_ext.hip", "chunk_scan.hip",
            "chunk_scan_bf16.hip", "decode.hip", "long_seq.hip", "backward.hip",
-           "scan_f32_recurrent.hip", "chunk_gram.hip", "chunk_scan_state.hip"]
+           "scan_f32_recurrent.hip", "chunk_gram.hip", "chunk_scan_state.hip",
+           "backward_chunk.hip"]
 CHECKED = ["chunk_scan_bf16.hip", "chunk_scan.hip", "backward.hip", "chunk_gram.hip",
-           "chunk_scan_state.hip"]   # MFMA chains, DPP
+           "chunk_scan_state.hip", "backward_chunk.hip"]   # MFMA chains, DPP
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

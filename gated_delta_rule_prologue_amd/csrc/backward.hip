@@ -748,6 +748,22 @@ static hipError_t launch_bwd_T(const BwdArgs& p, hipStream_t s)
     return launch_wk<T>(p, dkw, dim3((unsigned)((threads + 255) / 256)), s);
 }
 
+hipError_t launch_write_key_bwd(const BwdArgs& p, const float* dkw, hipStream_t s)
+{
+    if (!bwd_supported(p.dk, p.dv) || p.L < 1 || p.L > 16)
+        return hipErrorInvalidValue;
+    const int64_t nconv = (int64_t)p.heads * p.dk * 4;
+    if (nconv > 0)
+        hipLaunchKernelGGL(bwd::zero_kernel, dim3((unsigned)((nconv + 255) / 256)), dim3(256), 0, s, p.gconv,
+                           nconv);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || p.total_tokens == 0)
+        return err;
+    const int64_t threads = ((int64_t)(p.total_tokens + bwd::kC - 1) / bwd::kC) * p.heads * p.dk;
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    return p.bf16 ? launch_wk<uint16_t>(p, dkw, grid, s) : launch_wk<float>(p, dkw, grid, s);
+}
+
 hipError_t launch_bwd(const BwdArgs& p, hipStream_t s)
 {
     if (!bwd_supported(p.dk, p.dv) || p.L < 1 || p.L > 16)

@@ -609,7 +609,9 @@ __device__ __forceinline__ void state_chunk(f32x4_t (&S)[D / 16], const unsigned
     //      rows past the chunk's last token fall outside the buffer range
     const int c0 = c.seq0 + ch * kC;
     const int nt = chunk_tokens(c, ch);
-    const __amdgpu_buffer_rsrc_t orsrc = rsrc(c.o + (int64_t)c0 * c.rowV, nt * (int)c.rowV * 2);
+    // (no o: an empty range, the stores are dropped)
+    const __amdgpu_buffer_rsrc_t orsrc =
+        rsrc(c.o ? c.o + (int64_t)c0 * c.rowV : c.k, c.o ? nt * (int)c.rowV * 2 : 0);
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
         const int t = tb * 16 + li;
@@ -624,7 +626,8 @@ __global__ __launch_bounds__(kWaves * 64) void scan_state_kernel(
     const uint16_t* __restrict__ kw, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ g, const uint16_t* __restrict__ b,
     const int32_t* __restrict__ cu, int H, int DV, int n_slices, const float* __restrict__ s_init,
-    const uint16_t* __restrict__ mats, uint16_t* __restrict__ o, float* __restrict__ s_final)
+    const uint16_t* __restrict__ mats, uint16_t* __restrict__ o, float* __restrict__ s_final,
+    uint16_t* __restrict__ ck = nullptr, uint16_t* __restrict__ ckT = nullptr)
 {
     using Ly = Lay<D>;
     constexpr int NI = D / 16;
@@ -662,14 +665,31 @@ __global__ __launch_bounds__(kWaves * 64) void scan_state_kernel(
         }
         lds_barrier();                           // chunk 0 prepared
         for (int ch = 0; ch < c.nchunks; ++ch) {
+            if (ck) {
+                // the chunk's start state, bf16, as rows [dk][dv] and transposed [dv][dk]
+                // per (virtual chunk, head) (the chunkwise backward reads both)
+                const int64_t vc = (c.vbase + ch) * H + c.e;
+                const int col = c.j0 + jb * 16 + li;
+#pragma unroll
+                for (int ib = 0; ib < NI; ++ib) {
+                    const int r0 = ib * 16 + lg * 4;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        ck[(vc * D + r0 + r) * DV + col] = (uint16_t)(pack_bf16x2(S[ib][r], 0.f) & 0xffffu);
+                    *reinterpret_cast<uint2*>(ckT + (vc * DV + col) * D + r0) =
+                        make_uint2(pack_bf16x2(S[ib][0], S[ib][1]), pack_bf16x2(S[ib][2], S[ib][3]));
+                }
+            }
             state_chunk<D>(S, smem + (ch & 1) * Ly::szBuf, c, ch, jb);
             lds_barrier();
         }
+        if (s_final) {
 #pragma unroll
-        for (int ib = 0; ib < NI; ++ib) {
+            for (int ib = 0; ib < NI; ++ib) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                s_final[sb + (int64_t)(ib * 16 + lg * 4 + r) * DV + li] = S[ib][r];
+                for (int r = 0; r < 4; ++r)
+                    s_final[sb + (int64_t)(ib * 16 + lg * 4 + r) * DV + li] = S[ib][r];
+            }
         }
     } else {
         const int h = wave - 2;
@@ -696,7 +716,7 @@ bool scan_state_supported(int dk, int dv)
     return (dk == 64 || dk == 128) && dv > 0 && dv % stscan::kDVS == 0;
 }
 
-hipError_t launch_scan_state(const ScanArgs& p, const void* mats, hipStream_t stream)
+hipError_t launch_scan_state(const ScanArgs& p, const void* mats, hipStream_t stream, void* ck, void* ckT)
 {
     if (!p.bf16 || !scan_state_supported(p.dk, p.dv))
         return hipErrorInvalidValue;
@@ -709,7 +729,7 @@ hipError_t launch_scan_state(const ScanArgs& p, const void* mats, hipStream_t st
                        (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.kw,
                        (const uint16_t*)p.v, (const uint16_t*)p.g, (const uint16_t*)p.b,
                        p.cu_seqlens, p.heads, p.dv, n_slices, p.s_init, (const uint16_t*)mats,
-                       (uint16_t*)p.o, p.s_final);
+                       (uint16_t*)p.o, p.s_final, (uint16_t*)ck, (uint16_t*)ckT);
     return hipGetLastError();
 }
 

@@ -77,6 +77,28 @@ struct BwdArgs {
     float* ws;                      // bwd_workspace_floats(...) floats
 };
 size_t bwd_workspace_floats(int n_seqs, int total_tokens, int heads, int dk, int dv);
+
+// Chunkwise backward (bf16, backward_chunk.hip).  Pass B: the carried gradient
+// of every chunk's end state, from the last chunk to the first, as bf16
+// [virtual chunk][H][dk][dv] (dck) and [virtual chunk][H][dv][dk] (dckT), and
+// dS_init (fp32, optional).  p holds q, k, g, b, cu_seqlens and the shape.
+hipError_t launch_bwd_state(const ScanArgs& p, const void* dO, const void* mats, const float* dS_final,
+                            void* dck, void* dckT, float* dS_init, hipStream_t stream);
+struct BwdChunkBufs {
+    const void *dO, *mats, *ck, *ckT, *dck, *dckT;
+    void *xg, *drg;                 // X and dR, bf16 [T][H][dv]
+    float *gq, *gk, *gkw, *gv, *gg, *gb;
+    float *scal;                    // fp32 [3][T][H]
+    float *sdot;                    // fp32 [virtual chunk][H]
+};
+// Passes C1, C2: every gradient of the scan's inputs (q, k, kw, v, g, b) from
+// the checkpoints; p.kw holds the write keys.  Stores (no accumulation): dq,
+// dk, dkw, dv, dg, db are written whole.
+hipError_t launch_bwd_grads(const ScanArgs& p, const BwdChunkBufs& w, hipStream_t stream);
+// The write-key part of the backward pass alone (backward.hip): from dkw (fp32
+// [T][H][dk]) it writes du, da, dh, adds the write-key terms to dk and db (both
+// hold the scan's gradients on entry), and writes dconv_w (zeroed here first).
+hipError_t launch_write_key_bwd(const BwdArgs& p, const float* dkw, hipStream_t stream);
 bool bwd_supported(int dk, int dv);
 hipError_t launch_bwd(const BwdArgs& p, hipStream_t stream);
 
@@ -94,7 +116,10 @@ bool scan_supported(bool bf16, int dk, int dv, int dv_slice);
 // sequential state products from them (chunk_scan_state.hip).
 size_t gram_workspace_bytes(int n_seqs, int total_tokens, int heads);
 hipError_t launch_gram(const ScanArgs& p, void* ws, hipStream_t stream);
-hipError_t launch_scan_state(const ScanArgs& p, const void* mats, hipStream_t stream);
+// ck / ckT (optional): every chunk's start state, bf16, [virtual chunk][H][dk][dv]
+// and [virtual chunk][H][dv][dk]; p.o and p.s_final may be null (not written)
+hipError_t launch_scan_state(const ScanArgs& p, const void* mats, hipStream_t stream, void* ck = nullptr,
+                             void* ckT = nullptr);
 bool scan_state_supported(int dk, int dv);
 
 // fp32 scan token by token (fp32 inputs at dk = 128, whose chunkwise tiles

@@ -438,10 +438,48 @@ prism_status prism_fwd_resume(const prism_dims* d, const void* q, const void* k,
                     S_final, k_hist_out, workspace, workspace_bytes, stream);
 }
 
+// Chunkwise backward (PRISM_BWD_CHUNKED=1, bf16, dk and dv in {64, 128}): the
+// forward state products again with every chunk's start state kept (bf16), the
+// carried state gradient backwards chunk by chunk, then every input gradient
+// of all chunks at once on MFMA, then the write-key chain backwards.
+bool use_bwd_chunked(const prism_dims* d)
+{
+    return env_int("PRISM_BWD_CHUNKED", 0) == 1 && d->dtype == PRISM_BF16 &&
+           (d->dk == 64 || d->dk == 128) && (d->dv == 64 || d->dv == 128) && d->total_tokens > 0;
+}
+
+// Workspace of the chunkwise backward after kw, each part 256-byte aligned.
+struct BwdChunkLayout {
+    size_t mats, ck, ckT, dck, dckT, xg, drg, dkw, scal, sdot, total;
+};
+
+BwdChunkLayout bwd_chunk_layout(const prism_dims* d)
+{
+    BwdChunkLayout w;
+    const size_t nv = (size_t)(d->total_tokens / 64 + d->n_seqs) * d->heads;    // (virtual chunk, head)
+    const size_t st = round256(nv * d->dk * d->dv * 2);
+    const size_t tv = round256((size_t)d->total_tokens * d->heads * d->dv * 2);
+    size_t o = kw_bytes(d);
+    w.mats = o; o += round256(prism::gram_workspace_bytes(d->n_seqs, d->total_tokens, d->heads));
+    w.ck = o; o += st;
+    w.ckT = o; o += st;
+    w.dck = o; o += st;
+    w.dckT = o; o += st;
+    w.xg = o; o += tv;
+    w.drg = o; o += tv;
+    w.dkw = o; o += round256((size_t)d->total_tokens * d->heads * d->dk * 4);
+    w.scal = o; o += round256((size_t)3 * d->total_tokens * d->heads * 4);
+    w.sdot = o; o += round256(nv * 4);
+    w.total = o;
+    return w;
+}
+
 size_t prism_bwd_workspace_bytes(const prism_dims* d, int L)
 {
     if (!dims_ok(d) || L < 1 || L > PRISM_MAX_LEVELS)
         return 0;
+    if (use_bwd_chunked(d))
+        return bwd_chunk_layout(d).total;
     return kw_bytes(d) + prism::bwd_workspace_floats(d->n_seqs, d->total_tokens, d->heads, d->dk,
                                                      d->dv) * sizeof(float);
 }
@@ -490,8 +528,47 @@ prism_status prism_bwd_ex(const prism_dims* d, const void* q, const void* k, con
     p.gq = dq; p.gk = dk; p.gv = dv; p.gu = du; p.ga = da; p.gh = dh; p.gg = dg; p.gb = db;
     p.gconv = dconv_w;
     p.gs_init = dS_init;
-    p.ws = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + kw_bytes(d));
-    return from_hip(prism::launch_bwd(p, (hipStream_t)stream));
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    if (!use_bwd_chunked(d)) {
+        p.ws = reinterpret_cast<float*>(ws + kw_bytes(d));
+        return from_hip(prism::launch_bwd(p, (hipStream_t)stream));
+    }
+    const BwdChunkLayout w = bwd_chunk_layout(d);
+    prism::ScanArgs sp;
+    sp.bf16 = true;
+    sp.n_seqs = d->n_seqs;
+    sp.total_tokens = d->total_tokens;
+    sp.heads = d->heads;
+    sp.dk = d->dk;
+    sp.dv = d->dv;
+    sp.dv_slice = 32;
+    sp.specialised = false;
+    sp.ws_waves = 8;
+    sp.q = q; sp.k = k; sp.kw = workspace; sp.v = v; sp.g = g; sp.b = b;
+    sp.cu_seqlens = cu_seqlens;
+    sp.s_init = S_init;
+    sp.o = nullptr;
+    sp.s_final = nullptr;
+    prism::BwdChunkBufs cb;
+    cb.dO = dO;
+    cb.mats = ws + w.mats;
+    cb.ck = ws + w.ck; cb.ckT = ws + w.ckT; cb.dck = ws + w.dck; cb.dckT = ws + w.dckT;
+    cb.xg = ws + w.xg; cb.drg = ws + w.drg;
+    cb.gq = dq; cb.gk = dk; cb.gkw = reinterpret_cast<float*>(ws + w.dkw); cb.gv = dv;
+    cb.gg = dg; cb.gb = db;
+    cb.scal = reinterpret_cast<float*>(ws + w.scal);
+    cb.sdot = reinterpret_cast<float*>(ws + w.sdot);
+    const hipStream_t s = (hipStream_t)stream;
+    hipError_t e = prism::launch_gram(sp, ws + w.mats, s);
+    if (e == hipSuccess)
+        e = prism::launch_scan_state(sp, ws + w.mats, s, ws + w.ck, ws + w.ckT);
+    if (e == hipSuccess)
+        e = prism::launch_bwd_state(sp, dO, ws + w.mats, dS_final, ws + w.dck, ws + w.dckT, dS_init, s);
+    if (e == hipSuccess)
+        e = prism::launch_bwd_grads(sp, cb, s);
+    if (e == hipSuccess)
+        e = prism::launch_write_key_bwd(p, cb.gkw, s);
+    return from_hip(e);
 }
 
 prism_status prism_bwd(const prism_dims* d, const void* q, const void* k, const void* v,
