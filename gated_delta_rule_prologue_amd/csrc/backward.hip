@@ -38,7 +38,9 @@
 namespace prism {
 namespace bwd {
 
-constexpr int kC = 16;                           // token block of the write-key backward
+constexpr int kC = 16;                           // tokens of one wavefront of the write-key backward
+constexpr int kWkBlock = 64;                     // tokens of one workgroup of the write-key backward
+constexpr int kWkRows = 16;                      // token blocks per slab of the dconv_w reduction
 constexpr int kCols = 8;                         // value columns per wavefront of the scan backward
 constexpr int kMaxSeg = 8;                       // segments per sequence of the scan backward
 
@@ -491,13 +493,45 @@ __global__ __launch_bounds__(64) void scan_bwd_kernel(
     }
 }
 
-// One thread per (head e, channel i, block of 16 tokens): for each token of the
-// block, the write key backwards.  dkw (fp32) comes from the scan backward.
-// The thread also runs the chain backward for the three tokens after its block,
-// so every contribution to dk of its block's tokens (b k and the four taps of
-// the tokens that read them) is summed in registers and added to dk, which
-// already holds the scan's part, with one read-modify-write: no other thread
-// of this kernel touches those elements.
+// The write key backwards.  One workgroup per (block of 64 tokens, head, 64
+// channels): lane = channel, wavefront w = the block's tokens 16 w .. 16 w + 15.
+// dkw (fp32) comes from the scan backward.  Each wavefront also runs the chain
+// backward for the three tokens after its own, so every contribution to dk of
+// its tokens (b k and the four taps of the tokens that read them) is summed in
+// registers and added to dk, which already holds the scan's part, with one
+// read-modify-write: no other wavefront touches those elements.  The keys of
+// the taps slide through registers (one load per token), the next token's
+// loads are issued before this token's arithmetic, db takes one atomic per
+// (token, head, 64 channels), and the taps' gradients are summed over the
+// workgroup and stored per token block (reduced by wk_reduce_kernel: no
+// atomics on the 4 x H x dk weights).
+template <typename T, int L>
+struct WkTok {
+    float gkw, kt, bt;
+    float a[L > 1 ? L - 1 : 1], u[L > 1 ? L - 1 : 1], h[L > 1 ? L - 1 : 1];
+};
+
+template <typename T, int L>
+__device__ __forceinline__ void wk_load(WkTok<T, L>& x, const T* k, const T* u, const T* a, const T* h,
+                                        const T* b, const float* dkw, int t, int T_total, int H, int DK,
+                                        int e, int i)
+{
+    const bool in = t < T_total;
+    const int64_t rk = ((int64_t)t * H + e) * DK + i;
+    x.gkw = in ? dkw[rk] : 0.f;
+    x.kt = in ? ld(k, rk) : 0.f;
+    x.bt = in ? ld(b, (int64_t)t * H + e) : 0.f;
+    if constexpr (L > 1) {
+        const int64_t lb = (int64_t)t * H * (L - 1) * DK + (int64_t)e * (L - 1) * DK + i;
+#pragma unroll
+        for (int l = 0; l < L - 1; ++l) {
+            x.a[l] = in ? ld(a, lb + (int64_t)l * DK) : 0.f;
+            x.u[l] = in ? ld(u, lb + (int64_t)l * DK) : 0.f;
+            x.h[l] = in ? ld(h, lb + (int64_t)l * DK) : 0.f;
+        }
+    }
+}
+
 template <typename T, int L>
 __global__ __launch_bounds__(256) void write_key_bwd_kernel(
     const T* __restrict__ k, const T* __restrict__ u, const T* __restrict__ a,
@@ -505,131 +539,173 @@ __global__ __launch_bounds__(256) void write_key_bwd_kernel(
     const int32_t* __restrict__ cu, int n_seqs, int T_total, int H, int DK, bool gelu,
     const float* __restrict__ dkw, float* __restrict__ dk, float* __restrict__ du,
     float* __restrict__ da, float* __restrict__ dh, float* __restrict__ db,
-    float* __restrict__ dconv_w)
+    float* __restrict__ dconv_part)
 {
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int i = (int)(gid % DK);
-    const int e = (int)((gid / DK) % H);
-    const int64_t blk = gid / ((int64_t)DK * H);
-    const int t_lo = (int)(blk * kC);
-    if (t_lo >= T_total)
-        return;
+    __shared__ float4 red[4][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ng = DK / 64;
+    const int cg = blockIdx.x % ng, e = (blockIdx.x / ng) % H;
+    const int tb = blockIdx.x / (ng * H);
+    const int i = cg * 64 + lane;
+    const int t_lo = tb * kWkBlock + wave * kC;
     const int t_hi = min(T_total, t_lo + kC);
     float w[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m)
         w[m] = ld(conv_w, ((int64_t)e * DK + i) * 4 + m);
-    // sequence of t_lo
-    int lo = 0, hi = n_seqs;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (cu[mid] <= t_lo) lo = mid; else hi = mid;
-    }
-    int sn = lo;
-    int s0 = cu[sn], s1 = cu[sn + 1];            // bounds of the sequence holding t
     float dw[4] = {0.f, 0.f, 0.f, 0.f};
-    // dr_0 of tokens t-3 .. t and the end of the sequence each belongs to
-    float dr[4] = {0.f, 0.f, 0.f, 0.f};
-    int se[4] = {-1, -1, -1, -1};
-    const int64_t lrow = (int64_t)H * (L - 1) * DK;
-    for (int t = t_lo; t < t_hi + 3; ++t) {
-#pragma unroll
-        for (int x = 0; x < 3; ++x) {
-            dr[x] = dr[x + 1];
-            se[x] = se[x + 1];
+    if (t_lo < T_total) {
+        // sequence of t_lo
+        int lo = 0, hi = n_seqs;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (cu[mid] <= t_lo) lo = mid; else hi = mid;
         }
-        dr[3] = 0.f;
-        se[3] = -1;
-        if (t < T_total) {
-            while (s1 <= t) {                    // the sequence holding t (skips empty ones)
-                ++sn;
-                s0 = s1;
-                s1 = cu[sn + 1];
+        int sn = lo;
+        int s0 = cu[sn], s1 = cu[sn + 1];        // bounds of the sequence holding t
+        // keys of tokens t-3 .. t (raw: the sequence start masks them per token)
+        float kwin[4];
+#pragma unroll
+        for (int m = 0; m < 3; ++m) {
+            const int tau = t_lo - 3 + m;
+            kwin[m + 1] = tau >= 0 ? ld(k, ((int64_t)tau * H + e) * DK + i) : 0.f;
+        }
+        // dr_0 of tokens t-3 .. t with the end of the sequence each belongs to, and
+        // the dkw and b of those tokens (dk of token t-3 is completed at token t)
+        float dr[4] = {0.f, 0.f, 0.f, 0.f}, gh[4] = {0.f, 0.f, 0.f, 0.f}, bh[4] = {0.f, 0.f, 0.f, 0.f};
+        int se[4] = {-1, -1, -1, -1};
+        const int t_end = min(T_total, t_hi + 3);
+        WkTok<T, L> nx;
+        wk_load<T, L>(nx, k, u, a, h, b, dkw, t_lo, T_total, H, DK, e, i);
+        for (int t = t_lo; t < t_hi + 3; ++t) {
+#pragma unroll
+            for (int x = 0; x < 3; ++x) {
+                dr[x] = dr[x + 1];
+                se[x] = se[x + 1];
+                gh[x] = gh[x + 1];
+                bh[x] = bh[x + 1];
+                kwin[x] = kwin[x + 1];
             }
-            se[3] = s1;
-            const bool own = t < t_hi;
-            const int64_t rk = ((int64_t)t * H + e) * DK + i;
-            const float g_kw = dkw[rk];
-            if (own) {                           // db from the b k part of the key
-                const float kt = ld(k, rk);
-                float dbp = g_kw * kt;
-                for (int o = 32; o > 0; o >>= 1) // one atomic per wavefront: its lanes are
-                    dbp += __shfl_xor(dbp, o);   // 64 channels of one (token, head) when DK >= 64
-                if (DK >= 64) {
-                    if ((threadIdx.x & 63) == 0)
+            dr[3] = 0.f;
+            se[3] = -1;
+            gh[3] = 0.f;
+            bh[3] = 0.f;
+            kwin[3] = 0.f;
+            const int tau = t - 3;
+            const int64_t rt = ((int64_t)tau * H + e) * DK + i;
+            const float dk_old = tau >= t_lo ? dk[rt] : 0.f;
+            if (t < t_end) {
+                const WkTok<T, L> cur = nx;
+                if (t + 1 < t_end)
+                    wk_load<T, L>(nx, k, u, a, h, b, dkw, t + 1, T_total, H, DK, e, i);
+                while (s1 <= t) {                // the sequence holding t (skips empty ones)
+                    ++sn;
+                    s0 = s1;
+                    s1 = cu[sn + 1];
+                }
+                se[3] = s1;
+                gh[3] = cur.gkw;
+                bh[3] = cur.bt;
+                kwin[3] = cur.kt;
+                const bool own = t < t_hi;
+                if (own) {                       // db from the b k part of the key: one
+                    float dbp = cur.gkw * cur.kt; // atomic per wavefront (64 channels)
+                    for (int o = 32; o > 0; o >>= 1)
+                        dbp += __shfl_xor(dbp, o);
+                    if (lane == 0)
                         atomicAdd(db + (int64_t)t * H + e, dbp);
-                } else {
-                    atomicAdd(db + (int64_t)t * H + e, g_kw * kt);
                 }
-            }
-            if constexpr (L > 1) {
-                float kx[4];
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int tau = t - 3 + m;
-                    kx[m] = tau >= s0 ? ld(k, ((int64_t)tau * H + e) * DK + i) : 0.f;
-                }
-                const float r0 = w[0] * kx[0] + w[1] * kx[1] + w[2] * kx[2] + w[3] * kx[3];
-                // residuals r_l, l = 1 .. L-1 (the closed form as a running product, or
-                // the GELU refinement chain)
-                float r[L];
-                r[1] = r0;
-                const int64_t lb = (int64_t)t * lrow + (int64_t)e * (L - 1) * DK + i;
-#pragma unroll
-                for (int l = 1; l < L - 1; ++l) {
-                    const float al = ld(a, lb + (int64_t)(l - 1) * DK), hl = ld(h, lb + (int64_t)(l - 1) * DK);
-                    r[l + 1] = gelu ? r[l] - al * gelu_as(hl * r[l]) : r[l] * (1.f - al * hl);
-                }
-                float dr_next = 0.f;
-#pragma unroll
-                for (int l = L - 1; l >= 1; --l) {
-                    const int64_t sl = lb + (int64_t)(l - 1) * DK;
-                    const float al = ld(a, sl), ul = ld(u, sl), hl = ld(h, sl);
-                    float dal = g_kw * ul * r[l], dhl = 0.f, drl = g_kw * al * ul;
-                    if (l <= L - 2) {
-                        if (gelu) {              // r_{l+1} = r_l - a_l GELU(h_l r_l)
-                            float gp;
-                            const float gv = gelu_as_grad(hl * r[l], gp);
-                            dal -= dr_next * gv;
-                            dhl = -dr_next * al * r[l] * gp;
-                            drl += dr_next * (1.f - al * hl * gp);
-                        } else {                 // r_{l+1} = r_l (1 - a_l h_l)
-                            dal -= dr_next * hl * r[l];
-                            dhl = -dr_next * al * r[l];
-                            drl += dr_next * (1.f - al * hl);
-                        }
-                    }
-                    if (own) {
-                        du[sl] = g_kw * al * r[l];
-                        da[sl] = dal;
-                        dh[sl] = dhl;
-                    }
-                    dr_next = drl;
-                }
-                dr[3] = dr_next;                 // dr_0 of token t
-                if (own) {                       // the taps: dw_m += dr_0 k_{t-3+m}
+                if constexpr (L > 1) {
+                    float kx[4];
 #pragma unroll
                     for (int m = 0; m < 4; ++m)
-                        dw[m] += dr_next * kx[m];
+                        kx[m] = t - 3 + m >= s0 ? kwin[m] : 0.f;
+                    const float r0 = w[0] * kx[0] + w[1] * kx[1] + w[2] * kx[2] + w[3] * kx[3];
+                    // residuals r_l, l = 1 .. L-1 (the closed form as a running product, or
+                    // the GELU refinement chain)
+                    float r[L];
+                    r[1] = r0;
+#pragma unroll
+                    for (int l = 1; l < L - 1; ++l) {
+                        const float al = cur.a[l - 1], hl = cur.h[l - 1];
+                        r[l + 1] = gelu ? r[l] - al * gelu_as(hl * r[l]) : r[l] * (1.f - al * hl);
+                    }
+                    float dr_next = 0.f;
+                    const int64_t lb = (int64_t)t * H * (L - 1) * DK + (int64_t)e * (L - 1) * DK + i;
+#pragma unroll
+                    for (int l = L - 1; l >= 1; --l) {
+                        const float al = cur.a[l - 1], ul = cur.u[l - 1], hl = cur.h[l - 1];
+                        const float g_kw = cur.gkw;
+                        float dal = g_kw * ul * r[l], dhl = 0.f, drl = g_kw * al * ul;
+                        if (l <= L - 2) {
+                            if (gelu) {          // r_{l+1} = r_l - a_l GELU(h_l r_l)
+                                float gp;
+                                const float gv = gelu_as_grad(hl * r[l], gp);
+                                dal -= dr_next * gv;
+                                dhl = -dr_next * al * r[l] * gp;
+                                drl += dr_next * (1.f - al * hl * gp);
+                            } else {             // r_{l+1} = r_l (1 - a_l h_l)
+                                dal -= dr_next * hl * r[l];
+                                dhl = -dr_next * al * r[l];
+                                drl += dr_next * (1.f - al * hl);
+                            }
+                        }
+                        if (own) {
+                            const int64_t sl = lb + (int64_t)(l - 1) * DK;
+                            du[sl] = g_kw * al * r[l];
+                            da[sl] = dal;
+                            dh[sl] = dhl;
+                        }
+                        dr_next = drl;
+                    }
+                    dr[3] = dr_next;             // dr_0 of token t
+                    if (own) {                   // the taps: dw_m += dr_0 k_{t-3+m}
+#pragma unroll
+                        for (int m = 0; m < 4; ++m)
+                            dw[m] += dr_next * kx[m];
+                    }
                 }
             }
-        }
-        // dk of token tau = t - 3: b dkw, and w_{3-d} dr_0 of token tau + d in its sequence
-        const int tau = t - 3;
-        if (tau >= t_lo) {
-            const int64_t rt = ((int64_t)tau * H + e) * DK + i;
-            float acc = ld(b, (int64_t)tau * H + e) * dkw[rt] + w[3] * dr[0];
+            // dk of token tau = t - 3: b dkw, and w_{3-d} dr_0 of token tau + d in its sequence
+            if (tau >= t_lo) {
+                float acc = bh[0] * gh[0] + w[3] * dr[0];
 #pragma unroll
-            for (int dd = 1; dd < 4; ++dd)
-                if (se[dd] == se[0])
-                    acc += w[3 - dd] * dr[dd];
-            dk[rt] += acc;
+                for (int dd = 1; dd < 4; ++dd)
+                    if (se[dd] == se[0])
+                        acc += w[3 - dd] * dr[dd];
+                dk[rt] = dk_old + acc;
+            }
         }
     }
-    if constexpr (L > 1)
+    red[wave][lane] = make_float4(dw[0], dw[1], dw[2], dw[3]);
+    __syncthreads();
+    if (wave == 0) {
+        float4 sum = red[0][lane];
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-            atomicAdd(dconv_w + ((int64_t)e * DK + i) * 4 + m, dw[m]);
+        for (int x = 1; x < 4; ++x) {
+            const float4 y = red[x][lane];
+            sum.x += y.x; sum.y += y.y; sum.z += y.z; sum.w += y.w;
+        }
+        *reinterpret_cast<float4*>(dconv_part + (((int64_t)tb * H + e) * DK + i) * 4) = sum;
+    }
+}
+
+// dconv_w = the sum over token blocks of the per-block partials [nb][n], in two
+// passes: slabs of kWkRows blocks into [slabs][n], then the slabs (rows = nb)
+__global__ __launch_bounds__(256) void wk_reduce_kernel(const float* __restrict__ part, int nb, int n,
+                                                        int rows, float* __restrict__ out)
+{
+    const int o = blockIdx.x * 256 + threadIdx.x;
+    const int s = blockIdx.y;
+    if (o >= n)
+        return;
+    const int b0 = s * rows, b1 = min(nb, b0 + rows);
+    float acc = 0.f;
+#pragma unroll 8
+    for (int bb = b0; bb < b1; ++bb)
+        acc += part[(int64_t)bb * n + o];
+    out[(int64_t)s * n + o] = acc;
 }
 
 __global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ p, int64_t n)
@@ -640,12 +716,20 @@ __global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ p, int64_
 
 }  // namespace bwd
 
+size_t wk_workspace_floats(int total_tokens, int heads, int dk)
+{
+    const int64_t nb = (total_tokens + bwd::kWkBlock - 1) / bwd::kWkBlock;
+    const int64_t slabs = (nb + bwd::kWkRows - 1) / bwd::kWkRows;
+    return (size_t)((nb + slabs) * heads * dk * 4);
+}
+
 size_t bwd_workspace_floats(int n_seqs, int total_tokens, int heads, int dk, int dv)
 {
     const int64_t slots = total_tokens / bwd::sub_len(dk) + n_seqs + 1;
     return (size_t)(slots * heads * dk * dv)                      // sub-chunk start states
          + (size_t)n_seqs * bwd::kMaxSeg * heads * dk * dv        // segment-boundary gradients
-         + (size_t)total_tokens * heads * dk;                     // dkw
+         + (size_t)total_tokens * heads * dk                      // dkw
+         + wk_workspace_floats(total_tokens, heads, dk);          // dconv_w partials
 }
 
 // Segments per sequence for the scan backward.  The segment walk holds two
@@ -669,37 +753,54 @@ int bwd_segments(int n_seqs, int heads, int dv)
 bool bwd_supported(int dk, int dv) { return (dk == 64 || dk == 128) && (dv == 64 || dv == 128); }
 
 template <typename T, int L>
-static hipError_t launch_wk_L(const BwdArgs& p, const float* dkw, dim3 grid, hipStream_t s)
+static hipError_t launch_wk_L(const BwdArgs& p, const float* dkw, float* part, hipStream_t s)
 {
-    hipLaunchKernelGGL((bwd::write_key_bwd_kernel<T, L>), grid, dim3(256), 0, s, (const T*)p.k,
-                       (const T*)p.u, (const T*)p.a, (const T*)p.h, (const T*)p.b,
-                       (const T*)p.conv_w, p.cu_seqlens, p.n_seqs, p.total_tokens, p.heads, p.dk,
-                       p.gelu, dkw, p.gk, p.gu, p.ga, p.gh, p.gb, p.gconv);
+    const int64_t nb = (p.total_tokens + bwd::kWkBlock - 1) / bwd::kWkBlock;
+    const int n = p.heads * p.dk * 4;
+    if (nb > 0)
+        hipLaunchKernelGGL((bwd::write_key_bwd_kernel<T, L>), dim3((unsigned)(nb * p.heads * (p.dk / 64))),
+                           dim3(256), 0, s, (const T*)p.k, (const T*)p.u, (const T*)p.a, (const T*)p.h,
+                           (const T*)p.b, (const T*)p.conv_w, p.cu_seqlens, p.n_seqs, p.total_tokens,
+                           p.heads, p.dk, p.gelu, dkw, p.gk, p.gu, p.ga, p.gh, p.gb, part);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || n == 0)
+        return err;
+    // the partials [nb][n] -> slabs [ns][n] -> dconv_w (every element written)
+    const int ns = (int)((nb + bwd::kWkRows - 1) / bwd::kWkRows);
+    float* slabs = part + nb * n;
+    const unsigned gx = (unsigned)((n + 255) / 256);
+    if (ns > 0) {
+        hipLaunchKernelGGL(bwd::wk_reduce_kernel, dim3(gx, (unsigned)ns), dim3(256), 0, s, part, (int)nb, n,
+                           bwd::kWkRows, slabs);
+        if ((err = hipGetLastError()) != hipSuccess)
+            return err;
+    }
+    hipLaunchKernelGGL(bwd::wk_reduce_kernel, dim3(gx, 1), dim3(256), 0, s, slabs, ns, n, ns, p.gconv);
     return hipGetLastError();
 }
 
 // The level count as a template parameter: the chain loops unroll and each
 // token's loads issue together.
 template <typename T>
-static hipError_t launch_wk(const BwdArgs& p, const float* dkw, dim3 grid, hipStream_t s)
+static hipError_t launch_wk(const BwdArgs& p, const float* dkw, float* part, hipStream_t s)
 {
     switch (p.L) {
-    case 1: return launch_wk_L<T, 1>(p, dkw, grid, s);
-    case 2: return launch_wk_L<T, 2>(p, dkw, grid, s);
-    case 3: return launch_wk_L<T, 3>(p, dkw, grid, s);
-    case 4: return launch_wk_L<T, 4>(p, dkw, grid, s);
-    case 5: return launch_wk_L<T, 5>(p, dkw, grid, s);
-    case 6: return launch_wk_L<T, 6>(p, dkw, grid, s);
-    case 7: return launch_wk_L<T, 7>(p, dkw, grid, s);
-    case 8: return launch_wk_L<T, 8>(p, dkw, grid, s);
-    case 9: return launch_wk_L<T, 9>(p, dkw, grid, s);
-    case 10: return launch_wk_L<T, 10>(p, dkw, grid, s);
-    case 11: return launch_wk_L<T, 11>(p, dkw, grid, s);
-    case 12: return launch_wk_L<T, 12>(p, dkw, grid, s);
-    case 13: return launch_wk_L<T, 13>(p, dkw, grid, s);
-    case 14: return launch_wk_L<T, 14>(p, dkw, grid, s);
-    case 15: return launch_wk_L<T, 15>(p, dkw, grid, s);
-    case 16: return launch_wk_L<T, 16>(p, dkw, grid, s);
+    case 1: return launch_wk_L<T, 1>(p, dkw, part, s);
+    case 2: return launch_wk_L<T, 2>(p, dkw, part, s);
+    case 3: return launch_wk_L<T, 3>(p, dkw, part, s);
+    case 4: return launch_wk_L<T, 4>(p, dkw, part, s);
+    case 5: return launch_wk_L<T, 5>(p, dkw, part, s);
+    case 6: return launch_wk_L<T, 6>(p, dkw, part, s);
+    case 7: return launch_wk_L<T, 7>(p, dkw, part, s);
+    case 8: return launch_wk_L<T, 8>(p, dkw, part, s);
+    case 9: return launch_wk_L<T, 9>(p, dkw, part, s);
+    case 10: return launch_wk_L<T, 10>(p, dkw, part, s);
+    case 11: return launch_wk_L<T, 11>(p, dkw, part, s);
+    case 12: return launch_wk_L<T, 12>(p, dkw, part, s);
+    case 13: return launch_wk_L<T, 13>(p, dkw, part, s);
+    case 14: return launch_wk_L<T, 14>(p, dkw, part, s);
+    case 15: return launch_wk_L<T, 15>(p, dkw, part, s);
+    case 16: return launch_wk_L<T, 16>(p, dkw, part, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -725,10 +826,11 @@ static hipError_t launch_bwd_T(const BwdArgs& p, hipStream_t s)
     zero(dkw, (int64_t)T_ * H * DK);
     zero(p.gg, (int64_t)T_ * H);
     zero(p.gb, (int64_t)T_ * H);
-    zero(p.gconv, (int64_t)H * DK * 4);
     hipError_t err = hipGetLastError();
-    if (err != hipSuccess || wgs == 0)
+    if (err != hipSuccess)
         return err;
+    if (wgs == 0)
+        return launch_wk<T>(p, dkw, dkw + (int64_t)T_ * H * DK, s);
     // checkpoints and (P > 1) the segment-boundary gradients, then the segments
     hipLaunchKernelGGL((bwd::scan_bwd_kernel<T, DK, 0>), dim3((unsigned)(wgs * (P > 1 ? 2 : 1))),
                        dim3(64), 0, s, (const T*)p.q, (const T*)p.k, (const T*)p.kw,
@@ -742,26 +844,16 @@ static hipError_t launch_bwd_T(const BwdArgs& p, hipStream_t s)
                        (const T*)p.g, (const T*)p.b, (const T*)p.dO, p.cu_seqlens, H, p.dv,
                        p.s_init, p.ds_final, ckpt, gbuf, P, (int)wgs, p.gq, p.gk, dkw, p.gv,
                        p.gg, p.gb, p.gs_init);
-    if ((err = hipGetLastError()) != hipSuccess || T_ == 0)
+    if ((err = hipGetLastError()) != hipSuccess)
         return err;
-    const int64_t threads = ((int64_t)(T_ + bwd::kC - 1) / bwd::kC) * H * DK;
-    return launch_wk<T>(p, dkw, dim3((unsigned)((threads + 255) / 256)), s);
+    return launch_wk<T>(p, dkw, dkw + (int64_t)T_ * H * DK, s);
 }
 
-hipError_t launch_write_key_bwd(const BwdArgs& p, const float* dkw, hipStream_t s)
+hipError_t launch_write_key_bwd(const BwdArgs& p, const float* dkw, float* part, hipStream_t s)
 {
     if (!bwd_supported(p.dk, p.dv) || p.L < 1 || p.L > 16)
         return hipErrorInvalidValue;
-    const int64_t nconv = (int64_t)p.heads * p.dk * 4;
-    if (nconv > 0)
-        hipLaunchKernelGGL(bwd::zero_kernel, dim3((unsigned)((nconv + 255) / 256)), dim3(256), 0, s, p.gconv,
-                           nconv);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess || p.total_tokens == 0)
-        return err;
-    const int64_t threads = ((int64_t)(p.total_tokens + bwd::kC - 1) / bwd::kC) * p.heads * p.dk;
-    const dim3 grid((unsigned)((threads + 255) / 256));
-    return p.bf16 ? launch_wk<uint16_t>(p, dkw, grid, s) : launch_wk<float>(p, dkw, grid, s);
+    return p.bf16 ? launch_wk<uint16_t>(p, dkw, part, s) : launch_wk<float>(p, dkw, part, s);
 }
 
 hipError_t launch_bwd(const BwdArgs& p, hipStream_t s)

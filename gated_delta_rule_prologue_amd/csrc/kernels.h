@@ -97,8 +97,10 @@ struct BwdChunkBufs {
 hipError_t launch_bwd_grads(const ScanArgs& p, const BwdChunkBufs& w, hipStream_t stream);
 // The write-key part of the backward pass alone (backward.hip): from dkw (fp32
 // [T][H][dk]) it writes du, da, dh, adds the write-key terms to dk and db (both
-// hold the scan's gradients on entry), and writes dconv_w (zeroed here first).
-hipError_t launch_write_key_bwd(const BwdArgs& p, const float* dkw, hipStream_t stream);
+// hold the scan's gradients on entry), and writes dconv_w; part holds
+// wk_workspace_floats(T, H, dk) floats of scratch (per-block partials).
+size_t wk_workspace_floats(int total_tokens, int heads, int dk);
+hipError_t launch_write_key_bwd(const BwdArgs& p, const float* dkw, float* part, hipStream_t stream);
 bool bwd_supported(int dk, int dv);
 hipError_t launch_bwd(const BwdArgs& p, hipStream_t stream);
 

@@ -450,7 +450,7 @@ bool use_bwd_chunked(const prism_dims* d)
 
 // Workspace of the chunkwise backward after kw, each part 256-byte aligned.
 struct BwdChunkLayout {
-    size_t mats, ck, ckT, dck, dckT, xg, drg, dkw, scal, sdot, total;
+    size_t mats, ck, ckT, dck, dckT, xg, drg, dkw, scal, sdot, wk, total;
 };
 
 BwdChunkLayout bwd_chunk_layout(const prism_dims* d)
@@ -470,6 +470,7 @@ BwdChunkLayout bwd_chunk_layout(const prism_dims* d)
     w.dkw = o; o += round256((size_t)d->total_tokens * d->heads * d->dk * 4);
     w.scal = o; o += round256((size_t)3 * d->total_tokens * d->heads * 4);
     w.sdot = o; o += round256(nv * 4);
+    w.wk = o; o += round256(prism::wk_workspace_floats(d->total_tokens, d->heads, d->dk) * 4);
     w.total = o;
     return w;
 }
@@ -567,7 +568,7 @@ prism_status prism_bwd_ex(const prism_dims* d, const void* q, const void* k, con
     if (e == hipSuccess)
         e = prism::launch_bwd_grads(sp, cb, s);
     if (e == hipSuccess)
-        e = prism::launch_write_key_bwd(p, cb.gkw, s);
+        e = prism::launch_write_key_bwd(p, cb.gkw, reinterpret_cast<float*>(ws + w.wk), s);
     return from_hip(e);
 }
 
