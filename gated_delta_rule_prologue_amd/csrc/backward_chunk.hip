@@ -352,9 +352,10 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Passes C1 and C2: one workgroup per (virtual chunk, head), four wavefronts;
-// wavefront w owns the chunk's tokens 16 w .. 16 w + 15 of every output, so
-// every gradient row is written by one workgroup (no atomics).
+// Passes C1 and C2: one workgroup per (virtual chunk, head), eight wavefronts
+// (two per SIMD); wavefront w owns the chunk's tokens 16 (w & 3) .. + 15 and
+// column half w >> 2 of every output, so every gradient element is written by
+// one workgroup (no global atomics).
 //   C1: X = T (diag(b gamma) K S0 + A_kkw V), dX, dR = T^T dX (as in pass B),
 //       dV = diag(fac) KW dS1 + A_qkw^T dO + A_kkw^T dR, and the state terms
 //       dQ = diag(gamma) dO S0^T, dK = diag(b gamma) dR S0^T - diag(fac) X dS1^T,
@@ -369,10 +370,9 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(
 // MFMA fragment as one 16-byte read.
 // ---------------------------------------------------------------------------
 struct CtxC {
-    const uint16_t *q, *k, *kw, *v, *dO, *g, *b, *mats, *ck, *ckT, *dck, *dckT;
-    int H, DV, c0, nt, lane;
+    const uint16_t *g, *b;
+    int H, DV, c0, nt, lane, e;
     int64_t rowQK, rowV, vcid;                   // vcid: (virtual chunk) * H + head
-    int e;
 };
 
 // the sequence of virtual chunk vch (chunks numbered floor(cu[n] / 64) + n + i)
@@ -406,33 +406,55 @@ __device__ __forceinline__ bf16x8_t ldg16(const uint16_t* p)
     return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
 }
 
-// rows [64][W] of a token-major tensor (row stride `row`, chunk start c0, nt
-// tokens, zeros past them) into LDS rows of pitch LD, by all 256 threads
-template <int W, int LD>
-__device__ __forceinline__ void stage_rows(uint16_t* dst, const uint16_t* src, int64_t row, int nt, int tid)
-{
-    constexpr int PPR = W / 8;
-    const auto rs = rsrc(src, nt * (int)row * 2);
-    for (int p = tid; p < kC * PPR; p += 256) {
-        const uint4 x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                      rs, ((p / PPR) * (int)row + (p % PPR) * 8) * 2, 0, 0));
-        *reinterpret_cast<uint4*>(dst + (p / PPR) * LD + (p % PPR) * 8) = x;
-    }
-}
+// Staging of the chunk-parallel kernels (kNW wavefronts): every load of a
+// tensor's 64 x W tile is issued into registers before any LDS store, so the
+// workgroup waits for memory once.  Rows past the chunk's nt tokens read as zero.
+constexpr int kNW = 8;
 
-// one stored lower-triangular matrix (ten blocks) as a full 64 x 64 matrix of
-// pitch LDC, zeros above the diagonal blocks
-template <int LDC>
-__device__ __forceinline__ void stage_mat(uint16_t* dst, const uint16_t* m, int tid)
-{
-    for (int idx = tid; idx < 16 * 32; idx += 256) {
-        const int bi = idx / 128, bj = (idx / 32) % 4, p = idx % 32, r = p / 2, hh = p % 2;
-        uint4 x = make_uint4(0u, 0u, 0u, 0u);
-        if (bj <= bi)
-            x = *reinterpret_cast<const uint4*>(m + gram::blk_index(bi, bj) * gram::kBlockElems + gram::swz(r, 8 * hh));
-        *reinterpret_cast<uint4*>(dst + (16 * bi + r) * LDC + 16 * bj + 8 * hh) = x;
+template <int W>
+struct StageRows {
+    static constexpr int PPR = W / 8, N = kC * PPR / (kNW * 64);
+    uint4 x[N];
+    __device__ __forceinline__ void load(const uint16_t* src, int64_t row, int nt, int tid)
+    {
+        const auto rs = rsrc(src, nt * (int)row * 2);
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            const int p = tid + kNW * 64 * j;
+            x[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rs, ((p / PPR) * (int)row + (p % PPR) * 8) * 2, 0, 0));
+        }
     }
-}
+    template <int LD>
+    __device__ __forceinline__ void store(uint16_t* dst, int tid) const
+    {
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            const int p = tid + kNW * 64 * j;
+            *reinterpret_cast<uint4*>(dst + (p / PPR) * LD + (p % PPR) * 8) = x[j];
+        }
+    }
+};
+
+// one stored lower-triangular matrix (ten blocks) as a full 64 x 64 matrix,
+// zeros above the diagonal blocks: thread tid moves one 16-byte half row
+struct StageMat {
+    uint4 x;
+    __device__ __forceinline__ void load(const uint16_t* m, int tid)
+    {
+        const int bi = tid / 128, bj = (tid / 32) % 4, p = tid % 32;
+        x = make_uint4(0u, 0u, 0u, 0u);
+        if (bj <= bi)
+            x = *reinterpret_cast<const uint4*>(m + gram::blk_index(bi, bj) * gram::kBlockElems +
+                                                gram::swz(p / 2, 8 * (p % 2)));
+    }
+    template <int LDC>
+    __device__ __forceinline__ void store(uint16_t* dst, int tid) const
+    {
+        const int bi = tid / 128, bj = (tid / 32) % 4, p = tid % 32;
+        *reinterpret_cast<uint4*>(dst + (16 * bi + p / 2) * LDC + 16 * bj + 8 * (p % 2)) = x;
+    }
+};
 
 // gates of the chunk (wavefront 0, lane = token): gamma, b gamma, fac, lambda
 // (log2 of gamma), g, b (64 each), then gamma_C
@@ -456,6 +478,14 @@ __device__ __forceinline__ void gates_c(float* G, const CtxC& c)
     if (lane == 0)
         G[6 * kC] = __builtin_amdgcn_exp2f(lamC);
 }
+constexpr int kGateBytes = 6 * kC * 4 + 16;
+
+__device__ __forceinline__ void st_rows(uint16_t* dst, int ld, int t0, const f32x4_t& x, int col)
+{
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        dst[(t0 + r) * ld + col] = (uint16_t)(pack_bf16x2(x[r], 0.f) & 0xffffu);
+}
 
 template <int D, int DV>
 struct LayC1 {
@@ -464,12 +494,15 @@ struct LayC1 {
     static constexpr int oK = 0, oKW = szD, oQ = 2 * szD, oV = 3 * szD, oO = oV + szV;
     static constexpr int oT = oO + szV, oAkw = oT + szM, oNqk = oAkw + szM, oAqw = oNqk + szM;
     static constexpr int oR = oAqw + szM, oX = oR + szV, oG = oX + szV;
-    static constexpr int total = oG + 6 * kC * 4 + 16 + 16;
+    static constexpr int oSc = oG + kGateBytes;  // per-token dot products (3 x 64)
+    static constexpr int oRed = oSc + 3 * kC * 4;
+    static constexpr int total = oRed + kNW * 4;
     static_assert(total <= 160 * 1024, "LDS budget");
 };
 
+// C1.  Wavefront w: token rows 16 (w & 3) .., value (or key) column half w >> 2.
 template <int D, int DV>
-__global__ __launch_bounds__(256) void bwd_c1_kernel(
+__global__ __launch_bounds__(kNW * 64) void bwd_c1_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ kw,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO, const uint16_t* __restrict__ g,
     const uint16_t* __restrict__ b, const int32_t* __restrict__ cu, int n_seqs, int H,
@@ -480,16 +513,17 @@ __global__ __launch_bounds__(256) void bwd_c1_kernel(
 {
     using Ly = LayC1<D, DV>;
     constexpr int LDD = Ly::LDD, LDV = Ly::LDV, LDC = Ly::LDC;
-    constexpr int NKD = D / 32, NKV = DV / 32, NTD = D / 16, NTV = DV / 16;
+    constexpr int NKD = D / 32, NKV = DV / 32;
+    constexpr int HV = DV / 32, HD = D / 32;     // 16-column tiles of a column half
     __shared__ __attribute__((aligned(16))) unsigned char smem[Ly::total];
     const int tid = threadIdx.x;
-    const int tb = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tb = wave & 3, nh = wave >> 2;
     const int vch = blockIdx.x / H, e = blockIdx.x % H;
     CtxC c;
     if (!locate(cu, n_seqs, vch, c.c0, c.nt))
         return;
-    c.q = q; c.k = k; c.kw = kw; c.v = v; c.dO = dO; c.g = g; c.b = b; c.mats = mats;
-    c.ck = ck; c.ckT = ckT; c.dck = dck; c.dckT = dckT;
+    c.g = g; c.b = b;
     c.H = H; c.DV = DV; c.e = e; c.lane = tid & 63;
     c.rowQK = (int64_t)H * D;
     c.rowV = (int64_t)H * DV;
@@ -507,24 +541,39 @@ __global__ __launch_bounds__(256) void bwd_c1_kernel(
     uint16_t* sR = reinterpret_cast<uint16_t*>(smem + Ly::oR);
     uint16_t* sX = reinterpret_cast<uint16_t*>(smem + Ly::oX);
     float* G = reinterpret_cast<float*>(smem + Ly::oG);
+    float* sSc = reinterpret_cast<float*>(smem + Ly::oSc);
+    float* sRed = reinterpret_cast<float*>(smem + Ly::oRed);
 
     {
         const int64_t r0 = (int64_t)c.c0 * c.rowQK + (int64_t)e * D, v0 = (int64_t)c.c0 * c.rowV + (int64_t)e * DV;
-        stage_rows<D, LDD>(sK, k + r0, c.rowQK, c.nt, tid);
-        stage_rows<D, LDD>(sKW, kw + r0, c.rowQK, c.nt, tid);
-        stage_rows<D, LDD>(sQ, q + r0, c.rowQK, c.nt, tid);
-        stage_rows<DV, LDV>(sV, v + v0, c.rowV, c.nt, tid);
-        stage_rows<DV, LDV>(sO, dO + v0, c.rowV, c.nt, tid);
         const uint16_t* m = mats + c.vcid * (int64_t)gram::kChunkElems;
-        stage_mat<LDC>(sT, m + gram::kMatT * gram::kMatElems, tid);
-        stage_mat<LDC>(sAkw, m + gram::kMatAkkw * gram::kMatElems, tid);
-        stage_mat<LDC>(sNqk, m + gram::kMatNAqk * gram::kMatElems, tid);
-        stage_mat<LDC>(sAqw, m + gram::kMatAqkw * gram::kMatElems, tid);
-        if (tb == 0)
+        StageRows<D> xk, xkw, xq;
+        StageRows<DV> xv, xo;
+        StageMat mt, makw, mnqk, maqw;
+        xk.load(k + r0, c.rowQK, c.nt, tid);
+        xkw.load(kw + r0, c.rowQK, c.nt, tid);
+        xq.load(q + r0, c.rowQK, c.nt, tid);
+        xv.load(v + v0, c.rowV, c.nt, tid);
+        xo.load(dO + v0, c.rowV, c.nt, tid);
+        mt.load(m + gram::kMatT * gram::kMatElems, tid);
+        makw.load(m + gram::kMatAkkw * gram::kMatElems, tid);
+        mnqk.load(m + gram::kMatNAqk * gram::kMatElems, tid);
+        maqw.load(m + gram::kMatAqkw * gram::kMatElems, tid);
+        if (wave == 0)
             gates_c(G, c);
+        xk.template store<LDD>(sK, tid);
+        xkw.template store<LDD>(sKW, tid);
+        xq.template store<LDD>(sQ, tid);
+        xv.template store<LDV>(sV, tid);
+        xo.template store<LDV>(sO, tid);
+        mt.template store<LDC>(sT, tid);
+        makw.template store<LDC>(sAkw, tid);
+        mnqk.template store<LDC>(sNqk, tid);
+        maqw.template store<LDC>(sAqw, tid);
+        if (tid < 3 * kC)
+            sSc[tid] = 0.f;
     }
     lds_barrier();
-    const float* sGam = G;
     const float* sBG = G + kC;
     const float* sFac = G + 2 * kC;
     const int t0 = tb * 16 + lg * 4;             // this lane's first token row of a tile
@@ -532,28 +581,24 @@ __global__ __launch_bounds__(256) void bwd_c1_kernel(
     const uint16_t* ck0 = ck + c.vcid * (int64_t)D * DV;
     const uint16_t* dckT0 = dckT + c.vcid * (int64_t)DV * D;
     const uint16_t* dck0 = dck + c.vcid * (int64_t)D * DV;
-    auto st_rows = [&](uint16_t* dst, int ld, const f32x4_t& x, int col) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            dst[(t0 + r) * ld + col] = (uint16_t)(pack_bf16x2(x[r], 0.f) & 0xffffu);
-    };
+    const int v0c = nh * (DV / 2), d0c = nh * (D / 2);   // first column of this wavefront's half
 
     // ---- R = diag(b gamma) K S0 + A_kkw V -> sR
     {
-        f32x4_t acc[NTV];
+        f32x4_t acc[HV];
 #pragma unroll
-        for (int n = 0; n < NTV; ++n)
+        for (int n = 0; n < HV; ++n)
             acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kp = 0; kp < NKD; ++kp) {
             const bf16x8_t a = frag_row(sK + tb * 16 * LDD + kp * 32, LDD, lane);
 #pragma unroll
-            for (int n = 0; n < NTV; ++n)
-                acc[n] = mma32(a, ldg16(ckT0 + (n * 16 + li) * D + kp * 32 + lg * 8), acc[n]);
+            for (int n = 0; n < HV; ++n)
+                acc[n] = mma32(a, ldg16(ckT0 + (v0c + n * 16 + li) * D + kp * 32 + lg * 8), acc[n]);
         }
         const float4 bg = *reinterpret_cast<const float4*>(sBG + t0);
 #pragma unroll
-        for (int n = 0; n < NTV; ++n) {
+        for (int n = 0; n < HV; ++n) {
             acc[n][0] *= bg.x; acc[n][1] *= bg.y; acc[n][2] *= bg.z; acc[n][3] *= bg.w;
         }
 #pragma unroll
@@ -561,40 +606,40 @@ __global__ __launch_bounds__(256) void bwd_c1_kernel(
             if (h2 <= tb / 2) {
                 const bf16x8_t a = frag_row(sAkw + tb * 16 * LDC + h2 * 32, LDC, lane);
 #pragma unroll
-                for (int n = 0; n < NTV; ++n)
-                    acc[n] = mma32(a, frag_col(sV + h2 * 32 * LDV + n * 16, LDV, lane), acc[n]);
+                for (int n = 0; n < HV; ++n)
+                    acc[n] = mma32(a, frag_col(sV + h2 * 32 * LDV + v0c + n * 16, LDV, lane), acc[n]);
             }
         }
 #pragma unroll
-        for (int n = 0; n < NTV; ++n)
-            st_rows(sR, LDV, acc[n], n * 16 + li);
+        for (int n = 0; n < HV; ++n)
+            st_rows(sR, LDV, t0, acc[n], v0c + n * 16 + li);
     }
     lds_barrier();
-    // ---- X = T R -> sX (and memory)
+    // ---- X = T R -> sX
     {
-        f32x4_t acc[NTV];
+        f32x4_t acc[HV];
 #pragma unroll
-        for (int n = 0; n < NTV; ++n)
+        for (int n = 0; n < HV; ++n)
             acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int h2 = 0; h2 <= 1; ++h2) {
             if (h2 <= tb / 2) {
                 const bf16x8_t a = frag_row(sT + tb * 16 * LDC + h2 * 32, LDC, lane);
 #pragma unroll
-                for (int n = 0; n < NTV; ++n)
-                    acc[n] = mma32(a, frag_col(sR + h2 * 32 * LDV + n * 16, LDV, lane), acc[n]);
+                for (int n = 0; n < HV; ++n)
+                    acc[n] = mma32(a, frag_col(sR + h2 * 32 * LDV + v0c + n * 16, LDV, lane), acc[n]);
             }
         }
 #pragma unroll
-        for (int n = 0; n < NTV; ++n)
-            st_rows(sX, LDV, acc[n], n * 16 + li);
+        for (int n = 0; n < HV; ++n)
+            st_rows(sX, LDV, t0, acc[n], v0c + n * 16 + li);
     }
     lds_barrier();
     // ---- dX = (-A_qk)^T dO - diag(fac) K dS1 -> sR
     {
-        f32x4_t y[NTV], xl[NTV];
+        f32x4_t y[HV], xl[HV];
 #pragma unroll
-        for (int n = 0; n < NTV; ++n) {
+        for (int n = 0; n < HV; ++n) {
             y[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             xl[n] = y[n];
         }
@@ -602,54 +647,55 @@ __global__ __launch_bounds__(256) void bwd_c1_kernel(
         for (int kp = 0; kp < NKD; ++kp) {
             const bf16x8_t a = frag_row(sK + tb * 16 * LDD + kp * 32, LDD, lane);
 #pragma unroll
-            for (int n = 0; n < NTV; ++n)
-                y[n] = mma32(a, ldg16(dckT0 + (n * 16 + li) * D + kp * 32 + lg * 8), y[n]);
+            for (int n = 0; n < HV; ++n)
+                y[n] = mma32(a, ldg16(dckT0 + (v0c + n * 16 + li) * D + kp * 32 + lg * 8), y[n]);
         }
 #pragma unroll
         for (int h2 = 0; h2 <= 1; ++h2) {
             if (h2 >= tb / 2) {
                 const bf16x8_t a = frag_col(sNqk + h2 * 32 * LDC + tb * 16, LDC, lane);
 #pragma unroll
-                for (int n = 0; n < NTV; ++n)
-                    xl[n] = mma32(a, frag_col(sO + h2 * 32 * LDV + n * 16, LDV, lane), xl[n]);
+                for (int n = 0; n < HV; ++n)
+                    xl[n] = mma32(a, frag_col(sO + h2 * 32 * LDV + v0c + n * 16, LDV, lane), xl[n]);
             }
         }
         const float4 f = *reinterpret_cast<const float4*>(sFac + t0);
 #pragma unroll
-        for (int n = 0; n < NTV; ++n) {
+        for (int n = 0; n < HV; ++n) {
             const f32x4_t dx = {xl[n][0] - f.x * y[n][0], xl[n][1] - f.y * y[n][1], xl[n][2] - f.z * y[n][2],
                                 xl[n][3] - f.w * y[n][3]};
-            st_rows(sR, LDV, dx, n * 16 + li);
+            st_rows(sR, LDV, t0, dx, v0c + n * 16 + li);
         }
     }
     lds_barrier();
     // ---- dR = T^T dX -> sR (after every wavefront has read dX)
     {
-        f32x4_t acc[NTV];
+        f32x4_t acc[HV];
 #pragma unroll
-        for (int n = 0; n < NTV; ++n)
+        for (int n = 0; n < HV; ++n)
             acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int h2 = 0; h2 <= 1; ++h2) {
             if (h2 >= tb / 2) {
                 const bf16x8_t a = frag_col(sT + h2 * 32 * LDC + tb * 16, LDC, lane);
 #pragma unroll
-                for (int n = 0; n < NTV; ++n)
-                    acc[n] = mma32(a, frag_col(sR + h2 * 32 * LDV + n * 16, LDV, lane), acc[n]);
+                for (int n = 0; n < HV; ++n)
+                    acc[n] = mma32(a, frag_col(sR + h2 * 32 * LDV + v0c + n * 16, LDV, lane), acc[n]);
             }
         }
         lds_barrier();
 #pragma unroll
-        for (int n = 0; n < NTV; ++n)
-            st_rows(sR, LDV, acc[n], n * 16 + li);
+        for (int n = 0; n < HV; ++n)
+            st_rows(sR, LDV, t0, acc[n], v0c + n * 16 + li);
     }
     lds_barrier();
 
-    // ---- X and dR rows to memory for C2 (this wavefront's 16 rows)
+    // ---- X and dR rows to memory for C2 (this wavefront's rows and column half)
     {
-        constexpr int PPR = DV / 8;
-        for (int p = lane; p < 16 * PPR; p += 64) {
-            const int t = tb * 16 + p / PPR, cc = (p % PPR) * 8;
+        constexpr int PPH = DV / 16;             // 16-byte vectors of half a row
+#pragma unroll
+        for (int p = lane; p < 16 * PPH; p += 64) {
+            const int t = tb * 16 + p / PPH, cc = v0c + (p % PPH) * 8;
             if (t < c.nt) {
                 const int64_t o = (int64_t)(c.c0 + t) * c.rowV + (int64_t)e * DV + cc;
                 *reinterpret_cast<uint4*>(xg + o) = *reinterpret_cast<const uint4*>(sX + t * LDV + cc);
@@ -657,7 +703,7 @@ __global__ __launch_bounds__(256) void bwd_c1_kernel(
             }
         }
     }
-    const float4 gam4 = *reinterpret_cast<const float4*>(sGam + t0);
+    const float4 gam4 = *reinterpret_cast<const float4*>(G + t0);
     const float4 bg4 = *reinterpret_cast<const float4*>(sBG + t0);
     const float4 fac4 = *reinterpret_cast<const float4*>(sFac + t0);
     const float gam[4] = {gam4.x, gam4.y, gam4.z, gam4.w}, bgm[4] = {bg4.x, bg4.y, bg4.z, bg4.w},
@@ -669,19 +715,19 @@ __global__ __launch_bounds__(256) void bwd_c1_kernel(
 
     // ---- dV = diag(fac) KW dS1 + A_qkw^T dO + A_kkw^T dR
     {
-        f32x4_t acc[NTV];
+        f32x4_t acc[HV];
 #pragma unroll
-        for (int n = 0; n < NTV; ++n)
+        for (int n = 0; n < HV; ++n)
             acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kp = 0; kp < NKD; ++kp) {
             const bf16x8_t a = frag_row(sKW + tb * 16 * LDD + kp * 32, LDD, lane);
 #pragma unroll
-            for (int n = 0; n < NTV; ++n)
-                acc[n] = mma32(a, ldg16(dckT0 + (n * 16 + li) * D + kp * 32 + lg * 8), acc[n]);
+            for (int n = 0; n < HV; ++n)
+                acc[n] = mma32(a, ldg16(dckT0 + (v0c + n * 16 + li) * D + kp * 32 + lg * 8), acc[n]);
         }
 #pragma unroll
-        for (int n = 0; n < NTV; ++n)
+        for (int n = 0; n < HV; ++n)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 acc[n][r] *= fac[r];
@@ -691,35 +737,35 @@ __global__ __launch_bounds__(256) void bwd_c1_kernel(
                 const bf16x8_t a1 = frag_col(sAqw + h2 * 32 * LDC + tb * 16, LDC, lane);
                 const bf16x8_t a2 = frag_col(sAkw + h2 * 32 * LDC + tb * 16, LDC, lane);
 #pragma unroll
-                for (int n = 0; n < NTV; ++n) {
-                    acc[n] = mma32(a1, frag_col(sO + h2 * 32 * LDV + n * 16, LDV, lane), acc[n]);
-                    acc[n] = mma32(a2, frag_col(sR + h2 * 32 * LDV + n * 16, LDV, lane), acc[n]);
+                for (int n = 0; n < HV; ++n) {
+                    acc[n] = mma32(a1, frag_col(sO + h2 * 32 * LDV + v0c + n * 16, LDV, lane), acc[n]);
+                    acc[n] = mma32(a2, frag_col(sR + h2 * 32 * LDV + v0c + n * 16, LDV, lane), acc[n]);
                 }
             }
         }
 #pragma unroll
-        for (int n = 0; n < NTV; ++n)
+        for (int n = 0; n < HV; ++n)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 if (row_ok(r))
-                    gv[gidx(r, c.rowV, DV, n * 16 + li)] = acc[n][r];
+                    gv[gidx(r, c.rowV, DV, v0c + n * 16 + li)] = acc[n][r];
     }
 
-    // ---- dQ, dK, dKW (channel tiles), with the dot products of each token row
+    // ---- dQ, dK, dKW (key column half), with the dot products of each token row
     float kd[4] = {0.f, 0.f, 0.f, 0.f}, qd[4] = {0.f, 0.f, 0.f, 0.f}, fd[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int n = 0; n < NTD; ++n) {
+    for (int n = 0; n < HD; ++n) {
+        const int col = d0c + n * 16 + li;
         f32x4_t zq = {0.f, 0.f, 0.f, 0.f}, z1 = zq, z2 = zq, z3 = zq;
 #pragma unroll
         for (int kp = 0; kp < NKV; ++kp) {
-            const bf16x8_t s0r = ldg16(ck0 + (n * 16 + li) * DV + kp * 32 + lg * 8);
-            const bf16x8_t s1r = ldg16(dck0 + (n * 16 + li) * DV + kp * 32 + lg * 8);
+            const bf16x8_t s0r = ldg16(ck0 + col * DV + kp * 32 + lg * 8);
+            const bf16x8_t s1r = ldg16(dck0 + col * DV + kp * 32 + lg * 8);
             zq = mma32(frag_row(sO + tb * 16 * LDV + kp * 32, LDV, lane), s0r, zq);   // dO S0^T
             z1 = mma32(frag_row(sR + tb * 16 * LDV + kp * 32, LDV, lane), s0r, z1);   // dR S0^T
             z2 = mma32(frag_row(sX + tb * 16 * LDV + kp * 32, LDV, lane), s1r, z2);   // X dS1^T
             z3 = mma32(frag_row(sV + tb * 16 * LDV + kp * 32, LDV, lane), s1r, z3);   // V dS1^T
         }
-        const int col = n * 16 + li;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float kv = bf16_to_f32(sK[(t0 + r) * LDD + col]);
@@ -741,18 +787,17 @@ __global__ __launch_bounds__(256) void bwd_c1_kernel(
         kd[r] = sum16(kd[r]);
         qd[r] = sum16(qd[r]);
         fd[r] = sum16(fd[r]);
-        if (li == 0 && row_ok(r)) {
-            const int64_t o = (int64_t)(c.c0 + t0 + r) * H + e;
-            scal[o] = kd[r];
-            scal[(int64_t)T * H + o] = qd[r];
-            scal[2 * (int64_t)T * H + o] = fd[r];
+        if (li == 0) {                           // the two column halves meet in LDS
+            atomicAdd(sSc + t0 + r, kd[r]);
+            atomicAdd(sSc + kC + t0 + r, qd[r]);
+            atomicAdd(sSc + 2 * kC + t0 + r, fd[r]);
         }
     }
 
     // ---- <S0, dS1>
     {
         float acc = 0.f;
-        for (int p = tid; p < D * DV / 8; p += 256) {
+        for (int p = tid; p < D * DV / 8; p += kNW * 64) {
             const uint4 a = *reinterpret_cast<const uint4*>(ck0 + p * 8);
             const uint4 bb = *reinterpret_cast<const uint4*>(dck0 + p * 8);
             const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {bb.x, bb.y, bb.z, bb.w};
@@ -764,13 +809,22 @@ __global__ __launch_bounds__(256) void bwd_c1_kernel(
         acc = sum16(acc);
         acc += __shfl_xor(acc, 16, 64);
         acc += __shfl_xor(acc, 32, 64);
-        float* red = G + 6 * kC + 4;             // four floats
-        lds_barrier();
         if (lane == 0)
-            red[tb] = acc;
-        lds_barrier();
-        if (tid == 0)
-            sdot[c.vcid] = red[0] + red[1] + red[2] + red[3];
+            sRed[wave] = acc;
+    }
+    lds_barrier();
+    if (tid < kC && tid < c.nt) {
+        const int64_t o = (int64_t)(c.c0 + tid) * H + e;
+        scal[o] = sSc[tid];
+        scal[(int64_t)T * H + o] = sSc[kC + tid];
+        scal[2 * (int64_t)T * H + o] = sSc[2 * kC + tid];
+    }
+    if (tid == 0) {
+        float s = 0.f;
+#pragma unroll
+        for (int x = 0; x < kNW; ++x)
+            s += sRed[x];
+        sdot[c.vcid] = s;
     }
 }
 
@@ -780,17 +834,19 @@ struct LayC2 {
     static constexpr int szD = kC * LDD * 2, szV = kC * LDV * 2, szM = kC * LDC * 2;
     static constexpr int oK = 0, oKW = szD, oQ = 2 * szD, oV = 3 * szD, oO = oV + szV, oX = oO + szV;
     static constexpr int oR = oX + szV, oMqk = oR + szV, oMqw = oMqk + szM, oMkk = oMqw + szM, oMkw = oMkk + szM;
-    static constexpr int oG = oMkw + szM;        // gates (6 x 64 + gamma_C), then l (64), db (64)
-    static constexpr int total = oG + 6 * kC * 4 + 16 + 2 * kC * 4;
+    static constexpr int oG = oMkw + szM;        // gates, then l (64), db (64)
+    static constexpr int total = oG + kGateBytes + 2 * kC * 4;
     static_assert(total <= 160 * 1024, "LDS budget");
 };
 
-// block pairs (t-block, s-block), s <= t, by wavefront: 3, 3, 2, 2
+// block pairs (t-block, s-block), s <= t, in order (0,0) (1,0) (1,1) (2,0) ..
 __device__ __forceinline__ constexpr int pair_t(int p) { return p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3; }
 __device__ __forceinline__ constexpr int pair_s(int p) { return p - pair_t(p) * (pair_t(p) + 1) / 2; }
 
+// C2.  Pair stage: wavefront w takes pairs w and w + 8; product stage: token
+// rows 16 (w & 3) .., key column half w >> 2.
 template <int D, int DV>
-__global__ __launch_bounds__(256) void bwd_c2_kernel(
+__global__ __launch_bounds__(kNW * 64) void bwd_c2_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ kw,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO, const uint16_t* __restrict__ g,
     const uint16_t* __restrict__ b, const int32_t* __restrict__ cu, int n_seqs, int H,
@@ -800,7 +856,7 @@ __global__ __launch_bounds__(256) void bwd_c2_kernel(
 {
     using Ly = LayC2<D, DV>;
     constexpr int LDD = Ly::LDD, LDV = Ly::LDV, LDC = Ly::LDC;
-    constexpr int NKD = D / 32, NKV = DV / 32, NTD = D / 16;
+    constexpr int NKD = D / 32, NKV = DV / 32, HD = D / 32;
     __shared__ __attribute__((aligned(16))) unsigned char smem[Ly::total];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -825,20 +881,24 @@ __global__ __launch_bounds__(256) void bwd_c2_kernel(
     uint16_t* sMkk = reinterpret_cast<uint16_t*>(smem + Ly::oMkk);
     uint16_t* sMkw = reinterpret_cast<uint16_t*>(smem + Ly::oMkw);
     float* G = reinterpret_cast<float*>(smem + Ly::oG);
-    float* sL = G + 6 * kC + 4;                  // d/d ln gamma per token
+    float* sL = reinterpret_cast<float*>(smem + Ly::oG + kGateBytes);   // d/d ln gamma per token
     float* sDB = sL + kC;                        // db (Gram part) per token
 
     {
         const int64_t r0 = (int64_t)c.c0 * c.rowQK + (int64_t)e * D, v0 = (int64_t)c.c0 * c.rowV + (int64_t)e * DV;
-        stage_rows<D, LDD>(sK, k + r0, c.rowQK, c.nt, tid);
-        stage_rows<D, LDD>(sKW, kw + r0, c.rowQK, c.nt, tid);
-        stage_rows<D, LDD>(sQ, q + r0, c.rowQK, c.nt, tid);
-        stage_rows<DV, LDV>(sV, v + v0, c.rowV, c.nt, tid);
-        stage_rows<DV, LDV>(sO, dO + v0, c.rowV, c.nt, tid);
-        stage_rows<DV, LDV>(sX, xg + v0, c.rowV, c.nt, tid);
-        stage_rows<DV, LDV>(sR, drg + v0, c.rowV, c.nt, tid);
+        StageRows<D> xk, xkw, xq;
+        StageRows<DV> xv, xo, xx, xr;
+        xk.load(k + r0, c.rowQK, c.nt, tid);
+        xkw.load(kw + r0, c.rowQK, c.nt, tid);
+        xq.load(q + r0, c.rowQK, c.nt, tid);
+        xv.load(v + v0, c.rowV, c.nt, tid);
+        xo.load(dO + v0, c.rowV, c.nt, tid);
+        xx.load(xg + v0, c.rowV, c.nt, tid);
+        xr.load(drg + v0, c.rowV, c.nt, tid);
+        if (wave == 0)
+            gates_c(G, c);
         // the M matrices' blocks above the diagonal stay zero
-        for (int idx = tid; idx < 4 * 16 * 32; idx += 256) {
+        for (int idx = tid; idx < 4 * 16 * 32; idx += kNW * 64) {
             const int mtx = idx / 512, bi = (idx / 128) % 4, bj = (idx / 32) % 4, p = idx % 32;
             if (bj > bi) {
                 uint16_t* M = mtx == 0 ? sMqk : mtx == 1 ? sMqw : mtx == 2 ? sMkk : sMkw;
@@ -848,18 +908,23 @@ __global__ __launch_bounds__(256) void bwd_c2_kernel(
         }
         if (tid < 2 * kC)
             sL[tid] = 0.f;                       // sL and sDB
-        if (wave == 0)
-            gates_c(G, c);
+        xk.template store<LDD>(sK, tid);
+        xkw.template store<LDD>(sKW, tid);
+        xq.template store<LDD>(sQ, tid);
+        xv.template store<LDV>(sV, tid);
+        xo.template store<LDV>(sO, tid);
+        xx.template store<LDV>(sX, tid);
+        xr.template store<LDV>(sR, tid);
     }
     lds_barrier();
     const float* sLam = G + 3 * kC;
     const float* sB = G + 5 * kC;
 
     // ---- block pairs: Gram products and their gradients
-    for (int p = wave; p < 10; p += 4) {
+    for (int p = wave; p < 10; p += kNW) {
         const int tb = pair_t(p), sb = pair_s(p);
-        f32x4_t gkk = {0.f, 0.f, 0.f, 0.f}, gkw = gkk, aqk = gkk, aqw = gkk;
-        f32x4_t dqw = gkk, dqk = gkk, dkk = gkk, dkw = gkk;
+        f32x4_t gkk = {0.f, 0.f, 0.f, 0.f}, gkw2 = gkk, aqk = gkk, aqw = gkk;
+        f32x4_t dqw = gkk, dqk = gkk, dkk = gkk, dkw2 = gkk;
 #pragma unroll
         for (int kp = 0; kp < NKD; ++kp) {
             const bf16x8_t ak = frag_row(sK + tb * 16 * LDD + kp * 32, LDD, lane);
@@ -867,7 +932,7 @@ __global__ __launch_bounds__(256) void bwd_c2_kernel(
             const bf16x8_t bk = frag_row(sK + sb * 16 * LDD + kp * 32, LDD, lane);
             const bf16x8_t bw = frag_row(sKW + sb * 16 * LDD + kp * 32, LDD, lane);
             gkk = mma32(ak, bk, gkk);
-            gkw = mma32(ak, bw, gkw);
+            gkw2 = mma32(ak, bw, gkw2);
             aqk = mma32(aq, bk, aqk);
             aqw = mma32(aq, bw, aqw);
         }
@@ -880,35 +945,29 @@ __global__ __launch_bounds__(256) void bwd_c2_kernel(
             dqw = mma32(ao, bv, dqw);
             dqk = mma32(ao, bx, dqk);
             dkk = mma32(ar, bx, dkk);
-            dkw = mma32(ar, bv, dkw);
+            dkw2 = mma32(ar, bv, dkw2);
         }
         // element (t, s): t = 16 tb + 4 lg + r, s = 16 sb + li
         const int s = sb * 16 + li;
         const float ls = sLam[s];
         float rowsum[4], dbs[4], colsum = 0.f;
-        f32x4_t mqk, mqw, mkk, mkw;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = tb * 16 + lg * 4 + r;
             const float bt = sB[t];
             const float dec = __builtin_amdgcn_exp2f(fminf(sLam[t] - ls, 0.f));
             const float m0 = s <= t ? dec : 0.f, m1 = s < t ? dec : 0.f;
-            const float Aqk = m0 * aqk[r], Aqw = m0 * aqw[r], Gkk = m1 * gkk[r], Gkw = m1 * gkw[r];
+            const float Aqk = m0 * aqk[r], Aqw = m0 * aqw[r], Gkk = m1 * gkk[r], Gkw = m1 * gkw2[r];
             const float dAqw = s <= t ? dqw[r] : 0.f, dAqk = s <= t ? -dqk[r] : 0.f;
-            const float dAkk = s < t ? -dkk[r] : 0.f, dAkw = s < t ? dkw[r] : 0.f;
-            mqk[r] = dAqk * m0;
-            mqw[r] = dAqw * m0;
-            mkk[r] = dAkk * bt * m1;
-            mkw[r] = dAkw * bt * m1;
+            const float dAkk = s < t ? -dkk[r] : 0.f, dAkw = s < t ? dkw2[r] : 0.f;
             dbs[r] = dAkk * Gkk + dAkw * Gkw;
             const float cc = dAkk * bt * Gkk + dAkw * bt * Gkw + dAqk * Aqk + dAqw * Aqw;
             rowsum[r] = cc;
             colsum += cc;
-            // M into LDS: row t, column s
-            sMqk[t * LDC + s] = (uint16_t)(pack_bf16x2(mqk[r], 0.f) & 0xffffu);
-            sMqw[t * LDC + s] = (uint16_t)(pack_bf16x2(mqw[r], 0.f) & 0xffffu);
-            sMkk[t * LDC + s] = (uint16_t)(pack_bf16x2(mkk[r], 0.f) & 0xffffu);
-            sMkw[t * LDC + s] = (uint16_t)(pack_bf16x2(mkw[r], 0.f) & 0xffffu);
+            sMqk[t * LDC + s] = (uint16_t)(pack_bf16x2(dAqk * m0, 0.f) & 0xffffu);
+            sMqw[t * LDC + s] = (uint16_t)(pack_bf16x2(dAqw * m0, 0.f) & 0xffffu);
+            sMkk[t * LDC + s] = (uint16_t)(pack_bf16x2(dAkk * bt * m1, 0.f) & 0xffffu);
+            sMkw[t * LDC + s] = (uint16_t)(pack_bf16x2(dAkw * bt * m1, 0.f) & 0xffffu);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -927,18 +986,32 @@ __global__ __launch_bounds__(256) void bwd_c2_kernel(
     lds_barrier();
 
     // ---- dQ += M_qk K + M_qkw KW;  dK += (M_kk + M_kk^T) K + M_kkw KW + M_qk^T Q;
-    //      dKW += M_kkw^T K + M_qkw^T Q   (wavefront: tokens 16 tb ..)
+    //      dKW += M_kkw^T K + M_qkw^T Q   (token rows 16 tb .., key column half nh)
     {
-        const int tb = wave;
+        const int tb = wave & 3, nh = wave >> 2;
         const int t0 = tb * 16 + lg * 4;
+        const int d0c = nh * (D / 2);
+        // the values C1 stored, read before the products
+        float oq[HD][4], ok[HD][4], ow[HD][4];
 #pragma unroll
-        for (int n = 0; n < NTD; ++n) {
+        for (int n = 0; n < HD; ++n)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bool in = t0 + r < c.nt;
+                const int64_t o = (int64_t)(c.c0 + (in ? t0 + r : 0)) * c.rowQK + (int64_t)e * D + d0c + n * 16 + li;
+                oq[n][r] = in ? gq[o] : 0.f;
+                ok[n][r] = in ? gk[o] : 0.f;
+                ow[n][r] = in ? gkw[o] : 0.f;
+            }
+#pragma unroll
+        for (int n = 0; n < HD; ++n) {
+            const int nc = d0c + n * 16;
             f32x4_t aq = {0.f, 0.f, 0.f, 0.f}, ak = aq, aw = aq;
 #pragma unroll
             for (int h2 = 0; h2 <= 1; ++h2) {
-                const bf16x8_t bK = frag_col(sK + h2 * 32 * LDD + n * 16, LDD, lane);
-                const bf16x8_t bW = frag_col(sKW + h2 * 32 * LDD + n * 16, LDD, lane);
-                const bf16x8_t bQ = frag_col(sQ + h2 * 32 * LDD + n * 16, LDD, lane);
+                const bf16x8_t bK = frag_col(sK + h2 * 32 * LDD + nc, LDD, lane);
+                const bf16x8_t bW = frag_col(sKW + h2 * 32 * LDD + nc, LDD, lane);
+                const bf16x8_t bQ = frag_col(sQ + h2 * 32 * LDD + nc, LDD, lane);
                 if (h2 <= tb / 2) {                // s <= t: rows of M
                     aq = mma32(frag_row(sMqk + tb * 16 * LDC + h2 * 32, LDC, lane), bK, aq);
                     aq = mma32(frag_row(sMqw + tb * 16 * LDC + h2 * 32, LDC, lane), bW, aq);
@@ -952,14 +1025,13 @@ __global__ __launch_bounds__(256) void bwd_c2_kernel(
                     aw = mma32(frag_col(sMqw + h2 * 32 * LDC + tb * 16, LDC, lane), bQ, aw);
                 }
             }
-            const int col = n * 16 + li;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 if (t0 + r < c.nt) {
-                    const int64_t o = (int64_t)(c.c0 + t0 + r) * c.rowQK + (int64_t)e * D + col;
-                    gq[o] += aq[r];
-                    gk[o] += ak[r];
-                    gkw[o] += aw[r];
+                    const int64_t o = (int64_t)(c.c0 + t0 + r) * c.rowQK + (int64_t)e * D + nc + li;
+                    gq[o] = oq[n][r] + aq[r];
+                    gk[o] = ok[n][r] + ak[r];
+                    gkw[o] = ow[n][r] + aw[r];
                 }
             }
         }
@@ -1002,7 +1074,7 @@ static hipError_t launch_c_T(const ScanArgs& p, const BwdChunkBufs& w, hipStream
     const int64_t blocks = (int64_t)(p.total_tokens / kC + p.n_seqs) * p.heads;
     if (blocks == 0)
         return hipSuccess;
-    hipLaunchKernelGGL((bwdc::bwd_c1_kernel<D, DV>), dim3((unsigned)blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((bwdc::bwd_c1_kernel<D, DV>), dim3((unsigned)blocks), dim3(bwdc::kNW * 64), 0, stream,
                        (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.kw,
                        (const uint16_t*)p.v, (const uint16_t*)w.dO, (const uint16_t*)p.g,
                        (const uint16_t*)p.b, p.cu_seqlens, p.n_seqs, p.heads, (const uint16_t*)w.mats,
@@ -1012,7 +1084,7 @@ static hipError_t launch_c_T(const ScanArgs& p, const BwdChunkBufs& w, hipStream
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
-    hipLaunchKernelGGL((bwdc::bwd_c2_kernel<D, DV>), dim3((unsigned)blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((bwdc::bwd_c2_kernel<D, DV>), dim3((unsigned)blocks), dim3(bwdc::kNW * 64), 0, stream,
                        (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.kw,
                        (const uint16_t*)p.v, (const uint16_t*)w.dO, (const uint16_t*)p.g,
                        (const uint16_t*)p.b, p.cu_seqlens, p.n_seqs, p.heads, (const uint16_t*)w.xg,
