@@ -345,13 +345,20 @@ def bwd_bench(w, inp, dev_copies, steps, warmup, with_oracle=False):
     flops = bwd_flops(w, T)
     ach = nbytes / (ms * 1e-3) / 1e9
     tf = flops / (ms * 1e-3) / 1e12
+    # bf16 runs the chunkwise form (MFMA products; its floor is the HBM traffic
+    # of the inputs and gradients), fp32 or PRISM_BWD_CHUNKED=0 the token walk
+    # (fp32 vector arithmetic)
+    chunked = esize == 2 and os.environ.get("PRISM_BWD_CHUNKED", "1") == "1"
+    hbm = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": "backward (all launches)",
+           "avg_launch_us": ms * 1e3, "algorithmic_bytes": nbytes}
+    alu = {"bound": "alu", "achieved": tf, "peak": FP32_VALU_PEAK_TFLOPS,
+           "unit": "TFLOP/s", "frac": tf / FP32_VALU_PEAK_TFLOPS, "traffic": None,
+           "kernel": "backward (all launches)", "avg_launch_us": ms * 1e3,
+           "algorithmic_flops": flops}
     res = {"tokens_per_s": steps * T / elapsed, "us_per_call": ms * 1e3,
-            "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_VALU_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": tf / FP32_VALU_PEAK_TFLOPS, "traffic": None,
-                         "kernel": "backward (all launches)", "avg_launch_us": ms * 1e3,
-                         "algorithmic_flops": flops},
-            "hbm": {"achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": ach / HBM_PEAK_GBS, "algorithmic_bytes": nbytes}}
+           "path": "chunkwise" if chunked else "token walk",
+           "roofline": hbm if chunked else alu, "hbm": hbm}
     if with_oracle:
         # a bounded sample: as many whole (sequence, head) chains as host threads
         # (the oracle keeps every state of a chain), scaled to tokens/s of the

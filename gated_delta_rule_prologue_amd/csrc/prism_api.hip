@@ -438,13 +438,15 @@ prism_status prism_fwd_resume(const prism_dims* d, const void* q, const void* k,
                     S_final, k_hist_out, workspace, workspace_bytes, stream);
 }
 
-// Chunkwise backward (PRISM_BWD_CHUNKED=1, bf16, dk and dv in {64, 128}): the
-// forward state products again with every chunk's start state kept (bf16), the
-// carried state gradient backwards chunk by chunk, then every input gradient
-// of all chunks at once on MFMA, then the write-key chain backwards.
+// Chunkwise backward (bf16, dk and dv in {64, 128}; PRISM_BWD_CHUNKED=0 selects
+// the token walk instead): the forward state products again with every chunk's
+// start state kept (bf16), the carried state gradient backwards chunk by chunk,
+// then every input gradient of all chunks at once on MFMA, then the write-key
+// chain backwards.  At the LM layer (B=8, T=2048, H=6, d=128) 0.89 ms against
+// 3.5 ms for the token walk.
 bool use_bwd_chunked(const prism_dims* d)
 {
-    return env_int("PRISM_BWD_CHUNKED", 0) == 1 && d->dtype == PRISM_BF16 &&
+    return env_int("PRISM_BWD_CHUNKED", 1) == 1 && d->dtype == PRISM_BF16 &&
            (d->dk == 64 || d->dk == 128) && (d->dv == 64 || d->dv == 128) && d->total_tokens > 0;
 }
 

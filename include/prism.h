@@ -281,11 +281,19 @@ size_t prism_scan_workspace_bytes(const prism_dims* d);
  * gradients of the loss  sum_t <dO_t, o_t> + <dS_final, S_final>  with respect
  * to every input, by reverse-mode differentiation of the token recurrence
  * (WeChat page sections 核心迭代形式, 消除 Token 间串行, 消除 Step 间串行;
- * gist.science section 2.1).  The write keys are recomputed by the prologue;
- * the scan is walked backwards token by token, in up to 8 segments per
- * sequence side by side, from states checkpointed every 4 tokens (16 at
- * dk = 64) and gradients stored at the segment ends, which the workspace
- * holds (about 4 B * H * dk * dv * (T / 4 + 9 n_seqs)).
+ * gist.science section 2.1).  The write keys are recomputed by the prologue.
+ * bf16 inputs: the gradients come from the chunkwise (UT / WY) form of the
+ * recurrence that the forward evaluates (WeChat page section 消除 Token 间串行):
+ * the per-chunk products are recomputed with every 64-token chunk's start
+ * state kept in bf16, the state gradient is carried backwards chunk by chunk,
+ * and every other gradient of all chunks is formed at once on the matrix
+ * cores; the workspace holds about H * (20 KB + 8 B * dk * dv) per chunk and
+ * H * (6 dk + 4 dv + 12) bytes per token.  fp32 inputs (and bf16 with
+ * PRISM_BWD_CHUNKED=0): the scan is walked backwards token by token, in up to
+ * 8 segments per sequence side by side, from states checkpointed every 4
+ * tokens (16 at dk = 64) and gradients stored at the segment ends, which the
+ * workspace holds (about 4 B * H * dk * dv * (T / 4 + 9 n_seqs)).  The
+ * workspace size depends on PRISM_BWD_CHUNKED at the time of the query.
  *
  *   inputs as in prism_fwd; S_init as in prism_fwd_resume (NULL = zero)
  *   dO          [T, H, dv], input dtype
@@ -296,9 +304,9 @@ size_t prism_scan_workspace_bytes(const prism_dims* d);
  *   dg, db      out fp32 [T, H]              dconv_w  out fp32 [H, dk, 4]
  *   dS_init     out fp32 [n_seqs, H, dk, dv] or NULL (not written)
  *   workspace   prism_bwd_workspace_bytes(d, L) bytes
- * dk, dv in {64, 128}, else PRISM_EUNSUPPORTED.  Gradients accumulated over
- * value slices and tokens use fp32 atomics, so the last bits may differ from
- * run to run.
+ * dk, dv in {64, 128}, else PRISM_EUNSUPPORTED.  Some gradients are summed
+ * with fp32 atomics (db over channel groups; on the token walk also over value
+ * slices), so the last bits may differ from run to run.
  */
 size_t prism_bwd_workspace_bytes(const prism_dims* d, int L);
 prism_status prism_bwd(const prism_dims* d,

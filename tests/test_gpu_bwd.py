@@ -1,7 +1,9 @@
 """GPU parity of the backward pass (prism_bwd_ex with the closed-form residual
 chain, and with the GELU refinement chain) against the fp64 oracle's backward (itself pinned against finite differences
 and torch autograd): every gradient, max-relative error per tensor, at the
-forward's tolerances (1e-4 fp32 inputs, 1e-2 bf16 inputs)."""
+forward's tolerances (1e-4 fp32 inputs, 1e-2 bf16 inputs).  The default path:
+chunkwise for bf16 inputs, the token walk for fp32 (test_gpu_bwd_chunked.py
+selects each path explicitly)."""
 import numpy as np
 import pytest
 
@@ -135,13 +137,16 @@ def _chain_rows(x, inp, chains):
     return np.concatenate(parts).astype(np.float64)
 
 
+@pytest.mark.parametrize("path", ["chunked", "token"])
 @pytest.mark.parametrize("name,chains", [("long-context-64k", [5]),
                                          ("varlen-histories", [3, 1010, 2047, 2600, 4095])])
-def test_bwd_large_workloads_sampled_chains(name, chains):
-    """The 64k workload (one sequence of 65,536 tokens, H=16, d=128: the backward
-    cuts it into 8 segments and keeps checkpoints of ~18 GB) and the varlen
-    workload (4,096 chains: one segment each): every gradient of the sampled
-    chains, compared row by row (only those rows are copied to the host)."""
+def test_bwd_large_workloads_sampled_chains(name, chains, path, monkeypatch):
+    """The 64k workload (one sequence of 65,536 tokens, H=16, d=128: the token
+    walk cuts it into 8 segments and keeps checkpoints of ~18 GB, the chunkwise
+    form keeps 1,025 chunk states) and the varlen workload (4,096 chains): every
+    gradient of the sampled chains, compared row by row (only those rows are
+    copied to the host), on both backward paths."""
+    monkeypatch.setenv("PRISM_BWD_CHUNKED", "1" if path == "chunked" else "0")
     import torch
     from gated_delta_rule_prologue_amd import binding
     from gated_delta_rule_prologue_amd.inputs import f32_to_bf16_bits, to_float
@@ -217,6 +222,7 @@ def test_bwd_segment_counts(segs, monkeypatch):
     side from gradients stored at their ends by a reverse sweep of G alone:
     any P gives the oracle's gradients, on ragged and empty sequences."""
     monkeypatch.setenv("PRISM_BWD_SEGMENTS", segs)
+    monkeypatch.setenv("PRISM_BWD_CHUNKED", "0")     # the token walk (bf16 default: chunkwise)
     w = W(dtype="bf16", dk=128, dv=128, L=4, lengths=(300, 1, 0, 97, 33))
     inp = make_inputs(w)
     say(f"segments {segs}")

@@ -1,9 +1,10 @@
-"""GPU parity of the chunkwise backward (PRISM_BWD_CHUNKED=1, bf16): the
-forward state products again with each chunk's start state kept, the carried
-state gradient chunk by chunk, then every input gradient of all chunks at once
-on MFMA.  Checked against the fp64 oracle's backward (pinned against finite
-differences and torch autograd), every gradient, at the bf16 tolerance, and
-against the token-recurrent backward."""
+"""GPU parity of the two bf16 backward paths, each selected explicitly: the
+chunkwise form (PRISM_BWD_CHUNKED=1, the default: the forward state products
+again with each chunk's start state kept, the carried state gradient chunk by
+chunk, then every input gradient of all chunks at once on MFMA) and the token
+walk (PRISM_BWD_CHUNKED=0).  Checked against the fp64 oracle's backward
+(pinned against finite differences and torch autograd), every gradient, at
+the bf16 tolerance, and against each other."""
 import numpy as np
 import pytest
 
@@ -27,6 +28,11 @@ def _gpu():
 @pytest.fixture
 def chunked(monkeypatch):
     monkeypatch.setenv("PRISM_BWD_CHUNKED", "1")
+
+
+@pytest.fixture
+def token_walk(monkeypatch):
+    monkeypatch.setenv("PRISM_BWD_CHUNKED", "0")
 
 
 def _chunked_ws_bytes(inp):
@@ -61,6 +67,14 @@ def test_chunked_bwd_matches_oracle(w, chunked):
     assert int(binding.lib().prism_bwd_workspace_bytes(d, inp.L)) == _chunked_ws_bytes(inp), \
         "the chunkwise path is not the one taken"
     say(f"chunked bwd {w}")
+    got, ref = run(inp)
+    check(got, ref, "bf16")
+
+
+@pytest.mark.parametrize("w", CASES[:2], ids=lambda w: f"dk{w.dk}-dv{w.dv}-L{w.L}")
+def test_token_walk_bwd_matches_oracle(w, token_walk):
+    inp = make_inputs(w)
+    say(f"token-walk bwd {w}")
     got, ref = run(inp)
     check(got, ref, "bf16")
 
@@ -105,6 +119,7 @@ def test_chunked_agrees_with_token_recurrent(monkeypatch):
         torch.cuda.synchronize()
         return {n: g[n].cpu().numpy().astype(np.float64) for n in NAMES if g[n] is not None}
 
+    monkeypatch.setenv("PRISM_BWD_CHUNKED", "0")
     a = go()
     monkeypatch.setenv("PRISM_BWD_CHUNKED", "1")
     b = go()
@@ -116,9 +131,11 @@ def test_chunked_agrees_with_token_recurrent(monkeypatch):
 
 @pytest.mark.parametrize("name,chains", [("lm-130m-layer", [5, 37]),
                                          ("recsys-history", [0, 77, 130, 255])])
-def test_chunked_bwd_full_size_sampled_chains(name, chains, chunked):
+def test_token_walk_bwd_full_size_sampled_chains(name, chains, token_walk):
     """The LM layer (B=8, T=2048, H=6, d=128, L=4) and the recommendation
-    histories (B=64, T=1024, H=4, d=64, L=4): every gradient of sampled chains."""
+    histories (B=64, T=1024, H=4, d=64, L=4) on the token walk (the default
+    path's full-size cases are in test_gpu_bwd.py): every gradient of sampled
+    chains."""
     w = BY_NAME[name]
     inp = make_inputs(w)
     say(f"chunked {name}: chains {chains}")
