@@ -74,10 +74,15 @@ def algorithmic_work(w, n_seqs, T, esize):
     ht = T * H
     pro = esize * (dk + 2 * (L - 1) * dk + max(L - 2, 0) * dk + 1 + dk) * ht
     scan = esize * (3 * dk + dv + 2 + dv) * ht + 4 * n_seqs * H * dk * dv
-    C = 64
-    flops_ht = 10 * C * dk + 8 * C * dv + 8 * dk * dv + round(2 * C * C / 3)
-    return {"prologue_bytes": pro, "scan_bytes": scan, "scan_flops": flops_ht * ht,
+    return {"prologue_bytes": pro, "scan_bytes": scan, "scan_flops": scan_flops_ht(w) * ht,
             "head_tokens": ht}
+
+
+def scan_flops_ht(w):
+    """Dense MFMA flops of the chunkwise scan per head-token (C = 64; see
+    algorithmic_work)."""
+    C, dk, dv = 64, w.dk, w.dv
+    return 10 * C * dk + 8 * C * dv + 8 * dk * dv + round(2 * C * C / 3)
 
 
 def source_sha(paths):
@@ -302,6 +307,19 @@ def bwd_flops(w, T):
     return 37 * T * w.heads * w.dk * w.dv
 
 
+def bwd_chunk_flops(w, T):
+    """Dense MFMA flops of one backward pass in its chunkwise form (C = 64), per
+    head-token: the forward's chunk algebra recomputed (scan_flops), the
+    reverse state pass (K dS1, A_qk^T dO, T^T dX, Q^T dO, K^T dR:
+    6 dk dv + 4 C dv), the state-dependent gradients (K S0, A_kkw V, T R, K dS1,
+    A_qk^T dO, T^T dX, KW dS1, A_qkw^T dO, A_kkw^T dR, then dO S0^T, dR S0^T,
+    X dS1^T, V dS1^T: 14 dk dv + 12 C dv) and the Gram-side gradients (four Gram
+    products, four dA products, eight M products: 24 C dk + 8 C dv)."""
+    C, dk, dv = 64, w.dk, w.dv
+    per = 20 * dk * dv + 24 * C * dk + 24 * C * dv
+    return (per + scan_flops_ht(w)) * T * w.heads
+
+
 def bwd_bench(w, inp, dev_copies, steps, warmup, with_oracle=False):
     """Time prism_bwd (gradients of every input) on the workload, with the
     upstream gradient dO and no carried state."""
@@ -359,6 +377,11 @@ def bwd_bench(w, inp, dev_copies, steps, warmup, with_oracle=False):
     res = {"tokens_per_s": steps * T / elapsed, "us_per_call": ms * 1e3,
            "path": "chunkwise" if chunked else "token walk",
            "roofline": hbm if chunked else alu, "hbm": hbm}
+    if chunked:
+        mf = bwd_chunk_flops(w, T)
+        tfm = mf / (ms * 1e-3) / 1e12
+        res["mfma"] = {"achieved": tfm, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                       "frac": tfm / BF16_PEAK_TFLOPS, "algorithmic_flops": mf}
     if with_oracle:
         # a bounded sample: as many whole (sequence, head) chains as host threads
         # (the oracle keeps every state of a chain), scaled to tokens/s of the

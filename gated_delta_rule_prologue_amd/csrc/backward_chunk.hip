@@ -543,6 +543,14 @@ __global__ __launch_bounds__(kNW * 64) void bwd_c1_kernel(
     float* G = reinterpret_cast<float*>(smem + Ly::oG);
     float* sSc = reinterpret_cast<float*>(smem + Ly::oSc);
     float* sRed = reinterpret_cast<float*>(smem + Ly::oRed);
+    const int t0 = tb * 16 + lg * 4;             // this lane's first token row of a tile
+    const uint16_t* ckT0 = ckT + c.vcid * (int64_t)DV * D;
+    const uint16_t* ck0 = ck + c.vcid * (int64_t)D * DV;
+    const uint16_t* dckT0 = dckT + c.vcid * (int64_t)DV * D;
+    const uint16_t* dck0 = dck + c.vcid * (int64_t)D * DV;
+    const int v0c = nh * (DV / 2), d0c = nh * (D / 2);   // first column of this wavefront's half
+    // B fragments of S0 (the first product) and of dS1 (dX and dV), read ahead
+    bf16x8_t fS[NKD][HV];
 
     {
         const int64_t r0 = (int64_t)c.c0 * c.rowQK + (int64_t)e * D, v0 = (int64_t)c.c0 * c.rowV + (int64_t)e * DV;
@@ -559,6 +567,12 @@ __global__ __launch_bounds__(kNW * 64) void bwd_c1_kernel(
         makw.load(m + gram::kMatAkkw * gram::kMatElems, tid);
         mnqk.load(m + gram::kMatNAqk * gram::kMatElems, tid);
         maqw.load(m + gram::kMatAqkw * gram::kMatElems, tid);
+        // S0 fragments of the first product, in flight with the staging
+#pragma unroll
+        for (int kp = 0; kp < NKD; ++kp)
+#pragma unroll
+            for (int n = 0; n < HV; ++n)
+                fS[kp][n] = ldg16(ckT0 + (v0c + n * 16 + li) * D + kp * 32 + lg * 8);
         if (wave == 0)
             gates_c(G, c);
         xk.template store<LDD>(sK, tid);
@@ -576,12 +590,6 @@ __global__ __launch_bounds__(kNW * 64) void bwd_c1_kernel(
     lds_barrier();
     const float* sBG = G + kC;
     const float* sFac = G + 2 * kC;
-    const int t0 = tb * 16 + lg * 4;             // this lane's first token row of a tile
-    const uint16_t* ckT0 = ckT + c.vcid * (int64_t)DV * D;
-    const uint16_t* ck0 = ck + c.vcid * (int64_t)D * DV;
-    const uint16_t* dckT0 = dckT + c.vcid * (int64_t)DV * D;
-    const uint16_t* dck0 = dck + c.vcid * (int64_t)D * DV;
-    const int v0c = nh * (DV / 2), d0c = nh * (D / 2);   // first column of this wavefront's half
 
     // ---- R = diag(b gamma) K S0 + A_kkw V -> sR
     {
@@ -594,8 +602,14 @@ __global__ __launch_bounds__(kNW * 64) void bwd_c1_kernel(
             const bf16x8_t a = frag_row(sK + tb * 16 * LDD + kp * 32, LDD, lane);
 #pragma unroll
             for (int n = 0; n < HV; ++n)
-                acc[n] = mma32(a, ldg16(ckT0 + (v0c + n * 16 + li) * D + kp * 32 + lg * 8), acc[n]);
+                acc[n] = mma32(a, fS[kp][n], acc[n]);
         }
+        // dS1 fragments for dX and dV, in flight from here
+#pragma unroll
+        for (int kp = 0; kp < NKD; ++kp)
+#pragma unroll
+            for (int n = 0; n < HV; ++n)
+                fS[kp][n] = ldg16(dckT0 + (v0c + n * 16 + li) * D + kp * 32 + lg * 8);
         const float4 bg = *reinterpret_cast<const float4*>(sBG + t0);
 #pragma unroll
         for (int n = 0; n < HV; ++n) {
@@ -648,7 +662,7 @@ __global__ __launch_bounds__(kNW * 64) void bwd_c1_kernel(
             const bf16x8_t a = frag_row(sK + tb * 16 * LDD + kp * 32, LDD, lane);
 #pragma unroll
             for (int n = 0; n < HV; ++n)
-                y[n] = mma32(a, ldg16(dckT0 + (v0c + n * 16 + li) * D + kp * 32 + lg * 8), y[n]);
+                y[n] = mma32(a, fS[kp][n], y[n]);
         }
 #pragma unroll
         for (int h2 = 0; h2 <= 1; ++h2) {
@@ -724,7 +738,7 @@ __global__ __launch_bounds__(kNW * 64) void bwd_c1_kernel(
             const bf16x8_t a = frag_row(sKW + tb * 16 * LDD + kp * 32, LDD, lane);
 #pragma unroll
             for (int n = 0; n < HV; ++n)
-                acc[n] = mma32(a, ldg16(dckT0 + (v0c + n * 16 + li) * D + kp * 32 + lg * 8), acc[n]);
+                acc[n] = mma32(a, fS[kp][n], acc[n]);
         }
 #pragma unroll
         for (int n = 0; n < HV; ++n)

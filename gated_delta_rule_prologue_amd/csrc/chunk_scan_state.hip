@@ -256,18 +256,22 @@ struct Frags {
                                  sq, ((tb * 16 + li) * (int)c.rowQK + n * 16 + 4 * lg) * 2, 0, 0));
         }
     }
+    template <bool WO>
     __device__ void load(const Ctx& c, int ch, int h)
     {
         load_t(c, ch);
-        load_qk(c, ch);
-        load_q(c, ch, h);
+        if constexpr (WO) {
+            load_qk(c, ch);
+            load_q(c, ch, h);
+        }
     }
 };
 
 // ---- helper h: chunk ch into buffer buf (rows, gates, W, Q', U, O_loc) from
 // st (rows of ch) and fr (fragments of ch), loading each for chunk ch + 1 as
 // soon as chunk ch is done with it.  Reads only what this wavefront wrote.
-template <int D>
+// WO false (no outputs wanted: the states alone): Q' and O_loc are skipped.
+template <int D, bool WO>
 __device__ __forceinline__ void prepare(Rows<D>& st, Frags<D>& fr, unsigned char* buf, float* scr,
                                         const Ctx& c, int ch, int h)
 {
@@ -387,6 +391,8 @@ __device__ __forceinline__ void prepare(Rows<D>& st, Frags<D>& fr, unsigned char
     SCHED_FENCE();
     fr.load_t(c, ch + 1);
     SCHED_FENCE();
+    if constexpr (!WO)
+        return;
 
     // Q'^T = diag(gamma) Q^T - W^T A_qk^T (the stored matrix is -A_qk); W^T read back
     {
@@ -462,8 +468,8 @@ __device__ __forceinline__ void prepare(Rows<D>& st, Frags<D>& fr, unsigned char
 // S0 enters the products as a 16x16x32 operand built from the accumulators.
 // The LDS reads of each step are issued one step ahead (SCHED_FENCE keeps the
 // scheduler from sinking them next to their uses: a wavefront alone on its
-// SIMD has nothing else to hide the LDS latency with).
-template <int D>
+// SIMD has nothing else to hide the LDS latency with).  WO false: no O.
+template <int D, bool WO>
 __device__ __forceinline__ void state_chunk(f32x4_t (&S)[D / 16], const unsigned char* buf, const Ctx& c,
                                             int ch, int jb)
 {
@@ -499,12 +505,14 @@ __device__ __forceinline__ void state_chunk(f32x4_t (&S)[D / 16], const unsigned
     // Q' row fragments and O_loc, read while X runs
     bf16x8_t qf[4][NKP];
     u32x2_t ob[4];
+    if constexpr (WO) {
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
+        for (int tb = 0; tb < 4; ++tb) {
 #pragma unroll
-        for (int kp = 0; kp < NKP; ++kp)
-            qf[tb][kp] = *reinterpret_cast<const bf16x8_t*>(sQp + wy_off<D>(tb * 16 + li, kp * 32 + lg * 8));
-        ob[tb] = sO[tb * 64 + lane];
+            for (int kp = 0; kp < NKP; ++kp)
+                qf[tb][kp] = *reinterpret_cast<const bf16x8_t*>(sQp + wy_off<D>(tb * 16 + li, kp * 32 + lg * 8));
+            ob[tb] = sO[tb * 64 + lane];
+        }
     }
     SCHED_FENCE();
 
@@ -542,14 +550,16 @@ __device__ __forceinline__ void state_chunk(f32x4_t (&S)[D / 16], const unsigned
 
     // ---- O^T = (Q' S0)^T + O_loc^T
     f32x4_t OT[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-        OT[tb] = unpack4(ob[tb]);
-#pragma unroll
-    for (int kp = 0; kp < NKP; ++kp) {
+    if constexpr (WO) {
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
-            OT[tb] = mma32(s0q[kp], qf[tb][kp], OT[tb]);
+            OT[tb] = unpack4(ob[tb]);
+#pragma unroll
+        for (int kp = 0; kp < NKP; ++kp) {
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+                OT[tb] = mma32(s0q[kp], qf[tb][kp], OT[tb]);
+        }
     }
     SCHED_FENCE();
 
@@ -607,11 +617,11 @@ __device__ __forceinline__ void state_chunk(f32x4_t (&S)[D / 16], const unsigned
 
     // ---- O rows (lane (li, lg): token tb * 16 + li, value columns 4 lg .. of block jb);
     //      rows past the chunk's last token fall outside the buffer range
+    if constexpr (!WO)
+        return;
     const int c0 = c.seq0 + ch * kC;
     const int nt = chunk_tokens(c, ch);
-    // (no o: an empty range, the stores are dropped)
-    const __amdgpu_buffer_rsrc_t orsrc =
-        rsrc(c.o ? c.o + (int64_t)c0 * c.rowV : c.k, c.o ? nt * (int)c.rowV * 2 : 0);
+    const __amdgpu_buffer_rsrc_t orsrc = rsrc(c.o + (int64_t)c0 * c.rowV, nt * (int)c.rowV * 2);
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
         const int t = tb * 16 + li;
@@ -620,7 +630,7 @@ __device__ __forceinline__ void state_chunk(f32x4_t (&S)[D / 16], const unsigned
     }
 }
 
-template <int D>
+template <int D, bool WO>
 __global__ __launch_bounds__(kWaves * 64) void scan_state_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ kw, const uint16_t* __restrict__ v,
@@ -680,7 +690,7 @@ __global__ __launch_bounds__(kWaves * 64) void scan_state_kernel(
                         make_uint2(pack_bf16x2(S[ib][0], S[ib][1]), pack_bf16x2(S[ib][2], S[ib][3]));
                 }
             }
-            state_chunk<D>(S, smem + (ch & 1) * Ly::szBuf, c, ch, jb);
+            state_chunk<D, WO>(S, smem + (ch & 1) * Ly::szBuf, c, ch, jb);
             lds_barrier();
         }
         if (s_final) {
@@ -697,13 +707,13 @@ __global__ __launch_bounds__(kWaves * 64) void scan_state_kernel(
         Rows<D> rows;
         Frags<D> fr;
         rows.load(c, 0, h);
-        fr.load(c, 0, h);
-        prepare<D>(rows, fr, smem, scr, c, 0, h);
+        fr.template load<WO>(c, 0, h);
+        prepare<D, WO>(rows, fr, smem, scr, c, 0, h);
         lds_barrier();
         // chunk ch + 1 into the buffer the state wavefronts are not reading
         // (past the last chunk this prepares an empty chunk no one reads)
         for (int ch = 0; ch < c.nchunks; ++ch) {
-            prepare<D>(rows, fr, smem + ((ch + 1) & 1) * Ly::szBuf, scr, c, ch + 1, h);
+            prepare<D, WO>(rows, fr, smem + ((ch + 1) & 1) * Ly::szBuf, scr, c, ch + 1, h);
             lds_barrier();
         }
     }
@@ -724,7 +734,9 @@ hipError_t launch_scan_state(const ScanArgs& p, const void* mats, hipStream_t st
     const int64_t blocks = (int64_t)p.n_seqs * p.heads * n_slices;
     if (blocks == 0)
         return hipSuccess;
-    auto kern = p.dk == 64 ? stscan::scan_state_kernel<64> : stscan::scan_state_kernel<128>;
+    // without o (the backward's recomputation of the states) the output terms are skipped
+    auto kern = p.o ? (p.dk == 64 ? stscan::scan_state_kernel<64, true> : stscan::scan_state_kernel<128, true>)
+                    : (p.dk == 64 ? stscan::scan_state_kernel<64, false> : stscan::scan_state_kernel<128, false>);
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(stscan::kWaves * 64), 0, stream,
                        (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.kw,
                        (const uint16_t*)p.v, (const uint16_t*)p.g, (const uint16_t*)p.b,
