@@ -501,33 +501,49 @@ __global__ __launch_bounds__(64) void scan_bwd_kernel(
 // registers and added to dk, which already holds the scan's part, with one
 // read-modify-write: no other wavefront touches those elements.  The keys of
 // the taps slide through registers (one load per token), the next token's
-// loads are issued before this token's arithmetic, db takes one atomic per
-// (token, head, 64 channels), and the taps' gradients are summed over the
-// workgroup and stored per token block (reduced by wk_reduce_kernel: no
-// atomics on the 4 x H x dk weights).
+// loads are issued before this token's arithmetic (the token loop is unrolled
+// and every load is bounded, so the code is straight-line), db takes one
+// atomic per (token, head, 64 channels), and the taps' gradients are summed
+// over the workgroup and stored per token block (reduced by wk_reduce_kernel:
+// no atomics on the 4 x H x dk weights).
 template <typename T, int L>
 struct WkTok {
     float gkw, kt, bt;
     float a[L > 1 ? L - 1 : 1], u[L > 1 ? L - 1 : 1], h[L > 1 ? L - 1 : 1];
 };
 
-template <typename T, int L>
-__device__ __forceinline__ void wk_load(WkTok<T, L>& x, const T* k, const T* u, const T* a, const T* h,
-                                        const T* b, const float* dkw, int t, int T_total, int H, int DK,
-                                        int e, int i)
+// One element through a bounded buffer resource (zero outside its range).
+__device__ __forceinline__ float bld(__amdgpu_buffer_rsrc_t r, int i, const uint16_t*)
 {
-    const bool in = t < T_total;
-    const int64_t rk = ((int64_t)t * H + e) * DK + i;
-    x.gkw = in ? dkw[rk] : 0.f;
-    x.kt = in ? ld(k, rk) : 0.f;
-    x.bt = in ? ld(b, (int64_t)t * H + e) : 0.f;
+    return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, i * 2, 0, 0));
+}
+__device__ __forceinline__ float bld(__amdgpu_buffer_rsrc_t r, int i, const float*)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, i * 4, 0, 0));
+}
+
+// Buffer resources over the rows [rb, re) of the tensors a wavefront reads:
+// element offsets relative to row rb; rows outside the range read as zero, so
+// no load needs a branch.
+template <typename T>
+struct WkSrc {
+    __amdgpu_buffer_rsrc_t k, u, a, h, b, dkw, dk;
+};
+
+template <typename T, int L>
+__device__ __forceinline__ void wk_load(WkTok<T, L>& x, const WkSrc<T>& r, int tr, int H, int DK, int e, int i)
+{
+    const int rk = (tr * H + e) * DK + i;
+    x.gkw = bld(r.dkw, rk, (const float*)nullptr);
+    x.kt = bld(r.k, rk, (const T*)nullptr);
+    x.bt = bld(r.b, tr * H + e, (const T*)nullptr);
     if constexpr (L > 1) {
-        const int64_t lb = (int64_t)t * H * (L - 1) * DK + (int64_t)e * (L - 1) * DK + i;
+        const int lb = (tr * H + e) * (L - 1) * DK + i;
 #pragma unroll
         for (int l = 0; l < L - 1; ++l) {
-            x.a[l] = in ? ld(a, lb + (int64_t)l * DK) : 0.f;
-            x.u[l] = in ? ld(u, lb + (int64_t)l * DK) : 0.f;
-            x.h[l] = in ? ld(h, lb + (int64_t)l * DK) : 0.f;
+            x.a[l] = bld(r.a, lb + l * DK, (const T*)nullptr);
+            x.u[l] = bld(r.u, lb + l * DK, (const T*)nullptr);
+            x.h[l] = bld(r.h, lb + l * DK, (const T*)nullptr);
         }
     }
 }
@@ -541,6 +557,7 @@ __global__ __launch_bounds__(256) void write_key_bwd_kernel(
     float* __restrict__ da, float* __restrict__ dh, float* __restrict__ db,
     float* __restrict__ dconv_part)
 {
+    constexpr int NIT = kC + 3;                  // own tokens and the three after them
     __shared__ float4 red[4][64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -556,29 +573,54 @@ __global__ __launch_bounds__(256) void write_key_bwd_kernel(
         w[m] = ld(conv_w, ((int64_t)e * DK + i) * 4 + m);
     float dw[4] = {0.f, 0.f, 0.f, 0.f};
     if (t_lo < T_total) {
-        // sequence of t_lo
-        int lo = 0, hi = n_seqs;
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (cu[mid] <= t_lo) lo = mid; else hi = mid;
+        // sequence bounds of token t_lo - 3 + j in lane j (a token outside [0, T)
+        // gets the end -1, which matches no token's)
+        int sq0 = 0, sq1 = -1;
+        {
+            const int tt = t_lo - 3 + lane;
+            if (lane < NIT + 3 && tt >= 0 && tt < T_total) {
+                int lo = 0, hi = n_seqs;             // largest n with cu[n] <= tt
+                while (hi - lo > 1) {
+                    const int mid = (lo + hi) >> 1;
+                    if (cu[mid] <= tt) lo = mid; else hi = mid;
+                }
+                sq0 = cu[lo];
+                sq1 = cu[lo + 1];
+            }
         }
-        int sn = lo;
-        int s0 = cu[sn], s1 = cu[sn + 1];        // bounds of the sequence holding t
+        const int rb = max(0, t_lo - 3), re = min(T_total, t_lo + NIT);
+        const int nr = re - rb;
+        const int64_t rowK = (int64_t)H * DK, rowL = rowK * (L > 1 ? L - 1 : 1);
+        auto mk = [](const void* p, int64_t bytes) {
+            return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+        };
+        WkSrc<T> r;
+        r.k = mk(k + rb * rowK, nr * rowK * sizeof(T));
+        r.dkw = mk(dkw + rb * rowK, nr * rowK * 4);
+        r.dk = mk(dk + rb * rowK, nr * rowK * 4);
+        r.b = mk(b + (int64_t)rb * H, (int64_t)nr * H * sizeof(T));
+        if constexpr (L > 1) {
+            r.u = mk(u + rb * rowL, nr * rowL * sizeof(T));
+            r.a = mk(a + rb * rowL, nr * rowL * sizeof(T));
+            r.h = mk(h + rb * rowL, nr * rowL * sizeof(T));
+        }
+        const int t0r = t_lo - rb;               // row of t_lo in the ranges
         // keys of tokens t-3 .. t (raw: the sequence start masks them per token)
         float kwin[4];
 #pragma unroll
-        for (int m = 0; m < 3; ++m) {
-            const int tau = t_lo - 3 + m;
-            kwin[m + 1] = tau >= 0 ? ld(k, ((int64_t)tau * H + e) * DK + i) : 0.f;
-        }
+        for (int m = 0; m < 3; ++m)
+            kwin[m + 1] = bld(r.k, (t0r - 3 + m) * (int)rowK + e * DK + i, (const T*)nullptr);
         // dr_0 of tokens t-3 .. t with the end of the sequence each belongs to, and
         // the dkw and b of those tokens (dk of token t-3 is completed at token t)
         float dr[4] = {0.f, 0.f, 0.f, 0.f}, gh[4] = {0.f, 0.f, 0.f, 0.f}, bh[4] = {0.f, 0.f, 0.f, 0.f};
         int se[4] = {-1, -1, -1, -1};
-        const int t_end = min(T_total, t_hi + 3);
         WkTok<T, L> nx;
-        wk_load<T, L>(nx, k, u, a, h, b, dkw, t_lo, T_total, H, DK, e, i);
-        for (int t = t_lo; t < t_hi + 3; ++t) {
+        wk_load<T, L>(nx, r, t0r, H, DK, e, i);
+        // fully unrolled: straight-line code, so every wait counts exactly the
+        // loads it needs (a loop would wait for all of them at its head)
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int t = t_lo + it;
 #pragma unroll
             for (int x = 0; x < 3; ++x) {
                 dr[x] = dr[x + 1];
@@ -587,94 +629,85 @@ __global__ __launch_bounds__(256) void write_key_bwd_kernel(
                 bh[x] = bh[x + 1];
                 kwin[x] = kwin[x + 1];
             }
-            dr[3] = 0.f;
-            se[3] = -1;
-            gh[3] = 0.f;
-            bh[3] = 0.f;
-            kwin[3] = 0.f;
             const int tau = t - 3;
-            const int64_t rt = ((int64_t)tau * H + e) * DK + i;
-            const float dk_old = tau >= t_lo ? dk[rt] : 0.f;
-            if (t < t_end) {
-                const WkTok<T, L> cur = nx;
-                if (t + 1 < t_end)
-                    wk_load<T, L>(nx, k, u, a, h, b, dkw, t + 1, T_total, H, DK, e, i);
-                while (s1 <= t) {                // the sequence holding t (skips empty ones)
-                    ++sn;
-                    s0 = s1;
-                    s1 = cu[sn + 1];
+            float dk_old = 0.f;
+            if (it >= 3)
+                dk_old = bld(r.dk, (tau - rb) * (int)rowK + e * DK + i, (const float*)nullptr);
+            const WkTok<T, L> cur = nx;
+            if (it + 1 < NIT)
+                wk_load<T, L>(nx, r, t0r + it + 1, H, DK, e, i);
+            const int s0 = __builtin_amdgcn_readlane(sq0, it + 3);
+            se[3] = __builtin_amdgcn_readlane(sq1, it + 3);
+            gh[3] = cur.gkw;
+            bh[3] = cur.bt;
+            kwin[3] = cur.kt;
+            const bool own = t < t_hi;
+            if (own) {                           // db from the b k part of the key: one
+                float dbp = cur.gkw * cur.kt;     // atomic per wavefront (64 channels)
+                for (int o = 32; o > 0; o >>= 1)
+                    dbp += __shfl_xor(dbp, o);
+                if (lane == 0)
+                    atomicAdd(db + (int64_t)t * H + e, dbp);
+            }
+            dr[3] = 0.f;
+            if constexpr (L > 1) {
+                float kx[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    kx[m] = t - 3 + m >= s0 ? kwin[m] : 0.f;
+                const float r0 = w[0] * kx[0] + w[1] * kx[1] + w[2] * kx[2] + w[3] * kx[3];
+                // residuals r_l, l = 1 .. L-1 (the closed form as a running product, or
+                // the GELU refinement chain)
+                float rr[L];
+                rr[1] = r0;
+#pragma unroll
+                for (int l = 1; l < L - 1; ++l) {
+                    const float al = cur.a[l - 1], hl = cur.h[l - 1];
+                    rr[l + 1] = gelu ? rr[l] - al * gelu_as(hl * rr[l]) : rr[l] * (1.f - al * hl);
                 }
-                se[3] = s1;
-                gh[3] = cur.gkw;
-                bh[3] = cur.bt;
-                kwin[3] = cur.kt;
-                const bool own = t < t_hi;
-                if (own) {                       // db from the b k part of the key: one
-                    float dbp = cur.gkw * cur.kt; // atomic per wavefront (64 channels)
-                    for (int o = 32; o > 0; o >>= 1)
-                        dbp += __shfl_xor(dbp, o);
-                    if (lane == 0)
-                        atomicAdd(db + (int64_t)t * H + e, dbp);
+                float dr_next = 0.f;
+                const int64_t lb = ((int64_t)t * H + e) * (L - 1) * DK + i;
+#pragma unroll
+                for (int l = L - 1; l >= 1; --l) {
+                    const float al = cur.a[l - 1], ul = cur.u[l - 1], hl = cur.h[l - 1];
+                    const float g_kw = cur.gkw;
+                    float dal = g_kw * ul * rr[l], dhl = 0.f, drl = g_kw * al * ul;
+                    if (l <= L - 2) {
+                        if (gelu) {              // r_{l+1} = r_l - a_l GELU(h_l r_l)
+                            float gp;
+                            const float gv = gelu_as_grad(hl * rr[l], gp);
+                            dal -= dr_next * gv;
+                            dhl = -dr_next * al * rr[l] * gp;
+                            drl += dr_next * (1.f - al * hl * gp);
+                        } else {                 // r_{l+1} = r_l (1 - a_l h_l)
+                            dal -= dr_next * hl * rr[l];
+                            dhl = -dr_next * al * rr[l];
+                            drl += dr_next * (1.f - al * hl);
+                        }
+                    }
+                    if (own) {
+                        const int64_t sl = lb + (int64_t)(l - 1) * DK;
+                        du[sl] = g_kw * al * rr[l];
+                        da[sl] = dal;
+                        dh[sl] = dhl;
+                    }
+                    dr_next = drl;
                 }
-                if constexpr (L > 1) {
-                    float kx[4];
+                dr[3] = dr_next;                 // dr_0 of token t
+                if (own) {                       // the taps: dw_m += dr_0 k_{t-3+m}
 #pragma unroll
                     for (int m = 0; m < 4; ++m)
-                        kx[m] = t - 3 + m >= s0 ? kwin[m] : 0.f;
-                    const float r0 = w[0] * kx[0] + w[1] * kx[1] + w[2] * kx[2] + w[3] * kx[3];
-                    // residuals r_l, l = 1 .. L-1 (the closed form as a running product, or
-                    // the GELU refinement chain)
-                    float r[L];
-                    r[1] = r0;
-#pragma unroll
-                    for (int l = 1; l < L - 1; ++l) {
-                        const float al = cur.a[l - 1], hl = cur.h[l - 1];
-                        r[l + 1] = gelu ? r[l] - al * gelu_as(hl * r[l]) : r[l] * (1.f - al * hl);
-                    }
-                    float dr_next = 0.f;
-                    const int64_t lb = (int64_t)t * H * (L - 1) * DK + (int64_t)e * (L - 1) * DK + i;
-#pragma unroll
-                    for (int l = L - 1; l >= 1; --l) {
-                        const float al = cur.a[l - 1], ul = cur.u[l - 1], hl = cur.h[l - 1];
-                        const float g_kw = cur.gkw;
-                        float dal = g_kw * ul * r[l], dhl = 0.f, drl = g_kw * al * ul;
-                        if (l <= L - 2) {
-                            if (gelu) {          // r_{l+1} = r_l - a_l GELU(h_l r_l)
-                                float gp;
-                                const float gv = gelu_as_grad(hl * r[l], gp);
-                                dal -= dr_next * gv;
-                                dhl = -dr_next * al * r[l] * gp;
-                                drl += dr_next * (1.f - al * hl * gp);
-                            } else {             // r_{l+1} = r_l (1 - a_l h_l)
-                                dal -= dr_next * hl * r[l];
-                                dhl = -dr_next * al * r[l];
-                                drl += dr_next * (1.f - al * hl);
-                            }
-                        }
-                        if (own) {
-                            const int64_t sl = lb + (int64_t)(l - 1) * DK;
-                            du[sl] = g_kw * al * r[l];
-                            da[sl] = dal;
-                            dh[sl] = dhl;
-                        }
-                        dr_next = drl;
-                    }
-                    dr[3] = dr_next;             // dr_0 of token t
-                    if (own) {                   // the taps: dw_m += dr_0 k_{t-3+m}
-#pragma unroll
-                        for (int m = 0; m < 4; ++m)
-                            dw[m] += dr_next * kx[m];
-                    }
+                        dw[m] += dr_next * kx[m];
                 }
             }
             // dk of token tau = t - 3: b dkw, and w_{3-d} dr_0 of token tau + d in its sequence
-            if (tau >= t_lo) {
+            if (it >= 3 && tau < t_hi) {
                 float acc = bh[0] * gh[0] + w[3] * dr[0];
 #pragma unroll
                 for (int dd = 1; dd < 4; ++dd)
                     if (se[dd] == se[0])
                         acc += w[3 - dd] * dr[dd];
-                dk[rt] = dk_old + acc;
+                dk[((int64_t)tau * H + e) * DK + i] = dk_old + acc;
             }
         }
     }
