@@ -460,24 +460,36 @@ def main():
                          w.L, kw=c["kw"], stream=stream)
         scan(c)
 
+    # warmup through the checked binding calls; the timed loop then calls the C ABI
+    # with the same tensors, marshalled once (raw_args)
     for i in range(args.warmup):
         launch(copies[i % len(copies)])
     torch.cuda.synchronize()
+    import ctypes
+    lib = binding.lib()
+    pargs, sargs = [], []
+    for c in copies:
+        pargs.append([ctypes.byref(dims)] + raw_args(c["k"], c["u"], c["a"], c["h"], c["b"], c["conv_w"],
+                                                      c["cu_seqlens"], w.L, c["kw"], stream.cuda_stream))
+        sargs.append([ctypes.byref(dims)] + raw_args(c["q"], c["k"], c["kw"], c["v"], c["g"], c["b"],
+                                                      c["cu_seqlens"], None, c["o"], c["S"], c["ws"],
+                                                      split_bytes, stream.cuda_stream))
 
     K = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     torch.cuda.synchronize()
+    status = 0
     t0 = time.perf_counter()
     for i in range(K):
-        c = copies[i % len(copies)]
+        j = i % len(copies)
         ev[i][0].record(stream)
-        binding.prologue(c["k"], c["u"], c["a"], c["h"], c["b"], c["conv_w"], c["cu_seqlens"],
-                         w.L, kw=c["kw"], stream=stream)
+        status |= lib.prism_prologue(*pargs[j])
         ev[i][1].record(stream)
-        scan(c)
+        status |= lib.prism_scan_ex(*sargs[j])
         ev[i][2].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    assert status == 0, binding.status_str(status)
     last = copies[(K - 1) % len(copies)]
 
     pro_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
@@ -492,9 +504,6 @@ def main():
 
     # the non-linear refinement variant of the prologue (GELU residual chain), same
     # inputs and bytes, timed on its own after the forward steps
-    import ctypes
-    lib = binding.lib()
-    dims = binding.Dims(n_seqs, T, w.heads, w.dk, w.dv, binding.PRISM_BF16 if esize == 2 else 0)
     gargs = []
     for c in copies:                       # checked calls through the binding
         binding.prologue_ex(c["k"], c["u"], c["a"], c["h"], c["b"], c["conv_w"], c["cu_seqlens"],

@@ -727,6 +727,21 @@ __global__ __launch_bounds__(kNW * 64) void bwd_c1_kernel(
         return (int64_t)(c.c0 + t0 + r) * rowlen + (int64_t)e * wdt + col;
     };
 
+    // B fragments of S0^T and dS1^T for the last products (rows of the checkpoints),
+    // two 16-row tiles ahead, the first two in flight from here
+    bf16x8_t f0[2][NKV], f1[2][NKV];
+    auto load_fin = [&](int n, int slot) {
+        const int col = d0c + n * 16 + li;
+#pragma unroll
+        for (int kp = 0; kp < NKV; ++kp) {
+            f0[slot][kp] = ldg16(ck0 + col * DV + kp * 32 + lg * 8);
+            f1[slot][kp] = ldg16(dck0 + col * DV + kp * 32 + lg * 8);
+        }
+    };
+    load_fin(0, 0);
+    if (HD > 1)
+        load_fin(1, 1);
+
     // ---- dV = diag(fac) KW dS1 + A_qkw^T dO + A_kkw^T dR
     {
         f32x4_t acc[HV];
@@ -765,21 +780,34 @@ __global__ __launch_bounds__(kNW * 64) void bwd_c1_kernel(
                     gv[gidx(r, c.rowV, DV, v0c + n * 16 + li)] = acc[n][r];
     }
 
-    // ---- dQ, dK, dKW (key column half), with the dot products of each token row
+    // ---- dQ, dK, dKW (key column half), with the dot products of each token row;
+    //      the wavefronts of token block 0 also sum S0 . dS1 over their half of the
+    //      rows from the same fragments (every element exactly once)
     float kd[4] = {0.f, 0.f, 0.f, 0.f}, qd[4] = {0.f, 0.f, 0.f, 0.f}, fd[4] = {0.f, 0.f, 0.f, 0.f};
+    float sd = 0.f;
 #pragma unroll
     for (int n = 0; n < HD; ++n) {
         const int col = d0c + n * 16 + li;
         f32x4_t zq = {0.f, 0.f, 0.f, 0.f}, z1 = zq, z2 = zq, z3 = zq;
 #pragma unroll
         for (int kp = 0; kp < NKV; ++kp) {
-            const bf16x8_t s0r = ldg16(ck0 + col * DV + kp * 32 + lg * 8);
-            const bf16x8_t s1r = ldg16(dck0 + col * DV + kp * 32 + lg * 8);
+            const bf16x8_t s0r = f0[n & 1][kp];
+            const bf16x8_t s1r = f1[n & 1][kp];
             zq = mma32(frag_row(sO + tb * 16 * LDV + kp * 32, LDV, lane), s0r, zq);   // dO S0^T
             z1 = mma32(frag_row(sR + tb * 16 * LDV + kp * 32, LDV, lane), s0r, z1);   // dR S0^T
             z2 = mma32(frag_row(sX + tb * 16 * LDV + kp * 32, LDV, lane), s1r, z2);   // X dS1^T
             z3 = mma32(frag_row(sV + tb * 16 * LDV + kp * 32, LDV, lane), s1r, z3);   // V dS1^T
+            if (tb == 0) {
+                const uint4 a4 = __builtin_bit_cast(uint4, s0r), b4 = __builtin_bit_cast(uint4, s1r);
+                const uint32_t aw[4] = {a4.x, a4.y, a4.z, a4.w}, bw[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    sd += __uint_as_float(aw[x] << 16) * __uint_as_float(bw[x] << 16) +
+                          __uint_as_float(aw[x] & 0xffff0000u) * __uint_as_float(bw[x] & 0xffff0000u);
+            }
         }
+        if (n + 2 < HD)
+            load_fin(n + 2, n & 1);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float kv = bf16_to_f32(sK[(t0 + r) * LDD + col]);
@@ -808,23 +836,13 @@ __global__ __launch_bounds__(kNW * 64) void bwd_c1_kernel(
         }
     }
 
-    // ---- <S0, dS1>
-    {
-        float acc = 0.f;
-        for (int p = tid; p < D * DV / 8; p += kNW * 64) {
-            const uint4 a = *reinterpret_cast<const uint4*>(ck0 + p * 8);
-            const uint4 bb = *reinterpret_cast<const uint4*>(dck0 + p * 8);
-            const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {bb.x, bb.y, bb.z, bb.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                acc += __uint_as_float(aw[i] << 16) * __uint_as_float(bw[i] << 16) +
-                       __uint_as_float(aw[i] & 0xffff0000u) * __uint_as_float(bw[i] & 0xffff0000u);
-        }
-        acc = sum16(acc);
-        acc += __shfl_xor(acc, 16, 64);
-        acc += __shfl_xor(acc, 32, 64);
+    // ---- <S0, dS1>: the two halves from the token-block-0 wavefronts
+    if (tb == 0) {
+        sd = sum16(sd);
+        sd += __shfl_xor(sd, 16, 64);
+        sd += __shfl_xor(sd, 32, 64);
         if (lane == 0)
-            sRed[wave] = acc;
+            sRed[nh] = sd;
     }
     lds_barrier();
     if (tid < kC && tid < c.nt) {
@@ -833,13 +851,8 @@ __global__ __launch_bounds__(kNW * 64) void bwd_c1_kernel(
         scal[(int64_t)T * H + o] = sSc[kC + tid];
         scal[2 * (int64_t)T * H + o] = sSc[2 * kC + tid];
     }
-    if (tid == 0) {
-        float s = 0.f;
-#pragma unroll
-        for (int x = 0; x < kNW; ++x)
-            s += sRed[x];
-        sdot[c.vcid] = s;
-    }
+    if (tid == 0)
+        sdot[c.vcid] = sRed[0] + sRed[1];
 }
 
 template <int D, int DV>
