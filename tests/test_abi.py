@@ -258,3 +258,37 @@ def test_scan_workspace_bytes_for_forced_split(lib, monkeypatch):
     monkeypatch.delenv("PRISM_SCAN_TWOPASS")
     monkeypatch.setenv("PRISM_SPLIT", str(P))
     assert B.scan_workspace_bytes(B.make_dims(n, T, H, 64, 64, B.PRISM_F32)) == 0
+
+
+def test_bwd_workspace_bytes_both_paths(lib, monkeypatch):
+    """prism_bwd_workspace_bytes.  bf16 (the chunkwise backward, default): write
+    keys, per-chunk matrices (20 KB per head and virtual chunk), four bf16 state
+    checkpoints (dk x dv per head and virtual chunk), X and dR (bf16 [T, H, dv]),
+    dkw (fp32 [T, H, dk]), three fp32 per-token scalars, one fp32 per head and
+    virtual chunk, and the dconv_w partials (per 64-token block and per slab of
+    16 blocks, 4 H dk floats each), every part rounded up to 256 bytes.  fp32, or
+    PRISM_BWD_CHUNKED=0: the token walk's checkpoints, segment gradients, dkw and
+    the same partials, after the write keys."""
+    up = lambda x: (x + 255) // 256 * 256
+    n, T, H, dk, dv, L = 3, 1000, 2, 128, 64, 4
+    nv = (T // 64 + n) * H
+    nb = (T + 63) // 64
+    wk = (nb + (nb + 15) // 16) * H * dk * 4
+    chunked = (up(T * H * dk * 2) + up(nv * 20480) + 4 * up(nv * dk * dv * 2) + 2 * up(T * H * dv * 2)
+               + up(T * H * dk * 4) + up(3 * T * H * 4) + up(nv * 4) + up(wk * 4))
+    walk = lambda e, s: up(T * H * dk * e) + 4 * ((T // s + n + 1) * H * dk * dv + n * 8 * H * dk * dv
+                                                  + T * H * dk + wk)
+    from gated_delta_rule_prologue_amd import binding as B
+    d16 = B.make_dims(n, T, H, dk, dv, B.PRISM_BF16)
+    d32 = B.make_dims(n, T, H, dk, dv, B.PRISM_F32)
+    lib.prism_bwd_workspace_bytes.restype = ctypes.c_size_t
+    monkeypatch.delenv("PRISM_BWD_CHUNKED", raising=False)
+    assert lib.prism_bwd_workspace_bytes(ctypes.byref(d16), L) == chunked
+    assert lib.prism_bwd_workspace_bytes(ctypes.byref(d32), L) == walk(4, 4)
+    monkeypatch.setenv("PRISM_BWD_CHUNKED", "0")
+    assert lib.prism_bwd_workspace_bytes(ctypes.byref(d16), L) == walk(2, 4)
+    monkeypatch.setenv("PRISM_BWD_CHUNKED", "1")
+    # no tokens: the token walk (the chunkwise form needs at least one chunk)
+    e16 = B.make_dims(n, 0, H, dk, dv, B.PRISM_BF16)
+    assert lib.prism_bwd_workspace_bytes(ctypes.byref(e16), L) == 256 + 4 * ((n + 1) * H * dk * dv
+                                                                           + n * 8 * H * dk * dv)
