@@ -304,6 +304,8 @@ size_t prism_scan_workspace_bytes(const prism_dims* d);
  *   dg, db      out fp32 [T, H]              dconv_w  out fp32 [H, dk, 4]
  *   dS_init     out fp32 [n_seqs, H, dk, dv] or NULL (not written)
  *   workspace   prism_bwd_workspace_bytes(d, L) bytes
+ * On the chunkwise form dg is (dL/d ln g) / g: a forget gate of exactly 0 gives a
+ * non-finite dg there (the token walk has no such limit).
  * dk, dv in {64, 128}, else PRISM_EUNSUPPORTED.  Some gradients are summed
  * with fp32 atomics (db over channel groups; on the token walk also over value
  * slices), so the last bits may differ from run to run.
