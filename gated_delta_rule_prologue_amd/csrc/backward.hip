@@ -614,8 +614,13 @@ __global__ __launch_bounds__(256) void write_key_bwd_kernel(
         // the dkw and b of those tokens (dk of token t-3 is completed at token t)
         float dr[4] = {0.f, 0.f, 0.f, 0.f}, gh[4] = {0.f, 0.f, 0.f, 0.f}, bh[4] = {0.f, 0.f, 0.f, 0.f};
         int se[4] = {-1, -1, -1, -1};
-        WkTok<T, L> nx;
+        // the next two tokens' loads in flight while a token is computed (up to
+        // L = 4: beyond, the second set of registers costs more occupancy than it hides)
+        constexpr int AHEAD = L <= 4 ? 2 : 1;
+        WkTok<T, L> nx, nx2;
         wk_load<T, L>(nx, r, t0r, H, DK, e, i);
+        if constexpr (AHEAD == 2)
+            wk_load<T, L>(nx2, r, t0r + 1, H, DK, e, i);
         // fully unrolled: straight-line code, so every wait counts exactly the
         // loads it needs (a loop would wait for all of them at its head)
 #pragma unroll
@@ -634,8 +639,13 @@ __global__ __launch_bounds__(256) void write_key_bwd_kernel(
             if (it >= 3)
                 dk_old = bld(r.dk, (tau - rb) * (int)rowK + e * DK + i, (const float*)nullptr);
             const WkTok<T, L> cur = nx;
-            if (it + 1 < NIT)
+            if constexpr (AHEAD == 2) {
+                nx = nx2;
+                if (it + 2 < NIT)
+                    wk_load<T, L>(nx2, r, t0r + it + 2, H, DK, e, i);
+            } else if (it + 1 < NIT) {
                 wk_load<T, L>(nx, r, t0r + it + 1, H, DK, e, i);
+            }
             const int s0 = __builtin_amdgcn_readlane(sq0, it + 3);
             se[3] = __builtin_amdgcn_readlane(sq1, it + 3);
             gh[3] = cur.gkw;
