@@ -85,87 +85,100 @@ struct CtxB {
     int64_t rowQK, rowV, vbase;
 };
 
-// mover m (0, 1): tokens 32 m .. 32 m + 31 of chunk ch into buffer buf; mover 0
-// also expands T and the gates, mover 1 expands -A_qk
+// mover m (0, 1): tokens 32 m .. 32 m + 31 of chunk ch (q, k rows, the dO slice),
+// and the chunk's T (mover 0, with the gates) or -A_qk (mover 1).  The loads of a
+// chunk go to registers (load) one chunk before they are stored into an LDS
+// buffer (store), so each has a whole chunk period to arrive.
 template <int D>
-__device__ __forceinline__ void stage_b(const CtxB& c, unsigned char* buf, int ch, int m)
-{
-    using Ly = LayB<D>;
-    const int lane = c.lane;
-    const int c0 = c.seq0 + ch * kC;
-    const int nt = __builtin_amdgcn_readfirstlane(max(0, min(kC, c.seq1 - c0)));
-    const auto rk = rsrc(c.k + (int64_t)c0 * c.rowQK + (int64_t)c.e * D, nt * (int)c.rowQK * 2);
-    const auto rq = rsrc(c.q + (int64_t)c0 * c.rowQK + (int64_t)c.e * D, nt * (int)c.rowQK * 2);
-    const auto ro = rsrc(c.dO + (int64_t)c0 * c.rowV + (int64_t)c.e * c.DV + c.j0, nt * (int)c.rowV * 2);
-    constexpr int PPR = D / 8, NPQ = D / 16;
-    uint4 vk[NPQ], vq[NPQ], vo[2];
+struct StageB {
+    static constexpr int PPR = D / 8, NPQ = D / 16;
+    uint4 vk[NPQ], vq[NPQ], vo[2], vm[5];
+    uint16_t gv, bv;
+    int nt;
+
+    __device__ __forceinline__ void load(const CtxB& c, int ch, int m)
+    {
+        const int lane = c.lane;
+        const int c0 = c.seq0 + ch * kC;
+        nt = __builtin_amdgcn_readfirstlane(max(0, min(kC, c.seq1 - c0)));
+        const auto rk = rsrc(c.k + (int64_t)c0 * c.rowQK + (int64_t)c.e * D, nt * (int)c.rowQK * 2);
+        const auto rq = rsrc(c.q + (int64_t)c0 * c.rowQK + (int64_t)c.e * D, nt * (int)c.rowQK * 2);
+        const auto ro = rsrc(c.dO + (int64_t)c0 * c.rowV + (int64_t)c.e * c.DV + c.j0, nt * (int)c.rowV * 2);
 #pragma unroll
-    for (int x = 0; x < NPQ; ++x) {
-        const int p = lane + 64 * x;
-        const int off = ((32 * m + p / PPR) * (int)c.rowQK + (p % PPR) * 8) * 2;
-        vk[x] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
-        vq[x] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
-    }
+        for (int x = 0; x < NPQ; ++x) {
+            const int p = lane + 64 * x;
+            const int off = ((32 * m + p / PPR) * (int)c.rowQK + (p % PPR) * 8) * 2;
+            vk[x] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+            vq[x] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+        }
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-        const int p = lane + 64 * x;
-        vo[x] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              ro, ((32 * m + p / 4) * (int)c.rowV + (p % 4) * 8) * 2, 0, 0));
-    }
-    // the chunk's stored matrix (T for mover 0, -A_qk for mover 1): ten 16x16 blocks
-    const int mat = m == 0 ? gram::kMatT : gram::kMatNAqk;
-    const auto rm = rsrc(c.mats + ((c.vbase + ch) * c.H + c.e) * (int64_t)gram::kChunkElems + mat * gram::kMatElems,
-                         gram::kMatElems * 2);
-    uint4 vm[5];
+        for (int x = 0; x < 2; ++x) {
+            const int p = lane + 64 * x;
+            vo[x] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  ro, ((32 * m + p / 4) * (int)c.rowV + (p % 4) * 8) * 2, 0, 0));
+        }
+        // the chunk's stored matrix (T for mover 0, -A_qk for mover 1): ten 16x16 blocks
+        const int mat = m == 0 ? gram::kMatT : gram::kMatNAqk;
+        const auto rm = rsrc(c.mats + ((c.vbase + ch) * c.H + c.e) * (int64_t)gram::kChunkElems +
+                                 mat * gram::kMatElems,
+                             gram::kMatElems * 2);
 #pragma unroll
-    for (int x = 0; x < 5; ++x) {
-        const int idx = lane + 64 * x, blk = idx / 32, p = idx % 32;
-        const int r = p / 2, hh = p % 2;
-        vm[x] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              rm, (blk * gram::kBlockElems + gram::swz(r, 8 * hh)) * 2, 0, 0));
+        for (int x = 0; x < 5; ++x) {
+            const int idx = lane + 64 * x, blk = idx / 32, p = idx % 32;
+            const int r = p / 2, hh = p % 2;
+            vm[x] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rm, (blk * gram::kBlockElems + gram::swz(r, 8 * hh)) * 2, 0, 0));
+        }
+        gv = 0;
+        bv = 0;
+        if (m == 0) {
+            const auto rg = rsrc(c.g + (int64_t)c0 * c.H + c.e, nt * c.H * 2);
+            const auto rb = rsrc(c.b + (int64_t)c0 * c.H + c.e, nt * c.H * 2);
+            gv = __builtin_amdgcn_raw_buffer_load_b16(rg, lane * c.H * 2, 0, 0);
+            bv = __builtin_amdgcn_raw_buffer_load_b16(rb, lane * c.H * 2, 0, 0);
+        }
     }
-    uint16_t gv = 0, bv = 0;
-    if (m == 0) {
-        const auto rg = rsrc(c.g + (int64_t)c0 * c.H + c.e, nt * c.H * 2);
-        const auto rb = rsrc(c.b + (int64_t)c0 * c.H + c.e, nt * c.H * 2);
-        gv = __builtin_amdgcn_raw_buffer_load_b16(rg, lane * c.H * 2, 0, 0);
-        bv = __builtin_amdgcn_raw_buffer_load_b16(rb, lane * c.H * 2, 0, 0);
-    }
-    uint16_t* sK = reinterpret_cast<uint16_t*>(buf + Ly::oK);
-    uint16_t* sQ = reinterpret_cast<uint16_t*>(buf + Ly::oQ);
-    uint16_t* sO = reinterpret_cast<uint16_t*>(buf + Ly::oO);
-    uint16_t* sM = reinterpret_cast<uint16_t*>(buf + (m == 0 ? Ly::oT : Ly::oN));
+
+    __device__ __forceinline__ void store(const CtxB& c, unsigned char* buf, int m) const
+    {
+        using Ly = LayB<D>;
+        const int lane = c.lane;
+        uint16_t* sK = reinterpret_cast<uint16_t*>(buf + Ly::oK);
+        uint16_t* sQ = reinterpret_cast<uint16_t*>(buf + Ly::oQ);
+        uint16_t* sO = reinterpret_cast<uint16_t*>(buf + Ly::oO);
+        uint16_t* sM = reinterpret_cast<uint16_t*>(buf + (m == 0 ? Ly::oT : Ly::oN));
 #pragma unroll
-    for (int x = 0; x < NPQ; ++x) {
-        const int p = lane + 64 * x;
-        const int off = (32 * m + p / PPR) * Ly::LDD + (p % PPR) * 8;
-        *reinterpret_cast<uint4*>(sK + off) = vk[x];
-        *reinterpret_cast<uint4*>(sQ + off) = vq[x];
-    }
+        for (int x = 0; x < NPQ; ++x) {
+            const int p = lane + 64 * x;
+            const int off = (32 * m + p / PPR) * Ly::LDD + (p % PPR) * 8;
+            *reinterpret_cast<uint4*>(sK + off) = vk[x];
+            *reinterpret_cast<uint4*>(sQ + off) = vq[x];
+        }
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-        const int p = lane + 64 * x;
-        *reinterpret_cast<uint4*>(sO + (32 * m + p / 4) * Ly::LDV + (p % 4) * 8) = vo[x];
-    }
+        for (int x = 0; x < 2; ++x) {
+            const int p = lane + 64 * x;
+            *reinterpret_cast<uint4*>(sO + (32 * m + p / 4) * Ly::LDV + (p % 4) * 8) = vo[x];
+        }
 #pragma unroll
-    for (int x = 0; x < 5; ++x) {
-        const int idx = lane + 64 * x, blk = idx / 32, p = idx % 32;
-        const int r = p / 2, hh = p % 2;
-        *reinterpret_cast<uint4*>(sM + (16 * blk_i(blk) + r) * Ly::LDC + 16 * blk_j(blk) + 8 * hh) = vm[x];
+        for (int x = 0; x < 5; ++x) {
+            const int idx = lane + 64 * x, blk = idx / 32, p = idx % 32;
+            const int r = p / 2, hh = p % 2;
+            *reinterpret_cast<uint4*>(sM + (16 * blk_i(blk) + r) * Ly::LDC + 16 * blk_j(blk) + 8 * hh) = vm[x];
+        }
+        if (m == 0) {
+            float* G = reinterpret_cast<float*>(buf + Ly::oG);
+            const float l2 = lane < nt ? __log2f(fmaxf(bf16_to_f32(gv), 1e-30f)) : 0.f;
+            const float lam = wave_inclusive_sum(l2);
+            const float lamC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam), 63));
+            const float gam = __builtin_amdgcn_exp2f(lam);
+            G[lane] = gam;
+            G[kC + lane] = bf16_to_f32(bv) * gam;
+            G[2 * kC + lane] = __builtin_amdgcn_exp2f(lamC - lam);
+            if (lane == 0)
+                G[3 * kC] = __builtin_amdgcn_exp2f(lamC);
+        }
     }
-    if (m == 0) {
-        float* G = reinterpret_cast<float*>(buf + Ly::oG);
-        const float l2 = lane < nt ? __log2f(fmaxf(bf16_to_f32(gv), 1e-30f)) : 0.f;
-        const float lam = wave_inclusive_sum(l2);
-        const float lamC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam), 63));
-        const float gam = __builtin_amdgcn_exp2f(lam);
-        G[lane] = gam;
-        G[kC + lane] = bf16_to_f32(bv) * gam;
-        G[2 * kC + lane] = __builtin_amdgcn_exp2f(lamC - lam);
-        if (lane == 0)
-            G[3 * kC] = __builtin_amdgcn_exp2f(lamC);
-    }
-}
+};
 
 // state wavefront jb: one chunk of the recurrence for value columns j0 + 16 jb ..
 template <int D>
@@ -339,13 +352,23 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(
                     dS_init[sb + (int64_t)(ib * 16 + lg * 4 + r) * DV + li] = dS[ib][r];
         }
     } else {
+        // chunk ch - 1 is stored while chunk ch - 2 loads (past the first chunk the
+        // ranges are empty and nothing is stored)
         const int m = wave - 2;
-        if (c.nchunks > 0)
-            stage_b<D>(c, smem + ((c.nchunks - 1) & 1) * Ly::szBuf, c.nchunks - 1, m);
+        StageB<D> st;
+        if (c.nchunks > 0) {
+            st.load(c, c.nchunks - 1, m);
+            st.store(c, smem + ((c.nchunks - 1) & 1) * Ly::szBuf, m);
+        }
+        if (c.nchunks > 1)
+            st.load(c, c.nchunks - 2, m);
         lds_barrier();
         for (int ch = c.nchunks - 1; ch >= 0; --ch) {
-            if (ch >= 1)
-                stage_b<D>(c, smem + ((ch - 1) & 1) * Ly::szBuf, ch - 1, m);
+            if (ch >= 1) {
+                st.store(c, smem + ((ch - 1) & 1) * Ly::szBuf, m);
+                if (ch >= 2)
+                    st.load(c, ch - 2, m);
+            }
             lds_barrier();
         }
     }
