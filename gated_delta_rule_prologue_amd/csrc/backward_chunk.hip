@@ -375,20 +375,21 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Passes C1 and C2: one workgroup per (virtual chunk, head), eight wavefronts
-// (two per SIMD); wavefront w owns the chunk's tokens 16 (w & 3) .. + 15 and
-// column half w >> 2 of every output, so every gradient element is written by
-// one workgroup (no global atomics).
-//   C1: X = T (diag(b gamma) K S0 + A_kkw V), dX, dR = T^T dX (as in pass B),
-//       dV = diag(fac) KW dS1 + A_qkw^T dO + A_kkw^T dR, and the state terms
-//       dQ = diag(gamma) dO S0^T, dK = diag(b gamma) dR S0^T - diag(fac) X dS1^T,
-//       dKW = diag(fac) V dS1^T, with the per-token dot products the decay and b
-//       gradients need; X and dR go to memory for C2.
-//   C2: the Gram matrices and their gradients dA_qkw = tril0(dO V^T),
-//       dA_qk = -tril0(dO X^T), dA_kk = -tril-1(dR X^T), dA_kkw = tril-1(dR V^T),
-//       M = dA (.) D (b by row for the kk pair), then
-//       dQ += M_qk K + M_qkw KW, dK += (M_kk + M_kk^T) K + M_kkw KW + M_qk^T Q,
-//       dKW += M_kkw^T K + M_qkw^T Q, db and dg (d/d ln gamma summed backwards).
+// The chunk-parallel gradients: one workgroup per (virtual chunk, head), eight
+// wavefronts (two per SIMD); wavefront w owns the chunk's tokens 16 (w & 3) ..
+// + 15 and column half w >> 2 of every output, so every gradient element is
+// written once, by one workgroup (no global atomics).  In order:
+//   X = T (diag(b gamma) K S0 + A_kkw V), dX, dR = T^T dX (as in pass B),
+//   dV = diag(fac) KW dS1 + A_qkw^T dO + A_kkw^T dR;
+//   the Gram matrices and their gradients dA_qkw = tril0(dO V^T),
+//   dA_qk = -tril0(dO X^T), dA_kk = -tril-1(dR X^T), dA_kkw = tril-1(dR V^T),
+//   M = dA (.) D (b by row for the kk pair), with the row and column sums the
+//   decay gradient needs;
+//   dQ = diag(gamma) dO S0^T + M_qk K + M_qkw KW,
+//   dK = diag(b gamma) dR S0^T - diag(fac) X dS1^T + (M_kk + M_kk^T) K + M_kkw KW + M_qk^T Q,
+//   dKW = diag(fac) V dS1^T + M_kkw^T K + M_qkw^T Q, with the per-token dot
+//   products the decay and b gradients need; then db and dg (d/d ln gamma
+//   summed backwards over the chunk).
 // S0 and dS1 come from the bf16 checkpoints, whose two layouts give every
 // MFMA fragment as one 16-byte read.
 // ---------------------------------------------------------------------------
@@ -510,31 +511,39 @@ __device__ __forceinline__ void st_rows(uint16_t* dst, int ld, int t0, const f32
         dst[(t0 + r) * ld + col] = (uint16_t)(pack_bf16x2(x[r], 0.f) & 0xffffu);
 }
 
+// block pairs (t-block, s-block), s <= t, in order (0,0) (1,0) (1,1) (2,0) ..
+__device__ __forceinline__ constexpr int pair_t(int p) { return p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3; }
+__device__ __forceinline__ constexpr int pair_s(int p) { return p - pair_t(p) * (pair_t(p) + 1) / 2; }
+
 template <int D, int DV>
-struct LayC1 {
+struct LayG {
     static constexpr int LDD = D + 8, LDV = DV + 8, LDC = kC + 8;
     static constexpr int szD = kC * LDD * 2, szV = kC * LDV * 2, szM = kC * LDC * 2;
     static constexpr int oK = 0, oKW = szD, oQ = 2 * szD, oV = 3 * szD, oO = oV + szV;
     static constexpr int oT = oO + szV, oAkw = oT + szM, oNqk = oAkw + szM, oAqw = oNqk + szM;
     static constexpr int oR = oAqw + szM, oX = oR + szV, oG = oX + szV;
-    static constexpr int oSc = oG + kGateBytes;  // per-token dot products (3 x 64)
-    static constexpr int oRed = oSc + 3 * kC * 4;
+    static constexpr int oSc = oG + kGateBytes;  // per-token dot products (3 x 64), then the
+    static constexpr int oL = oSc + 3 * kC * 4;  // decay gradient l and db's Gram part (64 each)
+    static constexpr int oRed = oL + 2 * kC * 4;
     static constexpr int total = oRed + kNW * 4;
     static_assert(total <= 160 * 1024, "LDS budget");
 };
 
-// C1.  Wavefront w: token rows 16 (w & 3) .., value (or key) column half w >> 2.
+// The chunk-parallel gradients of one (chunk, head).  Wavefront w: token rows
+// 16 (w & 3) .., value (or key) column half w >> 2; in the block-pair stage,
+// pairs w and w + 8.  The stored T, A_kkw, -A_qk and A_qkw tiles are dead after
+// dV, and their LDS holds M_qk, M_qkw, M_kk and M_kkw from there on.
 template <int D, int DV>
-__global__ __launch_bounds__(kNW * 64) void bwd_c1_kernel(
+__global__ __launch_bounds__(kNW * 64) void bwd_grads_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ kw,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO, const uint16_t* __restrict__ g,
     const uint16_t* __restrict__ b, const int32_t* __restrict__ cu, int n_seqs, int H,
     const uint16_t* __restrict__ mats, const uint16_t* __restrict__ ck, const uint16_t* __restrict__ ckT,
-    const uint16_t* __restrict__ dck, const uint16_t* __restrict__ dckT, uint16_t* __restrict__ xg,
-    uint16_t* __restrict__ drg, float* __restrict__ gq, float* __restrict__ gk, float* __restrict__ gkw,
-    float* __restrict__ gv, float* __restrict__ scal, float* __restrict__ sdot, int T)
+    const uint16_t* __restrict__ dck, const uint16_t* __restrict__ dckT, float* __restrict__ gq,
+    float* __restrict__ gk, float* __restrict__ gkw, float* __restrict__ gv, float* __restrict__ gg,
+    float* __restrict__ gb)
 {
-    using Ly = LayC1<D, DV>;
+    using Ly = LayG<D, DV>;
     constexpr int LDD = Ly::LDD, LDV = Ly::LDV, LDC = Ly::LDC;
     constexpr int NKD = D / 32, NKV = DV / 32;
     constexpr int HV = DV / 32, HD = D / 32;     // 16-column tiles of a column half
@@ -565,6 +574,8 @@ __global__ __launch_bounds__(kNW * 64) void bwd_c1_kernel(
     uint16_t* sX = reinterpret_cast<uint16_t*>(smem + Ly::oX);
     float* G = reinterpret_cast<float*>(smem + Ly::oG);
     float* sSc = reinterpret_cast<float*>(smem + Ly::oSc);
+    float* sL = reinterpret_cast<float*>(smem + Ly::oL);   // d/d ln gamma per token
+    float* sDB = sL + kC;                                  // db (Gram part) per token
     float* sRed = reinterpret_cast<float*>(smem + Ly::oRed);
     const int t0 = tb * 16 + lg * 4;             // this lane's first token row of a tile
     const uint16_t* ckT0 = ckT + c.vcid * (int64_t)DV * D;
@@ -607,8 +618,8 @@ __global__ __launch_bounds__(kNW * 64) void bwd_c1_kernel(
         makw.template store<LDC>(sAkw, tid);
         mnqk.template store<LDC>(sNqk, tid);
         maqw.template store<LDC>(sAqw, tid);
-        if (tid < 3 * kC)
-            sSc[tid] = 0.f;
+        if (tid < 5 * kC)
+            sSc[tid] = 0.f;                      // sSc, sL and sDB
     }
     lds_barrier();
     const float* sBG = G + kC;
@@ -727,19 +738,6 @@ __global__ __launch_bounds__(kNW * 64) void bwd_c1_kernel(
     }
     lds_barrier();
 
-    // ---- X and dR rows to memory for C2 (this wavefront's rows and column half)
-    {
-        constexpr int PPH = DV / 16;             // 16-byte vectors of half a row
-#pragma unroll
-        for (int p = lane; p < 16 * PPH; p += 64) {
-            const int t = tb * 16 + p / PPH, cc = v0c + (p % PPH) * 8;
-            if (t < c.nt) {
-                const int64_t o = (int64_t)(c.c0 + t) * c.rowV + (int64_t)e * DV + cc;
-                *reinterpret_cast<uint4*>(xg + o) = *reinterpret_cast<const uint4*>(sX + t * LDV + cc);
-                *reinterpret_cast<uint4*>(drg + o) = *reinterpret_cast<const uint4*>(sR + t * LDV + cc);
-            }
-        }
-    }
     const float4 gam4 = *reinterpret_cast<const float4*>(G + t0);
     const float4 bg4 = *reinterpret_cast<const float4*>(sBG + t0);
     const float4 fac4 = *reinterpret_cast<const float4*>(sFac + t0);
@@ -803,170 +801,21 @@ __global__ __launch_bounds__(kNW * 64) void bwd_c1_kernel(
                     gv[gidx(r, c.rowV, DV, v0c + n * 16 + li)] = acc[n][r];
     }
 
-    // ---- dQ, dK, dKW (key column half), with the dot products of each token row;
-    //      the wavefronts of token block 0 also sum S0 . dS1 over their half of the
-    //      rows from the same fragments (every element exactly once)
-    float kd[4] = {0.f, 0.f, 0.f, 0.f}, qd[4] = {0.f, 0.f, 0.f, 0.f}, fd[4] = {0.f, 0.f, 0.f, 0.f};
-    float sd = 0.f;
-#pragma unroll
-    for (int n = 0; n < HD; ++n) {
-        const int col = d0c + n * 16 + li;
-        f32x4_t zq = {0.f, 0.f, 0.f, 0.f}, z1 = zq, z2 = zq, z3 = zq;
-#pragma unroll
-        for (int kp = 0; kp < NKV; ++kp) {
-            const bf16x8_t s0r = f0[n & 1][kp];
-            const bf16x8_t s1r = f1[n & 1][kp];
-            zq = mma32(frag_row(sO + tb * 16 * LDV + kp * 32, LDV, lane), s0r, zq);   // dO S0^T
-            z1 = mma32(frag_row(sR + tb * 16 * LDV + kp * 32, LDV, lane), s0r, z1);   // dR S0^T
-            z2 = mma32(frag_row(sX + tb * 16 * LDV + kp * 32, LDV, lane), s1r, z2);   // X dS1^T
-            z3 = mma32(frag_row(sV + tb * 16 * LDV + kp * 32, LDV, lane), s1r, z3);   // V dS1^T
-            if (tb == 0) {
-                const uint4 a4 = __builtin_bit_cast(uint4, s0r), b4 = __builtin_bit_cast(uint4, s1r);
-                const uint32_t aw[4] = {a4.x, a4.y, a4.z, a4.w}, bw[4] = {b4.x, b4.y, b4.z, b4.w};
-#pragma unroll
-                for (int x = 0; x < 4; ++x)
-                    sd += __uint_as_float(aw[x] << 16) * __uint_as_float(bw[x] << 16) +
-                          __uint_as_float(aw[x] & 0xffff0000u) * __uint_as_float(bw[x] & 0xffff0000u);
-            }
-        }
-        if (n + 2 < HD)
-            load_fin(n + 2, n & 1);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float kv = bf16_to_f32(sK[(t0 + r) * LDD + col]);
-            const float qv = bf16_to_f32(sQ[(t0 + r) * LDD + col]);
-            const float wv = bf16_to_f32(sKW[(t0 + r) * LDD + col]);
-            kd[r] += kv * z1[r];
-            qd[r] += qv * zq[r];
-            fd[r] += wv * z3[r] - kv * z2[r];
-            if (row_ok(r)) {
-                const int64_t o = gidx(r, c.rowQK, D, col);
-                gq[o] = gam[r] * zq[r];
-                gk[o] = bgm[r] * z1[r] - fac[r] * z2[r];
-                gkw[o] = fac[r] * z3[r];
-            }
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        kd[r] = sum16(kd[r]);
-        qd[r] = sum16(qd[r]);
-        fd[r] = sum16(fd[r]);
-        if (li == 0) {                           // the two column halves meet in LDS
-            atomicAdd(sSc + t0 + r, kd[r]);
-            atomicAdd(sSc + kC + t0 + r, qd[r]);
-            atomicAdd(sSc + 2 * kC + t0 + r, fd[r]);
-        }
-    }
-
-    // ---- <S0, dS1>: the two halves from the token-block-0 wavefronts
-    if (tb == 0) {
-        sd = sum16(sd);
-        sd += __shfl_xor(sd, 16, 64);
-        sd += __shfl_xor(sd, 32, 64);
-        if (lane == 0)
-            sRed[nh] = sd;
-    }
+    // the four matrices are dead from here: their LDS holds M
     lds_barrier();
-    if (tid < kC && tid < c.nt) {
-        const int64_t o = (int64_t)(c.c0 + tid) * H + e;
-        scal[o] = sSc[tid];
-        scal[(int64_t)T * H + o] = sSc[kC + tid];
-        scal[2 * (int64_t)T * H + o] = sSc[2 * kC + tid];
-    }
-    if (tid == 0)
-        sdot[c.vcid] = sRed[0] + sRed[1];
-}
-
-template <int D, int DV>
-struct LayC2 {
-    static constexpr int LDD = D + 8, LDV = DV + 8, LDC = kC + 8;
-    static constexpr int szD = kC * LDD * 2, szV = kC * LDV * 2, szM = kC * LDC * 2;
-    static constexpr int oK = 0, oKW = szD, oQ = 2 * szD, oV = 3 * szD, oO = oV + szV, oX = oO + szV;
-    static constexpr int oR = oX + szV, oMqk = oR + szV, oMqw = oMqk + szM, oMkk = oMqw + szM, oMkw = oMkk + szM;
-    static constexpr int oG = oMkw + szM;        // gates, then l (64), db (64)
-    static constexpr int total = oG + kGateBytes + 2 * kC * 4;
-    static_assert(total <= 160 * 1024, "LDS budget");
-};
-
-// block pairs (t-block, s-block), s <= t, in order (0,0) (1,0) (1,1) (2,0) ..
-__device__ __forceinline__ constexpr int pair_t(int p) { return p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3; }
-__device__ __forceinline__ constexpr int pair_s(int p) { return p - pair_t(p) * (pair_t(p) + 1) / 2; }
-
-// C2.  Pair stage: wavefront w takes pairs w and w + 8; product stage: token
-// rows 16 (w & 3) .., key column half w >> 2.
-template <int D, int DV>
-__global__ __launch_bounds__(kNW * 64) void bwd_c2_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ kw,
-    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO, const uint16_t* __restrict__ g,
-    const uint16_t* __restrict__ b, const int32_t* __restrict__ cu, int n_seqs, int H,
-    const uint16_t* __restrict__ xg, const uint16_t* __restrict__ drg, const float* __restrict__ scal,
-    const float* __restrict__ sdot, float* __restrict__ gq, float* __restrict__ gk, float* __restrict__ gkw,
-    float* __restrict__ gg, float* __restrict__ gb, int T)
-{
-    using Ly = LayC2<D, DV>;
-    constexpr int LDD = Ly::LDD, LDV = Ly::LDV, LDC = Ly::LDC;
-    constexpr int NKD = D / 32, NKV = DV / 32, HD = D / 32;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[Ly::total];
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int vch = blockIdx.x / H, e = blockIdx.x % H;
-    CtxC c;
-    if (!locate(cu, n_seqs, vch, c.c0, c.nt))
-        return;
-    c.g = g; c.b = b; c.H = H; c.e = e; c.lane = tid & 63;
-    c.rowQK = (int64_t)H * D;
-    c.rowV = (int64_t)H * DV;
-    c.vcid = (int64_t)vch * H + e;
-    const int lane = c.lane, li = lane & 15, lg = lane >> 4;
-    uint16_t* sK = reinterpret_cast<uint16_t*>(smem + Ly::oK);
-    uint16_t* sKW = reinterpret_cast<uint16_t*>(smem + Ly::oKW);
-    uint16_t* sQ = reinterpret_cast<uint16_t*>(smem + Ly::oQ);
-    uint16_t* sV = reinterpret_cast<uint16_t*>(smem + Ly::oV);
-    uint16_t* sO = reinterpret_cast<uint16_t*>(smem + Ly::oO);
-    uint16_t* sX = reinterpret_cast<uint16_t*>(smem + Ly::oX);
-    uint16_t* sR = reinterpret_cast<uint16_t*>(smem + Ly::oR);
-    uint16_t* sMqk = reinterpret_cast<uint16_t*>(smem + Ly::oMqk);
-    uint16_t* sMqw = reinterpret_cast<uint16_t*>(smem + Ly::oMqw);
-    uint16_t* sMkk = reinterpret_cast<uint16_t*>(smem + Ly::oMkk);
-    uint16_t* sMkw = reinterpret_cast<uint16_t*>(smem + Ly::oMkw);
-    float* G = reinterpret_cast<float*>(smem + Ly::oG);
-    float* sL = reinterpret_cast<float*>(smem + Ly::oG + kGateBytes);   // d/d ln gamma per token
-    float* sDB = sL + kC;                        // db (Gram part) per token
-
-    {
-        const int64_t r0 = (int64_t)c.c0 * c.rowQK + (int64_t)e * D, v0 = (int64_t)c.c0 * c.rowV + (int64_t)e * DV;
-        StageRows<D> xk, xkw, xq;
-        StageRows<DV> xv, xo, xx, xr;
-        xk.load(k + r0, c.rowQK, c.nt, tid);
-        xkw.load(kw + r0, c.rowQK, c.nt, tid);
-        xq.load(q + r0, c.rowQK, c.nt, tid);
-        xv.load(v + v0, c.rowV, c.nt, tid);
-        xo.load(dO + v0, c.rowV, c.nt, tid);
-        xx.load(xg + v0, c.rowV, c.nt, tid);
-        xr.load(drg + v0, c.rowV, c.nt, tid);
-        if (wave == 0)
-            gates_c(G, c);
-        // the M matrices' blocks above the diagonal stay zero
-        for (int idx = tid; idx < 4 * 16 * 32; idx += kNW * 64) {
-            const int mtx = idx / 512, bi = (idx / 128) % 4, bj = (idx / 32) % 4, p = idx % 32;
-            if (bj > bi) {
-                uint16_t* M = mtx == 0 ? sMqk : mtx == 1 ? sMqw : mtx == 2 ? sMkk : sMkw;
-                *reinterpret_cast<uint4*>(M + (16 * bi + p / 2) * LDC + 16 * bj + 8 * (p % 2)) =
-                    make_uint4(0u, 0u, 0u, 0u);
-            }
+    uint16_t* sMqk = sT;
+    uint16_t* sMqw = sAkw;
+    uint16_t* sMkk = sNqk;
+    uint16_t* sMkw = sAqw;
+    // the M matrices' blocks above the diagonal stay zero
+    for (int idx = tid; idx < 4 * 16 * 32; idx += kNW * 64) {
+        const int mtx = idx / 512, bi = (idx / 128) % 4, bj = (idx / 32) % 4, p = idx % 32;
+        if (bj > bi) {
+            uint16_t* M = mtx == 0 ? sMqk : mtx == 1 ? sMqw : mtx == 2 ? sMkk : sMkw;
+            *reinterpret_cast<uint4*>(M + (16 * bi + p / 2) * LDC + 16 * bj + 8 * (p % 2)) =
+                make_uint4(0u, 0u, 0u, 0u);
         }
-        if (tid < 2 * kC)
-            sL[tid] = 0.f;                       // sL and sDB
-        xk.template store<LDD>(sK, tid);
-        xkw.template store<LDD>(sKW, tid);
-        xq.template store<LDD>(sQ, tid);
-        xv.template store<LDV>(sV, tid);
-        xo.template store<LDV>(sO, tid);
-        xx.template store<LDV>(sX, tid);
-        xr.template store<LDV>(sR, tid);
     }
-    lds_barrier();
     const float* sLam = G + 3 * kC;
     const float* sB = G + 5 * kC;
 
@@ -1035,76 +884,121 @@ __global__ __launch_bounds__(kNW * 64) void bwd_c2_kernel(
     }
     lds_barrier();
 
-    // ---- dQ += M_qk K + M_qkw KW;  dK += (M_kk + M_kk^T) K + M_kkw KW + M_qk^T Q;
-    //      dKW += M_kkw^T K + M_qkw^T Q   (token rows 16 tb .., key column half nh)
-    {
-        const int tb = wave & 3, nh = wave >> 2;
-        const int t0 = tb * 16 + lg * 4;
-        const int d0c = nh * (D / 2);
-        // the values C1 stored, read before the products
-        float oq[HD][4], ok[HD][4], ow[HD][4];
+    // ---- dQ, dK, dKW (key column half), with the dot products of each token row;
+    //      the wavefronts of token block 0 also sum S0 . dS1 over their half of the
+    //      rows from the same fragments (every element exactly once)
+    float kd[4] = {0.f, 0.f, 0.f, 0.f}, qd[4] = {0.f, 0.f, 0.f, 0.f}, fd[4] = {0.f, 0.f, 0.f, 0.f};
+    float sd = 0.f;
 #pragma unroll
-        for (int n = 0; n < HD; ++n)
+    for (int n = 0; n < HD; ++n) {
+        const int col = d0c + n * 16 + li;
+        f32x4_t zq = {0.f, 0.f, 0.f, 0.f}, z1 = zq, z2 = zq, z3 = zq;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const bool in = t0 + r < c.nt;
-                const int64_t o = (int64_t)(c.c0 + (in ? t0 + r : 0)) * c.rowQK + (int64_t)e * D + d0c + n * 16 + li;
-                oq[n][r] = in ? gq[o] : 0.f;
-                ok[n][r] = in ? gk[o] : 0.f;
-                ow[n][r] = in ? gkw[o] : 0.f;
+        for (int kp = 0; kp < NKV; ++kp) {
+            const bf16x8_t s0r = f0[n & 1][kp];
+            const bf16x8_t s1r = f1[n & 1][kp];
+            zq = mma32(frag_row(sO + tb * 16 * LDV + kp * 32, LDV, lane), s0r, zq);   // dO S0^T
+            z1 = mma32(frag_row(sR + tb * 16 * LDV + kp * 32, LDV, lane), s0r, z1);   // dR S0^T
+            z2 = mma32(frag_row(sX + tb * 16 * LDV + kp * 32, LDV, lane), s1r, z2);   // X dS1^T
+            z3 = mma32(frag_row(sV + tb * 16 * LDV + kp * 32, LDV, lane), s1r, z3);   // V dS1^T
+            if (tb == 0) {
+                const uint4 a4 = __builtin_bit_cast(uint4, s0r), b4 = __builtin_bit_cast(uint4, s1r);
+                const uint32_t ua[4] = {a4.x, a4.y, a4.z, a4.w}, ub[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    sd += __uint_as_float(ua[x] << 16) * __uint_as_float(ub[x] << 16) +
+                          __uint_as_float(ua[x] & 0xffff0000u) * __uint_as_float(ub[x] & 0xffff0000u);
             }
+        }
+        if (n + 2 < HD)
+            load_fin(n + 2, n & 1);
 #pragma unroll
-        for (int n = 0; n < HD; ++n) {
-            const int nc = d0c + n * 16;
-            f32x4_t aq = {0.f, 0.f, 0.f, 0.f}, ak = aq, aw = aq;
+        for (int r = 0; r < 4; ++r) {
+            const float kv = bf16_to_f32(sK[(t0 + r) * LDD + col]);
+            const float qv = bf16_to_f32(sQ[(t0 + r) * LDD + col]);
+            const float wv = bf16_to_f32(sKW[(t0 + r) * LDD + col]);
+            kd[r] += kv * z1[r];
+            qd[r] += qv * zq[r];
+            fd[r] += wv * z3[r] - kv * z2[r];
+        }
+        // dQ = diag(gamma) dO S0^T + M_qk K + M_qkw KW,
+        // dK = diag(b gamma) dR S0^T - diag(fac) X dS1^T + (M_kk + M_kk^T) K + M_kkw KW + M_qk^T Q,
+        // dKW = diag(fac) V dS1^T + M_kkw^T K + M_qkw^T Q
+        f32x4_t aq, ak, aw;
 #pragma unroll
-            for (int h2 = 0; h2 <= 1; ++h2) {
-                const bf16x8_t bK = frag_col(sK + h2 * 32 * LDD + nc, LDD, lane);
-                const bf16x8_t bW = frag_col(sKW + h2 * 32 * LDD + nc, LDD, lane);
-                const bf16x8_t bQ = frag_col(sQ + h2 * 32 * LDD + nc, LDD, lane);
-                if (h2 <= tb / 2) {                // s <= t: rows of M
-                    aq = mma32(frag_row(sMqk + tb * 16 * LDC + h2 * 32, LDC, lane), bK, aq);
-                    aq = mma32(frag_row(sMqw + tb * 16 * LDC + h2 * 32, LDC, lane), bW, aq);
-                    ak = mma32(frag_row(sMkk + tb * 16 * LDC + h2 * 32, LDC, lane), bK, ak);
-                    ak = mma32(frag_row(sMkw + tb * 16 * LDC + h2 * 32, LDC, lane), bW, ak);
-                }
-                if (h2 >= tb / 2) {                // s >= t: columns of M (transposes)
-                    ak = mma32(frag_col(sMkk + h2 * 32 * LDC + tb * 16, LDC, lane), bK, ak);
-                    ak = mma32(frag_col(sMqk + h2 * 32 * LDC + tb * 16, LDC, lane), bQ, ak);
-                    aw = mma32(frag_col(sMkw + h2 * 32 * LDC + tb * 16, LDC, lane), bK, aw);
-                    aw = mma32(frag_col(sMqw + h2 * 32 * LDC + tb * 16, LDC, lane), bQ, aw);
-                }
+        for (int r = 0; r < 4; ++r) {
+            aq[r] = gam[r] * zq[r];
+            ak[r] = bgm[r] * z1[r] - fac[r] * z2[r];
+            aw[r] = fac[r] * z3[r];
+        }
+        const int nc = d0c + n * 16;
+#pragma unroll
+        for (int h2 = 0; h2 <= 1; ++h2) {
+            const bf16x8_t bK = frag_col(sK + h2 * 32 * LDD + nc, LDD, lane);
+            const bf16x8_t bW = frag_col(sKW + h2 * 32 * LDD + nc, LDD, lane);
+            const bf16x8_t bQ = frag_col(sQ + h2 * 32 * LDD + nc, LDD, lane);
+            if (h2 <= tb / 2) {                // s <= t: rows of M
+                aq = mma32(frag_row(sMqk + tb * 16 * LDC + h2 * 32, LDC, lane), bK, aq);
+                aq = mma32(frag_row(sMqw + tb * 16 * LDC + h2 * 32, LDC, lane), bW, aq);
+                ak = mma32(frag_row(sMkk + tb * 16 * LDC + h2 * 32, LDC, lane), bK, ak);
+                ak = mma32(frag_row(sMkw + tb * 16 * LDC + h2 * 32, LDC, lane), bW, ak);
             }
+            if (h2 >= tb / 2) {                // s >= t: columns of M (transposes)
+                ak = mma32(frag_col(sMkk + h2 * 32 * LDC + tb * 16, LDC, lane), bK, ak);
+                ak = mma32(frag_col(sMqk + h2 * 32 * LDC + tb * 16, LDC, lane), bQ, ak);
+                aw = mma32(frag_col(sMkw + h2 * 32 * LDC + tb * 16, LDC, lane), bK, aw);
+                aw = mma32(frag_col(sMqw + h2 * 32 * LDC + tb * 16, LDC, lane), bQ, aw);
+            }
+        }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if (t0 + r < c.nt) {
-                    const int64_t o = (int64_t)(c.c0 + t0 + r) * c.rowQK + (int64_t)e * D + nc + li;
-                    gq[o] = oq[n][r] + aq[r];
-                    gk[o] = ok[n][r] + ak[r];
-                    gkw[o] = ow[n][r] + aw[r];
-                }
+        for (int r = 0; r < 4; ++r) {
+            if (row_ok(r)) {
+                const int64_t o = gidx(r, c.rowQK, D, col);
+                gq[o] = aq[r];
+                gk[o] = ak[r];
+                gkw[o] = aw[r];
             }
         }
     }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        kd[r] = sum16(kd[r]);
+        qd[r] = sum16(qd[r]);
+        fd[r] = sum16(fd[r]);
+        if (li == 0) {                           // the two column halves meet in LDS
+            atomicAdd(sSc + t0 + r, kd[r]);
+            atomicAdd(sSc + kC + t0 + r, qd[r]);
+            atomicAdd(sSc + 2 * kC + t0 + r, fd[r]);
+        }
+    }
+
+    // ---- <S0, dS1>: the two halves from the token-block-0 wavefronts
+    if (tb == 0) {
+        sd = sum16(sd);
+        sd += __shfl_xor(sd, 16, 64);
+        sd += __shfl_xor(sd, 32, 64);
+        if (lane == 0)
+            sRed[nh] = sd;
+    }
+    lds_barrier();
 
     // ---- db and dg (wavefront 0, lane = token)
     if (wave == 0) {
         const int t = lane;
         const bool ok = t < c.nt;
         const int64_t o = (int64_t)(c.c0 + t) * H + e;
-        const float kS = ok ? scal[o] : 0.f, qS = ok ? scal[(int64_t)T * H + o] : 0.f;
-        const float fd = ok ? scal[2 * (int64_t)T * H + o] : 0.f;
-        const float gam = G[t], bgm = G[kC + t], fac = G[2 * kC + t], gt = G[4 * kC + t];
+        const float kS = sSc[t], qS = sSc[kC + t], fdv = sSc[2 * kC + t];
+        const float gmt = G[t], bgt = G[kC + t], fct = G[2 * kC + t], gt = G[4 * kC + t];
         if (ok)
-            gb[o] = sDB[t] + gam * kS;
-        const float ffd = fac * fd;
-        float l = sL[t] + bgm * kS + gam * qS - ffd;
+            gb[o] = sDB[t] + gmt * kS;
+        const float ffd = fct * fdv;
+        float l = sL[t] + bgt * kS + gmt * qS - ffd;
         // the chunk's last token: gamma_C carries sum fac dfac and <S0, dS1>
         float tot = ffd;
         for (int x = 1; x < 64; x <<= 1)
             tot += __shfl_xor(tot, x, 64);
         if (t == 63)
-            l += tot + G[6 * kC] * sdot[c.vcid];
+            l += tot + G[6 * kC] * (sRed[0] + sRed[1]);
         // d ln g_t = sum of l over t' >= t: a prefix sum over reversed lanes
         const float rev = __shfl(l, 63 - t, 64);
         const float cs = wave_inclusive_sum(rev);
@@ -1119,27 +1013,17 @@ __global__ __launch_bounds__(kNW * 64) void bwd_c2_kernel(
 using bwdc::kC;
 
 template <int D, int DV>
-static hipError_t launch_c_T(const ScanArgs& p, const BwdChunkBufs& w, hipStream_t stream)
+static hipError_t launch_g_T(const ScanArgs& p, const BwdChunkBufs& w, hipStream_t stream)
 {
     const int64_t blocks = (int64_t)(p.total_tokens / kC + p.n_seqs) * p.heads;
     if (blocks == 0)
         return hipSuccess;
-    hipLaunchKernelGGL((bwdc::bwd_c1_kernel<D, DV>), dim3((unsigned)blocks), dim3(bwdc::kNW * 64), 0, stream,
+    hipLaunchKernelGGL((bwdc::bwd_grads_kernel<D, DV>), dim3((unsigned)blocks), dim3(bwdc::kNW * 64), 0, stream,
                        (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.kw,
                        (const uint16_t*)p.v, (const uint16_t*)w.dO, (const uint16_t*)p.g,
                        (const uint16_t*)p.b, p.cu_seqlens, p.n_seqs, p.heads, (const uint16_t*)w.mats,
                        (const uint16_t*)w.ck, (const uint16_t*)w.ckT, (const uint16_t*)w.dck,
-                       (const uint16_t*)w.dckT, (uint16_t*)w.xg, (uint16_t*)w.drg, w.gq, w.gk, w.gkw,
-                       w.gv, w.scal, w.sdot, p.total_tokens);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess)
-        return err;
-    hipLaunchKernelGGL((bwdc::bwd_c2_kernel<D, DV>), dim3((unsigned)blocks), dim3(bwdc::kNW * 64), 0, stream,
-                       (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.kw,
-                       (const uint16_t*)p.v, (const uint16_t*)w.dO, (const uint16_t*)p.g,
-                       (const uint16_t*)p.b, p.cu_seqlens, p.n_seqs, p.heads, (const uint16_t*)w.xg,
-                       (const uint16_t*)w.drg, w.scal, w.sdot, w.gq, w.gk, w.gkw, w.gg, w.gb,
-                       p.total_tokens);
+                       (const uint16_t*)w.dckT, w.gq, w.gk, w.gkw, w.gv, w.gg, w.gb);
     return hipGetLastError();
 }
 
@@ -1148,10 +1032,10 @@ hipError_t launch_bwd_grads(const ScanArgs& p, const BwdChunkBufs& w, hipStream_
     if (!p.bf16)
         return hipErrorInvalidValue;
     if (p.dk == 64)
-        return p.dv == 64 ? launch_c_T<64, 64>(p, w, stream) : p.dv == 128 ? launch_c_T<64, 128>(p, w, stream)
+        return p.dv == 64 ? launch_g_T<64, 64>(p, w, stream) : p.dv == 128 ? launch_g_T<64, 128>(p, w, stream)
                                                                            : hipErrorInvalidValue;
     if (p.dk == 128)
-        return p.dv == 64 ? launch_c_T<128, 64>(p, w, stream) : p.dv == 128 ? launch_c_T<128, 128>(p, w, stream)
+        return p.dv == 64 ? launch_g_T<128, 64>(p, w, stream) : p.dv == 128 ? launch_g_T<128, 128>(p, w, stream)
                                                                             : hipErrorInvalidValue;
     return hipErrorInvalidValue;
 }

@@ -86,14 +86,11 @@ hipError_t launch_bwd_state(const ScanArgs& p, const void* dO, const void* mats,
                             void* dck, void* dckT, float* dS_init, hipStream_t stream);
 struct BwdChunkBufs {
     const void *dO, *mats, *ck, *ckT, *dck, *dckT;
-    void *xg, *drg;                 // X and dR, bf16 [T][H][dv]
     float *gq, *gk, *gkw, *gv, *gg, *gb;
-    float *scal;                    // fp32 [3][T][H]
-    float *sdot;                    // fp32 [virtual chunk][H]
 };
-// Passes C1, C2: every gradient of the scan's inputs (q, k, kw, v, g, b) from
-// the checkpoints; p.kw holds the write keys.  Stores (no accumulation): dq,
-// dk, dkw, dv, dg, db are written whole.
+// The chunk-parallel gradients: every gradient of the scan's inputs (q, k, kw,
+// v, g, b) from the checkpoints, in one launch; p.kw holds the write keys.
+// Stores (no accumulation): dq, dk, dkw, dv, dg, db are written whole.
 hipError_t launch_bwd_grads(const ScanArgs& p, const BwdChunkBufs& w, hipStream_t stream);
 // The write-key part of the backward pass alone (backward.hip): from dkw (fp32
 // [T][H][dk]) it writes du, da, dh, adds the write-key terms to dk and db (both

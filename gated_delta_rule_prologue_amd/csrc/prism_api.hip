@@ -452,7 +452,7 @@ bool use_bwd_chunked(const prism_dims* d)
 
 // Workspace of the chunkwise backward after kw, each part 256-byte aligned.
 struct BwdChunkLayout {
-    size_t mats, ck, ckT, dck, dckT, xg, drg, dkw, scal, sdot, wk, total;
+    size_t mats, ck, ckT, dck, dckT, dkw, wk, total;
 };
 
 BwdChunkLayout bwd_chunk_layout(const prism_dims* d)
@@ -460,18 +460,13 @@ BwdChunkLayout bwd_chunk_layout(const prism_dims* d)
     BwdChunkLayout w;
     const size_t nv = (size_t)(d->total_tokens / 64 + d->n_seqs) * d->heads;    // (virtual chunk, head)
     const size_t st = round256(nv * d->dk * d->dv * 2);
-    const size_t tv = round256((size_t)d->total_tokens * d->heads * d->dv * 2);
     size_t o = kw_bytes(d);
     w.mats = o; o += round256(prism::gram_workspace_bytes(d->n_seqs, d->total_tokens, d->heads));
     w.ck = o; o += st;
     w.ckT = o; o += st;
     w.dck = o; o += st;
     w.dckT = o; o += st;
-    w.xg = o; o += tv;
-    w.drg = o; o += tv;
     w.dkw = o; o += round256((size_t)d->total_tokens * d->heads * d->dk * 4);
-    w.scal = o; o += round256((size_t)3 * d->total_tokens * d->heads * 4);
-    w.sdot = o; o += round256(nv * 4);
     w.wk = o; o += round256(prism::wk_workspace_floats(d->total_tokens, d->heads, d->dk) * 4);
     w.total = o;
     return w;
@@ -556,11 +551,8 @@ prism_status prism_bwd_ex(const prism_dims* d, const void* q, const void* k, con
     cb.dO = dO;
     cb.mats = ws + w.mats;
     cb.ck = ws + w.ck; cb.ckT = ws + w.ckT; cb.dck = ws + w.dck; cb.dckT = ws + w.dckT;
-    cb.xg = ws + w.xg; cb.drg = ws + w.drg;
     cb.gq = dq; cb.gk = dk; cb.gkw = reinterpret_cast<float*>(ws + w.dkw); cb.gv = dv;
     cb.gg = dg; cb.gb = db;
-    cb.scal = reinterpret_cast<float*>(ws + w.scal);
-    cb.sdot = reinterpret_cast<float*>(ws + w.sdot);
     const hipStream_t s = (hipStream_t)stream;
     hipError_t e = prism::launch_gram(sp, ws + w.mats, s);
     if (e == hipSuccess)

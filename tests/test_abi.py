@@ -263,10 +263,9 @@ def test_scan_workspace_bytes_for_forced_split(lib, monkeypatch):
 def test_bwd_workspace_bytes_both_paths(lib, monkeypatch):
     """prism_bwd_workspace_bytes.  bf16 (the chunkwise backward, default): write
     keys, per-chunk matrices (20 KB per head and virtual chunk), four bf16 state
-    checkpoints (dk x dv per head and virtual chunk), X and dR (bf16 [T, H, dv]),
-    dkw (fp32 [T, H, dk]), three fp32 per-token scalars, one fp32 per head and
-    virtual chunk, and the dconv_w partials (per 64-token block and per slab of
-    16 blocks, 4 H dk floats each), every part rounded up to 256 bytes.  fp32, or
+    checkpoints (dk x dv per head and virtual chunk), dkw (fp32 [T, H, dk]) and
+    the dconv_w partials (per 64-token block and per slab of 16 blocks, 4 H dk
+    floats each), every part rounded up to 256 bytes.  fp32, or
     PRISM_BWD_CHUNKED=0: the token walk's checkpoints, segment gradients, dkw and
     the same partials, after the write keys."""
     up = lambda x: (x + 255) // 256 * 256
@@ -274,8 +273,8 @@ def test_bwd_workspace_bytes_both_paths(lib, monkeypatch):
     nv = (T // 64 + n) * H
     nb = (T + 63) // 64
     wk = (nb + (nb + 15) // 16) * H * dk * 4
-    chunked = (up(T * H * dk * 2) + up(nv * 20480) + 4 * up(nv * dk * dv * 2) + 2 * up(T * H * dv * 2)
-               + up(T * H * dk * 4) + up(3 * T * H * 4) + up(nv * 4) + up(wk * 4))
+    chunked = (up(T * H * dk * 2) + up(nv * 20480) + 4 * up(nv * dk * dv * 2) + up(T * H * dk * 4)
+               + up(wk * 4))
     walk = lambda e, s: up(T * H * dk * e) + 4 * ((T // s + n + 1) * H * dk * dv + n * 8 * H * dk * dv
                                                   + T * H * dk + wk)
     from gated_delta_rule_prologue_amd import binding as B

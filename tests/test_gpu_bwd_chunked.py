@@ -37,16 +37,15 @@ def token_walk(monkeypatch):
 
 def _chunked_ws_bytes(inp):
     """The chunkwise path's workspace, laid out as the library lays it out
-    (write keys, per-chunk matrices, four bf16 state checkpoints, X and dR,
-    dkw, three per-token scalars, one per-chunk scalar, the write-key
-    backward's partial sums of dconv_w; 256-byte parts)."""
+    (write keys, per-chunk matrices, four bf16 state checkpoints, dkw, the
+    write-key backward's partial sums of dconv_w; 256-byte parts)."""
     r = lambda n: (n + 255) // 256 * 256
     T, H, dk, dv, n = inp.total_tokens, inp.heads, inp.dk, inp.dv, inp.n_seqs
     nv = (T // 64 + n) * H
     nb = (T + 63) // 64                            # write-key blocks and their slabs of 16
     wk = (nb + (nb + 15) // 16) * H * dk * 4 * 4
     return (max(r(T * H * dk * 2), 256) + r(nv * 20480) + 4 * r(nv * dk * dv * 2)
-            + 2 * r(T * H * dv * 2) + r(T * H * dk * 4) + r(3 * T * H * 4) + r(nv * 4) + r(wk))
+            + r(T * H * dk * 4) + r(wk))
 
 
 CASES = [
