@@ -40,6 +40,13 @@ namespace bf16scan {
 
 constexpr int kC = 64;
 constexpr int kThreads = 256;
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+// Cache-policy operand of a buffer access that is coherent at device scope
+// (gfx950 sc1): written where, and read from where, every compute unit of
+// every XCD sees the same data, whichever L2 it sits behind.
+constexpr int kScopeDevice = 16;
+constexpr int kNontemporal = 2;                  // cache-policy operand: streaming (nt)
+constexpr int kProducerWaves = 8;                // wavefronts of a write-key producer block
 
 using namespace mfma;
 
@@ -695,7 +702,8 @@ struct WsCtx {
     int n, e, H, DV, j0, seq0, seq1, nchunks, lane;
     bool s_identity;                             // start from S = I (the transition-only job)
     int64_t rowQK, rowV;
-};
+    const int* kw_ready;                         // write keys made by producer blocks: one flag
+};                                               // per (virtual chunk, head), nonzero once stored
 
 template <int D, int DVS>
 struct WsBuf {
@@ -817,12 +825,16 @@ __device__ __forceinline__ void invert_diag(const uint16_t* scr, uint16_t* Akk, 
 // gist.science summary of arXiv 2602.10796, section 2.2):
 //   r_1  = sum_m w[e,i,m] k[t-3+m]   (ShortConv, taps before the sequence start read 0)
 //   r_{l+1} = r_l (1 - a_l h_l),  kw = b k + sum_{l=1..L-1} a_l r_l u_l.
-// Four wavefronts (r = 0..3) share a chunk: lane (channel piece p = lane % (D/8),
-// token strip) walks ST consecutive tokens of 8 channels, so the conv taps stay
-// in registers; with L <= 4 the inputs of token j + 1 are loaded while token j
-// is computed.
+// NWV wavefronts (r = 0 .. NWV - 1) share a chunk: lane (channel piece
+// p = lane % (D/8), token strip) walks ST consecutive tokens of 8 channels, so
+// the conv taps stay in registers; with L <= 4 the inputs of token j + 1 are
+// loaded while token j is computed.
 // Every load is a bounded buffer load: taps before the sequence start and
 // tokens past the chunk's end read zeros (a zero kw row there).
+// The rows go to an LDS tile (row stride D + 8), or with GLOBAL to the kw rows
+// of the chunk in device memory through a buffer range that ends at the chunk's
+// last token (rows past it are dropped), stored coherently at device scope
+// (sc1) for readers on other compute units.
 template <int D>
 __device__ __forceinline__ void load_taps(const WsCtx& c, float (&w)[8][4])
 {
@@ -841,13 +853,14 @@ __device__ __forceinline__ void load_taps(const WsCtx& c, float (&w)[8][4])
     }
 }
 
-template <int D, int LF>
+template <int D, int LF, int NWV = 4, bool GLOBAL = false>
 __device__ __forceinline__ void fused_kw(const WsCtx& c, uint16_t* sKW, int ch, int r, const float (&w)[8][4])
 {
     constexpr int LDD = D + 8;
     constexpr int NPC = D / 8;                   // 16-byte channel pieces per row
     constexpr int SPW = 64 / NPC;                // token strips per wavefront
-    constexpr int ST = kC / (4 * SPW);           // tokens per strip
+    constexpr int ST = kC / (NWV * SPW);         // tokens per strip
+    static_assert(ST >= 1 && ST * NWV * SPW == kC, "strips cover the chunk");
     constexpr int NS = LF - 1;                   // u, a slots (levels 1 .. L-1)
     constexpr int NH = LF > 2 ? LF - 2 : 1;      // h slots read (the last one never is)
     constexpr uint32_t fl = 0x00020000;
@@ -866,6 +879,9 @@ __device__ __forceinline__ void fused_kw(const WsCtx& c, uint16_t* sKW, int ch, 
     const auto rh = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(c.h + lbase), 0, nt * lrow * 2, fl);
     const auto rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(c.b + (int64_t)c0 * c.H + c.e), 0,
                                                       nt * c.H * 2, fl);
+    // GLOBAL: sKW is the kw array [T, H, D]; the range ends at the chunk's last token
+    const auto rkw = __builtin_amdgcn_make_buffer_rsrc(sKW + (GLOBAL ? (int64_t)c0 * rowQK + c.e * D : 0), 0,
+                                                       GLOBAL ? nt * rowQK * 2 : 0, fl);
     auto ld = [&](__amdgpu_buffer_rsrc_t rs, int off) {
         return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
     };
@@ -941,9 +957,13 @@ __device__ __forceinline__ void fused_kw(const WsCtx& c, uint16_t* sKW, int ch, 
                     rr[i] *= 1.f - av[i] * hv[i];
             }
         }
-        *reinterpret_cast<uint4*>(sKW + (tl0 + j) * LDD + pc) =
-            make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
-                       pack_bf16x2(acc[6], acc[7]));
+        const uint4 out = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                     pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+        if constexpr (GLOBAL)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, out), rkw,
+                                                   ((tl0 + j) * rowQK + pc) * 2, 0, kScopeDevice);
+        else
+            *reinterpret_cast<uint4*>(sKW + (tl0 + j) * LDD + pc) = out;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             x3[i] = x2[i];
@@ -966,8 +986,15 @@ __device__ __forceinline__ void fused_kw(const WsCtx& c, uint16_t* sKW, int ch, 
 // kw alone, and the Gram helper with KWR = r >= 0 computes its quarter of every
 // chunk's kw rows (fused_kw) in phase B, two chunks ahead, where the kw rows
 // would otherwise have been stored.
+// KWP: the write keys are made during the scan by producer blocks of the same
+// launch.  Before a chunk's kw rows are loaded, its readiness count is read
+// (issued ahead of the chunk's other loads, so that waiting for it waits for
+// nothing else) and, until all kProducerWaves producer wavefronts have counted
+// their parts, polled; a bounded wait.  The flag and
+// the kw rows are read coherently at device scope, like the producers wrote
+// them.
 template <int D, int DVS, int ROLE, int LB0, int NLB, bool GATES, int SLOT, bool INV = false,
-          int SIG = -1, bool EARLY = false, int LF = 0, int KWR = -1>
+          int SIG = -1, bool EARLY = false, int LF = 0, int KWR = -1, bool KWP = false>
 __device__ __forceinline__ void helper_loop(const WsCtx& c)
 {
     static_assert(KWR < 0 || (LF > 0 && NLB == 0), "fused write keys: Gram helpers only");
@@ -1034,19 +1061,56 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
         for (int ks = 0; ks < KS; ++ks) {
             const int off = (((LB0 + u) * 16 + ks * RPI + pr) * rowQK + pc) * 2;
             rk[u][ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r.k, off, 0, 0));
-            if constexpr (LF == 0)
+            if constexpr (LF == 0 && !KWP)
                 rw[u][ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r.kw, off, 0, 0));
             rq[u][ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r.q, off, 0, 0));
         }
         const int offv = (((LB0 + u) * 16 + lane / VL) * rowV + (lane % VL) * 8) * 2;
         rv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r.v, offv, 0, 0));
     };
+    auto load_kw_block = [&](const Src& r, int u) {
+        const int rowQK = (int)c.rowQK;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int off = (((LB0 + u) * 16 + ks * RPI + pr) * rowQK + pc) * 2;
+            rw[u][ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r.kw, off, 0,
+                                                                                        kScopeDevice));
+        }
+    };
     auto load = [&](int ch) {
         const Src r = src(ch);
-        load_gates(r);
+        if constexpr (KWP) {
+            const int* fp = c.kw_ready + ((int64_t)(c.seq0 / kC + c.n + ch)) * c.H + c.e;
+            int ready = __hip_atomic_load(fp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            SCHED_FENCE();
+            load_gates(r);
 #pragma unroll
-        for (int u = 0; u < NLB; ++u)
-            load_block(r, u);
+            for (int u = 0; u < NLB; ++u)
+                load_block(r, u);
+            SCHED_FENCE();
+            // the first test outside the polling loop, so that it waits for the
+            // flag load alone (a loop head would wait for every load)
+            if (__builtin_amdgcn_readfirstlane(ready) < kProducerWaves) {
+                for (int spin = 0; spin < (1 << 16); ++spin) {
+                    __builtin_amdgcn_s_sleep(2);
+                    ready = __hip_atomic_load(fp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (__builtin_amdgcn_readfirstlane(ready) >= kProducerWaves)
+                        break;
+                }
+                // a wait that gives up is counted (the kw rows read may then be stale)
+                if (__builtin_amdgcn_readfirstlane(ready) < kProducerWaves && lane == 0)
+                    atomicAdd(&g_wait_giveups, 1u);
+            }
+            asm volatile("" ::: "memory");       // the kw loads stay below the wait
+#pragma unroll
+            for (int u = 0; u < NLB; ++u)
+                load_kw_block(r, u);
+        } else {
+            load_gates(r);
+#pragma unroll
+            for (int u = 0; u < NLB; ++u)
+                load_block(r, u);
+        }
     };
     uint16_t cg = 0x3f80u, cb = 0u;              // gates of the chunk being prepared
     // parts: 0 all rows, 1 q and k only (and the gates), 2 kw and v only
@@ -1413,13 +1477,223 @@ __device__ __forceinline__ void state_loop(const WsCtx& c, int jb)
     }
 }
 
+// Write-key producers: blocks 0 .. n_prod - 1 of a scan launch whose other
+// blocks run the scan on the remaining compute units.  They form the kw rows
+// of every (chunk, sequence, head) item with the prologue's arithmetic (the
+// same steps as fused_kw), in chunk-major order so that every chain's chunk c
+// is ready about when its scan reaches it, store them coherently at device
+// scope, and count each wavefront's part into the item's flag once its
+// stores have completed.  Eight wavefronts share an item (lane: 8 channels of
+// a strip of ST tokens).  The loads of the next item are issued before the wait for the
+// current item's stores, so the two latencies overlap.  Producers wait for
+// nothing but their own memory operations, so the scan blocks that wait for
+// them (a bounded wait) cannot stall them.
+template <int D, int LF>
+__device__ __forceinline__ void produce_kw(const WsCtx& c, const int32_t* __restrict__ cu, int n_seqs,
+                                           int n_prod, uint16_t* kw_out, int* ready)
+{
+    constexpr int NPC = D / 8;                   // 16-byte channel pieces per row
+    constexpr int SPW = 64 / NPC;                // token strips per wavefront
+    constexpr int ST = kC / (kProducerWaves * SPW);   // tokens per strip
+    constexpr int NS = LF - 1;                   // u, a slots (levels 1 .. L-1)
+    constexpr int NH = LF > 2 ? LF - 2 : 1;      // h slots read (the last one never is)
+    constexpr uint32_t fl = 0x00020000;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pc = (lane % NPC) * 8;
+    const int tl0 = (wave * SPW + lane / NPC) * ST;          // first token of the strip, chunk-relative
+    const int H = c.H, rowQK = (int)c.rowQK, lrow = H * NS * D;
+
+    int* sMax = reinterpret_cast<int*>(c.smem);  // the longest sequence's chunk count
+    if (tid == 0)
+        *sMax = 0;
+    __syncthreads();
+    for (int n = tid; n < n_seqs; n += blockDim.x)
+        atomicMax(sMax, (cu[n + 1] - cu[n] + kC - 1) / kC);
+    __syncthreads();
+    const int n_chains = n_seqs * H;
+    const int64_t items = (int64_t)*sMax * n_chains;
+
+    struct Item {
+        int ch, n, e, s0, s1;
+    };
+    // the first item with tokens at index >= i (stride n_prod), or `items`
+    auto next_item = [&](int64_t i, Item& it) {
+        for (; i < items; i += n_prod) {
+            const int ch = (int)(i / n_chains), chain = (int)(i % n_chains);
+            const int n = chain / H;
+            const int s0 = cu[n], s1 = cu[n + 1];
+            if (ch * kC < s1 - s0) {
+                it.ch = ch; it.n = n; it.e = chain % H; it.s0 = s0; it.s1 = s1;
+                return i;
+            }
+        }
+        return items;
+    };
+    struct In {
+        uint4 w[4];                              // conv taps of the lane's channels (bf16)
+        uint4 hk[3];                             // k at tl0 - 1, tl0 - 2, tl0 - 3
+        uint4 k[ST], u[ST][NS], a[ST][NS], h[ST][NH];
+        uint16_t b[ST];
+    };
+    auto ld = [](__amdgpu_buffer_rsrc_t rs, int off) {
+        return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+    };
+    // u, a, h are read once: nontemporal, so they do not displace the rows the
+    // scan blocks share through L2
+    auto ldn = [](__amdgpu_buffer_rsrc_t rs, int off) {
+        return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kNontemporal));
+    };
+    // Bounded buffer loads: taps before the sequence start and tokens past the
+    // chunk's end read zeros.
+    auto fetch = [&](const Item& it, In& x) {
+        const int c0 = it.s0 + it.ch * kC;
+        const int nt = min(kC, it.s1 - c0);
+        const int hb = max(it.s0, c0 - 3);       // first k row a tap may read
+        const auto rk = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(c.k + (int64_t)hb * rowQK + it.e * D), 0, (c0 + nt - hb) * rowQK * 2, fl);
+        const int64_t lbase = (int64_t)c0 * lrow + (int64_t)it.e * NS * D;
+        const auto ru = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(c.u + lbase), 0, nt * lrow * 2, fl);
+        const auto ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(c.a + lbase), 0, nt * lrow * 2, fl);
+        const auto rh = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(c.h + lbase), 0, nt * lrow * 2, fl);
+        const auto rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(c.b + (int64_t)c0 * H + it.e), 0,
+                                                          nt * H * 2, fl);
+        const uint4* wp = reinterpret_cast<const uint4*>(c.cw + ((int64_t)it.e * D + pc) * 4);   // [H][D][4]
+#pragma unroll
+        for (int x4 = 0; x4 < 4; ++x4)
+            x.w[x4] = wp[x4];
+        auto koff = [&](int tl) { return ((c0 + tl - hb) * rowQK + pc) * 2; };   // negative: before the range
+#pragma unroll
+        for (int m = 0; m < 3; ++m)
+            x.hk[m] = ld(rk, koff(tl0 - 1 - m));
+#pragma unroll
+        for (int j = 0; j < ST; ++j) {
+            x.k[j] = ld(rk, koff(tl0 + j));
+            const int lo = ((tl0 + j) * lrow + pc) * 2;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                x.u[j][s] = ldn(ru, lo + s * D * 2);
+                x.a[j][s] = ldn(ra, lo + s * D * 2);
+                if (s < LF - 2)
+                    x.h[j][s] = ldn(rh, lo + s * D * 2);
+            }
+            x.b[j] = __builtin_amdgcn_raw_buffer_load_b16(rb, (tl0 + j) * H * 2, 0, 0);
+        }
+    };
+    auto unpack = [](const uint4& v, float* out) {
+        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[2 * i] = __uint_as_float(wv[i] << 16);
+            out[2 * i + 1] = __uint_as_float(wv[i] & 0xffff0000u);
+        }
+    };
+    // kw rows of the item (rows past the chunk's end dropped by the range)
+    auto emit = [&](const Item& it, const In& x) {
+        const int c0 = it.s0 + it.ch * kC;
+        const int nt = min(kC, it.s1 - c0);
+        const auto rkw = __builtin_amdgcn_make_buffer_rsrc(kw_out + (int64_t)c0 * rowQK + it.e * D, 0,
+                                                           nt * rowQK * 2, fl);
+        float w[8][4];                           // tap m of channel pc + i
+#pragma unroll
+        for (int x4 = 0; x4 < 4; ++x4) {
+            const uint32_t wv[4] = {x.w[x4].x, x.w[x4].y, x.w[x4].z, x.w[x4].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int lo = 8 * x4 + 2 * i, hi = lo + 1;
+                w[lo / 4][lo % 4] = __uint_as_float(wv[i] << 16);
+                w[hi / 4][hi % 4] = __uint_as_float(wv[i] & 0xffff0000u);
+            }
+        }
+        float x1[8], x2[8], x3[8];               // k at t - 1, t - 2, t - 3
+        unpack(x.hk[0], x1);
+        unpack(x.hk[1], x2);
+        unpack(x.hk[2], x3);
+#pragma unroll
+        for (int j = 0; j < ST; ++j) {
+            float kt[8], rr[8], acc[8];
+            unpack(x.k[j], kt);
+            const float bt = bf16_to_f32(x.b[j]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                rr[i] = w[i][3] * kt[i] + w[i][2] * x1[i] + w[i][1] * x2[i] + w[i][0] * x3[i];
+                acc[i] = bt * kt[i];
+            }
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                float av[8], uv[8];
+                unpack(x.a[j][s], av);
+                unpack(x.u[j][s], uv);
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    acc[i] += av[i] * rr[i] * uv[i];
+                if (s < LF - 2) {
+                    float hv[8];
+                    unpack(x.h[j][s], hv);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        rr[i] *= 1.f - av[i] * hv[i];
+                }
+            }
+            const uint4 out = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                         pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, out), rkw,
+                                                   ((tl0 + j) * rowQK + pc) * 2, 0, kScopeDevice);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                x3[i] = x2[i];
+                x2[i] = x1[i];
+                x1[i] = kt[i];
+            }
+        }
+    };
+    // Once every memory operation of this wavefront has completed (the stores
+    // of the item just emitted, the loads of the next), its part of the item is
+    // visible at device scope: count it in the item's flag.  No workgroup
+    // barrier: the wavefronts run out of step, so one's wait overlaps the
+    // others' loads.  The item is ready when all kProducerWaves have counted.
+    auto finish = [&](const Item& it) {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0);
+        asm volatile("" ::: "memory");
+        if (lane == 0)
+            __hip_atomic_fetch_add(ready + (int64_t)(it.s0 / kC + it.n + it.ch) * H + it.e, 1, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    };
+
+    Item cur, nxt;
+    In X;
+    int64_t i = next_item(blockIdx.x, cur);
+    if (i < items)
+        fetch(cur, X);
+    while (i < items) {
+        const int64_t j = next_item(i + n_prod, nxt);
+        emit(cur, X);
+        SCHED_FENCE();
+        if (j < items)
+            fetch(nxt, X);
+        finish(cur);
+        i = j;
+        cur = nxt;
+    }
+}
+
+__global__ __launch_bounds__(256) void clear_ready_kernel(int* __restrict__ p, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        p[i] = 0;
+}
+
 // NW wavefronts: 4 (one per SIMD) or 8 (two per SIMD; slices of 32 columns).
 // Wavefront w runs on SIMD w % 4: with eight, the two state wavefronts share
 // their SIMDs with the two row movers, and each remaining SIMD runs two Gram
 // helpers (five pairs per SIMD).
 // LF > 0: the write keys are computed in the kernel from u, a, h and the conv
 // taps cw (L = LF levels, closed form, no carried history) instead of read from kw.
-template <int D, int DVS, int NW, int LF = 0>
+// PK > 0: the first n_prod blocks are write-key producers (produce_kw, L = PK
+// levels) that write kw and raise kw_ready flags; the scan blocks after them
+// read kw once flagged.
+template <int D, int DVS, int NW, int LF = 0, int PK = 0>
 __global__ __launch_bounds__(NW * 64) void scan_ws_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ kw, const uint16_t* __restrict__ v,
@@ -1429,9 +1703,11 @@ __global__ __launch_bounds__(NW * 64) void scan_ws_kernel(
     float* __restrict__ s_final, int split_block, int DV1, int n_slices1, uint16_t* __restrict__ o1,
     float* __restrict__ s_final1, int skip1, const uint16_t* __restrict__ u = nullptr,
     const uint16_t* __restrict__ a = nullptr, const uint16_t* __restrict__ h = nullptr,
-    const uint16_t* __restrict__ cw = nullptr)
+    const uint16_t* __restrict__ cw = nullptr, int n_prod = 0, int* kw_ready = nullptr,
+    uint16_t* kw_out = nullptr)
 {
     static_assert(LF == 0 || NW == 8, "fused write keys: the eight-wavefront kernel");
+    static_assert(PK == 0 || (NW == 8 && LF == 0), "write-key producers: the eight-wavefront kernel");
     using Ly = LayoutWS<D, DVS>;
     constexpr int NJ = DVS / 16;
     static_assert(NJ == 1 || NJ == 2, "one or two state wavefronts");
@@ -1446,17 +1722,33 @@ __global__ __launch_bounds__(NW * 64) void scan_ws_kernel(
     // writing o1 and s_final1.  One launch keeps both on the chip at once.
     // With skip1 = P > 1 the second scan leaves out sequences 0, P, 2P, ...
     // (first segments started from zero need no transition).
-    const bool job1 = (int)blockIdx.x >= split_block;
+    if constexpr (PK > 0) {
+        if ((int)blockIdx.x < n_prod) {
+            WsCtx pc;
+            pc.smem = smem;
+            pc.k = k; pc.b = b; pc.u = u; pc.a = a; pc.h = h; pc.cw = cw;
+            pc.H = H;
+            pc.rowQK = (int64_t)H * D;
+            const int n_seqs = (int)((gridDim.x - (unsigned)n_prod) / (unsigned)n_slices) / H;
+            produce_kw<D, PK>(pc, cu, n_seqs, n_prod, kw_out, kw_ready);
+            return;
+        }
+    }
+    // scan blocks are numbered from 0 after the producers (n_prod is a multiple
+    // of the XCD count, so the XCD of a block is unchanged by the renumbering)
+    const unsigned bid = blockIdx.x - (unsigned)(PK > 0 ? n_prod : 0);
+    const unsigned nbk = gridDim.x - (unsigned)(PK > 0 ? n_prod : 0);
+    const bool job1 = (int)bid >= split_block;
     int slice, chain;
     if (job1) {
-        xcd_map(blockIdx.x - (unsigned)split_block, gridDim.x - (unsigned)split_block, n_slices1,
+        xcd_map(bid - (unsigned)split_block, nbk - (unsigned)split_block, n_slices1,
                 slice, chain);
         if (skip1 > 1) {
             const int s1 = chain / H;
             chain = ((s1 / (skip1 - 1)) * skip1 + 1 + s1 % (skip1 - 1)) * H + chain % H;
         }
     } else {
-        xcd_map(blockIdx.x, min(gridDim.x, (unsigned)split_block), n_slices, slice, chain);
+        xcd_map(bid, min(nbk, (unsigned)split_block), n_slices, slice, chain);
     }
 
     WsCtx c;
@@ -1480,6 +1772,7 @@ __global__ __launch_bounds__(NW * 64) void scan_ws_kernel(
     c.lane = tid & 63;
     c.rowQK = (int64_t)H * D;
     c.rowV = (int64_t)H * c.DV;              // the second job's rows are DV1 wide
+    c.kw_ready = kw_ready;
 
     {
         // matrices (their upper blocks are never written), gates, scratch
@@ -1497,8 +1790,8 @@ __global__ __launch_bounds__(NW * 64) void scan_ws_kernel(
         switch (wave) {
         case 2: helper_loop<D, DVS, 4, 0, 0, true, 0, false, 0, false, LF, K0>(c); break;   // (0,0) (1,1), gates
         case 3: helper_loop<D, DVS, 6, 0, 0, false, 1, false, -1, false, LF, K1>(c); break; // (1,0) (2,0) (2,1)
-        case 4: helper_loop<D, DVS, 7, 0, 2, false, 0, true, -1, true, LF>(c); break;       // rows 0, 1; T_tt
-        case 5: helper_loop<D, DVS, 7, 2, 2, false, 0, false, -1, true, LF>(c); break;      // rows of blocks 2, 3
+        case 4: helper_loop<D, DVS, 7, 0, 2, false, 0, true, -1, true, LF, -1, (PK > 0)>(c); break;  // rows 0, 1; T_tt
+        case 5: helper_loop<D, DVS, 7, 2, 2, false, 0, false, -1, true, LF, -1, (PK > 0)>(c); break; // rows of blocks 2, 3
         case 6: helper_loop<D, DVS, 5, 0, 0, false, 2, false, 1, false, LF, K2>(c); break;  // (2,2) (3,3)
         default: helper_loop<D, DVS, 3, 0, 0, false, 3, false, -1, false, LF, K3>(c); break; // (3,0) (3,1) (3,2)
         }
@@ -1545,6 +1838,30 @@ static hipError_t launch_fused(const ScanArgs& p, hipStream_t stream)
                        p.cu_seqlens, p.heads, p.dv, n_slices, p.s_init, (uint16_t*)p.o,
                        p.s_final, 0x7fffffff, 0, 1, nullptr, nullptr, 0, (const uint16_t*)p.u,
                        (const uint16_t*)p.a, (const uint16_t*)p.h, (const uint16_t*)p.conv_w);
+    return hipGetLastError();
+}
+
+// The scan with write-key producers: the readiness flags cleared (a fill
+// kernel, so the pair can be captured into a HIP graph), then one launch of
+// p.kw_producers producer blocks followed by the scan blocks.
+template <int D, int L>
+static hipError_t launch_prod(const ScanArgs& p, hipStream_t stream)
+{
+    const int n_slices = p.dv / 32;
+    const int64_t blocks = (int64_t)p.n_seqs * p.heads * n_slices;
+    if (blocks == 0)
+        return hipSuccess;
+    const int64_t nflags = ((int64_t)p.total_tokens / kC + p.n_seqs) * p.heads;
+    const int64_t cb = (nflags + 255) / 256;
+    hipLaunchKernelGGL(clear_ready_kernel, dim3((unsigned)(cb < 1024 ? cb : 1024)), dim3(256), 0, stream,
+                       p.kw_ready, nflags);
+    hipLaunchKernelGGL((scan_ws_kernel<D, 32, 8, 0, L>), dim3((unsigned)(blocks + p.kw_producers)), dim3(512),
+                       0, stream, (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.kw,
+                       (const uint16_t*)p.v, (const uint16_t*)p.g, (const uint16_t*)p.b,
+                       p.cu_seqlens, p.heads, p.dv, n_slices, p.s_init, (uint16_t*)p.o,
+                       p.s_final, 0x7fffffff, 0, 1, nullptr, nullptr, 0, (const uint16_t*)p.u,
+                       (const uint16_t*)p.a, (const uint16_t*)p.h, (const uint16_t*)p.conv_w,
+                       p.kw_producers, p.kw_ready, const_cast<uint16_t*>((const uint16_t*)p.kw));
     return hipGetLastError();
 }
 
@@ -1627,6 +1944,13 @@ hipError_t launch_scan_bf16(const ScanArgs& p, hipStream_t s)
         if (!scan_fused_kw_supported(p.dk, p.dv, p.fused_L) || !p.specialised || p.ws_waves != 8 ||
             p.dv_slice != 32 || !p.u || !p.a || !p.h || !p.conv_w)
             return hipErrorInvalidValue;
+        if (p.kw_producers > 0) {
+            if (p.kw_producers % bf16scan::kXcds != 0 || !p.kw_ready)
+                return hipErrorInvalidValue;
+            if (p.dk == 64)
+                return p.fused_L == 4 ? bf16scan::launch_prod<64, 4>(p, s) : bf16scan::launch_prod<64, 8>(p, s);
+            return bf16scan::launch_prod<128, 4>(p, s);
+        }
         if (p.dk == 64)
             return p.fused_L == 4 ? bf16scan::launch_fused<64, 4>(p, s) : bf16scan::launch_fused<64, 8>(p, s);
         return bf16scan::launch_fused<128, 4>(p, s);

@@ -34,6 +34,13 @@ struct ScanArgs {
     // history) instead of reading kw; 0 reads kw
     int fused_L = 0;
     const void *u = nullptr, *a = nullptr, *h = nullptr, *conv_w = nullptr;
+    // with fused_L > 0 and kw_producers > 0 (a multiple of 8): that many
+    // producer blocks in the scan launch write kw (the workspace array) and
+    // count their eight wavefronts into one flag per (virtual chunk
+    // floor(cu[n] / 64) + n + c, head) in kw_ready ((T / 64 + n_seqs) * H ints,
+    // cleared by the launch) instead
+    int kw_producers = 0;
+    int* kw_ready = nullptr;
 };
 
 hipError_t launch_prologue(const PrologueArgs& p, hipStream_t stream);

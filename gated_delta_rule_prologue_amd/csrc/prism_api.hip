@@ -229,9 +229,48 @@ bool use_fused_kw(const prism_dims* d, int L, int residual, const void* k_hist)
            d->total_tokens > 0;
 }
 
+// Write-key producers (opt-in, PRISM_KW_PRODUCERS=1): prism_fwd runs no
+// prologue launch; the scan launch carries producer blocks on the compute units
+// its own blocks leave idle, which form kw chunk by chunk while the scan runs
+// and flag each chunk's rows for it.  Same shapes as the fused write keys, and
+// the scan must leave at least eight compute units idle (one producer per XCD).
+// Returns the producer count (a multiple of 8, at most 128), or 0.  On MI355X
+// the one launch is slower than the prologue and scan launches (the producers
+// and the scan slow each other down), so it is off by default.
+bool kw_producers_requested() { return env_int("PRISM_KW_PRODUCERS", 0) == 1; }
+
+int kw_producers_for(const prism_dims* d, int L, int residual, const void* k_hist)
+{
+    if (!kw_producers_requested() || d->dtype != PRISM_BF16 ||
+        residual != PRISM_RESIDUAL_LINEAR || k_hist ||
+        !prism::scan_fused_kw_supported(d->dk, d->dv, L) || !use_bf16_kernel(d, 32) ||
+        pick_dv_slice(d) != 32 || !ws8_enabled() || env_int("PRISM_SCAN_SPECIALISED", 1) == 0 ||
+        env_int("PRISM_SCAN_WAVES", 8) == 4 || split_for(d) >= 2 || use_two_pass(d) ||
+        d->total_tokens == 0)
+        return 0;
+    const int64_t blocks = (int64_t)d->n_seqs * d->heads * (d->dv / 32);
+    const int64_t idle = (int64_t)device_cus() - blocks;
+    if (idle < 8)
+        return 0;
+    return (int)(idle / 8 * 8 < 128 ? idle / 8 * 8 : 128);
+}
+
+// Bytes of the producers' readiness flags (one int per virtual chunk and head),
+// reserved in the forward workspace when the producers are requested, for every
+// shape they can serve, whichever way the call goes.
+size_t kw_ready_bytes(const prism_dims* d, int L)
+{
+    if (!kw_producers_requested() || d->dtype != PRISM_BF16 || d->total_tokens == 0 ||
+        !prism::scan_fused_kw_supported(d->dk, d->dv, L))
+        return 0;
+    return round256(((size_t)d->total_tokens / 64 + (size_t)d->n_seqs) * (size_t)d->heads * 4);
+}
+
 struct FusedKw {
     int L = 0;
     const void *u = nullptr, *a = nullptr, *h = nullptr, *conv_w = nullptr;
+    int producers = 0;                           // > 0: producer blocks (kw written, flags raised)
+    int* ready = nullptr;
 };
 
 prism_status scan_impl(const prism_dims* d, const void* q, const void* k, const void* kw,
@@ -266,6 +305,8 @@ prism_status scan_impl(const prism_dims* d, const void* q, const void* k, const 
     if (fk.L > 0) {
         p.fused_L = fk.L;
         p.u = fk.u; p.a = fk.a; p.h = fk.h; p.conv_w = fk.conv_w;
+        p.kw_producers = fk.producers;
+        p.kw_ready = fk.ready;
         return from_hip(prism::launch_scan_bf16(p, (hipStream_t)stream));
     }
     if (use_f32_recurrent(d))
@@ -303,10 +344,14 @@ prism_status fwd_impl(const prism_dims* d, const void* q, const void* k, const v
     prism_status st = check_scan_shape(d);
     if (st != PRISM_OK)
         return st;
-    if (use_fused_kw(d, L, residual, k_hist)) {
+    const int producers = use_fused_kw(d, L, residual, k_hist) ? 0 : kw_producers_for(d, L, residual, k_hist);
+    if (use_fused_kw(d, L, residual, k_hist) || producers > 0) {
         FusedKw fk;
         fk.L = L;
         fk.u = u; fk.a = a; fk.h = h; fk.conv_w = conv_w;
+        fk.producers = producers;
+        fk.ready = reinterpret_cast<int*>(static_cast<unsigned char*>(workspace) + kw_bytes(d) +
+                                          prism_scan_workspace_bytes(d));
         st = scan_impl(d, q, k, workspace, v, g, b, cu_seqlens, S_init, o, S_final,
                        static_cast<unsigned char*>(workspace) + kw_bytes(d), stream, fk);
     } else {
@@ -359,7 +404,7 @@ size_t prism_workspace_bytes(const prism_dims* d, int L)
 {
     if (!dims_ok(d) || L < 1 || L > PRISM_MAX_LEVELS)
         return 0;
-    return kw_bytes(d) + prism_scan_workspace_bytes(d);
+    return kw_bytes(d) + prism_scan_workspace_bytes(d) + kw_ready_bytes(d, L);
 }
 
 prism_status prism_prologue(const prism_dims* d, const void* k, const void* u, const void* a,

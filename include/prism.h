@@ -91,11 +91,22 @@ typedef struct {
 
 /* Bytes of device workspace prism_fwd (and prism_fwd_resume) needs: the write
  * keys kw [T, H, dk] in the input dtype, rounded up to 256 bytes, plus
- * prism_scan_workspace_bytes(d).  Returns 0 for invalid dims or L. */
+ * prism_scan_workspace_bytes(d), plus, when the in-scan write-key producers
+ * are requested (PRISM_KW_PRODUCERS=1 in the environment of the size query and
+ * of the call), for bf16 inputs with T > 0 at the shapes they serve (dk and dv
+ * 64 or 128, L = 4; also L = 8 at dk = 64), their readiness flags:
+ * 4 (floor(T / 64) + n_seqs) H bytes rounded up to 256.  Returns 0 for
+ * invalid dims or L. */
 size_t prism_workspace_bytes(const prism_dims* d, int L);
 
 /*
- * Full forward pass: prologue then chunkwise scan, both on `stream`.
+ * Full forward pass: prologue then chunkwise scan, both on `stream`.  With
+ * PRISM_KW_PRODUCERS=1, for bf16 inputs with the closed-form chain at the
+ * shapes above, when the scan's workgroups leave at least eight compute units
+ * idle, the prologue runs inside the scan launch instead: producer workgroups
+ * on the idle compute units form the write keys chunk by chunk while the scan
+ * runs, and the scan reads each chunk's keys once they are flagged.  Both
+ * evaluate the same formulas; results agree up to rounding order.
  *
  *   q, k         [T, H, dk]
  *   v            [T, H, dv]

@@ -74,17 +74,29 @@ def test_workspace_bytes(lib, monkeypatch):
     """prism_workspace_bytes: the write keys (input dtype, 256-byte rounded)
     plus, for the opt-in two-pass bf16 scan, the per-chunk matrices: 20 KB (T,
     A_kkw, A_qkw, -A_qk as ten bf16 16x16 blocks each) per head and virtual
-    chunk, floor(T / 64) + n_seqs virtual chunks."""
+    chunk, floor(T / 64) + n_seqs virtual chunks; plus, at the bf16 shapes the
+    in-scan write-key producers serve (L = 4, or 8 at dk = 64), one int32
+    readiness flag per head and virtual chunk (256-byte rounded)."""
     from gated_delta_rule_prologue_amd import binding as B
     up = lambda x: (x + 255) // 256 * 256
     d = B.make_dims(8, 16384, 6, 128, 128, B.PRISM_BF16)
     monkeypatch.delenv("PRISM_SCAN_TWOPASS", raising=False)
+    monkeypatch.delenv("PRISM_KW_PRODUCERS", raising=False)
     assert B.workspace_bytes(d, 4) == 16384 * 6 * 128 * 2
     assert B.scan_workspace_bytes(d) == 0
     monkeypatch.setenv("PRISM_SCAN_TWOPASS", "1")
     assert B.workspace_bytes(d, 4) == 16384 * 6 * 128 * 2 + up((16384 // 64 + 8) * 6 * 20480)
     assert B.scan_workspace_bytes(d) == up((16384 // 64 + 8) * 6 * 20480)
     monkeypatch.delenv("PRISM_SCAN_TWOPASS")
+    # the opt-in write-key producers add their flags at the shapes they serve
+    monkeypatch.setenv("PRISM_KW_PRODUCERS", "1")
+    flags = up((16384 // 64 + 8) * 6 * 4)
+    assert B.workspace_bytes(d, 4) == 16384 * 6 * 128 * 2 + flags
+    assert B.workspace_bytes(d, 3) == 16384 * 6 * 128 * 2              # none at L = 3
+    d64 = B.make_dims(3, 1000, 2, 64, 64, B.PRISM_BF16)
+    assert B.workspace_bytes(d64, 8) == up(1000 * 2 * 64 * 2) + up((1000 // 64 + 3) * 2 * 4)
+    assert B.workspace_bytes(B.make_dims(3, 1000, 2, 128, 64, B.PRISM_BF16), 8) == up(1000 * 2 * 128 * 2)
+    monkeypatch.delenv("PRISM_KW_PRODUCERS")
     d32 = B.make_dims(1, 3, 1, 64, 64, B.PRISM_F32)
     assert B.workspace_bytes(d32, 2) == 768
     assert B.workspace_bytes(B.make_dims(1, 0, 1, 64, 64, B.PRISM_BF16), 1) == 256
