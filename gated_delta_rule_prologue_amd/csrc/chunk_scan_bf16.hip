@@ -994,7 +994,7 @@ __device__ __forceinline__ void fused_kw(const WsCtx& c, uint16_t* sKW, int ch, 
 // the kw rows are read coherently at device scope, like the producers wrote
 // them.
 template <int D, int DVS, int ROLE, int LB0, int NLB, bool GATES, int SLOT, bool INV = false,
-          int SIG = -1, bool EARLY = false, int LF = 0, int KWR = -1, bool KWP = false>
+          int SIG = -1, int LF = 0, int KWR = -1, bool KWP = false>
 __device__ __forceinline__ void helper_loop(const WsCtx& c)
 {
     static_assert(KWR < 0 || (LF > 0 && NLB == 0), "fused write keys: Gram helpers only");
@@ -1113,29 +1113,24 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
         }
     };
     uint16_t cg = 0x3f80u, cb = 0u;              // gates of the chunk being prepared
-    // parts: 0 all rows, 1 q and k only (and the gates), 2 kw and v only
-    auto store_rows = [&](int ch, int parts) {
+    // the rows in flight into the row buffer of chunk ch (and the gates taken over)
+    auto store_rows = [&](int ch) {
         uint16_t *sQ = m.Q(ch), *sK = m.K(ch), *sKW = m.KW(ch), *sV = m.V(ch);
 #pragma unroll
         for (int u = 0; u < NLB; ++u) {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int off = ((LB0 + u) * 16 + ks * RPI + pr) * LDD + pc;
-                if (parts != 2) {
-                    *reinterpret_cast<uint4*>(sK + off) = rk[u][ks];
-                    *reinterpret_cast<uint4*>(sQ + off) = rq[u][ks];
-                }
+                *reinterpret_cast<uint4*>(sK + off) = rk[u][ks];
+                *reinterpret_cast<uint4*>(sQ + off) = rq[u][ks];
                 if constexpr (LF == 0)
-                    if (parts != 1)
-                        *reinterpret_cast<uint4*>(sKW + off) = rw[u][ks];
+                    *reinterpret_cast<uint4*>(sKW + off) = rw[u][ks];
             }
-            if (parts != 1 && lane < 16 * VL)
+            if (lane < 16 * VL)
                 *reinterpret_cast<uint4*>(sV + ((LB0 + u) * 16 + lane / VL) * LDV + (lane % VL) * 8) = rv[u];
         }
-        if (parts != 2) {
-            cg = nin ? ng : (uint16_t)0x3f80u;
-            cb = nb;
-        }
+        cg = nin ? ng : (uint16_t)0x3f80u;
+        cb = nb;
     };
 
     // ---- one chunk's matrices in registers (bf16 pairs, accumulator layout)
@@ -1164,11 +1159,6 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
                 invert_cols(m.Scr() + lane * 16, tinv, li);
                 __builtin_amdgcn_s_setprio(0);
             }
-            // kw and v rows of chunk lch go to the buffer chunk lch - 2 uses: the
-            // state path has read that chunk's kw and v in its a-step (phase B of
-            // the previous chunk), so only q and k wait for phase B
-            if (EARLY && lch >= 0)
-                store_rows(lch, 2);
             return;
         }
         Src lsrc;
@@ -1377,7 +1367,7 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
         load(0);
     lds_barrier();                               // LDS cleared
     if (nch > 0) {
-        store_rows(0, 0);
+        store_rows(0);
         if (nch > 1)
             load(1);
         if constexpr (KWR >= 0)
@@ -1388,7 +1378,7 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
         prep(0, -1);
         write_mats();
         if (nch > 1) {
-            store_rows(1, 0);
+            store_rows(1);
             if constexpr (KWR >= 0)
                 fused_kw<D, LF>(c, m.KW(1), 1, KWR, taps);
         }
@@ -1405,7 +1395,7 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
         if (ch + 1 < nch)
             write_mats();
         if (ch + 2 < nch) {
-            store_rows(ch + 2, EARLY ? 1 : 0);
+            store_rows(ch + 2);
             // kw rows of chunk ch + 2 into the buffer whose kw chunk ch no longer needs
             if constexpr (KWR >= 0)
                 fused_kw<D, LF>(c, m.KW(ch + 2), ch + 2, KWR, taps);
@@ -1788,12 +1778,12 @@ __global__ __launch_bounds__(NW * 64) void scan_ws_kernel(
     } else if constexpr (NW == 8) {
         constexpr int K0 = LF ? 0 : -1, K1 = LF ? 1 : -1, K2 = LF ? 2 : -1, K3 = LF ? 3 : -1;
         switch (wave) {
-        case 2: helper_loop<D, DVS, 4, 0, 0, true, 0, false, 0, false, LF, K0>(c); break;   // (0,0) (1,1), gates
-        case 3: helper_loop<D, DVS, 6, 0, 0, false, 1, false, -1, false, LF, K1>(c); break; // (1,0) (2,0) (2,1)
-        case 4: helper_loop<D, DVS, 7, 0, 2, false, 0, true, -1, true, LF, -1, (PK > 0)>(c); break;  // rows 0, 1; T_tt
-        case 5: helper_loop<D, DVS, 7, 2, 2, false, 0, false, -1, true, LF, -1, (PK > 0)>(c); break; // rows of blocks 2, 3
-        case 6: helper_loop<D, DVS, 5, 0, 0, false, 2, false, 1, false, LF, K2>(c); break;  // (2,2) (3,3)
-        default: helper_loop<D, DVS, 3, 0, 0, false, 3, false, -1, false, LF, K3>(c); break; // (3,0) (3,1) (3,2)
+        case 2: helper_loop<D, DVS, 4, 0, 0, true, 0, false, 0, LF, K0>(c); break;   // (0,0) (1,1), gates
+        case 3: helper_loop<D, DVS, 6, 0, 0, false, 1, false, -1, LF, K1>(c); break; // (1,0) (2,0) (2,1)
+        case 4: helper_loop<D, DVS, 7, 0, 2, false, 0, true, -1, LF, -1, (PK > 0)>(c); break;  // rows 0, 1; T_tt
+        case 5: helper_loop<D, DVS, 7, 2, 2, false, 0, false, -1, LF, -1, (PK > 0)>(c); break; // rows of blocks 2, 3
+        case 6: helper_loop<D, DVS, 5, 0, 0, false, 2, false, 1, LF, K2>(c); break;  // (2,2) (3,3)
+        default: helper_loop<D, DVS, 3, 0, 0, false, 3, false, -1, LF, K3>(c); break; // (3,0) (3,1) (3,2)
         }
     } else if constexpr (NJ == 2) {              // diagonal pairs | six off-diagonal pairs
         if (wave == 2)
