@@ -144,7 +144,6 @@ __global__ __launch_bounds__(256) void correct_kernel(
         const_cast<uint16_t*>(op + ((int64_t)t_first * H + e) * D), 0, rows * H * D * 2, kRsrcFlags);
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
         o + ((int64_t)t_first * H + e) * DV, 0, rows * H * DV * 2, kRsrcFlags);
-    uint4 A[2][KS], Ov[2][OV];
     auto fetch = [&](int i, uint4 (&a)[KS], uint4 (&ov)[OV]) {
         const int r0 = i * 64;                   // tile rows from t_first
 #pragma unroll
@@ -158,20 +157,21 @@ __global__ __launch_bounds__(256) void correct_kernel(
                 ro, ((r0 + row) * H * DV + c8) * 2, 0, 0));
         }
     };
-    fetch(0, A[0], Ov[0]);
-    __syncthreads();                             // sB staged
-#pragma unroll 2
-    for (int i = 0; i < ntiles; ++i) {
-        const int cur = i & 1;
-        if (i + 1 < ntiles)
-            fetch(i + 1, A[cur ^ 1], Ov[cur ^ 1]);
+    // tile i from (a, ov), with the loads of tile i + 1 issued into (an, ovn)
+    // first.  Two named register sets used alternately (the loop below is
+    // unrolled by two), so that the loads land where they are used: a runtime
+    // buffer index made the compiler copy, and so wait for, every load at once.
+    // No branch around a load either: past the last tile the buffer ranges read
+    // zeros and drop the stores, so the loop runs whole pairs of tiles.
+    auto tile = [&](int i, const uint4 (&a)[KS], const uint4 (&ov)[OV], uint4 (&an)[KS], uint4 (&ovn)[OV]) {
+        fetch(i + 1, an, ovn);
         f32x4_t acc[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
             acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8_t af = __builtin_bit_cast(bf16x8_t, A[cur][ks]);
+            const bf16x8_t af = __builtin_bit_cast(bf16x8_t, a[ks]);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 const bf16x8_t bfr = __builtin_bit_cast(
@@ -185,11 +185,11 @@ __global__ __launch_bounds__(256) void correct_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 sC[(wave * 16 + g * 4 + r) * LDC + nb * 16 + m] = acc[nb][r];
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int r = 0; r < OV; ++r) {
             const int x = tid + r * 256, row = x / (DV / 8), c8 = (x % (DV / 8)) * 8;
-            const uint32_t w[4] = {Ov[cur][r].x, Ov[cur][r].y, Ov[cur][r].z, Ov[cur][r].w};
+            const uint32_t w[4] = {ov[r].x, ov[r].y, ov[r].z, ov[r].w};
             uint32_t res[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -201,7 +201,14 @@ __global__ __launch_bounds__(256) void correct_kernel(
                 __builtin_bit_cast(v4u_t, make_uint4(res[0], res[1], res[2], res[3])), ro,
                 ((i * 64 + row) * H * DV + c8) * 2, 0, 0);
         }
-        __syncthreads();                         // sC consumed
+        lds_barrier();                           // sC consumed
+    };
+    uint4 A0[KS], O0[OV], A1[KS], O1[OV];
+    fetch(0, A0, O0);
+    lds_barrier();                               // sB staged
+    for (int i = 0; i < ntiles; i += 2) {
+        tile(i, A0, O0, A1, O1);
+        tile(i + 1, A1, O1, A0, O0);
     }
 }
 
