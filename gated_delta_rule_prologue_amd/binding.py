@@ -8,7 +8,8 @@ Names follow the C ABI: ``fwd`` -> prism_fwd, ``fwd_resume`` ->
 prism_fwd_resume, ``fwd_noalloc`` -> prism_fwd_noalloc, ``decode_step`` -> prism_decode_step, ``prologue`` ->
 prism_prologue, ``prologue_ex`` -> prism_prologue_ex, ``scan`` -> prism_scan,
 ``scan_ex`` -> prism_scan_ex, ``workspace_bytes`` -> prism_workspace_bytes,
-``scan_workspace_bytes`` -> prism_scan_workspace_bytes, ``bwd`` -> prism_bwd_ex (prism_bwd
+``scan_workspace_bytes`` -> prism_scan_workspace_bytes, ``fwd_ckpt`` -> prism_fwd_ckpt,
+``checkpoint_bytes`` -> prism_checkpoint_bytes, ``bwd`` -> prism_bwd_ex or prism_bwd_ckpt (prism_bwd
 with a residual choice), ``scan_wait_giveups`` -> prism_scan_wait_giveups.
 """
 from __future__ import annotations
@@ -80,6 +81,12 @@ def lib():
         L.prism_bwd.restype = I
         L.prism_bwd_ex.argtypes = [D] + [P] * 10 + [I, I] + [P] * 14 + [S, P]
         L.prism_bwd_ex.restype = I
+        L.prism_checkpoint_bytes.argtypes = [D]
+        L.prism_checkpoint_bytes.restype = S
+        L.prism_fwd_ckpt.argtypes = [D] + [P] * 10 + [I, I] + [P] * 5 + [S, P]
+        L.prism_fwd_ckpt.restype = I
+        L.prism_bwd_ckpt.argtypes = [D] + [P] * 10 + [I, I] + [P] * 15 + [S, P]
+        L.prism_bwd_ckpt.restype = I
         L.prism_decode_step.restype = I
         L.prism_status_str.argtypes = [I]
         L.prism_status_str.restype = ctypes.c_char_p
@@ -348,9 +355,51 @@ def decode_step(q, k, v, u, g, b, a, h, conv_w, L: int, S, k_hist, o=None, strea
     return o
 
 
+def checkpoint_bytes(dims: Dims) -> int:
+    """Bytes of prism_fwd_ckpt's chunk-start states for the shape (0: none)."""
+    return int(lib().prism_checkpoint_bytes(ctypes.byref(dims)))
+
+
+def fwd_ckpt(q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L: int, S_init=None, o=None,
+             S_final=None, checkpoints=None, workspace=None, stream=None, residual="linear"):
+    """Forward pass that keeps every chunk's start state for the backward
+    (prism_fwd_ckpt).  Returns (o, S_final, checkpoints), the last a uint8
+    device tensor of checkpoint_bytes(dims) bytes to pass to bwd()."""
+    d = _dims_of(q, v, cu_seqlens)
+    _check_write_branch(d, q.dtype, k, u, a, h, b, conv_w, L)
+    _check_scan(d, q.dtype, q, k, k, v, g, b)
+    n, H = d.n_seqs, d.heads
+    if S_init is not None:
+        _expect("S_init", S_init, (n, H, d.dk, d.dv), torch.float32)
+    need = workspace_bytes(d, L)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    cb = checkpoint_bytes(d)
+    if checkpoints is None:
+        checkpoints = torch.empty(max(cb, 1), dtype=torch.uint8, device=q.device)
+    if o is None:
+        o = torch.empty_like(v)
+    if S_final is None:
+        S_final = torch.empty((n, H, d.dk, d.dv), dtype=torch.float32, device=q.device)
+    _expect("o", o, v.shape, v.dtype)
+    _expect("S_final", S_final, (n, H, d.dk, d.dv), torch.float32)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    if checkpoints.numel() * checkpoints.element_size() < cb:
+        raise ValueError(f"checkpoints need {cb} bytes")
+    _check("prism_fwd_ckpt", lib().prism_fwd_ckpt(
+        ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(g), _ptr(b), _ptr(a), _ptr(h),
+        _ptr(conv_w), _ptr(cu_seqlens), int(L), RESIDUAL[residual], _ptr(S_init), _ptr(o),
+        _ptr(S_final), _ptr(checkpoints), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o, S_final, checkpoints
+
+
 def bwd(q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L: int, dO, dS_final=None, S_init=None,
-        want_dS_init: bool = True, workspace=None, stream=None, residual="linear") -> dict:
-    """Gradients of sum <dO, o> + <dS_final, S_final> (prism_bwd_ex;
+        want_dS_init: bool = True, workspace=None, stream=None, residual="linear",
+        checkpoints=None) -> dict:
+    """Gradients of sum <dO, o> + <dS_final, S_final> (prism_bwd_ex, or
+    prism_bwd_ckpt with the ``checkpoints`` of fwd_ckpt on the same inputs;
     ``residual`` "linear" closed-form chain or "gelu"): a dict of fp32 tensors
     q, k, v, u, a, h, g, b, conv_w and S_init (the last when ``want_dS_init``)."""
     if residual not in RESIDUAL:
@@ -375,13 +424,19 @@ def bwd(q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L: int, dO, dS_final=None, S
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if workspace.numel() * workspace.element_size() < need:
         raise ValueError(f"workspace needs {need} bytes")
-    _check("prism_bwd_ex", lib().prism_bwd_ex(
-        ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(g), _ptr(b), _ptr(a), _ptr(h),
-        _ptr(conv_w), _ptr(cu_seqlens), int(L), RESIDUAL[residual], _ptr(S_init), _ptr(dO),
-        _ptr(dS_final),
-        _ptr(out["q"]), _ptr(out["k"]), _ptr(out["v"]), _ptr(out["u"]), _ptr(out["g"]),
-        _ptr(out["b"]), _ptr(out["a"]), _ptr(out["h"]), _ptr(out["conv_w"]), _ptr(out["S_init"]),
-        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    grads = (_ptr(out["q"]), _ptr(out["k"]), _ptr(out["v"]), _ptr(out["u"]), _ptr(out["g"]),
+             _ptr(out["b"]), _ptr(out["a"]), _ptr(out["h"]), _ptr(out["conv_w"]), _ptr(out["S_init"]))
+    head = (ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(g), _ptr(b), _ptr(a), _ptr(h),
+            _ptr(conv_w), _ptr(cu_seqlens), int(L), RESIDUAL[residual], _ptr(S_init), _ptr(dO),
+            _ptr(dS_final))
+    tail = (_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if checkpoints is not None:
+        cb = checkpoint_bytes(d)
+        if checkpoints.numel() * checkpoints.element_size() < cb:
+            raise ValueError(f"checkpoints need {cb} bytes")
+        _check("prism_bwd_ckpt", lib().prism_bwd_ckpt(*head, *grads, _ptr(checkpoints), *tail))
+    else:
+        _check("prism_bwd_ex", lib().prism_bwd_ex(*head, *grads, *tail))
     return out
 
 

@@ -703,7 +703,9 @@ struct WsCtx {
     bool s_identity;                             // start from S = I (the transition-only job)
     int64_t rowQK, rowV;
     const int* kw_ready;                         // write keys made by producer blocks: one flag
-};                                               // per (virtual chunk, head), nonzero once stored
+                                                 // per (virtual chunk, head), counted once stored
+    uint16_t *ck, *ckT;                          // chunk-start states for the backward, or null
+};
 
 template <int D, int DVS>
 struct WsBuf {
@@ -1407,7 +1409,7 @@ __device__ __forceinline__ void helper_loop(const WsCtx& c)
 // State wavefront jb: value columns 16 jb .. 16 jb + 15 of the slice.
 // INV: wavefront 0 inverts the diagonal blocks (in phase B).  SPLIT: the a-step
 // of chunk ch + 1 runs in phase B of chunk ch, beside the helpers' stores.
-template <int D, int DVS, bool INV, bool SPLIT>
+template <int D, int DVS, bool INV, bool SPLIT, bool CK = false>
 __device__ __forceinline__ void state_loop(const WsCtx& c, int jb)
 {
     constexpr int NI = D / 16;
@@ -1436,6 +1438,42 @@ __device__ __forceinline__ void state_loop(const WsCtx& c, int jb)
     auto a_of = [&](int ch) {
         const float* G = m.G(ch);
         a_step<D, DVS>(S, s0b, vf, m.KW(ch), m.V(ch), G + 2 * kC, G[2 * kC - 1], jb, lane);
+        if constexpr (CK) {
+            // the chunk's start state (s0b: bf16 of S before the a-step) as rows
+            // [dk][dv] and transposed [dv][dk] per (virtual chunk, head).  A lane
+            // holds four consecutive rows of one column: one 8-byte store into the
+            // transposed copy; for the rows, the four lanes of each quad (four
+            // consecutive columns) transpose their 4 x 4 block with two DPP
+            // exchanges so that a lane holds four consecutive columns of one row.
+            // The lane-dependent choices are byte permutes with per-lane selectors
+            // (v_perm_b32: selector bytes 0-3 pick the second operand's bytes, 4-7
+            // the first's), not branches.
+            const int64_t vc = ((int64_t)(c.seq0 / kC + c.n + ch)) * c.H + c.e;
+            const int col = c.j0 + jb * 16 + li;
+            const int qp = li & 3;               // position in the quad
+            constexpr uint32_t kFirst = 0x07060504u, kSecond = 0x03020100u;
+            const uint32_t sel_lo = qp < 2 ? kFirst : kSecond, sel_hi = qp < 2 ? kSecond : kFirst;
+            // even lanes: low halves of (own, partner); odd lanes: high halves of (partner, own)
+            const uint32_t sel_pair = (qp & 1) ? 0x03020706u : 0x05040100u;
+            uint16_t* rows = c.ck + (vc * D + lg * 4 + qp) * c.DV + col - qp;
+#pragma unroll
+            for (int ib = 0; ib < D / 16; ++ib) {
+                *reinterpret_cast<v4s_t*>(c.ckT + (vc * c.DV + col) * D + ib * 16 + lg * 4) = s0b[ib];
+                const uint2 w = __builtin_bit_cast(uint2, s0b[ib]);   // rows (0,1), (2,3) of column li
+                // exchange with lane qp ^ 2: lanes 0, 1 keep rows 0, 1 and take those of
+                // lanes 2, 3; lanes 2, 3 keep rows 2, 3 and take those of lanes 0, 1
+                const uint32_t send = __builtin_amdgcn_perm(w.y, w.x, sel_lo);
+                const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x4e, 0xf, 0xf, false);
+                const uint32_t a0 = __builtin_amdgcn_perm(recv, w.x, sel_hi);
+                const uint32_t a1 = __builtin_amdgcn_perm(recv, w.y, sel_lo);
+                // exchange with lane qp ^ 1 and interleave the 16-bit halves
+                const uint32_t b0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)a0, 0xb1, 0xf, 0xf, false);
+                const uint32_t b1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)a1, 0xb1, 0xf, 0xf, false);
+                // row ib * 16 + lg * 4 + qp, columns col - qp .. col - qp + 3
+                *reinterpret_cast<uint2*>(rows + (int64_t)ib * 16 * c.DV) =
+                    make_uint2(__builtin_amdgcn_perm(b0, a0, sel_pair), __builtin_amdgcn_perm(b1, a1, sel_pair));
+            }
+        }
     };
     if (SPLIT && c.nchunks > 0)
         a_of(0);
@@ -1683,7 +1721,8 @@ __global__ __launch_bounds__(256) void clear_ready_kernel(int* __restrict__ p, i
 // PK > 0: the first n_prod blocks are write-key producers (produce_kw, L = PK
 // levels) that write kw and raise kw_ready flags; the scan blocks after them
 // read kw once flagged.
-template <int D, int DVS, int NW, int LF = 0, int PK = 0>
+// CK: the state wavefronts also write every chunk's start state (ck, ckT).
+template <int D, int DVS, int NW, int LF = 0, int PK = 0, bool CK = false>
 __global__ __launch_bounds__(NW * 64) void scan_ws_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ kw, const uint16_t* __restrict__ v,
@@ -1694,10 +1733,11 @@ __global__ __launch_bounds__(NW * 64) void scan_ws_kernel(
     float* __restrict__ s_final1, int skip1, const uint16_t* __restrict__ u = nullptr,
     const uint16_t* __restrict__ a = nullptr, const uint16_t* __restrict__ h = nullptr,
     const uint16_t* __restrict__ cw = nullptr, int n_prod = 0, int* kw_ready = nullptr,
-    uint16_t* kw_out = nullptr)
+    uint16_t* kw_out = nullptr, uint16_t* __restrict__ ck = nullptr, uint16_t* __restrict__ ckT = nullptr)
 {
     static_assert(LF == 0 || NW == 8, "fused write keys: the eight-wavefront kernel");
     static_assert(PK == 0 || (NW == 8 && LF == 0), "write-key producers: the eight-wavefront kernel");
+    static_assert(!CK || (NW == 8 && LF == 0 && PK == 0), "checkpoints: the eight-wavefront kernel");
     using Ly = LayoutWS<D, DVS>;
     constexpr int NJ = DVS / 16;
     static_assert(NJ == 1 || NJ == 2, "one or two state wavefronts");
@@ -1763,6 +1803,8 @@ __global__ __launch_bounds__(NW * 64) void scan_ws_kernel(
     c.rowQK = (int64_t)H * D;
     c.rowV = (int64_t)H * c.DV;              // the second job's rows are DV1 wide
     c.kw_ready = kw_ready;
+    c.ck = ck;
+    c.ckT = ckT;
 
     {
         // matrices (their upper blocks are never written), gates, scratch
@@ -1774,7 +1816,7 @@ __global__ __launch_bounds__(NW * 64) void scan_ws_kernel(
 
     // Every role passes the same number of barriers: 4 + 2 per chunk.
     if (wave < NJ) {
-        state_loop<D, DVS, NW == 4, NW == 8>(c, wave);
+        state_loop<D, DVS, NW == 4, NW == 8, CK>(c, wave);
     } else if constexpr (NW == 8) {
         constexpr int K0 = LF ? 0 : -1, K1 = LF ? 1 : -1, K2 = LF ? 2 : -1, K3 = LF ? 3 : -1;
         switch (wave) {
@@ -1800,18 +1842,19 @@ __global__ __launch_bounds__(NW * 64) void scan_ws_kernel(
     }
 }
 
-template <int D, int DVS, int NW>
+template <int D, int DVS, int NW, bool CK = false>
 static hipError_t launch_ws(const ScanArgs& p, hipStream_t stream)
 {
     const int n_slices = p.dv / DVS;
     const int64_t blocks = (int64_t)p.n_seqs * p.heads * n_slices;
     if (blocks == 0)
         return hipSuccess;
-    hipLaunchKernelGGL((scan_ws_kernel<D, DVS, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
+    hipLaunchKernelGGL((scan_ws_kernel<D, DVS, NW, 0, 0, CK>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
                        (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.kw,
                        (const uint16_t*)p.v, (const uint16_t*)p.g, (const uint16_t*)p.b,
                        p.cu_seqlens, p.heads, p.dv, n_slices, p.s_init, (uint16_t*)p.o,
-                       p.s_final, 0x7fffffff, 0, 1, nullptr, nullptr, 0);
+                       p.s_final, 0x7fffffff, 0, 1, nullptr, nullptr, 0, nullptr, nullptr, nullptr,
+                       nullptr, 0, nullptr, nullptr, (uint16_t*)p.ck, (uint16_t*)p.ckT);
     return hipGetLastError();
 }
 
@@ -1930,6 +1973,12 @@ hipError_t launch_scan_bf16(const ScanArgs& p, hipStream_t s)
 {
     if (!scan_bf16_supported(p.dk, p.dv, p.dv_slice))
         return hipErrorInvalidValue;
+    if (p.ck || p.ckT) {                         // checkpoints: the eight-wavefront kernel only
+        if (!p.ck || !p.ckT || p.fused_L > 0 || !p.specialised || p.ws_waves != 8 || p.dv_slice != 32)
+            return hipErrorInvalidValue;
+        return p.dk == 64 ? bf16scan::launch_ws<64, 32, 8, true>(p, s)
+                          : bf16scan::launch_ws<128, 32, 8, true>(p, s);
+    }
     if (p.fused_L > 0) {
         if (!scan_fused_kw_supported(p.dk, p.dv, p.fused_L) || !p.specialised || p.ws_waves != 8 ||
             p.dv_slice != 32 || !p.u || !p.a || !p.h || !p.conv_w)

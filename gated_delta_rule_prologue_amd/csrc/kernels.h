@@ -41,6 +41,10 @@ struct ScanArgs {
     // cleared by the launch) instead
     int kw_producers = 0;
     int* kw_ready = nullptr;
+    // chunk-start states for the chunkwise backward (bf16 [nv, H, dk, dv] and
+    // transposed [nv, H, dv, dk], nv = T / 64 + n_seqs), or null: the
+    // eight-wavefront kernel
+    void *ck = nullptr, *ckT = nullptr;
 };
 
 hipError_t launch_prologue(const PrologueArgs& p, hipStream_t stream);
@@ -99,6 +103,7 @@ struct BwdChunkBufs {
 // v, g, b) from the checkpoints, in one launch; p.kw holds the write keys.
 // Stores (no accumulation): dq, dk, dkw, dv, dg, db are written whole.
 hipError_t launch_bwd_grads(const ScanArgs& p, const BwdChunkBufs& w, hipStream_t stream);
+
 // The write-key part of the backward pass alone (backward.hip): from dkw (fp32
 // [T][H][dk]) it writes du, da, dh, adds the write-key terms to dk and db (both
 // hold the scan's gradients on entry), and writes dconv_w; part holds

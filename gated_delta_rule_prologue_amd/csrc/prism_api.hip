@@ -483,11 +483,15 @@ prism_status prism_fwd_resume(const prism_dims* d, const void* q, const void* k,
                     S_final, k_hist_out, workspace, workspace_bytes, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
 // Chunkwise backward (bf16, dk and dv in {64, 128}; PRISM_BWD_CHUNKED=0 selects
 // the token walk instead): the forward state products again with every chunk's
 // start state kept (bf16), the carried state gradient backwards chunk by chunk,
 // then every input gradient of all chunks at once on MFMA, then the write-key
-// chain backwards.  At the LM layer (B=8, T=2048, H=6, d=128) 0.89 ms against
+// chain backwards.  At the LM layer (B=8, T=2048, H=6, d=128) 0.64 ms against
 // 3.5 ms for the token walk.
 bool use_bwd_chunked(const prism_dims* d)
 {
@@ -499,6 +503,16 @@ bool use_bwd_chunked(const prism_dims* d)
 struct BwdChunkLayout {
     size_t mats, ck, ckT, dck, dckT, dkw, wk, total;
 };
+
+// Bytes of one of the two checkpoint arrays (bf16 chunk-start states [nv, H, dk, dv]
+// and their transposes), 256-byte rounded; 0 where the chunkwise backward does not
+// serve the shape (it is bf16 with dk, dv in {64, 128}).
+size_t checkpoint_half(const prism_dims* d)
+{
+    if (d->dtype != PRISM_BF16 || !prism::bwd_supported(d->dk, d->dv))
+        return 0;
+    return round256((size_t)(d->total_tokens / 64 + d->n_seqs) * d->heads * d->dk * d->dv * 2);
+}
 
 BwdChunkLayout bwd_chunk_layout(const prism_dims* d)
 {
@@ -517,6 +531,10 @@ BwdChunkLayout bwd_chunk_layout(const prism_dims* d)
     return w;
 }
 
+}  // namespace
+
+extern "C" {
+
 size_t prism_bwd_workspace_bytes(const prism_dims* d, int L)
 {
     if (!dims_ok(d) || L < 1 || L > PRISM_MAX_LEVELS)
@@ -527,13 +545,19 @@ size_t prism_bwd_workspace_bytes(const prism_dims* d, int L)
                                                      d->dv) * sizeof(float);
 }
 
-prism_status prism_bwd_ex(const prism_dims* d, const void* q, const void* k, const void* v,
-                          const void* u, const void* g, const void* b, const void* a, const void* h,
-                          const void* conv_w, const int32_t* cu_seqlens, int L, int residual,
-                          const float* S_init, const void* dO, const float* dS_final, float* dq,
-                          float* dk, float* dv, float* du, float* dg, float* db, float* da,
-                          float* dh, float* dconv_w, float* dS_init, void* workspace,
-                          size_t workspace_bytes, void* stream)
+}  // extern "C"
+
+namespace {
+
+// The backward pass; with ckpt (prism_fwd_ckpt's chunk-start states of the same
+// inputs) the chunkwise form reads them instead of recomputing them.
+prism_status bwd_impl(const prism_dims* d, const void* q, const void* k, const void* v,
+                      const void* u, const void* g, const void* b, const void* a, const void* h,
+                      const void* conv_w, const int32_t* cu_seqlens, int L, int residual,
+                      const float* S_init, const void* dO, const float* dS_final, float* dq,
+                      float* dk, float* dv, float* du, float* dg, float* db, float* da,
+                      float* dh, float* dconv_w, float* dS_init, const void* ckpt, void* workspace,
+                      size_t workspace_bytes, void* stream)
 {
     if (!dims_ok(d) || L < 1 || L > PRISM_MAX_LEVELS || !residual_ok(residual))
         return PRISM_EINVAL;
@@ -573,6 +597,8 @@ prism_status prism_bwd_ex(const prism_dims* d, const void* q, const void* k, con
     p.gs_init = dS_init;
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     if (!use_bwd_chunked(d)) {
+        if (ckpt)                                // checkpoints serve the chunkwise form only
+            return PRISM_EUNSUPPORTED;
         p.ws = reinterpret_cast<float*>(ws + kw_bytes(d));
         return from_hip(prism::launch_bwd(p, (hipStream_t)stream));
     }
@@ -595,12 +621,16 @@ prism_status prism_bwd_ex(const prism_dims* d, const void* q, const void* k, con
     prism::BwdChunkBufs cb;
     cb.dO = dO;
     cb.mats = ws + w.mats;
-    cb.ck = ws + w.ck; cb.ckT = ws + w.ckT; cb.dck = ws + w.dck; cb.dckT = ws + w.dckT;
+    // the chunk-start states: recomputed below, or prism_fwd_ckpt's checkpoints
+    const unsigned char* ckb = static_cast<const unsigned char*>(ckpt);
+    cb.ck = ckpt ? (const void*)ckb : (const void*)(ws + w.ck);
+    cb.ckT = ckpt ? (const void*)(ckb + checkpoint_half(d)) : (const void*)(ws + w.ckT);
+    cb.dck = ws + w.dck; cb.dckT = ws + w.dckT;
     cb.gq = dq; cb.gk = dk; cb.gkw = reinterpret_cast<float*>(ws + w.dkw); cb.gv = dv;
     cb.gg = dg; cb.gb = db;
     const hipStream_t s = (hipStream_t)stream;
     hipError_t e = prism::launch_gram(sp, ws + w.mats, s);
-    if (e == hipSuccess)
+    if (e == hipSuccess && !ckpt)
         e = prism::launch_scan_state(sp, ws + w.mats, s, ws + w.ck, ws + w.ckT);
     if (e == hipSuccess)
         e = prism::launch_bwd_state(sp, dO, ws + w.mats, dS_final, ws + w.dck, ws + w.dckT, dS_init, s);
@@ -609,6 +639,102 @@ prism_status prism_bwd_ex(const prism_dims* d, const void* q, const void* k, con
     if (e == hipSuccess)
         e = prism::launch_write_key_bwd(p, cb.gkw, reinterpret_cast<float*>(ws + w.wk), s);
     return from_hip(e);
+}
+
+// The forward pass that also keeps every chunk's start state for the chunkwise
+// backward: the prologue, then the eight-wavefront bf16 scan over whole
+// sequences (no segment split: its segments start from zero), whose state
+// wavefronts store the checkpoints.
+prism_status fwd_ckpt_impl(const prism_dims* d, const void* q, const void* k, const void* v,
+                           const void* u, const void* g, const void* b, const void* a, const void* h,
+                           const void* conv_w, const int32_t* cu_seqlens, int L, int residual,
+                           const float* S_init, void* o, float* S_final, void* ckpt,
+                           void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!dims_ok(d) || L < 1 || L > PRISM_MAX_LEVELS || !residual_ok(residual))
+        return PRISM_EINVAL;
+    if (!tok_ok(d, q) || !tok_ok(d, k) || !tok_ok(d, v) || !tok_ok(d, g) || !tok_ok(d, b) ||
+        !ptr_ok(conv_w) || !ptr_ok(cu_seqlens) || !tok_ok(d, o) || !ptr_ok(S_final) ||
+        !ptr_ok(workspace) || !ptr_ok(ckpt) || !opt_ok(S_init))
+        return PRISM_EINVAL;
+    if (L > 1 && (!tok_ok(d, u) || !tok_ok(d, a) || !tok_ok(d, h)))
+        return PRISM_EINVAL;
+    if (workspace_bytes < kw_bytes(d))
+        return PRISM_EINVAL;
+    if (checkpoint_half(d) == 0 || !use_bf16_kernel(d, 32) || !ws8_enabled() ||
+        env_int("PRISM_SCAN_SPECIALISED", 1) == 0 || env_int("PRISM_SCAN_WAVES", 8) == 4)
+        return PRISM_EUNSUPPORTED;
+    prism_status st = prologue_impl(d, k, u, a, h, b, conv_w, nullptr, cu_seqlens, L, residual,
+                                    workspace, stream);
+    if (st != PRISM_OK)
+        return st;
+    prism::ScanArgs p;
+    p.bf16 = true;
+    p.n_seqs = d->n_seqs;
+    p.total_tokens = d->total_tokens;
+    p.heads = d->heads;
+    p.dk = d->dk;
+    p.dv = d->dv;
+    p.dv_slice = 32;
+    p.specialised = true;
+    p.ws_waves = 8;
+    p.q = q; p.k = k; p.kw = workspace; p.v = v; p.g = g; p.b = b;
+    p.cu_seqlens = cu_seqlens;
+    p.s_init = S_init;
+    p.o = o;
+    p.s_final = S_final;
+    p.ck = ckpt;
+    p.ckT = static_cast<unsigned char*>(ckpt) + checkpoint_half(d);
+    return from_hip(prism::launch_scan_bf16(p, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t prism_checkpoint_bytes(const prism_dims* d)
+{
+    return dims_ok(d) ? 2 * checkpoint_half(d) : 0;
+}
+
+prism_status prism_fwd_ckpt(const prism_dims* d, const void* q, const void* k, const void* v,
+                            const void* u, const void* g, const void* b, const void* a,
+                            const void* h, const void* conv_w, const int32_t* cu_seqlens, int L,
+                            int residual, const float* S_init, void* o, float* S_final,
+                            void* checkpoints, void* workspace, size_t workspace_bytes, void* stream)
+{
+    return fwd_ckpt_impl(d, q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L, residual, S_init, o,
+                         S_final, checkpoints, workspace, workspace_bytes, stream);
+}
+
+prism_status prism_bwd_ckpt(const prism_dims* d, const void* q, const void* k, const void* v,
+                            const void* u, const void* g, const void* b, const void* a, const void* h,
+                            const void* conv_w, const int32_t* cu_seqlens, int L, int residual,
+                            const float* S_init, const void* dO, const float* dS_final, float* dq,
+                            float* dk, float* dv, float* du, float* dg, float* db, float* da,
+                            float* dh, float* dconv_w, float* dS_init, const void* checkpoints,
+                            void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!ptr_ok(checkpoints))
+        return PRISM_EINVAL;
+    if (checkpoint_half(d) == 0)
+        return PRISM_EUNSUPPORTED;
+    return bwd_impl(d, q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L, residual, S_init, dO, dS_final,
+                    dq, dk, dv, du, dg, db, da, dh, dconv_w, dS_init, checkpoints, workspace,
+                    workspace_bytes, stream);
+}
+
+prism_status prism_bwd_ex(const prism_dims* d, const void* q, const void* k, const void* v,
+                          const void* u, const void* g, const void* b, const void* a, const void* h,
+                          const void* conv_w, const int32_t* cu_seqlens, int L, int residual,
+                          const float* S_init, const void* dO, const float* dS_final, float* dq,
+                          float* dk, float* dv, float* du, float* dg, float* db, float* da,
+                          float* dh, float* dconv_w, float* dS_init, void* workspace,
+                          size_t workspace_bytes, void* stream)
+{
+    return bwd_impl(d, q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L, residual, S_init, dO, dS_final,
+                    dq, dk, dv, du, dg, db, da, dh, dconv_w, dS_init, nullptr, workspace,
+                    workspace_bytes, stream);
 }
 
 prism_status prism_bwd(const prism_dims* d, const void* q, const void* k, const void* v,

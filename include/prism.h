@@ -348,6 +348,58 @@ prism_status prism_bwd_ex(const prism_dims* d,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Training pair: a forward pass that keeps every 64-token chunk's start state,
+ * and a backward pass that reads those checkpoints instead of recomputing them
+ * (the chunkwise form of the recurrence, WeChat page section 消除 Token 间串行:
+ * within a chunk the outputs and the next state follow from the chunk's start
+ * state, so the backward needs the start state of every chunk).
+ *
+ * prism_checkpoint_bytes: bytes of the checkpoints for the shape, two bf16
+ * arrays, each rounded up to 256 bytes: the start states [nv, H, dk, dv] and
+ * the same states transposed [nv, H, dv, dk], nv = floor(T / 64) + n_seqs,
+ * chunk c of sequence n at slot floor(cu_seqlens[n] / 64) + n + c (slots of
+ * no chunk are not written).  0 where the chunkwise backward does not serve
+ * the shape (dtype not bf16, dk or dv not 64 or 128) or the dims are invalid.
+ */
+size_t prism_checkpoint_bytes(const prism_dims* d);
+
+/* prism_fwd_resume without carried history (k_hist = NULL) that also writes
+ * the checkpoints, a device buffer of prism_checkpoint_bytes(d) bytes
+ * (caller-owned; the call writes it and keeps nothing).  The scan runs over
+ * whole sequences (no segment split, whose segments start from zero), on the
+ * eight-wavefront bf16 kernel; outputs as in prism_fwd_resume.  The workspace
+ * is prism_workspace_bytes(d, L) bytes, as for prism_fwd.
+ * PRISM_EUNSUPPORTED for shapes with no checkpoints (see above) or when the
+ * environment selects another scan kernel (PRISM_SCAN_GENERIC=1,
+ * PRISM_SCAN_SPECIALISED=0, PRISM_SCAN_WAVES=4); PRISM_EINVAL for invalid
+ * arguments, a null checkpoint buffer included. */
+prism_status prism_fwd_ckpt(const prism_dims* d,
+                            const void* q, const void* k, const void* v,
+                            const void* u, const void* g, const void* b,
+                            const void* a, const void* h, const void* conv_w,
+                            const int32_t* cu_seqlens, int L, int residual, const float* S_init,
+                            void* o, float* S_final, void* checkpoints,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* prism_bwd_ex on the chunkwise form with the chunk-start states read from
+ * `checkpoints` (written by prism_fwd_ckpt for the same inputs, S_init and
+ * residual chain; read only) instead of recomputed: one launch fewer.
+ * Arguments, layouts, workspace and errors otherwise as in prism_bwd_ex;
+ * PRISM_EUNSUPPORTED where the chunkwise form does not run (shapes with no
+ * checkpoints, PRISM_BWD_CHUNKED=0); PRISM_EINVAL for a null checkpoint
+ * buffer. */
+prism_status prism_bwd_ckpt(const prism_dims* d,
+                            const void* q, const void* k, const void* v,
+                            const void* u, const void* g, const void* b,
+                            const void* a, const void* h, const void* conv_w,
+                            const int32_t* cu_seqlens, int L, int residual, const float* S_init,
+                            const void* dO, const float* dS_final,
+                            float* dq, float* dk, float* dv, float* du, float* dg, float* db,
+                            float* da, float* dh, float* dconv_w, float* dS_init,
+                            const void* checkpoints, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
  * Diagnostic: the number of bounded in-kernel waits that gave up since the
  * last reset, on the current device.  The eight-wavefront bf16 scan has one
  * bounded LDS-flag wait per chunk (the workgroup's diagonal-inverse handoff);

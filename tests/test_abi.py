@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
               "prism_status_str", "prism_abi_version", "prism_fwd_resume", "prism_decode_step",
               "prism_prologue_ex", "prism_scan_ex", "prism_scan_workspace_bytes", "prism_bwd",
               "prism_bwd_workspace_bytes", "prism_bwd_ex", "prism_scan_wait_giveups",
-              "prism_fwd_noalloc"):
+              "prism_fwd_noalloc", "prism_checkpoint_bytes", "prism_fwd_ckpt", "prism_bwd_ckpt"):
         assert n in names
 
 
@@ -303,3 +303,26 @@ def test_bwd_workspace_bytes_both_paths(lib, monkeypatch):
     e16 = B.make_dims(n, 0, H, dk, dv, B.PRISM_BF16)
     assert lib.prism_bwd_workspace_bytes(ctypes.byref(e16), L) == 256 + 4 * ((n + 1) * H * dk * dv
                                                                            + n * 8 * H * dk * dv)
+
+
+def test_checkpoint_bytes_and_argument_checks(lib):
+    """prism_checkpoint_bytes: two bf16 arrays of floor(T / 64) + n_seqs
+    chunk-start states per head (rows and transposes), 256-byte rounded, for the
+    shapes the chunkwise backward serves; 0 elsewhere.  The checkpoint entry
+    points reject a null buffer and unserved shapes before touching the device."""
+    from gated_delta_rule_prologue_amd import binding as B
+    up = lambda x: (x + 255) // 256 * 256
+    d = B.make_dims(8, 16384, 6, 128, 128, B.PRISM_BF16)
+    assert B.checkpoint_bytes(d) == 2 * up((16384 // 64 + 8) * 6 * 128 * 128 * 2)
+    assert B.checkpoint_bytes(B.make_dims(3, 100, 2, 64, 128, B.PRISM_BF16)) == 2 * up((1 + 3) * 2 * 64 * 128 * 2)
+    assert B.checkpoint_bytes(B.make_dims(1, 100, 1, 64, 64, B.PRISM_F32)) == 0
+    assert B.checkpoint_bytes(B.make_dims(1, 100, 1, 32, 64, B.PRISM_BF16)) == 0
+    assert B.checkpoint_bytes(B.make_dims(0, 0, 1, 64, 64, B.PRISM_BF16)) == 0
+    fwd = lambda d, ck: lib.prism_fwd_ckpt(ctypes.byref(d), *([FAKE] * 10), 2, 0, None, FAKE, FAKE, ck,
+                                           FAKE, 1 << 30, None)
+    bwd = lambda d, ck: lib.prism_bwd_ckpt(ctypes.byref(d), *([FAKE] * 10), 2, 0, None, FAKE, None,
+                                           *([FAKE] * 9), None, ck, FAKE, 1 << 30, None)
+    ok = B.make_dims(2, 100, 2, 64, 64, B.PRISM_BF16)
+    assert fwd(ok, None) == B.PRISM_EINVAL and bwd(ok, None) == B.PRISM_EINVAL
+    f32 = B.make_dims(2, 100, 2, 64, 64, B.PRISM_F32)
+    assert fwd(f32, FAKE) == B.PRISM_EUNSUPPORTED and bwd(f32, FAKE) == B.PRISM_EUNSUPPORTED
