@@ -19,8 +19,11 @@ The line also carries a "decode" object: the single-token decode step
 (prism_decode_step, state and convolution history carried in place) timed
 on serving batches shaped like the recommendation and language-model layers,
 each against its HBM roofline, and a "backward" object: prism_bwd (the
-gradients of every input for an upstream dO) on the same workload.  Both are
-measured after the forward pass and are not part of "value".
+gradients of every input for an upstream dO) on the same workload, with a
+"training_pair" inside it where the chunkwise backward serves the shape:
+prism_fwd_ckpt then prism_bwd_ckpt, the forward keeping every chunk's start
+state for the backward.  Both are measured after the forward pass and are not
+part of "value".
 """
 from __future__ import annotations
 
@@ -321,6 +324,71 @@ def bwd_chunk_flops(w, T):
     return (per + scan_flops_ht(w)) * T * w.heads
 
 
+def training_pair_bench(w, inp, dims, dev_copies, steps, warmup, bwd_args):
+    """Time a training step's pair: prism_fwd_ckpt (the forward, keeping every
+    chunk's start state) then prism_bwd_ckpt (every gradient, reading those
+    states instead of recomputing them), HIP events around each call; and the
+    same loop of prism_fwd then prism_bwd (recomputing them) on the same input
+    copies, so both pairs see the same cache state."""
+    import ctypes
+    import torch
+    from gated_delta_rule_prologue_amd import binding
+    stream = torch.cuda.current_stream()
+    lib = binding.lib()
+    T = inp.total_tokens
+    cb = binding.checkpoint_bytes(dims)
+    fneed = binding.workspace_bytes(dims, w.L)
+    lin = binding.RESIDUAL["linear"]
+    fargs, bargs, pargs = [], [], []
+    for c in dev_copies:
+        c["ck"] = torch.empty(cb, dtype=torch.uint8, device="cuda")
+        c["fws"] = torch.empty(fneed, dtype=torch.uint8, device="cuda")
+        o, S, _ = binding.fwd_ckpt(c["q"], c["k"], c["v"], c["u"], c["g"], c["b"], c["a"], c["h"],
+                                   c["conv_w"], c["cu_seqlens"], w.L, checkpoints=c["ck"],
+                                   workspace=c["fws"])
+        out = binding.bwd(c["q"], c["k"], c["v"], c["u"], c["g"], c["b"], c["a"], c["h"],
+                          c["conv_w"], c["cu_seqlens"], w.L, c["dO"], want_dS_init=True,
+                          workspace=c["bws"], checkpoints=c["ck"])
+        fargs.append([ctypes.byref(dims)] + raw_args(
+            c["q"], c["k"], c["v"], c["u"], c["g"], c["b"], c["a"], c["h"], c["conv_w"],
+            c["cu_seqlens"], w.L, lin, None, o, S, c["ck"], c["fws"], fneed, stream.cuda_stream))
+        bargs.append([ctypes.byref(dims)] + raw_args(
+            c["q"], c["k"], c["v"], c["u"], c["g"], c["b"], c["a"], c["h"], c["conv_w"],
+            c["cu_seqlens"], w.L, lin, None, c["dO"], None, out["q"], out["k"], out["v"],
+            out["u"], out["g"], out["b"], out["a"], out["h"], out["conv_w"], out["S_init"],
+            c["ck"], c["bws"], c["bws"].numel(), stream.cuda_stream))
+        pargs.append([ctypes.byref(dims)] + raw_args(
+            c["q"], c["k"], c["v"], c["u"], c["g"], c["b"], c["a"], c["h"], c["conv_w"],
+            c["cu_seqlens"], w.L, o, S, c["fws"], fneed, stream.cuda_stream))
+
+    def pair(fwd, bwd, fa, ba):
+        for i in range(warmup):
+            fwd(*fa[i % len(fa)])
+            bwd(*ba[i % len(ba)])
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        status = 0
+        t0 = time.perf_counter()
+        for i in range(steps):
+            ev[i][0].record(stream)
+            status |= fwd(*fa[i % len(fa)])
+            ev[i][1].record(stream)
+            status |= bwd(*ba[i % len(ba)])
+            ev[i][2].record(stream)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        assert status == 0, binding.status_str(status)
+        f_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+        b_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+        return steps * T / elapsed, f_ms * 1e3, b_ms * 1e3
+
+    tps, f_us, b_us = pair(lib.prism_fwd_ckpt, lib.prism_bwd_ckpt, fargs, bargs)
+    _, rf_us, rb_us = pair(lib.prism_fwd, lib.prism_bwd, pargs, bwd_args)
+    return {"tokens_per_s": tps, "us_per_step": f_us + b_us,
+            "fwd_ckpt_us": f_us, "bwd_ckpt_us": b_us, "checkpoint_bytes": cb,
+            "recompute_pair": {"us_per_step": rf_us + rb_us, "fwd_us": rf_us, "bwd_us": rb_us}}
+
+
 def bwd_bench(w, inp, dev_copies, steps, warmup, with_oracle=False):
     """Time prism_bwd (gradients of every input) on the workload, with the
     upstream gradient dO and no carried state."""
@@ -383,6 +451,9 @@ def bwd_bench(w, inp, dev_copies, steps, warmup, with_oracle=False):
         tfm = mf / (ms * 1e-3) / 1e12
         res["mfma"] = {"achieved": tfm, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                        "frac": tfm / BF16_PEAK_TFLOPS, "algorithmic_flops": mf}
+        if binding.checkpoint_bytes(dims) > 0:
+            res["training_pair"] = training_pair_bench(w, inp, dims, dev_copies, steps, warmup,
+                                                       args)
     if with_oracle:
         # a bounded sample: as many whole (sequence, head) chains as host threads
         # (the oracle keeps every state of a chain), scaled to tokens/s of the
