@@ -344,14 +344,13 @@ def training_pair_bench(w, inp, dims, dev_copies, steps, warmup, bwd_args):
         c["ck"] = torch.empty(cb, dtype=torch.uint8, device="cuda")
         c["fws"] = torch.empty(fneed, dtype=torch.uint8, device="cuda")
         o, S, _ = binding.fwd_ckpt(c["q"], c["k"], c["v"], c["u"], c["g"], c["b"], c["a"], c["h"],
-                                   c["conv_w"], c["cu_seqlens"], w.L, checkpoints=c["ck"],
-                                   workspace=c["fws"])
+                                   c["conv_w"], c["cu_seqlens"], w.L, checkpoints=c["ck"])
         out = binding.bwd(c["q"], c["k"], c["v"], c["u"], c["g"], c["b"], c["a"], c["h"],
                           c["conv_w"], c["cu_seqlens"], w.L, c["dO"], want_dS_init=True,
                           workspace=c["bws"], checkpoints=c["ck"])
         fargs.append([ctypes.byref(dims)] + raw_args(
             c["q"], c["k"], c["v"], c["u"], c["g"], c["b"], c["a"], c["h"], c["conv_w"],
-            c["cu_seqlens"], w.L, lin, None, o, S, c["ck"], c["fws"], fneed, stream.cuda_stream))
+            c["cu_seqlens"], w.L, lin, None, o, S, c["ck"], None, 0, stream.cuda_stream))
         bargs.append([ctypes.byref(dims)] + raw_args(
             c["q"], c["k"], c["v"], c["u"], c["g"], c["b"], c["a"], c["h"], c["conv_w"],
             c["cu_seqlens"], w.L, lin, None, c["dO"], None, out["q"], out["k"], out["v"],

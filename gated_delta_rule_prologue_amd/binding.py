@@ -362,8 +362,9 @@ def checkpoint_bytes(dims: Dims) -> int:
 
 def fwd_ckpt(q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L: int, S_init=None, o=None,
              S_final=None, checkpoints=None, workspace=None, stream=None, residual="linear"):
-    """Forward pass that keeps every chunk's start state for the backward
-    (prism_fwd_ckpt).  Returns (o, S_final, checkpoints), the last a uint8
+    """Forward pass that keeps every chunk's start state and the write keys for
+    the backward (prism_fwd_ckpt; it uses no workspace, ``workspace`` is passed
+    through if given).  Returns (o, S_final, checkpoints), the last a uint8
     device tensor of checkpoint_bytes(dims) bytes to pass to bwd()."""
     d = _dims_of(q, v, cu_seqlens)
     _check_write_branch(d, q.dtype, k, u, a, h, b, conv_w, L)
@@ -371,9 +372,6 @@ def fwd_ckpt(q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L: int, S_init=None, o=
     n, H = d.n_seqs, d.heads
     if S_init is not None:
         _expect("S_init", S_init, (n, H, d.dk, d.dv), torch.float32)
-    need = workspace_bytes(d, L)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     cb = checkpoint_bytes(d)
     if checkpoints is None:
         checkpoints = torch.empty(max(cb, 1), dtype=torch.uint8, device=q.device)
@@ -383,15 +381,13 @@ def fwd_ckpt(q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L: int, S_init=None, o=
         S_final = torch.empty((n, H, d.dk, d.dv), dtype=torch.float32, device=q.device)
     _expect("o", o, v.shape, v.dtype)
     _expect("S_final", S_final, (n, H, d.dk, d.dv), torch.float32)
-    if workspace.numel() * workspace.element_size() < need:
-        raise ValueError(f"workspace needs {need} bytes")
     if checkpoints.numel() * checkpoints.element_size() < cb:
         raise ValueError(f"checkpoints need {cb} bytes")
     _check("prism_fwd_ckpt", lib().prism_fwd_ckpt(
         ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(g), _ptr(b), _ptr(a), _ptr(h),
         _ptr(conv_w), _ptr(cu_seqlens), int(L), RESIDUAL[residual], _ptr(S_init), _ptr(o),
         _ptr(S_final), _ptr(checkpoints), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream)))
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)))
     return o, S_final, checkpoints
 
 

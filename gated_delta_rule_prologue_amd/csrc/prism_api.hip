@@ -514,6 +514,14 @@ size_t checkpoint_half(const prism_dims* d)
     return round256((size_t)(d->total_tokens / 64 + d->n_seqs) * d->heads * d->dk * d->dv * 2);
 }
 
+// The checkpoints of prism_fwd_ckpt: the chunk-start states, their transposes
+// and the write keys kw, each part 256-byte aligned; 0 where they do not serve.
+size_t checkpoint_total(const prism_dims* d)
+{
+    const size_t half = checkpoint_half(d);
+    return half ? 2 * half + kw_bytes(d) : 0;
+}
+
 BwdChunkLayout bwd_chunk_layout(const prism_dims* d)
 {
     BwdChunkLayout w;
@@ -549,8 +557,9 @@ size_t prism_bwd_workspace_bytes(const prism_dims* d, int L)
 
 namespace {
 
-// The backward pass; with ckpt (prism_fwd_ckpt's chunk-start states of the same
-// inputs) the chunkwise form reads them instead of recomputing them.
+// The backward pass; with ckpt (prism_fwd_ckpt's chunk-start states and write
+// keys of the same inputs) the chunkwise form reads them instead of recomputing
+// them.
 prism_status bwd_impl(const prism_dims* d, const void* q, const void* k, const void* v,
                       const void* u, const void* g, const void* b, const void* a, const void* h,
                       const void* conv_w, const int32_t* cu_seqlens, int L, int residual,
@@ -573,10 +582,18 @@ prism_status bwd_impl(const prism_dims* d, const void* q, const void* k, const v
         return PRISM_EUNSUPPORTED;
     if (workspace_bytes < prism_bwd_workspace_bytes(d, L))
         return PRISM_EINVAL;
-    prism_status st = prologue_impl(d, k, u, a, h, b, conv_w, nullptr, cu_seqlens, L, residual,
-                                    workspace, stream);
-    if (st != PRISM_OK)
-        return st;
+    if (ckpt && !use_bwd_chunked(d))             // checkpoints serve the chunkwise form only
+        return PRISM_EUNSUPPORTED;
+    // the write keys: prism_fwd_ckpt's, after the two state arrays, or recomputed
+    // into the workspace
+    void* kwp = ckpt ? static_cast<unsigned char*>(const_cast<void*>(ckpt)) + 2 * checkpoint_half(d)
+                     : workspace;
+    if (!ckpt) {
+        const prism_status st = prologue_impl(d, k, u, a, h, b, conv_w, nullptr, cu_seqlens, L,
+                                              residual, workspace, stream);
+        if (st != PRISM_OK)
+            return st;
+    }
     prism::BwdArgs p;
     p.bf16 = d->dtype == PRISM_BF16;
     p.n_seqs = d->n_seqs;
@@ -586,7 +603,7 @@ prism_status bwd_impl(const prism_dims* d, const void* q, const void* k, const v
     p.dv = d->dv;
     p.L = L;
     p.gelu = residual == PRISM_RESIDUAL_GELU;
-    p.q = q; p.k = k; p.v = v; p.kw = workspace; p.u = u; p.a = a; p.h = h; p.g = g; p.b = b;
+    p.q = q; p.k = k; p.v = v; p.kw = kwp; p.u = u; p.a = a; p.h = h; p.g = g; p.b = b;
     p.conv_w = conv_w;
     p.dO = dO;
     p.cu_seqlens = cu_seqlens;
@@ -597,8 +614,6 @@ prism_status bwd_impl(const prism_dims* d, const void* q, const void* k, const v
     p.gs_init = dS_init;
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     if (!use_bwd_chunked(d)) {
-        if (ckpt)                                // checkpoints serve the chunkwise form only
-            return PRISM_EUNSUPPORTED;
         p.ws = reinterpret_cast<float*>(ws + kw_bytes(d));
         return from_hip(prism::launch_bwd(p, (hipStream_t)stream));
     }
@@ -613,7 +628,7 @@ prism_status bwd_impl(const prism_dims* d, const void* q, const void* k, const v
     sp.dv_slice = 32;
     sp.specialised = false;
     sp.ws_waves = 8;
-    sp.q = q; sp.k = k; sp.kw = workspace; sp.v = v; sp.g = g; sp.b = b;
+    sp.q = q; sp.k = k; sp.kw = kwp; sp.v = v; sp.g = g; sp.b = b;
     sp.cu_seqlens = cu_seqlens;
     sp.s_init = S_init;
     sp.o = nullptr;
@@ -641,10 +656,11 @@ prism_status bwd_impl(const prism_dims* d, const void* q, const void* k, const v
     return from_hip(e);
 }
 
-// The forward pass that also keeps every chunk's start state for the chunkwise
-// backward: the prologue, then the eight-wavefront bf16 scan over whole
-// sequences (no segment split: its segments start from zero), whose state
-// wavefronts store the checkpoints.
+// The forward pass that also keeps every chunk's start state and the write keys
+// for the chunkwise backward: the prologue (kw into the checkpoints), then the
+// eight-wavefront bf16 scan over whole sequences (no segment split: its segments
+// start from zero), whose state wavefronts store the chunk-start states.  The
+// workspace is not used.
 prism_status fwd_ckpt_impl(const prism_dims* d, const void* q, const void* k, const void* v,
                            const void* u, const void* g, const void* b, const void* a, const void* h,
                            const void* conv_w, const int32_t* cu_seqlens, int L, int residual,
@@ -655,17 +671,19 @@ prism_status fwd_ckpt_impl(const prism_dims* d, const void* q, const void* k, co
         return PRISM_EINVAL;
     if (!tok_ok(d, q) || !tok_ok(d, k) || !tok_ok(d, v) || !tok_ok(d, g) || !tok_ok(d, b) ||
         !ptr_ok(conv_w) || !ptr_ok(cu_seqlens) || !tok_ok(d, o) || !ptr_ok(S_final) ||
-        !ptr_ok(workspace) || !ptr_ok(ckpt) || !opt_ok(S_init))
+        !ptr_ok(ckpt) || !opt_ok(S_init))
         return PRISM_EINVAL;
     if (L > 1 && (!tok_ok(d, u) || !tok_ok(d, a) || !tok_ok(d, h)))
         return PRISM_EINVAL;
-    if (workspace_bytes < kw_bytes(d))
-        return PRISM_EINVAL;
+    (void)workspace;
+    (void)workspace_bytes;
     if (checkpoint_half(d) == 0 || !use_bf16_kernel(d, 32) || !ws8_enabled() ||
         env_int("PRISM_SCAN_SPECIALISED", 1) == 0 || env_int("PRISM_SCAN_WAVES", 8) == 4)
         return PRISM_EUNSUPPORTED;
+    unsigned char* ckb = static_cast<unsigned char*>(ckpt);
+    void* kwp = ckb + 2 * checkpoint_half(d);
     prism_status st = prologue_impl(d, k, u, a, h, b, conv_w, nullptr, cu_seqlens, L, residual,
-                                    workspace, stream);
+                                    kwp, stream);
     if (st != PRISM_OK)
         return st;
     prism::ScanArgs p;
@@ -678,13 +696,13 @@ prism_status fwd_ckpt_impl(const prism_dims* d, const void* q, const void* k, co
     p.dv_slice = 32;
     p.specialised = true;
     p.ws_waves = 8;
-    p.q = q; p.k = k; p.kw = workspace; p.v = v; p.g = g; p.b = b;
+    p.q = q; p.k = k; p.kw = kwp; p.v = v; p.g = g; p.b = b;
     p.cu_seqlens = cu_seqlens;
     p.s_init = S_init;
     p.o = o;
     p.s_final = S_final;
-    p.ck = ckpt;
-    p.ckT = static_cast<unsigned char*>(ckpt) + checkpoint_half(d);
+    p.ck = ckb;
+    p.ckT = ckb + checkpoint_half(d);
     return from_hip(prism::launch_scan_bf16(p, (hipStream_t)stream));
 }
 
@@ -694,7 +712,7 @@ extern "C" {
 
 size_t prism_checkpoint_bytes(const prism_dims* d)
 {
-    return dims_ok(d) ? 2 * checkpoint_half(d) : 0;
+    return dims_ok(d) ? checkpoint_total(d) : 0;
 }
 
 prism_status prism_fwd_ckpt(const prism_dims* d, const void* q, const void* k, const void* v,

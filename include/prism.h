@@ -354,12 +354,13 @@ prism_status prism_bwd_ex(const prism_dims* d,
  * within a chunk the outputs and the next state follow from the chunk's start
  * state, so the backward needs the start state of every chunk).
  *
- * prism_checkpoint_bytes: bytes of the checkpoints for the shape, two bf16
- * arrays, each rounded up to 256 bytes: the start states [nv, H, dk, dv] and
- * the same states transposed [nv, H, dv, dk], nv = floor(T / 64) + n_seqs,
- * chunk c of sequence n at slot floor(cu_seqlens[n] / 64) + n + c (slots of
- * no chunk are not written).  0 where the chunkwise backward does not serve
- * the shape (dtype not bf16, dk or dv not 64 or 128) or the dims are invalid.
+ * prism_checkpoint_bytes: bytes of the checkpoints for the shape, three bf16
+ * arrays, each rounded up to 256 bytes: the start states [nv, H, dk, dv], the
+ * same states transposed [nv, H, dv, dk], nv = floor(T / 64) + n_seqs, chunk c
+ * of sequence n at slot floor(cu_seqlens[n] / 64) + n + c (slots of no chunk
+ * are not written), then the write keys kw [T, H, dk] (at least 256 bytes).
+ * 0 where the chunkwise backward does not serve the shape (dtype not bf16, dk
+ * or dv not 64 or 128) or the dims are invalid.
  */
 size_t prism_checkpoint_bytes(const prism_dims* d);
 
@@ -367,8 +368,10 @@ size_t prism_checkpoint_bytes(const prism_dims* d);
  * the checkpoints, a device buffer of prism_checkpoint_bytes(d) bytes
  * (caller-owned; the call writes it and keeps nothing).  The scan runs over
  * whole sequences (no segment split, whose segments start from zero), on the
- * eight-wavefront bf16 kernel; outputs as in prism_fwd_resume.  The workspace
- * is prism_workspace_bytes(d, L) bytes, as for prism_fwd.
+ * eight-wavefront bf16 kernel; outputs as in prism_fwd_resume.  The write
+ * keys go into the checkpoints, so the workspace is neither read nor written
+ * (it may be NULL with workspace_bytes 0; the arguments keep the call shape of
+ * the other forward entry points).
  * PRISM_EUNSUPPORTED for shapes with no checkpoints (see above) or when the
  * environment selects another scan kernel (PRISM_SCAN_GENERIC=1,
  * PRISM_SCAN_SPECIALISED=0, PRISM_SCAN_WAVES=4); PRISM_EINVAL for invalid
@@ -383,7 +386,8 @@ prism_status prism_fwd_ckpt(const prism_dims* d,
 
 /* prism_bwd_ex on the chunkwise form with the chunk-start states read from
  * `checkpoints` (written by prism_fwd_ckpt for the same inputs, S_init and
- * residual chain; read only) instead of recomputed: one launch fewer.
+ * residual chain; read only) and the write keys read from there too, instead
+ * of recomputed: two launches fewer (the prologue and the state recompute).
  * Arguments, layouts, workspace and errors otherwise as in prism_bwd_ex;
  * PRISM_EUNSUPPORTED where the chunkwise form does not run (shapes with no
  * checkpoints, PRISM_BWD_CHUNKED=0); PRISM_EINVAL for a null checkpoint

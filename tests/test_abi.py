@@ -307,14 +307,17 @@ def test_bwd_workspace_bytes_both_paths(lib, monkeypatch):
 
 def test_checkpoint_bytes_and_argument_checks(lib):
     """prism_checkpoint_bytes: two bf16 arrays of floor(T / 64) + n_seqs
-    chunk-start states per head (rows and transposes), 256-byte rounded, for the
-    shapes the chunkwise backward serves; 0 elsewhere.  The checkpoint entry
-    points reject a null buffer and unserved shapes before touching the device."""
+    chunk-start states per head (rows and transposes) and the bf16 write keys
+    [T, H, dk], each 256-byte rounded (kw at least 256), for the shapes the
+    chunkwise backward serves; 0 elsewhere.  The checkpoint entry points reject
+    a null buffer and unserved shapes before touching the device."""
     from gated_delta_rule_prologue_amd import binding as B
     up = lambda x: (x + 255) // 256 * 256
     d = B.make_dims(8, 16384, 6, 128, 128, B.PRISM_BF16)
-    assert B.checkpoint_bytes(d) == 2 * up((16384 // 64 + 8) * 6 * 128 * 128 * 2)
-    assert B.checkpoint_bytes(B.make_dims(3, 100, 2, 64, 128, B.PRISM_BF16)) == 2 * up((1 + 3) * 2 * 64 * 128 * 2)
+    assert B.checkpoint_bytes(d) == 2 * up((16384 // 64 + 8) * 6 * 128 * 128 * 2) + up(16384 * 6 * 128 * 2)
+    assert B.checkpoint_bytes(B.make_dims(3, 100, 2, 64, 128, B.PRISM_BF16)) == \
+        2 * up((1 + 3) * 2 * 64 * 128 * 2) + up(100 * 2 * 64 * 2)
+    assert B.checkpoint_bytes(B.make_dims(2, 0, 1, 64, 64, B.PRISM_BF16)) == 2 * up(2 * 64 * 64 * 2) + 256
     assert B.checkpoint_bytes(B.make_dims(1, 100, 1, 64, 64, B.PRISM_F32)) == 0
     assert B.checkpoint_bytes(B.make_dims(1, 100, 1, 32, 64, B.PRISM_BF16)) == 0
     assert B.checkpoint_bytes(B.make_dims(0, 0, 1, 64, 64, B.PRISM_BF16)) == 0

@@ -73,15 +73,17 @@ def _go(inp, residual="linear", with_state=True, seed=4):
     off = max(_up(inp.total_tokens * inp.heads * inp.dk * 2), 256) + _up(nv * 20480)
     half = _up(nv * inp.dk * inp.dv * 2)
     rec = ws[off:off + 2 * half].cpu().numpy()
+    rec_kw = ws[:off].cpu().numpy()
     ref = oracle.bwd(inp, to_float(d_o_bits).astype(np.float64), dS_final=dsf, S_init=S0, residual=residual)
     return ((to_host(o1), to_host(s1)), (to_host(o2), to_host(s2)), host(gc), host(gr),
-            ck.cpu().numpy(), rec, half, ref)
+            ck.cpu().numpy(), rec, half, ref, rec_kw)
 
 
-def _check_checkpoints(inp, ck, rec, half):
+def _check_checkpoints(inp, ck, rec, half, rec_kw=None):
     """Both checkpoint arrays against the chunk-start states the recompute
     leaves in its workspace (rows, then transposes), on the slots that hold a
-    chunk; and the transposes against the rows."""
+    chunk; the transposes against the rows; and the stored write keys bit for
+    bit against the recompute's (the same prologue on the same inputs)."""
     H, dk, dv = inp.heads, inp.dk, inp.dv
     slots = _slots(inp)
     n = (inp.total_tokens // 64 + inp.n_seqs) * H * dk * dv
@@ -97,6 +99,9 @@ def _check_checkpoints(inp, ck, rec, half):
     if slots:
         t = rows[1].reshape(len(slots), H, dv, dk).transpose(0, 1, 3, 2).reshape(len(slots), H, dk * dv)
         assert np.array_equal(rows[0], t), "the two checkpoint arrays are not transposes"
+    if rec_kw is not None:
+        nkw = inp.total_tokens * H * dk * 2
+        assert np.array_equal(ck[2 * half:2 * half + nkw], rec_kw[:nkw]), "checkpointed kw differs"
 
 
 CASES = [
@@ -111,9 +116,9 @@ CASES = [
 def test_checkpointed_training_pair(w):
     inp = make_inputs(w)
     say(f"checkpointed pair {w}")
-    (o1, s1), (o2, s2), gc, gr, ck, rec, half, ref = _go(inp)
+    (o1, s1), (o2, s2), gc, gr, ck, rec, half, ref, rec_kw = _go(inp)
     assert np.array_equal(o1, o2) and np.array_equal(s1, s2), "fwd_ckpt outputs differ from fwd_resume"
-    _check_checkpoints(inp, ck, rec, half)
+    _check_checkpoints(inp, ck, rec, half, rec_kw)
     check(gc, ref, "bf16")
     for n in NAMES:
         if gc[n] is not None and gr[n] is not None:
@@ -123,8 +128,9 @@ def test_checkpointed_training_pair(w):
 def test_checkpointed_pair_gelu_without_state():
     from tests.test_gpu_gelu import amplify
     inp = amplify(make_inputs(W(dk=128, dv=128, L=5, lengths=(200, 65))))
-    (o1, s1), (o2, s2), gc, gr, ck, rec, half, ref = _go(inp, residual="gelu", with_state=False)
+    (o1, s1), (o2, s2), gc, gr, ck, rec, half, ref, rec_kw = _go(inp, residual="gelu", with_state=False)
     assert np.array_equal(o1, o2) and np.array_equal(s1, s2)
+    _check_checkpoints(inp, ck, rec, half, rec_kw)
     check(gc, ref, "bf16")
 
 
@@ -152,7 +158,8 @@ def test_checkpointed_pair_lm_layer():
     nv = (inp.total_tokens // 64 + inp.n_seqs) * inp.heads
     off = max(_up(inp.total_tokens * inp.heads * inp.dk * 2), 256) + _up(nv * 20480)
     half = _up(nv * inp.dk * inp.dv * 2)
-    _check_checkpoints(inp, ck.cpu().numpy(), ws[off:off + 2 * half].cpu().numpy(), half)
+    _check_checkpoints(inp, ck.cpu().numpy(), ws[off:off + 2 * half].cpu().numpy(), half,
+                       ws[:off].cpu().numpy())
     for n in NAMES:
         if gc[n] is None or gr[n] is None:
             continue
