@@ -325,11 +325,13 @@ def bwd_chunk_flops(w, T):
 
 
 def training_pair_bench(w, inp, dims, dev_copies, steps, warmup, bwd_args):
-    """Time a training step's pair: prism_fwd_ckpt (the forward, keeping every
-    chunk's start state) then prism_bwd_ckpt (every gradient, reading those
-    states instead of recomputing them), HIP events around each call; and the
-    same loop of prism_fwd then prism_bwd (recomputing them) on the same input
-    copies, so both pairs see the same cache state."""
+    """Time a training step's pair: prism_fwd_ckpt (the forward, keeping the
+    write keys and every chunk's start state) then prism_bwd_ckpt (every
+    gradient, reading those instead of recomputing them; the token-sized
+    gradients in bf16, as a bf16 training loop takes them), HIP events around
+    each call; and the same loop of prism_fwd then prism_bwd (recomputing,
+    fp32 gradients) on the same input copies, so both pairs see the same cache
+    state."""
     import ctypes
     import torch
     from gated_delta_rule_prologue_amd import binding
@@ -347,13 +349,13 @@ def training_pair_bench(w, inp, dims, dev_copies, steps, warmup, bwd_args):
                                    c["conv_w"], c["cu_seqlens"], w.L, checkpoints=c["ck"])
         out = binding.bwd(c["q"], c["k"], c["v"], c["u"], c["g"], c["b"], c["a"], c["h"],
                           c["conv_w"], c["cu_seqlens"], w.L, c["dO"], want_dS_init=True,
-                          workspace=c["bws"], checkpoints=c["ck"])
+                          workspace=c["bws"], checkpoints=c["ck"], grad_dtype=torch.bfloat16)
         fargs.append([ctypes.byref(dims)] + raw_args(
             c["q"], c["k"], c["v"], c["u"], c["g"], c["b"], c["a"], c["h"], c["conv_w"],
             c["cu_seqlens"], w.L, lin, None, o, S, c["ck"], None, 0, stream.cuda_stream))
         bargs.append([ctypes.byref(dims)] + raw_args(
             c["q"], c["k"], c["v"], c["u"], c["g"], c["b"], c["a"], c["h"], c["conv_w"],
-            c["cu_seqlens"], w.L, lin, None, c["dO"], None, out["q"], out["k"], out["v"],
+            c["cu_seqlens"], w.L, lin, binding.PRISM_BF16, None, c["dO"], None, out["q"], out["k"], out["v"],
             out["u"], out["g"], out["b"], out["a"], out["h"], out["conv_w"], out["S_init"],
             c["ck"], c["bws"], c["bws"].numel(), stream.cuda_stream))
         pargs.append([ctypes.byref(dims)] + raw_args(

@@ -1,8 +1,9 @@
 """torch.autograd wrapper of the operator: the forward runs prism_fwd_ckpt where
 the chunkwise backward serves the shape (keeping every chunk's start state for
-the backward, prism_bwd_ckpt), else prism_fwd_resume and prism_bwd_ex (all in
-libprism; nothing is computed here except casting the fp32 gradients to each
-input's dtype).
+the backward, prism_bwd_ckpt, which stores the token-sized gradients of bf16
+inputs in bf16 directly), else prism_fwd_resume and prism_bwd_ex (all in
+libprism; nothing is computed here except casting the remaining fp32 gradients
+to each input's dtype).
 
     o, S_final = prism(q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L,
                        S_init=None, residual="linear")
@@ -53,7 +54,8 @@ class PrismFunction(torch.autograd.Function):
         grads = None
         if ckpt is not None:
             try:
-                grads = binding.bwd(*args, checkpoints=ckpt, **kw)
+                gdt = torch.bfloat16 if q.dtype == torch.bfloat16 else None
+                grads = binding.bwd(*args, checkpoints=ckpt, grad_dtype=gdt, **kw)
             except binding.PrismError as err:        # PRISM_BWD_CHUNKED=0 since the forward
                 if err.status != binding.PRISM_EUNSUPPORTED:
                     raise

@@ -85,7 +85,7 @@ def lib():
         L.prism_checkpoint_bytes.restype = S
         L.prism_fwd_ckpt.argtypes = [D] + [P] * 10 + [I, I] + [P] * 5 + [S, P]
         L.prism_fwd_ckpt.restype = I
-        L.prism_bwd_ckpt.argtypes = [D] + [P] * 10 + [I, I] + [P] * 15 + [S, P]
+        L.prism_bwd_ckpt.argtypes = [D] + [P] * 10 + [I, I, I] + [P] * 15 + [S, P]
         L.prism_bwd_ckpt.restype = I
         L.prism_decode_step.restype = I
         L.prism_status_str.argtypes = [I]
@@ -393,11 +393,13 @@ def fwd_ckpt(q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L: int, S_init=None, o=
 
 def bwd(q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L: int, dO, dS_final=None, S_init=None,
         want_dS_init: bool = True, workspace=None, stream=None, residual="linear",
-        checkpoints=None) -> dict:
+        checkpoints=None, grad_dtype=None) -> dict:
     """Gradients of sum <dO, o> + <dS_final, S_final> (prism_bwd_ex, or
     prism_bwd_ckpt with the ``checkpoints`` of fwd_ckpt on the same inputs;
-    ``residual`` "linear" closed-form chain or "gelu"): a dict of fp32 tensors
-    q, k, v, u, a, h, g, b, conv_w and S_init (the last when ``want_dS_init``)."""
+    ``residual`` "linear" closed-form chain or "gelu"): a dict of tensors q, k,
+    v, u, a, h, g, b, conv_w and S_init (the last when ``want_dS_init``), all
+    fp32, except that with checkpoints ``grad_dtype=torch.bfloat16`` stores q,
+    k, v, u, a, h in bf16 (each the fp32 value rounded to nearest even)."""
     if residual not in RESIDUAL:
         raise ValueError(f"residual must be one of {sorted(RESIDUAL)}")
     d = _dims_of(q, v, cu_seqlens)
@@ -408,13 +410,18 @@ def bwd(q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L: int, dO, dS_final=None, S
     for name, x in (("dS_final", dS_final), ("S_init", S_init)):
         if x is not None:
             _expect(name, x, (n, H, dk, dv), torch.float32)
+    if grad_dtype not in (None, torch.float32, torch.bfloat16):
+        raise ValueError("grad_dtype must be torch.float32 or torch.bfloat16")
+    if grad_dtype == torch.bfloat16 and checkpoints is None:
+        raise ValueError("bf16 gradients need the checkpoints of fwd_ckpt")
     f32 = dict(dtype=torch.float32, device=q.device)
-    out = {"q": torch.empty((T, H, dk), **f32), "k": torch.empty((T, H, dk), **f32),
-           "v": torch.empty((T, H, dv), **f32), "g": torch.empty((T, H), **f32),
+    gt = dict(dtype=grad_dtype or torch.float32, device=q.device)
+    out = {"q": torch.empty((T, H, dk), **gt), "k": torch.empty((T, H, dk), **gt),
+           "v": torch.empty((T, H, dv), **gt), "g": torch.empty((T, H), **f32),
            "b": torch.empty((T, H), **f32), "conv_w": torch.empty((H, dk, 4), **f32),
            "S_init": torch.empty((n, H, dk, dv), **f32) if want_dS_init else None}
     for name in ("u", "a", "h"):
-        out[name] = torch.empty((T, H, L - 1, dk), **f32) if L > 1 else None
+        out[name] = torch.empty((T, H, L - 1, dk), **gt) if L > 1 else None
     need = int(lib().prism_bwd_workspace_bytes(ctypes.byref(d), int(L)))
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -423,16 +430,18 @@ def bwd(q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L: int, dO, dS_final=None, S
     grads = (_ptr(out["q"]), _ptr(out["k"]), _ptr(out["v"]), _ptr(out["u"]), _ptr(out["g"]),
              _ptr(out["b"]), _ptr(out["a"]), _ptr(out["h"]), _ptr(out["conv_w"]), _ptr(out["S_init"]))
     head = (ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(g), _ptr(b), _ptr(a), _ptr(h),
-            _ptr(conv_w), _ptr(cu_seqlens), int(L), RESIDUAL[residual], _ptr(S_init), _ptr(dO),
-            _ptr(dS_final))
+            _ptr(conv_w), _ptr(cu_seqlens), int(L), RESIDUAL[residual])
+    state = (_ptr(S_init), _ptr(dO), _ptr(dS_final))
     tail = (_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     if checkpoints is not None:
         cb = checkpoint_bytes(d)
         if checkpoints.numel() * checkpoints.element_size() < cb:
             raise ValueError(f"checkpoints need {cb} bytes")
-        _check("prism_bwd_ckpt", lib().prism_bwd_ckpt(*head, *grads, _ptr(checkpoints), *tail))
+        gd = PRISM_BF16 if grad_dtype == torch.bfloat16 else PRISM_F32
+        _check("prism_bwd_ckpt", lib().prism_bwd_ckpt(*head, gd, *state, *grads, _ptr(checkpoints),
+                                                       *tail))
     else:
-        _check("prism_bwd_ex", lib().prism_bwd_ex(*head, *grads, *tail))
+        _check("prism_bwd_ex", lib().prism_bwd_ex(*head, *state, *grads, *tail))
     return out
 
 

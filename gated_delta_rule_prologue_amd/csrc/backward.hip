@@ -548,13 +548,16 @@ __device__ __forceinline__ void wk_load(WkTok<T, L>& x, const WkSrc<T>& r, int t
     }
 }
 
-template <typename T, int L>
+// G: the storage type of dk, du, da, dh (fp32, or bf16 rounded to nearest even
+// from the same fp32 values).  dk_in holds the scan's part of dk in fp32; it is
+// dk itself when G is fp32 (hence no __restrict__ on either).
+template <typename T, int L, typename G>
 __global__ __launch_bounds__(256) void write_key_bwd_kernel(
     const T* __restrict__ k, const T* __restrict__ u, const T* __restrict__ a,
     const T* __restrict__ h, const T* __restrict__ b, const T* __restrict__ conv_w,
     const int32_t* __restrict__ cu, int n_seqs, int T_total, int H, int DK, bool gelu,
-    const float* __restrict__ dkw, float* __restrict__ dk, float* __restrict__ du,
-    float* __restrict__ da, float* __restrict__ dh, float* __restrict__ db,
+    const float* __restrict__ dkw, const float* dk_in, G* dk, G* __restrict__ du,
+    G* __restrict__ da, G* __restrict__ dh, float* __restrict__ db,
     float* __restrict__ dconv_part)
 {
     constexpr int NIT = kC + 3;                  // own tokens and the three after them
@@ -597,7 +600,7 @@ __global__ __launch_bounds__(256) void write_key_bwd_kernel(
         WkSrc<T> r;
         r.k = mk(k + rb * rowK, nr * rowK * sizeof(T));
         r.dkw = mk(dkw + rb * rowK, nr * rowK * 4);
-        r.dk = mk(dk + rb * rowK, nr * rowK * 4);
+        r.dk = mk(dk_in + rb * rowK, nr * rowK * 4);
         r.b = mk(b + (int64_t)rb * H, (int64_t)nr * H * sizeof(T));
         if constexpr (L > 1) {
             r.u = mk(u + rb * rowL, nr * rowL * sizeof(T));
@@ -697,9 +700,9 @@ __global__ __launch_bounds__(256) void write_key_bwd_kernel(
                     }
                     if (own) {
                         const int64_t sl = lb + (int64_t)(l - 1) * DK;
-                        du[sl] = g_kw * al * rr[l];
-                        da[sl] = dal;
-                        dh[sl] = dhl;
+                        du[sl] = from_f32<G>(g_kw * al * rr[l]);
+                        da[sl] = from_f32<G>(dal);
+                        dh[sl] = from_f32<G>(dhl);
                     }
                     dr_next = drl;
                 }
@@ -717,7 +720,7 @@ __global__ __launch_bounds__(256) void write_key_bwd_kernel(
                 for (int dd = 1; dd < 4; ++dd)
                     if (se[dd] == se[0])
                         acc += w[3 - dd] * dr[dd];
-                dk[((int64_t)tau * H + e) * DK + i] = dk_old + acc;
+                dk[((int64_t)tau * H + e) * DK + i] = from_f32<G>(dk_old + acc);
             }
         }
     }
@@ -795,16 +798,31 @@ int bwd_segments(int n_seqs, int heads, int dv)
 
 bool bwd_supported(int dk, int dv) { return (dk == 64 || dk == 128) && (dv == 64 || dv == 128); }
 
+template <typename T, int L, typename G>
+static void launch_wk_kernel(const BwdArgs& p, const float* dkw, float* part, int64_t nb, hipStream_t s)
+{
+    // with bf16 gradients gk, gu, ga, gh hold bf16 and the scan's fp32 part of dk
+    // is in gk_part; otherwise gk holds that part on entry
+    const float* dk_in = p.grad_bf16 ? p.gk_part : p.gk;
+    hipLaunchKernelGGL((bwd::write_key_bwd_kernel<T, L, G>), dim3((unsigned)(nb * p.heads * (p.dk / 64))),
+                       dim3(256), 0, s, (const T*)p.k, (const T*)p.u, (const T*)p.a, (const T*)p.h,
+                       (const T*)p.b, (const T*)p.conv_w, p.cu_seqlens, p.n_seqs, p.total_tokens,
+                       p.heads, p.dk, p.gelu, dkw, dk_in, reinterpret_cast<G*>(p.gk),
+                       reinterpret_cast<G*>(p.gu), reinterpret_cast<G*>(p.ga), reinterpret_cast<G*>(p.gh),
+                       p.gb, part);
+}
+
 template <typename T, int L>
 static hipError_t launch_wk_L(const BwdArgs& p, const float* dkw, float* part, hipStream_t s)
 {
     const int64_t nb = (p.total_tokens + bwd::kWkBlock - 1) / bwd::kWkBlock;
     const int n = p.heads * p.dk * 4;
-    if (nb > 0)
-        hipLaunchKernelGGL((bwd::write_key_bwd_kernel<T, L>), dim3((unsigned)(nb * p.heads * (p.dk / 64))),
-                           dim3(256), 0, s, (const T*)p.k, (const T*)p.u, (const T*)p.a, (const T*)p.h,
-                           (const T*)p.b, (const T*)p.conv_w, p.cu_seqlens, p.n_seqs, p.total_tokens,
-                           p.heads, p.dk, p.gelu, dkw, p.gk, p.gu, p.ga, p.gh, p.gb, part);
+    if (nb > 0) {
+        if (p.grad_bf16)
+            launch_wk_kernel<T, L, uint16_t>(p, dkw, part, nb, s);
+        else
+            launch_wk_kernel<T, L, float>(p, dkw, part, nb, s);
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || n == 0)
         return err;
@@ -894,7 +912,7 @@ static hipError_t launch_bwd_T(const BwdArgs& p, hipStream_t s)
 
 hipError_t launch_write_key_bwd(const BwdArgs& p, const float* dkw, float* part, hipStream_t s)
 {
-    if (!bwd_supported(p.dk, p.dv) || p.L < 1 || p.L > 16)
+    if (!bwd_supported(p.dk, p.dv) || p.L < 1 || p.L > 16 || (p.grad_bf16 && (!p.bf16 || !p.gk_part)))
         return hipErrorInvalidValue;
     return p.bf16 ? launch_wk<uint16_t>(p, dkw, part, s) : launch_wk<float>(p, dkw, part, s);
 }

@@ -533,14 +533,14 @@ struct LayG {
 // 16 (w & 3) .., value (or key) column half w >> 2; in the block-pair stage,
 // pairs w and w + 8.  The stored T, A_kkw, -A_qk and A_qkw tiles are dead after
 // dV, and their LDS holds M_qk, M_qkw, M_kk and M_kkw from there on.
-template <int D, int DV>
+template <int D, int DV, typename GT>
 __global__ __launch_bounds__(kNW * 64) void bwd_grads_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ kw,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO, const uint16_t* __restrict__ g,
     const uint16_t* __restrict__ b, const int32_t* __restrict__ cu, int n_seqs, int H,
     const uint16_t* __restrict__ mats, const uint16_t* __restrict__ ck, const uint16_t* __restrict__ ckT,
-    const uint16_t* __restrict__ dck, const uint16_t* __restrict__ dckT, float* __restrict__ gq,
-    float* __restrict__ gk, float* __restrict__ gkw, float* __restrict__ gv, float* __restrict__ gg,
+    const uint16_t* __restrict__ dck, const uint16_t* __restrict__ dckT, GT* __restrict__ gq,
+    float* __restrict__ gk, float* __restrict__ gkw, GT* __restrict__ gv, float* __restrict__ gg,
     float* __restrict__ gb)
 {
     using Ly = LayG<D, DV>;
@@ -798,7 +798,7 @@ __global__ __launch_bounds__(kNW * 64) void bwd_grads_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 if (row_ok(r))
-                    gv[gidx(r, c.rowV, DV, v0c + n * 16 + li)] = acc[n][r];
+                    gv[gidx(r, c.rowV, DV, v0c + n * 16 + li)] = from_f32<GT>(acc[n][r]);
     }
 
     // the four matrices are dead from here: their LDS holds M
@@ -954,7 +954,7 @@ __global__ __launch_bounds__(kNW * 64) void bwd_grads_kernel(
         for (int r = 0; r < 4; ++r) {
             if (row_ok(r)) {
                 const int64_t o = gidx(r, c.rowQK, D, col);
-                gq[o] = aq[r];
+                gq[o] = from_f32<GT>(aq[r]);
                 gk[o] = ak[r];
                 gkw[o] = aw[r];
             }
@@ -1012,18 +1012,28 @@ __global__ __launch_bounds__(kNW * 64) void bwd_grads_kernel(
 
 using bwdc::kC;
 
+template <int D, int DV, typename G>
+static void launch_g_TG(const ScanArgs& p, const BwdChunkBufs& w, int64_t blocks, hipStream_t stream)
+{
+    hipLaunchKernelGGL((bwdc::bwd_grads_kernel<D, DV, G>), dim3((unsigned)blocks), dim3(bwdc::kNW * 64), 0,
+                       stream, (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.kw,
+                       (const uint16_t*)p.v, (const uint16_t*)w.dO, (const uint16_t*)p.g,
+                       (const uint16_t*)p.b, p.cu_seqlens, p.n_seqs, p.heads, (const uint16_t*)w.mats,
+                       (const uint16_t*)w.ck, (const uint16_t*)w.ckT, (const uint16_t*)w.dck,
+                       (const uint16_t*)w.dckT, static_cast<G*>(w.gq), w.gk, w.gkw, static_cast<G*>(w.gv),
+                       w.gg, w.gb);
+}
+
 template <int D, int DV>
 static hipError_t launch_g_T(const ScanArgs& p, const BwdChunkBufs& w, hipStream_t stream)
 {
     const int64_t blocks = (int64_t)(p.total_tokens / kC + p.n_seqs) * p.heads;
     if (blocks == 0)
         return hipSuccess;
-    hipLaunchKernelGGL((bwdc::bwd_grads_kernel<D, DV>), dim3((unsigned)blocks), dim3(bwdc::kNW * 64), 0, stream,
-                       (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.kw,
-                       (const uint16_t*)p.v, (const uint16_t*)w.dO, (const uint16_t*)p.g,
-                       (const uint16_t*)p.b, p.cu_seqlens, p.n_seqs, p.heads, (const uint16_t*)w.mats,
-                       (const uint16_t*)w.ck, (const uint16_t*)w.ckT, (const uint16_t*)w.dck,
-                       (const uint16_t*)w.dckT, w.gq, w.gk, w.gkw, w.gv, w.gg, w.gb);
+    if (w.grad_bf16)
+        launch_g_TG<D, DV, uint16_t>(p, w, blocks, stream);
+    else
+        launch_g_TG<D, DV, float>(p, w, blocks, stream);
     return hipGetLastError();
 }
 

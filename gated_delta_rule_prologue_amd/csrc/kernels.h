@@ -84,6 +84,10 @@ struct BwdArgs {
     const float* s_init;            // or null (zero)
     const float* ds_final;          // or null (zero)
     float *gq, *gk, *gv, *gu, *ga, *gh, *gg, *gb, *gconv;
+    // the chunkwise path only: gq, gk, gv, gu, ga, gh hold bf16 (round to nearest
+    // even) instead of fp32, and the scan's fp32 part of dk is in gk_part
+    bool grad_bf16 = false;
+    const float* gk_part = nullptr;
     float* gs_init;                 // or null (not written)
     float* ws;                      // bwd_workspace_floats(...) floats
 };
@@ -97,11 +101,14 @@ hipError_t launch_bwd_state(const ScanArgs& p, const void* dO, const void* mats,
                             void* dck, void* dckT, float* dS_init, hipStream_t stream);
 struct BwdChunkBufs {
     const void *dO, *mats, *ck, *ckT, *dck, *dckT;
-    float *gq, *gk, *gkw, *gv, *gg, *gb;
+    void *gq, *gv;                               // fp32, or bf16 when grad_bf16
+    float *gk, *gkw, *gg, *gb;                   // fp32 (gk: the scan's part of dk)
+    bool grad_bf16 = false;
 };
 // The chunk-parallel gradients: every gradient of the scan's inputs (q, k, kw,
 // v, g, b) from the checkpoints, in one launch; p.kw holds the write keys.
-// Stores (no accumulation): dq, dk, dkw, dv, dg, db are written whole.
+// Stores (no accumulation): dq, dk, dkw, dv, dg, db are written whole; dq and dv
+// in bf16 (round to nearest even) when w.grad_bf16, the rest in fp32.
 hipError_t launch_bwd_grads(const ScanArgs& p, const BwdChunkBufs& w, hipStream_t stream);
 
 // The write-key part of the backward pass alone (backward.hip): from dkw (fp32

@@ -559,16 +559,17 @@ namespace {
 
 // The backward pass; with ckpt (prism_fwd_ckpt's chunk-start states and write
 // keys of the same inputs) the chunkwise form reads them instead of recomputing
-// them.
+// them, and may store dq, dk, dv, du, da, dh in bf16 (grad_dtype PRISM_BF16).
 prism_status bwd_impl(const prism_dims* d, const void* q, const void* k, const void* v,
                       const void* u, const void* g, const void* b, const void* a, const void* h,
                       const void* conv_w, const int32_t* cu_seqlens, int L, int residual,
-                      const float* S_init, const void* dO, const float* dS_final, float* dq,
-                      float* dk, float* dv, float* du, float* dg, float* db, float* da,
-                      float* dh, float* dconv_w, float* dS_init, const void* ckpt, void* workspace,
+                      int grad_dtype, const float* S_init, const void* dO, const float* dS_final,
+                      void* dq, void* dk, void* dv, void* du, float* dg, float* db, void* da,
+                      void* dh, float* dconv_w, float* dS_init, const void* ckpt, void* workspace,
                       size_t workspace_bytes, void* stream)
 {
-    if (!dims_ok(d) || L < 1 || L > PRISM_MAX_LEVELS || !residual_ok(residual))
+    if (!dims_ok(d) || L < 1 || L > PRISM_MAX_LEVELS || !residual_ok(residual) ||
+        (grad_dtype != PRISM_F32 && grad_dtype != PRISM_BF16))
         return PRISM_EINVAL;
     if (!tok_ok(d, q) || !tok_ok(d, k) || !tok_ok(d, v) || !tok_ok(d, g) || !tok_ok(d, b) ||
         !tok_ok(d, dO) || !ptr_ok(conv_w) || !ptr_ok(cu_seqlens) || !tok_ok(d, dq) ||
@@ -583,6 +584,11 @@ prism_status bwd_impl(const prism_dims* d, const void* q, const void* k, const v
     if (workspace_bytes < prism_bwd_workspace_bytes(d, L))
         return PRISM_EINVAL;
     if (ckpt && !use_bwd_chunked(d))             // checkpoints serve the chunkwise form only
+        return PRISM_EUNSUPPORTED;
+    // bf16 gradients: the chunkwise form with checkpoints, whose unused state
+    // region of the workspace then holds the scan's fp32 part of dk
+    const bool grad_bf16 = grad_dtype == PRISM_BF16;
+    if (grad_bf16 && !ckpt)
         return PRISM_EUNSUPPORTED;
     // the write keys: prism_fwd_ckpt's, after the two state arrays, or recomputed
     // into the workspace
@@ -609,7 +615,10 @@ prism_status bwd_impl(const prism_dims* d, const void* q, const void* k, const v
     p.cu_seqlens = cu_seqlens;
     p.s_init = S_init;
     p.ds_final = dS_final;
-    p.gq = dq; p.gk = dk; p.gv = dv; p.gu = du; p.ga = da; p.gh = dh; p.gg = dg; p.gb = db;
+    // typed fp32 here; they hold bf16 when grad_bf16 (the chunkwise path only)
+    p.gq = static_cast<float*>(dq); p.gk = static_cast<float*>(dk); p.gv = static_cast<float*>(dv);
+    p.gu = static_cast<float*>(du); p.ga = static_cast<float*>(da); p.gh = static_cast<float*>(dh);
+    p.gg = dg; p.gb = db;
     p.gconv = dconv_w;
     p.gs_init = dS_init;
     unsigned char* ws = static_cast<unsigned char*>(workspace);
@@ -641,8 +650,13 @@ prism_status bwd_impl(const prism_dims* d, const void* q, const void* k, const v
     cb.ck = ckpt ? (const void*)ckb : (const void*)(ws + w.ck);
     cb.ckT = ckpt ? (const void*)(ckb + checkpoint_half(d)) : (const void*)(ws + w.ckT);
     cb.dck = ws + w.dck; cb.dckT = ws + w.dckT;
-    cb.gq = dq; cb.gk = dk; cb.gkw = reinterpret_cast<float*>(ws + w.dkw); cb.gv = dv;
+    cb.gq = dq; cb.gv = dv;
+    cb.gk = grad_bf16 ? reinterpret_cast<float*>(ws + w.ck) : static_cast<float*>(dk);
+    cb.gkw = reinterpret_cast<float*>(ws + w.dkw);
     cb.gg = dg; cb.gb = db;
+    cb.grad_bf16 = grad_bf16;
+    p.grad_bf16 = grad_bf16;
+    p.gk_part = cb.gk;
     const hipStream_t s = (hipStream_t)stream;
     hipError_t e = prism::launch_gram(sp, ws + w.mats, s);
     if (e == hipSuccess && !ckpt)
@@ -728,18 +742,19 @@ prism_status prism_fwd_ckpt(const prism_dims* d, const void* q, const void* k, c
 prism_status prism_bwd_ckpt(const prism_dims* d, const void* q, const void* k, const void* v,
                             const void* u, const void* g, const void* b, const void* a, const void* h,
                             const void* conv_w, const int32_t* cu_seqlens, int L, int residual,
-                            const float* S_init, const void* dO, const float* dS_final, float* dq,
-                            float* dk, float* dv, float* du, float* dg, float* db, float* da,
-                            float* dh, float* dconv_w, float* dS_init, const void* checkpoints,
-                            void* workspace, size_t workspace_bytes, void* stream)
+                            int grad_dtype, const float* S_init, const void* dO,
+                            const float* dS_final, void* dq, void* dk, void* dv, void* du,
+                            float* dg, float* db, void* da, void* dh, float* dconv_w,
+                            float* dS_init, const void* checkpoints, void* workspace,
+                            size_t workspace_bytes, void* stream)
 {
     if (!ptr_ok(checkpoints))
         return PRISM_EINVAL;
     if (checkpoint_half(d) == 0)
         return PRISM_EUNSUPPORTED;
-    return bwd_impl(d, q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L, residual, S_init, dO, dS_final,
-                    dq, dk, dv, du, dg, db, da, dh, dconv_w, dS_init, checkpoints, workspace,
-                    workspace_bytes, stream);
+    return bwd_impl(d, q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L, residual, grad_dtype, S_init,
+                    dO, dS_final, dq, dk, dv, du, dg, db, da, dh, dconv_w, dS_init, checkpoints,
+                    workspace, workspace_bytes, stream);
 }
 
 prism_status prism_bwd_ex(const prism_dims* d, const void* q, const void* k, const void* v,
@@ -750,8 +765,8 @@ prism_status prism_bwd_ex(const prism_dims* d, const void* q, const void* k, con
                           float* dh, float* dconv_w, float* dS_init, void* workspace,
                           size_t workspace_bytes, void* stream)
 {
-    return bwd_impl(d, q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L, residual, S_init, dO, dS_final,
-                    dq, dk, dv, du, dg, db, da, dh, dconv_w, dS_init, nullptr, workspace,
+    return bwd_impl(d, q, k, v, u, g, b, a, h, conv_w, cu_seqlens, L, residual, PRISM_F32, S_init, dO,
+                    dS_final, dq, dk, dv, du, dg, db, da, dh, dconv_w, dS_init, nullptr, workspace,
                     workspace_bytes, stream);
 }
 

@@ -388,18 +388,23 @@ prism_status prism_fwd_ckpt(const prism_dims* d,
  * `checkpoints` (written by prism_fwd_ckpt for the same inputs, S_init and
  * residual chain; read only) and the write keys read from there too, instead
  * of recomputed: two launches fewer (the prologue and the state recompute).
+ * grad_dtype (a prism_dtype) is the storage type of the six token-sized
+ * gradients dq, dk, dv [T, H, d] and du, da, dh [T, H, L-1, dk]: PRISM_F32, or
+ * PRISM_BF16 for each of them rounded to nearest even from the fp32 value the
+ * PRISM_F32 call stores (half the bytes written, and no cast for a bf16
+ * training loop).  dg, db, dconv_w and dS_init are fp32 either way.
  * Arguments, layouts, workspace and errors otherwise as in prism_bwd_ex;
  * PRISM_EUNSUPPORTED where the chunkwise form does not run (shapes with no
  * checkpoints, PRISM_BWD_CHUNKED=0); PRISM_EINVAL for a null checkpoint
- * buffer. */
+ * buffer or another grad_dtype. */
 prism_status prism_bwd_ckpt(const prism_dims* d,
                             const void* q, const void* k, const void* v,
                             const void* u, const void* g, const void* b,
                             const void* a, const void* h, const void* conv_w,
-                            const int32_t* cu_seqlens, int L, int residual, const float* S_init,
-                            const void* dO, const float* dS_final,
-                            float* dq, float* dk, float* dv, float* du, float* dg, float* db,
-                            float* da, float* dh, float* dconv_w, float* dS_init,
+                            const int32_t* cu_seqlens, int L, int residual, int grad_dtype,
+                            const float* S_init, const void* dO, const float* dS_final,
+                            void* dq, void* dk, void* dv, void* du, float* dg, float* db,
+                            void* da, void* dh, float* dconv_w, float* dS_init,
                             const void* checkpoints, void* workspace, size_t workspace_bytes,
                             void* stream);
 

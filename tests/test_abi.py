@@ -323,9 +323,11 @@ def test_checkpoint_bytes_and_argument_checks(lib):
     assert B.checkpoint_bytes(B.make_dims(0, 0, 1, 64, 64, B.PRISM_BF16)) == 0
     fwd = lambda d, ck: lib.prism_fwd_ckpt(ctypes.byref(d), *([FAKE] * 10), 2, 0, None, FAKE, FAKE, ck,
                                            FAKE, 1 << 30, None)
-    bwd = lambda d, ck: lib.prism_bwd_ckpt(ctypes.byref(d), *([FAKE] * 10), 2, 0, None, FAKE, None,
-                                           *([FAKE] * 9), None, ck, FAKE, 1 << 30, None)
+    bwd = lambda d, ck, gd=B.PRISM_F32: lib.prism_bwd_ckpt(ctypes.byref(d), *([FAKE] * 10), 2, 0, gd, None,
+                                                           FAKE, None, *([FAKE] * 9), None, ck, FAKE,
+                                                           1 << 30, None)
     ok = B.make_dims(2, 100, 2, 64, 64, B.PRISM_BF16)
     assert fwd(ok, None) == B.PRISM_EINVAL and bwd(ok, None) == B.PRISM_EINVAL
+    assert bwd(ok, FAKE, 2) == B.PRISM_EINVAL and bwd(ok, FAKE, -1) == B.PRISM_EINVAL
     f32 = B.make_dims(2, 100, 2, 64, 64, B.PRISM_F32)
     assert fwd(f32, FAKE) == B.PRISM_EUNSUPPORTED and bwd(f32, FAKE) == B.PRISM_EUNSUPPORTED

@@ -166,3 +166,80 @@ def test_checkpointed_pair_lm_layer():
         err = max_rel(to_host(gc[n]), to_host(gr[n]))
         say(f"  lm-130m-layer d{n}: checkpoints vs recompute {err:.3e}")
         assert err <= TOL["bf16"], (n, err)
+
+
+# ----------------------------------------------------------------------------- bf16 gradients
+BF16_GRADS = ("q", "k", "v", "u", "a", "h")
+
+
+def _bf16_and_f32_grads(inp, residual="linear", with_state=True, seed=6):
+    """The checkpoint backward on the same inputs and checkpoints, once with
+    fp32 and once with bf16 token-sized gradients."""
+    import torch
+    from gated_delta_rule_prologue_amd import binding
+    from tests.test_gpu_state import dev_tensor, start_state
+    dev = binding.to_device(inp)
+    rng = np.random.default_rng(seed)
+    d_o_bits = f32_to_bf16_bits(rng.standard_normal((inp.total_tokens, inp.heads, inp.dv)).astype(np.float32))
+    d_o = dev_tensor(d_o_bits)
+    S0 = start_state(inp) if with_state else None
+    dsf = rng.standard_normal((inp.n_seqs, inp.heads, inp.dk, inp.dv)).astype(np.float32) if with_state else None
+    S0_t = dev_tensor(S0) if with_state else None
+    dsf_t = dev_tensor(dsf) if with_state else None
+    args = (dev["q"], dev["k"], dev["v"], dev["u"], dev["g"], dev["b"], dev["a"], dev["h"],
+            dev["conv_w"], dev["cu_seqlens"], inp.L)
+    _, _, ck = binding.fwd_ckpt(*args, S_init=S0_t, residual=residual)
+    kw = dict(dS_final=dsf_t, S_init=S0_t, residual=residual, checkpoints=ck)
+    g32 = binding.bwd(*args, d_o, **kw)
+    g16 = binding.bwd(*args, d_o, grad_dtype=torch.bfloat16, **kw)
+    torch.cuda.synchronize()
+    return g32, g16, d_o_bits, S0, dsf
+
+
+def _check_rounded(inp, g32, g16):
+    """Each bf16 gradient is its fp32 twin rounded to nearest even, bit for bit
+    (both come from the same fp32 arithmetic); the fp32-only gradients agree
+    up to the arbitrary order of the LDS sums behind dg and db."""
+    import torch
+    for n in BF16_GRADS:
+        if g32[n] is None:
+            assert g16[n] is None
+            continue
+        assert g16[n].dtype == torch.bfloat16 and g16[n].shape == g32[n].shape
+        got = g16[n].view(torch.int16).cpu().numpy().view(np.uint16)
+        want = f32_to_bf16_bits(g32[n].cpu().numpy())
+        bad = int(np.count_nonzero(got != want))
+        say(f"  d{n}: {got.size} bf16 elements, {bad} differ from the rounded fp32 gradient")
+        assert bad == 0, n
+    for n in ("g", "b", "conv_w", "S_init"):
+        if g32[n] is not None:
+            assert g16[n].dtype == torch.float32
+            assert max_rel(to_host(g16[n]), to_host(g32[n])) <= 1e-5, n
+
+
+@pytest.mark.parametrize("w", CASES[:2] + CASES[3:], ids=lambda w: f"dk{w.dk}-dv{w.dv}-L{w.L}")
+def test_bf16_gradients_are_the_rounded_fp32_ones(w):
+    inp = make_inputs(w)
+    say(f"bf16 gradients {w}")
+    g32, g16, d_o_bits, S0, dsf = _bf16_and_f32_grads(inp)
+    _check_rounded(inp, g32, g16)
+    ref = oracle.bwd(inp, to_float(d_o_bits).astype(np.float64), dS_final=dsf, S_init=S0)
+    check({n: (to_host(g16[n]) if g16[n] is not None else None) for n in NAMES}, ref, "bf16")
+
+
+def test_bf16_gradients_gelu_one_level():
+    """The GELU chain, and L = 1 (no u, a, h: only dq, dk, dv in bf16)."""
+    from tests.test_gpu_gelu import amplify
+    inp = amplify(make_inputs(W(dk=128, dv=128, L=5, lengths=(200, 65))))
+    g32, g16, *_ = _bf16_and_f32_grads(inp, residual="gelu", with_state=False)
+    _check_rounded(inp, g32, g16)
+    inp = make_inputs(CASES[2])
+    g32, g16, *_ = _bf16_and_f32_grads(inp)
+    _check_rounded(inp, g32, g16)
+
+
+def test_bf16_gradients_lm_layer():
+    """The LM layer at full size (B=8, T=2048, H=6, d=128, L=4)."""
+    inp = make_inputs(BY_NAME["lm-130m-layer"])
+    g32, g16, *_ = _bf16_and_f32_grads(inp, with_state=False)
+    _check_rounded(inp, g32, g16)
