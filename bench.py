@@ -184,6 +184,70 @@ def decode_bytes(n, H, dk, dv, L, esize):
     return chains * per + H * 4 * dk * esize
 
 
+_HIP = None
+
+
+def _hip_runtime():
+    """The HIP runtime this process already runs on (the libamdhip64 torch
+    loaded, which libprism's calls resolve to as well), bound through ctypes."""
+    global _HIP
+    if _HIP is None:
+        import ctypes
+        import torch
+        torch.cuda.init()
+        path = next(line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64" in line)
+        h = ctypes.CDLL(path)
+        h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        for f in (h.hipEventCreateWithFlags, h.hipEventRecord, h.hipEventElapsedTime, h.hipEventDestroy):
+            f.restype = ctypes.c_int
+        _HIP = h
+    return _HIP
+
+
+class TimingEvent:
+    """A HIP event for timing only, created with hipEventDisableSystemFence: its
+    record makes no system-scope release, so it neither writes back nor
+    invalidates the caches between the launches it brackets (a default event
+    does both, which lengthens the interval it closes and slows the launch
+    after it).  Same use as TimingEvent(): record on
+    the launch stream, synchronize, then elapsed_time in ms."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        self._h = _hip_runtime()
+        self._e = ctypes.c_void_p()
+        st = self._h.hipEventCreateWithFlags(ctypes.byref(self._e), self.DISABLE_SYSTEM_FENCE)
+        if st != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({st})")
+
+    def record(self, stream):
+        st = self._h.hipEventRecord(self._e, ctypes_stream(stream))
+        if st != 0:
+            raise RuntimeError(f"hipEventRecord failed ({st})")
+
+    def elapsed_time(self, end):
+        import ctypes
+        ms = ctypes.c_float()
+        st = self._h.hipEventElapsedTime(ctypes.byref(ms), self._e, end._e)
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({st})")
+        return ms.value
+
+    def __del__(self):
+        if getattr(self, "_e", None) is not None and self._e.value:
+            self._h.hipEventDestroy(self._e)
+
+
+def ctypes_stream(stream):
+    """A torch stream (or None: the current one) as the hipStream_t value."""
+    import torch
+    return (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
+
+
 def raw_args(*xs):
     """Arguments of one C-ABI call, marshalled once: tensors as device pointers.
     A timed loop of short kernels calls the library with these directly, so
@@ -233,7 +297,7 @@ def decode_bench(steps, warmup, with_oracle=False):
         for i in range(warmup):
             lib.prism_decode_step(*args[i % ncopy])
         torch.cuda.synchronize()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        ev = [[TimingEvent() for _ in range(2)] for _ in range(steps)]
         status = 0
         t0 = time.perf_counter()
         for i in range(steps):
@@ -262,7 +326,7 @@ def decode_bench(steps, warmup, with_oracle=False):
                 lib.prism_decode_step(*(args[i % ncopy][:-1] + [cap]))
         graph.replay()
         torch.cuda.synchronize()
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0, g1 = TimingEvent(), TimingEvent()
         g0.record(stream)
         for _ in range(R):
             graph.replay()
@@ -367,7 +431,7 @@ def training_pair_bench(w, inp, dims, dev_copies, steps, warmup, bwd_args):
             fwd(*fa[i % len(fa)])
             bwd(*ba[i % len(ba)])
         torch.cuda.synchronize()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        ev = [[TimingEvent() for _ in range(3)] for _ in range(steps)]
         status = 0
         t0 = time.perf_counter()
         for i in range(steps):
@@ -418,7 +482,7 @@ def bwd_bench(w, inp, dev_copies, steps, warmup, with_oracle=False):
     for i in range(warmup):
         lib.prism_bwd(*args[i % len(args)])
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    ev = [[TimingEvent() for _ in range(2)] for _ in range(steps)]
     status = 0
     t0 = time.perf_counter()
     for i in range(steps):
@@ -549,13 +613,14 @@ def main():
                                                       split_bytes, stream.cuda_stream))
 
     K = args.steps
-    # Launch durations come from HIP events on the launch stream, recorded
-    # around both launches of every EV_EVERY-th step of the timed region: each
-    # event is a packet of its own in the queue (about 2-3 us of gap apiece), so
-    # sampling keeps the instrumentation from weighing on the timed throughput.
+    # Launch durations come from HIP events on the launch stream (TimingEvent:
+    # no cache writeback or invalidation at a record), recorded around both
+    # launches of every EV_EVERY-th step of the timed region: each event is
+    # still a packet of its own in the queue, so sampling keeps the
+    # instrumentation from weighing on the timed throughput.
     EV_EVERY = 4
     sampled = [i for i in range(K) if i % EV_EVERY == 0]
-    ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
+    ev = {i: [TimingEvent() for _ in range(3)] for i in sampled}
     torch.cuda.synchronize()
     status = 0
     t0 = time.perf_counter()
@@ -594,7 +659,7 @@ def main():
         gargs.append([ctypes.byref(dims)] + raw_args(c["k"], c["u"], c["a"], c["h"], c["b"],
                                                       c["conv_w"], None, c["cu_seqlens"], w.L, 1,
                                                       c["kw"], stream.cuda_stream))
-    gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    gev = [[TimingEvent() for _ in range(2)] for _ in range(K)]
     status = 0
     for i in range(K):
         gev[i][0].record(stream)
