@@ -227,6 +227,26 @@ def test_bf16_gradients_are_the_rounded_fp32_ones(w):
     check({n: (to_host(g16[n]) if g16[n] is not None else None) for n in NAMES}, ref, "bf16")
 
 
+EDGE = [
+    # the most levels, empty and one-token sequences, a chunk of 63 and of 65 tokens
+    W(dk=64, dv=128, L=16, lengths=(1, 0, 200, 63, 65)),
+    # whole chunks only, five heads, two levels
+    W(dk=128, dv=64, L=2, lengths=(64, 64, 128), H=5),
+    # forget gates near zero: the in-chunk decays underflow fp32
+    W(dk=64, dv=64, L=6, lengths=(300, 17), g_mu=-3.0),
+]
+
+
+@pytest.mark.parametrize("w", EDGE, ids=["L16-ragged", "H5-whole-chunks", "strong-decay"])
+def test_bf16_gradients_edge_shapes(w):
+    inp = make_inputs(w)
+    say(f"bf16 gradients, edge shape {w}")
+    g32, g16, d_o_bits, S0, dsf = _bf16_and_f32_grads(inp)
+    _check_rounded(inp, g32, g16)
+    ref = oracle.bwd(inp, to_float(d_o_bits).astype(np.float64), dS_final=dsf, S_init=S0)
+    check({n: (to_host(g16[n]) if g16[n] is not None else None) for n in NAMES}, ref, "bf16")
+
+
 def test_bf16_gradients_gelu_one_level():
     """The GELU chain, and L = 1 (no u, a, h: only dq, dk, dv in bf16)."""
     from tests.test_gpu_gelu import amplify
