@@ -263,3 +263,35 @@ def test_bf16_gradients_lm_layer():
     inp = make_inputs(BY_NAME["lm-130m-layer"])
     g32, g16, *_ = _bf16_and_f32_grads(inp, with_state=False)
     _check_rounded(inp, g32, g16)
+
+
+@pytest.mark.parametrize("name", ["recsys-history", "varlen-histories"])
+def test_checkpointed_pair_full_size(name):
+    """The recommendation histories (B=64, T=1024, H=4, d=64, L=4) and the
+    variable-length batch (512 sequences, H=8, d=64, L=8) at full size: the
+    checkpoint backward against the recomputing one on every gradient, and its
+    bf16 gradients against its fp32 ones bit for bit."""
+    import torch
+    from gated_delta_rule_prologue_amd import binding
+    inp = make_inputs(BY_NAME[name])
+    say(f"{name}: T={inp.total_tokens} chains={inp.n_seqs * inp.heads}")
+    dev = binding.to_device(inp)
+    rng = np.random.default_rng(8)
+    from tests.test_gpu_state import dev_tensor
+    d_o = dev_tensor(f32_to_bf16_bits(rng.standard_normal((inp.total_tokens, inp.heads, inp.dv)).astype(np.float32)))
+    args = (dev["q"], dev["k"], dev["v"], dev["u"], dev["g"], dev["b"], dev["a"], dev["h"],
+            dev["conv_w"], dev["cu_seqlens"], inp.L)
+    o1, s1, ck = binding.fwd_ckpt(*args)
+    o2, s2 = binding.fwd(*args)
+    assert np.array_equal(to_host(o1), to_host(o2)) and np.array_equal(to_host(s1), to_host(s2))
+    gc = binding.bwd(*args, d_o, checkpoints=ck, want_dS_init=False)
+    gb = binding.bwd(*args, d_o, checkpoints=ck, want_dS_init=False, grad_dtype=torch.bfloat16)
+    gr = binding.bwd(*args, d_o, want_dS_init=False)
+    torch.cuda.synchronize()
+    for n in NAMES:
+        if gc[n] is None or gr[n] is None:
+            continue
+        err = max_rel(to_host(gc[n]), to_host(gr[n]))
+        say(f"  {name} d{n}: checkpoints vs recompute {err:.3e}")
+        assert err <= TOL["bf16"], (n, err)
+    _check_rounded(inp, gc, gb)
