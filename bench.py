@@ -22,7 +22,8 @@ each against its HBM roofline, and a "backward" object: prism_bwd (the
 gradients of every input for an upstream dO) on the same workload, with a
 "training_pair" inside it where the chunkwise backward serves the shape:
 prism_fwd_ckpt then prism_bwd_ckpt, the forward keeping every chunk's start
-state for the backward.  Both are measured after the forward pass and are not
+state for the backward (and the same step through the torch.autograd
+wrapper).  Both are measured after the forward pass and are not
 part of "value".
 """
 from __future__ import annotations
@@ -449,8 +450,30 @@ def training_pair_bench(w, inp, dims, dev_copies, steps, warmup, bwd_args):
 
     tps, f_us, b_us = pair(lib.prism_fwd_ckpt, lib.prism_bwd_ckpt, fargs, bargs)
     _, rf_us, rb_us = pair(lib.prism_fwd, lib.prism_bwd, pargs, bwd_args)
+
+    # the same step through the torch.autograd wrapper (which makes the same two
+    # calls, plus its own allocations and the casts of the fp32 gradients dg, db,
+    # dconv_w), gradients of <dO, o> with respect to every input
+    from gated_delta_rule_prologue_amd.autograd import prism
+    names = ("q", "k", "v", "u", "g", "b", "a", "h", "conv_w")
+    leaves = [{n: c[n].detach().requires_grad_(True) for n in names} for c in dev_copies]
+
+    def ag_step(i):
+        c, x = dev_copies[i % len(dev_copies)], leaves[i % len(leaves)]
+        o, _ = prism(*(x[n] for n in names), c["cu_seqlens"], w.L)
+        return torch.autograd.grad(o, [x[n] for n in names], grad_outputs=c["dO"])
+
+    for i in range(warmup):
+        ag_step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ag_step(i)
+    torch.cuda.synchronize()
+    ag_us = (time.perf_counter() - t0) / steps * 1e6
     return {"tokens_per_s": tps, "us_per_step": f_us + b_us,
             "fwd_ckpt_us": f_us, "bwd_ckpt_us": b_us, "checkpoint_bytes": cb,
+            "autograd_us_per_step": ag_us,
             "recompute_pair": {"us_per_step": rf_us + rb_us, "fwd_us": rf_us, "bwd_us": rb_us}}
 
 
