@@ -1442,36 +1442,19 @@ __device__ __forceinline__ void state_loop(const WsCtx& c, int jb)
             // the chunk's start state (s0b: bf16 of S before the a-step) as rows
             // [dk][dv] and transposed [dv][dk] per (virtual chunk, head).  A lane
             // holds four consecutive rows of one column: one 8-byte store into the
-            // transposed copy; for the rows, the four lanes of each quad (four
-            // consecutive columns) transpose their 4 x 4 block with two DPP
-            // exchanges so that a lane holds four consecutive columns of one row.
-            // The lane-dependent choices are byte permutes with per-lane selectors
-            // (v_perm_b32: selector bytes 0-3 pick the second operand's bytes, 4-7
-            // the first's), not branches.
+            // transposed copy; for the rows, the four lanes of each quad transpose
+            // their 4 x 4 block (QuadTranspose) so that a lane stores four
+            // consecutive columns of one row.
             const int64_t vc = ((int64_t)(c.seq0 / kC + c.n + ch)) * c.H + c.e;
             const int col = c.j0 + jb * 16 + li;
             const int qp = li & 3;               // position in the quad
-            constexpr uint32_t kFirst = 0x07060504u, kSecond = 0x03020100u;
-            const uint32_t sel_lo = qp < 2 ? kFirst : kSecond, sel_hi = qp < 2 ? kSecond : kFirst;
-            // even lanes: low halves of (own, partner); odd lanes: high halves of (partner, own)
-            const uint32_t sel_pair = (qp & 1) ? 0x03020706u : 0x05040100u;
+            const QuadTranspose qt(qp);
             uint16_t* rows = c.ck + (vc * D + lg * 4 + qp) * c.DV + col - qp;
 #pragma unroll
             for (int ib = 0; ib < D / 16; ++ib) {
                 *reinterpret_cast<v4s_t*>(c.ckT + (vc * c.DV + col) * D + ib * 16 + lg * 4) = s0b[ib];
-                const uint2 w = __builtin_bit_cast(uint2, s0b[ib]);   // rows (0,1), (2,3) of column li
-                // exchange with lane qp ^ 2: lanes 0, 1 keep rows 0, 1 and take those of
-                // lanes 2, 3; lanes 2, 3 keep rows 2, 3 and take those of lanes 0, 1
-                const uint32_t send = __builtin_amdgcn_perm(w.y, w.x, sel_lo);
-                const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x4e, 0xf, 0xf, false);
-                const uint32_t a0 = __builtin_amdgcn_perm(recv, w.x, sel_hi);
-                const uint32_t a1 = __builtin_amdgcn_perm(recv, w.y, sel_lo);
-                // exchange with lane qp ^ 1 and interleave the 16-bit halves
-                const uint32_t b0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)a0, 0xb1, 0xf, 0xf, false);
-                const uint32_t b1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)a1, 0xb1, 0xf, 0xf, false);
                 // row ib * 16 + lg * 4 + qp, columns col - qp .. col - qp + 3
-                *reinterpret_cast<uint2*>(rows + (int64_t)ib * 16 * c.DV) =
-                    make_uint2(__builtin_amdgcn_perm(b0, a0, sel_pair), __builtin_amdgcn_perm(b1, a1, sel_pair));
+                *reinterpret_cast<uint2*>(rows + (int64_t)ib * 16 * c.DV) = qt(__builtin_bit_cast(uint2, s0b[ib]));
             }
         }
     };

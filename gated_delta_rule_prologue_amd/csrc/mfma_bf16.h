@@ -164,4 +164,37 @@ __device__ __forceinline__ void subst(float (&x)[16], const float (&a)[16])
 }
 
 }  // namespace mfma
+
+// A 4 x 4 block of bf16 spread over the four lanes of a quad (four consecutive
+// columns): lane p holds rows 0 .. 3 of column p as w (w.x rows 0 and 1, w.y
+// rows 2 and 3, low halves first).  operator() returns row p of columns 0 .. 3
+// in the same packing, so that a lane can store four consecutive columns of one
+// row with one 8-byte store.  An exchange with lane p ^ 2 (DPP quad_perm) gives
+// lanes 0, 1 the row pairs (0, 1) and lanes 2, 3 the pairs (2, 3) of the
+// partner's column; an exchange with lane p ^ 1 then interleaves the 16-bit
+// halves.  The lane-dependent choices are byte permutes with per-lane selectors
+// (v_perm_b32: selector bytes 0-3 take the second operand's bytes, 4-7 the
+// first's), not branches.
+struct QuadTranspose {
+    uint32_t sel_lo, sel_hi, sel_pair;
+    __device__ __forceinline__ explicit QuadTranspose(int p)
+    {
+        constexpr uint32_t kFirst = 0x07060504u, kSecond = 0x03020100u;
+        sel_lo = p < 2 ? kFirst : kSecond;
+        sel_hi = p < 2 ? kSecond : kFirst;
+        // even lanes: low halves of (own, partner); odd lanes: high halves of (partner, own)
+        sel_pair = (p & 1) ? 0x03020706u : 0x05040100u;
+    }
+    __device__ __forceinline__ uint2 operator()(uint2 w) const
+    {
+        const uint32_t send = __builtin_amdgcn_perm(w.y, w.x, sel_lo);
+        const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x4e, 0xf, 0xf, false);
+        const uint32_t a0 = __builtin_amdgcn_perm(recv, w.x, sel_hi);
+        const uint32_t a1 = __builtin_amdgcn_perm(recv, w.y, sel_lo);
+        const uint32_t b0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)a0, 0xb1, 0xf, 0xf, false);
+        const uint32_t b1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)a1, 0xb1, 0xf, 0xf, false);
+        return make_uint2(__builtin_amdgcn_perm(b0, a0, sel_pair), __builtin_amdgcn_perm(b1, a1, sel_pair));
+    }
+};
+
 }  // namespace prism
