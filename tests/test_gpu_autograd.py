@@ -1,6 +1,11 @@
 """The autograd wrapper (gated_delta_rule_prologue_amd.autograd.prism): loss.backward()
-through prism_fwd_resume and prism_bwd_ex gives the gradients of the fp64
-oracle's backward for every input and the start state."""
+gives the gradients of the fp64 oracle's backward for every input and the
+start state, in each input's dtype, on each of its routes: prism_fwd_ckpt then
+prism_bwd_ckpt with bf16 gradients (the default), prism_fwd_ckpt then the
+recomputing backward when the token walk is forced (PRISM_BWD_CHUNKED=0, which
+prism_bwd_ckpt refuses), and prism_fwd_resume then prism_bwd_ex when the
+environment selects a scan kernel prism_fwd_ckpt does not run
+(PRISM_SCAN_SPECIALISED=0)."""
 import numpy as np
 import pytest
 
@@ -23,9 +28,19 @@ def _gpu():
     binding.lib()
 
 
-@pytest.mark.parametrize("residual,use_state", [("linear", True), ("gelu", True), ("linear", False)])
-def test_autograd_matches_oracle(residual, use_state):
+ROUTES = {"checkpoints": {}, "token-walk": {"PRISM_BWD_CHUNKED": "0"},
+          "recompute": {"PRISM_SCAN_SPECIALISED": "0"}}
+
+
+@pytest.mark.parametrize("residual,use_state,route", [("linear", True, "checkpoints"),
+                                                      ("gelu", True, "checkpoints"),
+                                                      ("linear", False, "checkpoints"),
+                                                      ("linear", True, "token-walk"),
+                                                      ("gelu", True, "recompute")])
+def test_autograd_matches_oracle(residual, use_state, route, monkeypatch):
     import torch
+    for name, value in ROUTES[route].items():
+        monkeypatch.setenv(name, value)
     from gated_delta_rule_prologue_amd import binding
     from gated_delta_rule_prologue_amd.autograd import prism
     w = Workload("ag", heads=2, dk=64, dv=64, L=3, dtype="bf16", seed=81, lengths=[90, 1, 0, 40])
@@ -50,8 +65,10 @@ def test_autograd_matches_oracle(residual, use_state):
     ref = oracle.bwd(inp, d_o.astype(np.float64), dS_final=dsf if use_state else None, S_init=S0,
                      residual=residual)
     for n in FIELDS + ("S_init",):
-        got = (S0_t if n == "S_init" else leaves[n]).grad
+        src = S0_t if n == "S_init" else leaves[n]
+        got = src.grad
         assert got is not None, n
+        assert got.dtype == src.dtype and got.shape == src.shape, n
         err = max_rel(got.float().cpu().numpy(), ref[n])
-        say(f"{residual} state={use_state} d{n} err {err:.3e}")
+        say(f"{route} {residual} state={use_state} d{n} err {err:.3e}")
         assert err <= TOL["bf16"], (n, err)
