@@ -132,13 +132,20 @@ __global__ __launch_bounds__(256) void prologue_kernel(
             w[c][m] = to_f32(wp[m]);
     }
 
-    // sequence containing t0: the largest n with cu[n] <= t0 (then t0 < cu[n+1])
+    // sequence containing t0: the largest n with cu[n] <= t0 (then t0 < cu[n+1]).
+    // The binary search runs once per wavefront, for its first live lane's strip
+    // (the smallest t0 of the wavefront), on wavefront-uniform values, so its
+    // dependent loads are scalar; each lane then walks forward to its own strip
+    // (none or one step where a wavefront spans two strips of long sequences).
+    const int t0w = __builtin_amdgcn_readfirstlane(t0);
     int lo = 0, hi = n_seqs;
     while (hi - lo > 1) {
         int mid = (lo + hi) >> 1;
-        if (cu[mid] <= t0) lo = mid; else hi = mid;
+        if (cu[mid] <= t0w) lo = mid; else hi = mid;
     }
     int n = lo;
+    while (cu[n + 1] <= t0)                          // t0 < cu[n_seqs]: ends by n_seqs - 1
+        ++n;
     int seq_start = cu[n];
     int next_start = cu[n + 1];
 
