@@ -122,54 +122,10 @@ __global__ __launch_bounds__(256) void prologue_kernel(
     const int e = (cg * V) / dk;
     const int i0 = (cg * V) % dk;
 
-    // conv taps for this thread's channels: w[e][i0 + c][m]
-    float w[V][4];
-#pragma unroll
-    for (int c = 0; c < V; ++c) {
-        const T* wp = conv_w + ((int64_t)e * dk + i0 + c) * 4;
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-            w[c][m] = to_f32(wp[m]);
-    }
-
-    // sequence containing t0: the largest n with cu[n] <= t0 (then t0 < cu[n+1]).
-    // The binary search runs once per wavefront, for its first live lane's strip
-    // (the smallest t0 of the wavefront), on wavefront-uniform values, so its
-    // dependent loads are scalar; each lane then walks forward to its own strip
-    // (none or one step where a wavefront spans two strips of long sequences).
-    const int t0w = __builtin_amdgcn_readfirstlane(t0);
-    int lo = 0, hi = n_seqs;
-    while (hi - lo > 1) {
-        int mid = (lo + hi) >> 1;
-        if (cu[mid] <= t0w) lo = mid; else hi = mid;
-    }
-    int n = lo;
-    while (cu[n + 1] <= t0)                          // t0 < cu[n_seqs]: ends by n_seqs - 1
-        ++n;
-    int seq_start = cu[n];
-    int next_start = cu[n + 1];
-
     const int64_t row = (int64_t)H * dk;                 // elements per token of k / kw
     const int64_t lrow = (int64_t)H * (L - 1) * dk;      // elements per token of u / a / h
     const int64_t koff = (int64_t)e * dk + i0;
     const int64_t loff = (int64_t)e * (L - 1) * dk + i0;
-
-    // conv history: x1 = k[t-1], x2 = k[t-2], x3 = k[t-3]; before the sequence
-    // start the carried history of sequence n (slot 2 = the token just before
-    // it) or zero
-    float x1[V], x2[V], x3[V];
-#pragma unroll
-    for (int c = 0; c < V; ++c) { x1[c] = 0.f; x2[c] = 0.f; x3[c] = 0.f; }
-    auto tap = [&](int tau, int start, int seq, float* x) {
-        if (tau >= start)
-            LV::load(k + (int64_t)tau * row + koff, x);
-        else if (HIST)
-            LV::load(k_hist + ((int64_t)seq * H * 3 + (int64_t)e * 3 + (tau - start + 3)) * dk + i0, x);
-    };
-    tap(t0 - 1, seq_start, n, x1);
-    tap(t0 - 2, seq_start, n, x2);
-    tap(t0 - 3, seq_start, n, x3);
-    int hseq = n;                                        // sequence of the latest reset (HIST)
 
     // Software pipeline over the strip: the raw inputs of token t + 1 are in
     // flight while token t is computed, so a thread always has two tokens of
@@ -194,6 +150,82 @@ __global__ __launch_bounds__(256) void prologue_kernel(
                 x.h[s] = R::ld(hb + s * dk);
         }
     };
+    // the strip's first token is loaded before anything else, so that its loads
+    // are in flight during the sequence lookup and the history loads
+    In X[2];
+    fetch(t0, X[0]);
+
+    // conv taps for this thread's channels: w[e][i0 + c][m]
+    float w[V][4];
+#pragma unroll
+    for (int c = 0; c < V; ++c) {
+        const T* wp = conv_w + ((int64_t)e * dk + i0 + c) * 4;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            w[c][m] = to_f32(wp[m]);
+    }
+
+    // sequence containing t0: the largest n with cu[n] <= t0 (then t0 < cu[n+1]).
+    // Binary searches on wavefront-uniform values (scalar loads, which wait on
+    // their own counter, not behind the token loads in flight): one for the
+    // wavefront's first live strip, one for its last.  Where both lie in the
+    // same sequence, so does every lane's strip; otherwise each lane walks
+    // forward from the first one's sequence.
+    auto seq_of = [&](int t) {
+        int lo = 0, hi = n_seqs;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (cu[mid] <= t) lo = mid; else hi = mid;
+        }
+        return lo;
+    };
+    const int t0w = __builtin_amdgcn_readfirstlane(t0);
+    // the first live lane's gid + 63 bounds every lane's gid: its strip (clamped)
+    // is at or past every lane's strip; uniform, so it is computed once, in SALU
+    const int64_t gw = ((int64_t)__builtin_amdgcn_readfirstlane((int)(gid >> 32)) << 32) |
+                       (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)gid);
+    const int t0l = (int)min(((gw + 63) / groups) * strip, (int64_t)T_total - 1);
+    const int nw = seq_of(t0w);
+    int n, seq_start, next_start;
+    if (nw == seq_of(t0l)) {
+        n = nw;
+        seq_start = cu[nw];
+        next_start = cu[nw + 1];
+    } else {
+        n = nw;
+        while (cu[n + 1] <= t0)                      // t0 < cu[n_seqs]: ends by n_seqs - 1
+            ++n;
+        seq_start = cu[n];
+        next_start = cu[n + 1];
+    }
+
+    // conv history: x1 = k[t-1], x2 = k[t-2], x3 = k[t-3]; before the sequence
+    // start the carried history of sequence n (slot 2 = the token just before
+    // it) or zero
+    float x1[V], x2[V], x3[V];
+#pragma unroll
+    for (int c = 0; c < V; ++c) { x1[c] = 0.f; x2[c] = 0.f; x3[c] = 0.f; }
+    auto tap = [&](int tau, int start, int seq, float* x) {
+        if constexpr (HIST) {
+            if (tau >= start)
+                LV::load(k + (int64_t)tau * row + koff, x);
+            else
+                LV::load(k_hist + ((int64_t)seq * H * 3 + (int64_t)e * 3 + (tau - start + 3)) * dk + i0, x);
+        } else {
+            // unconditional (a clamped row, zeroed before the sequence start), so
+            // the three history loads issue together instead of one per branch
+            LV::load(k + (int64_t)max(tau, 0) * row + koff, x);
+            const bool in = tau >= start;
+#pragma unroll
+            for (int c = 0; c < V; ++c)
+                x[c] = in ? x[c] : 0.f;
+        }
+    };
+    tap(t0 - 1, seq_start, n, x1);
+    tap(t0 - 2, seq_start, n, x2);
+    tap(t0 - 3, seq_start, n, x3);
+    int hseq = n;                                        // sequence of the latest reset (HIST)
+
     auto unpack = [&](const RV& v, float* out) {
         constexpr int W = LV::B / 4;
 #pragma unroll
@@ -266,8 +298,6 @@ __global__ __launch_bounds__(256) void prologue_kernel(
     // loop-carried copies (which would wait for the loads just issued), and the
     // prefetches are unconditional (past a short strip's end they re-read its
     // last token), so every wait is for the older set only.
-    In X[2];
-    fetch(t0, X[0]);
 #pragma unroll
     for (int i = 0; i < STRIP; ++i) {
         if (i + 1 < STRIP)
