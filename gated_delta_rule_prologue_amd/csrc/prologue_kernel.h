@@ -207,10 +207,12 @@ __global__ __launch_bounds__(256) void prologue_kernel(
     for (int c = 0; c < V; ++c) { x1[c] = 0.f; x2[c] = 0.f; x3[c] = 0.f; }
     auto tap = [&](int tau, int start, int seq, float* x) {
         if constexpr (HIST) {
-            if (tau >= start)
-                LV::load(k + (int64_t)tau * row + koff, x);
-            else
-                LV::load(k_hist + ((int64_t)seq * H * 3 + (int64_t)e * 3 + (tau - start + 3)) * dk + i0, x);
+            // one unconditional load from the row chosen per lane: k inside the
+            // sequence, the carried history before it (tau >= start - 3 here)
+            const T* src = tau >= start
+                               ? k + (int64_t)max(tau, 0) * row + koff
+                               : k_hist + ((int64_t)seq * H * 3 + (int64_t)e * 3 + (tau - start + 3)) * dk + i0;
+            LV::load(src, x);
         } else {
             // unconditional (a clamped row, zeroed before the sequence start), so
             // the three history loads issue together instead of one per branch
