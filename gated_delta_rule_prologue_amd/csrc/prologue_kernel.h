@@ -339,13 +339,19 @@ static hipError_t launch_LV(const PrologueArgs& p, hipStream_t stream)
 
 // Channels per thread: 16-byte or 8-byte accesses (the narrow form halves the
 // registers a thread holds, which doubles the wavefronts in flight).  With a
-// carried history or the GELU chain: 16-byte groups and strips of 8 tokens only.
+// carried history or the GELU chain: 16-byte groups, strips of 4 (the default) or 8.
 // EXT: the history / GELU kernels (their own translation units).
 template <typename T, int L, bool EXT>
 static hipError_t launch_L(const PrologueArgs& p, hipStream_t stream)
 {
     constexpr int wide = 16 / (int)sizeof(T), narrow = 8 / (int)sizeof(T);
     if constexpr (EXT) {
+        if (p.strip == 4) {
+            if (p.gelu && L > 2)
+                return p.k_hist ? launch_LVS<T, L, wide, 4, true, true>(p, stream)
+                                : launch_LVS<T, L, wide, 4, false, true>(p, stream);
+            return launch_LVS<T, L, wide, 4, true>(p, stream);
+        }
         if (p.gelu && L > 2)
             return p.k_hist ? launch_LVS<T, L, wide, 8, true, true>(p, stream)
                             : launch_LVS<T, L, wide, 8, false, true>(p, stream);
